@@ -1,0 +1,291 @@
+"""Reference (oracle) for the Memory Sparse Attention routing + sparse-attention path.
+
+TEST INFRASTRUCTURE ONLY.  Plain, slow, float64 numpy code that states what the
+path computes, step by step, so that the HIP kernels can be checked against it.
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import it; the product library never does, and it shares no
+code, constants or helpers with ``sparse_retrieval_memory_amd/``.
+
+Sources (web pages on MSA; cited by page and section):
+
+* [abstract]  "MSA: Memory Sparse Attention for Efficient End-to-End Memory
+  Model Scaling to 100M Tokens", chatpaper.ai page, Abstract.
+* [medium]    "Evermind & Shanda Group - MSA: Memory Sparse Attention ...",
+  medium write-up: sec. 2 (system architecture, sparse-attention bullets),
+  sec. 4B (Memory Parallel & tiered storage), sec. 4C (Memory Interleave).
+* [blab]      b-lab.team summary of MSA: sec. 1 "Memory-Sparse Attention (MSA)
+  Layer" (Scalable Sparse Attention, Document-wise RoPE and Global RoPE
+  bullets), sec. 2 (KV cache compression + Memory Parallel), sec. 3 (Memory
+  Interleave) and the three-stage inference pipeline (Global Memory Encoding,
+  Online Routing & Context Assembly, Sparse Generation).
+* [blog]      jkf87.github.io post on MSA, "core technique 1: Top-k Sparse
+  Attention", "core technique 2: Document-wise RoPE".
+
+Readings where the pages leave a step open (each listed in the design doc):
+
+* pooled chunks never cross documents; a trailing partial chunk is averaged
+  over its actual length;
+* document-wise RoPE is applied to K at document-local positions *before*
+  pooling; K_r, Q_r and V are not rotated;
+* RoPE pairs dimension i with i + D/2, frequency base**(-2i/D)  (parity
+  unpinned: no page fixes the pairing);
+* cosine := 0 when either vector has zero norm;
+* head mean is taken over cosines, then the max over query tokens;
+* document score = max over the document's chunk scores;
+* top-k ties go to the lower document id;
+* global RoPE: query row i sits at position k + (Tl - Tq) + i, local key j at
+  k + j, pooled memory keys keep their document-local rotation;
+* every memory entry is visible to every query row; local keys are causal;
+* q-head h reads kv-head h // (Hq / Hkv);
+* the pooled cache is stored as bf16 (round to nearest even) -- the inputs'
+  precision -- and everything downstream of the store is float64;
+* interleave: retrieved documents are excluded from later rounds and their
+  pooled router keys (every chunk, all heads) join the router rows.
+"""
+
+from __future__ import annotations
+
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+
+# --------------------------------------------------------------------- bf16
+def bf16_to_f64(bits) -> np.ndarray:
+    """bf16 bit patterns (uint16/int16) -> float64 (exact)."""
+    b = np.asarray(bits).astype(np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def round_bf16(x) -> np.ndarray:
+    """Round float64 to the nearest bf16 value (ties to even); returns float64.
+
+    Written from the format: 8 significant bits, so scale the frexp mantissa
+    (in [0.5, 1)) by 2**8 and round half-to-even.  Finite, normal-range inputs.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    return np.ldexp(np.rint(m * 256.0) / 256.0, e)
+
+
+def f64_to_bf16_bits(x) -> np.ndarray:
+    """Bit patterns of ``round_bf16(x)`` (exact: the value is a bf16 number)."""
+    r = round_bf16(x).astype(np.float32)
+    return (r.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+# --------------------------------------------------------------------- RoPE
+def rope(x: np.ndarray, pos, base: float) -> np.ndarray:
+    """Rotary position embedding of the last axis at integer positions ``pos``.
+
+    [blab] sec. 1, Document-wise RoPE and Global RoPE bullets: a rotary
+    embedding whose positions restart per document (and, for the query, start
+    after the retrieved blocks).  Pair (x_i, x_{i+D/2}) is rotated by the angle
+    pos * base**(-2i/D).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    D = x.shape[-1]
+    half = D // 2
+    theta = base ** (-2.0 * np.arange(half, dtype=np.float64) / D)
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * theta
+    c, s = np.cos(ang), np.sin(ang)
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+# ------------------------------------------------------------------ pooling
+def chunk_offsets(doc_len: Sequence[int], chunk: int) -> np.ndarray:
+    """CSR offsets of pooled chunks: document d owns ceil(L_d / chunk) chunks."""
+    L = np.asarray(doc_len, dtype=np.int64)
+    off = np.zeros(len(L) + 1, dtype=np.int64)
+    np.cumsum((L + chunk - 1) // chunk, out=off[1:])
+    return off
+
+
+def pool(K, V, Kr, doc_len: Sequence[int], chunk: int, base: float):
+    """Chunk-mean pooling of one routed layer's K, V, K_r.
+
+    [medium] sec. 2 and [blab] sec. 1: each document is cut into fixed-length
+    chunks and K, V and the router key K_r are mean-pooled per chunk; [blab]
+    pipeline stage "Global Memory Encoding" caches the pooled (K, V, K_r).
+    Keys are rotated at document-local positions first ([blab] sec. 1,
+    Document-wise RoPE).  Inputs: float64 [n_tok, H, D] in document order.
+    Returns float64 (Kbar, Vbar, Krbar) [n_chunks, H, D] and the chunk offsets.
+    """
+    K, V, Kr = (np.asarray(a, dtype=np.float64) for a in (K, V, Kr))
+    L = np.asarray(doc_len, dtype=np.int64)
+    off_c = chunk_offsets(L, chunk)
+    n_chunks = int(off_c[-1])
+    H, D = K.shape[1], K.shape[2]
+    Kb = np.empty((n_chunks, H, D))
+    Vb = np.empty((n_chunks, H, D))
+    Rb = np.empty((n_chunks, H, D))
+    t0 = 0
+    for d, Ld in enumerate(L):
+        local = np.arange(Ld)
+        Krot = rope(K[t0:t0 + Ld], local[:, None], base)      # same angle for every head
+        for j in range(int(off_c[d + 1] - off_c[d])):
+            a, b = j * chunk, min((j + 1) * chunk, int(Ld))
+            g = int(off_c[d]) + j
+            Kb[g] = Krot[a:b].mean(axis=0)
+            Vb[g] = V[t0 + a:t0 + b].mean(axis=0)
+            Rb[g] = Kr[t0 + a:t0 + b].mean(axis=0)
+        t0 += int(Ld)
+    return Kb, Vb, Rb, off_c
+
+
+# ------------------------------------------------------------------ routing
+def head_mean_cosine(Qr, Krbar) -> np.ndarray:
+    """S[r, g] = (1/H) * sum_h cos(Qr[r, h], Krbar[g, h]);  cos := 0 for a zero vector.
+
+    [medium] sec. 2: cosine similarity between the query and memory chunks;
+    [blab] sec. 1: similarity is averaged over heads (then maxed over tokens).
+    Qr: [R, H, D], Krbar: [G, H, D] (float64).
+    """
+    Qr = np.asarray(Qr, dtype=np.float64)
+    Kb = np.asarray(Krbar, dtype=np.float64)
+    R, H, _ = Qr.shape
+    S = np.zeros((R, Kb.shape[0]))
+    for h in range(H):
+        q, k = Qr[:, h, :], Kb[:, h, :]
+        nq = np.sqrt((q * q).sum(axis=1))
+        nk = np.sqrt((k * k).sum(axis=1))
+        iq = np.divide(1.0, nq, out=np.zeros_like(nq), where=nq > 0)
+        ik = np.divide(1.0, nk, out=np.zeros_like(nk), where=nk > 0)
+        S += (q @ k.T) * iq[:, None] * ik[None, :]
+    return S / H
+
+
+def route(Qr, Krbar, doc_chunk_off, exclude=None, block: int = 65536):
+    """Chunk and document relevance for a batch of queries.
+
+    [blab] sec. 1: the query's router projection Q_r is matched against the
+    pooled K_r by cosine similarity, averaged over heads, then the token-wise
+    maximum is taken; [medium] sec. 2 / [blab] pipeline stage 2: the result
+    ranks documents.  Document score = max over its chunks.  Excluded
+    documents score -inf.
+
+    Qr: [B, T, H, D]; Krbar: [G, H, D]; doc_chunk_off: [n_docs + 1];
+    exclude: bool [B, n_docs] or None.  Returns (chunk_scores [B, G],
+    doc_scores [B, n_docs]) float64.  Streams Krbar in blocks of chunks.
+    """
+    Qr = np.asarray(Qr, dtype=np.float64)
+    B, T, H, D = Qr.shape
+    G = Krbar.shape[0]
+    off = np.asarray(doc_chunk_off, dtype=np.int64)
+    chunk = np.empty((B, G))
+    rows = Qr.reshape(B * T, H, D)
+    for g0 in range(0, G, block):
+        g1 = min(G, g0 + block)
+        S = head_mean_cosine(rows, np.asarray(Krbar[g0:g1], dtype=np.float64))
+        chunk[:, g0:g1] = S.reshape(B, T, g1 - g0).max(axis=1)
+    doc = np.maximum.reduceat(chunk, off[:-1], axis=1) if G else np.empty((B, 0))
+    if exclude is not None:
+        doc = np.where(np.asarray(exclude, dtype=bool), -np.inf, doc)
+    return chunk, doc
+
+
+def topk(doc_scores, k: int) -> Tuple[np.ndarray, np.ndarray]:
+    """The k best documents per query: score descending, ties to the lower id.
+
+    [medium] sec. 2, [blab] sec. 1 and pipeline stage 2, [blog] core
+    technique 1: select the top-k most relevant documents.
+    """
+    s = np.asarray(doc_scores, dtype=np.float64)
+    B, n = s.shape
+    idx = np.empty((B, k), dtype=np.int64)
+    for b in range(B):
+        order = np.lexsort((np.arange(n), -s[b]))
+        idx[b] = order[:k]
+    return idx, np.take_along_axis(s, idx, axis=1)
+
+
+def assemble(top_idx_row: Sequence[int], doc_chunk_off) -> np.ndarray:
+    """Global chunk indices of the selected documents, in rank order, chunks in order.
+
+    [blab] pipeline stage 2: only the selected documents' pooled K/V are loaded
+    and joined to the local context; [medium] sec. 4B: content KV of the
+    selected items is fetched from host memory.
+    """
+    off = np.asarray(doc_chunk_off, dtype=np.int64)
+    parts = [np.arange(off[d], off[d + 1]) for d in top_idx_row]
+    return np.concatenate(parts) if parts else np.zeros(0, dtype=np.int64)
+
+
+# ---------------------------------------------------------------- attention
+def attend(Q, Kloc, Vloc, Kmem, Vmem, rope_offset: int, base: float, scale: float,
+           return_probs: bool = False):
+    """Sparse attention of one query over [pooled memory ++ causal local KV].
+
+    [medium] sec. 2 and [blab] sec. 1: the selected documents' compressed K/V
+    are concatenated with the query's local K/V for autoregressive decoding;
+    [blab] sec. 1, Global RoPE: the query's start index is offset by k, the
+    number of retrieved blocks.  Q: [Tq, Hq, D]; Kloc, Vloc: [Tl, Hkv, D];
+    Kmem, Vmem: [M, Hkv, D] (already rotated at document-local positions).
+    Returns O [Tq, Hq, D] float64 (and the probabilities [Hq, Tq, M + Tl]).
+    """
+    Q = np.asarray(Q, dtype=np.float64)
+    Kloc = np.asarray(Kloc, dtype=np.float64)
+    Vloc = np.asarray(Vloc, dtype=np.float64)
+    Kmem = np.asarray(Kmem, dtype=np.float64).reshape(-1, Kloc.shape[1], Kloc.shape[2])
+    Vmem = np.asarray(Vmem, dtype=np.float64).reshape(-1, Kloc.shape[1], Kloc.shape[2])
+    Tq, Hq, D = Q.shape
+    Tl, Hkv, _ = Kloc.shape
+    M = Kmem.shape[0]
+    group = Hq // Hkv
+    qpos = rope_offset + (Tl - Tq) + np.arange(Tq)
+    kpos = rope_offset + np.arange(Tl)
+    Qrot = rope(Q, qpos[:, None], base)
+    Krot = rope(Kloc, kpos[:, None], base)
+    visible = np.ones((Tq, M + Tl), dtype=bool)
+    visible[:, M:] = np.arange(Tl)[None, :] <= ((Tl - Tq) + np.arange(Tq))[:, None]
+    O = np.empty((Tq, Hq, D))
+    P_all = np.empty((Hq, Tq, M + Tl)) if return_probs else None
+    for h in range(Hq):
+        g = h // group
+        keys = np.concatenate([Kmem[:, g], Krot[:, g]], axis=0)
+        vals = np.concatenate([Vmem[:, g], Vloc[:, g]], axis=0)
+        logits = (Qrot[:, h] @ keys.T) * scale
+        logits = np.where(visible, logits, -np.inf)
+        mx = logits.max(axis=1, keepdims=True)
+        e = np.exp(logits - mx)
+        P = e / e.sum(axis=1, keepdims=True)
+        O[:, h] = P @ vals
+        if return_probs:
+            P_all[h] = P
+    return (O, P_all) if return_probs else O
+
+
+# --------------------------------------------------------------- interleave
+def interleave(Qr, Krbar, Kbar, Vbar, doc_chunk_off, k: int, rounds: int,
+               Q, Kloc, Vloc, base: float, scale: float, exclude0=None) -> List[Dict]:
+    """Memory Interleave for one query: rounds of route -> top-k -> attend.
+
+    [medium] sec. 4C and [blab] sec. 3: retrieval and context expansion repeat,
+    and documents found in one round become part of the next round's query.
+    Reading: each round routes with the original router rows plus the pooled
+    router keys of every chunk retrieved so far (retrieval order), excludes
+    documents already retrieved, and attends over all retrieved documents
+    (retrieval order) with the global RoPE offset equal to their count.
+    Qr: [T0, H, D]; Krbar/Kbar/Vbar: [G, H, D] (the bf16 store as float64).
+    """
+    off = np.asarray(doc_chunk_off, dtype=np.int64)
+    n_docs = len(off) - 1
+    Qr = np.asarray(Qr, dtype=np.float64)
+    retrieved: List[int] = []
+    out = []
+    for r in range(rounds):
+        extra = assemble(retrieved, off)
+        rows = np.concatenate([Qr, np.asarray(Krbar[extra], dtype=np.float64)], axis=0) if len(extra) else Qr
+        excl = np.zeros(n_docs, dtype=bool) if exclude0 is None else np.asarray(exclude0, bool).copy()
+        excl[retrieved] = True
+        chunk_s, doc_s = route(rows[None], Krbar, off, excl[None])
+        idx, sc = topk(doc_s, k)
+        new = [int(d) for d in idx[0]]
+        retrieved += new
+        mem = assemble(retrieved, off)
+        O = attend(Q, Kloc, Vloc, np.asarray(Kbar[mem]), np.asarray(Vbar[mem]),
+                   rope_offset=len(retrieved), base=base, scale=scale)
+        out.append(dict(rows=rows, doc_scores=doc_s[0], chunk_scores=chunk_s[0], top_idx=np.array(new),
+                        top_scores=sc[0], retrieved=list(retrieved), mem_chunks=mem, O=O))
+    return out

@@ -1,0 +1,325 @@
+"""Pins for the oracle: closed forms, hand-worked examples, invariants, library
+routines in special cases and brute force on tiny inputs.
+
+Each test pins the oracle to something other than itself, chosen so that a
+plausible slip (a dropped term, a sign, a transposed operand, a wrong axis or
+index) fails at least one of them.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import bruteforce as bf
+from oracle import msa_oracle as O
+from synth import splitmix as sm
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")))
+BASE = 1.0e6
+
+
+def rng(seed=0):
+    return np.random.default_rng(seed)
+
+
+# ----------------------------------------------------------------- bf16 round
+def test_round_bf16_ties_and_known_values():
+    one = 1.0
+    assert O.round_bf16(one + 2 ** -8) == 1.0                    # tie -> even (1.0)
+    assert O.round_bf16(one + 3 * 2 ** -8) == 1.0 + 2 ** -6      # tie -> even (mantissa 2)
+    assert O.round_bf16(one + 2 ** -8 + 2 ** -20) == 1.0 + 2 ** -7
+    assert O.round_bf16(-(one + 2 ** -8)) == -1.0
+    assert O.round_bf16(0.0) == 0.0
+
+
+def test_round_bf16_matches_independent_generator_rounding():
+    # synth rounds through round-to-odd float32; oracle rounds the frexp mantissa
+    x = rng(1).standard_normal(200000) * np.exp(rng(2).uniform(-20, 20, 200000))
+    a = O.f64_to_bf16_bits(x)
+    b = sm.f64_to_bf16_bits(x)
+    assert np.array_equal(a, b)
+
+
+# ----------------------------------------------------------------------- RoPE
+def test_rope_golden():
+    g = GOLD["rope_d4"]
+    for c in g["cases"]:
+        got = O.rope(np.array(c["x"], float), c["pos"], g["base"])
+        np.testing.assert_allclose(got, c["expect"], rtol=0, atol=1e-14)
+
+
+def test_rope_identity_norm_composition_relativity():
+    x = rng(3).standard_normal((5, 128))
+    np.testing.assert_array_equal(O.rope(x, 0, BASE), x)
+    y = O.rope(x, np.arange(5) * 97, BASE)
+    np.testing.assert_allclose(np.linalg.norm(y, axis=1), np.linalg.norm(x, axis=1), rtol=1e-13)
+    np.testing.assert_allclose(O.rope(O.rope(x, 17, BASE), 40, BASE), O.rope(x, 57, BASE), atol=1e-12)
+    q, k = x[0], x[1]
+    d1 = O.rope(q, 300, BASE) @ O.rope(k, 120, BASE)
+    d2 = O.rope(q, 1300, BASE) @ O.rope(k, 1120, BASE)
+    assert abs(d1 - d2) < 1e-10
+    # pairing: dimension i only mixes with i + D/2
+    e = np.zeros(128); e[5] = 1.0
+    r = O.rope(e, 11, BASE)
+    assert set(np.flatnonzero(np.abs(r) > 1e-15)) <= {5, 69}
+
+
+def test_rope_bruteforce():
+    x = rng(4).standard_normal((3, 16))
+    for p in (0, 1, 9, 1234):
+        for row in x:
+            np.testing.assert_allclose(O.rope(row, p, BASE), bf.rope_vec(list(row), p, BASE), atol=1e-13)
+
+
+# -------------------------------------------------------------------- pooling
+def test_pool_golden_partial_chunk():
+    g = GOLD["pool_partial_chunk"]
+    K = np.array(g["K"], float); V = np.array(g["V"], float)
+    Kb, Vb, Rb, off = O.pool(K, V, V, g["doc_len"], g["chunk"], g["base"])
+    np.testing.assert_allclose(Vb, g["expect_V"], atol=1e-15)
+    np.testing.assert_allclose(Rb, g["expect_V"], atol=1e-15)
+    np.testing.assert_allclose(Kb, g["expect_K"], atol=1e-15)
+    assert list(off) == [0, 2, 3]
+
+
+def test_pool_constant_mean_linearity_avgpool():
+    r = rng(5)
+    L = [130, 64, 1, 200]
+    n = sum(L)
+    V = r.standard_normal((n, 2, 8)); Kr = r.standard_normal((n, 2, 8)); K = r.standard_normal((n, 2, 8))
+    # constant chunk -> that constant
+    Vc = np.broadcast_to(np.arange(16.0).reshape(1, 2, 8), (n, 2, 8))
+    _, Vb, _, off = O.pool(K, Vc, Kr, L, 64, BASE)
+    assert np.all(Vb == np.arange(16.0).reshape(1, 2, 8))
+    # chunk >= doc length -> per-document mean
+    _, Vb, Rb, off = O.pool(K, V, Kr, L, 512, BASE)
+    t = np.concatenate([[0], np.cumsum(L)])
+    for d in range(len(L)):
+        np.testing.assert_allclose(Vb[d], V[t[d]:t[d + 1]].mean(axis=0), rtol=1e-13)
+    # linearity in V and Kr
+    V2 = r.standard_normal((n, 2, 8))
+    a = O.pool(K, V, Kr, L, 64, BASE)[1]; b = O.pool(K, V2, Kr, L, 64, BASE)[1]
+    c = O.pool(K, 2 * V - 3 * V2, Kr, L, 64, BASE)[1]
+    np.testing.assert_allclose(c, 2 * a - 3 * b, atol=1e-12)
+    # full chunks of an unrotated tensor equal torch avg_pool1d over the document
+    Kb, Vb, Rb, off = O.pool(K, V, Kr, L, 64, BASE)
+    doc0 = torch.from_numpy(V[:128].reshape(128, 16).T.copy())[None]       # [1, C, L]
+    ap = torch.nn.functional.avg_pool1d(doc0, 64, 64)[0].T.numpy().reshape(2, 2, 8)
+    np.testing.assert_allclose(Vb[:2], ap, atol=1e-13)
+    # partial trailing chunk of doc 0: tokens 128..129 only
+    np.testing.assert_allclose(Vb[2], V[128:130].mean(axis=0), atol=1e-14)
+    assert list(off) == [0, 3, 4, 5, 9]
+
+
+def test_pool_rope_positions_restart_per_document():
+    # same raw K in two documents -> same pooled Kbar (positions restart at 0)
+    r = rng(6)
+    Kdoc = r.standard_normal((70, 2, 8))
+    K = np.concatenate([Kdoc, Kdoc]); V = np.zeros_like(K)
+    Kb, _, _, _ = O.pool(K, V, V, [70, 70], 64, BASE)
+    np.testing.assert_allclose(Kb[0:2], Kb[2:4], atol=1e-14)
+    # and the first chunk differs from the unrotated mean (rotation really applied)
+    assert np.abs(Kb[0] - Kdoc[:64].mean(axis=0)).max() > 1e-3
+
+
+def test_pool_bruteforce():
+    r = rng(7)
+    L = [5, 3, 8]
+    n = sum(L)
+    K, V, Kr = (r.standard_normal((n, 2, 4)) for _ in range(3))
+    Kb, Vb, Rb, _ = O.pool(K, V, Kr, L, 3, 100.0)
+    bK, bV, bR = bf.pool(K.tolist(), V.tolist(), Kr.tolist(), L, 3, 100.0)
+    np.testing.assert_allclose(Kb, bK, atol=1e-13)
+    np.testing.assert_allclose(Vb, bV, atol=1e-13)
+    np.testing.assert_allclose(Rb, bR, atol=1e-13)
+
+
+# -------------------------------------------------------------------- routing
+def test_route_golden():
+    g = GOLD["route_two_docs"]
+    off = np.concatenate([[0], np.cumsum(g["doc_chunks"])])
+    ch, doc = O.route(np.array(g["Qr"], float), np.array(g["Krbar"], float), off)
+    np.testing.assert_allclose(ch, g["expect_chunk"], atol=1e-15)
+    np.testing.assert_allclose(doc, g["expect_doc"], atol=1e-15)
+
+
+def _rand_route_case(seed, B=2, T=5, H=3, D=16, ndocs=7):
+    r = rng(seed)
+    n_ch = r.integers(1, 4, ndocs)
+    off = np.concatenate([[0], np.cumsum(n_ch)])
+    Qr = r.standard_normal((B, T, H, D))
+    Kb = r.standard_normal((int(off[-1]), H, D))
+    return Qr, Kb, off, n_ch
+
+
+def test_route_bruteforce_and_exclusion():
+    Qr, Kb, off, n_ch = _rand_route_case(8)
+    excl = np.zeros((2, 7), bool); excl[1, 3] = True
+    ch, doc = O.route(Qr, Kb, off, excl)
+    bch, bdoc = bf.route(Qr.tolist(), Kb.tolist(), list(n_ch), excl.tolist())
+    np.testing.assert_allclose(ch, bch, atol=1e-13)
+    np.testing.assert_allclose(doc, bdoc, atol=1e-13)
+    assert doc[1, 3] == -np.inf and np.isfinite(doc[0, 3])
+
+
+def test_route_invariants():
+    Qr, Kb, off, _ = _rand_route_case(9, B=1, T=4, H=8, D=32, ndocs=9)
+    ch, doc = O.route(Qr, Kb, off)
+    assert np.all(np.abs(ch) <= 1 + 1e-12)
+    # scaling rows by powers of two (exact) leaves every score unchanged
+    sc = 2.0 ** rng(10).integers(-6, 7, size=(Kb.shape[0], 8, 1))
+    ch2, doc2 = O.route(Qr * 4.0, Kb * sc, off)
+    np.testing.assert_allclose(ch2, ch, atol=1e-14)
+    # a router row identical to a chunk in every head scores exactly 1 there
+    Q1 = Qr.copy(); Q1[0, 2] = Kb[5]
+    ch3, _ = O.route(Q1, Kb, off)
+    assert abs(ch3[0, 5] - 1.0) < 1e-14
+    # permuting documents permutes document scores
+    n_docs = len(off) - 1
+    perm = rng(11).permutation(n_docs)
+    blocks = [Kb[off[d]:off[d + 1]] for d in perm]
+    Kp = np.concatenate(blocks)
+    offp = np.concatenate([[0], np.cumsum([len(b) for b in blocks])])
+    _, docp = O.route(Qr, Kp, offp)
+    np.testing.assert_allclose(docp[0], doc[0, perm], atol=1e-14)
+    # head mean, not head sum: H identical heads give the single-head cosine
+    qs = rng(12).standard_normal((1, 1, 1, 32)); ks = rng(13).standard_normal((3, 1, 32))
+    c1, _ = O.route(qs, ks, [0, 3])
+    c8, _ = O.route(np.repeat(qs, 8, axis=2), np.repeat(ks, 8, axis=1), [0, 3])
+    np.testing.assert_allclose(c8, c1, atol=1e-14)
+
+
+def test_route_reduces_to_torch_cosine_similarity():
+    r = rng(14)
+    q = r.standard_normal((1, 1, 1, 64)); k = r.standard_normal((10, 1, 64))
+    ch, _ = O.route(q, k, np.arange(11))
+    ref = torch.nn.functional.cosine_similarity(torch.from_numpy(q[0, 0]), torch.from_numpy(k[:, 0]), dim=-1)
+    np.testing.assert_allclose(ch[0], ref.numpy(), atol=1e-14)
+
+
+def test_route_zero_vectors_score_zero():
+    q = np.zeros((1, 1, 2, 4)); q[0, 0, 1] = [1, 0, 0, 0]
+    k = np.zeros((1, 2, 4)); k[0, 0] = [1, 1, 1, 1]; k[0, 1] = [2, 0, 0, 0]
+    ch, _ = O.route(q, k, [0, 1])
+    assert ch[0, 0] == 0.5          # head 0 has a zero query -> 0; head 1 -> 1; mean 0.5
+
+
+def test_route_token_max_not_mean():
+    # two tokens, one matching: the chunk score is the max over tokens
+    k = rng(15).standard_normal((1, 2, 8))
+    q = np.stack([k[0], -k[0]])[None]
+    ch, _ = O.route(q, k, [0, 1])
+    assert abs(ch[0, 0] - 1.0) < 1e-14
+
+
+# ---------------------------------------------------------------------- top-k
+def test_topk_golden_ties():
+    g = GOLD["topk_ties"]
+    idx, sc = O.topk(np.array([g["scores"]]), g["k"])
+    assert list(idx[0]) == g["expect"]
+
+
+def test_topk_vs_sorted_torch_and_bruteforce():
+    r = rng(16)
+    s = np.round(r.standard_normal((3, 50)), 1)      # many ties
+    for b in range(3):
+        ref = sorted(range(50), key=lambda i: (-s[b, i], i))[:9]
+        idx, _ = O.topk(s[b:b + 1], 9)
+        assert list(idx[0]) == ref
+        assert list(idx[0]) == bf.topk(list(s[b]), 9)
+    d = r.standard_normal((2, 40))
+    idx, sc = O.topk(d, 7)
+    tv, ti = torch.topk(torch.from_numpy(d), 7, dim=1)
+    assert np.array_equal(idx, ti.numpy())
+    np.testing.assert_array_equal(sc, tv.numpy())
+    # -inf (excluded) documents come last, lowest id first
+    e = np.array([[-np.inf, 0.3, -np.inf, 0.1]])
+    assert list(O.topk(e, 4)[0][0]) == [1, 3, 0, 2]
+
+
+def test_assemble_rank_order():
+    off = np.array([0, 2, 5, 6])
+    assert list(O.assemble([2, 0, 1], off)) == [5, 0, 1, 2, 3, 4]
+
+
+# ------------------------------------------------------------------ attention
+def test_attend_golden():
+    g = GOLD["attend_tiny"]
+    for c in g["cases"]:
+        o = O.attend(np.array(g["Q"], float), np.array(g["Kloc"], float), np.array(g["Vloc"], float),
+                     np.array(g["Kmem"], float), np.array(g["Vmem"], float), c["offset"], g["base"], g["scale"])
+        np.testing.assert_allclose(o, c["expect"], atol=1e-14)
+
+
+def _att_case(seed, Tq=3, Tl=5, M=4, Hq=4, Hkv=2, D=16):
+    r = rng(seed)
+    return (r.standard_normal((Tq, Hq, D)), r.standard_normal((Tl, Hkv, D)), r.standard_normal((Tl, Hkv, D)),
+            r.standard_normal((M, Hkv, D)), r.standard_normal((M, Hkv, D)))
+
+
+def test_attend_bruteforce():
+    Q, Kl, Vl, Km, Vm = _att_case(17)
+    for off in (0, 3):
+        o = O.attend(Q, Kl, Vl, Km, Vm, off, 100.0, 0.25)
+        b = bf.attend(Q.tolist(), Kl.tolist(), Vl.tolist(), Km.tolist(), Vm.tolist(), off, 100.0, 0.25)
+        np.testing.assert_allclose(o, b, atol=1e-12)
+
+
+def test_attend_invariants():
+    Q, Kl, Vl, Km, Vm = _att_case(18, Tq=4, Tl=6, M=5, Hq=8, Hkv=2, D=32)
+    o, P = O.attend(Q, Kl, Vl, Km, Vm, 5, BASE, 32 ** -0.5, return_probs=True)
+    np.testing.assert_allclose(P.sum(axis=-1), 1.0, atol=1e-13)
+    # causal: row i sees local keys j <= (Tl - Tq) + i only
+    assert np.all(P[:, 0, 5 + 3:] == 0) and np.all(P[:, 0, 5:5 + 3] > 0)
+    # constant V -> that V
+    vc = rng(19).standard_normal((1, 2, 32))
+    oc = O.attend(Q, Kl, np.broadcast_to(vc, Vl.shape), Km, np.broadcast_to(vc, Vm.shape), 5, BASE, 0.2)
+    np.testing.assert_allclose(oc, np.broadcast_to(np.repeat(vc, 4, axis=1), oc.shape), atol=1e-13)
+    # permuting memory entries leaves the output unchanged
+    p = rng(20).permutation(5)
+    np.testing.assert_allclose(O.attend(Q, Kl, Vl, Km[p], Vm[p], 5, BASE, 0.2),
+                               O.attend(Q, Kl, Vl, Km, Vm, 5, BASE, 0.2), atol=1e-13)
+    # a single dominant logit returns that memory row's V (kv-head 1 serves q-heads 4..7)
+    # (dimension 15 of D=32 has frequency 1e6**(-30/32): RoPE barely turns it)
+    Km2 = Km.copy(); Km2[3, 1] = 0.0
+    Qd = np.zeros_like(Q); Qd[:, 4:, 15] = 1.0
+    Km2[3, 1, 15] = 1e4
+    od = O.attend(Qd, np.zeros_like(Kl), Vl, Km2, Vm, 0, BASE, 1.0)
+    np.testing.assert_allclose(od[0, 4], Vm[3, 1], atol=1e-12)
+
+
+def test_attend_m0_is_causal_gqa_sdpa_and_offset_free():
+    Q, Kl, Vl, Km, Vm = _att_case(21, Tq=4, Tl=7, M=0, Hq=8, Hkv=2, D=32)
+    o = O.attend(Q, Kl, Vl, Km[:0], Vm[:0], 0, BASE, 32 ** -0.5)
+    # textbook: rotate at positions (Tl-Tq)+i and j, repeat kv heads, bottom-right causal mask
+    Qr = O.rope(Q, (3 + np.arange(4))[:, None], BASE)
+    Kr = O.rope(Kl, np.arange(7)[:, None], BASE)
+    q = torch.from_numpy(Qr).permute(1, 0, 2)[None]
+    k = torch.from_numpy(np.repeat(Kr, 4, axis=1)).permute(1, 0, 2)[None]
+    v = torch.from_numpy(np.repeat(Vl, 4, axis=1)).permute(1, 0, 2)[None]
+    mask = torch.from_numpy(np.arange(7)[None, :] <= (3 + np.arange(4))[:, None])
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask, scale=32 ** -0.5)
+    np.testing.assert_allclose(o, ref[0].permute(1, 0, 2).numpy(), atol=1e-12)
+    # with no memory, shifting the offset changes nothing (RoPE depends on differences)
+    o7 = O.attend(Q, Kl, Vl, Km[:0], Vm[:0], 7, BASE, 32 ** -0.5)
+    np.testing.assert_allclose(o7, o, atol=1e-11)
+
+
+def test_attend_offset_matters_with_memory():
+    Q, Kl, Vl, Km, Vm = _att_case(22, M=4)
+    a = O.attend(Q, Kl, Vl, Km, Vm, 4, BASE, 0.25)
+    b = O.attend(Q, Kl, Vl, Km, Vm, 5, BASE, 0.25)
+    assert np.abs(a - b).max() > 1e-6
+
+
+def test_attend_gqa_mapping():
+    # q-head h must read kv-head h // (Hq/Hkv): zero one kv head's V and see which q-heads go to 0
+    Q, Kl, Vl, Km, Vm = _att_case(23, Hq=8, Hkv=2)
+    Vl2, Vm2 = Vl.copy(), Vm.copy()
+    Vl2[:, 1] = 0; Vm2[:, 1] = 0
+    o = O.attend(Q, Kl, Vl2, Km, Vm2, 2, BASE, 0.25)
+    assert np.all(o[:, 4:] == 0) and np.all(np.abs(o[:, :4]).max(axis=-1) > 0)
