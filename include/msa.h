@@ -1,0 +1,212 @@
+/*
+ * msa.h -- C ABI of the Memory Sparse Attention (MSA) routing + sparse-attention
+ * hot path for AMD Instinct MI355X (gfx950).
+ *
+ * The calls follow the three-stage inference pipeline the MSA pages describe
+ * (b-lab.team summary of MSA, "Global Memory Encoding", "Online Routing &
+ * Context Assembly", "Sparse Generation"):
+ *
+ *   msa_pool_chunks         offline: chunk-mean pooled (Kbar, Vbar, Krbar) cache
+ *   msa_route_scores        online: cosine routing scan over every Krbar chunk
+ *   msa_topk_docs           online: the k most relevant documents
+ *   msa_fetch_docs          online: copy the selected content KV from pinned host
+ *   msa_gather_docs         online: same, as one device kernel reading mapped host memory
+ *   msa_sparse_attn_decode  generation: GQA attention over [memory ++ local KV]
+ *
+ * Conventions (every call):
+ *   - Tensors are row-major with the last dimension contiguous.  bf16 tensors
+ *     are passed as uint16_t bit patterns.  Pointers are device pointers
+ *     unless the parameter name ends in _host.
+ *   - The caller allocates and frees every buffer (including workspaces and the
+ *     pinned host store).  The library allocates nothing and keeps no state
+ *     besides a thread-local error message.
+ *   - Calls are asynchronous on `stream`; results are valid once the stream has
+ *     reached the call.  Arguments are validated on the host before anything
+ *     is launched: an invalid call returns a negative status and launches
+ *     nothing.  HIP launch errors return MSA_ERR_HIP.  msa_last_error() gives
+ *     a human-readable reason for the last failure on the calling thread.
+ *   - Device pointers must be 16-byte aligned.
+ */
+#ifndef MSA_H_
+#define MSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MSA_OK 0
+#define MSA_ERR_INVALID_ARG (-1)   /* null pointer, bad size, bad alignment, ... */
+#define MSA_ERR_UNSUPPORTED (-2)   /* a shape this build does not implement (e.g. D != 128) */
+#define MSA_ERR_WORKSPACE (-3)     /* workspace smaller than the *_workspace_bytes() value */
+#define MSA_ERR_HIP (-4)           /* a HIP runtime call failed */
+
+#define MSA_VERSION 100            /* 1.0.0 */
+
+int msa_version(void);
+const char* msa_status_string(int status);
+/* Reason for the most recent failing call on this thread ("" if none). */
+const char* msa_last_error(void);
+
+/*
+ * msa_pool_chunks -- chunk-mean pooling of one routed layer (offline encoding).
+ *
+ * Defined by: medium write-up sec. 2 and b-lab.team summary sec. 1 (documents
+ * are cut into fixed-length chunks and K, V and the router key K_r are
+ * mean-pooled per chunk); b-lab.team sec. 1, Document-wise RoPE (positions
+ * restart at 0 in every document).
+ *
+ * For document d with L_d = doc_tok_off[d+1] - doc_tok_off[d] tokens and chunk
+ * j covering local tokens [j*chunk_len, min((j+1)*chunk_len, L_d)), chunk
+ * g = doc_chunk_off[d] + j gets
+ *   Kbar[g]  = mean_t RoPE(K[t], t_local)     (pairs (i, i+D/2), angle t_local*base^(-2i/D))
+ *   Vbar[g]  = mean_t V[t]
+ *   Krbar[g] = mean_t Kr[t]
+ * accumulated in fp32 (angles in fp64) and rounded to bf16 (nearest even).
+ * A trailing partial chunk is averaged over its actual length.
+ *
+ *   K, V, Kr            bf16 [n_tok, H, D]          tokens of the documents, in order
+ *   doc_tok_off         int64 [n_docs+1] (device)   token offsets; doc_tok_off[0] may be
+ *                                                    non-zero (slab processing): token t of
+ *                                                    the corpus is row t - doc_tok_off[0]
+ *   doc_chunk_off       int64 [n_docs+1] (device)   chunk offsets, doc_chunk_off[d+1] -
+ *                                                    doc_chunk_off[d] = ceil(L_d/chunk_len) >= 1;
+ *                                                    output row = chunk - doc_chunk_off[0]
+ *   n_tok, n_chunks     rows of the inputs / outputs (used for validation and bounds)
+ *   H in {1,2,4,8,16}, D == 128, chunk_len in [1, 1024]
+ *   Kbar, Vbar, Krbar   bf16 [n_chunks, H, D] outputs
+ */
+int msa_pool_chunks(const uint16_t* K, const uint16_t* V, const uint16_t* Kr,
+                    const int64_t* doc_tok_off, const int64_t* doc_chunk_off, int64_t n_docs,
+                    int64_t n_tok, int64_t n_chunks, int H, int D, int chunk_len,
+                    double rope_base, uint16_t* Kbar, uint16_t* Vbar, uint16_t* Krbar,
+                    hipStream_t stream);
+
+/*
+ * msa_route_scores -- routing scan: chunk and document relevance.
+ *
+ * Defined by: b-lab.team summary sec. 1 (cosine similarity of the query's
+ * router projection Q_r with the pooled K_r, averaged over heads, then the
+ * token-wise maximum) and medium write-up sec. 2 (chunk similarity selects the
+ * most relevant documents).
+ *
+ *   S[b,t,g]           = (1/H) sum_h cos(Qr[b,t,h,:], Krbar[g,h,:])   (cos := 0 on a zero vector)
+ *   chunk_scores[b,g]  = max_{t<T} S[b,t,g]
+ *   doc_scores[b,d]    = max over d's chunks, or -inf where doc_exclude[b,d] != 0
+ *
+ *   Qr            bf16 [B, T, H, D]
+ *   Krbar         bf16 [n_chunks, H, D]        (HBM-resident routing-key store)
+ *   doc_chunk_off int64 [n_docs+1] (device), doc_chunk_off[0] == 0, doc_chunk_off[n_docs] == n_chunks
+ *   doc_exclude   uint8 [B, n_docs] or NULL
+ *   doc_scores    fp32 [B, n_docs] out
+ *   chunk_scores  fp32 [B, n_chunks] out, or NULL
+ *   workspace     >= msa_route_workspace_bytes(B, T, H, D, n_chunks, n_docs) bytes
+ *   H in {1,2,4,8}, D == 128, B >= 1, T >= 1, n_docs >= 1.
+ * Products use the raw bf16 operands (exact) with fp32 accumulation; norms are
+ * applied in fp32.  Results are deterministic (max reductions only).
+ */
+size_t msa_route_workspace_bytes(int B, int T, int H, int D, int64_t n_chunks, int64_t n_docs);
+int msa_route_scores(const uint16_t* Qr, int B, int T, int H, int D,
+                     const uint16_t* Krbar, int64_t n_chunks,
+                     const int64_t* doc_chunk_off, int64_t n_docs,
+                     const uint8_t* doc_exclude, float* doc_scores, float* chunk_scores,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * msa_topk_docs -- the k most relevant documents per query.
+ *
+ * Defined by: medium write-up sec. 2, b-lab.team sec. 1 and pipeline stage 2,
+ * jkf87 blog "core technique 1: Top-k Sparse Attention".
+ *
+ *   doc_scores  fp32 [B, n_docs]
+ *   top_idx     int32 [B, k] out: score descending, equal scores -> lower id first
+ *   top_scores  fp32 [B, k] out
+ *   1 <= k <= min(n_docs, 1024); n_docs < 2^31.
+ *   workspace   >= msa_topk_workspace_bytes(B, n_docs, k) bytes
+ */
+size_t msa_topk_workspace_bytes(int B, int64_t n_docs, int k);
+int msa_topk_docs(const float* doc_scores, int B, int64_t n_docs, int k,
+                  int32_t* top_idx, float* top_scores,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * msa_fetch_docs -- context assembly from the host tier (host-driven copies).
+ *
+ * Defined by: medium write-up sec. 4B and b-lab.team sec. 2 (routing keys stay
+ * in GPU memory, content K/V live in host DRAM and only the selected items are
+ * fetched asynchronously); b-lab.team pipeline stage 2 (load only the
+ * selected Kbar/Vbar).
+ *
+ * For each query b, the selected documents' chunks are copied in rank order,
+ * chunks in order, with one hipMemcpyAsync per run of adjacent chunks, on
+ * `side`; `done` (if not NULL) is recorded on `side` after the last copy.
+ *
+ *   top_idx_host        int32 [B, k] (host)
+ *   host_store          bf16 [n_chunks, 2, H, D] pinned host memory: entry g = (Kbar[g], Vbar[g])
+ *   doc_chunk_off_host  int64 [n_docs+1] (host)
+ *   staging             bf16 [B, Mmax, 2, H, D] (device) out
+ *   mem_len_host        int32 [B] (host) out: entries written for each query
+ * Fails with MSA_ERR_INVALID_ARG (nothing copied) if a selected id is out of
+ * range or a query's chunks exceed Mmax.
+ */
+int msa_fetch_docs(const int32_t* top_idx_host, int B, int k,
+                   const uint16_t* host_store, const int64_t* doc_chunk_off_host, int64_t n_docs,
+                   int H, int D, uint16_t* staging, int Mmax, int32_t* mem_len_host,
+                   hipStream_t side, hipEvent_t done);
+
+/*
+ * msa_gather_docs -- the same assembly as msa_fetch_docs, done by one kernel on
+ * `stream` that reads the (mapped, pinned) host store directly, so the selected
+ * ids never travel to the host.  Chunks beyond Mmax are dropped and mem_len is
+ * capped at Mmax (check mem_len against the expected total if that matters).
+ *
+ *   top_idx        int32 [B, k] (device)
+ *   host_store     pinned host memory [n_chunks, 2, H, D], device-accessible
+ *   doc_chunk_off  int64 [n_docs+1] (device)
+ *   staging        bf16 [B, Mmax, 2, H, D] (device) out
+ *   mem_len        int32 [B] (device) out
+ */
+int msa_gather_docs(const int32_t* top_idx, int B, int k,
+                    const uint16_t* host_store, const int64_t* doc_chunk_off, int64_t n_docs,
+                    int H, int D, uint16_t* staging, int Mmax, int32_t* mem_len,
+                    hipStream_t stream);
+
+/*
+ * msa_sparse_attn_decode -- GQA attention over [pooled memory ++ causal local KV].
+ *
+ * Defined by: medium write-up sec. 2 and b-lab.team sec. 1 (the selected
+ * documents' compressed K/V are concatenated with the query's local K/V for
+ * autoregressive decoding); b-lab.team sec. 1, Global RoPE (the query's start
+ * index is offset by k, the number of retrieved blocks).
+ *
+ * Query row i sits at position rope_offset + (Tl - Tq) + i, local key j at
+ * rope_offset + j (both rotated here); memory keys are used as given (already
+ * rotated at document-local positions by msa_pool_chunks).  Every memory entry
+ * is visible to every row; local key j is visible to row i iff
+ * j <= (Tl - Tq) + i.  q-head h reads kv-head h / (Hq / Hkv).
+ *   O[b,i,h,:] = softmax_j(scale * <q_i, k_j>) . v_j
+ *
+ *   Q           bf16 [B, Tq, Hq, D] (unrotated)
+ *   Kloc, Vloc  bf16 [B, Tl, Hkv, D] (Kloc unrotated)
+ *   Kmem, Vmem  bf16, entry m of query b at ptr + (b*Mmax + m) * mem_entry_stride,
+ *               each entry [Hkv, D]; the staging layout of msa_fetch_docs gives
+ *               Kmem = staging, Vmem = staging + Hkv*D, mem_entry_stride = 2*Hkv*D
+ *   mem_len     int32 [B] (device): entries used per query (clamped to [0, Mmax])
+ *   O           fp32 [B, Tq, Hq, D] out
+ *   D == 128, 1 <= Tq <= Tl, Hq % Hkv == 0, Hkv <= 16, rope_offset >= 0.
+ */
+int msa_sparse_attn_decode(const uint16_t* Q, int B, int Tq, int Hq, int D,
+                           const uint16_t* Kloc, const uint16_t* Vloc, int Tl, int Hkv,
+                           const uint16_t* Kmem, const uint16_t* Vmem,
+                           int64_t mem_entry_stride, int Mmax, const int32_t* mem_len,
+                           int rope_offset, double rope_base, float scale,
+                           float* O, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_H_ */

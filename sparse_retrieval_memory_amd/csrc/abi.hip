@@ -1,0 +1,189 @@
+// C ABI entry points of libmsa: host-side argument validation, then the
+// launchers in the kernel sources.  Nothing is launched when validation fails.
+#include "msa_internal.h"
+
+#include <string.h>
+
+namespace msa {
+
+static thread_local char g_err[512] = "";
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+
+void clear_error() { g_err[0] = '\0'; }
+
+}  // namespace msa
+
+using msa::aligned16;
+
+extern "C" {
+
+int msa_version(void) { return MSA_VERSION; }
+
+const char* msa_status_string(int status) {
+  switch (status) {
+    case MSA_OK: return "ok";
+    case MSA_ERR_INVALID_ARG: return "invalid argument";
+    case MSA_ERR_UNSUPPORTED: return "unsupported shape";
+    case MSA_ERR_WORKSPACE: return "workspace too small";
+    case MSA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* msa_last_error(void) { return msa::g_err; }
+
+int msa_pool_chunks(const uint16_t* K, const uint16_t* V, const uint16_t* Kr, const int64_t* doc_tok_off,
+                    const int64_t* doc_chunk_off, int64_t n_docs, int64_t n_tok, int64_t n_chunks, int H,
+                    int D, int chunk_len, double rope_base, uint16_t* Kbar, uint16_t* Vbar,
+                    uint16_t* Krbar, hipStream_t stream) {
+  msa::clear_error();
+  MSA_CHECK_ARG(n_docs >= 1 && n_tok >= 0 && n_chunks >= 0, "n_docs >= 1, n_tok >= 0, n_chunks >= 0 required");
+  MSA_CHECK_ARG(doc_tok_off && doc_chunk_off, "null offset array");
+  MSA_CHECK_ARG(n_chunks == 0 || (K && V && Kr && Kbar && Vbar && Krbar), "null tensor pointer");
+  MSA_CHECK_ARG(chunk_len >= 1 && chunk_len <= 1024, "chunk_len must be in [1, 1024]");
+  MSA_CHECK_ARG(rope_base > 1.0, "rope_base must be > 1");
+  MSA_CHECK_SUPPORTED(D == 128, "D=%d unsupported (D must be 128)", D);
+  MSA_CHECK_SUPPORTED(H == 1 || H == 2 || H == 4 || H == 8 || H == 16, "H=%d unsupported", H);
+  MSA_CHECK_ARG(n_chunks <= 0x7FFFFFFF, "n_chunks must fit a grid dimension");
+  MSA_CHECK_ARG(n_chunks == 0 || (aligned16(K) && aligned16(V) && aligned16(Kr) && aligned16(Kbar) &&
+                                  aligned16(Vbar) && aligned16(Krbar)),
+                "tensor pointers must be 16-byte aligned");
+  return msa::launch_pool(K, V, Kr, doc_tok_off, doc_chunk_off, n_docs, n_tok, n_chunks, H, chunk_len,
+                          rope_base, Kbar, Vbar, Krbar, stream);
+}
+
+size_t msa_route_workspace_bytes(int B, int T, int H, int D, int64_t n_chunks, int64_t n_docs) {
+  (void)D;
+  if (B < 1 || T < 1 || n_chunks < 0 || n_docs < 1) return 0;
+  return msa::route_workspace(B, T, H, n_chunks, n_docs);
+}
+
+int msa_route_scores(const uint16_t* Qr, int B, int T, int H, int D, const uint16_t* Krbar, int64_t n_chunks,
+                     const int64_t* doc_chunk_off, int64_t n_docs, const uint8_t* doc_exclude,
+                     float* doc_scores, float* chunk_scores, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream) {
+  msa::clear_error();
+  MSA_CHECK_ARG(B >= 1 && T >= 1, "B >= 1 and T >= 1 required (B=%d, T=%d)", B, T);
+  MSA_CHECK_ARG(n_docs >= 1 && n_chunks >= 0, "n_docs >= 1 and n_chunks >= 0 required");
+  MSA_CHECK_ARG(Qr && doc_chunk_off && doc_scores && (Krbar || n_chunks == 0), "null pointer");
+  MSA_CHECK_SUPPORTED(D == 128, "D=%d unsupported (D must be 128)", D);
+  MSA_CHECK_SUPPORTED(H == 1 || H == 2 || H == 4 || H == 8, "H=%d unsupported (1, 2, 4 or 8)", H);
+  MSA_CHECK_ARG((int64_t)B * T <= (1 << 24), "B*T too large");
+  MSA_CHECK_ARG(n_docs < 0x7FFFFFFF / 256 * 256 && n_chunks < ((int64_t)1 << 40), "size out of range");
+  MSA_CHECK_ARG(aligned16(Qr) && (n_chunks == 0 || aligned16(Krbar)), "Qr and Krbar must be 16-byte aligned");
+  const size_t need = msa::route_workspace(B, T, H, n_chunks, n_docs);
+  if (workspace_bytes < need || (need > 0 && workspace == nullptr)) {
+    msa::set_error("workspace %zu bytes < required %zu", workspace_bytes, need);
+    return MSA_ERR_WORKSPACE;
+  }
+  MSA_CHECK_ARG(workspace == nullptr || aligned16(workspace), "workspace must be 16-byte aligned");
+  return msa::launch_route(Qr, B, T, H, Krbar, n_chunks, doc_chunk_off, n_docs, doc_exclude, doc_scores,
+                           chunk_scores, workspace, stream);
+}
+
+size_t msa_topk_workspace_bytes(int B, int64_t n_docs, int k) {
+  if (B < 1 || n_docs < 1 || k < 1) return 0;
+  return msa::topk_workspace(B, n_docs, k);
+}
+
+int msa_topk_docs(const float* doc_scores, int B, int64_t n_docs, int k, int32_t* top_idx, float* top_scores,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  msa::clear_error();
+  MSA_CHECK_ARG(B >= 1 && n_docs >= 1, "B >= 1 and n_docs >= 1 required");
+  MSA_CHECK_ARG(k >= 1 && k <= n_docs, "k=%d must satisfy 1 <= k <= n_docs (%lld)", k, (long long)n_docs);
+  MSA_CHECK_ARG(n_docs < 0x7FFFFFFF, "n_docs must be < 2^31");
+  MSA_CHECK_ARG(B <= 65535, "B must be <= 65535");
+  MSA_CHECK_ARG(doc_scores && top_idx && top_scores, "null pointer");
+  MSA_CHECK_SUPPORTED(k <= 1024, "k=%d unsupported (k <= 1024)", k);
+  const size_t need = msa::topk_workspace(B, n_docs, k);
+  if (workspace_bytes < need || workspace == nullptr) {
+    msa::set_error("workspace %zu bytes < required %zu", workspace_bytes, need);
+    return MSA_ERR_WORKSPACE;
+  }
+  MSA_CHECK_ARG(aligned16(workspace), "workspace must be 16-byte aligned");
+  return msa::launch_topk(doc_scores, B, n_docs, k, top_idx, top_scores, workspace, stream);
+}
+
+int msa_fetch_docs(const int32_t* top_idx_host, int B, int k, const uint16_t* host_store,
+                   const int64_t* doc_chunk_off_host, int64_t n_docs, int H, int D, uint16_t* staging, int Mmax,
+                   int32_t* mem_len_host, hipStream_t side, hipEvent_t done) {
+  msa::clear_error();
+  MSA_CHECK_ARG(B >= 1 && k >= 1 && n_docs >= 1 && Mmax >= 1 && H >= 1, "B, k, n_docs, Mmax, H must be >= 1");
+  MSA_CHECK_ARG(top_idx_host && host_store && doc_chunk_off_host && staging && mem_len_host, "null pointer");
+  MSA_CHECK_SUPPORTED(D == 128, "D=%d unsupported (D must be 128)", D);
+  const int64_t entry = 2LL * H * D;              // elements per staged entry
+  // validate everything before the first copy
+  for (int b = 0; b < B; ++b) {
+    int64_t m = 0;
+    for (int r = 0; r < k; ++r) {
+      const int32_t d = top_idx_host[(int64_t)b * k + r];
+      MSA_CHECK_ARG(d >= 0 && d < n_docs, "top_idx[%d,%d]=%d out of range", b, r, d);
+      const int64_t n = doc_chunk_off_host[d + 1] - doc_chunk_off_host[d];
+      MSA_CHECK_ARG(n >= 1, "document %d has no chunks", d);
+      m += n;
+    }
+    MSA_CHECK_ARG(m <= Mmax, "query %d needs %lld entries > Mmax=%d", b, (long long)m, Mmax);
+    mem_len_host[b] = (int32_t)m;
+  }
+  for (int b = 0; b < B; ++b) {
+    int64_t m = 0;
+    int r = 0;
+    while (r < k) {
+      // merge runs of documents whose chunks are adjacent in the store
+      const int32_t d = top_idx_host[(int64_t)b * k + r];
+      const int64_t g0 = doc_chunk_off_host[d];
+      int64_t g1 = doc_chunk_off_host[d + 1];
+      int r2 = r + 1;
+      while (r2 < k && doc_chunk_off_host[top_idx_host[(int64_t)b * k + r2]] == g1) {
+        g1 = doc_chunk_off_host[top_idx_host[(int64_t)b * k + r2] + 1];
+        ++r2;
+      }
+      const size_t bytes = (size_t)((g1 - g0) * entry) * sizeof(uint16_t);
+      MSA_CHECK_HIP(hipMemcpyAsync(staging + ((int64_t)b * Mmax + m) * entry, host_store + g0 * entry, bytes,
+                                   hipMemcpyHostToDevice, side));
+      m += g1 - g0;
+      r = r2;
+    }
+  }
+  if (done) MSA_CHECK_HIP(hipEventRecord(done, side));
+  return MSA_OK;
+}
+
+int msa_gather_docs(const int32_t* top_idx, int B, int k, const uint16_t* host_store, const int64_t* doc_chunk_off,
+                    int64_t n_docs, int H, int D, uint16_t* staging, int Mmax, int32_t* mem_len,
+                    hipStream_t stream) {
+  msa::clear_error();
+  MSA_CHECK_ARG(B >= 1 && B <= 65535 && k >= 1 && n_docs >= 1 && Mmax >= 1 && H >= 1, "bad sizes");
+  MSA_CHECK_ARG(top_idx && host_store && doc_chunk_off && staging && mem_len, "null pointer");
+  MSA_CHECK_SUPPORTED(D == 128, "D=%d unsupported (D must be 128)", D);
+  MSA_CHECK_ARG(aligned16(host_store) && aligned16(staging), "host_store and staging must be 16-byte aligned");
+  return msa::launch_gather(top_idx, B, k, host_store, doc_chunk_off, n_docs, H, staging, Mmax, mem_len, stream);
+}
+
+int msa_sparse_attn_decode(const uint16_t* Q, int B, int Tq, int Hq, int D, const uint16_t* Kloc,
+                           const uint16_t* Vloc, int Tl, int Hkv, const uint16_t* Kmem, const uint16_t* Vmem,
+                           int64_t mem_entry_stride, int Mmax, const int32_t* mem_len, int rope_offset,
+                           double rope_base, float scale, float* O, hipStream_t stream) {
+  msa::clear_error();
+  MSA_CHECK_ARG(B >= 1 && B <= 65535 && Tq >= 1 && Tl >= Tq, "need B >= 1, 1 <= Tq <= Tl");
+  MSA_CHECK_ARG(Hkv >= 1 && Hq >= Hkv && Hq % Hkv == 0 && Hq <= 65535, "need Hq %% Hkv == 0");
+  MSA_CHECK_SUPPORTED(D == 128, "D=%d unsupported (D must be 128)", D);
+  MSA_CHECK_SUPPORTED(Hkv <= 16, "Hkv=%d unsupported (<= 16)", Hkv);
+  MSA_CHECK_ARG(Mmax >= 0 && rope_offset >= 0 && rope_base > 1.0, "need Mmax >= 0, rope_offset >= 0, base > 1");
+  MSA_CHECK_ARG(Q && Kloc && Vloc && O && mem_len, "null pointer");
+  MSA_CHECK_ARG(Mmax == 0 || (Kmem && Vmem && mem_entry_stride >= (int64_t)Hkv * D && mem_entry_stride % 8 == 0),
+                "memory pointers/stride invalid");
+  MSA_CHECK_ARG(aligned16(Q) && aligned16(Kloc) && aligned16(Vloc) && aligned16(O) &&
+                    (Mmax == 0 || (aligned16(Kmem) && aligned16(Vmem))),
+                "pointers must be 16-byte aligned");
+  return msa::launch_attn(Q, B, Tq, Hq, Kloc, Vloc, Tl, Hkv, Kmem, Vmem, mem_entry_stride, Mmax, mem_len,
+                          rope_offset, rope_base, scale, O, stream);
+}
+
+}  // extern "C"

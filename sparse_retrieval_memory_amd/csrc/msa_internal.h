@@ -1,0 +1,131 @@
+// Internal helpers shared by the HIP sources of libmsa (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/msa.h"
+
+namespace msa {
+
+// ------------------------------------------------------------ error reporting
+void set_error(const char* fmt, ...);
+void clear_error();
+
+#define MSA_CHECK_ARG(cond, ...)                 \
+  do {                                           \
+    if (!(cond)) {                               \
+      ::msa::set_error(__VA_ARGS__);             \
+      return MSA_ERR_INVALID_ARG;                \
+    }                                            \
+  } while (0)
+
+#define MSA_CHECK_SUPPORTED(cond, ...)           \
+  do {                                           \
+    if (!(cond)) {                               \
+      ::msa::set_error(__VA_ARGS__);             \
+      return MSA_ERR_UNSUPPORTED;                \
+    }                                            \
+  } while (0)
+
+#define MSA_CHECK_HIP(expr)                                                   \
+  do {                                                                        \
+    hipError_t e_ = (expr);                                                   \
+    if (e_ != hipSuccess) {                                                   \
+      ::msa::set_error("%s failed: %s", #expr, hipGetErrorString(e_));        \
+      return MSA_ERR_HIP;                                                     \
+    }                                                                         \
+  } while (0)
+
+#define MSA_CHECK_LAUNCH()                                                    \
+  do {                                                                        \
+    hipError_t e_ = hipGetLastError();                                        \
+    if (e_ != hipSuccess) {                                                   \
+      ::msa::set_error("kernel launch failed: %s", hipGetErrorString(e_));    \
+      return MSA_ERR_HIP;                                                     \
+    }                                                                         \
+  } while (0)
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// ------------------------------------------------------------ device helpers
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (finite values)
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Order-preserving map float -> uint32 (a < b  <=>  enc(a) < enc(b) for non-NaN).
+__device__ __forceinline__ uint32_t enc_f32(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float dec_f32(uint32_t e) {
+  uint32_t u = (e & 0x80000000u) ? (e & 0x7FFFFFFFu) : ~e;
+  return __uint_as_float(u);
+}
+
+// sum of a*b over two packed bf16 pairs, fp32 accumulate
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// LDS-only barrier: wait for this wave's LDS traffic, then s_barrier.  Unlike
+// __syncthreads() it does not wait for outstanding global loads, so LDS-DMA
+// prefetches stay in flight across it.  The waits use the builtin (gfx9
+// encoding) so the compiler's own wait-count tracking sees them.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), vmcnt/expcnt untouched
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+// Wait until every vector-memory operation issued by this wave has completed.
+__device__ __forceinline__ void wait_vmem_all() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  asm volatile("" ::: "memory");
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Asynchronous 16-byte-per-lane global -> LDS copy.  The LDS destination of
+// lane i is lds_base + 16 * i (lds_base must be wave-uniform).
+__device__ __forceinline__ void dma16(const void* gptr, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(gptr, (lds_void_t*)lds_base, 16, 0, 0);
+}
+
+}  // namespace msa
+
+// kernel-family launchers (defined in the .hip files)
+namespace msa {
+int launch_pool(const uint16_t* K, const uint16_t* V, const uint16_t* Kr, const int64_t* doc_tok_off,
+                const int64_t* doc_chunk_off, int64_t n_docs, int64_t n_tok, int64_t n_chunks, int H,
+                int chunk_len, double rope_base, uint16_t* Kbar, uint16_t* Vbar, uint16_t* Krbar,
+                hipStream_t stream);
+int launch_route(const uint16_t* Qr, int B, int T, int H, const uint16_t* Krbar, int64_t n_chunks,
+                 const int64_t* doc_chunk_off, int64_t n_docs, const uint8_t* doc_exclude,
+                 float* doc_scores, float* chunk_scores, void* workspace, hipStream_t stream);
+size_t route_workspace(int B, int T, int H, int64_t n_chunks, int64_t n_docs);
+int launch_topk(const float* doc_scores, int B, int64_t n_docs, int k, int32_t* top_idx,
+                float* top_scores, void* workspace, hipStream_t stream);
+size_t topk_workspace(int B, int64_t n_docs, int k);
+int launch_attn(const uint16_t* Q, int B, int Tq, int Hq, const uint16_t* Kloc, const uint16_t* Vloc,
+                int Tl, int Hkv, const uint16_t* Kmem, const uint16_t* Vmem, int64_t mem_entry_stride,
+                int Mmax, const int32_t* mem_len, int rope_offset, double rope_base, float scale,
+                float* O, hipStream_t stream);
+int launch_gather(const int32_t* top_idx, int B, int k, const uint16_t* host_store,
+                  const int64_t* doc_chunk_off, int64_t n_docs, int H, uint16_t* staging, int Mmax,
+                  int32_t* mem_len, hipStream_t stream);
+}  // namespace msa

@@ -1,0 +1,453 @@
+// Routing scan: chunk relevance of every pooled router key, then document max.
+//
+// What is computed (b-lab.team summary of MSA, sec. 1, Scalable Sparse
+// Attention; medium write-up, sec. 2): for every pooled chunk g,
+//   chunk[b,g] = max_t (1/H) sum_h cos(Qr[b,t,h], Krbar[g,h])
+// and a document's score is the max over its chunks.  The scan reads the whole
+// HBM-resident Krbar store once per call (the only O(L) online step), so the
+// kernels are built around streaming it at HBM rate:
+//
+//  * MFMA path (rows = B*T > 15): each workgroup keeps 128 router rows
+//    resident in registers (4 waves x 32 rows x all heads, bf16 MFMA A
+//    operands) and streams 64 KB tiles of 32 chunks through LDS with
+//    asynchronous global->LDS DMA (double buffered, XOR-swizzled so the MFMA
+//    B-operand reads are bank-conflict free).  Per head: 8 x
+//    v_mfma_f32_32x32x16_bf16 on the raw bf16 operands (exact products, fp32
+//    accumulation), then an fp32 epilogue multiplies by 1/|q| and 1/|k| and
+//    adds into the head sum; the token max is a register max plus one
+//    cross-lane step, combined across waves/workgroups with an integer
+//    atomicMax on an order-preserving encoding (deterministic).
+//  * VALU path (rows <= 15): one thread per (chunk, head) holds that 256-byte
+//    slice in registers, dots it with every router row (LDS broadcast reads,
+//    v_dot2_f32_bf16), and a DPP butterfly sums the heads.
+//
+// Normalisation is applied in fp32 after the exact bf16 dot products instead
+// of rounding normalised vectors to bf16, which would move scores by ~1e-3.
+#include "msa_internal.h"
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+namespace msa {
+namespace {
+
+constexpr int D = 128;
+constexpr int TC = 32;   // chunks per MFMA tile (MFMA N)
+constexpr int NW = 4;    // waves per MFMA workgroup
+constexpr int RW = 32;   // router rows per wave (MFMA M)
+constexpr int VALU_MAX_ROWS = 15;
+
+__global__ void fill_u32_kernel(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
+  int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = v;
+}
+
+__device__ __forceinline__ float sq_norm_piece(uint4 v, float acc) {
+  acc = dot2_bf16(v.x, v.x, acc);
+  acc = dot2_bf16(v.y, v.y, acc);
+  acc = dot2_bf16(v.z, v.z, acc);
+  acc = dot2_bf16(v.w, v.w, acc);
+  return acc;
+}
+
+__device__ __forceinline__ float inv_norm(float ss) { return ss > 0.f ? 1.0f / sqrtf(ss) : 0.f; }
+
+// ------------------------------------------------------------------ MFMA path
+template <int H>
+struct Tile {
+  static constexpr int ROW_BYTES = H * D * 2;       // one pooled chunk, all heads
+  static constexpr int PIECES = ROW_BYTES / 16;     // 16-byte pieces per chunk row
+  static constexpr int BYTES = TC * ROW_BYTES;      // 8 KB * H
+  static constexpr int DMA_ITERS = BYTES / (16 * 256);
+};
+
+// Issue the asynchronous copy of chunk tile `tile` into `lds`.  LDS slot j holds
+// logical piece (j % PIECES) ^ (n & 15) of chunk n = j / PIECES; the XOR stays
+// inside a 256-byte group, so each wave instruction still reads 1 KB of
+// contiguous global memory.  Chunks past the end are clamped to the last chunk
+// (their results are never written).
+template <int H>
+__device__ __forceinline__ void issue_tile(const uint8_t* __restrict__ kr, int64_t n_chunks,
+                                           int64_t tile, uint8_t* lds, int wave, int lane) {
+  using TL = Tile<H>;
+#pragma unroll
+  for (int i = 0; i < TL::DMA_ITERS; ++i) {
+    const int slot0 = (i * NW + wave) * 64;
+    const int slot = slot0 + lane;
+    const int n = slot / TL::PIECES;
+    const int lp = (slot % TL::PIECES) ^ (n & 15);
+    int64_t g = tile * TC + n;
+    if (g >= n_chunks) g = n_chunks - 1;
+    dma16(kr + g * TL::ROW_BYTES + lp * 16, lds + slot0 * 16);
+  }
+}
+
+// One tile of the MFMA scan: wait for `cur` (filled by the previous step),
+// start filling `nxt` with the following tile, then score `cur`.  `cur` and
+// `nxt` are distinct LDS arrays so the compiler can see that reading one does
+// not depend on the DMA into the other.
+template <int H>
+__device__ __forceinline__ void mfma_tile_step(const uint8_t* __restrict__ kr, int64_t n_chunks, int64_t tile,
+                                               bool has_next, const uint8_t* cur, uint8_t* nxt,
+                                               float (*lds_rk)[TC], float (*lds_rq)[RW], const bf16x8_t (&qf)[H][8],
+                                               bool wave_active, int b, int t0, int T, uint32_t* chunk_enc,
+                                               int tid, int wave, int lane) {
+  using TL = Tile<H>;
+  const int half = lane >> 5;
+  const int nb = lane & 31;                   // this lane's chunk column in the tile
+  wait_vmem_all();
+  lds_barrier();                              // tile visible; previous tile fully consumed
+  if (has_next) issue_tile<H>(kr, n_chunks, tile + 1, nxt, wave, lane);
+
+  if (tid < TC * H) {                         // 1/|k| for (chunk n, head h)
+    const int n = tid % TC, h = tid / TC;
+    const uint8_t* row = cur + n * TL::ROW_BYTES;
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int pp = (16 * h + i) ^ (n & 15);
+      ss = sq_norm_piece(*reinterpret_cast<const uint4*>(row + pp * 16), ss);
+    }
+    lds_rk[h][n] = inv_norm(ss);
+  }
+  lds_barrier();
+
+  if (wave_active) {
+    f32x16_t sacc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+    const uint8_t* brow = cur + nb * TL::ROW_BYTES;
+#pragma unroll
+    for (int h = 0; h < H; ++h) {
+      bf16x8_t bv[8];
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const int pp = (16 * h + 2 * ks + half) ^ (nb & 15);
+        bv[ks] = *reinterpret_cast<const bf16x8_t*>(brow + pp * 16);
+      }
+      f32x16_t acc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[h][ks], bv[ks], acc, 0, 0, 0);
+      const float rk = lds_rk[h][nb];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 rq = *reinterpret_cast<const float4*>(&lds_rq[h][8 * q4 + 4 * half]);
+        sacc[4 * q4 + 0] = fmaf(acc[4 * q4 + 0], rk * rq.x, sacc[4 * q4 + 0]);
+        sacc[4 * q4 + 1] = fmaf(acc[4 * q4 + 1], rk * rq.y, sacc[4 * q4 + 1]);
+        sacc[4 * q4 + 2] = fmaf(acc[4 * q4 + 2], rk * rq.z, sacc[4 * q4 + 2]);
+        sacc[4 * q4 + 3] = fmaf(acc[4 * q4 + 3], rk * rq.w, sacc[4 * q4 + 3]);
+      }
+    }
+    // token max: accumulator i of this lane holds row 8*(i/4) + 4*half + i%4
+    float v = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = 8 * (i >> 2) + 4 * half + (i & 3);
+      if (t0 + row < T) v = fmaxf(v, sacc[i]);
+    }
+    v = fmaxf(v, __shfl_xor(v, 32));
+    const int64_t g = tile * TC + nb;
+    if (half == 0 && g < n_chunks)
+      atomicMax(&chunk_enc[(int64_t)b * n_chunks + g], enc_f32(v * (1.0f / H)));
+  }
+}
+
+template <int H>
+__global__ void __launch_bounds__(256, 1)
+route_mfma_kernel(const uint16_t* __restrict__ Qr, int B, int T, int RTq, int P, int S,
+                  const uint16_t* __restrict__ Krbar, int64_t n_chunks, int64_t tiles_per_slice,
+                  uint32_t* __restrict__ chunk_enc) {
+  using TL = Tile<H>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a[TL::BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_b[TL::BYTES];
+  __shared__ __attribute__((aligned(16))) float lds_rk[H][TC];
+  __shared__ __attribute__((aligned(16))) float lds_rq[NW][H][RW];
+
+  // XCD-aware block mapping: workgroups are dealt round-robin to the 8 XCDs;
+  // keep the P row blocks of one chunk slice on the same XCD so they share
+  // that XCD's L2 copy of the slice.
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7;
+  const int j = bid >> 3;
+  const int p = j % P;
+  const int s = (j / P) * 8 + xcd;
+  if (s >= S) return;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int half = lane >> 5, m = lane & 31;
+  const int rt = p * NW + wave;               // global row tile of this wave
+  const bool wave_active = rt < B * RTq;
+  const int b = wave_active ? rt / RTq : 0;
+  const int t0 = (rt % RTq) * RW;
+
+  // --- resident router rows: A operands for all heads and k-steps
+  bf16x8_t qf[H][8];
+  {
+    const int t = t0 + m;
+    const bool valid = wave_active && t < T;
+    const uint16_t* qrow = Qr + ((int64_t)b * T + t) * H * D;
+#pragma unroll
+    for (int h = 0; h < H; ++h) {
+      float ss = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (valid) v = *reinterpret_cast<const uint4*>(qrow + h * D + 16 * ks + 8 * half);
+        qf[h][ks] = __builtin_bit_cast(bf16x8_t, v);
+        ss = sq_norm_piece(v, ss);
+      }
+      ss += __shfl_xor(ss, 32);
+      if (half == 0) lds_rq[wave][h][m] = inv_norm(ss);
+    }
+  }
+
+  const int64_t n_tiles = (n_chunks + TC - 1) / TC;
+  const int64_t tile_begin = (int64_t)s * tiles_per_slice;
+  int64_t tile_end = tile_begin + tiles_per_slice;
+  if (tile_end > n_tiles) tile_end = n_tiles;
+  if (tile_begin >= tile_end) return;
+
+  const uint8_t* kr = reinterpret_cast<const uint8_t*>(Krbar);
+  issue_tile<H>(kr, n_chunks, tile_begin, lds_a, wave, lane);
+  for (int64_t tile = tile_begin; tile < tile_end; tile += 2) {
+    mfma_tile_step<H>(kr, n_chunks, tile, tile + 1 < tile_end, lds_a, lds_b, lds_rk, lds_rq[wave], qf,
+                      wave_active, b, t0, T, chunk_enc, tid, wave, lane);
+    if (tile + 1 < tile_end)
+      mfma_tile_step<H>(kr, n_chunks, tile + 1, tile + 2 < tile_end, lds_b, lds_a, lds_rk, lds_rq[wave], qf,
+                        wave_active, b, t0, T, chunk_enc, tid, wave, lane);
+  }
+}
+
+// ------------------------------------------------------------------ VALU path
+template <int H>
+__device__ __forceinline__ float head_sum(float x) {
+  if (H >= 2) x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+  if (H >= 4) x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
+  if (H >= 8) x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false));
+  return x;
+}
+
+// one 64 KB tile = (256 / H) chunks; thread tid owns (chunk tid / H, head tid % H)
+template <int H>
+__device__ __forceinline__ void issue_tile_valu(const uint8_t* __restrict__ kr, int64_t n_chunks,
+                                                int64_t tile, uint8_t* lds, int wave, int lane) {
+  constexpr int CPT = 256 / H;
+  constexpr int ROW = H * D * 2;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int slot0 = (i * NW + wave) * 64;
+    const int slot = slot0 + lane;
+    const int owner = slot >> 4;             // (chunk, head) pair = the thread that reads it
+    const int lp = (slot & 15) ^ (owner & 15);
+    const int n = owner / H, h = owner % H;
+    int64_t g = tile * CPT + n;
+    if (g >= n_chunks) g = n_chunks - 1;
+    dma16(kr + g * ROW + h * (D * 2) + lp * 16, lds + slot0 * 16);
+  }
+}
+
+template <int H>
+__device__ __forceinline__ void valu_tile_step(const uint8_t* __restrict__ kr, int64_t n_chunks, int64_t tile,
+                                               bool has_next, const uint8_t* cur, uint8_t* nxt,
+                                               const uint8_t* lds_q, const float (&rq)[VALU_MAX_ROWS], int B, int T,
+                                               uint32_t* chunk_enc, int tid, int wave, int lane) {
+  constexpr int CPT = 256 / H;
+  const int h = tid % H;
+  const int sw = tid & 15;
+  wait_vmem_all();
+  lds_barrier();
+  if (has_next) issue_tile_valu<H>(kr, n_chunks, tile + 1, nxt, wave, lane);
+
+  // this thread's (chunk, head) slice
+  uint4 kv[16];
+  const uint8_t* mine = cur + tid * 256;
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    kv[i] = *reinterpret_cast<const uint4*>(mine + ((i ^ sw) * 16));
+    ss = sq_norm_piece(kv[i], ss);
+  }
+  const float rk = inv_norm(ss);
+  const int64_t g = tile * CPT + tid / H;
+
+  const uint8_t* qh = lds_q + h * 256;
+  int r = 0;
+  for (int bq = 0; bq < B; ++bq) {
+    float best = -INFINITY;
+    for (int t = 0; t < T; ++t, ++r) {
+      const uint8_t* qrow = qh + r * H * 256;
+      float dot = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint4 qv = *reinterpret_cast<const uint4*>(qrow + ((i ^ h) & 15) * 16);
+        dot = dot2_bf16(qv.x, kv[i].x, dot);
+        dot = dot2_bf16(qv.y, kv[i].y, dot);
+        dot = dot2_bf16(qv.z, kv[i].z, dot);
+        dot = dot2_bf16(qv.w, kv[i].w, dot);
+      }
+      float rqr = rq[0];
+#pragma unroll
+      for (int rr = 1; rr < VALU_MAX_ROWS; ++rr) rqr = (r == rr) ? rq[rr] : rqr;
+      const float sc = head_sum<H>(dot * rk * rqr);
+      best = fmaxf(best, sc);
+    }
+    if (h == 0 && g < n_chunks) chunk_enc[(int64_t)bq * n_chunks + g] = enc_f32(best * (1.0f / H));
+  }
+}
+
+template <int H>
+__global__ void __launch_bounds__(256, 1)
+route_valu_kernel(const uint16_t* __restrict__ Qr, int B, int T,
+                  const uint16_t* __restrict__ Krbar, int64_t n_chunks, int64_t tiles_per_block,
+                  uint32_t* __restrict__ chunk_enc) {
+  constexpr int CPT = 256 / H;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a[65536];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_b[65536];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_q[VALU_MAX_ROWS * H * D * 2];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int h = tid % H;
+  const int R = B * T;
+
+  // stage the router rows: row r, head hh, piece i stored at piece i ^ hh
+  for (int x = tid; x < R * H * 16; x += 256) {
+    const int i = x & 15, hh = (x >> 4) % H, r = (x >> 4) / H;
+    const uint4 v = *reinterpret_cast<const uint4*>(Qr + ((int64_t)r * H + hh) * D + 8 * i);
+    *reinterpret_cast<uint4*>(lds_q + (((r * H + hh) * 16) + (i ^ (hh & 15))) * 16) = v;
+  }
+  // 1/|q| of every row for this thread's head
+  float rq[VALU_MAX_ROWS];
+#pragma unroll
+  for (int r = 0; r < VALU_MAX_ROWS; ++r) {
+    float ss = 0.f;
+    if (r < R) {
+      const uint16_t* q = Qr + ((int64_t)r * H + h) * D;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ss = sq_norm_piece(*reinterpret_cast<const uint4*>(q + 8 * i), ss);
+    }
+    rq[r] = inv_norm(ss);
+  }
+
+  const int64_t n_tiles = (n_chunks + CPT - 1) / CPT;
+  const int64_t tile_begin = (int64_t)blockIdx.x * tiles_per_block;
+  int64_t tile_end = tile_begin + tiles_per_block;
+  if (tile_end > n_tiles) tile_end = n_tiles;
+  if (tile_begin >= tile_end) return;
+
+  const uint8_t* kr = reinterpret_cast<const uint8_t*>(Krbar);
+  issue_tile_valu<H>(kr, n_chunks, tile_begin, lds_a, wave, lane);
+  for (int64_t tile = tile_begin; tile < tile_end; tile += 2) {
+    valu_tile_step<H>(kr, n_chunks, tile, tile + 1 < tile_end, lds_a, lds_b, lds_q, rq, B, T, chunk_enc, tid,
+                      wave, lane);
+    if (tile + 1 < tile_end)
+      valu_tile_step<H>(kr, n_chunks, tile + 1, tile + 2 < tile_end, lds_b, lds_a, lds_q, rq, B, T, chunk_enc,
+                        tid, wave, lane);
+  }
+}
+
+// ------------------------------------------------------------ document max
+__global__ void __launch_bounds__(256)
+doc_reduce_kernel(const uint32_t* __restrict__ chunk_enc, int64_t n_chunks,
+                  const int64_t* __restrict__ doc_chunk_off, int64_t n_docs,
+                  const uint8_t* __restrict__ doc_exclude, float* __restrict__ doc_scores,
+                  float* __restrict__ chunk_scores) {
+  const int b = blockIdx.y;
+  const int64_t d = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (d >= n_docs) return;
+  int64_t g0 = doc_chunk_off[d], g1 = doc_chunk_off[d + 1];
+  if (g0 < 0) g0 = 0;
+  if (g1 > n_chunks) g1 = n_chunks;
+  const uint32_t* ce = chunk_enc + (int64_t)b * n_chunks;
+  uint32_t best = 0;
+  for (int64_t g = g0; g < g1; ++g) {
+    const uint32_t e = ce[g];
+    best = e > best ? e : best;
+    if (chunk_scores) chunk_scores[(int64_t)b * n_chunks + g] = dec_f32(e);
+  }
+  float s = (g1 > g0) ? dec_f32(best) : -INFINITY;
+  if (doc_exclude && doc_exclude[(int64_t)b * n_docs + d]) s = -INFINITY;
+  doc_scores[(int64_t)b * n_docs + d] = s;
+}
+
+int num_cus() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      cus = v;
+    else
+      cus = 256;
+  }
+  return cus;
+}
+
+template <int H>
+int launch_route_h(const uint16_t* Qr, int B, int T, const uint16_t* Krbar, int64_t n_chunks,
+                   uint32_t* chunk_enc, hipStream_t stream) {
+  const int R = B * T;
+  const int cus = num_cus();
+  if (R <= VALU_MAX_ROWS) {
+    constexpr int CPT = 256 / H;
+    const int64_t n_tiles = (n_chunks + CPT - 1) / CPT;
+    int64_t blocks = n_tiles < cus ? n_tiles : cus;
+    if (blocks < 1) blocks = 1;
+    const int64_t per = (n_tiles + blocks - 1) / blocks;
+    blocks = (n_tiles + per - 1) / per;
+    hipLaunchKernelGGL(route_valu_kernel<H>, dim3((unsigned)blocks), dim3(256), 0, stream, Qr, B, T,
+                       Krbar, n_chunks, per, chunk_enc);
+    MSA_CHECK_LAUNCH();
+    return MSA_OK;
+  }
+  const int RTq = (T + RW - 1) / RW;
+  const int P = (B * RTq + NW - 1) / NW;
+  const int64_t n_tiles = (n_chunks + TC - 1) / TC;
+  int64_t S = (cus + P - 1) / P;
+  S = ((S + 7) / 8) * 8;
+  if (S > n_tiles) S = n_tiles;
+  if (S < 1) S = 1;
+  const int64_t per = (n_tiles + S - 1) / S;
+  S = (n_tiles + per - 1) / per;
+  const int64_t grid = ((S + 7) / 8) * 8 * (int64_t)P;
+  // fill with the encoding's minimum: below every float, so atomicMax takes the first value
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(256), dim3(256), 0, stream, chunk_enc, (int64_t)B * n_chunks, 0u);
+  MSA_CHECK_LAUNCH();
+  hipLaunchKernelGGL(route_mfma_kernel<H>, dim3((unsigned)grid), dim3(256), 0, stream, Qr, B, T, RTq, P,
+                     (int)S, Krbar, n_chunks, per, chunk_enc);
+  MSA_CHECK_LAUNCH();
+  return MSA_OK;
+}
+
+}  // namespace
+
+size_t route_workspace(int B, int T, int H, int64_t n_chunks, int64_t n_docs) {
+  (void)T; (void)H; (void)n_docs;
+  return ((size_t)B * (size_t)n_chunks * sizeof(uint32_t) + 255) & ~(size_t)255;
+}
+
+int launch_route(const uint16_t* Qr, int B, int T, int H, const uint16_t* Krbar, int64_t n_chunks,
+                 const int64_t* doc_chunk_off, int64_t n_docs, const uint8_t* doc_exclude,
+                 float* doc_scores, float* chunk_scores, void* workspace, hipStream_t stream) {
+  uint32_t* chunk_enc = reinterpret_cast<uint32_t*>(workspace);
+  int rc = MSA_OK;
+  if (n_chunks > 0) {
+    switch (H) {
+      case 1: rc = launch_route_h<1>(Qr, B, T, Krbar, n_chunks, chunk_enc, stream); break;
+      case 2: rc = launch_route_h<2>(Qr, B, T, Krbar, n_chunks, chunk_enc, stream); break;
+      case 4: rc = launch_route_h<4>(Qr, B, T, Krbar, n_chunks, chunk_enc, stream); break;
+      case 8: rc = launch_route_h<8>(Qr, B, T, Krbar, n_chunks, chunk_enc, stream); break;
+      default: set_error("H=%d unsupported", H); return MSA_ERR_UNSUPPORTED;
+    }
+    if (rc != MSA_OK) return rc;
+  }
+  dim3 grid((unsigned)((n_docs + 255) / 256), (unsigned)B);
+  hipLaunchKernelGGL(doc_reduce_kernel, grid, dim3(256), 0, stream, chunk_enc, n_chunks, doc_chunk_off,
+                     n_docs, doc_exclude, doc_scores, chunk_scores);
+  MSA_CHECK_LAUNCH();
+  return MSA_OK;
+}
+
+}  // namespace msa

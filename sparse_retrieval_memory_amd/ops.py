@@ -1,0 +1,166 @@
+"""Torch-tensor wrappers with the C ABI's names (argument marshalling only).
+
+Every step runs in libmsa's HIP kernels; PyTorch only provides device memory,
+pinned host memory and streams.  bf16 tensors may be ``torch.bfloat16`` or
+``int16``/``uint16`` views of the bits.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+
+_ws_cache = {}
+
+
+def _p(t: Optional[torch.Tensor]):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _bf16(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.element_size() != 2 or t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"{name} must be a bf16 tensor (or its 16-bit bits), got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _dev(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+
+
+def workspace(nbytes: int, device, tag: str = "route") -> torch.Tensor:
+    """A cached device scratch buffer of at least nbytes (one per device and tag).
+
+    Calls on one stream reuse it in order; callers that run on several streams
+    at once pass their own buffers instead."""
+    key = (torch.device(device), tag)
+    buf = _ws_cache.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=key[0])
+        _ws_cache[key] = buf
+    return buf
+
+
+def pool_chunks(K, V, Kr, doc_tok_off, doc_chunk_off, n_chunks: int, chunk_len: int = 64,
+                rope_base: float = 1.0e6, out: Optional[Tuple] = None, stream=None):
+    """msa_pool_chunks: returns (Kbar, Vbar, Krbar) bf16 [n_chunks, H, D]."""
+    for t, n in ((K, "K"), (V, "V"), (Kr, "Kr")):
+        _bf16(t, n); _dev(t, n)
+    n_tok, H, D = K.shape
+    n_docs = doc_tok_off.numel() - 1
+    if out is None:
+        out = tuple(torch.empty((n_chunks, H, D), dtype=K.dtype, device=K.device) for _ in range(3))
+    Kb, Vb, Rb = out
+    _lib.call("msa_pool_chunks", _p(K), _p(V), _p(Kr), _p(doc_tok_off), _p(doc_chunk_off), n_docs, n_tok,
+              n_chunks, H, D, chunk_len, float(rope_base), _p(Kb), _p(Vb), _p(Rb), _stream(stream))
+    return Kb, Vb, Rb
+
+
+def route_workspace_bytes(B, T, H, D, n_chunks, n_docs) -> int:
+    return int(_lib.load().msa_route_workspace_bytes(B, T, H, D, n_chunks, n_docs))
+
+
+def route_scores(Qr, Krbar, doc_chunk_off, doc_exclude=None, want_chunk_scores: bool = False,
+                 doc_scores=None, chunk_scores=None, ws=None, stream=None):
+    """msa_route_scores: doc_scores fp32 [B, n_docs] (and chunk_scores [B, n_chunks])."""
+    _bf16(Qr, "Qr"); _bf16(Krbar, "Krbar"); _dev(Qr, "Qr")
+    B, T, H, D = Qr.shape
+    n_chunks = Krbar.shape[0]
+    n_docs = doc_chunk_off.numel() - 1
+    dev = Qr.device
+    if doc_scores is None:
+        doc_scores = torch.empty((B, n_docs), dtype=torch.float32, device=dev)
+    if want_chunk_scores and chunk_scores is None:
+        chunk_scores = torch.empty((B, n_chunks), dtype=torch.float32, device=dev)
+    need = route_workspace_bytes(B, T, H, D, n_chunks, n_docs)
+    if ws is None:
+        ws = workspace(need, dev)
+    if doc_exclude is not None:
+        assert doc_exclude.dtype in (torch.uint8, torch.bool) and doc_exclude.shape == (B, n_docs)
+        doc_exclude = doc_exclude.contiguous()
+    _lib.call("msa_route_scores", _p(Qr), B, T, H, D, _p(Krbar), n_chunks, _p(doc_chunk_off), n_docs,
+              _p(doc_exclude), _p(doc_scores), _p(chunk_scores), _p(ws), ws.numel(), _stream(stream))
+    if chunk_scores is not None:
+        return doc_scores, chunk_scores
+    return doc_scores
+
+
+def topk_workspace_bytes(B, n_docs, k) -> int:
+    return int(_lib.load().msa_topk_workspace_bytes(B, n_docs, k))
+
+
+def topk_docs(doc_scores, k: int, top_idx=None, top_scores=None, ws=None, stream=None):
+    """msa_topk_docs: (top_idx int32 [B, k], top_scores fp32 [B, k])."""
+    _dev(doc_scores, "doc_scores")
+    assert doc_scores.dtype == torch.float32 and doc_scores.is_contiguous()
+    B, n_docs = doc_scores.shape
+    dev = doc_scores.device
+    if top_idx is None:
+        top_idx = torch.empty((B, k), dtype=torch.int32, device=dev)
+    if top_scores is None:
+        top_scores = torch.empty((B, k), dtype=torch.float32, device=dev)
+    need = topk_workspace_bytes(B, n_docs, k)
+    if ws is None:
+        ws = workspace(need, dev, "topk")
+    _lib.call("msa_topk_docs", _p(doc_scores), B, n_docs, k, _p(top_idx), _p(top_scores), _p(ws), ws.numel(),
+              _stream(stream))
+    return top_idx, top_scores
+
+
+def fetch_docs(top_idx_host, host_store, doc_chunk_off_host, staging, Mmax: int, side_stream=None,
+               done_event=None) -> torch.Tensor:
+    """msa_fetch_docs: host-driven copies of the selected docs into staging; returns mem_len (host int32)."""
+    assert top_idx_host.device.type == "cpu" and top_idx_host.dtype == torch.int32
+    assert doc_chunk_off_host.device.type == "cpu" and doc_chunk_off_host.dtype == torch.int64
+    top_idx_host = top_idx_host.contiguous()
+    B, k = top_idx_host.shape
+    n_docs = doc_chunk_off_host.numel() - 1
+    H, D = host_store.shape[-2], host_store.shape[-1]
+    mem_len = torch.empty(B, dtype=torch.int32)
+    side = side_stream if side_stream is not None else torch.cuda.current_stream()
+    ev = ctypes.c_void_p(0 if done_event is None else done_event.cuda_event)
+    _lib.call("msa_fetch_docs", _p(top_idx_host), B, k, _p(host_store), _p(doc_chunk_off_host), n_docs, H, D,
+              _p(staging), Mmax, _p(mem_len), ctypes.c_void_p(side.cuda_stream), ev)
+    return mem_len
+
+
+def gather_docs(top_idx, host_store, doc_chunk_off, staging, Mmax: int, mem_len=None, stream=None):
+    """msa_gather_docs: device-side assembly; returns mem_len (device int32 [B])."""
+    B, k = top_idx.shape
+    n_docs = doc_chunk_off.numel() - 1
+    H, D = host_store.shape[-2], host_store.shape[-1]
+    if mem_len is None:
+        mem_len = torch.empty(B, dtype=torch.int32, device=top_idx.device)
+    _lib.call("msa_gather_docs", _p(top_idx), B, k, _p(host_store), _p(doc_chunk_off), n_docs, H, D,
+              _p(staging), Mmax, _p(mem_len), _stream(stream))
+    return mem_len
+
+
+def sparse_attn_decode(Q, Kloc, Vloc, Kmem, Vmem, mem_entry_stride: int, Mmax: int, mem_len,
+                       rope_offset: int, rope_base: float = 1.0e6, scale: Optional[float] = None,
+                       out=None, stream=None):
+    """msa_sparse_attn_decode: O fp32 [B, Tq, Hq, D]."""
+    _bf16(Q, "Q"); _bf16(Kloc, "Kloc"); _bf16(Vloc, "Vloc")
+    B, Tq, Hq, D = Q.shape
+    _, Tl, Hkv, _ = Kloc.shape
+    if scale is None:
+        scale = D ** -0.5
+    if out is None:
+        out = torch.empty((B, Tq, Hq, D), dtype=torch.float32, device=Q.device)
+    kp = Kmem.data_ptr() if Kmem is not None else 0
+    vp = Vmem.data_ptr() if Vmem is not None else 0
+    _lib.call("msa_sparse_attn_decode", _p(Q), B, Tq, Hq, D, _p(Kloc), _p(Vloc), Tl, Hkv, ctypes.c_void_p(kp),
+              ctypes.c_void_p(vp), mem_entry_stride, Mmax, _p(mem_len), rope_offset, float(rope_base),
+              float(scale), _p(out), _stream(stream))
+    return out

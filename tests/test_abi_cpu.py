@@ -1,0 +1,88 @@
+"""The C ABI without a GPU: the library loads, exports every symbol the header
+declares, and rejects invalid arguments on the host before launching anything."""
+
+import ctypes
+import os
+
+import pytest
+
+from sparse_retrieval_memory_amd import _lib
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libmsa.so not built")
+N = None
+
+
+def test_exports_every_declared_symbol():
+    lib = _lib.load()
+    names = _lib.declared_symbols()
+    assert {"msa_pool_chunks", "msa_route_scores", "msa_topk_docs", "msa_sparse_attn_decode",
+            "msa_fetch_docs", "msa_gather_docs"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(_lib.SIGNATURES) == set(names)
+    assert lib.msa_version() == 100
+    assert lib.msa_status_string(-3) == b"workspace too small"
+
+
+def _code(name, *args):
+    return _lib.raw(name, *args)
+
+
+def test_route_validation():
+    p = ctypes.c_void_p(16)
+    E = _lib
+    assert _code("msa_route_scores", p, 0, 4, 8, 128, p, 10, p, 2, N, p, N, p, 1 << 20, N) == E.MSA_ERR_INVALID_ARG
+    assert _code("msa_route_scores", p, 1, 0, 8, 128, p, 10, p, 2, N, p, N, p, 1 << 20, N) == E.MSA_ERR_INVALID_ARG
+    assert _code("msa_route_scores", N, 1, 4, 8, 128, p, 10, p, 2, N, p, N, p, 1 << 20, N) == E.MSA_ERR_INVALID_ARG
+    assert _code("msa_route_scores", p, 1, 4, 8, 64, p, 10, p, 2, N, p, N, p, 1 << 20, N) == E.MSA_ERR_UNSUPPORTED
+    assert _code("msa_route_scores", p, 1, 4, 3, 128, p, 10, p, 2, N, p, N, p, 1 << 20, N) == E.MSA_ERR_UNSUPPORTED
+    assert _code("msa_route_scores", ctypes.c_void_p(18), 1, 4, 8, 128, p, 10, p, 2, N, p, N, p, 1 << 20, N) \
+        == E.MSA_ERR_INVALID_ARG                                   # misaligned
+    need = _lib.load().msa_route_workspace_bytes(2, 4, 8, 128, 1000, 10)
+    assert need >= 2 * 1000 * 4
+    assert _code("msa_route_scores", p, 2, 4, 8, 128, p, 1000, p, 10, N, p, N, p, need - 1, N) == E.MSA_ERR_WORKSPACE
+    assert b"workspace" in _lib.load().msa_last_error()
+
+
+def test_topk_validation():
+    p = ctypes.c_void_p(16)
+    E = _lib
+    ws = 1 << 20
+    assert _code("msa_topk_docs", p, 1, 10, 0, p, p, p, ws, N) == E.MSA_ERR_INVALID_ARG
+    assert _code("msa_topk_docs", p, 1, 10, 11, p, p, p, ws, N) == E.MSA_ERR_INVALID_ARG
+    assert _code("msa_topk_docs", p, 1, 5000, 2000, p, p, p, ws, N) == E.MSA_ERR_UNSUPPORTED
+    assert _code("msa_topk_docs", p, 1, 10, 4, p, p, p, 0, N) == E.MSA_ERR_WORKSPACE
+
+
+def test_pool_and_attention_validation():
+    p = ctypes.c_void_p(16)
+    E = _lib
+    assert _code("msa_pool_chunks", p, p, p, p, p, 4, 100, 4, 8, 96, 64, 1e6, p, p, p, N) == E.MSA_ERR_UNSUPPORTED
+    assert _code("msa_pool_chunks", p, p, p, p, p, 4, 100, 4, 8, 128, 0, 1e6, p, p, p, N) == E.MSA_ERR_INVALID_ARG
+    assert _code("msa_pool_chunks", p, p, p, p, p, 4, 100, 4, 8, 128, 64, 1.0, p, p, p, N) == E.MSA_ERR_INVALID_ARG
+    # attention: Tq > Tl, Hq % Hkv, D
+    args = lambda B=1, Tq=4, Hq=32, D=128, Tl=4, Hkv=8: (p, B, Tq, Hq, D, p, p, Tl, Hkv, p, p, 2048, 8, p, 0, 1e6,
+                                                         0.1, p, N)
+    assert _code("msa_sparse_attn_decode", *args(Tq=5)) == E.MSA_ERR_INVALID_ARG
+    assert _code("msa_sparse_attn_decode", *args(Hq=30)) == E.MSA_ERR_INVALID_ARG
+    assert _code("msa_sparse_attn_decode", *args(D=64)) == E.MSA_ERR_UNSUPPORTED
+
+
+def test_fetch_validation_host_side():
+    import numpy as np
+    top = np.array([[0, 5]], dtype=np.int32)                       # 5 is out of range
+    off = np.array([0, 2, 3, 4], dtype=np.int64)
+    ml = np.zeros(1, dtype=np.int32)
+    p = ctypes.c_void_p(16)
+    rc = _code("msa_fetch_docs", top.ctypes.data, 1, 2, p, off.ctypes.data, 3, 8, 128, p, 16, ml.ctypes.data, N, N)
+    assert rc == _lib.MSA_ERR_INVALID_ARG
+    top = np.array([[0, 2]], dtype=np.int32)                       # needs 3 entries > Mmax 2
+    rc = _code("msa_fetch_docs", top.ctypes.data, 1, 2, p, off.ctypes.data, 3, 8, 128, p, 2, ml.ctypes.data, N, N)
+    assert rc == _lib.MSA_ERR_INVALID_ARG
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        _lib.load()

@@ -1,0 +1,250 @@
+"""GPU parity: every kernel through the C ABI against the fp64 oracle, on the
+same seeded inputs, at sizes that span several tiles and a ragged tail, plus
+the edge cases (1-chunk documents, k = 1, k = n_docs, single query token,
+empty memory).  Rules P1-P4 are in tests/parity.py."""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import msa_oracle as O
+from sparse_retrieval_memory_amd import ops
+from synth import configs as C
+from synth import native
+from synth import splitmix as sm
+
+from tests.parity import ATT_TOL, SCORE_TOL, bf16_ulp_diff, check_topk, dev_bits, host_bits, rel_rows
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def announce(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def f64(bits):
+    return O.bf16_to_f64(bits)
+
+
+# ------------------------------------------------------------------ generator
+def test_device_generator_matches_host():
+    for (seed, tid, layer, start, n) in [(1, 3, 0, 0, 4096), (7, 11, 5, 12345, 100003), (2, 9, 17, 2**33 + 5, 777)]:
+        announce("fill", seed, tid, layer, start, n)
+        out = torch.empty(n, dtype=torch.int16, device=DEV)
+        native.fill_normal_bf16_device(out, seed, tid, layer, start)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(out), sm.normal_bf16(seed, tid, layer, start, n))
+
+
+# -------------------------------------------------------------------- routing
+def _route_case(B, T, H, n_docs, seed, lens=None):
+    r = np.random.default_rng(seed)
+    if lens is None:
+        lens = r.integers(1, 7, n_docs)                  # chunks per document, includes 1-chunk docs
+    off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    G = int(off[-1])
+    Qr = sm.normal_bf16(seed, sm.TID_QR, 0, 0, B * T * H * 128).reshape(B, T, H, 128)
+    Kr = sm.normal_bf16(seed, sm.TID_KRBAR, 0, 0, G * H * 128).reshape(G, H, 128)
+    return Qr, Kr, off
+
+
+def _run_route(Qr, Kr, off, exclude=None):
+    doc, ch = ops.route_scores(dev_bits(Qr), dev_bits(Kr), torch.from_numpy(off).to(DEV),
+                               None if exclude is None else torch.from_numpy(exclude.astype(np.uint8)).to(DEV),
+                               want_chunk_scores=True)
+    torch.cuda.synchronize()
+    return doc.cpu().numpy().astype(np.float64), ch.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("B,T,H", [(1, 1, 8), (1, 2, 8), (1, 7, 8), (1, 15, 8), (3, 5, 8), (2, 3, 4), (1, 9, 1),
+                                   (1, 16, 8), (1, 17, 8), (1, 32, 8), (1, 33, 8), (1, 64, 8), (1, 100, 8),
+                                   (1, 128, 8), (1, 130, 8), (2, 64, 8), (5, 40, 8), (3, 20, 2), (1, 48, 4),
+                                   (1, 260, 8)])
+def test_route_scores_match_oracle(B, T, H):
+    announce("route", B, T, H)
+    Qr, Kr, off = _route_case(B, T, H, n_docs=337, seed=100 + B * 1000 + T * 10 + H)
+    doc, ch = _run_route(Qr, Kr, off)
+    ref_ch, ref_doc = O.route(f64(Qr), f64(Kr), off)
+    assert np.abs(ch - ref_ch).max() <= SCORE_TOL
+    assert np.abs(doc - ref_doc).max() <= SCORE_TOL
+
+
+def test_route_exclusion_and_zero_vectors():
+    Qr, Kr, off = _route_case(2, 40, 8, n_docs=97, seed=5)
+    Kr = Kr.copy(); Qr = Qr.copy()
+    Kr[3, 2] = 0                       # zero head in a chunk -> cosine 0 for that head
+    Qr[1, 7, 5] = 0                    # zero query head
+    excl = np.zeros((2, 97), bool); excl[0, [1, 50]] = True; excl[1, 96] = True
+    announce("route-exclude")
+    doc, ch = _run_route(Qr, Kr, off, excl)
+    ref_ch, ref_doc = O.route(f64(Qr), f64(Kr), off, excl)
+    assert np.all(doc[excl] == -np.inf)
+    assert np.abs(doc[~excl] - ref_doc[~excl]).max() <= SCORE_TOL
+    assert np.abs(ch - ref_ch).max() <= SCORE_TOL
+
+
+def test_route_valu_exclusion():
+    Qr, Kr, off = _route_case(1, 3, 8, n_docs=50, seed=6)
+    excl = np.zeros((1, 50), bool); excl[0, ::7] = True
+    announce("route-valu-exclude")
+    doc, _ = _run_route(Qr, Kr, off, excl)
+    _, ref_doc = O.route(f64(Qr), f64(Kr), off, excl)
+    assert np.all(doc[excl] == -np.inf)
+    assert np.abs(doc[~excl] - ref_doc[~excl]).max() <= SCORE_TOL
+
+
+def test_route_deterministic():
+    Qr, Kr, off = _route_case(1, 128, 8, n_docs=3000, seed=8)
+    announce("route-determinism")
+    a, _ = _run_route(Qr, Kr, off)
+    b, _ = _run_route(Qr, Kr, off)
+    assert np.array_equal(a.view(np.uint64), b.view(np.uint64))
+
+
+# ---------------------------------------------------------------------- top-k
+@pytest.mark.parametrize("B,n,k", [(1, 64, 4), (1, 1000, 16), (16, 20000, 16), (1, 200000, 16), (4, 20000, 8),
+                                   (1, 7, 7), (3, 5, 1), (2, 4097, 1024), (1, 2049, 2), (2, 100, 100)])
+def test_topk_matches_oracle(B, n, k):
+    announce("topk", B, n, k)
+    r = np.random.default_rng(B * 7 + n + k)
+    s = r.standard_normal((B, n)).astype(np.float32)
+    s[:, ::5] = np.round(s[:, ::5], 1)                       # ties
+    if n > 10:
+        s[0, 3] = -np.inf
+    idx, sc = ops.topk_docs(torch.from_numpy(s).to(DEV), k)
+    torch.cuda.synchronize()
+    idx = idx.cpu().numpy(); sc = sc.cpu().numpy()
+    ref_idx, ref_sc = O.topk(s.astype(np.float64), k)
+    # the scores are exact fp32 inputs: selection and order must be identical
+    assert np.array_equal(idx, ref_idx)
+    assert np.array_equal(sc.astype(np.float64), ref_sc)
+
+
+# ---------------------------------------------------------------------- pool
+@pytest.mark.parametrize("H,lens", [(8, [1, 63, 64, 65, 130, 512, 7, 200]), (4, [64, 3, 129]), (16, [70, 1]),
+                                    (2, [300, 5, 64])])
+def test_pool_matches_oracle(H, lens):
+    announce("pool", H, lens)
+    w = C.config(1, n_docs=len(lens), length_law="custom", custom_lengths=tuple(lens), H=H)
+    K = C.raw_block(w, "K", 0, w.n_tok); V = C.raw_block(w, "V", 0, w.n_tok); Kr = C.raw_block(w, "Kr", 0, w.n_tok)
+    Kb, Vb, Rb = ops.pool_chunks(dev_bits(K), dev_bits(V), dev_bits(Kr), torch.from_numpy(w.doc_tok_off).to(DEV),
+                                 torch.from_numpy(w.doc_chunk_off).to(DEV), w.n_chunks, 64, w.rope_base)
+    torch.cuda.synchronize()
+    rK, rV, rR, off = O.pool(f64(K), f64(V), f64(Kr), w.doc_len, 64, w.rope_base)
+    assert bf16_ulp_diff(host_bits(Vb), O.f64_to_bf16_bits(rV)).max() <= 1
+    assert bf16_ulp_diff(host_bits(Rb), O.f64_to_bf16_bits(rR)).max() <= 1
+    assert bf16_ulp_diff(host_bits(Kb), O.f64_to_bf16_bits(rK)).max() <= 2
+
+
+def test_pool_slab_with_offset_bases():
+    # a slab of documents 3..5 of a corpus: offsets rebased by the caller's first row
+    lens = [100, 64, 1, 300, 65, 2]
+    w = C.config(1, n_docs=6, length_law="custom", custom_lengths=tuple(lens))
+    K = C.raw_block(w, "K", 0, w.n_tok); V = C.raw_block(w, "V", 0, w.n_tok); Kr = C.raw_block(w, "Kr", 0, w.n_tok)
+    t0, t1 = int(w.doc_tok_off[3]), int(w.doc_tok_off[6])
+    c0, c1 = int(w.doc_chunk_off[3]), int(w.doc_chunk_off[6])
+    announce("pool-slab")
+    Kb, Vb, Rb = ops.pool_chunks(dev_bits(K[t0:t1]), dev_bits(V[t0:t1]), dev_bits(Kr[t0:t1]),
+                                 torch.from_numpy(w.doc_tok_off[3:]).to(DEV),
+                                 torch.from_numpy(w.doc_chunk_off[3:]).to(DEV), c1 - c0, 64, w.rope_base)
+    torch.cuda.synchronize()
+    rK, rV, rR, off = O.pool(f64(K), f64(V), f64(Kr), w.doc_len, 64, w.rope_base)
+    assert bf16_ulp_diff(host_bits(Vb), O.f64_to_bf16_bits(rV[c0:c1])).max() <= 1
+    assert bf16_ulp_diff(host_bits(Kb), O.f64_to_bf16_bits(rK[c0:c1])).max() <= 2
+
+
+# ------------------------------------------------------------------ attention
+@pytest.mark.parametrize("B,Tq,Tl,M,offset", [(1, 32, 32, 32, 4), (1, 1, 128, 262, 16), (1, 128, 128, 262, 16),
+                                              (2, 64, 64, 133, 16), (1, 5, 9, 0, 0), (1, 17, 40, 1, 3),
+                                              (3, 16, 16, 70, 8), (1, 128, 128, 448, 16)])
+def test_attention_matches_oracle(B, Tq, Tl, M, offset):
+    announce("attn", B, Tq, Tl, M, offset)
+    seed = B * 1000 + Tq + M
+    Hq, Hkv, D = 32, 8, 128
+    Q = sm.normal_bf16(seed, sm.TID_Q, 0, 0, B * Tq * Hq * D).reshape(B, Tq, Hq, D)
+    Kl = sm.normal_bf16(seed, sm.TID_KLOC, 0, 0, B * Tl * Hkv * D).reshape(B, Tl, Hkv, D)
+    Vl = sm.normal_bf16(seed, sm.TID_VLOC, 0, 0, B * Tl * Hkv * D).reshape(B, Tl, Hkv, D)
+    Mmax = max(M, 1)
+    st = sm.normal_bf16(seed, sm.TID_KBAR, 0, 0, B * Mmax * 2 * Hkv * D).reshape(B, Mmax, 2, Hkv, D)
+    mem_len = np.array([max(M - 3 * b, 0) for b in range(B)], dtype=np.int32)
+    stg = dev_bits(st)
+    O_gpu = ops.sparse_attn_decode(dev_bits(Q), dev_bits(Kl), dev_bits(Vl), stg, stg[:, :, 1], 2 * Hkv * D, Mmax,
+                                   torch.from_numpy(mem_len).to(DEV), offset, 1e6)
+    torch.cuda.synchronize()
+    o = O_gpu.cpu().numpy()
+    for b in range(B):
+        m = int(mem_len[b])
+        ref = O.attend(f64(Q[b]), f64(Kl[b]), f64(Vl[b]), f64(st[b, :m, 0]), f64(st[b, :m, 1]), offset, 1e6,
+                       D ** -0.5)
+        assert rel_rows(o[b], ref) <= ATT_TOL
+        assert rel_rows(o[b], ref) <= 1e-4          # fp32 path: far inside the bf16 budget
+
+
+# ---------------------------------------------------------------- assembly
+def test_fetch_and_gather_assemble_rank_order():
+    announce("fetch/gather")
+    H, D = 8, 128
+    lens = np.array([3, 1, 5, 2, 4, 1, 6], dtype=np.int64)
+    off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    G = int(off[-1])
+    store_np = sm.normal_bf16(9, sm.TID_KBAR, 0, 0, G * 2 * H * D).reshape(G, 2, H, D)
+    store = torch.from_numpy(store_np.view(np.int16)).pin_memory()
+    top = np.array([[2, 3, 0], [6, 1, 4]], dtype=np.int32)     # 2,3 adjacent -> one copy
+    Mmax = 12
+    staging = torch.zeros((2, Mmax, 2, H, D), dtype=torch.int16, device=DEV)
+    side = torch.cuda.Stream()
+    ev = torch.cuda.Event()
+    ml = ops.fetch_docs(torch.from_numpy(top), store, torch.from_numpy(off), staging, Mmax, side, ev)
+    ev.synchronize()
+    st = host_bits(staging)
+    for b in range(2):
+        chunks = O.assemble(top[b], off)
+        assert ml[b] == len(chunks)
+        assert np.array_equal(st[b, :len(chunks)], store_np[chunks])
+    staging2 = torch.zeros_like(staging)
+    ml2 = ops.gather_docs(torch.from_numpy(top).to(DEV), store, torch.from_numpy(off).to(DEV), staging2, Mmax)
+    torch.cuda.synchronize()
+    assert np.array_equal(ml2.cpu().numpy(), ml.numpy())
+    assert np.array_equal(host_bits(staging2), st)
+
+
+# ------------------------------------------------------------- end to end
+def test_cfg1_end_to_end_step():
+    """Pool raw K/V/Kr, route, top-k, fetch from pinned host, attend (Tq = T and Tq = 1)."""
+    w = C.config(1)
+    announce("cfg1 e2e", w.describe())
+    K = C.raw_block(w, "K", 0, w.n_tok); V = C.raw_block(w, "V", 0, w.n_tok); Kr = C.raw_block(w, "Kr", 0, w.n_tok)
+    q = C.queries(w)
+    tok_off = torch.from_numpy(w.doc_tok_off).to(DEV); ch_off = torch.from_numpy(w.doc_chunk_off).to(DEV)
+    Kb, Vb, Rb = ops.pool_chunks(dev_bits(K), dev_bits(V), dev_bits(Kr), tok_off, ch_off, w.n_chunks, 64, w.rope_base)
+    doc = ops.route_scores(dev_bits(q["Qr"]), Rb, ch_off)
+    idx, sc = ops.topk_docs(doc, w.k)
+    store = torch.stack([Kb, Vb], dim=1).cpu().pin_memory()          # [G, 2, H, D] host tier
+    Mmax = int(w.doc_n_chunks.max()) * w.k
+    staging = torch.zeros((1, Mmax, 2, w.H, w.D), dtype=torch.int16, device=DEV)
+    ml = ops.fetch_docs(idx.cpu(), store, torch.from_numpy(w.doc_chunk_off), staging, Mmax)
+    ml_dev = ml.to(DEV)
+    outs = {}
+    for Tq in (w.Tq, 1):
+        Qx = dev_bits(q["Q"][:, -Tq:])
+        outs[Tq] = ops.sparse_attn_decode(Qx, dev_bits(q["Kloc"]), dev_bits(q["Vloc"]), staging, staging[:, :, 1],
+                                          2 * w.H * w.D, Mmax, ml_dev, w.k, w.rope_base)
+    torch.cuda.synchronize()
+    # oracle pipeline, independently from raw inputs
+    rK, rV, rR, off = O.pool(f64(K), f64(V), f64(Kr), w.doc_len, 64, w.rope_base)
+    rK, rV, rR = O.round_bf16(rK), O.round_bf16(rV), O.round_bf16(rR)
+    _, ref_doc = O.route(f64(q["Qr"]), rR, off)
+    assert np.abs(doc.cpu().numpy() - ref_doc).max() <= 1e-4       # pooled stores may differ by 1 ulp
+    gi = idx.cpu().numpy()[0]
+    check_topk(gi, ref_doc[0], w.k)
+    (_, needle), = C.planted_docs(w)
+    assert gi[0] == needle
+    mem = O.assemble(gi, off)
+    for Tq, o in outs.items():
+        ref = O.attend(f64(q["Q"][0, -Tq:]), f64(q["Kloc"][0]), f64(q["Vloc"][0]), rK[mem], rV[mem], w.k,
+                       w.rope_base, w.D ** -0.5)
+        assert rel_rows(o.cpu().numpy()[0], ref) <= ATT_TOL
