@@ -7,6 +7,7 @@
  * Context Assembly", "Sparse Generation"):
  *
  *   msa_pool_chunks         offline: chunk-mean pooled (Kbar, Vbar, Krbar) cache
+ *   msa_krbar_inv_norms     offline: 1/|Krbar| per chunk and head, stored beside the store
  *   msa_route_scores        online: cosine routing scan over every Krbar chunk
  *   msa_topk_docs           online: the k most relevant documents
  *   msa_fetch_docs          online: copy the selected content KV from pinned host
@@ -99,6 +100,8 @@ int msa_pool_chunks(const uint16_t* K, const uint16_t* V, const uint16_t* Kr,
  *
  *   Qr            bf16 [B, T, H, D]
  *   Krbar         bf16 [n_chunks, H, D]        (HBM-resident routing-key store)
+ *   krbar_inv_norm fp32 [n_chunks, H] from msa_krbar_inv_norms for this Krbar, or
+ *                 NULL (the scan then derives the norms from the tiles it streams)
  *   doc_chunk_off int64 [n_docs+1] (device), doc_chunk_off[0] == 0, doc_chunk_off[n_docs] == n_chunks
  *   doc_exclude   uint8 [B, n_docs] or NULL
  *   doc_scores    fp32 [B, n_docs] out
@@ -110,10 +113,27 @@ int msa_pool_chunks(const uint16_t* K, const uint16_t* V, const uint16_t* Kr,
  */
 size_t msa_route_workspace_bytes(int B, int T, int H, int D, int64_t n_chunks, int64_t n_docs);
 int msa_route_scores(const uint16_t* Qr, int B, int T, int H, int D,
-                     const uint16_t* Krbar, int64_t n_chunks,
+                     const uint16_t* Krbar, const float* krbar_inv_norm, int64_t n_chunks,
                      const int64_t* doc_chunk_off, int64_t n_docs,
                      const uint8_t* doc_exclude, float* doc_scores, float* chunk_scores,
                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * msa_krbar_inv_norms -- 1/|Krbar[g, h, :]| for every pooled chunk and head.
+ *
+ * The cosine of msa_route_scores (b-lab.team summary sec. 1) divides by the
+ * norm of each pooled router key.  The store is built once, offline (b-lab.team
+ * pipeline stage 1), so its norms can be computed once beside it and streamed
+ * with it (32 bytes per 2 KB chunk at H = 8) instead of being recomputed by every
+ * query's scan.  Zero vectors give 0 (so their cosine is 0).
+ *
+ *   Krbar      bf16 [n_chunks, H, D], D == 128
+ *   inv_norm   fp32 [n_chunks, H] out (hardware reciprocal square root, ~1 ulp)
+ * Pass the result as krbar_inv_norm to msa_route_scores (used when H >= 4 and
+ * B*T > 15; otherwise the scan computes the norms itself).
+ */
+int msa_krbar_inv_norms(const uint16_t* Krbar, int64_t n_chunks, int H, int D, float* inv_norm,
+                        hipStream_t stream);
 
 /*
  * msa_topk_docs -- the k most relevant documents per query.

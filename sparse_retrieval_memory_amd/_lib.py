@@ -34,8 +34,9 @@ SIGNATURES = {
     "msa_pool_chunks": (c_i, [c_p, c_p, c_p, c_p, c_p, c_i64, c_i64, c_i64, c_i, c_i, c_i, c_d,
                               c_p, c_p, c_p, c_p]),
     "msa_route_workspace_bytes": (c_sz, [c_i, c_i, c_i, c_i, c_i64, c_i64]),
-    "msa_route_scores": (c_i, [c_p, c_i, c_i, c_i, c_i, c_p, c_i64, c_p, c_i64, c_p, c_p, c_p,
+    "msa_route_scores": (c_i, [c_p, c_i, c_i, c_i, c_i, c_p, c_p, c_i64, c_p, c_i64, c_p, c_p, c_p,
                                c_p, c_sz, c_p]),
+    "msa_krbar_inv_norms": (c_i, [c_p, c_i64, c_i, c_i, c_p, c_p]),
     "msa_topk_workspace_bytes": (c_sz, [c_i, c_i64, c_i]),
     "msa_topk_docs": (c_i, [c_p, c_i, c_i64, c_i, c_p, c_p, c_p, c_sz, c_p]),
     "msa_fetch_docs": (c_i, [c_p, c_i, c_i, c_p, c_p, c_i64, c_i, c_i, c_p, c_i, c_p, c_p, c_p]),

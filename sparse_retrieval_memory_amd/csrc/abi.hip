@@ -64,10 +64,21 @@ size_t msa_route_workspace_bytes(int B, int T, int H, int D, int64_t n_chunks, i
   return msa::route_workspace(B, T, H, n_chunks, n_docs);
 }
 
-int msa_route_scores(const uint16_t* Qr, int B, int T, int H, int D, const uint16_t* Krbar, int64_t n_chunks,
-                     const int64_t* doc_chunk_off, int64_t n_docs, const uint8_t* doc_exclude,
-                     float* doc_scores, float* chunk_scores, void* workspace, size_t workspace_bytes,
-                     hipStream_t stream) {
+int msa_krbar_inv_norms(const uint16_t* Krbar, int64_t n_chunks, int H, int D, float* inv_norm,
+                        hipStream_t stream) {
+  msa::clear_error();
+  MSA_CHECK_ARG(n_chunks >= 0 && H >= 1, "n_chunks >= 0 and H >= 1 required");
+  MSA_CHECK_ARG(n_chunks == 0 || (Krbar && inv_norm), "null pointer");
+  MSA_CHECK_SUPPORTED(D == 128, "D=%d unsupported (D must be 128)", D);
+  MSA_CHECK_ARG(n_chunks == 0 || aligned16(Krbar), "Krbar must be 16-byte aligned");
+  MSA_CHECK_ARG(n_chunks * H < ((int64_t)1 << 38), "size out of range");
+  return msa::launch_krbar_norms(Krbar, n_chunks, H, inv_norm, stream);
+}
+
+int msa_route_scores(const uint16_t* Qr, int B, int T, int H, int D, const uint16_t* Krbar,
+                     const float* krbar_inv_norm, int64_t n_chunks, const int64_t* doc_chunk_off, int64_t n_docs,
+                     const uint8_t* doc_exclude, float* doc_scores, float* chunk_scores, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
   msa::clear_error();
   MSA_CHECK_ARG(B >= 1 && T >= 1, "B >= 1 and T >= 1 required (B=%d, T=%d)", B, T);
   MSA_CHECK_ARG(n_docs >= 1 && n_chunks >= 0, "n_docs >= 1 and n_chunks >= 0 required");
@@ -83,8 +94,9 @@ int msa_route_scores(const uint16_t* Qr, int B, int T, int H, int D, const uint1
     return MSA_ERR_WORKSPACE;
   }
   MSA_CHECK_ARG(workspace == nullptr || aligned16(workspace), "workspace must be 16-byte aligned");
-  return msa::launch_route(Qr, B, T, H, Krbar, n_chunks, doc_chunk_off, n_docs, doc_exclude, doc_scores,
-                           chunk_scores, workspace, stream);
+  MSA_CHECK_ARG(krbar_inv_norm == nullptr || aligned16(krbar_inv_norm), "krbar_inv_norm must be 16-byte aligned");
+  return msa::launch_route(Qr, B, T, H, Krbar, krbar_inv_norm, n_chunks, doc_chunk_off, n_docs, doc_exclude,
+                           doc_scores, chunk_scores, workspace, stream);
 }
 
 size_t msa_topk_workspace_bytes(int B, int64_t n_docs, int k) {

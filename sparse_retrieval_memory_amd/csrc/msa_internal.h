@@ -114,9 +114,10 @@ int launch_pool(const uint16_t* K, const uint16_t* V, const uint16_t* Kr, const 
                 const int64_t* doc_chunk_off, int64_t n_docs, int64_t n_tok, int64_t n_chunks, int H,
                 int chunk_len, double rope_base, uint16_t* Kbar, uint16_t* Vbar, uint16_t* Krbar,
                 hipStream_t stream);
-int launch_route(const uint16_t* Qr, int B, int T, int H, const uint16_t* Krbar, int64_t n_chunks,
-                 const int64_t* doc_chunk_off, int64_t n_docs, const uint8_t* doc_exclude,
+int launch_route(const uint16_t* Qr, int B, int T, int H, const uint16_t* Krbar, const float* inv_norm,
+                 int64_t n_chunks, const int64_t* doc_chunk_off, int64_t n_docs, const uint8_t* doc_exclude,
                  float* doc_scores, float* chunk_scores, void* workspace, hipStream_t stream);
+int launch_krbar_norms(const uint16_t* Krbar, int64_t n_chunks, int H, float* inv_norm, hipStream_t stream);
 size_t route_workspace(int B, int T, int H, int64_t n_chunks, int64_t n_docs);
 int launch_topk(const float* doc_scores, int B, int64_t n_docs, int k, int32_t* top_idx,
                 float* top_scores, void* workspace, hipStream_t stream);

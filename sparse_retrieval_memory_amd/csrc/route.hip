@@ -51,119 +51,222 @@ __device__ __forceinline__ float sq_norm_piece(uint4 v, float acc) {
 }
 
 __device__ __forceinline__ float inv_norm(float ss) { return ss > 0.f ? 1.0f / sqrtf(ss) : 0.f; }
+// hardware reciprocal square root (about 1 ulp): used on the scan's hot path
+__device__ __forceinline__ float inv_norm_fast(float ss) { return ss > 0.f ? __builtin_amdgcn_rsqf(ss) : 0.f; }
 
 // ------------------------------------------------------------------ MFMA path
+// Workgroup = 4 row tiles x HS head groups = 8 waves (H >= 2), two per SIMD:
+// wave (rt, hs) keeps rows [32 rt, 32 rt + 32) of its row block and heads
+// [hs*HPW, (hs+1)*HPW) resident as MFMA A operands (128 VGPRs for H = 8), so
+// one wave's MFMAs overlap the other's epilogue.  The two head groups of a
+// row tile add their partial head sums through LDS before the token max; the
+// two waves take turns finishing a tile, which lets a single exchange buffer
+// ride on the next tile's barrier instead of needing one of its own.
 template <int H>
-struct Tile {
+struct Cfg {
   static constexpr int ROW_BYTES = H * D * 2;       // one pooled chunk, all heads
   static constexpr int PIECES = ROW_BYTES / 16;     // 16-byte pieces per chunk row
-  static constexpr int BYTES = TC * ROW_BYTES;      // 8 KB * H
-  static constexpr int DMA_ITERS = BYTES / (16 * 256);
+  static constexpr int BYTES = TC * ROW_BYTES;      // tile bytes in HBM: 8 KB * H
+  // LDS row stride: for H >= 4 each chunk row is skewed by 16 bytes so the 32
+  // lanes of an MFMA B-operand read (one chunk each, same offset) hit distinct
+  // banks; for H <= 2 (a DMA instruction spans several rows) rows are packed
+  // and the 16-byte pieces are XOR-swizzled instead
+  static constexpr bool SKEW = PIECES >= 64;
+  static constexpr int ROW_STRIDE = SKEW ? ROW_BYTES + 16 : ROW_BYTES;
+  static constexpr int TILE_LDS = TC * ROW_STRIDE;
+  static constexpr int RK_BYTES = TC * H * 4;       // the tile's 1/|k| block (fp32 [TC][H])
+  static constexpr int HS = H >= 2 ? 2 : 1;         // head groups per row tile
+  static constexpr int HPW = H / HS;                // heads per wave
+  static constexpr int NWAVES = NW * HS;
+  static constexpr int THREADS = 64 * NWAVES;
+  static constexpr int DMA_ITERS = BYTES / (16 * THREADS);
 };
 
-// Issue the asynchronous copy of chunk tile `tile` into `lds`.  LDS slot j holds
-// logical piece (j % PIECES) ^ (n & 15) of chunk n = j / PIECES; the XOR stays
-// inside a 256-byte group, so each wave instruction still reads 1 KB of
-// contiguous global memory.  Chunks past the end are clamped to the last chunk
-// (their results are never written).
-template <int H>
-__device__ __forceinline__ void issue_tile(const uint8_t* __restrict__ kr, int64_t n_chunks,
-                                           int64_t tile, uint8_t* lds, int wave, int lane) {
-  using TL = Tile<H>;
+// Issue the asynchronous copy of chunk tile `tile` into `lds`.  Each wave
+// instruction moves 1 KB of contiguous global memory (half a chunk row for
+// H = 8) into the row's skewed LDS slot; for H <= 2 LDS slot j instead holds
+// piece (j % PIECES) ^ (n & 15) of chunk n = j / PIECES.  Chunks past the end
+// are clamped to the last chunk (their results are never written).  With stored norms (H >= 4) the tile's
+// fp32 [TC][H] block of 1/|k| follows into `lds_rk` (16-byte granules never
+// straddle a chunk boundary for H >= 4, so clamping is per chunk).
+template <int H, bool NORMS>
+__device__ __forceinline__ void issue_tile(const uint8_t* __restrict__ kr, const float* __restrict__ knorm,
+                                           int64_t n_chunks, int64_t tile, uint8_t* lds, float* lds_rk,
+                                           int wave, int lane) {
+  using CF = Cfg<H>;
+  const bool full = (tile + 1) * TC <= n_chunks;      // uniform: only the last tile needs clamping
 #pragma unroll
-  for (int i = 0; i < TL::DMA_ITERS; ++i) {
-    const int slot0 = (i * NW + wave) * 64;
-    const int slot = slot0 + lane;
-    const int n = slot / TL::PIECES;
-    const int lp = (slot % TL::PIECES) ^ (n & 15);
+  for (int i = 0; i < CF::DMA_ITERS; ++i) {
+    const int slot0 = (i * CF::NWAVES + wave) * 64;   // wave-uniform
+    int n, pp;
+    if constexpr (CF::PIECES >= 64) {
+      n = slot0 / CF::PIECES;                         // one chunk per wave instruction: uniform
+      pp = slot0 % CF::PIECES + lane;
+    } else {
+      n = (slot0 + lane) / CF::PIECES;
+      pp = (slot0 + lane) % CF::PIECES;
+    }
     int64_t g = tile * TC + n;
-    if (g >= n_chunks) g = n_chunks - 1;
-    dma16(kr + g * TL::ROW_BYTES + lp * 16, lds + slot0 * 16);
+    if (!full && g >= n_chunks) g = n_chunks - 1;
+    if constexpr (CF::SKEW) {
+      // scalar row base + 32-bit lane offset; LDS destination = the row's skewed slot
+      const uint64_t base = (uint64_t)(kr + g * CF::ROW_BYTES + (slot0 % CF::PIECES) * 16);
+      const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
+      const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+      const uint8_t* sb = (const uint8_t*)(((uint64_t)hi << 32) | lo);
+      dma16(sb + (uint32_t)lane * 16u, lds + n * CF::ROW_STRIDE + (slot0 % CF::PIECES) * 16);
+    } else {
+      const uint32_t off = (uint32_t)((pp ^ (n & 15)) * 16);
+      dma16(kr + g * CF::ROW_BYTES + off, lds + slot0 * 16);
+    }
+  }
+  if constexpr (NORMS) {
+    // granule `lane` = floats [4 lane, 4 lane + 4) of the tile's [TC][H] block,
+    // i.e. heads (4 lane) % H .. +3 of chunk 4 lane / H (never straddles a chunk for H >= 4)
+    static_assert(H >= 4, "stored norms need 16-byte granules within one chunk");
+    constexpr int GR = CF::RK_BYTES / 16;             // granules per tile (<= 64)
+    if (wave == CF::NWAVES - 1 && lane < GR) {
+      if (full) {
+        const uint64_t base = (uint64_t)(knorm + tile * TC * H);
+        const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
+        const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+        dma16((const uint8_t*)(((uint64_t)hi << 32) | lo) + (uint32_t)lane * 16u, lds_rk);
+      } else {
+        const int n = lane * 4 / H;
+        const int64_t g = (tile * TC + n < n_chunks) ? tile * TC + n : n_chunks - 1;
+        dma16(knorm + g * H + (lane * 4) % H, lds_rk);
+      }
+    }
   }
 }
 
-// One tile of the MFMA scan: wait for `cur` (filled by the previous step),
-// start filling `nxt` with the following tile, then score `cur`.  `cur` and
-// `nxt` are distinct LDS arrays so the compiler can see that reading one does
-// not depend on the DMA into the other.
-template <int H>
-__device__ __forceinline__ void mfma_tile_step(const uint8_t* __restrict__ kr, int64_t n_chunks, int64_t tile,
-                                               bool has_next, const uint8_t* cur, uint8_t* nxt,
-                                               float (*lds_rk)[TC], float (*lds_rq)[RW], const bf16x8_t (&qf)[H][8],
-                                               bool wave_active, int b, int t0, int T, uint32_t* chunk_enc,
-                                               int tid, int wave, int lane) {
-  using TL = Tile<H>;
-  const int half = lane >> 5;
-  const int nb = lane & 31;                   // this lane's chunk column in the tile
-  wait_vmem_all();
-  lds_barrier();                              // tile visible; previous tile fully consumed
-  if (has_next) issue_tile<H>(kr, n_chunks, tile + 1, nxt, wave, lane);
-
-  if (tid < TC * H) {                         // 1/|k| for (chunk n, head h)
-    const int n = tid % TC, h = tid / TC;
-    const uint8_t* row = cur + n * TL::ROW_BYTES;
-    float ss = 0.f;
+// Token max of a finished 32-row x 32-chunk head sum, then the chunk's atomic max.
+__device__ __forceinline__ void finish_tile(const f32x16_t& sacc, int half, int nb, int t0, int T, int b,
+                                            int64_t tile, int64_t n_chunks, float inv_h, uint32_t* chunk_enc) {
+  // accumulator i of this lane holds row 8*(i/4) + 4*half + i%4
+  float v = -INFINITY;
+  if (t0 + RW <= T) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int pp = (16 * h + i) ^ (n & 15);
-      ss = sq_norm_piece(*reinterpret_cast<const uint4*>(row + pp * 16), ss);
-    }
-    lds_rk[h][n] = inv_norm(ss);
-  }
-  lds_barrier();
-
-  if (wave_active) {
-    f32x16_t sacc;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
-    const uint8_t* brow = cur + nb * TL::ROW_BYTES;
-#pragma unroll
-    for (int h = 0; h < H; ++h) {
-      bf16x8_t bv[8];
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const int pp = (16 * h + 2 * ks + half) ^ (nb & 15);
-        bv[ks] = *reinterpret_cast<const bf16x8_t*>(brow + pp * 16);
-      }
-      f32x16_t acc;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[h][ks], bv[ks], acc, 0, 0, 0);
-      const float rk = lds_rk[h][nb];
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const float4 rq = *reinterpret_cast<const float4*>(&lds_rq[h][8 * q4 + 4 * half]);
-        sacc[4 * q4 + 0] = fmaf(acc[4 * q4 + 0], rk * rq.x, sacc[4 * q4 + 0]);
-        sacc[4 * q4 + 1] = fmaf(acc[4 * q4 + 1], rk * rq.y, sacc[4 * q4 + 1]);
-        sacc[4 * q4 + 2] = fmaf(acc[4 * q4 + 2], rk * rq.z, sacc[4 * q4 + 2]);
-        sacc[4 * q4 + 3] = fmaf(acc[4 * q4 + 3], rk * rq.w, sacc[4 * q4 + 3]);
-      }
-    }
-    // token max: accumulator i of this lane holds row 8*(i/4) + 4*half + i%4
-    float v = -INFINITY;
+    for (int i = 0; i < 16; ++i) v = fmaxf(v, sacc[i]);
+  } else {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int row = 8 * (i >> 2) + 4 * half + (i & 3);
       if (t0 + row < T) v = fmaxf(v, sacc[i]);
     }
-    v = fmaxf(v, __shfl_xor(v, 32));
-    const int64_t g = tile * TC + nb;
-    if (half == 0 && g < n_chunks)
-      atomicMax(&chunk_enc[(int64_t)b * n_chunks + g], enc_f32(v * (1.0f / H)));
+  }
+  v = fmaxf(v, __shfl_xor(v, 32));
+  const int64_t g = tile * TC + nb;
+  if (half == 0 && g < n_chunks) atomicMax(&chunk_enc[(int64_t)b * n_chunks + g], enc_f32(v * inv_h));
+}
+
+// One tile of the MFMA scan: wait for `cur` (filled by the previous step),
+// start filling `nxt` with the following tile, finish the previous tile's head
+// sum if this wave is its receiver, then score `cur`.  `cur`/`nxt` are
+// distinct LDS arrays so the compiler can see that reading one does not
+// depend on the DMA into the other.  PAR is the tile's parity within the
+// workgroup's range: on even tiles head group 1 sends and group 0 finishes,
+// on odd tiles the other way round.
+template <int H, bool NORMS, int PAR>
+__device__ __forceinline__ void mfma_tile_step(const uint8_t* __restrict__ kr, const float* __restrict__ knorm,
+                                               int64_t n_chunks, int64_t tile, bool has_prev, bool has_next,
+                                               const uint8_t* cur, const float* cur_rk, uint8_t* nxt, float* nxt_rk,
+                                               float (*lds_rq)[RW], f32x4_t* xchg,
+                                               const bf16x8_t (&qf)[Cfg<H>::HPW][8], f32x16_t& sprev,
+                                               bool wave_active, int hs, int b, int t0, int T,
+                                               uint32_t* chunk_enc, int wave, int lane) {
+  using CF = Cfg<H>;
+  const int half = lane >> 5;
+  const int nb = lane & 31;                   // this lane's chunk column in the tile
+  wait_vmem_all();
+  lds_barrier();                              // tile visible; previous tile fully consumed
+  if (has_next) issue_tile<H, NORMS>(kr, knorm, n_chunks, tile + 1, nxt, nxt_rk, wave, lane);
+
+  f32x4_t* x = xchg + lane;                   // layout [q4][lane]: 16-byte lane stride, conflict-free
+  if (CF::HS == 2 && has_prev && wave_active && hs == (PAR == 0 ? 1 : 0)) {
+    // receiver of the previous tile (parity 1 - PAR): add the sender's half and finish it
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const f32x4_t o = x[q4 * 64];
+      sprev[4 * q4] += o[0]; sprev[4 * q4 + 1] += o[1]; sprev[4 * q4 + 2] += o[2]; sprev[4 * q4 + 3] += o[3];
+    }
+    finish_tile(sprev, half, nb, t0, T, b, tile - 1, n_chunks, 1.0f / H, chunk_enc);
+  }
+  if (!wave_active) return;
+
+  f32x16_t sacc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+  const uint8_t* brow = cur + nb * CF::ROW_STRIDE;
+#pragma unroll
+  for (int hh = 0; hh < CF::HPW; ++hh) {
+    const int h = hs * CF::HPW + hh;
+    f32x16_t acc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+    float ss = 0.f;                           // |k|^2 over this lane's 64 of chunk nb's dims
+#pragma unroll
+    for (int k4 = 0; k4 < 8; k4 += 4) {
+      bf16x8_t bv[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int lp = 16 * h + 2 * (k4 + ks) + half;
+        const int pp = CF::SKEW ? lp : (lp ^ (nb & 15));
+        bv[ks] = *reinterpret_cast<const bf16x8_t*>(brow + pp * 16);
+      }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[hh][k4 + ks], bv[ks], acc, 0, 0, 0);
+        if constexpr (!NORMS) ss = sq_norm_piece(__builtin_bit_cast(uint4, bv[ks]), ss);
+      }
+    }
+    float rk;
+    if constexpr (NORMS) {
+      rk = cur_rk[nb * H + h];
+    } else {
+      ss += __shfl_xor(ss, 32);               // lanes l and l^32 hold the two halves of chunk nb
+      rk = inv_norm_fast(ss);
+    }
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const float4 rq = *reinterpret_cast<const float4*>(&lds_rq[h][8 * q4 + 4 * half]);
+      sacc[4 * q4 + 0] = fmaf(acc[4 * q4 + 0], rk * rq.x, sacc[4 * q4 + 0]);
+      sacc[4 * q4 + 1] = fmaf(acc[4 * q4 + 1], rk * rq.y, sacc[4 * q4 + 1]);
+      sacc[4 * q4 + 2] = fmaf(acc[4 * q4 + 2], rk * rq.z, sacc[4 * q4 + 2]);
+      sacc[4 * q4 + 3] = fmaf(acc[4 * q4 + 3], rk * rq.w, sacc[4 * q4 + 3]);
+    }
+    // keep heads from being interleaved by the scheduler: bounds register pressure
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if constexpr (CF::HS == 2) {
+    if (hs == (PAR == 0 ? 1 : 0)) {           // sender of this tile
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        x[q4 * 64] = f32x4_t{sacc[4 * q4], sacc[4 * q4 + 1], sacc[4 * q4 + 2], sacc[4 * q4 + 3]};
+    } else {
+      sprev = sacc;                           // finished at the start of the next step
+    }
+  } else {
+    finish_tile(sacc, half, nb, t0, T, b, tile, n_chunks, 1.0f / H, chunk_enc);
   }
 }
 
-template <int H>
-__global__ void __launch_bounds__(256, 1)
+template <int H, bool NORMS>
+__global__ void __launch_bounds__(Cfg<H>::THREADS, 1)
 route_mfma_kernel(const uint16_t* __restrict__ Qr, int B, int T, int RTq, int P, int S,
-                  const uint16_t* __restrict__ Krbar, int64_t n_chunks, int64_t tiles_per_slice,
-                  uint32_t* __restrict__ chunk_enc) {
-  using TL = Tile<H>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a[TL::BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_b[TL::BYTES];
-  __shared__ __attribute__((aligned(16))) float lds_rk[H][TC];
+                  const uint16_t* __restrict__ Krbar, const float* __restrict__ knorm, int64_t n_chunks,
+                  int64_t tiles_per_slice, uint32_t* __restrict__ chunk_enc) {
+  using CF = Cfg<H>;
+  // each buffer = the chunk tile followed by its 1/|k| block: one LDS object per
+  // buffer, so the compiler's DMA tracking never has to order DMAs into
+  // different objects (it would wait for the whole prefetch otherwise)
+  constexpr int RKB = NORMS ? CF::RK_BYTES : 0;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a[CF::TILE_LDS + RKB];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_b[CF::TILE_LDS + RKB];
+  float* rk_a = reinterpret_cast<float*>(lds_a + CF::TILE_LDS);
+  float* rk_b = reinterpret_cast<float*>(lds_b + CF::TILE_LDS);
   __shared__ __attribute__((aligned(16))) float lds_rq[NW][H][RW];
+  __shared__ __attribute__((aligned(16))) f32x4_t lds_x[NW][64 * 4];
 
   // XCD-aware block mapping: workgroups are dealt round-robin to the 8 XCDs;
   // keep the P row blocks of one chunk slice on the same XCD so they share
@@ -176,31 +279,34 @@ route_mfma_kernel(const uint16_t* __restrict__ Qr, int B, int T, int RTq, int P,
   if (s >= S) return;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int half = lane >> 5, m = lane & 31;
-  const int rt = p * NW + wave;               // global row tile of this wave
+  const int rtl = wave % NW;                  // row tile within the block
+  const int hs = wave / NW;                   // head group
+  const int rt = p * NW + rtl;                // global row tile
   const bool wave_active = rt < B * RTq;
   const int b = wave_active ? rt / RTq : 0;
   const int t0 = (rt % RTq) * RW;
 
-  // --- resident router rows: A operands for all heads and k-steps
-  bf16x8_t qf[H][8];
+  // --- resident router rows: A operands for this wave's heads and all k-steps
+  bf16x8_t qf[CF::HPW][8];
   {
     const int t = t0 + m;
     const bool valid = wave_active && t < T;
     const uint16_t* qrow = Qr + ((int64_t)b * T + t) * H * D;
 #pragma unroll
-    for (int h = 0; h < H; ++h) {
+    for (int hh = 0; hh < CF::HPW; ++hh) {
+      const int h = hs * CF::HPW + hh;
       float ss = 0.f;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
         uint4 v = make_uint4(0, 0, 0, 0);
         if (valid) v = *reinterpret_cast<const uint4*>(qrow + h * D + 16 * ks + 8 * half);
-        qf[h][ks] = __builtin_bit_cast(bf16x8_t, v);
+        qf[hh][ks] = __builtin_bit_cast(bf16x8_t, v);
         ss = sq_norm_piece(v, ss);
       }
       ss += __shfl_xor(ss, 32);
-      if (half == 0) lds_rq[wave][h][m] = inv_norm(ss);
+      if (half == 0) lds_rq[rtl][h][m] = inv_norm(ss);
     }
   }
 
@@ -211,13 +317,34 @@ route_mfma_kernel(const uint16_t* __restrict__ Qr, int B, int T, int RTq, int P,
   if (tile_begin >= tile_end) return;
 
   const uint8_t* kr = reinterpret_cast<const uint8_t*>(Krbar);
-  issue_tile<H>(kr, n_chunks, tile_begin, lds_a, wave, lane);
-  for (int64_t tile = tile_begin; tile < tile_end; tile += 2) {
-    mfma_tile_step<H>(kr, n_chunks, tile, tile + 1 < tile_end, lds_a, lds_b, lds_rk, lds_rq[wave], qf,
-                      wave_active, b, t0, T, chunk_enc, tid, wave, lane);
+  f32x16_t sprev;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) sprev[i] = 0.f;
+  issue_tile<H, NORMS>(kr, knorm, n_chunks, tile_begin, lds_a, rk_a, wave, lane);
+  int64_t tile = tile_begin;
+  for (; tile < tile_end; tile += 2) {
+    mfma_tile_step<H, NORMS, 0>(kr, knorm, n_chunks, tile, tile > tile_begin, tile + 1 < tile_end, lds_a, rk_a,
+                                lds_b, rk_b, lds_rq[rtl], lds_x[rtl], qf, sprev, wave_active, hs, b, t0, T,
+                                chunk_enc, wave, lane);
     if (tile + 1 < tile_end)
-      mfma_tile_step<H>(kr, n_chunks, tile + 1, tile + 2 < tile_end, lds_b, lds_a, lds_rk, lds_rq[wave], qf,
-                        wave_active, b, t0, T, chunk_enc, tid, wave, lane);
+      mfma_tile_step<H, NORMS, 1>(kr, knorm, n_chunks, tile + 1, true, tile + 2 < tile_end, lds_b, rk_b, lds_a,
+                                  rk_a, lds_rq[rtl], lds_x[rtl], qf, sprev, wave_active, hs, b, t0, T,
+                                  chunk_enc, wave, lane);
+  }
+  if constexpr (CF::HS == 2) {
+    // finish the last tile: its parity decides which head group receives
+    const int64_t last = tile_end - 1;
+    const int par = (int)((last - tile_begin) & 1);
+    lds_barrier();
+    if (wave_active && hs == (par == 0 ? 0 : 1)) {
+      f32x4_t* x = lds_x[rtl] + lane;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4_t o = x[q4 * 64];
+        sprev[4 * q4] += o[0]; sprev[4 * q4 + 1] += o[1]; sprev[4 * q4 + 2] += o[2]; sprev[4 * q4 + 3] += o[3];
+      }
+      finish_tile(sprev, half, m, t0, T, b, last, n_chunks, 1.0f / H, chunk_enc);
+    }
   }
 }
 
@@ -348,6 +475,21 @@ route_valu_kernel(const uint16_t* __restrict__ Qr, int B, int T,
   }
 }
 
+// ------------------------------------------------------ stored key norms
+// 1/|Krbar[g, h]| for every chunk and head, fp32 [n_chunks, H]; one thread per
+// (chunk, head).  Built once per routing-key store (offline, beside the store)
+// so the online scan needs no norm pass of its own.
+__global__ void __launch_bounds__(256)
+krbar_norms_kernel(const uint16_t* __restrict__ Krbar, int64_t n_rows, float* __restrict__ out) {
+  const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= n_rows) return;
+  const uint4* p = reinterpret_cast<const uint4*>(Krbar + r * D);
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) ss = sq_norm_piece(p[i], ss);
+  out[r] = inv_norm_fast(ss);
+}
+
 // ------------------------------------------------------------ document max
 __global__ void __launch_bounds__(256)
 doc_reduce_kernel(const uint32_t* __restrict__ chunk_enc, int64_t n_chunks,
@@ -386,8 +528,8 @@ int num_cus() {
 }
 
 template <int H>
-int launch_route_h(const uint16_t* Qr, int B, int T, const uint16_t* Krbar, int64_t n_chunks,
-                   uint32_t* chunk_enc, hipStream_t stream) {
+int launch_route_h(const uint16_t* Qr, int B, int T, const uint16_t* Krbar, const float* inv_norm,
+                   int64_t n_chunks, uint32_t* chunk_enc, hipStream_t stream) {
   const int R = B * T;
   const int cus = num_cus();
   if (R <= VALU_MAX_ROWS) {
@@ -415,8 +557,16 @@ int launch_route_h(const uint16_t* Qr, int B, int T, const uint16_t* Krbar, int6
   // fill with the encoding's minimum: below every float, so atomicMax takes the first value
   hipLaunchKernelGGL(fill_u32_kernel, dim3(256), dim3(256), 0, stream, chunk_enc, (int64_t)B * n_chunks, 0u);
   MSA_CHECK_LAUNCH();
-  hipLaunchKernelGGL(route_mfma_kernel<H>, dim3((unsigned)grid), dim3(256), 0, stream, Qr, B, T, RTq, P,
-                     (int)S, Krbar, n_chunks, per, chunk_enc);
+  if constexpr (H >= 4) {
+    if (inv_norm) {
+      hipLaunchKernelGGL((route_mfma_kernel<H, true>), dim3((unsigned)grid), dim3(Cfg<H>::THREADS), 0, stream, Qr,
+                         B, T, RTq, P, (int)S, Krbar, inv_norm, n_chunks, per, chunk_enc);
+      MSA_CHECK_LAUNCH();
+      return MSA_OK;
+    }
+  }
+  hipLaunchKernelGGL((route_mfma_kernel<H, false>), dim3((unsigned)grid), dim3(Cfg<H>::THREADS), 0, stream, Qr, B,
+                     T, RTq, P, (int)S, Krbar, (const float*)nullptr, n_chunks, per, chunk_enc);
   MSA_CHECK_LAUNCH();
   return MSA_OK;
 }
@@ -428,17 +578,26 @@ size_t route_workspace(int B, int T, int H, int64_t n_chunks, int64_t n_docs) {
   return ((size_t)B * (size_t)n_chunks * sizeof(uint32_t) + 255) & ~(size_t)255;
 }
 
-int launch_route(const uint16_t* Qr, int B, int T, int H, const uint16_t* Krbar, int64_t n_chunks,
-                 const int64_t* doc_chunk_off, int64_t n_docs, const uint8_t* doc_exclude,
+int launch_krbar_norms(const uint16_t* Krbar, int64_t n_chunks, int H, float* inv_norm, hipStream_t stream) {
+  const int64_t rows = n_chunks * H;
+  if (rows == 0) return MSA_OK;
+  hipLaunchKernelGGL(krbar_norms_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream, Krbar, rows,
+                     inv_norm);
+  MSA_CHECK_LAUNCH();
+  return MSA_OK;
+}
+
+int launch_route(const uint16_t* Qr, int B, int T, int H, const uint16_t* Krbar, const float* inv_norm,
+                 int64_t n_chunks, const int64_t* doc_chunk_off, int64_t n_docs, const uint8_t* doc_exclude,
                  float* doc_scores, float* chunk_scores, void* workspace, hipStream_t stream) {
   uint32_t* chunk_enc = reinterpret_cast<uint32_t*>(workspace);
   int rc = MSA_OK;
   if (n_chunks > 0) {
     switch (H) {
-      case 1: rc = launch_route_h<1>(Qr, B, T, Krbar, n_chunks, chunk_enc, stream); break;
-      case 2: rc = launch_route_h<2>(Qr, B, T, Krbar, n_chunks, chunk_enc, stream); break;
-      case 4: rc = launch_route_h<4>(Qr, B, T, Krbar, n_chunks, chunk_enc, stream); break;
-      case 8: rc = launch_route_h<8>(Qr, B, T, Krbar, n_chunks, chunk_enc, stream); break;
+      case 1: rc = launch_route_h<1>(Qr, B, T, Krbar, inv_norm, n_chunks, chunk_enc, stream); break;
+      case 2: rc = launch_route_h<2>(Qr, B, T, Krbar, inv_norm, n_chunks, chunk_enc, stream); break;
+      case 4: rc = launch_route_h<4>(Qr, B, T, Krbar, inv_norm, n_chunks, chunk_enc, stream); break;
+      case 8: rc = launch_route_h<8>(Qr, B, T, Krbar, inv_norm, n_chunks, chunk_enc, stream); break;
       default: set_error("H=%d unsupported", H); return MSA_ERR_UNSUPPORTED;
     }
     if (rc != MSA_OK) return rc;

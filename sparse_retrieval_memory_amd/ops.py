@@ -71,8 +71,18 @@ def route_workspace_bytes(B, T, H, D, n_chunks, n_docs) -> int:
     return int(_lib.load().msa_route_workspace_bytes(B, T, H, D, n_chunks, n_docs))
 
 
+def krbar_inv_norms(Krbar, out=None, stream=None):
+    """msa_krbar_inv_norms: fp32 [n_chunks, H] reciprocal norms of a routing-key store."""
+    _bf16(Krbar, "Krbar"); _dev(Krbar, "Krbar")
+    n_chunks, H, D = Krbar.shape
+    if out is None:
+        out = torch.empty((n_chunks, H), dtype=torch.float32, device=Krbar.device)
+    _lib.call("msa_krbar_inv_norms", _p(Krbar), n_chunks, H, D, _p(out), _stream(stream))
+    return out
+
+
 def route_scores(Qr, Krbar, doc_chunk_off, doc_exclude=None, want_chunk_scores: bool = False,
-                 doc_scores=None, chunk_scores=None, ws=None, stream=None):
+                 doc_scores=None, chunk_scores=None, ws=None, krbar_inv_norm=None, stream=None):
     """msa_route_scores: doc_scores fp32 [B, n_docs] (and chunk_scores [B, n_chunks])."""
     _bf16(Qr, "Qr"); _bf16(Krbar, "Krbar"); _dev(Qr, "Qr")
     B, T, H, D = Qr.shape
@@ -89,7 +99,9 @@ def route_scores(Qr, Krbar, doc_chunk_off, doc_exclude=None, want_chunk_scores: 
     if doc_exclude is not None:
         assert doc_exclude.dtype in (torch.uint8, torch.bool) and doc_exclude.shape == (B, n_docs)
         doc_exclude = doc_exclude.contiguous()
-    _lib.call("msa_route_scores", _p(Qr), B, T, H, D, _p(Krbar), n_chunks, _p(doc_chunk_off), n_docs,
+    if krbar_inv_norm is not None:
+        assert krbar_inv_norm.dtype == torch.float32 and krbar_inv_norm.shape == (n_chunks, H)
+    _lib.call("msa_route_scores", _p(Qr), B, T, H, D, _p(Krbar), _p(krbar_inv_norm), n_chunks, _p(doc_chunk_off), n_docs,
               _p(doc_exclude), _p(doc_scores), _p(chunk_scores), _p(ws), ws.numel(), _stream(stream))
     if chunk_scores is not None:
         return doc_scores, chunk_scores

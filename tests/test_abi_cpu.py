@@ -31,17 +31,22 @@ def _code(name, *args):
 def test_route_validation():
     p = ctypes.c_void_p(16)
     E = _lib
-    assert _code("msa_route_scores", p, 0, 4, 8, 128, p, 10, p, 2, N, p, N, p, 1 << 20, N) == E.MSA_ERR_INVALID_ARG
-    assert _code("msa_route_scores", p, 1, 0, 8, 128, p, 10, p, 2, N, p, N, p, 1 << 20, N) == E.MSA_ERR_INVALID_ARG
-    assert _code("msa_route_scores", N, 1, 4, 8, 128, p, 10, p, 2, N, p, N, p, 1 << 20, N) == E.MSA_ERR_INVALID_ARG
-    assert _code("msa_route_scores", p, 1, 4, 8, 64, p, 10, p, 2, N, p, N, p, 1 << 20, N) == E.MSA_ERR_UNSUPPORTED
-    assert _code("msa_route_scores", p, 1, 4, 3, 128, p, 10, p, 2, N, p, N, p, 1 << 20, N) == E.MSA_ERR_UNSUPPORTED
-    assert _code("msa_route_scores", ctypes.c_void_p(18), 1, 4, 8, 128, p, 10, p, 2, N, p, N, p, 1 << 20, N) \
+    assert _code("msa_route_scores", p, 0, 4, 8, 128, p, N, 10, p, 2, N, p, N, p, 1 << 20, N) == E.MSA_ERR_INVALID_ARG
+    assert _code("msa_route_scores", p, 1, 0, 8, 128, p, N, 10, p, 2, N, p, N, p, 1 << 20, N) == E.MSA_ERR_INVALID_ARG
+    assert _code("msa_route_scores", N, 1, 4, 8, 128, p, N, 10, p, 2, N, p, N, p, 1 << 20, N) == E.MSA_ERR_INVALID_ARG
+    assert _code("msa_route_scores", p, 1, 4, 8, 64, p, N, 10, p, 2, N, p, N, p, 1 << 20, N) == E.MSA_ERR_UNSUPPORTED
+    assert _code("msa_route_scores", p, 1, 4, 3, 128, p, N, 10, p, 2, N, p, N, p, 1 << 20, N) == E.MSA_ERR_UNSUPPORTED
+    assert _code("msa_route_scores", ctypes.c_void_p(18), 1, 4, 8, 128, p, N, 10, p, 2, N, p, N, p, 1 << 20, N) \
         == E.MSA_ERR_INVALID_ARG                                   # misaligned
     need = _lib.load().msa_route_workspace_bytes(2, 4, 8, 128, 1000, 10)
     assert need >= 2 * 1000 * 4
-    assert _code("msa_route_scores", p, 2, 4, 8, 128, p, 1000, p, 10, N, p, N, p, need - 1, N) == E.MSA_ERR_WORKSPACE
+    assert _code("msa_route_scores", p, 2, 4, 8, 128, p, N, 1000, p, 10, N, p, N, p, need - 1, N) == E.MSA_ERR_WORKSPACE
     assert b"workspace" in _lib.load().msa_last_error()
+    # misaligned stored norms
+    assert _code("msa_route_scores", p, 2, 4, 8, 128, p, ctypes.c_void_p(20), 1000, p, 10, N, p, N, p, need, N) \
+        == E.MSA_ERR_INVALID_ARG
+    assert _code("msa_krbar_inv_norms", p, 10, 8, 96, p, N) == E.MSA_ERR_UNSUPPORTED
+    assert _code("msa_krbar_inv_norms", N, 10, 8, 128, p, N) == E.MSA_ERR_INVALID_ARG
 
 
 def test_topk_validation():

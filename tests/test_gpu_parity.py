@@ -52,10 +52,12 @@ def _route_case(B, T, H, n_docs, seed, lens=None):
     return Qr, Kr, off
 
 
-def _run_route(Qr, Kr, off, exclude=None):
-    doc, ch = ops.route_scores(dev_bits(Qr), dev_bits(Kr), torch.from_numpy(off).to(DEV),
+def _run_route(Qr, Kr, off, exclude=None, stored_norms=False):
+    kr = dev_bits(Kr)
+    nrm = ops.krbar_inv_norms(kr) if stored_norms else None
+    doc, ch = ops.route_scores(dev_bits(Qr), kr, torch.from_numpy(off).to(DEV),
                                None if exclude is None else torch.from_numpy(exclude.astype(np.uint8)).to(DEV),
-                               want_chunk_scores=True)
+                               want_chunk_scores=True, krbar_inv_norm=nrm)
     torch.cuda.synchronize()
     return doc.cpu().numpy().astype(np.float64), ch.cpu().numpy().astype(np.float64)
 
@@ -73,6 +75,29 @@ def test_route_scores_match_oracle(B, T, H):
     assert np.abs(doc - ref_doc).max() <= SCORE_TOL
 
 
+@pytest.mark.parametrize("B,T,H", [(1, 128, 8), (1, 16, 8), (1, 130, 8), (2, 64, 8), (5, 40, 4), (1, 260, 8),
+                                   (16, 64, 8), (1, 3, 8)])
+def test_route_with_stored_norms_matches_oracle(B, T, H):
+    announce("route-stored-norms", B, T, H)
+    Qr, Kr, off = _route_case(B, T, H, n_docs=401, seed=7 + B * 100 + T + H)
+    doc, ch = _run_route(Qr, Kr, off, stored_norms=True)
+    ref_ch, ref_doc = O.route(f64(Qr), f64(Kr), off)
+    assert np.abs(ch - ref_ch).max() <= SCORE_TOL
+    assert np.abs(doc - ref_doc).max() <= SCORE_TOL
+
+
+def test_krbar_inv_norms_match_oracle():
+    Qr, Kr, off = _route_case(1, 1, 8, n_docs=200, seed=3)
+    Kr = Kr.copy()
+    Kr[5, 3] = 0
+    announce("krbar-norms")
+    n = ops.krbar_inv_norms(dev_bits(Kr)).cpu().numpy().astype(np.float64)
+    ref_n = np.linalg.norm(f64(Kr), axis=-1)
+    ref = np.divide(1.0, ref_n, out=np.zeros_like(ref_n), where=ref_n > 0)
+    assert n[5, 3] == 0.0
+    assert np.abs(n - ref).max() <= 1e-6 * np.abs(ref).max()
+
+
 def test_route_exclusion_and_zero_vectors():
     Qr, Kr, off = _route_case(2, 40, 8, n_docs=97, seed=5)
     Kr = Kr.copy(); Qr = Qr.copy()
@@ -80,11 +105,12 @@ def test_route_exclusion_and_zero_vectors():
     Qr[1, 7, 5] = 0                    # zero query head
     excl = np.zeros((2, 97), bool); excl[0, [1, 50]] = True; excl[1, 96] = True
     announce("route-exclude")
-    doc, ch = _run_route(Qr, Kr, off, excl)
     ref_ch, ref_doc = O.route(f64(Qr), f64(Kr), off, excl)
-    assert np.all(doc[excl] == -np.inf)
-    assert np.abs(doc[~excl] - ref_doc[~excl]).max() <= SCORE_TOL
-    assert np.abs(ch - ref_ch).max() <= SCORE_TOL
+    for stored in (False, True):
+        doc, ch = _run_route(Qr, Kr, off, excl, stored_norms=stored)
+        assert np.all(doc[excl] == -np.inf)
+        assert np.abs(doc[~excl] - ref_doc[~excl]).max() <= SCORE_TOL
+        assert np.abs(ch - ref_ch).max() <= SCORE_TOL
 
 
 def test_route_valu_exclusion():
@@ -100,9 +126,10 @@ def test_route_valu_exclusion():
 def test_route_deterministic():
     Qr, Kr, off = _route_case(1, 128, 8, n_docs=3000, seed=8)
     announce("route-determinism")
-    a, _ = _run_route(Qr, Kr, off)
-    b, _ = _run_route(Qr, Kr, off)
-    assert np.array_equal(a.view(np.uint64), b.view(np.uint64))
+    for stored in (False, True):
+        a, _ = _run_route(Qr, Kr, off, stored_norms=stored)
+        b, _ = _run_route(Qr, Kr, off, stored_norms=stored)
+        assert np.array_equal(a.view(np.uint64), b.view(np.uint64))
 
 
 # ---------------------------------------------------------------------- top-k
