@@ -5,12 +5,12 @@
 // Each document becomes one 64-bit key (order-preserving score bits << 32 |
 // ~doc_id), so "score descending, ties to the lower id" is plain descending
 // integer order and every key is unique -- the selection is exact and
-// deterministic.  Two passes of the same block-level routine:
-//   pass 1: (blocks x B) workgroups each reduce a slice of documents to its k
-//           best keys;
-//   pass 2: one workgroup per query reduces the blocks' candidates to k.
-// The block routine keeps a running top-k in LDS and repeatedly bitonic-sorts
-// it together with the next SORT_N - k keys.
+// deterministic.  k <= 32 (the workloads use 4, 8 and 16): group maxima, then
+// only the winning groups are sorted (below).  Larger k: two passes of a
+// block-level routine -- pass 1: (blocks x B) workgroups each reduce a slice
+// of documents to its k best keys; pass 2: one workgroup per query reduces the
+// blocks' candidates to k -- which keeps a running top-k in LDS and
+// repeatedly bitonic-sorts it together with the next SORT_N - k keys.
 #include "msa_internal.h"
 
 namespace msa {
@@ -84,6 +84,177 @@ topk_pass2(const uint64_t* __restrict__ cand, int64_t n_cand, int k, int32_t* __
   }
 }
 
+// ---------------------------------------------------------------- small k
+// k <= 32.  Group the documents in runs of 64 (one wave) and take each group's
+// best key.  Every one of the k best documents sits in a group whose best key
+// is at least its own, and distinct such groups have distinct best keys, so
+// the k best documents lie inside the k groups with the largest best keys.
+//   pass 1 (many workgroups): group maxima by a wave-wide max of 64-bit keys;
+//   pass 2 (one workgroup per query): each wave extracts the top k of its
+//           share of the group maxima from registers, one wave merges the
+//           lists, then the k winning groups' 64 documents each are gathered
+//           and reduced the same way.  Extraction needs no barriers or LDS
+//           sorts, which is what makes it fast at these sizes.
+constexpr int GROUP = 64;
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const uint32_t lo = __shfl_xor((uint32_t)v, m), hi = __shfl_xor((uint32_t)(v >> 32), m);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__global__ void __launch_bounds__(256)
+topk_group_max(const float* __restrict__ scores, int64_t n_docs, int64_t n_groups, uint64_t* __restrict__ gmax) {
+  const int b = blockIdx.y;
+  const int64_t d = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  uint64_t key = d < n_docs ? make_key(scores[(int64_t)b * n_docs + d], (uint32_t)d) : 0ull;
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) {
+    const uint64_t o = shfl_xor_u64(key, m);
+    key = o > key ? o : key;
+  }
+  const int64_t g = d / GROUP;
+  if ((threadIdx.x & 63) == 0 && g < n_groups) gmax[(int64_t)b * n_groups + g] = key;
+}
+
+// One DPP step of a 64-bit unsigned max: both halves move with the same
+// pattern; lanes without a source read 0 (bound_ctrl), the identity here.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint64_t dpp_max_step(uint64_t v) {
+  const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, CTRL, ROWS, 0xF, true);
+  const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, CTRL, ROWS, 0xF, true);
+  const uint64_t o = ((uint64_t)ohi << 32) | olo;
+  return o > v ? o : v;
+}
+
+// Max over the wave, returned uniformly: prefix max inside each row of 16
+// (row_shr 1, 2, 4, 8), then rows 1 and 3 take lane 15 of the row below
+// (row_bcast 15) and rows 2 and 3 take lane 31 (row_bcast 31), so lane 63
+// holds the total, which is read out as a scalar.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = dpp_max_step<0x111, 0xF>(v);
+  v = dpp_max_step<0x112, 0xF>(v);
+  v = dpp_max_step<0x114, 0xF>(v);
+  v = dpp_max_step<0x118, 0xF>(v);
+  v = dpp_max_step<0x142, 0xA>(v);
+  v = dpp_max_step<0x143, 0xC>(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Wave-wide top-k by extraction: every lane holds R keys in registers (0 =
+// empty); k rounds of a 64-bit wave argmax, the winning lane drops its key.
+// Lane r ends with the r-th largest key (r < k).  No barriers, no LDS.
+template <int R>
+__device__ __forceinline__ uint64_t wave_extract_topk(uint64_t (&kv)[R], int k, int lane) {
+  uint64_t lm = 0;
+#pragma unroll
+  for (int j = 0; j < R; ++j) lm = kv[j] > lm ? kv[j] : lm;
+  uint64_t mine = 0;
+  for (int r = 0; r < k; ++r) {
+    const uint64_t m = wave_max_u64(lm);
+    if (lane == r) mine = m;
+    if (m != 0ull && lm == m) {               // keys are unique: exactly one lane owns m
+      lm = 0;
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        kv[j] = kv[j] == m ? 0ull : kv[j];
+        lm = kv[j] > lm ? kv[j] : lm;
+      }
+    }
+  }
+  return mine;
+}
+
+constexpr int P2_WAVES = 4;
+constexpr int RA = 16;                        // group keys per lane per sweep
+
+template <int RB>   // RB = ceil(k / P2_WAVES) winning groups per wave in the gather step
+__global__ void __launch_bounds__(64 * P2_WAVES)
+topk_from_groups(const float* __restrict__ scores, const uint64_t* __restrict__ gmax, int64_t n_docs,
+                 int64_t n_groups, int k, int32_t* __restrict__ top_idx, float* __restrict__ top_scores) {
+  __shared__ uint64_t lists[P2_WAVES][64];
+  __shared__ uint64_t groups[64];
+  const int b = blockIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const uint64_t* gm = gmax + (int64_t)b * n_groups;
+
+  // A: each wave keeps a running top-k over its share of the group maxima
+  const int64_t per = (n_groups + P2_WAVES - 1) / P2_WAVES;
+  const int64_t g0 = wave * per;
+  const int64_t g1 = (g0 + per < n_groups) ? g0 + per : n_groups;
+  uint64_t run = 0;                           // lane r < k: the wave's r-th best so far
+  for (int64_t base = g0; base < g1 || base == g0; base += 64 * (RA - 1)) {
+    uint64_t kv[RA];
+#pragma unroll
+    for (int j = 0; j < RA - 1; ++j) {
+      const int64_t x = base + (int64_t)j * 64 + lane;
+      kv[j] = x < g1 ? gm[x] : 0ull;
+    }
+    kv[RA - 1] = run;
+    run = wave_extract_topk<RA>(kv, k, lane);
+    if (base + 64 * (RA - 1) >= g1) break;
+  }
+  lists[wave][lane] = run;
+  __syncthreads();
+  if (wave == 0) {
+    uint64_t kv[P2_WAVES];
+#pragma unroll
+    for (int w = 0; w < P2_WAVES; ++w) kv[w] = lists[w][lane];
+    groups[lane] = wave_extract_topk<P2_WAVES>(kv, k, lane);
+  }
+  __syncthreads();
+
+  // B: the k winning groups' documents; wave w takes groups w, w + P2_WAVES, ...
+  const float* row = scores + (int64_t)b * n_docs;
+  uint64_t kv[RB];
+#pragma unroll
+  for (int j = 0; j < RB; ++j) {
+    const int r = wave + j * P2_WAVES;
+    uint64_t key = 0;
+    if (r < k && groups[r] != 0ull) {
+      const uint32_t best_doc = 0xFFFFFFFFu - (uint32_t)(groups[r] & 0xFFFFFFFFull);
+      const int64_t d = (int64_t)(best_doc / GROUP) * GROUP + lane;
+      if (d < n_docs) key = make_key(row[d], (uint32_t)d);
+    }
+    kv[j] = key;
+  }
+  const uint64_t best = wave_extract_topk<RB>(kv, k, lane);
+  __syncthreads();
+  lists[wave][lane] = best;
+  __syncthreads();
+  if (wave == 0) {
+    uint64_t kw[P2_WAVES];
+#pragma unroll
+    for (int w = 0; w < P2_WAVES; ++w) kw[w] = lists[w][lane];
+    const uint64_t key = wave_extract_topk<P2_WAVES>(kw, k, lane);
+    if (lane < k) {
+      top_idx[(int64_t)b * k + lane] = (int32_t)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFull));
+      top_scores[(int64_t)b * k + lane] = dec_f32((uint32_t)(key >> 32));
+    }
+  }
+}
+
+int launch_topk_small(const float* doc_scores, int B, int64_t n_docs, int k, int32_t* top_idx, float* top_scores,
+                      uint64_t* gmax, hipStream_t stream) {
+  const int64_t n_groups = (n_docs + GROUP - 1) / GROUP;
+  hipLaunchKernelGGL(topk_group_max, dim3((unsigned)((n_docs + 255) / 256), (unsigned)B), dim3(256), 0, stream,
+                     doc_scores, n_docs, n_groups, gmax);
+  MSA_CHECK_LAUNCH();
+  const int rb = (k + P2_WAVES - 1) / P2_WAVES;
+#define MSA_TOPK_RB(RBV)                                                                                        \
+  hipLaunchKernelGGL((topk_from_groups<RBV>), dim3((unsigned)B), dim3(64 * P2_WAVES), 0, stream, doc_scores, gmax, \
+                     n_docs, n_groups, k, top_idx, top_scores)
+  if (rb <= 1) MSA_TOPK_RB(1);
+  else if (rb <= 2) MSA_TOPK_RB(2);
+  else if (rb <= 4) MSA_TOPK_RB(4);
+  else MSA_TOPK_RB(8);
+#undef MSA_TOPK_RB
+  MSA_CHECK_LAUNCH();
+  return MSA_OK;
+}
+
 int64_t pass1_blocks(int64_t n_docs, int k) {
   const int64_t piece = SORT_N - k;
   return (n_docs + piece - 1) / piece;
@@ -93,6 +264,7 @@ int64_t pass1_blocks(int64_t n_docs, int k) {
 
 size_t topk_workspace(int B, int64_t n_docs, int k) {
   if (k < 1 || k > KMAX) return 0;
+  if (k <= 32) return (size_t)B * (size_t)((n_docs + GROUP - 1) / GROUP) * sizeof(uint64_t);
   return (size_t)B * (size_t)pass1_blocks(n_docs, k) * (size_t)k * sizeof(uint64_t);
 }
 
@@ -102,9 +274,10 @@ int launch_topk(const float* doc_scores, int B, int64_t n_docs, int k, int32_t* 
     set_error("k=%d exceeds the supported maximum %d", k, KMAX);
     return MSA_ERR_UNSUPPORTED;
   }
+  uint64_t* cand = reinterpret_cast<uint64_t*>(workspace);
+  if (k <= 32) return launch_topk_small(doc_scores, B, n_docs, k, top_idx, top_scores, cand, stream);
   const int64_t nb = pass1_blocks(n_docs, k);
   const int64_t slice = SORT_N - k;
-  uint64_t* cand = reinterpret_cast<uint64_t*>(workspace);
   hipLaunchKernelGGL(topk_pass1, dim3((unsigned)nb, (unsigned)B), dim3(THREADS), 0, stream, doc_scores,
                      n_docs, k, slice, cand);
   MSA_CHECK_LAUNCH();

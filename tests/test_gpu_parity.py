@@ -134,7 +134,9 @@ def test_route_deterministic():
 
 # ---------------------------------------------------------------------- top-k
 @pytest.mark.parametrize("B,n,k", [(1, 64, 4), (1, 1000, 16), (16, 20000, 16), (1, 200000, 16), (4, 20000, 8),
-                                   (1, 7, 7), (3, 5, 1), (2, 4097, 1024), (1, 2049, 2), (2, 100, 100)])
+                                   (1, 7, 7), (3, 5, 1), (2, 4097, 1024), (1, 2049, 2), (2, 100, 100),
+                                   (1, 70000, 32), (2, 40000, 17), (3, 33000, 5), (1, 32768, 16), (1, 32769, 3),
+                                   (2, 513, 33), (1, 1, 1)])
 def test_topk_matches_oracle(B, n, k):
     announce("topk", B, n, k)
     r = np.random.default_rng(B * 7 + n + k)
