@@ -12,6 +12,7 @@
  *   msa_topk_docs           online: the k most relevant documents
  *   msa_fetch_docs          online: copy the selected content KV from pinned host
  *   msa_gather_docs         online: same, as one device kernel reading mapped host memory
+ *   msa_append_router_rows  interleave: the next round's router rows and exclusions
  *   msa_sparse_attn_decode  generation: GQA attention over [memory ++ local KV]
  *
  * Conventions (every call):
@@ -193,6 +194,37 @@ int msa_gather_docs(const int32_t* top_idx, int B, int k,
                     const uint16_t* host_store, const int64_t* doc_chunk_off, int64_t n_docs,
                     int H, int D, uint16_t* staging, int Mmax, int32_t* mem_len,
                     hipStream_t stream);
+
+/*
+ * msa_append_router_rows -- query preparation for the next Memory Interleave
+ * round.
+ *
+ * Defined by: medium write-up sec. 4C and b-lab.team summary sec. 3 (the
+ * documents retrieved in one round become part of the next round's query).
+ * Reading: the next round routes with the original router rows followed by
+ * the pooled router keys (all heads) of every chunk of every document
+ * retrieved so far, in retrieval order, and never selects those documents
+ * again.
+ *
+ * For each query b: rows[b, 0..T0) = Qr[b]; then, for i = 0..n_ids-1, the
+ * rows Krbar[g] of document ids[b, i]'s chunks g in order; the remaining rows
+ * up to T_out repeat rows[b, 0] (a repeated row changes no token max, so the
+ * scores of the padded batch equal those of each query's own rows).  Rows
+ * beyond T_out are dropped: size T_out = T0 + max_b (chunks of b's ids).
+ *
+ *   Qr             bf16 [B, T0, H, D] (device)
+ *   Krbar          bf16 [n_chunks, H, D] (device)
+ *   doc_chunk_off  int64 [n_docs+1] (device)
+ *   ids            int32 [B, n_ids] (device); ids outside [0, n_docs) are skipped
+ *   rows           bf16 [B, T_out, H, D] (device) out
+ *   n_rows         int32 [B] (device) out, or NULL: T0 + the listed chunks, capped at T_out
+ *   doc_exclude    uint8 [B, n_docs] (device) or NULL: set to 1 for every listed document
+ * D must be 128.  Asynchronous on `stream`.
+ */
+int msa_append_router_rows(const uint16_t* Qr, int B, int T0, int H, int D,
+                           const uint16_t* Krbar, const int64_t* doc_chunk_off, int64_t n_docs,
+                           const int32_t* ids, int n_ids, int T_out,
+                           uint16_t* rows, int32_t* n_rows, uint8_t* doc_exclude, hipStream_t stream);
 
 /*
  * msa_sparse_attn_decode -- GQA attention over [pooled memory ++ causal local KV].

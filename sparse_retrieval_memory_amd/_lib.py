@@ -41,6 +41,7 @@ SIGNATURES = {
     "msa_topk_docs": (c_i, [c_p, c_i, c_i64, c_i, c_p, c_p, c_p, c_sz, c_p]),
     "msa_fetch_docs": (c_i, [c_p, c_i, c_i, c_p, c_p, c_i64, c_i, c_i, c_p, c_i, c_p, c_p, c_p]),
     "msa_gather_docs": (c_i, [c_p, c_i, c_i, c_p, c_p, c_i64, c_i, c_i, c_p, c_i, c_p, c_p]),
+    "msa_append_router_rows": (c_i, [c_p, c_i, c_i, c_i, c_i, c_p, c_p, c_i64, c_p, c_i, c_i, c_p, c_p, c_p, c_p]),
     "msa_sparse_attn_decode": (c_i, [c_p, c_i, c_i, c_i, c_i, c_p, c_p, c_i, c_i, c_p, c_p, c_i64,
                                      c_i, c_p, c_i, c_d, c_f, c_p, c_p]),
 }

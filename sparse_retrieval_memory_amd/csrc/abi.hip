@@ -178,6 +178,19 @@ int msa_gather_docs(const int32_t* top_idx, int B, int k, const uint16_t* host_s
   return msa::launch_gather(top_idx, B, k, host_store, doc_chunk_off, n_docs, H, staging, Mmax, mem_len, stream);
 }
 
+int msa_append_router_rows(const uint16_t* Qr, int B, int T0, int H, int D, const uint16_t* Krbar,
+                           const int64_t* doc_chunk_off, int64_t n_docs, const int32_t* ids, int n_ids, int T_out,
+                           uint16_t* rows, int32_t* n_rows, uint8_t* doc_exclude, hipStream_t stream) {
+  msa::clear_error();
+  MSA_CHECK_ARG(B >= 1 && B <= 65535 && T0 >= 1 && H >= 1 && n_docs >= 1 && n_ids >= 0, "bad sizes");
+  MSA_CHECK_ARG(T_out >= T0 && T_out <= (1 << 24), "need T0 <= T_out <= 2^24");
+  MSA_CHECK_SUPPORTED(D == 128, "D=%d unsupported (D must be 128)", D);
+  MSA_CHECK_ARG(Qr && Krbar && doc_chunk_off && rows && (n_ids == 0 || ids), "null pointer");
+  MSA_CHECK_ARG(aligned16(Qr) && aligned16(Krbar) && aligned16(rows), "Qr, Krbar and rows must be 16-byte aligned");
+  return msa::launch_append_rows(Qr, B, T0, H, Krbar, doc_chunk_off, n_docs, ids, n_ids, T_out, rows, n_rows,
+                                 doc_exclude, stream);
+}
+
 int msa_sparse_attn_decode(const uint16_t* Q, int B, int Tq, int Hq, int D, const uint16_t* Kloc,
                            const uint16_t* Vloc, int Tl, int Hkv, const uint16_t* Kmem, const uint16_t* Vmem,
                            int64_t mem_entry_stride, int Mmax, const int32_t* mem_len, int rope_offset,

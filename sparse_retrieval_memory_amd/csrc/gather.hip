@@ -48,7 +48,65 @@ gather_kernel(const int32_t* __restrict__ top_idx, int k, const uint16_t* __rest
   for (int64_t i = threadIdx.x; i < vecs; i += THREADS) dst[i] = src[i];
 }
 
+// Router rows for the next interleave round (medium write-up sec. 4C and
+// b-lab.team summary sec. 3: documents retrieved in one round become part of
+// the next round's query).  rows[b] = Qr[b] (T0 rows), then the pooled router
+// keys of every chunk of ids[b, 0..n_ids) in that order, then row 0 repeated
+// up to T_out rows: a repeated row leaves every token max, hence every score,
+// unchanged.  One workgroup per (output row, query) copies one 2 KB row; the
+// first workgroup of each query also records the row count and marks the
+// listed documents as excluded (they are not selected again).
+__global__ void __launch_bounds__(128)
+append_rows_kernel(const uint16_t* __restrict__ Qr, int T0, const uint16_t* __restrict__ Krbar,
+                   const int64_t* __restrict__ doc_chunk_off, int64_t n_docs, const int32_t* __restrict__ ids,
+                   int n_ids, int T_out, int64_t row_elems, uint16_t* __restrict__ rows,
+                   int32_t* __restrict__ n_rows, uint8_t* __restrict__ doc_exclude) {
+  const int t = blockIdx.x, b = blockIdx.y;
+  const int32_t* my_ids = ids + (int64_t)b * n_ids;
+  const uint16_t* src = Qr + (int64_t)b * T0 * row_elems;            // row 0 of this query
+  int64_t total = 0;
+  if (t < T0) {
+    src = Qr + ((int64_t)b * T0 + t) * row_elems;
+  } else {
+    const int64_t want = t - T0;                                        // chunk rank among the listed docs
+    for (int i = 0; i < n_ids; ++i) {
+      const int32_t d = my_ids[i];
+      if (d < 0 || d >= n_docs) continue;
+      const int64_t g0 = doc_chunk_off[d], n = doc_chunk_off[d + 1] - g0;
+      if (want >= total && want < total + n) src = Krbar + (g0 + (want - total)) * row_elems;
+      total += n;
+    }
+  }
+  if (t == 0) {
+    if (threadIdx.x == 0) {
+      int64_t all = 0;
+      for (int i = 0; i < n_ids; ++i) {
+        const int32_t d = my_ids[i];
+        if (d >= 0 && d < n_docs) all += doc_chunk_off[d + 1] - doc_chunk_off[d];
+      }
+      if (n_rows) n_rows[b] = (int32_t)(T0 + all < T_out ? T0 + all : T_out);
+    }
+    if (doc_exclude)
+      for (int i = threadIdx.x; i < n_ids; i += blockDim.x) {
+        const int32_t d = my_ids[i];
+        if (d >= 0 && d < n_docs) doc_exclude[(int64_t)b * n_docs + d] = 1;
+      }
+  }
+  const uint4* s4 = reinterpret_cast<const uint4*>(src);
+  uint4* d4 = reinterpret_cast<uint4*>(rows + ((int64_t)b * T_out + t) * row_elems);
+  for (int64_t i = threadIdx.x; i < row_elems / 8; i += blockDim.x) d4[i] = s4[i];
+}
+
 }  // namespace
+
+int launch_append_rows(const uint16_t* Qr, int B, int T0, int H, const uint16_t* Krbar,
+                       const int64_t* doc_chunk_off, int64_t n_docs, const int32_t* ids, int n_ids, int T_out,
+                       uint16_t* rows, int32_t* n_rows, uint8_t* doc_exclude, hipStream_t stream) {
+  hipLaunchKernelGGL(append_rows_kernel, dim3((unsigned)T_out, (unsigned)B), dim3(128), 0, stream, Qr, T0, Krbar,
+                     doc_chunk_off, n_docs, ids, n_ids, T_out, (int64_t)H * 128, rows, n_rows, doc_exclude);
+  MSA_CHECK_LAUNCH();
+  return MSA_OK;
+}
 
 int launch_gather(const int32_t* top_idx, int B, int k, const uint16_t* host_store,
                   const int64_t* doc_chunk_off, int64_t n_docs, int H, uint16_t* staging, int Mmax,

@@ -126,6 +126,9 @@ int launch_attn(const uint16_t* Q, int B, int Tq, int Hq, const uint16_t* Kloc, 
                 int Tl, int Hkv, const uint16_t* Kmem, const uint16_t* Vmem, int64_t mem_entry_stride,
                 int Mmax, const int32_t* mem_len, int rope_offset, double rope_base, float scale,
                 float* O, hipStream_t stream);
+int launch_append_rows(const uint16_t* Qr, int B, int T0, int H, const uint16_t* Krbar,
+                       const int64_t* doc_chunk_off, int64_t n_docs, const int32_t* ids, int n_ids, int T_out,
+                       uint16_t* rows, int32_t* n_rows, uint8_t* doc_exclude, hipStream_t stream);
 int launch_gather(const int32_t* top_idx, int B, int k, const uint16_t* host_store,
                   const int64_t* doc_chunk_off, int64_t n_docs, int H, uint16_t* staging, int Mmax,
                   int32_t* mem_len, hipStream_t stream);

@@ -116,36 +116,38 @@ topk_group_max(const float* __restrict__ scores, int64_t n_docs, int64_t n_group
   if ((threadIdx.x & 63) == 0 && g < n_groups) gmax[(int64_t)b * n_groups + g] = key;
 }
 
-// One DPP step of a 64-bit unsigned max: both halves move with the same
-// pattern; lanes without a source read 0 (bound_ctrl), the identity here.
-template <int CTRL, int ROWS>
-__device__ __forceinline__ uint64_t dpp_max_step(uint64_t v) {
-  const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-  const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, CTRL, ROWS, 0xF, true);
-  const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, CTRL, ROWS, 0xF, true);
-  const uint64_t o = ((uint64_t)ohi << 32) | olo;
-  return o > v ? o : v;
+// Max over the wave of a 32-bit value, returned uniformly: prefix max inside
+// each row of 16 (row_shr 1, 2, 4, 8), then rows 1 and 3 take lane 15 of the
+// row below (row_bcast 15) and rows 2 and 3 take lane 31 (row_bcast 31), so
+// lane 63 holds the total.  Lanes without a source read 0, the identity.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  uint32_t o;
+  o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true); v = o > v ? o : v;
+  o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true); v = o > v ? o : v;
+  o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true); v = o > v ? o : v;
+  o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true); v = o > v ? o : v;
+  o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x142, 0xA, 0xF, true); v = o > v ? o : v;
+  o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x143, 0xC, 0xF, true); v = o > v ? o : v;
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
-// Max over the wave, returned uniformly: prefix max inside each row of 16
-// (row_shr 1, 2, 4, 8), then rows 1 and 3 take lane 15 of the row below
-// (row_bcast 15) and rows 2 and 3 take lane 31 (row_bcast 31), so lane 63
-// holds the total, which is read out as a scalar.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  v = dpp_max_step<0x111, 0xF>(v);
-  v = dpp_max_step<0x112, 0xF>(v);
-  v = dpp_max_step<0x114, 0xF>(v);
-  v = dpp_max_step<0x118, 0xF>(v);
-  v = dpp_max_step<0x142, 0xA>(v);
-  v = dpp_max_step<0x143, 0xC>(v);
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
-  return ((uint64_t)hi << 32) | lo;
+// Largest 64-bit key of the wave: the high words (the score) decide unless
+// several lanes share the largest one, then the low words (the id) do.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t v) {
+  const uint32_t hi = (uint32_t)(v >> 32), lo = (uint32_t)v;
+  const uint32_t mh = wave_max_u32(hi);
+  const uint64_t tie = __ballot(hi == mh);
+  uint32_t ml;
+  if (__popcll(tie) == 1)
+    ml = (uint32_t)__builtin_amdgcn_readlane((int)lo, __ffsll((unsigned long long)tie) - 1);
+  else
+    ml = wave_max_u32(hi == mh ? lo : 0u);
+  return ((uint64_t)mh << 32) | ml;
 }
 
 // Wave-wide top-k by extraction: every lane holds R keys in registers (0 =
-// empty); k rounds of a 64-bit wave argmax, the winning lane drops its key.
-// Lane r ends with the r-th largest key (r < k).  No barriers, no LDS.
+// empty); k rounds of a wave argmax, the winning lane drops its key.  Lane r
+// ends with the r-th largest key (r < k).  No barriers, no LDS.
 template <int R>
 __device__ __forceinline__ uint64_t wave_extract_topk(uint64_t (&kv)[R], int k, int lane) {
   uint64_t lm = 0;
@@ -153,7 +155,7 @@ __device__ __forceinline__ uint64_t wave_extract_topk(uint64_t (&kv)[R], int k, 
   for (int j = 0; j < R; ++j) lm = kv[j] > lm ? kv[j] : lm;
   uint64_t mine = 0;
   for (int r = 0; r < k; ++r) {
-    const uint64_t m = wave_max_u64(lm);
+    const uint64_t m = wave_max_key(lm);
     if (lane == r) mine = m;
     if (m != 0ull && lm == m) {               // keys are unique: exactly one lane owns m
       lm = 0;
@@ -167,10 +169,23 @@ __device__ __forceinline__ uint64_t wave_extract_topk(uint64_t (&kv)[R], int k, 
   return mine;
 }
 
-constexpr int P2_WAVES = 4;
-constexpr int RA = 16;                        // group keys per lane per sweep
+constexpr int P2_WAVES = 16;
+constexpr int RA = 5;                         // group keys per lane per sweep (4 new + the running list)
 
-template <int RB>   // RB = ceil(k / P2_WAVES) winning groups per wave in the gather step
+// Top k of P2_WAVES lists of k keys each (lists[w][r], r < k) by one wave;
+// key x = w * k + r sits in lane x % 64, slot x / 64 (RM = ceil(16 k / 64)).
+template <int RM>
+__device__ __forceinline__ uint64_t merge_lists(const uint64_t (*lists)[64], int k, int lane) {
+  uint64_t kv[RM];
+#pragma unroll
+  for (int j = 0; j < RM; ++j) {
+    const int x = j * 64 + lane;
+    kv[j] = x < P2_WAVES * k ? lists[x / k][x % k] : 0ull;
+  }
+  return wave_extract_topk<RM>(kv, k, lane);
+}
+
+template <int RM, int RB>   // RM: merge keys per lane; RB = ceil(k / P2_WAVES) winning groups per wave
 __global__ void __launch_bounds__(64 * P2_WAVES)
 topk_from_groups(const float* __restrict__ scores, const uint64_t* __restrict__ gmax, int64_t n_docs,
                  int64_t n_groups, int k, int32_t* __restrict__ top_idx, float* __restrict__ top_scores) {
@@ -185,7 +200,7 @@ topk_from_groups(const float* __restrict__ scores, const uint64_t* __restrict__ 
   const int64_t g0 = wave * per;
   const int64_t g1 = (g0 + per < n_groups) ? g0 + per : n_groups;
   uint64_t run = 0;                           // lane r < k: the wave's r-th best so far
-  for (int64_t base = g0; base < g1 || base == g0; base += 64 * (RA - 1)) {
+  for (int64_t base = g0;; base += 64 * (RA - 1)) {
     uint64_t kv[RA];
 #pragma unroll
     for (int j = 0; j < RA - 1; ++j) {
@@ -198,12 +213,7 @@ topk_from_groups(const float* __restrict__ scores, const uint64_t* __restrict__ 
   }
   lists[wave][lane] = run;
   __syncthreads();
-  if (wave == 0) {
-    uint64_t kv[P2_WAVES];
-#pragma unroll
-    for (int w = 0; w < P2_WAVES; ++w) kv[w] = lists[w][lane];
-    groups[lane] = wave_extract_topk<P2_WAVES>(kv, k, lane);
-  }
+  if (wave == 0) groups[lane] = merge_lists<RM>(lists, k, lane);
   __syncthreads();
 
   // B: the k winning groups' documents; wave w takes groups w, w + P2_WAVES, ...
@@ -221,14 +231,11 @@ topk_from_groups(const float* __restrict__ scores, const uint64_t* __restrict__ 
     kv[j] = key;
   }
   const uint64_t best = wave_extract_topk<RB>(kv, k, lane);
-  __syncthreads();
+  __syncthreads();                            // everyone has read `groups` and the lists
   lists[wave][lane] = best;
   __syncthreads();
   if (wave == 0) {
-    uint64_t kw[P2_WAVES];
-#pragma unroll
-    for (int w = 0; w < P2_WAVES; ++w) kw[w] = lists[w][lane];
-    const uint64_t key = wave_extract_topk<P2_WAVES>(kw, k, lane);
+    const uint64_t key = merge_lists<RM>(lists, k, lane);
     if (lane < k) {
       top_idx[(int64_t)b * k + lane] = (int32_t)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFull));
       top_scores[(int64_t)b * k + lane] = dec_f32((uint32_t)(key >> 32));
@@ -242,15 +249,14 @@ int launch_topk_small(const float* doc_scores, int B, int64_t n_docs, int k, int
   hipLaunchKernelGGL(topk_group_max, dim3((unsigned)((n_docs + 255) / 256), (unsigned)B), dim3(256), 0, stream,
                      doc_scores, n_docs, n_groups, gmax);
   MSA_CHECK_LAUNCH();
-  const int rb = (k + P2_WAVES - 1) / P2_WAVES;
-#define MSA_TOPK_RB(RBV)                                                                                        \
-  hipLaunchKernelGGL((topk_from_groups<RBV>), dim3((unsigned)B), dim3(64 * P2_WAVES), 0, stream, doc_scores, gmax, \
-                     n_docs, n_groups, k, top_idx, top_scores)
-  if (rb <= 1) MSA_TOPK_RB(1);
-  else if (rb <= 2) MSA_TOPK_RB(2);
-  else if (rb <= 4) MSA_TOPK_RB(4);
-  else MSA_TOPK_RB(8);
-#undef MSA_TOPK_RB
+#define MSA_TOPK_GROUPS(RMV, RBV)                                                                        \
+  hipLaunchKernelGGL((topk_from_groups<RMV, RBV>), dim3((unsigned)B), dim3(64 * P2_WAVES), 0, stream, doc_scores, \
+                     gmax, n_docs, n_groups, k, top_idx, top_scores)
+  if (k <= 4) MSA_TOPK_GROUPS(1, 1);
+  else if (k <= 8) MSA_TOPK_GROUPS(2, 1);
+  else if (k <= 16) MSA_TOPK_GROUPS(4, 1);
+  else MSA_TOPK_GROUPS(8, 2);
+#undef MSA_TOPK_GROUPS
   MSA_CHECK_LAUNCH();
   return MSA_OK;
 }

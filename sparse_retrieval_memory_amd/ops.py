@@ -141,6 +141,10 @@ def fetch_docs(top_idx_host, host_store, doc_chunk_off_host, staging, Mmax: int,
     H, D = host_store.shape[-2], host_store.shape[-1]
     mem_len = torch.empty(B, dtype=torch.int32)
     side = side_stream if side_stream is not None else torch.cuda.current_stream()
+    if done_event is not None and not done_event.cuda_event:
+        # torch creates the underlying event on its first record: create it here so the
+        # library can record it after the copies (an absent event would order nothing)
+        done_event.record(side)
     ev = ctypes.c_void_p(0 if done_event is None else done_event.cuda_event)
     _lib.call("msa_fetch_docs", _p(top_idx_host), B, k, _p(host_store), _p(doc_chunk_off_host), n_docs, H, D,
               _p(staging), Mmax, _p(mem_len), ctypes.c_void_p(side.cuda_stream), ev)
@@ -157,6 +161,27 @@ def gather_docs(top_idx, host_store, doc_chunk_off, staging, Mmax: int, mem_len=
     _lib.call("msa_gather_docs", _p(top_idx), B, k, _p(host_store), _p(doc_chunk_off), n_docs, H, D,
               _p(staging), Mmax, _p(mem_len), _stream(stream))
     return mem_len
+
+
+def append_router_rows(Qr, Krbar, doc_chunk_off, ids, T_out: int, rows=None, n_rows=None, doc_exclude=None,
+                       stream=None):
+    """msa_append_router_rows: the next interleave round's router rows bf16 [B, T_out, H, D].
+
+    Also marks ``ids`` in ``doc_exclude`` (uint8 [B, n_docs]) when given; returns (rows, n_rows)."""
+    _bf16(Qr, "Qr"); _bf16(Krbar, "Krbar"); _dev(Qr, "Qr")
+    B, T0, H, D = Qr.shape
+    n_docs = doc_chunk_off.numel() - 1
+    assert ids.dtype == torch.int32 and ids.is_cuda and ids.shape[0] == B
+    ids = ids.contiguous()
+    if rows is None:
+        rows = torch.empty((B, T_out, H, D), dtype=Qr.dtype, device=Qr.device)
+    if n_rows is None:
+        n_rows = torch.empty(B, dtype=torch.int32, device=Qr.device)
+    if doc_exclude is not None:
+        assert doc_exclude.dtype == torch.uint8 and doc_exclude.shape == (B, n_docs) and doc_exclude.is_contiguous()
+    _lib.call("msa_append_router_rows", _p(Qr), B, T0, H, D, _p(Krbar), _p(doc_chunk_off), n_docs, _p(ids),
+              ids.shape[1], T_out, _p(rows), _p(n_rows), _p(doc_exclude), _stream(stream))
+    return rows, n_rows
 
 
 def sparse_attn_decode(Q, Kloc, Vloc, Kmem, Vmem, mem_entry_stride: int, Mmax: int, mem_len,

@@ -16,7 +16,7 @@ def test_exports_every_declared_symbol():
     lib = _lib.load()
     names = _lib.declared_symbols()
     assert {"msa_pool_chunks", "msa_route_scores", "msa_topk_docs", "msa_sparse_attn_decode",
-            "msa_fetch_docs", "msa_gather_docs"} <= set(names)
+            "msa_fetch_docs", "msa_gather_docs", "msa_append_router_rows"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     assert set(_lib.SIGNATURES) == set(names)
@@ -71,6 +71,18 @@ def test_pool_and_attention_validation():
     assert _code("msa_sparse_attn_decode", *args(Tq=5)) == E.MSA_ERR_INVALID_ARG
     assert _code("msa_sparse_attn_decode", *args(Hq=30)) == E.MSA_ERR_INVALID_ARG
     assert _code("msa_sparse_attn_decode", *args(D=64)) == E.MSA_ERR_UNSUPPORTED
+
+
+def test_append_router_rows_validation():
+    p = ctypes.c_void_p(16)
+    E = _lib
+    args = lambda B=1, T0=4, H=8, D=128, n_ids=2, T_out=20, qr=p: (qr, B, T0, H, D, p, p, 10, p, n_ids, T_out, p, N, N,
+                                                                    N)
+    assert _code("msa_append_router_rows", *args(T_out=3)) == E.MSA_ERR_INVALID_ARG      # T_out < T0
+    assert _code("msa_append_router_rows", *args(D=64)) == E.MSA_ERR_UNSUPPORTED
+    assert _code("msa_append_router_rows", *args(B=0)) == E.MSA_ERR_INVALID_ARG
+    assert _code("msa_append_router_rows", *args(qr=N)) == E.MSA_ERR_INVALID_ARG
+    assert _code("msa_append_router_rows", *args(qr=ctypes.c_void_p(24))) == E.MSA_ERR_INVALID_ARG
 
 
 def test_fetch_validation_host_side():

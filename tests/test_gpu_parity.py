@@ -228,6 +228,7 @@ def test_fetch_and_gather_assemble_rank_order():
     side = torch.cuda.Stream()
     ev = torch.cuda.Event()
     ml = ops.fetch_docs(torch.from_numpy(top), store, torch.from_numpy(off), staging, Mmax, side, ev)
+    assert ev.cuda_event, "the completion event must exist so that it orders the copies"
     ev.synchronize()
     st = host_bits(staging)
     for b in range(2):

@@ -1,0 +1,319 @@
+"""The path at the workloads' full sizes on the GPU, in the launch
+configurations the benchmark uses, against the oracle: in full where the oracle
+finishes in seconds, otherwise on sampled documents and queries (every planted
+needle, the GPU's own selection, the shortest and longest documents and a
+seeded random sample).  Rules P2-P4 are in tests/parity.py."""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import msa_oracle as O
+from sparse_retrieval_memory_amd import ops
+from synth import configs as C
+from synth import native
+from synth import splitmix as sm
+
+from tests.parity import ATT_TOL, GAP, SCORE_TOL, check_topk, dev_bits, rel_rows
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def announce(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def f32(bits):
+    """bf16 bits -> float32 (exact); the oracle widens to float64 block by block."""
+    return (np.asarray(bits).astype(np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def device_krbar(w, layer):
+    """The pooled router-key store drawn on the device (same bits as the host generator), plants applied."""
+    t = torch.empty((w.n_chunks, w.H, w.D), dtype=torch.int16, device=DEV)
+    native.fill_normal_bf16_device(t, w.seed, sm.TID_KRBAR, layer, 0)
+    for g, row in C.pooled_plants(w, layer).items():
+        t[g].copy_(dev_bits(row))
+    return t
+
+
+def content_store(w):
+    """Pinned host content tier [G, 2, H, D]: pooled K and V drawn on the device, copied once."""
+    G = w.n_chunks
+    st = torch.empty((G, 2, w.H, w.D), dtype=torch.int16, pin_memory=True)
+    for j, tid in enumerate((sm.TID_KBAR, sm.TID_VBAR)):
+        t = torch.empty((G, w.H, w.D), dtype=torch.int16, device=DEV)
+        native.fill_normal_bf16_device(t, w.seed, tid, 0, 0)
+        st[:, j].copy_(t)
+        del t
+    return st
+
+
+def content_rows(w, chunks):
+    """The oracle's copy of the content rows (host generator): K, V [len(chunks), H, D] float32."""
+    K = np.stack([C.content_block(w, "K", int(g), int(g) + 1)[0] for g in chunks]) if len(chunks) else \
+        np.zeros((0, w.H, w.D), np.uint16)
+    V = np.stack([C.content_block(w, "V", int(g), int(g) + 1)[0] for g in chunks]) if len(chunks) else \
+        np.zeros((0, w.H, w.D), np.uint16)
+    return f32(K), f32(V)
+
+
+def sample_docs(w, extra, n=2000, seed=1):
+    rng = np.random.default_rng(seed)
+    lens = w.doc_n_chunks
+    s = set(int(x) for x in rng.choice(w.n_docs, size=min(n, w.n_docs), replace=False))
+    s |= {int(np.argmin(lens)), int(np.argmax(lens)), 0, w.n_docs - 1}
+    s |= set(int(x) for x in extra)
+    return np.array(sorted(s))
+
+
+def fetch_and_attend(w, idx_dev, store_t, q, b_rows=None):
+    """Fetch the selected documents' pooled K/V from the pinned tier and attend (Tq = T and Tq = 1)."""
+    B = idx_dev.shape[0]
+    Mmax = int(w.doc_n_chunks.max()) * w.k
+    staging = torch.zeros((B, Mmax, 2, w.H, w.D), dtype=torch.int16, device=DEV)
+    ml = ops.fetch_docs(idx_dev.cpu(), store_t, torch.from_numpy(w.doc_chunk_off), staging, Mmax)
+    ml_dev = ml.to(DEV)
+    outs = {}
+    for Tq in (w.Tq, 1):
+        outs[Tq] = ops.sparse_attn_decode(dev_bits(q["Q"][:, -Tq:]), dev_bits(q["Kloc"]), dev_bits(q["Vloc"]),
+                                          staging, staging[:, :, 1], 2 * w.H * w.D, Mmax, ml_dev, w.k,
+                                          w.rope_base)
+    torch.cuda.synchronize()
+    return {Tq: o.cpu().numpy() for Tq, o in outs.items()}, ml.numpy()
+
+
+def check_attention(w, q, outs, gpu_idx, batches):
+    for b in batches:
+        mem = O.assemble(gpu_idx[b], w.doc_chunk_off)
+        Km, Vm = content_rows(w, mem)
+        for Tq, o in outs.items():
+            ref = O.attend(f32(q["Q"][b, -Tq:]), f32(q["Kloc"][b]), f32(q["Vloc"][b]), Km, Vm, w.k, w.rope_base,
+                           w.D ** -0.5)
+            assert rel_rows(o[b], ref) <= ATT_TOL, (b, Tq)
+
+
+# ------------------------------------------------------------------ 1M tokens
+def test_cfg2_full_step():
+    """1,000 documents, 16.6K chunks, T = 128, k = 16: every score against the oracle."""
+    w = C.config(2)
+    announce("cfg2 full", w.describe())
+    kr = device_krbar(w, 0)
+    host_kr = C.krbar_block(w, 0, 0, w.n_chunks)
+    q = C.queries(w)
+    off = torch.from_numpy(w.doc_chunk_off).to(DEV)
+    _, ref_doc = O.route(f32(q["Qr"]), f32(host_kr), w.doc_chunk_off)
+    for norms in (None, ops.krbar_inv_norms(kr)):
+        doc = ops.route_scores(dev_bits(q["Qr"]), kr, off, krbar_inv_norm=norms)
+        assert np.abs(doc.cpu().numpy() - ref_doc).max() <= SCORE_TOL
+    idx, sc = ops.topk_docs(doc, w.k)
+    gi = idx.cpu().numpy()
+    check_topk(gi[0], ref_doc[0], w.k)
+    assert np.abs(sc.cpu().numpy()[0] - ref_doc[0, gi[0]]).max() <= SCORE_TOL
+    for b, d in C.planted_docs(w):
+        assert d in gi[b]
+    outs, ml = fetch_and_attend(w, idx, content_store(w), q)
+    assert ml[0] == len(O.assemble(gi[0], w.doc_chunk_off))
+    check_attention(w, q, outs, gi, [0])
+
+
+# ----------------------------------------------------------------- 10M tokens
+def test_cfg3_full_route_sampled_queries():
+    """20,000 documents, 165K chunks, 16 queries x 64 tokens (the MFMA-bound shape).
+
+    The GPU scores all 16 queries in one launch; the oracle checks every
+    document of four of them (P2, P3) and the needles of all sixteen."""
+    w = C.config(3)
+    announce("cfg3 full", w.describe())
+    kr = device_krbar(w, 0)
+    host_kr = f32(C.krbar_block(w, 0, 0, w.n_chunks))
+    q = C.queries(w)
+    off = torch.from_numpy(w.doc_chunk_off).to(DEV)
+    doc = ops.route_scores(dev_bits(q["Qr"]), kr, off, krbar_inv_norm=ops.krbar_inv_norms(kr))
+    idx, sc = ops.topk_docs(doc, w.k)
+    gd, gi = doc.cpu().numpy(), idx.cpu().numpy()
+    checked = [0, 5, 10, 15]
+    _, ref_doc = O.route(f32(q["Qr"])[checked], host_kr, w.doc_chunk_off)
+    for j, b in enumerate(checked):
+        assert np.abs(gd[b] - ref_doc[j]).max() <= SCORE_TOL
+        check_topk(gi[b], ref_doc[j], w.k)
+    for b, d in C.planted_docs(w):
+        assert gi[b, 0] == d
+    outs, _ = fetch_and_attend(w, idx, content_store(w), q)
+    check_attention(w, q, outs, gi, [0, 15])
+
+
+# ---------------------------------------------------------------- 100M tokens
+def test_cfg4_layer_sampled_documents():
+    """200,000 documents, 1.66M chunks (one routed layer of the 100M-token store).
+
+    The oracle scores a sample of documents (needles, the GPU's selection,
+    extremes, 2,000 random); P2 on all of them, and P3 in the form that holds
+    for a sample: the GPU's k-th score is no lower than any sampled document
+    outside its set (less the gap), and its selected scores are the oracle's."""
+    w = C.config(4)
+    layer = 3
+    announce("cfg4 layer", layer, w.describe())
+    kr = device_krbar(w, layer)
+    q = C.queries(w, layer)
+    off = torch.from_numpy(w.doc_chunk_off).to(DEV)
+    doc = ops.route_scores(dev_bits(q["Qr"]), kr, off, krbar_inv_norm=ops.krbar_inv_norms(kr))
+    idx, sc = ops.topk_docs(doc, w.k)
+    gd, gi, gs = doc.cpu().numpy()[0], idx.cpu().numpy()[0], sc.cpu().numpy()[0]
+    needles = [d for _, d in C.planted_docs(w, layer)]
+    docs = sample_docs(w, list(gi) + needles)
+    # oracle on the sampled documents' chunks only (the generator regenerates any chunk range)
+    ref = np.empty(len(docs))
+    Qr = f32(q["Qr"])
+    for i, d in enumerate(docs):
+        g0, g1 = int(w.doc_chunk_off[d]), int(w.doc_chunk_off[d + 1])
+        _, dd = O.route(Qr, f32(C.krbar_block(w, layer, g0, g1)), np.array([0, g1 - g0]))
+        ref[i] = dd[0, 0]
+    assert np.abs(gd[docs] - ref).max() <= SCORE_TOL
+    pos = {int(d): i for i, d in enumerate(docs)}
+    sel = np.array([ref[pos[int(d)]] for d in gi])
+    assert np.abs(gs - sel).max() <= SCORE_TOL
+    assert np.all(np.diff(sel) <= 2 * SCORE_TOL)       # descending, up to the score tolerance
+    outside = np.array([ref[i] for i, d in enumerate(docs) if int(d) not in set(int(x) for x in gi)])
+    assert outside.max() <= sel.min() + GAP
+    for d in needles:
+        assert d in gi
+    # the GPU's scores over all documents: its selection is the exact top-k of what it computed
+    order = np.lexsort((np.arange(w.n_docs), -gd.astype(np.float64)))[: w.k]
+    assert list(order) == list(gi)
+    outs, _ = fetch_and_attend(w, idx, content_store(w), q)
+    check_attention(w, q, outs, gi[None], [0])
+
+
+# ------------------------------------------------------- interleave (10M tokens)
+def gpu_pool_corpus(w, slab_tokens=1_000_000):
+    """Offline encoding on the device: raw K, V, K_r drawn on the device in document-aligned slabs (chain
+    plants applied), pooled into the full (Kbar, Vbar, Krbar) store."""
+    G, H, D, E = w.n_chunks, w.H, w.D, w.row_elems
+    out = tuple(torch.empty((G, H, D), dtype=torch.int16, device=DEV) for _ in range(3))
+    plants = C.raw_plants(w)
+    d0 = 0
+    while d0 < w.n_docs:
+        d1 = int(np.searchsorted(w.doc_tok_off, w.doc_tok_off[d0] + slab_tokens, side="right")) - 1
+        d1 = min(max(d1, d0 + 1), w.n_docs)
+        t0, t1 = int(w.doc_tok_off[d0]), int(w.doc_tok_off[d1])
+        c0, c1 = int(w.doc_chunk_off[d0]), int(w.doc_chunk_off[d1])
+        raw = []
+        for tid in (sm.TID_K, sm.TID_V, sm.TID_KR):
+            t = torch.empty((t1 - t0, H, D), dtype=torch.int16, device=DEV)
+            native.fill_normal_bf16_device(t, w.seed, tid, 0, t0 * E)
+            raw.append(t)
+        for tok, row in plants.items():
+            if t0 <= tok < t1:
+                raw[2][tok - t0].copy_(dev_bits(row))
+        ops.pool_chunks(*raw, torch.from_numpy(w.doc_tok_off[d0:d1 + 1].copy()).to(DEV),
+                        torch.from_numpy(w.doc_chunk_off[d0:d1 + 1].copy()).to(DEV), c1 - c0, w.chunk, w.rope_base,
+                        out=tuple(o[c0:c1] for o in out))
+        torch.cuda.synchronize()
+        del raw
+        d0 = d1
+    return out
+
+
+def oracle_pool_docs(w, docs):
+    """The oracle's pooled (rounded) rows of the given documents: {doc: (K, V, Kr) float64 [n_d, H, D]}."""
+    res = {}
+    for d in docs:
+        t0, t1 = int(w.doc_tok_off[d]), int(w.doc_tok_off[d + 1])
+        K, V, Kr = (O.bf16_to_f64(C.raw_block(w, x, t0, t1)) for x in ("K", "V", "Kr"))
+        pk, pv, pr, _ = O.pool(K, V, Kr, [t1 - t0], w.chunk, w.rope_base)
+        res[int(d)] = (O.round_bf16(pk), O.round_bf16(pv), O.round_bf16(pr))
+    return res
+
+
+def interleave_on_gpu(w, pooled, q):
+    from sparse_retrieval_memory_amd.interleave import Interleave
+    Kb, Vb, Rb = pooled
+    store = torch.stack([Kb, Vb], dim=1).cpu().pin_memory()
+    il = Interleave(krbar=Rb, doc_chunk_off=torch.from_numpy(w.doc_chunk_off).to(DEV),
+                    doc_chunk_off_host=torch.from_numpy(w.doc_chunk_off.copy()), content=store,
+                    krbar_inv_norm=ops.krbar_inv_norms(Rb), rope_base=w.rope_base)
+    res = il.run(dev_bits(q["Qr"]), dev_bits(q["Q"]), dev_bits(q["Kloc"]), dev_bits(q["Vloc"]), w.k, w.rounds,
+                 keep_scores=True)
+    torch.cuda.synchronize()
+    return res
+
+
+def test_cfg5_interleave_reduced_against_oracle():
+    """300 documents of the interleave corpus: pooled on the GPU from raw tokens, then 3 rounds per query,
+    every round against the oracle's own pooling and interleave loop."""
+    from tests.parity import bf16_ulp_diff, host_bits, pooled_k_ok
+    w = C.config(5, n_docs=300)
+    announce("cfg5 reduced", w.describe())
+    pooled = gpu_pool_corpus(w)
+    K = O.bf16_to_f64(C.raw_block(w, "K", 0, w.n_tok)); V = O.bf16_to_f64(C.raw_block(w, "V", 0, w.n_tok))
+    Kr = O.bf16_to_f64(C.raw_block(w, "Kr", 0, w.n_tok))
+    rK, rV, rR, off = O.pool(K, V, Kr, w.doc_len, w.chunk, w.rope_base)
+    rK, rV, rR = O.round_bf16(rK), O.round_bf16(rV), O.round_bf16(rR)
+    assert bf16_ulp_diff(host_bits(pooled[1]), O.f64_to_bf16_bits(rV)).max() <= 1
+    assert bf16_ulp_diff(host_bits(pooled[2]), O.f64_to_bf16_bits(rR)).max() <= 1
+    assert pooled_k_ok(host_bits(pooled[0]), rK)
+    q = C.queries(w)
+    res = interleave_on_gpu(w, pooled, q)
+    for b, ch in enumerate(C.chains(w)):
+        ref = O.interleave(f32(q["Qr"][b]), rR, rK, rV, off, w.k, w.rounds, f32(q["Q"][b]), f32(q["Kloc"][b]),
+                           f32(q["Vloc"][b]), w.rope_base, w.D ** -0.5)
+        for r in range(w.rounds):
+            g = res[r].doc_scores.cpu().numpy()[b]
+            s = ref[r]["doc_scores"]
+            fin = np.isfinite(s)
+            assert np.array_equal(fin, np.isfinite(g))                     # the same documents are excluded
+            assert np.abs(g[fin] - s[fin]).max() <= 1e-4                   # pooled stores may differ by an ulp
+            if check_topk(res[r].top_idx[b], s, w.k):
+                break      # an admissible different set (gap < 1e-3): later rounds no longer share inputs
+            assert rel_rows(res[r].O.cpu().numpy()[b], ref[r]["O"]) <= ATT_TOL
+        assert ch["A"] in res[0].top_idx[b] and ch["B"] in res[1].top_idx[b] and ch["C"] in res[2].top_idx[b]
+
+
+def test_cfg5_full_pool_and_interleave():
+    """The whole 10M-token interleave workload: pooled on the GPU in 1M-token slabs, 4 queries x 3 rounds.
+
+    Pooled rows against the oracle's pooling on sampled documents (P1); round-1 and round-2 document
+    scores against the oracle on sampled documents; every planted 3-hop chain recovered hop by hop;
+    no document retrieved twice."""
+    from tests.parity import bf16_ulp_diff, host_bits, pooled_k_ok
+    w = C.config(5)
+    announce("cfg5 full", w.describe())
+    pooled = gpu_pool_corpus(w)
+    q = C.queries(w)
+    res = interleave_on_gpu(w, pooled, q)
+    chains = C.chains(w)
+    for b, ch in enumerate(chains):
+        assert ch["A"] in res[0].top_idx[b], (b, "hop 1")
+        assert ch["B"] in res[1].top_idx[b], (b, "hop 2")
+        assert ch["C"] in res[2].top_idx[b], (b, "hop 3")
+        allr = res[-1].retrieved[b]
+        assert len(set(int(x) for x in allr)) == len(allr) == w.k * w.rounds
+    # pooled rows and scores on a document sample (chains, the GPU's picks, extremes, random)
+    extra = [ch[x] for ch in chains for x in ("A", "B", "C")] + list(res[0].top_idx.ravel()) + \
+        list(res[1].top_idx.ravel())
+    docs = sample_docs(w, extra, n=100)
+    ref = oracle_pool_docs(w, docs)
+    Kb, Vb, Rb = (host_bits(t) for t in pooled)
+    for d, (pk, pv, pr) in ref.items():
+        g0, g1 = int(w.doc_chunk_off[d]), int(w.doc_chunk_off[d + 1])
+        assert bf16_ulp_diff(Vb[g0:g1], O.f64_to_bf16_bits(pv)).max() <= 1
+        assert bf16_ulp_diff(Rb[g0:g1], O.f64_to_bf16_bits(pr)).max() <= 1
+        assert pooled_k_ok(Kb[g0:g1], pk)
+    Qr = f32(q["Qr"])
+    for r in (0, 1):
+        for b in range(w.B):
+            rows = Qr[b]
+            if r == 1:
+                rows = np.concatenate([rows] + [ref[int(d)][2] for d in res[0].top_idx[b]])
+            g = res[r].doc_scores.cpu().numpy()[b]
+            for d in docs:
+                _, dd = O.route(rows[None], ref[int(d)][2], np.array([0, len(ref[int(d)][2])]))
+                if r == 1 and d in set(int(x) for x in res[0].top_idx[b]):
+                    assert g[d] == -np.inf
+                else:
+                    assert abs(g[d] - dd[0, 0]) <= 1e-4, (r, b, d)
