@@ -4,12 +4,22 @@
 // decoding; b-lab.team sec. 1, Global RoPE: the query's start index is offset
 // by k, the number of retrieved blocks).
 //
-// Flash-style, fp32 throughout: one workgroup owns 16 query rows of one q-head
-// and streams keys in LDS tiles of 64 (memory entries first, then local keys,
-// stopping at the causal limit of its last row), keeping a running max, sum
-// and output per row (online softmax).  Query rows and local keys are rotated
-// here, with angles computed in fp64; memory keys arrive already rotated.
-// Scores are pre-scaled by log2(e) so the exponentials are exp2.
+// Flash-style on the matrix cores.  One workgroup owns 32 query rows of one
+// q-head; its 4 waves take every 4th tile of 32 keys (memory entries first,
+// then local keys up to the causal limit of the last row) and keep a running
+// max, sum and output per row; the waves' partial results are merged at the
+// end.  Per key tile, a wave computes S^T = K Q^T (keys x rows) with
+// v_mfma_f32_32x32x16_bf16, so every lane holds one query row's scores, and
+// the softmax statistics of a row live in one lane pair.  O^T += V^T P^T
+// then uses the same layout (V is transposed through LDS).
+//
+// Precision: the operands of both products are split into bf16 hi + lo parts
+// (q = qh + ql with |ql| <= 2^-9 |q|), so with fp32 accumulation the scores
+// and weighted sums keep ~2^-16 relative accuracy instead of bf16's 2^-8.
+// Memory keys and V are bf16 already (no lo part); rotated local keys and
+// queries, and the probabilities, are split.  RoPE angles are reduced in fp64
+// (position x frequency in revolutions) and evaluated in fp32.  Scores are
+// pre-scaled by scale * log2(e) so the exponentials are exp2.
 #include "msa_internal.h"
 
 #include <math.h>
@@ -18,193 +28,307 @@ namespace msa {
 namespace {
 
 constexpr int D = 128;
-constexpr int RQ = 16;     // query rows per workgroup
-constexpr int KT = 64;     // keys per tile
-constexpr int THREADS = 256;
-constexpr int KSTR = D + 4;  // padded LDS row (floats) for keys
+constexpr int RT = 32;          // query rows per workgroup (MFMA N)
+constexpr int KT = 32;          // keys per tile (MFMA M)
+constexpr int NWAVE = 4;
+constexpr int THREADS = 64 * NWAVE;
+constexpr int VT_STRIDE = KT + 8;   // bf16 per transposed V row (dims x keys), padded
 
-__device__ __forceinline__ void load_bf16x8(const uint16_t* p, float* out) {
-  const uint4 v = *reinterpret_cast<const uint4*>(p);
-  out[0] = bf16_lo(v.x); out[1] = bf16_hi(v.x);
-  out[2] = bf16_lo(v.y); out[3] = bf16_hi(v.y);
-  out[4] = bf16_lo(v.z); out[5] = bf16_hi(v.z);
-  out[6] = bf16_lo(v.w); out[7] = bf16_hi(v.w);
+struct bf16pair {
+  bf16x8_t hi, lo;
+};
+
+__device__ __forceinline__ uint32_t pack2(uint32_t a, uint32_t b) { return a | (b << 16); }
+
+// x -> (bf16 hi, bf16 lo) with hi = RNE(x), lo = RNE(x - hi); 8 values
+__device__ __forceinline__ bf16pair split8(const float (&x)[8]) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t h0 = f32_to_bf16_rne(x[2 * j]), h1 = f32_to_bf16_rne(x[2 * j + 1]);
+    const uint32_t l0 = f32_to_bf16_rne(x[2 * j] - __uint_as_float(h0 << 16));
+    const uint32_t l1 = f32_to_bf16_rne(x[2 * j + 1] - __uint_as_float(h1 << 16));
+    h[j] = pack2(h0, h1);
+    l[j] = pack2(l0, l1);
+  }
+  bf16pair r;
+  r.hi = __builtin_bit_cast(bf16x8_t, make_uint4(h[0], h[1], h[2], h[3]));
+  r.lo = __builtin_bit_cast(bf16x8_t, make_uint4(l[0], l[1], l[2], l[3]));
+  return r;
 }
 
-// cos/sin of pos * base^(-2i/D), evaluated in fp64
-__device__ __forceinline__ void rope_cs(double pos, int i, double log2_base, float* c, float* s) {
-  const double theta = exp2(-(2.0 * i / D) * log2_base);
-  double sn, cs;
-  sincos(pos * theta, &sn, &cs);
-  *c = (float)cs;
-  *s = (float)sn;
+__device__ __forceinline__ void unpack8(uint4 v, float (&x)[8]) {
+  x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x); x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
+  x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z); x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
 }
 
-__global__ void __launch_bounds__(THREADS, 2)
-attn_kernel(const uint16_t* __restrict__ Q, int Tq, int Hq, const uint16_t* __restrict__ Kloc,
-            const uint16_t* __restrict__ Vloc, int Tl, int Hkv, const uint16_t* __restrict__ Kmem,
-            const uint16_t* __restrict__ Vmem, int64_t mstride, int Mmax,
-            const int32_t* __restrict__ mem_len, int rope_offset, double log2_base, float scale_log2e,
-            float* __restrict__ O) {
-  __shared__ __attribute__((aligned(16))) float qs[RQ][D];
-  __shared__ __attribute__((aligned(16))) float ks[KT][KSTR];
-  __shared__ __attribute__((aligned(16))) float vs[KT][D];
-  __shared__ __attribute__((aligned(16))) float ps[RQ][KT];
+// cos/sin of pos * theta_i, theta_i = base^(-2i/D); rev_i = theta_i / (2 pi) in fp64.
+// The angle in revolutions is reduced to [-1/2, 1/2] in fp64, then evaluated in fp32.
+__device__ __forceinline__ void rope_cs(int pos, double rev_i, float* c, float* s) {
+  double r = (double)pos * rev_i;
+  r -= rint(r);
+  sincospif(2.0f * (float)r, s, c);
+}
+
+// Rotate the pairs (i, i + 64) held by one lane: lo[j] = dims 16 ks + 8 hf + j
+// (ks < 4), hi[j] = the same dims + 64.
+__device__ __forceinline__ void rotate_pairs(float (&lo)[8], float (&hi)[8], int pos, const double* rev, int d0) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float c, s;
+    rope_cs(pos, rev[d0 + j], &c, &s);
+    const float x1 = lo[j], x2 = hi[j];
+    lo[j] = x1 * c - x2 * s;
+    hi[j] = x2 * c + x1 * s;
+  }
+}
+
+__global__ void __launch_bounds__(THREADS, 1)
+attn_mfma_kernel(const uint16_t* __restrict__ Q, int Tq, int Hq, const uint16_t* __restrict__ Kloc,
+                 const uint16_t* __restrict__ Vloc, int Tl, int Hkv, const uint16_t* __restrict__ Kmem,
+                 const uint16_t* __restrict__ Vmem, int64_t mstride, int Mmax, const int32_t* __restrict__ mem_len,
+                 int rope_offset, double log2_base, float scale_log2e, float* __restrict__ O) {
+  __shared__ double rev[D / 2];
+  // per wave: V^T of its current tile [D][VT_STRIDE] bf16; reused at the end for the merge
+  __shared__ __attribute__((aligned(16))) float smem[NWAVE * D * RT];
+  static_assert(sizeof(smem) >= sizeof(uint16_t) * NWAVE * D * VT_STRIDE, "V^T area");
+  __shared__ float m_sh[NWAVE][RT], l_sh[NWAVE][RT];
 
   const int tid = threadIdx.x;
-  const int row0 = blockIdx.x * RQ;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int col = lane & 31, hf = lane >> 5;
+  const int r0 = blockIdx.x * RT;
   const int h = blockIdx.y;
   const int b = blockIdx.z;
   const int g = h / (Hq / Hkv);
   int M = mem_len[b];
   if (M < 0) M = 0;
   if (M > Mmax) M = Mmax;
+  int last = r0 + RT - 1;
+  if (last > Tq - 1) last = Tq - 1;
+  const int n_local = (Tl - Tq) + last + 1;
+  const int n_keys = M + n_local;
+  const int n_tiles = (n_keys + KT - 1) / KT;
 
-  // --- query rows: rotate at rope_offset + (Tl - Tq) + i, pre-scale
-  for (int x = tid; x < RQ * (D / 2); x += THREADS) {
-    const int r = x / (D / 2), i = x % (D / 2);
-    const int qi = row0 + r;
-    float a = 0.f, c2 = 0.f;
-    if (qi < Tq) {
-      const uint16_t* q = Q + (((int64_t)b * Tq + qi) * Hq + h) * D;
-      const float x1 = __uint_as_float((uint32_t)q[i] << 16);
-      const float x2 = __uint_as_float((uint32_t)q[i + D / 2] << 16);
-      float c, s;
-      rope_cs((double)(rope_offset + (Tl - Tq) + qi), i, log2_base, &c, &s);
-      a = (x1 * c - x2 * s) * scale_log2e;
-      c2 = (x2 * c + x1 * s) * scale_log2e;
+  if (tid < D / 2) rev[tid] = exp2(-(2.0 * tid / D) * log2_base) * 0.15915494309189535;   // / (2 pi)
+  __syncthreads();
+
+  // ---- Q^T as the B operand: lane (col, hf) holds query row r0 + col, dims 16 ks + 8 hf + j
+  bf16x8_t qh[8], ql[8];
+  {
+    const int row = r0 + col;
+    float lo[4][8], hi[4][8];
+    if (row < Tq) {
+      const uint16_t* q = Q + (((int64_t)b * Tq + row) * Hq + h) * D;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        unpack8(*reinterpret_cast<const uint4*>(q + 16 * ks + 8 * hf), lo[ks]);
+        unpack8(*reinterpret_cast<const uint4*>(q + 64 + 16 * ks + 8 * hf), hi[ks]);
+      }
+      const int pos = rope_offset + (Tl - Tq) + row;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) rotate_pairs(lo[ks], hi[ks], pos, rev, 16 * ks + 8 * hf);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) { lo[ks][j] = 0.f; hi[ks][j] = 0.f; }
     }
-    qs[r][i] = a;
-    qs[r][i + D / 2] = c2;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) { lo[ks][j] *= scale_log2e; hi[ks][j] *= scale_log2e; }
+      const bf16pair a = split8(lo[ks]), c = split8(hi[ks]);
+      qh[ks] = a.hi; ql[ks] = a.lo;
+      qh[ks + 4] = c.hi; ql[ks + 4] = c.lo;
+    }
   }
 
-  // per-thread roles
-  const int sr = tid / 16;          // score row / output row
-  const int sc = tid % 16;          // score key column (keys sc + 16 j)
-  const int od = (tid % 16) * 8;    // output dims [od, od + 8)
+  // running state of this lane's query row (both lanes of a pair keep identical copies)
   float m_run = -INFINITY, l_run = 0.f;
-  float o[8];
+  f32x16_t oacc[4];   // O^T: dim tile dt, rows = dims 32 dt + 8 (i/4) + 4 hf + i % 4, column = query row
 #pragma unroll
-  for (int i = 0; i < 8; ++i) o[i] = 0.f;
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
 
-  // keys this workgroup needs: all memory + local keys up to the causal limit of its last row
-  int last_row = row0 + RQ - 1;
-  if (last_row > Tq - 1) last_row = Tq - 1;
-  const int n_local = (Tl - Tq) + last_row + 1;   // local keys 0..n_local-1
-  const int n_keys = M + n_local;
-  const int64_t mem_base = (int64_t)b * Mmax;
+  const int qrow = r0 + col;
+  const int lim = (Tl - Tq) + qrow;      // last visible local key of this row
+  uint16_t (*myvt)[VT_STRIDE] = reinterpret_cast<uint16_t (*)[VT_STRIDE]>(smem) + wave * D;
 
-  for (int k0 = 0; k0 < n_keys; k0 += KT) {
-    __syncthreads();   // previous tile fully consumed (and qs visible on the first pass)
-    // load K and V tile: thread -> key tid / 4, quarter tid % 4
+  for (int t = wave; t < n_tiles; t += NWAVE) {
+    const int k0 = t * KT;
+    // ---- K tile as the A operand: lane (col, hf) holds key k0 + col, dims 16 ks + 8 hf + j
+    const int j = k0 + col;
+    bool local = false;
+    const uint16_t *kp = nullptr, *vp = nullptr;
+    if (j < M) {
+      kp = Kmem + ((int64_t)b * Mmax + j) * mstride + (int64_t)g * D;
+      vp = Vmem + ((int64_t)b * Mmax + j) * mstride + (int64_t)g * D;
+    } else if (j < n_keys) {
+      local = true;
+      kp = Kloc + (((int64_t)b * Tl + (j - M)) * Hkv + g) * D;
+      vp = Vloc + (((int64_t)b * Tl + (j - M)) * Hkv + g) * D;
+    }
+    // V tile -> LDS, transposed: myvt[dim][key]; lane (col, hf) copies dims [64 hf, 64 hf + 64) of key col
     {
-      const int kk = tid >> 2, qd = tid & 3;
-      const int j = k0 + kk;
-      float kx[32], vx[32];
-      if (j < n_keys) {
-        const uint16_t *kp, *vp;
-        if (j < M) {
-          kp = Kmem + (mem_base + j) * mstride + (int64_t)g * D;
-          vp = Vmem + (mem_base + j) * mstride + (int64_t)g * D;
+      uint4 vv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        vv[i] = vp ? *reinterpret_cast<const uint4*>(vp + 64 * hf + 8 * i) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t w4[4] = {vv[i].x, vv[i].y, vv[i].z, vv[i].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          myvt[64 * hf + 8 * i + 2 * e][col] = (uint16_t)(w4[e] & 0xFFFFu);
+          myvt[64 * hf + 8 * i + 2 * e + 1][col] = (uint16_t)(w4[e] >> 16);
+        }
+      }
+    }
+    f32x16_t s;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = 0.f;
+    const bool tile_local = __builtin_amdgcn_readfirstlane((int)(k0 + KT > M && M < n_keys)) != 0;
+    if (!tile_local) {
+      // memory keys only: exact bf16 operands, Q split in two
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const uint4 kv = kp ? *reinterpret_cast<const uint4*>(kp + 16 * (ks & 3) + 64 * (ks >> 2) + 8 * hf)
+                            : make_uint4(0, 0, 0, 0);
+        const bf16x8_t kb = __builtin_bit_cast(bf16x8_t, kv);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, qh[ks], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, ql[ks], s, 0, 0, 0);
+      }
+    } else {
+      float lo[4][8], hi[4][8];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        if (kp) {
+          unpack8(*reinterpret_cast<const uint4*>(kp + 16 * ks + 8 * hf), lo[ks]);
+          unpack8(*reinterpret_cast<const uint4*>(kp + 64 + 16 * ks + 8 * hf), hi[ks]);
         } else {
-          const int jl = j - M;
-          kp = Kloc + (((int64_t)b * Tl + jl) * Hkv + g) * D;
-          vp = Vloc + (((int64_t)b * Tl + jl) * Hkv + g) * D;
-        }
-        load_bf16x8(kp + 16 * qd, kx);
-        load_bf16x8(kp + 16 * qd + 8, kx + 8);
-        load_bf16x8(kp + 64 + 16 * qd, kx + 16);
-        load_bf16x8(kp + 64 + 16 * qd + 8, kx + 24);
-        load_bf16x8(vp + 32 * qd, vx);
-        load_bf16x8(vp + 32 * qd + 8, vx + 8);
-        load_bf16x8(vp + 32 * qd + 16, vx + 16);
-        load_bf16x8(vp + 32 * qd + 24, vx + 24);
-        if (j >= M) {
-          const double pos = (double)(rope_offset + (j - M));
-#pragma unroll 4
-          for (int e = 0; e < 16; ++e) {
-            float c, s;
-            rope_cs(pos, 16 * qd + e, log2_base, &c, &s);
-            const float x1 = kx[e], x2 = kx[16 + e];
-            kx[e] = x1 * c - x2 * s;
-            kx[16 + e] = x2 * c + x1 * s;
-          }
-        }
-      } else {
 #pragma unroll
-        for (int e = 0; e < 32; ++e) { kx[e] = 0.f; vx[e] = 0.f; }
+          for (int e = 0; e < 8; ++e) { lo[ks][e] = 0.f; hi[ks][e] = 0.f; }
+        }
+      }
+      if (local) {
+        const int pos = rope_offset + (j - M);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) rotate_pairs(lo[ks], hi[ks], pos, rev, 16 * ks + 8 * hf);
       }
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        ks[kk][16 * qd + e] = kx[e];
-        ks[kk][64 + 16 * qd + e] = kx[16 + e];
+      for (int ks = 0; ks < 8; ++ks) {
+        const bf16pair kb = split8(ks < 4 ? lo[ks] : hi[ks - 4]);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb.hi, qh[ks], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb.hi, ql[ks], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb.lo, qh[ks], s, 0, 0, 0);
       }
-#pragma unroll
-      for (int e = 0; e < 32; e += 4)
-        *reinterpret_cast<float4*>(&vs[kk][32 * qd + e]) = make_float4(vx[e], vx[e + 1], vx[e + 2], vx[e + 3]);
     }
-    __syncthreads();
 
-    // scores for row sr, keys sc + 16 jj
-    float s4[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int d = 0; d < D; d += 4) {
-      const float4 q = *reinterpret_cast<const float4*>(&qs[sr][d]);
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const float4 kv = *reinterpret_cast<const float4*>(&ks[sc + 16 * jj][d]);
-        s4[jj] = fmaf(q.x, kv.x, s4[jj]);
-        s4[jj] = fmaf(q.y, kv.y, s4[jj]);
-        s4[jj] = fmaf(q.z, kv.z, s4[jj]);
-        s4[jj] = fmaf(q.w, kv.w, s4[jj]);
-      }
-    }
-    const int qi = row0 + sr;
-    const int lim = (Tl - Tq) + qi;   // last visible local key of this row
+    // ---- mask and online softmax for this lane's row (keys 8 (i/4) + 4 hf + i % 4 of the tile)
     float tmax = -INFINITY;
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int j = k0 + sc + 16 * jj;
-      bool vis = j < n_keys && qi < Tq;
-      if (j >= M) vis = vis && (j - M) <= lim;
-      s4[jj] = vis ? s4[jj] : -INFINITY;
-      tmax = fmaxf(tmax, s4[jj]);
+    for (int i = 0; i < 16; ++i) {
+      const int key = k0 + 8 * (i >> 2) + 4 * hf + (i & 3);
+      bool vis = key < n_keys && qrow < Tq;
+      if (key >= M) vis = vis && (key - M) <= lim;
+      s[i] = vis ? s[i] : -INFINITY;
+      tmax = fmaxf(tmax, s[i]);
     }
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, off));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
     const float m_new = fmaxf(m_run, tmax);
     const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
-    float lsum = 0.f;
+    float p[16], psum = 0.f;
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const float pj = (m_new == -INFINITY) ? 0.f : exp2f(s4[jj] - m_new);
-      ps[sr][sc + 16 * jj] = pj;
-      lsum += pj;
+    for (int i = 0; i < 16; ++i) {
+      p[i] = (m_new == -INFINITY) ? 0.f : exp2f(s[i] - m_new);
+      psum += p[i];
     }
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) lsum += __shfl_xor(lsum, off);
-    l_run = l_run * alpha + lsum;
+    psum += __shfl_xor(psum, 32);
+    l_run = l_run * alpha + psum;
     m_run = m_new;
-    __syncthreads();
-
 #pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] *= alpha;
-    for (int j = 0; j < KT; ++j) {
-      const float pj = ps[sr][j];
-      const float4 v0 = *reinterpret_cast<const float4*>(&vs[j][od]);
-      const float4 v1 = *reinterpret_cast<const float4*>(&vs[j][od + 4]);
-      o[0] = fmaf(pj, v0.x, o[0]); o[1] = fmaf(pj, v0.y, o[1]);
-      o[2] = fmaf(pj, v0.z, o[2]); o[3] = fmaf(pj, v0.w, o[3]);
-      o[4] = fmaf(pj, v1.x, o[4]); o[5] = fmaf(pj, v1.y, o[5]);
-      o[6] = fmaf(pj, v1.z, o[6]); o[7] = fmaf(pj, v1.w, o[7]);
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+
+    // ---- P^T as the B operand (keys 16 st + 8 hf + e of this lane's row): swap halves with the partner
+    float send[8], recv[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      send[e] = hf == 0 ? p[4 + e] : p[e];
+      send[4 + e] = hf == 0 ? p[12 + e] : p[8 + e];
     }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) recv[e] = __shfl_xor(send[e], 32);
+    float pb[2][8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      pb[0][e] = hf == 0 ? p[e] : recv[e];
+      pb[0][4 + e] = hf == 0 ? recv[e] : p[4 + e];
+      pb[1][e] = hf == 0 ? p[8 + e] : recv[4 + e];
+      pb[1][4 + e] = hf == 0 ? recv[4 + e] : p[12 + e];
+    }
+    const bf16pair p0 = split8(pb[0]), p1 = split8(pb[1]);
+
+    // ---- O^T += V^T P^T: A = V^T (32 dims x 16 keys) from LDS
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // this wave's LDS writes of V^T have completed
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const bf16x8_t va = *reinterpret_cast<const bf16x8_t*>(&myvt[32 * dt + col][16 * st + 8 * hf]);
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, st == 0 ? p0.hi : p1.hi, oacc[dt], 0, 0, 0);
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, st == 0 ? p0.lo : p1.lo, oacc[dt], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();      // V^T reads done before the next tile overwrites it
   }
 
-  const int qi = row0 + sr;
-  if (qi < Tq) {
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    float* out = O + (((int64_t)b * Tq + qi) * Hq + h) * D + od;
-    *reinterpret_cast<float4*>(out) = make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
-    *reinterpret_cast<float4*>(out + 4) = make_float4(o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv);
+  // ---- merge the waves: O = sum_w 2^(m_w - m) O_w / sum_w 2^(m_w - m) l_w
+  if (hf == 0) {
+    m_sh[wave][col] = m_run;
+    l_sh[wave][col] = l_run;
+  }
+  __syncthreads();
+  float mx = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < NWAVE; ++w) mx = fmaxf(mx, m_sh[w][col]);
+  const float wscale = (m_run == -INFINITY) ? 0.f : exp2f(m_run - mx);
+  float lt = 0.f;
+#pragma unroll
+  for (int w = 0; w < NWAVE; ++w) lt += (m_sh[w][col] == -INFINITY) ? 0.f : l_sh[w][col] * exp2f(m_sh[w][col] - mx);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  // scaled partial outputs through LDS (fp32 [dims][rows] per wave, in the V^T area)
+  float* part = smem;                                         // NWAVE x D x RT floats
+  __syncthreads();
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int dim = 32 * dt + 8 * (i >> 2) + 4 * hf + (i & 3);
+      part[(wave * D + dim) * RT + col] = oacc[dt][i] * wscale * inv;
+    }
+  __syncthreads();
+  // thread -> (row, 16 dims): sum the waves' parts and write 16 contiguous floats
+  for (int x = tid; x < RT * (D / 16); x += THREADS) {
+    const int row = x / (D / 16), d0 = (x % (D / 16)) * 16;
+    if (r0 + row >= Tq) continue;
+    float* out = O + (((int64_t)b * Tq + r0 + row) * Hq + h) * D + d0;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float acc = 0.f;
+#pragma unroll
+        for (int w = 0; w < NWAVE; ++w) acc += part[(w * D + d0 + 4 * q4 + e) * RT + row];
+        v[e] = acc;
+      }
+      *reinterpret_cast<float4*>(out + 4 * q4) = make_float4(v[0], v[1], v[2], v[3]);
+    }
   }
 }
 
@@ -214,9 +338,9 @@ int launch_attn(const uint16_t* Q, int B, int Tq, int Hq, const uint16_t* Kloc, 
                 int Tl, int Hkv, const uint16_t* Kmem, const uint16_t* Vmem, int64_t mem_entry_stride,
                 int Mmax, const int32_t* mem_len, int rope_offset, double rope_base, float scale,
                 float* O, hipStream_t stream) {
-  dim3 grid((unsigned)((Tq + RQ - 1) / RQ), (unsigned)Hq, (unsigned)B);
+  dim3 grid((unsigned)((Tq + RT - 1) / RT), (unsigned)Hq, (unsigned)B);
   const float scale_log2e = scale * 1.4426950408889634f;
-  hipLaunchKernelGGL(attn_kernel, grid, dim3(THREADS), 0, stream, Q, Tq, Hq, Kloc, Vloc, Tl, Hkv, Kmem,
+  hipLaunchKernelGGL(attn_mfma_kernel, grid, dim3(THREADS), 0, stream, Q, Tq, Hq, Kloc, Vloc, Tl, Hkv, Kmem,
                      Vmem, mem_entry_stride, Mmax, mem_len, rope_offset, log2(rope_base), scale_log2e, O);
   MSA_CHECK_LAUNCH();
   return MSA_OK;
