@@ -7,15 +7,21 @@ chunk, 61 GB in total) and its own 128-token router query (batch 1).  One step
 runs the 18 layers in sequence; a layer is
 
     route (scan of all Krbar + document max) -> top-16 documents ->
-    ids to the host -> hipMemcpyAsync of the selected pooled K/V from pinned
-    host memory on a side stream -> GQA attention (32 q-heads, 128 query rows,
-    128 local tokens) over [fetched memory ++ local KV].
+    assemble the selected pooled K/V from the pinned host tier (one kernel
+    reading the mapped host memory; the ids never leave the GPU) ->
+    GQA attention (32 q-heads, 128 query rows, 128 local tokens) over
+    [fetched memory ++ local KV].
 
-Inputs are generated on the device before timing (seeded, synthetic); the
-pooled content store (Kbar|Vbar, 6.8 GB) sits in pinned host memory and is
-shared by all layers.  The printed JSON line reports memory tokens routed per
-second (per query), the step latency, the roofline of the routing call and
-the oracle's CPU throughput on a bounded sample of the same workload.
+The same step with the ids copied to the host and the content fetched by
+hipMemcpyAsync on a side stream is timed beside it, as are attention alone
+(128 rows and 1-row decode), top-k alone, the scan of the 10M-token batch-16
+workload (matrix-core bound), pooling throughput and the rounds of the
+10M-token interleave workload.  Inputs are generated on the device before
+timing (seeded, synthetic); the pooled content store (Kbar|Vbar, 6.8 GB) sits
+in pinned host memory and is shared by all layers.  The printed JSON line
+reports memory tokens routed per second (per query), the step latency, the
+roofline of the routing call and the oracle's CPU throughput on a bounded
+sample of the same workload.
 """
 
 from __future__ import annotations
@@ -33,6 +39,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_route_100M.json")
 
 
@@ -51,7 +58,11 @@ def cpu_baseline(w, seconds: float):
     """Oracle route + top-k on a bounded slice of layer 0 (documents from the start)."""
     from oracle import msa_oracle as O
     from synth import configs as C
-    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = 1
     q = C.queries(w, 0)
     Qr = O.bf16_to_f64(q["Qr"])
     d = 1000
@@ -131,6 +142,8 @@ def main():
     ml_dev = torch.empty(1, dtype=torch.int32, device=dev)
     O_out = torch.empty((1, w.Tq, w.Hq, D), dtype=torch.float32, device=dev)
     doc = torch.empty((1, w.n_docs), dtype=torch.float32, device=dev)
+    idx_d = torch.empty((1, k), dtype=torch.int32, device=dev)
+    sc_d = torch.empty((1, k), dtype=torch.float32, device=dev)
     ws_r = ops.workspace(ops.route_workspace_bytes(1, w.T, H, D, G, w.n_docs), dev, "bench-route")
     ws_k = ops.workspace(ops.topk_workspace_bytes(1, w.n_docs, k), dev, "bench-topk")
     comp = torch.cuda.current_stream()
@@ -141,16 +154,26 @@ def main():
     ev_r0 = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
     ev_r1 = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
     ev_a1 = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
-    selected = []
 
     def layer_step(layer, rec=None):
+        """route -> top-k -> device-side assembly from the pinned host tier -> attend (one stream, no host sync)."""
         if rec is not None:
             ev_r0[rec].record(comp)
         ops.route_scores(qr[layer], krbar[layer], off_dev, doc_scores=doc, ws=ws_r, krbar_inv_norm=knorm[layer])
         if rec is not None:
             ev_r1[rec].record(comp)
-        idx, _ = ops.topk_docs(doc, k, ws=ws_k)
-        top_host.copy_(idx, non_blocking=True)
+        ops.topk_docs(doc, k, top_idx=idx_d, top_scores=sc_d, ws=ws_k)
+        ops.gather_docs(idx_d, store, off_dev, staging, Mmax, mem_len=ml_dev)
+        ops.sparse_attn_decode(Q[layer], Kl[layer], Vl[layer], staging, staging[:, :, 1], 2 * H * D, Mmax, ml_dev,
+                               k, w.rope_base, out=O_out)
+        if rec is not None:
+            ev_a1[rec].record(comp)
+
+    def layer_step_host_fetch(layer):
+        """The same layer with the ids sent to the host and the content copied by hipMemcpyAsync on a side stream."""
+        ops.route_scores(qr[layer], krbar[layer], off_dev, doc_scores=doc, ws=ws_r, krbar_inv_norm=knorm[layer])
+        ops.topk_docs(doc, k, top_idx=idx_d, top_scores=sc_d, ws=ws_k)
+        top_host.copy_(idx_d, non_blocking=True)
         ev_ids.record(comp)
         ev_ids.synchronize()
         ml = ops.fetch_docs(top_host, store, off_host, staging, Mmax, side, ev_fetch)
@@ -159,16 +182,14 @@ def main():
         comp.wait_event(ev_fetch)
         ops.sparse_attn_decode(Q[layer], Kl[layer], Vl[layer], staging, staging[:, :, 1], 2 * H * D, Mmax, ml_dev,
                                k, w.rope_base, out=O_out)
-        if rec is not None:
-            ev_a1[rec].record(comp)
-        return top_host
 
     # ---------------------------------------------------------------- warmup
-    for s in range(args.warmup):
+    selected = []
+    for s_ in range(args.warmup):
         for layer in range(L):
-            ids = layer_step(layer)
-            if s == 0:
-                selected.append(ids.numpy()[0].copy())
+            layer_step(layer)
+            if s_ == 0:
+                selected.append(idx_d.cpu().numpy()[0].copy())
     torch.cuda.synchronize()
     needles_found = sum(int(d in selected[layer]) for layer in range(L) for (_, d) in C.planted_docs(w, layer))
     log(f"warmup done; planted needles retrieved: {needles_found}/{L * w.n_needles}")
@@ -176,72 +197,111 @@ def main():
     # ----------------------------------------------------------------- timed
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    for s in range(args.steps):
+    for s_ in range(args.steps):
         for layer in range(L):
-            layer_step(layer, rec=s * L + layer)
+            layer_step(layer, rec=s_ * L + layer)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     ms_step = elapsed * 1e3 / args.steps
     route_ms = np.array([a.elapsed_time(b) for a, b in zip(ev_r0, ev_r1)])
     layer_ms = np.array([a.elapsed_time(b) for a, b in zip(ev_r0, ev_a1)])
     tokens_per_s = w.n_tok * L * args.steps / elapsed
+    log(f"timed {args.steps} steps: {ms_step:.2f} ms/step")
 
     # ------------------------------------------------------- side measurements
-    # decode (Tq = 1) attention, device-side gather path, pooling throughput
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def time_ms(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    # the step with the host round trip and hipMemcpyAsync fetch
+    for layer in range(L):
+        layer_step_host_fetch(layer)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(3):
+        for layer in range(L):
+            layer_step_host_fetch(layer)
+    torch.cuda.synchronize()
+    host_fetch_step_ms = (time.perf_counter() - t0) * 1e3 / 3
     q1 = Q[0][:, -1:].contiguous()
-    e0.record()
-    for _ in range(50):
-        ops.sparse_attn_decode(q1, Kl[0], Vl[0], staging, staging[:, :, 1], 2 * H * D, Mmax, ml_dev, k, w.rope_base)
-    e1.record(); torch.cuda.synchronize()
-    decode_attn_us = e0.elapsed_time(e1) * 1e3 / 50
-    e0.record()
-    for _ in range(50):
-        ops.sparse_attn_decode(Q[0], Kl[0], Vl[0], staging, staging[:, :, 1], 2 * H * D, Mmax, ml_dev, k,
-                               w.rope_base, out=O_out)
-    e1.record(); torch.cuda.synchronize()
-    attn_us = e0.elapsed_time(e1) * 1e3 / 50
-    store_dev_view = store  # mapped pinned memory, read by the gather kernel over PCIe
-    gstag = torch.empty_like(staging)
-    e0.record()
-    for layer in range(L):
-        dscore = ops.route_scores(qr[layer], krbar[layer], off_dev, doc_scores=doc, ws=ws_r,
-                                  krbar_inv_norm=knorm[layer])
-        idx, _ = ops.topk_docs(dscore, k, ws=ws_k)
-        mld = ops.gather_docs(idx, store_dev_view, off_dev, gstag, Mmax)
-        ops.sparse_attn_decode(Q[layer], Kl[layer], Vl[layer], gstag, gstag[:, :, 1], 2 * H * D, Mmax, mld, k,
-                               w.rope_base, out=O_out)
-    e1.record(); torch.cuda.synchronize()
-    gather_step_ms = e0.elapsed_time(e1)
+    decode_attn_us = 1e3 * time_ms(lambda: ops.sparse_attn_decode(q1, Kl[0], Vl[0], staging, staging[:, :, 1], 2 * H * D,
+                                                                  Mmax, ml_dev, k, w.rope_base), 50)
+    attn_us = 1e3 * time_ms(lambda: ops.sparse_attn_decode(Q[0], Kl[0], Vl[0], staging, staging[:, :, 1], 2 * H * D,
+                                                           Mmax, ml_dev, k, w.rope_base, out=O_out), 50)
+    topk_us = 1e3 * time_ms(lambda: ops.topk_docs(doc, k, top_idx=idx_d, top_scores=sc_d, ws=ws_k), 50)
+    gather_us = 1e3 * time_ms(lambda: ops.gather_docs(idx_d, store, off_dev, staging, Mmax, mem_len=ml_dev), 50)
+    route_nonorm_ms = time_ms(lambda: ops.route_scores(qr[0], krbar[0], off_dev, doc_scores=doc, ws=ws_r), 10)
 
-    # the same scan without stored norms (the kernel derives them from the tiles it streams)
-    e0.record()
-    for layer in range(L):
-        ops.route_scores(qr[layer], krbar[layer], off_dev, doc_scores=doc, ws=ws_r)
-    e1.record(); torch.cuda.synchronize()
-    route_nonorm_ms = e0.elapsed_time(e1) / L
+    log("side measurements: host-fetch step, attention, top-k, gather done")
+    # the 10M-token batch-16 scan: 16 queries x 64 tokens over 165K chunks (matrix-core bound)
+    w3 = C.config(3)
+    kr3 = torch.empty((w3.n_chunks, H, D), dtype=torch.int16, device=dev)
+    native.fill_normal_bf16_device(kr3, w3.seed, sm.TID_KRBAR, 0, 0)
+    for g, row in C.pooled_plants(w3, 0).items():
+        kr3[g].copy_(bits(row))
+    kn3 = ops.krbar_inv_norms(kr3)
+    qr3 = bits(C.queries(w3, 0)["Qr"])
+    off3 = torch.from_numpy(w3.doc_chunk_off).to(dev)
+    doc3 = torch.empty((w3.B, w3.n_docs), dtype=torch.float32, device=dev)
+    ws3 = ops.workspace(ops.route_workspace_bytes(w3.B, w3.T, H, D, w3.n_chunks, w3.n_docs), dev, "bench-route3")
+    scan3_ms = time_ms(lambda: ops.route_scores(qr3, kr3, off3, doc_scores=doc3, ws=ws3, krbar_inv_norm=kn3), 20)
+    scan3_tflops = 2.0 * w3.B * w3.T * H * D * w3.n_chunks / (scan3_ms * 1e-3) / 1e12
+    del kr3, kn3, doc3
 
-    # pooling throughput on a 1M-token slab of the 10M-token interleave corpus
+    log(f"10M batch-16 scan: {scan3_ms:.3f} ms")
+    # pooling throughput, then the interleave workload's rounds (10M tokens, 4 queries, 3 rounds, top-8)
+    from sparse_retrieval_memory_amd.interleave import Interleave
     w5 = C.config(5)
-    d1 = int(np.searchsorted(w5.doc_tok_off, 1_000_000))
-    ntok, nch = int(w5.doc_tok_off[d1]), int(w5.doc_chunk_off[d1])
-    raw = []
-    for tid in (sm.TID_K, sm.TID_V, sm.TID_KR):
-        t = torch.empty((ntok, H, D), dtype=torch.int16, device=dev)
-        native.fill_normal_bf16_device(t, w5.seed, tid, 0, 0)
-        raw.append(t)
-    tok_off5 = torch.from_numpy(w5.doc_tok_off[:d1 + 1].copy()).to(dev)
-    ch_off5 = torch.from_numpy(w5.doc_chunk_off[:d1 + 1].copy()).to(dev)
-    pooled = tuple(torch.empty((nch, H, D), dtype=torch.int16, device=dev) for _ in range(3))
-    for _ in range(2):
-        ops.pool_chunks(*raw, tok_off5, ch_off5, nch, w5.chunk, w5.rope_base, out=pooled)
-    e0.record()
-    for _ in range(10):
-        ops.pool_chunks(*raw, tok_off5, ch_off5, nch, w5.chunk, w5.rope_base, out=pooled)
-    e1.record(); torch.cuda.synchronize()
-    pool_us = e0.elapsed_time(e1) * 1e3 / 10
-    pool_bytes = 3 * ntok * H * D * 2 + 3 * nch * H * D * 2
-    del raw, pooled
+    E = w5.row_elems
+    pooled5 = tuple(torch.empty((w5.n_chunks, H, D), dtype=torch.int16, device=dev) for _ in range(3))
+    plants5 = C.raw_plants(w5)
+    pool_us, pool_bytes = [], 0
+    d0 = 0
+    while d0 < w5.n_docs:
+        d1 = min(max(int(np.searchsorted(w5.doc_tok_off, w5.doc_tok_off[d0] + 1_000_000, side="right")) - 1, d0 + 1),
+                 w5.n_docs)
+        t0_, t1_ = int(w5.doc_tok_off[d0]), int(w5.doc_tok_off[d1])
+        c0_, c1_ = int(w5.doc_chunk_off[d0]), int(w5.doc_chunk_off[d1])
+        raw = []
+        for tid in (sm.TID_K, sm.TID_V, sm.TID_KR):
+            t = torch.empty((t1_ - t0_, H, D), dtype=torch.int16, device=dev)
+            native.fill_normal_bf16_device(t, w5.seed, tid, 0, t0_ * E)
+            raw.append(t)
+        for tok, row in plants5.items():
+            if t0_ <= tok < t1_:
+                raw[2][tok - t0_].copy_(bits(row))
+        tok_off5 = torch.from_numpy(w5.doc_tok_off[d0:d1 + 1].copy()).to(dev)
+        ch_off5 = torch.from_numpy(w5.doc_chunk_off[d0:d1 + 1].copy()).to(dev)
+        outs = tuple(o[c0_:c1_] for o in pooled5)
+        pool_us.append(1e3 * time_ms(lambda: ops.pool_chunks(*raw, tok_off5, ch_off5, c1_ - c0_, w5.chunk,
+                                                             w5.rope_base, out=outs), 3))
+        pool_bytes += 3 * (t1_ - t0_) * H * D * 2 + 3 * (c1_ - c0_) * H * D * 2
+        del raw
+        d0 = d1
+    store5 = torch.stack([pooled5[0], pooled5[1]], dim=1).cpu().pin_memory()
+    q5 = C.queries(w5, 0)
+    il = Interleave(krbar=pooled5[2], doc_chunk_off=torch.from_numpy(w5.doc_chunk_off).to(dev),
+                    doc_chunk_off_host=torch.from_numpy(w5.doc_chunk_off.copy()), content=store5,
+                    krbar_inv_norm=ops.krbar_inv_norms(pooled5[2]), rope_base=w5.rope_base)
+    args5 = (bits(q5["Qr"]), bits(q5["Q"]), bits(q5["Kloc"]), bits(q5["Vloc"]), w5.k, w5.rounds)
+    il.run(*args5)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    res5 = il.run(*args5)
+    torch.cuda.synchronize()
+    interleave_ms = (time.perf_counter() - t0) * 1e3
+    chains_ok = sum(int(ch["A"] in res5[0].top_idx[b] and ch["B"] in res5[1].top_idx[b] and
+                        ch["C"] in res5[2].top_idx[b]) for b, ch in enumerate(C.chains(w5)))
+    del pooled5, store5
+    log(f"interleave: 3 rounds in {interleave_ms:.2f} ms, chains {chains_ok}/{w5.B}")
 
     # ---------------------------------------------------------------- report
     route_bytes = G * H * D * 2 + G * H * 4 + 8 * (w.n_docs + 1) + w.B * w.T * H * D * 2 + 4 * w.B * w.n_docs
@@ -256,6 +316,8 @@ def main():
     if args.cpu_baseline_seconds > 0:
         log("timing the oracle on the host ...")
         cpu = cpu_baseline(w, args.cpu_baseline_seconds)
+    pct = lambda a: {"median": float(np.median(a)), "p10": float(np.percentile(a, 10)),
+                     "p90": float(np.percentile(a, 90)), "mean": float(np.mean(a)), "n": int(len(a))}
     out = {
         "metric": "memory tokens/s routed per query (Krbar scan GB/s) + route+attn step latency",
         "value": tokens_per_s,
@@ -272,22 +334,27 @@ def main():
         "config": {"workload": "100M-token memory, 18 routed layers, batch 1, 128-token query, top-16",
                    "n_docs": w.n_docs, "memory_tokens": w.n_tok, "n_chunks": G, "layers": L,
                    "router_heads": H, "head_dim": D, "q_heads": w.Hq, "chunk": w.chunk, "top_k": k,
-                   "step": "18 x (route -> top-k -> ids to host -> hipMemcpyAsync fetch (side stream) -> attend)"},
+                   "step": "18 x (route -> top-k -> assemble selected K/V from the pinned host tier by a device "
+                           "kernel -> attend), one stream"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "msa_route_scores (scan + document max), bytes = Krbar + its stored norms + "
                                "doc offsets + Qr + doc scores"},
         "cpu_baseline": cpu,
-        "route_ms_per_layer": {"mean": float(route_ms.mean()), "p10": float(np.percentile(route_ms, 10)),
-                               "p90": float(np.percentile(route_ms, 90))},
-        "layer_latency_ms": {"mean": float(layer_ms.mean()), "p10": float(np.percentile(layer_ms, 10)),
-                             "p90": float(np.percentile(layer_ms, 90))},
+        "route_ms_per_layer": pct(route_ms),
+        "layer_latency_ms": pct(layer_ms),
         "krbar_scan_GBps": achieved,
-        "route_ms_per_layer_norms_in_kernel": route_nonorm_ms,
         "memory_tokens_per_s_per_layer": w.n_tok / route_avg_s,
+        "host_fetch_step_ms": host_fetch_step_ms,
+        "route_ms_norms_in_kernel": route_nonorm_ms,
+        "topk_us": topk_us,
+        "gather_us": gather_us,
         "attn_us": {"tq128": attn_us, "tq1_decode": decode_attn_us},
-        "device_gather_18layer_step_ms": gather_step_ms,
-        "pool_GBps": pool_bytes / (pool_us * 1e-6) / 1e9,
+        "scan_10M_batch16": {"ms": scan3_ms, "TFLOPs": scan3_tflops,
+                             "mfma_frac": scan3_tflops / MFMA_BF16_PEAK_TFLOPS},
+        "pool_GBps": pool_bytes / (sum(pool_us) * 1e-6) / 1e9,
+        "interleave_10M_b4_3rounds_ms": interleave_ms,
+        "interleave_chains_recovered": f"{chains_ok}/{w5.B}",
         "needles_retrieved": f"{needles_found}/{L * w.n_needles}",
     }
     print(json.dumps(out), flush=True)
