@@ -84,12 +84,38 @@ def cpu_baseline(w, seconds: float):
                       f"fp64 numpy, {t_total:.1f} s"}
 
 
+def route_only(w, n, dev):
+    """One layer of the 100M-token store routed n times, after a 1 GiB device-to-device copy."""
+    import torch
+    from sparse_retrieval_memory_amd import ops
+    from synth import configs as C
+    from synth import native
+    from synth import splitmix as sm
+    kr = torch.empty((w.n_chunks, w.H, w.D), dtype=torch.int16, device=dev)
+    native.fill_normal_bf16_device(kr, w.seed, sm.TID_KRBAR, 0, 0)
+    qr = torch.from_numpy(C.queries(w, 0)["Qr"].view(np.int16)).to(dev)
+    off = torch.from_numpy(w.doc_chunk_off).to(dev)
+    nrm = ops.krbar_inv_norms(kr)
+    a = torch.empty(1 << 29, dtype=torch.int16, device=dev)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    for _ in range(n):
+        ops.route_scores(qr, kr, off, krbar_inv_norm=nrm)
+    torch.cuda.synchronize()
+    print(json.dumps({"route_only": n, "copy_bytes": a.numel() * 2, "n_chunks": w.n_chunks,
+                      "source_hash": route_source_hash()}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
+    ap.add_argument("--route-only", type=int, default=0, metavar="N",
+                    help="counter-collection mode: one 100M-token layer, a 1 GiB device copy (the reference for "
+                         "scaling FETCH_SIZE/WRITE_SIZE), then N routing calls; prints one line and exits")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share only (--gpus {args.gpus} requested); the path is not "
@@ -105,6 +131,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = C.config(4)
+    if args.route_only:
+        route_only(w, args.route_only, dev)
+        return
     G, H, D, L, k = w.n_chunks, w.H, w.D, w.n_layers, w.k
     log(f"workload {w.name}: {w.n_docs} docs, {w.n_tok} tokens, {G} chunks, {L} layers")
 

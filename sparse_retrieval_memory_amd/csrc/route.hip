@@ -198,13 +198,13 @@ __device__ __forceinline__ void mfma_tile_step(const uint8_t* __restrict__ kr, c
 #pragma unroll
   for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
   const uint8_t* brow = cur + nb * CF::ROW_STRIDE;
-#pragma unroll
-  for (int hh = 0; hh < CF::HPW; ++hh) {
+  // One head: 8 B-operand reads and the MFMA chain over the 128 dims (and, without
+  // stored norms, |k|^2 of this lane's half of chunk nb from the same reads).
+  auto head_mfma = [&](int hh, f32x16_t& acc, float& ss) {
     const int h = hs * CF::HPW + hh;
-    f32x16_t acc;
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-    float ss = 0.f;                           // |k|^2 over this lane's 64 of chunk nb's dims
+    ss = 0.f;
 #pragma unroll
     for (int k4 = 0; k4 < 8; k4 += 4) {
       bf16x8_t bv[4];
@@ -220,6 +220,10 @@ __device__ __forceinline__ void mfma_tile_step(const uint8_t* __restrict__ kr, c
         if constexpr (!NORMS) ss = sq_norm_piece(__builtin_bit_cast(uint4, bv[ks]), ss);
       }
     }
+  };
+  // Epilogue of one head: scale by 1/|k| (column) and 1/|q| (row) and add into the head sum.
+  auto head_epilogue = [&](int hh, const f32x16_t& acc, float ss) {
+    const int h = hs * CF::HPW + hh;
     float rk;
     if constexpr (NORMS) {
       rk = cur_rk[nb * H + h];
@@ -235,7 +239,21 @@ __device__ __forceinline__ void mfma_tile_step(const uint8_t* __restrict__ kr, c
       sacc[4 * q4 + 2] = fmaf(acc[4 * q4 + 2], rk * rq.z, sacc[4 * q4 + 2]);
       sacc[4 * q4 + 3] = fmaf(acc[4 * q4 + 3], rk * rq.w, sacc[4 * q4 + 3]);
     }
-    // keep heads from being interleaved by the scheduler: bounds register pressure
+  };
+  // Software pipeline over the heads: head hh + 1's MFMA chain is issued before head hh's
+  // epilogue, so the matrix unit keeps working while the vector unit finishes the previous
+  // head; at most two heads are in flight (a scheduling fence ends each step).
+  f32x16_t acc_a, acc_b;
+  float ss_a = 0.f, ss_b = 0.f;
+  head_mfma(0, acc_a, ss_a);
+#pragma unroll
+  for (int hh = 0; hh < CF::HPW; ++hh) {
+    f32x16_t& cur_acc = (hh & 1) ? acc_b : acc_a;
+    f32x16_t& nxt_acc = (hh & 1) ? acc_a : acc_b;
+    float& cur_ss = (hh & 1) ? ss_b : ss_a;
+    float& nxt_ss = (hh & 1) ? ss_a : ss_b;
+    if (hh + 1 < CF::HPW) head_mfma(hh + 1, nxt_acc, nxt_ss);
+    head_epilogue(hh, cur_acc, cur_ss);
     __builtin_amdgcn_sched_barrier(0);
   }
   if constexpr (CF::HS == 2) {
@@ -476,18 +494,21 @@ route_valu_kernel(const uint16_t* __restrict__ Qr, int B, int T,
 }
 
 // ------------------------------------------------------ stored key norms
-// 1/|Krbar[g, h]| for every chunk and head, fp32 [n_chunks, H]; one thread per
-// (chunk, head).  Built once per routing-key store (offline, beside the store)
-// so the online scan needs no norm pass of its own.
+// 1/|Krbar[g, h]| for every chunk and head, fp32 [n_chunks, H].  Built once per
+// routing-key store (offline, beside the store) so the online scan needs no
+// norm pass of its own.  16 lanes share one 256-byte (chunk, head) row: each
+// reads 16 contiguous bytes (the wave reads 1 KB contiguous), then the 16
+// partial sums are added across the lanes.
 __global__ void __launch_bounds__(256)
 krbar_norms_kernel(const uint16_t* __restrict__ Krbar, int64_t n_rows, float* __restrict__ out) {
-  const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (r >= n_rows) return;
-  const uint4* p = reinterpret_cast<const uint4*>(Krbar + r * D);
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t r = t >> 4;
+  const int piece = (int)(t & 15);
   float ss = 0.f;
+  if (r < n_rows) ss = sq_norm_piece(reinterpret_cast<const uint4*>(Krbar + r * D)[piece], 0.f);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) ss = sq_norm_piece(p[i], ss);
-  out[r] = inv_norm_fast(ss);
+  for (int m = 1; m < 16; m <<= 1) ss += __shfl_xor(ss, m);
+  if (r < n_rows && piece == 0) out[r] = inv_norm_fast(ss);
 }
 
 // ------------------------------------------------------------ document max
@@ -581,8 +602,8 @@ size_t route_workspace(int B, int T, int H, int64_t n_chunks, int64_t n_docs) {
 int launch_krbar_norms(const uint16_t* Krbar, int64_t n_chunks, int H, float* inv_norm, hipStream_t stream) {
   const int64_t rows = n_chunks * H;
   if (rows == 0) return MSA_OK;
-  hipLaunchKernelGGL(krbar_norms_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream, Krbar, rows,
-                     inv_norm);
+  hipLaunchKernelGGL(krbar_norms_kernel, dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0, stream, Krbar,
+                     rows, inv_norm);
   MSA_CHECK_LAUNCH();
   return MSA_OK;
 }
