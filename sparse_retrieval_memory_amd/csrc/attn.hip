@@ -18,8 +18,11 @@
 // and weighted sums keep ~2^-16 relative accuracy instead of bf16's 2^-8.
 // Memory keys and V are bf16 already (no lo part); rotated local keys and
 // queries, and the probabilities, are split.  RoPE angles are reduced in fp64
-// (position x frequency in revolutions) and evaluated in fp32.  Scores are
-// pre-scaled by scale * log2(e) so the exponentials are exp2.
+// (position x frequency in revolutions) and evaluated in fp32; up to 128 local
+// positions the workgroup first builds a cos/sin table in LDS (an exact value
+// every 32 positions, one-position rotations in between) that the query rows
+// and local keys read.  Scores are pre-scaled by scale * log2(e) so the
+// exponentials are exp2.
 #include "msa_internal.h"
 
 #include <math.h>
@@ -83,12 +86,35 @@ __device__ __forceinline__ void rotate_pairs(float (&lo)[8], float (&hi)[8], int
   }
 }
 
+// The same rotation with cos/sin read from a table: cs[p][i] = (cos, sin) of
+// position base + p at frequency i (the table of the workgroup's positions).
+__device__ __forceinline__ void rotate_pairs_tab(float (&lo)[8], float (&hi)[8], const float2* cs_row, int d0) {
+  const float4* t = reinterpret_cast<const float4*>(cs_row + d0);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float4 v = t[q];
+    const float c0 = v.x, s0 = v.y, c1 = v.z, s1 = v.w;
+    float x1 = lo[2 * q], x2 = hi[2 * q];
+    lo[2 * q] = x1 * c0 - x2 * s0;
+    hi[2 * q] = x2 * c0 + x1 * s0;
+    x1 = lo[2 * q + 1]; x2 = hi[2 * q + 1];
+    lo[2 * q + 1] = x1 * c1 - x2 * s1;
+    hi[2 * q + 1] = x2 * c1 + x1 * s1;
+  }
+}
+
+constexpr int TAB_POS = 128;    // positions the LDS cos/sin table covers (local keys and queries)
+constexpr int TAB_SEG = 32;     // positions one thread steps through from an exact start
+
 __global__ void __launch_bounds__(THREADS, 1)
 attn_mfma_kernel(const uint16_t* __restrict__ Q, int Tq, int Hq, const uint16_t* __restrict__ Kloc,
                  const uint16_t* __restrict__ Vloc, int Tl, int Hkv, const uint16_t* __restrict__ Kmem,
                  const uint16_t* __restrict__ Vmem, int64_t mstride, int Mmax, const int32_t* __restrict__ mem_len,
                  int rope_offset, double log2_base, float scale_log2e, float* __restrict__ O) {
   __shared__ double rev[D / 2];
+  // cos/sin of positions rope_offset + p (p < n_local <= TAB_POS), frequency i: every query row
+  // and local key of this workgroup sits at such a position
+  __shared__ __attribute__((aligned(16))) float2 cs_tab[TAB_POS][D / 2];
   // per wave: V^T of its current tile [D][VT_STRIDE] bf16; reused at the end for the merge
   __shared__ __attribute__((aligned(16))) float smem[NWAVE * D * RT];
   static_assert(sizeof(smem) >= sizeof(uint16_t) * NWAVE * D * VT_STRIDE, "V^T area");
@@ -112,6 +138,25 @@ attn_mfma_kernel(const uint16_t* __restrict__ Q, int Tq, int Hq, const uint16_t*
 
   if (tid < D / 2) rev[tid] = exp2(-(2.0 * tid / D) * log2_base) * 0.15915494309189535;   // / (2 pi)
   __syncthreads();
+  // Table for n_local <= TAB_POS: thread (frequency i, segment sg) starts from the exact angle at the
+  // segment's first position and steps by the exact one-position rotation (error ~1e-6 after 32 steps).
+  const bool use_tab = n_local <= TAB_POS;
+  if (use_tab) {
+    const int i = tid & (D / 2 - 1), sg = tid / (D / 2);
+    for (int p0 = sg * TAB_SEG; p0 < n_local; p0 += (THREADS / (D / 2)) * TAB_SEG) {
+      float c, s_, cd, sd;
+      rope_cs(rope_offset + p0, rev[i], &c, &s_);
+      rope_cs(1, rev[i], &cd, &sd);
+      const int p1 = p0 + TAB_SEG < n_local ? p0 + TAB_SEG : n_local;
+      for (int p = p0; p < p1; ++p) {
+        cs_tab[p][i] = make_float2(c, s_);
+        const float cn = c * cd - s_ * sd;
+        s_ = s_ * cd + c * sd;
+        c = cn;
+      }
+    }
+    __syncthreads();
+  }
 
   // ---- Q^T as the B operand: lane (col, hf) holds query row r0 + col, dims 16 ks + 8 hf + j
   bf16x8_t qh[8], ql[8];
@@ -125,9 +170,14 @@ attn_mfma_kernel(const uint16_t* __restrict__ Q, int Tq, int Hq, const uint16_t*
         unpack8(*reinterpret_cast<const uint4*>(q + 16 * ks + 8 * hf), lo[ks]);
         unpack8(*reinterpret_cast<const uint4*>(q + 64 + 16 * ks + 8 * hf), hi[ks]);
       }
-      const int pos = rope_offset + (Tl - Tq) + row;
+      const int p = (Tl - Tq) + row;
+      if (use_tab) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) rotate_pairs(lo[ks], hi[ks], pos, rev, 16 * ks + 8 * hf);
+        for (int ks = 0; ks < 4; ++ks) rotate_pairs_tab(lo[ks], hi[ks], cs_tab[p], 16 * ks + 8 * hf);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) rotate_pairs(lo[ks], hi[ks], rope_offset + p, rev, 16 * ks + 8 * hf);
+      }
     } else {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
@@ -156,11 +206,11 @@ attn_mfma_kernel(const uint16_t* __restrict__ Q, int Tq, int Hq, const uint16_t*
   const int lim = (Tl - Tq) + qrow;      // last visible local key of this row
   uint16_t (*myvt)[VT_STRIDE] = reinterpret_cast<uint16_t (*)[VT_STRIDE]>(smem) + wave * D;
 
-  for (int t = wave; t < n_tiles; t += NWAVE) {
-    const int k0 = t * KT;
-    // ---- K tile as the A operand: lane (col, hf) holds key k0 + col, dims 16 ks + 8 hf + j
-    const int j = k0 + col;
-    bool local = false;
+  // Raw K and V of key tile t for this lane (key k0 + col): K dims 16 (ks % 4) + 64 (ks / 4) + 8 hf + e
+  // (the A-operand order), V dims 64 hf + 8 i + e.  Keys past the end read as zeros.
+  auto load_tile = [&](int t, uint4 (&kr)[8], uint4 (&vr)[8], bool& local) {
+    const int j = t * KT + col;
+    local = false;
     const uint16_t *kp = nullptr, *vp = nullptr;
     if (j < M) {
       kp = Kmem + ((int64_t)b * Mmax + j) * mstride + (int64_t)g * D;
@@ -170,20 +220,34 @@ attn_mfma_kernel(const uint16_t* __restrict__ Q, int Tq, int Hq, const uint16_t*
       kp = Kloc + (((int64_t)b * Tl + (j - M)) * Hkv + g) * D;
       vp = Vloc + (((int64_t)b * Tl + (j - M)) * Hkv + g) * D;
     }
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      kr[ks] = kp ? *reinterpret_cast<const uint4*>(kp + 16 * (ks & 3) + 64 * (ks >> 2) + 8 * hf)
+                  : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      vr[i] = vp ? *reinterpret_cast<const uint4*>(vp + 64 * hf + 8 * i) : make_uint4(0, 0, 0, 0);
+  };
+
+  uint4 kc[8], vc[8];
+  bool lc = false;
+  if (wave < n_tiles) load_tile(wave, kc, vc, lc);
+  for (int t = wave; t < n_tiles; t += NWAVE) {
+    const int k0 = t * KT;
+    const int j = k0 + col;
+    // prefetch this wave's next tile while the current one is scored
+    uint4 kn[8], vn[8];
+    bool ln = false;
+    if (t + NWAVE < n_tiles) load_tile(t + NWAVE, kn, vn, ln);
+    const bool local = lc;
     // V tile -> LDS, transposed: myvt[dim][key]; lane (col, hf) copies dims [64 hf, 64 hf + 64) of key col
-    {
-      uint4 vv[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        vv[i] = vp ? *reinterpret_cast<const uint4*>(vp + 64 * hf + 8 * i) : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t w4[4] = {vc[i].x, vc[i].y, vc[i].z, vc[i].w};
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t w4[4] = {vv[i].x, vv[i].y, vv[i].z, vv[i].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          myvt[64 * hf + 8 * i + 2 * e][col] = (uint16_t)(w4[e] & 0xFFFFu);
-          myvt[64 * hf + 8 * i + 2 * e + 1][col] = (uint16_t)(w4[e] >> 16);
-        }
+      for (int e = 0; e < 4; ++e) {
+        myvt[64 * hf + 8 * i + 2 * e][col] = (uint16_t)(w4[e] & 0xFFFFu);
+        myvt[64 * hf + 8 * i + 2 * e + 1][col] = (uint16_t)(w4[e] >> 16);
       }
     }
     f32x16_t s;
@@ -194,9 +258,7 @@ attn_mfma_kernel(const uint16_t* __restrict__ Q, int Tq, int Hq, const uint16_t*
       // memory keys only: exact bf16 operands, Q split in two
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        const uint4 kv = kp ? *reinterpret_cast<const uint4*>(kp + 16 * (ks & 3) + 64 * (ks >> 2) + 8 * hf)
-                            : make_uint4(0, 0, 0, 0);
-        const bf16x8_t kb = __builtin_bit_cast(bf16x8_t, kv);
+        const bf16x8_t kb = __builtin_bit_cast(bf16x8_t, kc[ks]);
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, qh[ks], s, 0, 0, 0);
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, ql[ks], s, 0, 0, 0);
       }
@@ -204,18 +266,17 @@ attn_mfma_kernel(const uint16_t* __restrict__ Q, int Tq, int Hq, const uint16_t*
       float lo[4][8], hi[4][8];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        if (kp) {
-          unpack8(*reinterpret_cast<const uint4*>(kp + 16 * ks + 8 * hf), lo[ks]);
-          unpack8(*reinterpret_cast<const uint4*>(kp + 64 + 16 * ks + 8 * hf), hi[ks]);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) { lo[ks][e] = 0.f; hi[ks][e] = 0.f; }
-        }
+        unpack8(kc[ks], lo[ks]);
+        unpack8(kc[ks + 4], hi[ks]);
       }
       if (local) {
-        const int pos = rope_offset + (j - M);
+        if (use_tab) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) rotate_pairs(lo[ks], hi[ks], pos, rev, 16 * ks + 8 * hf);
+          for (int ks = 0; ks < 4; ++ks) rotate_pairs_tab(lo[ks], hi[ks], cs_tab[j - M], 16 * ks + 8 * hf);
+        } else {
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) rotate_pairs(lo[ks], hi[ks], rope_offset + (j - M), rev, 16 * ks + 8 * hf);
+        }
       }
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
@@ -285,6 +346,9 @@ attn_mfma_kernel(const uint16_t* __restrict__ Q, int Tq, int Hq, const uint16_t*
       }
     }
     __builtin_amdgcn_wave_barrier();      // V^T reads done before the next tile overwrites it
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { kc[i] = kn[i]; vc[i] = vn[i]; }
+    lc = ln;
   }
 
   // ---- merge the waves: O = sum_w 2^(m_w - m) O_w / sum_w 2^(m_w - m) l_w

@@ -10,8 +10,12 @@ offset equal to their count.
 
 This module only sequences the library's calls; every step runs in libmsa's
 kernels (``msa_append_router_rows``, ``msa_route_scores``, ``msa_topk_docs``,
-``msa_fetch_docs``, ``msa_sparse_attn_decode``).  The one host round trip per
-round is the selected ids, which the fetch needs on the host.
+``msa_gather_docs`` or ``msa_fetch_docs``, ``msa_sparse_attn_decode``).  The
+one host round trip per round is the selected ids: the host sizes the next
+round's router rows and the staging buffer from them.  The content is
+assembled on the device from the mapped pinned tier by default
+(``fetch="gather"``); ``fetch="copy"`` uses host-driven hipMemcpyAsync copies
+on a side stream instead.
 """
 
 from __future__ import annotations
@@ -47,7 +51,10 @@ class Interleave:
     side: Optional[torch.cuda.Stream] = None
     _bufs: dict = field(default_factory=dict)
 
-    def run(self, Qr, Q, Kloc, Vloc, k: int, rounds: int, keep_scores: bool = False) -> List[Round]:
+    def run(self, Qr, Q, Kloc, Vloc, k: int, rounds: int, keep_scores: bool = False,
+            fetch: str = "gather") -> List[Round]:
+        if fetch not in ("gather", "copy"):
+            raise ValueError(f"fetch must be 'gather' or 'copy', not {fetch!r}")
         dev = Qr.device
         B, T0, H, D = Qr.shape
         off_h = self.doc_chunk_off_host.numpy()
@@ -73,10 +80,15 @@ class Interleave:
             retrieved = np.concatenate([retrieved, new], axis=1).astype(np.int32)
             Mmax = int(n_chunks_of[retrieved].sum(axis=1).max())
             staging = torch.empty((B, Mmax, 2, H, D), dtype=Qr.dtype, device=dev)
-            ml = ops.fetch_docs(torch.from_numpy(retrieved), self.content, self.doc_chunk_off_host, staging, Mmax,
-                                side, fetched)
-            torch.cuda.current_stream().wait_event(fetched)
-            O = ops.sparse_attn_decode(Q, Kloc, Vloc, staging, staging[:, :, 1], 2 * H * D, Mmax, ml.to(dev),
+            if fetch == "gather":
+                ml = ops.gather_docs(torch.from_numpy(retrieved).to(dev, non_blocking=True), self.content,
+                                     self.doc_chunk_off, staging, Mmax)
+            else:
+                ml = ops.fetch_docs(torch.from_numpy(retrieved), self.content, self.doc_chunk_off_host, staging,
+                                    Mmax, side, fetched)
+                torch.cuda.current_stream().wait_event(fetched)
+                ml = ml.to(dev)
+            O = ops.sparse_attn_decode(Q, Kloc, Vloc, staging, staging[:, :, 1], 2 * H * D, Mmax, ml,
                                        retrieved.shape[1], self.rope_base)
             out.append(Round(top_idx=new, top_scores=sc.cpu().numpy(), retrieved=retrieved.copy(), n_rows=n_rows,
                              O=O, doc_scores=doc if keep_scores else None))

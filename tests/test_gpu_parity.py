@@ -189,7 +189,8 @@ def test_pool_slab_with_offset_bases():
 # ------------------------------------------------------------------ attention
 @pytest.mark.parametrize("B,Tq,Tl,M,offset", [(1, 32, 32, 32, 4), (1, 1, 128, 262, 16), (1, 128, 128, 262, 16),
                                               (2, 64, 64, 133, 16), (1, 5, 9, 0, 0), (1, 17, 40, 1, 3),
-                                              (3, 16, 16, 70, 8), (1, 128, 128, 448, 16)])
+                                              (3, 16, 16, 70, 8), (1, 128, 128, 448, 16),
+                                              (1, 64, 200, 40, 7), (2, 1, 300, 5, 2)])
 def test_attention_matches_oracle(B, Tq, Tl, M, offset):
     announce("attn", B, Tq, Tl, M, offset)
     seed = B * 1000 + Tq + M

@@ -230,7 +230,7 @@ def oracle_pool_docs(w, docs):
     return res
 
 
-def interleave_on_gpu(w, pooled, q):
+def interleave_on_gpu(w, pooled, q, fetch="gather"):
     from sparse_retrieval_memory_amd.interleave import Interleave
     Kb, Vb, Rb = pooled
     store = torch.stack([Kb, Vb], dim=1).cpu().pin_memory()
@@ -238,7 +238,7 @@ def interleave_on_gpu(w, pooled, q):
                     doc_chunk_off_host=torch.from_numpy(w.doc_chunk_off.copy()), content=store,
                     krbar_inv_norm=ops.krbar_inv_norms(Rb), rope_base=w.rope_base)
     res = il.run(dev_bits(q["Qr"]), dev_bits(q["Q"]), dev_bits(q["Kloc"]), dev_bits(q["Vloc"]), w.k, w.rounds,
-                 keep_scores=True)
+                 keep_scores=True, fetch=fetch)
     torch.cuda.synchronize()
     return res
 
@@ -259,6 +259,11 @@ def test_cfg5_interleave_reduced_against_oracle():
     assert pooled_k_ok(host_bits(pooled[0]), rK)
     q = C.queries(w)
     res = interleave_on_gpu(w, pooled, q)
+    # the host-copy assembly gives bit-identical rounds
+    res_copy = interleave_on_gpu(w, pooled, q, fetch="copy")
+    for r in range(w.rounds):
+        assert np.array_equal(res[r].retrieved, res_copy[r].retrieved)
+        assert torch.equal(res[r].O, res_copy[r].O)
     for b, ch in enumerate(C.chains(w)):
         ref = O.interleave(f32(q["Qr"][b]), rR, rK, rV, off, w.k, w.rounds, f32(q["Q"][b]), f32(q["Kloc"][b]),
                            f32(q["Vloc"][b]), w.rope_base, w.D ** -0.5)
