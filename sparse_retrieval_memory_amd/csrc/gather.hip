@@ -13,6 +13,7 @@ namespace msa {
 namespace {
 
 constexpr int THREADS = 256;
+constexpr int GATHER_SPLIT = 8;   // workgroups per selected document
 
 __global__ void __launch_bounds__(THREADS)
 gather_kernel(const int32_t* __restrict__ top_idx, int k, const uint16_t* __restrict__ host_store,
@@ -39,13 +40,16 @@ gather_kernel(const int32_t* __restrict__ top_idx, int k, const uint16_t* __rest
     sh_dst = before;
     sh_src = mine_src;
     sh_n = n;
-    if (r == 0) mem_len[b] = (int32_t)(total < Mmax ? total : Mmax);
+    if (r == 0 && blockIdx.z == 0) mem_len[b] = (int32_t)(total < Mmax ? total : Mmax);
   }
   __syncthreads();
+  // blockIdx.z splits one document's copy over several workgroups: reads over the host
+  // link are latency-bound, so more of them in flight is what speeds the copy up
   const int64_t vecs = sh_n * entry_elems / 8;    // 16-byte vectors
   const uint4* src = reinterpret_cast<const uint4*>(host_store + sh_src * entry_elems);
   uint4* dst = reinterpret_cast<uint4*>(staging + ((int64_t)b * Mmax + sh_dst) * entry_elems);
-  for (int64_t i = threadIdx.x; i < vecs; i += THREADS) dst[i] = src[i];
+  for (int64_t i = (int64_t)blockIdx.z * THREADS + threadIdx.x; i < vecs; i += (int64_t)gridDim.z * THREADS)
+    dst[i] = src[i];
 }
 
 // Router rows for the next interleave round (medium write-up sec. 4C and
@@ -112,7 +116,7 @@ int launch_gather(const int32_t* top_idx, int B, int k, const uint16_t* host_sto
                   const int64_t* doc_chunk_off, int64_t n_docs, int H, uint16_t* staging, int Mmax,
                   int32_t* mem_len, hipStream_t stream) {
   const int64_t entry_elems = 2LL * H * 128;
-  hipLaunchKernelGGL(gather_kernel, dim3((unsigned)k, (unsigned)B), dim3(THREADS), 0, stream, top_idx, k,
+  hipLaunchKernelGGL(gather_kernel, dim3((unsigned)k, (unsigned)B, GATHER_SPLIT), dim3(THREADS), 0, stream, top_idx, k,
                      host_store, doc_chunk_off, n_docs, entry_elems, staging, Mmax, mem_len);
   MSA_CHECK_LAUNCH();
   return MSA_OK;
