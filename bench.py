@@ -30,6 +30,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -47,10 +48,19 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
+def code_text(src: str) -> str:
+    """Source text with comments, trailing blanks and empty lines removed."""
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    lines = (re.sub(r"//.*", "", ln).rstrip() for ln in src.splitlines())
+    return "\n".join(ln for ln in lines if ln)
+
+
 def route_source_hash() -> str:
+    """Fingerprint of the scan kernel's code (comment edits leave it unchanged)."""
     h = hashlib.sha256()
     for f in ("route.hip", "msa_internal.h"):
-        h.update(open(os.path.join(ROOT, "sparse_retrieval_memory_amd", "csrc", f), "rb").read())
+        with open(os.path.join(ROOT, "sparse_retrieval_memory_amd", "csrc", f)) as fh:
+            h.update(code_text(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

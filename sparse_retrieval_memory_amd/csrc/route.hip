@@ -8,15 +8,17 @@
 // kernels are built around streaming it at HBM rate:
 //
 //  * MFMA path (rows = B*T > 15): each workgroup keeps 128 router rows
-//    resident in registers (4 waves x 32 rows x all heads, bf16 MFMA A
-//    operands) and streams 64 KB tiles of 32 chunks through LDS with
-//    asynchronous global->LDS DMA (double buffered, XOR-swizzled so the MFMA
-//    B-operand reads are bank-conflict free).  Per head: 8 x
+//    resident in registers (8 waves: 4 row tiles of 32 x 2 head groups, bf16
+//    MFMA A operands) and streams tiles of 32 chunks (64 KB for 8 heads)
+//    through LDS with asynchronous global->LDS DMA, double buffered; chunk
+//    rows are skewed by 16 bytes (XOR-swizzled pieces for H <= 2) so the
+//    MFMA B-operand reads are bank-conflict free.  Per head: 8 x
 //    v_mfma_f32_32x32x16_bf16 on the raw bf16 operands (exact products, fp32
 //    accumulation), then an fp32 epilogue multiplies by 1/|q| and 1/|k| and
-//    adds into the head sum; the token max is a register max plus one
-//    cross-lane step, combined across waves/workgroups with an integer
-//    atomicMax on an order-preserving encoding (deterministic).
+//    adds into the head sum (overlapped with the next head's MFMAs); the
+//    token max is a register max plus one cross-lane step, combined across
+//    waves/workgroups with an integer atomicMax on an order-preserving
+//    encoding (deterministic).
 //  * VALU path (rows <= 15): one thread per (chunk, head) holds that 256-byte
 //    slice in registers, dots it with every router row (LDS broadcast reads,
 //    v_dot2_f32_bf16), and a DPP butterfly sums the heads.

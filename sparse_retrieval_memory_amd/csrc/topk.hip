@@ -6,7 +6,7 @@
 // ~doc_id), so "score descending, ties to the lower id" is plain descending
 // integer order and every key is unique -- the selection is exact and
 // deterministic.  k <= 32 (the workloads use 4, 8 and 16): group maxima, then
-// only the winning groups are sorted (below).  Larger k: two passes of a
+// only the winning groups are searched (below).  Larger k: two passes of a
 // block-level routine -- pass 1: (blocks x B) workgroups each reduce a slice
 // of documents to its k best keys; pass 2: one workgroup per query reduces the
 // blocks' candidates to k -- which keeps a running top-k in LDS and
