@@ -84,62 +84,72 @@ struct Cfg {
   static constexpr int DMA_ITERS = BYTES / (16 * THREADS);
 };
 
-// Issue the asynchronous copy of chunk tile `tile` into `lds`.  Each wave
-// instruction moves 1 KB of contiguous global memory (half a chunk row for
-// H = 8) into the row's skewed LDS slot; for H <= 2 LDS slot j instead holds
-// piece (j % PIECES) ^ (n & 15) of chunk n = j / PIECES.  Chunks past the end
-// are clamped to the last chunk (their results are never written).  With stored norms (H >= 4) the tile's
-// fp32 [TC][H] block of 1/|k| follows into `lds_rk` (16-byte granules never
-// straddle a chunk boundary for H >= 4, so clamping is per chunk).
+// Asynchronous copy of chunk tile `tile` into `lds`, piece `i` of Cfg::DMA_ITERS:
+// each wave instruction moves 1 KB of contiguous global memory (half a chunk
+// row for H = 8) into the row's skewed LDS slot; for H <= 2 LDS slot j instead
+// holds piece (j % PIECES) ^ (n & 15) of chunk n = j / PIECES.  Chunks past the
+// end are clamped to the last chunk (their results are never written).
+template <int H>
+__device__ __forceinline__ void issue_piece(const uint8_t* __restrict__ kr, int64_t n_chunks, int64_t tile,
+                                            uint8_t* lds, int wave, int lane, int i) {
+  using CF = Cfg<H>;
+  const bool full = (tile + 1) * TC <= n_chunks;      // uniform: only the last tile needs clamping
+  const int slot0 = (i * CF::NWAVES + wave) * 64;     // wave-uniform
+  int n, pp;
+  if constexpr (CF::PIECES >= 64) {
+    n = slot0 / CF::PIECES;                           // one chunk per wave instruction: uniform
+    pp = slot0 % CF::PIECES + lane;
+  } else {
+    n = (slot0 + lane) / CF::PIECES;
+    pp = (slot0 + lane) % CF::PIECES;
+  }
+  int64_t g = tile * TC + n;
+  if (!full && g >= n_chunks) g = n_chunks - 1;
+  if constexpr (CF::SKEW) {
+    // scalar row base + 32-bit lane offset; LDS destination = the row's skewed slot
+    const uint64_t base = (uint64_t)(kr + g * CF::ROW_BYTES + (slot0 % CF::PIECES) * 16);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+    const uint8_t* sb = (const uint8_t*)(((uint64_t)hi << 32) | lo);
+    dma16(sb + (uint32_t)lane * 16u, lds + n * CF::ROW_STRIDE + (slot0 % CF::PIECES) * 16);
+  } else {
+    const uint32_t off = (uint32_t)((pp ^ (n & 15)) * 16);
+    dma16(kr + g * CF::ROW_BYTES + off, lds + slot0 * 16);
+  }
+}
+
+// With stored norms (H >= 4) the tile's fp32 [TC][H] block of 1/|k| goes into
+// `lds_rk` (one instruction of the last wave; 16-byte granules never straddle a
+// chunk boundary for H >= 4, so clamping is per chunk).
+template <int H>
+__device__ __forceinline__ void issue_norms(const float* __restrict__ knorm, int64_t n_chunks, int64_t tile,
+                                            float* lds_rk, int wave, int lane) {
+  using CF = Cfg<H>;
+  static_assert(H >= 4, "stored norms need 16-byte granules within one chunk");
+  constexpr int GR = CF::RK_BYTES / 16;               // granules per tile (<= 64)
+  const bool full = (tile + 1) * TC <= n_chunks;
+  if (wave == CF::NWAVES - 1 && lane < GR) {
+    if (full) {
+      const uint64_t base = (uint64_t)(knorm + tile * TC * H);
+      const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
+      const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+      dma16((const uint8_t*)(((uint64_t)hi << 32) | lo) + (uint32_t)lane * 16u, lds_rk);
+    } else {
+      const int n = lane * 4 / H;
+      const int64_t g = (tile * TC + n < n_chunks) ? tile * TC + n : n_chunks - 1;
+      dma16(knorm + g * H + (lane * 4) % H, lds_rk);
+    }
+  }
+}
+
+// The whole tile (and its norms block) at once.
 template <int H, bool NORMS>
 __device__ __forceinline__ void issue_tile(const uint8_t* __restrict__ kr, const float* __restrict__ knorm,
                                            int64_t n_chunks, int64_t tile, uint8_t* lds, float* lds_rk,
                                            int wave, int lane) {
-  using CF = Cfg<H>;
-  const bool full = (tile + 1) * TC <= n_chunks;      // uniform: only the last tile needs clamping
 #pragma unroll
-  for (int i = 0; i < CF::DMA_ITERS; ++i) {
-    const int slot0 = (i * CF::NWAVES + wave) * 64;   // wave-uniform
-    int n, pp;
-    if constexpr (CF::PIECES >= 64) {
-      n = slot0 / CF::PIECES;                         // one chunk per wave instruction: uniform
-      pp = slot0 % CF::PIECES + lane;
-    } else {
-      n = (slot0 + lane) / CF::PIECES;
-      pp = (slot0 + lane) % CF::PIECES;
-    }
-    int64_t g = tile * TC + n;
-    if (!full && g >= n_chunks) g = n_chunks - 1;
-    if constexpr (CF::SKEW) {
-      // scalar row base + 32-bit lane offset; LDS destination = the row's skewed slot
-      const uint64_t base = (uint64_t)(kr + g * CF::ROW_BYTES + (slot0 % CF::PIECES) * 16);
-      const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
-      const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
-      const uint8_t* sb = (const uint8_t*)(((uint64_t)hi << 32) | lo);
-      dma16(sb + (uint32_t)lane * 16u, lds + n * CF::ROW_STRIDE + (slot0 % CF::PIECES) * 16);
-    } else {
-      const uint32_t off = (uint32_t)((pp ^ (n & 15)) * 16);
-      dma16(kr + g * CF::ROW_BYTES + off, lds + slot0 * 16);
-    }
-  }
-  if constexpr (NORMS) {
-    // granule `lane` = floats [4 lane, 4 lane + 4) of the tile's [TC][H] block,
-    // i.e. heads (4 lane) % H .. +3 of chunk 4 lane / H (never straddles a chunk for H >= 4)
-    static_assert(H >= 4, "stored norms need 16-byte granules within one chunk");
-    constexpr int GR = CF::RK_BYTES / 16;             // granules per tile (<= 64)
-    if (wave == CF::NWAVES - 1 && lane < GR) {
-      if (full) {
-        const uint64_t base = (uint64_t)(knorm + tile * TC * H);
-        const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
-        const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
-        dma16((const uint8_t*)(((uint64_t)hi << 32) | lo) + (uint32_t)lane * 16u, lds_rk);
-      } else {
-        const int n = lane * 4 / H;
-        const int64_t g = (tile * TC + n < n_chunks) ? tile * TC + n : n_chunks - 1;
-        dma16(knorm + g * H + (lane * 4) % H, lds_rk);
-      }
-    }
-  }
+  for (int i = 0; i < Cfg<H>::DMA_ITERS; ++i) issue_piece<H>(kr, n_chunks, tile, lds, wave, lane, i);
+  if constexpr (NORMS) issue_norms<H>(knorm, n_chunks, tile, lds_rk, wave, lane);
 }
 
 // Token max of a finished 32-row x 32-chunk head sum, then the chunk's atomic max.
@@ -182,7 +192,17 @@ __device__ __forceinline__ void mfma_tile_step(const uint8_t* __restrict__ kr, c
   const int nb = lane & 31;                   // this lane's chunk column in the tile
   wait_vmem_all();
   lds_barrier();                              // tile visible; previous tile fully consumed
-  if (has_next) issue_tile<H, NORMS>(kr, knorm, n_chunks, tile + 1, nxt, nxt_rk, wave, lane);
+  // The next tile's copies are interleaved with this tile's first MFMAs (one after
+  // each), so the waves do not stall on issuing them while the matrix unit idles.  On the last step the copy re-reads the current tile into the unused
+  // buffer instead of branching around every instruction.
+  const int64_t tile_dma = has_next ? tile + 1 : tile;
+  if constexpr (NORMS) {
+    if (has_next) issue_norms<H>(knorm, n_chunks, tile + 1, nxt_rk, wave, lane);
+  }
+  if (!wave_active) {
+#pragma unroll
+    for (int i = 0; i < CF::DMA_ITERS; ++i) issue_piece<H>(kr, n_chunks, tile_dma, nxt, wave, lane, i);
+  }
 
   f32x4_t* x = xchg + lane;                   // layout [q4][lane]: 16-byte lane stride, conflict-free
   if (CF::HS == 2 && has_prev && wave_active && hs == (PAR == 0 ? 1 : 0)) {
@@ -220,6 +240,8 @@ __device__ __forceinline__ void mfma_tile_step(const uint8_t* __restrict__ kr, c
       for (int ks = 0; ks < 4; ++ks) {
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[hh][k4 + ks], bv[ks], acc, 0, 0, 0);
         if constexpr (!NORMS) ss = sq_norm_piece(__builtin_bit_cast(uint4, bv[ks]), ss);
+        const int mf = hh * 8 + k4 + ks;      // MFMA number within the step (compile time)
+        if (mf < CF::DMA_ITERS) issue_piece<H>(kr, n_chunks, tile_dma, nxt, wave, lane, mf);
       }
     }
   };
@@ -366,6 +388,7 @@ route_mfma_kernel(const uint16_t* __restrict__ Qr, int B, int T, int RTq, int P,
       finish_tile(sprev, half, m, t0, T, b, last, n_chunks, 1.0f / H, chunk_enc);
     }
   }
+  wait_vmem_all();                            // the last step's copy lands before the LDS is released
 }
 
 // ------------------------------------------------------------------ VALU path
