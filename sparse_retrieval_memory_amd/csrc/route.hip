@@ -84,37 +84,42 @@ struct Cfg {
   static constexpr int DMA_ITERS = BYTES / (16 * THREADS);
 };
 
-// Asynchronous copy of chunk tile `tile` into `lds`, piece `i` of Cfg::DMA_ITERS:
+// Source of one chunk tile's copies: the tile's first row (wave-uniform, kept in
+// scalar registers) and the last valid row index within the tile.  Chunks past
+// the end are clamped to the last chunk (their results are never written).
+struct TileSrc {
+  const uint8_t* base;
+  int nmax;
+};
+template <int H>
+__device__ __forceinline__ TileSrc tile_src(const uint8_t* __restrict__ kr, int64_t n_chunks, int64_t tile) {
+  const int64_t left = n_chunks - 1 - tile * TC;
+  const uint64_t base = (uint64_t)(kr + tile * TC * Cfg<H>::ROW_BYTES);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+  return TileSrc{(const uint8_t*)(((uint64_t)hi << 32) | lo),
+                 __builtin_amdgcn_readfirstlane(left < TC - 1 ? (int)left : TC - 1)};
+}
+
+// Asynchronous copy of piece `i` (of Cfg::DMA_ITERS) of a chunk tile into `lds`:
 // each wave instruction moves 1 KB of contiguous global memory (half a chunk
 // row for H = 8) into the row's skewed LDS slot; for H <= 2 LDS slot j instead
-// holds piece (j % PIECES) ^ (n & 15) of chunk n = j / PIECES.  Chunks past the
-// end are clamped to the last chunk (their results are never written).
+// holds piece (j % PIECES) ^ (n & 15) of chunk n = j / PIECES.
 template <int H>
-__device__ __forceinline__ void issue_piece(const uint8_t* __restrict__ kr, int64_t n_chunks, int64_t tile,
-                                            uint8_t* lds, int wave, int lane, int i) {
+__device__ __forceinline__ void issue_piece(const TileSrc& src, uint8_t* lds, int wave, int lane, int i) {
   using CF = Cfg<H>;
-  const bool full = (tile + 1) * TC <= n_chunks;      // uniform: only the last tile needs clamping
   const int slot0 = (i * CF::NWAVES + wave) * 64;     // wave-uniform
-  int n, pp;
-  if constexpr (CF::PIECES >= 64) {
-    n = slot0 / CF::PIECES;                           // one chunk per wave instruction: uniform
-    pp = slot0 % CF::PIECES + lane;
-  } else {
-    n = (slot0 + lane) / CF::PIECES;
-    pp = (slot0 + lane) % CF::PIECES;
-  }
-  int64_t g = tile * TC + n;
-  if (!full && g >= n_chunks) g = n_chunks - 1;
   if constexpr (CF::SKEW) {
-    // scalar row base + 32-bit lane offset; LDS destination = the row's skewed slot
-    const uint64_t base = (uint64_t)(kr + g * CF::ROW_BYTES + (slot0 % CF::PIECES) * 16);
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
-    const uint8_t* sb = (const uint8_t*)(((uint64_t)hi << 32) | lo);
+    const int n = slot0 / CF::PIECES;                 // one chunk per wave instruction: uniform
+    const int ne = n < src.nmax ? n : src.nmax;
+    const uint8_t* sb = src.base + ne * CF::ROW_BYTES + (slot0 % CF::PIECES) * 16;
     dma16(sb + (uint32_t)lane * 16u, lds + n * CF::ROW_STRIDE + (slot0 % CF::PIECES) * 16);
   } else {
+    const int n = (slot0 + lane) / CF::PIECES;
+    const int pp = (slot0 + lane) % CF::PIECES;
+    const int ne = n < src.nmax ? n : src.nmax;
     const uint32_t off = (uint32_t)((pp ^ (n & 15)) * 16);
-    dma16(kr + g * CF::ROW_BYTES + off, lds + slot0 * 16);
+    dma16(src.base + ne * CF::ROW_BYTES + off, lds + slot0 * 16);
   }
 }
 
@@ -147,8 +152,9 @@ template <int H, bool NORMS>
 __device__ __forceinline__ void issue_tile(const uint8_t* __restrict__ kr, const float* __restrict__ knorm,
                                            int64_t n_chunks, int64_t tile, uint8_t* lds, float* lds_rk,
                                            int wave, int lane) {
+  const TileSrc src = tile_src<H>(kr, n_chunks, tile);
 #pragma unroll
-  for (int i = 0; i < Cfg<H>::DMA_ITERS; ++i) issue_piece<H>(kr, n_chunks, tile, lds, wave, lane, i);
+  for (int i = 0; i < Cfg<H>::DMA_ITERS; ++i) issue_piece<H>(src, lds, wave, lane, i);
   if constexpr (NORMS) issue_norms<H>(knorm, n_chunks, tile, lds_rk, wave, lane);
 }
 
@@ -193,15 +199,16 @@ __device__ __forceinline__ void mfma_tile_step(const uint8_t* __restrict__ kr, c
   wait_vmem_all();
   lds_barrier();                              // tile visible; previous tile fully consumed
   // The next tile's copies are interleaved with this tile's first MFMAs (one after
-  // each), so the waves do not stall on issuing them while the matrix unit idles.  On the last step the copy re-reads the current tile into the unused
-  // buffer instead of branching around every instruction.
-  const int64_t tile_dma = has_next ? tile + 1 : tile;
+  // each), so the waves do not stall on issuing them while the matrix unit idles.
+  // On the last step the copy re-reads the current tile into the unused buffer
+  // instead of branching around every instruction.
+  const TileSrc src = tile_src<H>(kr, n_chunks, has_next ? tile + 1 : tile);
   if constexpr (NORMS) {
     if (has_next) issue_norms<H>(knorm, n_chunks, tile + 1, nxt_rk, wave, lane);
   }
   if (!wave_active) {
 #pragma unroll
-    for (int i = 0; i < CF::DMA_ITERS; ++i) issue_piece<H>(kr, n_chunks, tile_dma, nxt, wave, lane, i);
+    for (int i = 0; i < CF::DMA_ITERS; ++i) issue_piece<H>(src, nxt, wave, lane, i);
   }
 
   f32x4_t* x = xchg + lane;                   // layout [q4][lane]: 16-byte lane stride, conflict-free
@@ -241,12 +248,19 @@ __device__ __forceinline__ void mfma_tile_step(const uint8_t* __restrict__ kr, c
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[hh][k4 + ks], bv[ks], acc, 0, 0, 0);
         if constexpr (!NORMS) ss = sq_norm_piece(__builtin_bit_cast(uint4, bv[ks]), ss);
         const int mf = hh * 8 + k4 + ks;      // MFMA number within the step (compile time)
-        if (mf < CF::DMA_ITERS) issue_piece<H>(kr, n_chunks, tile_dma, nxt, wave, lane, mf);
+        if (mf < CF::DMA_ITERS) issue_piece<H>(src, nxt, wave, lane, mf);
       }
     }
   };
   // Epilogue of one head: scale by 1/|k| (column) and 1/|q| (row) and add into the head sum.
-  auto head_epilogue = [&](int hh, const f32x16_t& acc, float ss) {
+  // 1/|q| of the lane's 16 rows for head hh: loaded at the start of the pipeline step,
+  // ahead of the next head's MFMA chain, so the epilogue does not wait on LDS.
+  auto load_rq = [&](int hh, float4 (&rq)[4]) {
+    const int h = hs * CF::HPW + hh;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) rq[q4] = *reinterpret_cast<const float4*>(&lds_rq[h][8 * q4 + 4 * half]);
+  };
+  auto head_epilogue = [&](int hh, const f32x16_t& acc, float ss, const float4 (&rqv)[4]) {
     const int h = hs * CF::HPW + hh;
     float rk;
     if constexpr (NORMS) {
@@ -257,7 +271,7 @@ __device__ __forceinline__ void mfma_tile_step(const uint8_t* __restrict__ kr, c
     }
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
-      const float4 rq = *reinterpret_cast<const float4*>(&lds_rq[h][8 * q4 + 4 * half]);
+      const float4 rq = rqv[q4];
       sacc[4 * q4 + 0] = fmaf(acc[4 * q4 + 0], rk * rq.x, sacc[4 * q4 + 0]);
       sacc[4 * q4 + 1] = fmaf(acc[4 * q4 + 1], rk * rq.y, sacc[4 * q4 + 1]);
       sacc[4 * q4 + 2] = fmaf(acc[4 * q4 + 2], rk * rq.z, sacc[4 * q4 + 2]);
@@ -276,8 +290,10 @@ __device__ __forceinline__ void mfma_tile_step(const uint8_t* __restrict__ kr, c
     f32x16_t& nxt_acc = (hh & 1) ? acc_a : acc_b;
     float& cur_ss = (hh & 1) ? ss_b : ss_a;
     float& nxt_ss = (hh & 1) ? ss_a : ss_b;
+    float4 rqv[4];
+    load_rq(hh, rqv);
     if (hh + 1 < CF::HPW) head_mfma(hh + 1, nxt_acc, nxt_ss);
-    head_epilogue(hh, cur_acc, cur_ss);
+    head_epilogue(hh, cur_acc, cur_ss, rqv);
     __builtin_amdgcn_sched_barrier(0);
   }
   if constexpr (CF::HS == 2) {
