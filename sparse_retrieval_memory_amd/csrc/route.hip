@@ -214,10 +214,13 @@ __device__ __forceinline__ void mfma_tile_step(const uint8_t* __restrict__ kr, c
   f32x4_t* x = xchg + lane;                   // layout [q4][lane]: 16-byte lane stride, conflict-free
   if (CF::HS == 2 && has_prev && wave_active && hs == (PAR == 0 ? 1 : 0)) {
     // receiver of the previous tile (parity 1 - PAR): add the sender's half and finish it
+    f32x4_t o[4];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) o[q4] = x[q4 * 64];
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
-      const f32x4_t o = x[q4 * 64];
-      sprev[4 * q4] += o[0]; sprev[4 * q4 + 1] += o[1]; sprev[4 * q4 + 2] += o[2]; sprev[4 * q4 + 3] += o[3];
+      sprev[4 * q4] += o[q4][0]; sprev[4 * q4 + 1] += o[q4][1];
+      sprev[4 * q4 + 2] += o[q4][2]; sprev[4 * q4 + 3] += o[q4][3];
     }
     finish_tile(sprev, half, nb, t0, T, b, tile - 1, n_chunks, 1.0f / H, chunk_enc);
   }

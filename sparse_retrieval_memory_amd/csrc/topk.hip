@@ -185,6 +185,33 @@ __device__ __forceinline__ uint64_t merge_lists(const uint64_t (*lists)[64], int
   return wave_extract_topk<RM>(kv, k, lane);
 }
 
+// Phase A of the general path: each wave keeps a running top k over its share
+// of `n` keys (key(x), x < n), then one wave merges the lists; lane r of the
+// result holds the r-th largest key (0 past the end).  All threads must call it.
+template <int RM, typename Get>
+__device__ __forceinline__ void topk_by_waves(int64_t n, int k, Get key, uint64_t (*lists)[64], uint64_t* out,
+                                              int wave, int lane) {
+  const int64_t per = (n + P2_WAVES - 1) / P2_WAVES;
+  const int64_t g0 = wave * per;
+  const int64_t g1 = (g0 + per < n) ? g0 + per : n;
+  uint64_t run = 0;                           // lane r < k: the wave's r-th best so far
+  for (int64_t base = g0;; base += 64 * (RA - 1)) {
+    uint64_t kv[RA];
+#pragma unroll
+    for (int j = 0; j < RA - 1; ++j) {
+      const int64_t x = base + (int64_t)j * 64 + lane;
+      kv[j] = x < g1 ? key(x) : 0ull;
+    }
+    kv[RA - 1] = run;
+    run = wave_extract_topk<RA>(kv, k, lane);
+    if (base + 64 * (RA - 1) >= g1) break;
+  }
+  lists[wave][lane] = run;
+  __syncthreads();
+  if (wave == 0) out[lane] = merge_lists<RM>(lists, k, lane);
+  __syncthreads();
+}
+
 template <int RM, int RB>   // RM: merge keys per lane; RB = ceil(k / P2_WAVES) winning groups per wave
 __global__ void __launch_bounds__(64 * P2_WAVES)
 topk_from_groups(const float* __restrict__ scores, const uint64_t* __restrict__ gmax, int64_t n_docs,
@@ -195,26 +222,8 @@ topk_from_groups(const float* __restrict__ scores, const uint64_t* __restrict__ 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const uint64_t* gm = gmax + (int64_t)b * n_groups;
 
-  // A: each wave keeps a running top-k over its share of the group maxima
-  const int64_t per = (n_groups + P2_WAVES - 1) / P2_WAVES;
-  const int64_t g0 = wave * per;
-  const int64_t g1 = (g0 + per < n_groups) ? g0 + per : n_groups;
-  uint64_t run = 0;                           // lane r < k: the wave's r-th best so far
-  for (int64_t base = g0;; base += 64 * (RA - 1)) {
-    uint64_t kv[RA];
-#pragma unroll
-    for (int j = 0; j < RA - 1; ++j) {
-      const int64_t x = base + (int64_t)j * 64 + lane;
-      kv[j] = x < g1 ? gm[x] : 0ull;
-    }
-    kv[RA - 1] = run;
-    run = wave_extract_topk<RA>(kv, k, lane);
-    if (base + 64 * (RA - 1) >= g1) break;
-  }
-  lists[wave][lane] = run;
-  __syncthreads();
-  if (wave == 0) groups[lane] = merge_lists<RM>(lists, k, lane);
-  __syncthreads();
+  // A: the k best group maxima
+  topk_by_waves<RM>(n_groups, k, [&](int64_t x) { return gm[x]; }, lists, groups, wave, lane);
 
   // B: the k winning groups' documents; wave w takes groups w, w + P2_WAVES, ...
   const float* row = scores + (int64_t)b * n_docs;
@@ -243,6 +252,116 @@ topk_from_groups(const float* __restrict__ scores, const uint64_t* __restrict__ 
   }
 }
 
+// k <= P2_WAVES: the same two selections, each preceded by a threshold that
+// drops almost every key before any extraction.
+//   A: every wave takes the maximum of its share of the group maxima; these
+//      are P2_WAVES distinct keys, so the k-th largest of them (T0) is at most
+//      the k-th largest group maximum, and the k winning groups all have keys
+//      >= T0.  Keys >= T0 are appended to an LDS list.
+//   B: the k winning groups' best documents are k distinct documents with keys
+//      >= T1 = the k-th winning group's key, so the k best documents all have
+//      keys >= T1; those are appended to the list.
+// A list of at most 256 keys is reduced by one wave (k extraction rounds); a
+// longer one by all waves and a merge; if phase A's list would overflow LDS
+// (adversarial score layouts), the unfiltered path runs instead.
+constexpr int LIST_CAP = 1024;
+constexpr int ONE_WAVE = 4;                   // keys per lane when one wave reduces the list
+
+template <int RM>
+__device__ __forceinline__ void reduce_list(const uint64_t* list, int n, int k, uint64_t (*lists)[64], uint64_t* out,
+                                            int wave, int lane) {
+  if (n <= 64 * ONE_WAVE) {                   // uniform branch: n is read from LDS after a barrier
+    if (wave == 0) {
+      uint64_t kv[ONE_WAVE];
+#pragma unroll
+      for (int j = 0; j < ONE_WAVE; ++j) kv[j] = j * 64 + lane < n ? list[j * 64 + lane] : 0ull;
+      out[lane] = wave_extract_topk<ONE_WAVE>(kv, k, lane);
+    }
+    __syncthreads();
+  } else {
+    topk_by_waves<RM>(n, k, [&](int64_t x) { return list[x]; }, lists, out, wave, lane);
+  }
+}
+
+// Append the keys of `kv` that are >= t (and not empty) to list[*count ...].
+__device__ __forceinline__ void append_ge(uint64_t key, uint64_t t, uint64_t* list, int* count, int lane) {
+  const bool keep = key != 0ull && key >= t;
+  const uint64_t mask = __ballot(keep);
+  if (mask == 0ull) return;
+  int base = 0;
+  if (lane == 0) base = atomicAdd(count, __popcll(mask));
+  base = __shfl(base, 0);
+  const int pos = base + __popcll(mask & ((1ull << lane) - 1ull));
+  if (keep && pos < LIST_CAP) list[pos] = key;
+}
+
+template <int RM>
+__global__ void __launch_bounds__(64 * P2_WAVES)
+topk_from_groups_filtered(const float* __restrict__ scores, const uint64_t* __restrict__ gmax, int64_t n_docs,
+                          int64_t n_groups, int k, int32_t* __restrict__ top_idx, float* __restrict__ top_scores) {
+  __shared__ uint64_t lists[P2_WAVES][64];
+  __shared__ uint64_t groups[64];
+  __shared__ uint64_t list[LIST_CAP];
+  __shared__ uint64_t wmax[P2_WAVES];
+  __shared__ uint64_t thresh;
+  __shared__ int count;
+  const int b = blockIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const uint64_t* gm = gmax + (int64_t)b * n_groups;
+  const int64_t per = (n_groups + P2_WAVES - 1) / P2_WAVES;
+  const int64_t g0 = wave * per;
+  const int64_t g1 = (g0 + per < n_groups) ? g0 + per : n_groups;
+
+  // A1: wave maxima, then T0 = the k-th largest of them (0 if fewer than k are non-empty)
+  uint64_t lm = 0;
+  for (int64_t x = g0 + lane; x < g1; x += 64) lm = gm[x] > lm ? gm[x] : lm;
+  const uint64_t wm = wave_max_key(lm);
+  if (lane == 0) wmax[wave] = wm;
+  if (threadIdx.x == 0) { thresh = 0; count = 0; }
+  __syncthreads();
+  if (threadIdx.x < P2_WAVES) {
+    const uint64_t mine = wmax[threadIdx.x];
+    int rank = 0;
+#pragma unroll
+    for (int j = 0; j < P2_WAVES; ++j) rank += wmax[j] > mine;
+    if (rank == k - 1 && mine != 0ull) thresh = mine;   // keys are unique, so one lane at most
+  }
+  __syncthreads();
+  // A2: keys >= T0 into the list
+  const uint64_t t0 = thresh;
+  for (int64_t base = g0; base < g1; base += 64) {
+    const int64_t x = base + lane;
+    append_ge(x < g1 ? gm[x] : 0ull, t0, list, &count, lane);
+  }
+  __syncthreads();
+  const int na = count;
+  if (na > LIST_CAP) {
+    topk_by_waves<RM>(n_groups, k, [&](int64_t x) { return gm[x]; }, lists, groups, wave, lane);
+  } else {
+    reduce_list<RM>(list, na, k, lists, groups, wave, lane);
+  }
+
+  // B: documents of the k winning groups that are >= T1 (wave w takes group w)
+  const uint64_t t1 = groups[k - 1];
+  __syncthreads();                            // every wave has read `groups[k - 1]` and na
+  if (threadIdx.x == 0) count = 0;
+  __syncthreads();
+  const float* row = scores + (int64_t)b * n_docs;
+  if (wave < k && groups[wave] != 0ull) {
+    const uint32_t best_doc = 0xFFFFFFFFu - (uint32_t)(groups[wave] & 0xFFFFFFFFull);
+    const int64_t d = (int64_t)(best_doc / GROUP) * GROUP + lane;
+    append_ge(d < n_docs ? make_key(row[d], (uint32_t)d) : 0ull, t1, list, &count, lane);
+  }
+  __syncthreads();
+  const int nb = count;                       // <= k * 64 <= LIST_CAP
+  reduce_list<RM>(list, nb, k, lists, groups, wave, lane);
+  if (wave == 0 && lane < k) {
+    const uint64_t key = groups[lane];
+    top_idx[(int64_t)b * k + lane] = (int32_t)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFull));
+    top_scores[(int64_t)b * k + lane] = dec_f32((uint32_t)(key >> 32));
+  }
+}
+
 int launch_topk_small(const float* doc_scores, int B, int64_t n_docs, int k, int32_t* top_idx, float* top_scores,
                       uint64_t* gmax, hipStream_t stream) {
   const int64_t n_groups = (n_docs + GROUP - 1) / GROUP;
@@ -252,11 +371,15 @@ int launch_topk_small(const float* doc_scores, int B, int64_t n_docs, int k, int
 #define MSA_TOPK_GROUPS(RMV, RBV)                                                                        \
   hipLaunchKernelGGL((topk_from_groups<RMV, RBV>), dim3((unsigned)B), dim3(64 * P2_WAVES), 0, stream, doc_scores, \
                      gmax, n_docs, n_groups, k, top_idx, top_scores)
-  if (k <= 4) MSA_TOPK_GROUPS(1, 1);
-  else if (k <= 8) MSA_TOPK_GROUPS(2, 1);
-  else if (k <= 16) MSA_TOPK_GROUPS(4, 1);
+#define MSA_TOPK_FILTERED(RMV)                                                                          \
+  hipLaunchKernelGGL((topk_from_groups_filtered<RMV>), dim3((unsigned)B), dim3(64 * P2_WAVES), 0, stream,     \
+                     doc_scores, gmax, n_docs, n_groups, k, top_idx, top_scores)
+  if (k <= 4) MSA_TOPK_FILTERED(1);
+  else if (k <= 8) MSA_TOPK_FILTERED(2);
+  else if (k <= 16) MSA_TOPK_FILTERED(4);
   else MSA_TOPK_GROUPS(8, 2);
 #undef MSA_TOPK_GROUPS
+#undef MSA_TOPK_FILTERED
   MSA_CHECK_LAUNCH();
   return MSA_OK;
 }

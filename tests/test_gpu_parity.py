@@ -153,6 +153,33 @@ def test_topk_matches_oracle(B, n, k):
     assert np.array_equal(sc.astype(np.float64), ref_sc)
 
 
+@pytest.mark.parametrize("pattern", ["ascending", "descending", "constant", "one_block", "sparse_finite"])
+@pytest.mark.parametrize("n,k", [(200000, 16), (20000, 8), (3000, 4), (1000, 16), (130, 16)])
+def test_topk_score_layouts(pattern, n, k):
+    """Layouts that defeat the per-wave thresholds (the best keys packed into one wave's share, ties everywhere)."""
+    announce("topk layout", pattern, n, k)
+    r = np.random.default_rng(n + k)
+    if pattern == "ascending":
+        s = np.linspace(-1.0, 1.0, n, dtype=np.float32)
+    elif pattern == "descending":
+        s = np.linspace(1.0, -1.0, n, dtype=np.float32)
+    elif pattern == "constant":
+        s = np.full(n, 0.25, dtype=np.float32)
+    elif pattern == "one_block":                            # the top documents all inside one 64-document group run
+        s = r.standard_normal(n).astype(np.float32) * 0.01
+        m = min(40 * k, n - n // 3)
+        s[n // 3: n // 3 + m] = 1.0 + r.random(m).astype(np.float32)
+    else:                                                   # nearly everything excluded
+        s = np.full(n, -np.inf, dtype=np.float32)
+        s[r.choice(n, min(n, k + 3), replace=False)] = r.standard_normal(min(n, k + 3)).astype(np.float32)
+    s = s[None]
+    idx, sc = ops.topk_docs(torch.from_numpy(s).to(DEV), k)
+    torch.cuda.synchronize()
+    ref_idx, ref_sc = O.topk(s.astype(np.float64), k)
+    assert np.array_equal(idx.cpu().numpy(), ref_idx)
+    assert np.array_equal(sc.cpu().numpy().astype(np.float64), ref_sc)
+
+
 # ---------------------------------------------------------------------- pool
 @pytest.mark.parametrize("H,lens", [(8, [1, 63, 64, 65, 130, 512, 7, 200]), (4, [64, 3, 129]), (16, [70, 1]),
                                     (2, [300, 5, 64])])
