@@ -117,19 +117,77 @@ def route_only(w, n, dev):
                       "source_hash": route_source_hash()}), flush=True)
 
 
+def route_bytes_100M(w) -> int:
+    """Algorithmic HBM bytes of one route call: K̄_r + stored norms + offsets + Qr + document scores."""
+    G, H, D = w.n_chunks, w.H, w.D
+    return G * H * D * 2 + G * H * 4 + 8 * (w.n_docs + 1) + w.B * w.T * H * D * 2 + 4 * w.B * w.n_docs
+
+
+def traffic_from(fetch_csv: str, write_csv: str, w) -> dict:
+    """Per-launch HBM bytes of the scan kernel from two rocprofv3 --pmc runs of --route-only
+    (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each scaled by what the same counter
+    reads for the 1 GiB device-to-device copy that --route-only performs first."""
+    import csv
+
+    def read(path, counter):
+        kern, copy = [], []
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            if "route_mfma_kernel<8, true>" in r["Kernel_Name"]:
+                kern.append(float(r["Counter_Value"]))
+            elif "copyBuffer" in r["Kernel_Name"]:
+                copy.append(float(r["Counter_Value"]))
+        if not kern or not copy:
+            raise SystemExit(f"{path}: no {counter} values for the scan kernel or the reference copy")
+        return float(np.mean(kern)), max(copy)
+
+    copy_bytes = 1 << 30
+    fk, fc = read(fetch_csv, "FETCH_SIZE")
+    wk, wc = read(write_csv, "WRITE_SIZE")
+    fs, ws = copy_bytes / (fc * 1024), copy_bytes / (wc * 1024)
+    return {"kernel": "route_mfma_kernel<8, true> (stored norms)",
+            "workload": f"100M-token memory, one routed layer ({w.n_chunks:,} chunks), batch 1, "
+                        f"{w.B * w.T} router rows, stored norms",
+            "source_hash": route_source_hash(),
+            "source_hash_note": "sha256 (first 16 hex) of route.hip + msa_internal.h with comments and "
+                                "empty lines removed",
+            "fetch_kib_per_dispatch": fk, "write_kib_per_dispatch": wk,
+            "copy_reference": {"bytes": copy_bytes, "fetch_kib": fc, "write_kib": wc},
+            "fetch_scale": fs, "write_scale": ws,
+            "bytes_per_launch": int(round(fk * 1024 * fs + wk * 1024 * ws)),
+            "algorithmic_bytes_per_launch": route_bytes_100M(w),
+            "commands": ["cd /tmp && rocprofv3 --pmc FETCH_SIZE -d <out> -o run --output-format csv -- "
+                         "python3 <repo>/bench.py --route-only 5",
+                         "cd /tmp && rocprofv3 --pmc WRITE_SIZE -d <out> -o run --output-format csv -- "
+                         "python3 <repo>/bench.py --route-only 5",
+                         "python3 <repo>/bench.py --traffic-from <out>/run_counter_collection.csv (FETCH) "
+                         "<out>/run_counter_collection.csv (WRITE)"]}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
     ap.add_argument("--route-only", type=int, default=0, metavar="N",
                     help="counter-collection mode: one 100M-token layer, a 1 GiB device copy (the reference for "
                          "scaling FETCH_SIZE/WRITE_SIZE), then N routing calls; prints one line and exits")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the scan kernel's measured HBM traffic per launch (from the counter CSVs of two "
+                         "--route-only runs) to profiles/traffic_route_100M.json and exit; needs no GPU")
     args = ap.parse_args()
+    if args.traffic_from:
+        from synth import configs as C
+        tr = traffic_from(args.traffic_from[0], args.traffic_from[1], C.config(4))
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(tr, f, indent=1)
+        print(json.dumps({k: tr[k] for k in ("bytes_per_launch", "algorithmic_bytes_per_launch", "source_hash")}))
+        return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU's share only (--gpus {args.gpus} requested); the path is not "
-              "sharded across GPUs in this build.", file=sys.stderr)
+        print(f"bench.py measures one GPU's share only (--gpus {args.gpus} requested); the path runs on a "
+              "single GPU and is not sharded across GPUs.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -343,7 +401,7 @@ def main():
     log(f"interleave: 3 rounds in {interleave_ms:.2f} ms, chains {chains_ok}/{w5.B}")
 
     # ---------------------------------------------------------------- report
-    route_bytes = G * H * D * 2 + G * H * 4 + 8 * (w.n_docs + 1) + w.B * w.T * H * D * 2 + 4 * w.B * w.n_docs
+    route_bytes = route_bytes_100M(w)
     route_avg_s = float(route_ms.mean()) * 1e-3
     achieved = route_bytes / route_avg_s / 1e9
     traffic = None

@@ -39,9 +39,16 @@ constexpr int NW = 4;    // waves per MFMA workgroup
 constexpr int RW = 32;   // router rows per wave (MFMA M)
 constexpr int VALU_MAX_ROWS = 15;
 
+// p[0, n) = v; p is 16-byte aligned (the route workspace), so whole 16-byte stores
+// cover all but the last n % 4 words.
 __global__ void fill_u32_kernel(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
-  int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = v;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t n4 = n >> 2;
+  const uint4 q = make_uint4(v, v, v, v);
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride)
+    reinterpret_cast<uint4*>(p)[i] = q;
+  const int64_t t = (n4 << 2) + (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t < n) p[t] = v;
 }
 
 __device__ __forceinline__ float sq_norm_piece(uint4 v, float acc) {
@@ -214,13 +221,10 @@ __device__ __forceinline__ void mfma_tile_step(const uint8_t* __restrict__ kr, c
   f32x4_t* x = xchg + lane;                   // layout [q4][lane]: 16-byte lane stride, conflict-free
   if (CF::HS == 2 && has_prev && wave_active && hs == (PAR == 0 ? 1 : 0)) {
     // receiver of the previous tile (parity 1 - PAR): add the sender's half and finish it
-    f32x4_t o[4];
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) o[q4] = x[q4 * 64];
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
-      sprev[4 * q4] += o[q4][0]; sprev[4 * q4 + 1] += o[q4][1];
-      sprev[4 * q4 + 2] += o[q4][2]; sprev[4 * q4 + 3] += o[q4][3];
+      const f32x4_t o = x[q4 * 64];
+      sprev[4 * q4] += o[0]; sprev[4 * q4 + 1] += o[1]; sprev[4 * q4 + 2] += o[2]; sprev[4 * q4 + 3] += o[3];
     }
     finish_tile(sprev, half, nb, t0, T, b, tile - 1, n_chunks, 1.0f / H, chunk_enc);
   }
@@ -620,7 +624,12 @@ int launch_route_h(const uint16_t* Qr, int B, int T, const uint16_t* Krbar, cons
   S = (n_tiles + per - 1) / per;
   const int64_t grid = ((S + 7) / 8) * 8 * (int64_t)P;
   // fill with the encoding's minimum: below every float, so atomicMax takes the first value
-  hipLaunchKernelGGL(fill_u32_kernel, dim3(256), dim3(256), 0, stream, chunk_enc, (int64_t)B * n_chunks, 0u);
+  {
+    const int64_t n = (int64_t)B * n_chunks;
+    int64_t blocks = ((n >> 2) + 255) / 256;
+    blocks = blocks < 1 ? 1 : (blocks > 2048 ? 2048 : blocks);
+    hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, chunk_enc, n, 0u);
+  }
   MSA_CHECK_LAUNCH();
   if constexpr (H >= 4) {
     if (inv_norm) {
