@@ -43,16 +43,18 @@ struct bf16pair {
 
 __device__ __forceinline__ uint32_t pack2(uint32_t a, uint32_t b) { return a | (b << 16); }
 
-// x -> (bf16 hi, bf16 lo) with hi = RNE(x), lo = RNE(x - hi); 8 values
+// x -> (bf16 hi, bf16 lo) with hi = RNE(x), lo = RNE(x - hi); 8 values.  The
+// conversions are gfx950's packed fp32 -> bf16 instruction (round to nearest even).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt2_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+}
 __device__ __forceinline__ bf16pair split8(const float (&x)[8]) {
   uint32_t h[4], l[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const uint32_t h0 = f32_to_bf16_rne(x[2 * j]), h1 = f32_to_bf16_rne(x[2 * j + 1]);
-    const uint32_t l0 = f32_to_bf16_rne(x[2 * j] - __uint_as_float(h0 << 16));
-    const uint32_t l1 = f32_to_bf16_rne(x[2 * j + 1] - __uint_as_float(h1 << 16));
-    h[j] = pack2(h0, h1);
-    l[j] = pack2(l0, l1);
+    h[j] = cvt2_bf16(x[2 * j], x[2 * j + 1]);
+    l[j] = cvt2_bf16(x[2 * j] - bf16_lo(h[j]), x[2 * j + 1] - bf16_hi(h[j]));
   }
   bf16pair r;
   r.hi = __builtin_bit_cast(bf16x8_t, make_uint4(h[0], h[1], h[2], h[3]));
@@ -105,18 +107,28 @@ __device__ __forceinline__ void rotate_pairs_tab(float (&lo)[8], float (&hi)[8],
 
 constexpr int TAB_POS = 128;    // positions the LDS cos/sin table covers (local keys and queries)
 constexpr int TAB_SEG = 32;     // positions one thread steps through from an exact start
+constexpr int PART_STRIDE = D + 4;   // floats per (wave, row) in the merge area: 16-byte rows skewed by 4 banks
+
+// RoPE constants computed on the host in fp64 and passed with the launch:
+// rev[i] = theta_i / (2 pi); start[sg][i] = (cos, sin) at position rope_offset +
+// TAB_SEG * sg; step[i] = (cos, sin) of one position.
+struct RopeTables {
+  double rev[D / 2];
+  float2 start[TAB_POS / TAB_SEG][D / 2];
+  float2 step[D / 2];
+};
 
 __global__ void __launch_bounds__(THREADS, 1)
 attn_mfma_kernel(const uint16_t* __restrict__ Q, int Tq, int Hq, const uint16_t* __restrict__ Kloc,
                  const uint16_t* __restrict__ Vloc, int Tl, int Hkv, const uint16_t* __restrict__ Kmem,
                  const uint16_t* __restrict__ Vmem, int64_t mstride, int Mmax, const int32_t* __restrict__ mem_len,
-                 int rope_offset, double log2_base, float scale_log2e, float* __restrict__ O) {
+                 int rope_offset, const RopeTables tabs, float scale_log2e, float* __restrict__ O) {
   __shared__ double rev[D / 2];
   // cos/sin of positions rope_offset + p (p < n_local <= TAB_POS), frequency i: every query row
   // and local key of this workgroup sits at such a position
   __shared__ __attribute__((aligned(16))) float2 cs_tab[TAB_POS][D / 2];
   // per wave: V^T of its current tile [D][VT_STRIDE] bf16; reused at the end for the merge
-  __shared__ __attribute__((aligned(16))) float smem[NWAVE * D * RT];
+  __shared__ __attribute__((aligned(16))) float smem[NWAVE * RT * PART_STRIDE];
   static_assert(sizeof(smem) >= sizeof(uint16_t) * NWAVE * D * VT_STRIDE, "V^T area");
   __shared__ float m_sh[NWAVE][RT], l_sh[NWAVE][RT];
 
@@ -136,17 +148,57 @@ attn_mfma_kernel(const uint16_t* __restrict__ Q, int Tq, int Hq, const uint16_t*
   const int n_keys = M + n_local;
   const int n_tiles = (n_keys + KT - 1) / KT;
 
-  if (tid < D / 2) rev[tid] = exp2(-(2.0 * tid / D) * log2_base) * 0.15915494309189535;   // / (2 pi)
-  __syncthreads();
+  // Raw K and V of key tile t for this lane (key k0 + col): K dims 16 (ks % 4) + 64 (ks / 4) + 8 hf + e
+  // (the A-operand order), V dims 64 hf + 8 i + e.  Keys past the end read as zeros.
+  auto load_tile = [&](int t, uint4 (&kr)[8], uint4 (&vr)[8], bool& local) {
+    const int j = t * KT + col;
+    local = false;
+    const uint16_t *kp = nullptr, *vp = nullptr;
+    if (j < M) {
+      kp = Kmem + ((int64_t)b * Mmax + j) * mstride + (int64_t)g * D;
+      vp = Vmem + ((int64_t)b * Mmax + j) * mstride + (int64_t)g * D;
+    } else if (j < n_keys) {
+      local = true;
+      kp = Kloc + (((int64_t)b * Tl + (j - M)) * Hkv + g) * D;
+      vp = Vloc + (((int64_t)b * Tl + (j - M)) * Hkv + g) * D;
+    }
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      kr[ks] = kp ? *reinterpret_cast<const uint4*>(kp + 16 * (ks & 3) + 64 * (ks >> 2) + 8 * hf)
+                  : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      vr[i] = vp ? *reinterpret_cast<const uint4*>(vp + 64 * hf + 8 * i) : make_uint4(0, 0, 0, 0);
+  };
+
+  // The query rows and this wave's first key tile are loaded before the tables are
+  // built, so their memory latency overlaps the table set-up.
+  const int row = r0 + col;
+  uint4 qraw[8];
+  if (row < Tq) {
+    const uint16_t* q = Q + (((int64_t)b * Tq + row) * Hq + h) * D;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      qraw[ks] = *reinterpret_cast<const uint4*>(q + 16 * ks + 8 * hf);
+      qraw[ks + 4] = *reinterpret_cast<const uint4*>(q + 64 + 16 * ks + 8 * hf);
+    }
+  }
+  uint4 kc[8], vc[8];
+  bool lc = false;
+  if (wave < n_tiles) load_tile(wave, kc, vc, lc);
+
+  const bool use_tab = n_local <= TAB_POS;
+  if (!use_tab && tid < D / 2) rev[tid] = tabs.rev[tid];
   // Table for n_local <= TAB_POS: thread (frequency i, segment sg) starts from the exact angle at the
   // segment's first position and steps by the exact one-position rotation (error ~1e-6 after 32 steps).
-  const bool use_tab = n_local <= TAB_POS;
   if (use_tab) {
     const int i = tid & (D / 2 - 1), sg = tid / (D / 2);
-    for (int p0 = sg * TAB_SEG; p0 < n_local; p0 += (THREADS / (D / 2)) * TAB_SEG) {
-      float c, s_, cd, sd;
-      rope_cs(rope_offset + p0, rev[i], &c, &s_);
-      rope_cs(1, rev[i], &cd, &sd);
+    static_assert(THREADS / (D / 2) * TAB_SEG == TAB_POS, "one segment per thread covers the table");
+    const int p0 = sg * TAB_SEG;
+    if (p0 < n_local) {
+      const float2 st = tabs.start[sg][i], d1 = tabs.step[i];
+      float c = st.x, s_ = st.y;
+      const float cd = d1.x, sd = d1.y;
       const int p1 = p0 + TAB_SEG < n_local ? p0 + TAB_SEG : n_local;
       for (int p = p0; p < p1; ++p) {
         cs_tab[p][i] = make_float2(c, s_);
@@ -155,20 +207,18 @@ attn_mfma_kernel(const uint16_t* __restrict__ Q, int Tq, int Hq, const uint16_t*
         c = cn;
       }
     }
-    __syncthreads();
   }
+  __syncthreads();
 
   // ---- Q^T as the B operand: lane (col, hf) holds query row r0 + col, dims 16 ks + 8 hf + j
   bf16x8_t qh[8], ql[8];
   {
-    const int row = r0 + col;
     float lo[4][8], hi[4][8];
     if (row < Tq) {
-      const uint16_t* q = Q + (((int64_t)b * Tq + row) * Hq + h) * D;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        unpack8(*reinterpret_cast<const uint4*>(q + 16 * ks + 8 * hf), lo[ks]);
-        unpack8(*reinterpret_cast<const uint4*>(q + 64 + 16 * ks + 8 * hf), hi[ks]);
+        unpack8(qraw[ks], lo[ks]);
+        unpack8(qraw[ks + 4], hi[ks]);
       }
       const int p = (Tl - Tq) + row;
       if (use_tab) {
@@ -206,32 +256,6 @@ attn_mfma_kernel(const uint16_t* __restrict__ Q, int Tq, int Hq, const uint16_t*
   const int lim = (Tl - Tq) + qrow;      // last visible local key of this row
   uint16_t (*myvt)[VT_STRIDE] = reinterpret_cast<uint16_t (*)[VT_STRIDE]>(smem) + wave * D;
 
-  // Raw K and V of key tile t for this lane (key k0 + col): K dims 16 (ks % 4) + 64 (ks / 4) + 8 hf + e
-  // (the A-operand order), V dims 64 hf + 8 i + e.  Keys past the end read as zeros.
-  auto load_tile = [&](int t, uint4 (&kr)[8], uint4 (&vr)[8], bool& local) {
-    const int j = t * KT + col;
-    local = false;
-    const uint16_t *kp = nullptr, *vp = nullptr;
-    if (j < M) {
-      kp = Kmem + ((int64_t)b * Mmax + j) * mstride + (int64_t)g * D;
-      vp = Vmem + ((int64_t)b * Mmax + j) * mstride + (int64_t)g * D;
-    } else if (j < n_keys) {
-      local = true;
-      kp = Kloc + (((int64_t)b * Tl + (j - M)) * Hkv + g) * D;
-      vp = Vloc + (((int64_t)b * Tl + (j - M)) * Hkv + g) * D;
-    }
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-      kr[ks] = kp ? *reinterpret_cast<const uint4*>(kp + 16 * (ks & 3) + 64 * (ks >> 2) + 8 * hf)
-                  : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      vr[i] = vp ? *reinterpret_cast<const uint4*>(vp + 64 * hf + 8 * i) : make_uint4(0, 0, 0, 0);
-  };
-
-  uint4 kc[8], vc[8];
-  bool lc = false;
-  if (wave < n_tiles) load_tile(wave, kc, vc, lc);
   for (int t = wave; t < n_tiles; t += NWAVE) {
     const int k0 = t * KT;
     const int j = k0 + col;
@@ -365,33 +389,35 @@ attn_mfma_kernel(const uint16_t* __restrict__ Q, int Tq, int Hq, const uint16_t*
 #pragma unroll
   for (int w = 0; w < NWAVE; ++w) lt += (m_sh[w][col] == -INFINITY) ? 0.f : l_sh[w][col] * exp2f(m_sh[w][col] - mx);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  // scaled partial outputs through LDS (fp32 [dims][rows] per wave, in the V^T area)
-  float* part = smem;                                         // NWAVE x D x RT floats
+  // scaled partial outputs through LDS (fp32 [wave][row][dims], rows skewed; in the V^T area):
+  // accumulators i..i+3 of a dim tile are 4 consecutive dims, written as one 16-byte store
+  float* part = smem;                                         // NWAVE x RT x PART_STRIDE floats
+  const float sc = wscale * inv;
   __syncthreads();
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int dim = 32 * dt + 8 * (i >> 2) + 4 * hf + (i & 3);
-      part[(wave * D + dim) * RT + col] = oacc[dt][i] * wscale * inv;
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int dim = 32 * dt + 8 * i4 + 4 * hf;
+      *reinterpret_cast<float4*>(&part[(wave * RT + col) * PART_STRIDE + dim]) =
+          make_float4(oacc[dt][4 * i4] * sc, oacc[dt][4 * i4 + 1] * sc, oacc[dt][4 * i4 + 2] * sc,
+                      oacc[dt][4 * i4 + 3] * sc);
     }
   __syncthreads();
   // thread -> (row, 16 dims): sum the waves' parts and write 16 contiguous floats
   for (int x = tid; x < RT * (D / 16); x += THREADS) {
-    const int row = x / (D / 16), d0 = (x % (D / 16)) * 16;
-    if (r0 + row >= Tq) continue;
-    float* out = O + (((int64_t)b * Tq + r0 + row) * Hq + h) * D + d0;
+    const int row_ = x / (D / 16), d0 = (x % (D / 16)) * 16;
+    if (r0 + row_ >= Tq) continue;
+    float* out = O + (((int64_t)b * Tq + r0 + row_) * Hq + h) * D + d0;
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
-      float v[4];
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float acc = 0.f;
-#pragma unroll
-        for (int w = 0; w < NWAVE; ++w) acc += part[(w * D + d0 + 4 * q4 + e) * RT + row];
-        v[e] = acc;
+      for (int w = 0; w < NWAVE; ++w) {
+        const float4 v = *reinterpret_cast<const float4*>(&part[(w * RT + row_) * PART_STRIDE + d0 + 4 * q4]);
+        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
       }
-      *reinterpret_cast<float4*>(out + 4 * q4) = make_float4(v[0], v[1], v[2], v[3]);
+      *reinterpret_cast<float4*>(out + 4 * q4) = acc;
     }
   }
 }
@@ -404,8 +430,22 @@ int launch_attn(const uint16_t* Q, int B, int Tq, int Hq, const uint16_t* Kloc, 
                 float* O, hipStream_t stream) {
   dim3 grid((unsigned)((Tq + RT - 1) / RT), (unsigned)Hq, (unsigned)B);
   const float scale_log2e = scale * 1.4426950408889634f;
+  // RoPE constants in fp64: angle of position p at frequency i in revolutions, reduced to
+  // [-1/2, 1/2] before cos/sin (the same reduction the device fallback uses)
+  RopeTables tabs;
+  const double two_pi = 6.283185307179586;
+  for (int i = 0; i < D / 2; ++i) {
+    tabs.rev[i] = pow(rope_base, -2.0 * i / D) / two_pi;
+    auto cs = [&](double pos) {
+      double r = pos * tabs.rev[i];
+      r -= rint(r);
+      return make_float2((float)cos(two_pi * r), (float)sin(two_pi * r));
+    };
+    for (int sg = 0; sg < TAB_POS / TAB_SEG; ++sg) tabs.start[sg][i] = cs((double)rope_offset + TAB_SEG * sg);
+    tabs.step[i] = cs(1.0);
+  }
   hipLaunchKernelGGL(attn_mfma_kernel, grid, dim3(THREADS), 0, stream, Q, Tq, Hq, Kloc, Vloc, Tl, Hkv, Kmem,
-                     Vmem, mem_entry_stride, Mmax, mem_len, rope_offset, log2(rope_base), scale_log2e, O);
+                     Vmem, mem_entry_stride, Mmax, mem_len, rope_offset, tabs, scale_log2e, O);
   MSA_CHECK_LAUNCH();
   return MSA_OK;
 }
