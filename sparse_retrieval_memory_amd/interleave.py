@@ -37,6 +37,7 @@ class Round:
     n_rows: int                    # router rows routed this round (padded batch)
     O: torch.Tensor                # fp32 [B, Tq, Hq, D] on the device
     doc_scores: Optional[torch.Tensor] = None
+    ms: Optional[float] = None     # device time from the round's first launch to O (timing=True)
 
 
 @dataclass
@@ -52,7 +53,7 @@ class Interleave:
     _bufs: dict = field(default_factory=dict)
 
     def run(self, Qr, Q, Kloc, Vloc, k: int, rounds: int, keep_scores: bool = False,
-            fetch: str = "gather") -> List[Round]:
+            fetch: str = "gather", timing: bool = False) -> List[Round]:
         if fetch not in ("gather", "copy"):
             raise ValueError(f"fetch must be 'gather' or 'copy', not {fetch!r}")
         dev = Qr.device
@@ -65,7 +66,11 @@ class Interleave:
         side = self.side if self.side is not None else torch.cuda.Stream(device=dev)
         fetched = torch.cuda.Event()
         out: List[Round] = []
+        marks = []
         for r in range(rounds):
+            if timing:
+                marks.append([torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)])
+                marks[-1][0].record()
             if r == 0:
                 rows, n_rows = Qr, T0
             else:
@@ -90,6 +95,12 @@ class Interleave:
                 ml = ml.to(dev)
             O = ops.sparse_attn_decode(Q, Kloc, Vloc, staging, staging[:, :, 1], 2 * H * D, Mmax, ml,
                                        retrieved.shape[1], self.rope_base)
+            if timing:
+                marks[-1][1].record()
             out.append(Round(top_idx=new, top_scores=sc.cpu().numpy(), retrieved=retrieved.copy(), n_rows=n_rows,
                              O=O, doc_scores=doc if keep_scores else None))
+        if timing:
+            torch.cuda.synchronize(dev)
+            for rd, (a, b) in zip(out, marks):
+                rd.ms = a.elapsed_time(b)
         return out
