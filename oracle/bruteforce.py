@@ -50,6 +50,30 @@ def pool(K, V, Kr, doc_len, chunk, base):
     return Kb, Vb, Rb
 
 
+def encode_router_keys(hidden, W, doc_len, chunk, H, D):
+    """hidden: [n_tok][d_model]; W: [H*D][d_model].  Returns [n_chunks][H][D]:
+    per token, out feature f = sum_i hidden[t][i] * W[f][i]; then chunk means."""
+    dm = len(hidden[0])
+    out = []
+    t0 = 0
+    for Ld in doc_len:
+        n = (Ld + chunk - 1) // chunk
+        for j in range(n):
+            a, b = j * chunk, min((j + 1) * chunk, Ld)
+            acc = [[0.0] * D for _ in range(H)]
+            for t in range(a, b):
+                for h in range(H):
+                    for d in range(D):
+                        f = h * D + d
+                        s = 0.0
+                        for i in range(dm):
+                            s += hidden[t0 + t][i] * W[f][i]
+                        acc[h][d] += s / (b - a)
+            out.append(acc)
+        t0 += Ld
+    return out
+
+
 def cosine(a, b) -> float:
     na = math.sqrt(sum(x * x for x in a))
     nb = math.sqrt(sum(x * x for x in b))

@@ -134,6 +134,33 @@ def pool(K, V, Kr, doc_len: Sequence[int], chunk: int, base: float):
     return Kb, Vb, Rb, off_c
 
 
+def encode_router_keys(hidden, W, doc_len: Sequence[int], chunk: int, H: int, D: int):
+    """Global memory encoding of the router keys: project, then chunk-mean pool.
+
+    [blab] pipeline stage "Global Memory Encoding": a forward pass over the
+    corpus caches the chunk-pooled (K, V, K_r); [blab] sec. 1: documents'
+    router keys K_r are pooled per chunk like K and V, and a router projector
+    maps hidden states to the routing space.  Reading (the pages give no
+    formula): K_r,t = h_t W^T with W stored [H*D, d_model] (out x in, no bias),
+    split into H heads of D; the pooled key of a chunk is the mean of its
+    tokens' K_r,t (chunks as in `pool`).  hidden float64 [n_tok, d_model] in
+    document order.  Returns float64 [n_chunks, H, D] and the chunk offsets.
+    """
+    hidden = np.asarray(hidden, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    Kr = (hidden @ W.T).reshape(hidden.shape[0], H, D)        # every token's router key
+    L = np.asarray(doc_len, dtype=np.int64)
+    off_c = chunk_offsets(L, chunk)
+    out = np.empty((int(off_c[-1]), H, D))
+    t0 = 0
+    for d, Ld in enumerate(L):
+        for j in range(int(off_c[d + 1] - off_c[d])):
+            a, b = j * chunk, min((j + 1) * chunk, int(Ld))
+            out[int(off_c[d]) + j] = Kr[t0 + a:t0 + b].mean(axis=0)
+        t0 += int(Ld)
+    return out, off_c
+
+
 # ------------------------------------------------------------------ routing
 def head_mean_cosine(Qr, Krbar) -> np.ndarray:
     """S[r, g] = (1/H) * sum_h cos(Qr[r, h], Krbar[g, h]);  cos := 0 for a zero vector.

@@ -45,6 +45,8 @@ TID_KRBAR = 11     # pooled router keys drawn directly (per layer)
 TID_LEN = 12       # document lengths
 TID_PICK = 13      # needle / chain placement choices
 TID_CHAIN = 14     # chain link vectors (u, w)
+TID_HIDDEN = 15    # hidden states of the corpus  [n_tok, d_model]
+TID_WKR = 16       # router-key projection        [H * D, d_model]
 
 
 def mix64_int(z: int) -> int:

@@ -138,6 +138,56 @@ def test_pool_bruteforce():
     np.testing.assert_allclose(Rb, bR, atol=1e-13)
 
 
+# ----------------------------------------------------- router-key encoding
+def test_encode_one_hot_closed_form():
+    # one-hot hidden states select columns of W: K_r,t = W[:, i_t]; chunk means by hand
+    W = np.array([[1.0, 2.0, 3.0], [4.0, 5.0, 6.0]])            # [H*D = 2, d_model = 3]
+    hidden = np.eye(3)[[0, 2, 1, 0]]                              # tokens e0, e2, e1 | e0
+    out, off = O.encode_router_keys(hidden, W, [3, 1], 2, 1, 2)
+    np.testing.assert_array_equal(out.reshape(3, 2), [[2.0, 5.0], [2.0, 5.0], [1.0, 4.0]])
+    assert list(off) == [0, 2, 3]
+
+
+def test_encode_identity_projection_is_router_key_pooling():
+    r = rng(40)
+    L = [130, 64, 1, 77]
+    H, D = 2, 8
+    hid = r.standard_normal((sum(L), H * D))
+    out, off = O.encode_router_keys(hid, np.eye(H * D), L, 64, H, D)
+    K = r.standard_normal((sum(L), H, D))
+    _, _, Rb, off2 = O.pool(K, K, hid.reshape(-1, H, D), L, 64, BASE)
+    np.testing.assert_allclose(out, Rb, atol=1e-14)
+    assert np.array_equal(off, off2)
+
+
+def test_encode_bruteforce():
+    r = rng(41)
+    L = [5, 3, 7]
+    hid = r.standard_normal((sum(L), 6)); W = r.standard_normal((4, 6))
+    out, _ = O.encode_router_keys(hid, W, L, 3, 2, 2)
+    ref = bf.encode_router_keys(hid.tolist(), W.tolist(), L, 3, 2, 2)
+    np.testing.assert_allclose(out, ref, atol=1e-13)
+
+
+def test_encode_torch_linear_avgpool_and_pool_first():
+    r = rng(42)
+    L = [192, 100]
+    H, D, dm = 2, 4, 24
+    hid = r.standard_normal((sum(L), dm)); W = r.standard_normal((H * D, dm))
+    out, off = O.encode_router_keys(hid, W, L, 64, H, D)
+    # full chunks: torch Linear (no bias) then avg_pool1d over the first document
+    kr = torch.nn.functional.linear(torch.from_numpy(hid[:192]), torch.from_numpy(W))       # [192, H*D]
+    ap = torch.nn.functional.avg_pool1d(kr.T[None], 64, 64)[0].T.numpy()                    # [3, H*D]
+    np.testing.assert_allclose(out[:3].reshape(3, H * D), ap, atol=1e-12)
+    # the projection is linear: projecting each chunk's mean hidden state gives the same keys
+    t = 0
+    for d, Ld in enumerate(L):
+        for j in range(int(off[d + 1] - off[d])):
+            a, b = t + 64 * j, t + min(64 * (j + 1), Ld)
+            np.testing.assert_allclose(out[off[d] + j].ravel(), hid[a:b].mean(axis=0) @ W.T, atol=1e-12)
+        t += Ld
+
+
 # -------------------------------------------------------------------- routing
 def test_route_golden():
     g = GOLD["route_two_docs"]
