@@ -7,6 +7,7 @@
  * Context Assembly", "Sparse Generation"):
  *
  *   msa_pool_chunks         offline: chunk-mean pooled (Kbar, Vbar, Krbar) cache
+ *   msa_encode_router_keys  offline: router keys projected from hidden states, chunk-mean pooled
  *   msa_krbar_inv_norms     offline: 1/|Krbar| per chunk and head, stored beside the store
  *   msa_route_scores        online: cosine routing scan over every Krbar chunk
  *   msa_topk_docs           online: the k most relevant documents
@@ -86,6 +87,36 @@ int msa_pool_chunks(const uint16_t* K, const uint16_t* V, const uint16_t* Kr,
                     int64_t n_tok, int64_t n_chunks, int H, int D, int chunk_len,
                     double rope_base, uint16_t* Kbar, uint16_t* Vbar, uint16_t* Krbar,
                     hipStream_t stream);
+
+/*
+ * msa_encode_router_keys -- router keys of a corpus from its hidden states
+ * (offline encoding, the step that produces Krbar).
+ *
+ * Defined by: b-lab.team summary, pipeline stage "Global Memory Encoding" (a
+ * forward pass over the corpus caches chunk-pooled K_r) and sec. 1 (a router
+ * projector maps hidden states to the routing space; the router keys are
+ * chunk-mean pooled like K and V).  Reading: K_r,t = hidden[t] W^T, no bias.
+ *
+ * With chunks as in msa_pool_chunks (same offsets, a trailing partial chunk
+ * averaged over its actual length):
+ *   Krbar[g, h, :] = mean_{t in chunk g} (hidden[t] W^T)[h*D : (h+1)*D]
+ * computed as the projection of the chunk's mean hidden state (the same value
+ * in exact arithmetic): the mean is summed in fp32 and carried as a bf16 hi+lo
+ * pair (~2^-17 relative), the products are exact bf16 products accumulated in
+ * fp32, and the result is rounded to bf16 (nearest even).
+ *
+ *   hidden       bf16 [n_tok, d_model]        hidden states of the documents, in order
+ *   W            bf16 [H*D, d_model]          router-key projection (out x in)
+ *   doc_tok_off, doc_chunk_off, n_docs, n_tok, n_chunks, chunk_len: as in msa_pool_chunks
+ *   Krbar        bf16 [n_chunks, H, D] out
+ *   workspace    >= msa_encode_workspace_bytes(n_chunks, d_model) bytes (the chunk means)
+ *   d_model a multiple of 32 in [32, 8192]; H in {1,2,4,8,16}; D == 128; chunk_len in [1, 1024]
+ */
+size_t msa_encode_workspace_bytes(int64_t n_chunks, int d_model);
+int msa_encode_router_keys(const uint16_t* hidden, int64_t n_tok, int d_model, const uint16_t* W, int H,
+                           int D, const int64_t* doc_tok_off, const int64_t* doc_chunk_off, int64_t n_docs,
+                           int64_t n_chunks, int chunk_len, uint16_t* Krbar, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
 
 /*
  * msa_route_scores -- routing scan: chunk and document relevance.

@@ -58,6 +58,36 @@ int msa_pool_chunks(const uint16_t* K, const uint16_t* V, const uint16_t* Kr, co
                           rope_base, Kbar, Vbar, Krbar, stream);
 }
 
+size_t msa_encode_workspace_bytes(int64_t n_chunks, int d_model) {
+  if (n_chunks < 0 || d_model < 1) return 0;
+  return msa::encode_workspace(n_chunks, d_model);
+}
+
+int msa_encode_router_keys(const uint16_t* hidden, int64_t n_tok, int d_model, const uint16_t* W, int H, int D,
+                           const int64_t* doc_tok_off, const int64_t* doc_chunk_off, int64_t n_docs,
+                           int64_t n_chunks, int chunk_len, uint16_t* Krbar, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  msa::clear_error();
+  MSA_CHECK_ARG(n_docs >= 1 && n_tok >= 0 && n_chunks >= 0, "n_docs >= 1, n_tok >= 0, n_chunks >= 0 required");
+  MSA_CHECK_ARG(doc_tok_off && doc_chunk_off, "null offset array");
+  MSA_CHECK_ARG(n_chunks == 0 || (hidden && W && Krbar), "null tensor pointer");
+  MSA_CHECK_ARG(chunk_len >= 1 && chunk_len <= 1024, "chunk_len must be in [1, 1024]");
+  MSA_CHECK_SUPPORTED(D == 128, "D=%d unsupported (D must be 128)", D);
+  MSA_CHECK_SUPPORTED(H == 1 || H == 2 || H == 4 || H == 8 || H == 16, "H=%d unsupported", H);
+  MSA_CHECK_SUPPORTED(d_model >= 32 && d_model <= 8192 && d_model % 32 == 0,
+                      "d_model=%d unsupported (a multiple of 32 in [32, 8192])", d_model);
+  MSA_CHECK_ARG(n_chunks <= 0x7FFFFFFF && n_chunks * (int64_t)d_model < ((int64_t)1 << 40), "size out of range");
+  const size_t need = msa::encode_workspace(n_chunks, d_model);
+  if (n_chunks > 0 && (workspace == nullptr || workspace_bytes < need)) {
+    msa::set_error("workspace %zu bytes < required %zu", workspace_bytes, need);
+    return MSA_ERR_WORKSPACE;
+  }
+  MSA_CHECK_ARG(n_chunks == 0 || (aligned16(hidden) && aligned16(W) && aligned16(Krbar) && aligned16(workspace)),
+                "tensor and workspace pointers must be 16-byte aligned");
+  return msa::launch_encode(hidden, n_tok, d_model, W, H * D, doc_tok_off, doc_chunk_off, n_docs, n_chunks,
+                            chunk_len, Krbar, workspace, stream);
+}
+
 size_t msa_route_workspace_bytes(int B, int T, int H, int D, int64_t n_chunks, int64_t n_docs) {
   (void)D;
   if (B < 1 || T < 1 || n_chunks < 0 || n_docs < 1) return 0;

@@ -129,6 +129,10 @@ int launch_attn(const uint16_t* Q, int B, int Tq, int Hq, const uint16_t* Kloc, 
 int launch_append_rows(const uint16_t* Qr, int B, int T0, int H, const uint16_t* Krbar,
                        const int64_t* doc_chunk_off, int64_t n_docs, const int32_t* ids, int n_ids, int T_out,
                        uint16_t* rows, int32_t* n_rows, uint8_t* doc_exclude, hipStream_t stream);
+int launch_encode(const uint16_t* hidden, int64_t n_tok, int dm, const uint16_t* W, int N,
+                  const int64_t* doc_tok_off, const int64_t* doc_chunk_off, int64_t n_docs, int64_t n_chunks,
+                  int chunk_len, uint16_t* Krbar, void* workspace, hipStream_t stream);
+size_t encode_workspace(int64_t n_chunks, int dm);
 int launch_gather(const int32_t* top_idx, int B, int k, const uint16_t* host_store,
                   const int64_t* doc_chunk_off, int64_t n_docs, int H, uint16_t* staging, int Mmax,
                   int32_t* mem_len, hipStream_t stream);

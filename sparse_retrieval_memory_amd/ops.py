@@ -67,6 +67,30 @@ def pool_chunks(K, V, Kr, doc_tok_off, doc_chunk_off, n_chunks: int, chunk_len: 
     return Kb, Vb, Rb
 
 
+def encode_workspace_bytes(n_chunks: int, d_model: int) -> int:
+    return int(_lib.load().msa_encode_workspace_bytes(n_chunks, d_model))
+
+
+def encode_router_keys(hidden, W, doc_tok_off, doc_chunk_off, n_chunks: int, H: int, chunk_len: int = 64,
+                       out=None, ws=None, stream=None):
+    """msa_encode_router_keys: Krbar bf16 [n_chunks, H, D] from hidden [n_tok, d_model] and W [H*D, d_model]."""
+    _bf16(hidden, "hidden"); _bf16(W, "W"); _dev(hidden, "hidden"); _dev(W, "W")
+    n_tok, dm = hidden.shape
+    HD = W.shape[0]
+    if W.shape[1] != dm or HD % H:
+        raise ValueError(f"W must be [H*D, d_model], got {tuple(W.shape)} for d_model={dm}, H={H}")
+    D = HD // H
+    n_docs = doc_tok_off.numel() - 1
+    if out is None:
+        out = torch.empty((n_chunks, H, D), dtype=hidden.dtype, device=hidden.device)
+    need = encode_workspace_bytes(n_chunks, dm)
+    if ws is None:
+        ws = workspace(need, hidden.device, "encode")
+    _lib.call("msa_encode_router_keys", _p(hidden), n_tok, dm, _p(W), H, D, _p(doc_tok_off), _p(doc_chunk_off),
+              n_docs, n_chunks, chunk_len, _p(out), _p(ws), ws.numel() * ws.element_size(), _stream(stream))
+    return out
+
+
 def route_workspace_bytes(B, T, H, D, n_chunks, n_docs) -> int:
     return int(_lib.load().msa_route_workspace_bytes(B, T, H, D, n_chunks, n_docs))
 

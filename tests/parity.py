@@ -8,6 +8,8 @@ P3  top-k: the GPU set S is accepted iff every d in S has oracle score
     adjacent oracle gaps are >= 1e-3.
 P4  attention: per output row ||o - o*|| / ||o*|| <= 2e-2 (bf16 inputs, fp32
     accumulation); the oracle attends over the GPU's selected set.
+P5  encoded router keys: within 1 bf16 ulp, or half an ulp plus 2^-14 sum_k |mean h_k||W_nk|
+    (see encoded_keys_ok).
 P1  pooled V/Kr within 1 bf16 ulp of the oracle's rounded mean, K within 2
     ulps or 2^-20 absolute: K's terms are rotated in fp32 (each rounded), so a
     chunk mean that cancels to a tiny value keeps the accumulation's absolute
@@ -81,6 +83,26 @@ def pooled_k_ok(gpu_bits: np.ndarray, ref_f64: np.ndarray) -> bool:
         j = np.flatnonzero(big.ravel())[:3]
         print(f"[pooled K] {int(big.sum())} values beyond 2 ulps, all within {K_ABS_SLACK:.2e}: gpu "
               f"{gpu.ravel()[j].tolist()} oracle {np.asarray(ref_f64).ravel()[j].tolist()}", flush=True)
+    return True
+
+
+ENC_REL = 2.0 ** -14
+
+
+def encoded_keys_ok(gpu_bits: np.ndarray, ref_f64: np.ndarray, mag: np.ndarray) -> bool:
+    """P5 for the encoded router keys: within 1 bf16 ulp of the oracle's rounded value, or
+    within half an ulp plus ENC_REL * sum_k |mean h_k| |W_nk| (``mag``, per element): the
+    chunk mean is carried as a bf16 hi + lo pair (~2^-17 relative) and the products are
+    accumulated in fp32 over d_model terms, so an element whose terms cancel keeps an
+    absolute error of that order."""
+    ulps = bf16_ulp_diff(gpu_bits, O.f64_to_bf16_bits(ref_f64))
+    gpu = O.bf16_to_f64(gpu_bits)
+    half_ulp = np.abs(O.round_bf16(ref_f64)) * 2.0 ** -9 + 2.0 ** -133
+    bad = (ulps > 1) & (np.abs(gpu - ref_f64) > half_ulp + ENC_REL * mag)
+    if bad.any():
+        i = np.flatnonzero(bad.ravel())[:5]
+        raise AssertionError(f"encoded keys off at flat indices {i.tolist()}: gpu {gpu.ravel()[i].tolist()} "
+                             f"oracle {np.asarray(ref_f64).ravel()[i].tolist()} ulps {ulps.ravel()[i].tolist()}")
     return True
 
 

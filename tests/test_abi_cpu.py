@@ -16,7 +16,8 @@ def test_exports_every_declared_symbol():
     lib = _lib.load()
     names = _lib.declared_symbols()
     assert {"msa_pool_chunks", "msa_route_scores", "msa_topk_docs", "msa_sparse_attn_decode",
-            "msa_fetch_docs", "msa_gather_docs", "msa_append_router_rows"} <= set(names)
+            "msa_fetch_docs", "msa_gather_docs", "msa_append_router_rows", "msa_encode_router_keys",
+            "msa_encode_workspace_bytes"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     assert set(_lib.SIGNATURES) == set(names)
@@ -71,6 +72,24 @@ def test_pool_and_attention_validation():
     assert _code("msa_sparse_attn_decode", *args(Tq=5)) == E.MSA_ERR_INVALID_ARG
     assert _code("msa_sparse_attn_decode", *args(Hq=30)) == E.MSA_ERR_INVALID_ARG
     assert _code("msa_sparse_attn_decode", *args(D=64)) == E.MSA_ERR_UNSUPPORTED
+
+
+def test_encode_validation():
+    p = ctypes.c_void_p(16)
+    E = _lib
+    need = _lib.load().msa_encode_workspace_bytes(100, 2560)
+    assert need >= 2 * 100 * 2560 * 2
+    args = lambda dm=2560, H=8, D=128, chunk=64, ws=p, wsb=need, hid=p, n_chunks=100: (
+        hid, 6400, dm, p, H, D, p, p, 4, n_chunks, chunk, p, ws, wsb, N)
+    assert _code("msa_encode_router_keys", *args(dm=2500)) == E.MSA_ERR_UNSUPPORTED          # not a multiple of 32
+    assert _code("msa_encode_router_keys", *args(dm=16384)) == E.MSA_ERR_UNSUPPORTED
+    assert _code("msa_encode_router_keys", *args(D=64)) == E.MSA_ERR_UNSUPPORTED
+    assert _code("msa_encode_router_keys", *args(H=3)) == E.MSA_ERR_UNSUPPORTED
+    assert _code("msa_encode_router_keys", *args(chunk=0)) == E.MSA_ERR_INVALID_ARG
+    assert _code("msa_encode_router_keys", *args(hid=N)) == E.MSA_ERR_INVALID_ARG
+    assert _code("msa_encode_router_keys", *args(wsb=need - 1)) == E.MSA_ERR_WORKSPACE
+    assert _code("msa_encode_router_keys", *args(ws=N)) == E.MSA_ERR_WORKSPACE
+    assert _code("msa_encode_router_keys", *args(hid=ctypes.c_void_p(24))) == E.MSA_ERR_INVALID_ARG
 
 
 def test_append_router_rows_validation():

@@ -15,7 +15,8 @@ from synth import configs as C
 from synth import native
 from synth import splitmix as sm
 
-from tests.parity import ATT_TOL, SCORE_TOL, bf16_ulp_diff, check_topk, dev_bits, host_bits, rel_rows
+from tests.parity import (ATT_TOL, SCORE_TOL, bf16_ulp_diff, check_topk, dev_bits, encoded_keys_ok, host_bits,
+                          rel_rows)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -211,6 +212,47 @@ def test_pool_slab_with_offset_bases():
     rK, rV, rR, off = O.pool(f64(K), f64(V), f64(Kr), w.doc_len, 64, w.rope_base)
     assert bf16_ulp_diff(host_bits(Vb), O.f64_to_bf16_bits(rV[c0:c1])).max() <= 1
     assert bf16_ulp_diff(host_bits(Kb), O.f64_to_bf16_bits(rK[c0:c1])).max() <= 2
+
+
+# ------------------------------------------------------- router-key encoding
+def _encode_case(lens, dm, H, chunk, seed, first_doc=0):
+    """Encode documents first_doc.. of a corpus with the given lengths; returns gpu bits, oracle, magnitude."""
+    r = np.random.default_rng(seed)
+    n_tok = sum(lens)
+    hid = O.f64_to_bf16_bits(r.standard_normal((n_tok, dm)))
+    W = O.f64_to_bf16_bits(r.standard_normal((H * 128, dm)))
+    tok_off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    ch_off = O.chunk_offsets(lens, chunk)
+    t0, c0 = int(tok_off[first_doc]), int(ch_off[first_doc])
+    n_chunks = int(ch_off[-1]) - c0
+    out = ops.encode_router_keys(dev_bits(hid[t0:]), dev_bits(W), torch.from_numpy(tok_off[first_doc:]).to(DEV),
+                                 torch.from_numpy(ch_off[first_doc:]).to(DEV), n_chunks, H, chunk)
+    torch.cuda.synchronize()
+    ref, _ = O.encode_router_keys(O.bf16_to_f64(hid), O.bf16_to_f64(W), lens, chunk, H, 128)
+    # per element sum_k |mean hidden_k| |W_nk| of the exact chunk means (the error scale of P5)
+    hf = O.bf16_to_f64(hid)
+    means = np.stack([hf[int(tok_off[d]) + j * chunk: int(tok_off[d]) + min((j + 1) * chunk, lens[d])].mean(axis=0)
+                      for d in range(len(lens)) for j in range(int(ch_off[d + 1] - ch_off[d]))])
+    mag = (np.abs(means) @ np.abs(O.bf16_to_f64(W)).T).reshape(ref.shape)
+    return host_bits(out), ref[c0:], mag[c0:]
+
+
+@pytest.mark.parametrize("lens,dm,H,chunk", [([1, 63, 64, 65, 130, 300, 7, 2000, 64], 2560, 8, 64),
+                                             ([5, 3, 200], 64, 1, 64), ([100, 33, 257], 96, 2, 32),
+                                             ([64] * 300, 256, 4, 64), ([700, 1, 1024], 128, 16, 100)])
+def test_encode_router_keys_matches_oracle(lens, dm, H, chunk):
+    announce("encode", len(lens), dm, H, chunk)
+    gpu, ref, mag = _encode_case(lens, dm, H, chunk, seed=dm + H + chunk)
+    assert gpu.shape == ref.shape
+    assert encoded_keys_ok(gpu, ref, mag)
+    # most elements are exactly the oracle's rounded value
+    assert (bf16_ulp_diff(gpu, O.f64_to_bf16_bits(ref)) == 0).mean() > 0.9
+
+
+def test_encode_slab_with_offset_bases():
+    announce("encode-slab")
+    gpu, ref, mag = _encode_case([90, 64, 1, 300, 65, 2, 129], 512, 8, 64, seed=7, first_doc=3)
+    assert encoded_keys_ok(gpu, ref, mag)
 
 
 # ------------------------------------------------------------------ attention
