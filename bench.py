@@ -399,6 +399,30 @@ def main():
         pool_bytes += 3 * (t1_ - t0_) * H * D * 2 + 3 * (c1_ - c0_) * H * D * 2
         del raw
         d0 = d1
+    # router-key encoding of the same corpus from d_model = 2560 hidden states (1M-token slabs)
+    DM = 2560
+    w_kr = torch.empty((H * D, DM), dtype=torch.int16, device=dev)
+    native.fill_normal_bf16_device(w_kr, w5.seed, sm.TID_WKR, 0, 0)
+    enc_out = torch.empty((w5.n_chunks, H, D), dtype=torch.int16, device=dev)
+    enc_ms, enc_bytes, enc_flops = [], 0, 0
+    d0 = 0
+    while d0 < w5.n_docs:
+        d1 = min(max(int(np.searchsorted(w5.doc_tok_off, w5.doc_tok_off[d0] + 1_000_000, side="right")) - 1, d0 + 1),
+                 w5.n_docs)
+        t0_, t1_ = int(w5.doc_tok_off[d0]), int(w5.doc_tok_off[d1])
+        c0_, c1_ = int(w5.doc_chunk_off[d0]), int(w5.doc_chunk_off[d1])
+        hid = torch.empty((t1_ - t0_, DM), dtype=torch.int16, device=dev)
+        native.fill_normal_bf16_device(hid, w5.seed, sm.TID_HIDDEN, 0, t0_ * DM)
+        tok_off5 = torch.from_numpy(w5.doc_tok_off[d0:d1 + 1].copy()).to(dev)
+        ch_off5 = torch.from_numpy(w5.doc_chunk_off[d0:d1 + 1].copy()).to(dev)
+        enc_ms.append(time_ms(lambda: ops.encode_router_keys(hid, w_kr, tok_off5, ch_off5, c1_ - c0_, H, w5.chunk,
+                                                             out=enc_out[c0_:c1_]), 3))
+        enc_bytes += (t1_ - t0_) * DM * 2 + (c1_ - c0_) * H * D * 2
+        enc_flops += 2 * (c1_ - c0_) * DM * H * D
+        del hid
+        d0 = d1
+    enc_bytes += H * D * DM * 2
+    del w_kr, enc_out
     store5 = torch.stack([pooled5[0], pooled5[1]], dim=1).cpu().pin_memory()
     q5 = C.queries(w5, 0)
     il = Interleave(krbar=pooled5[2], doc_chunk_off=torch.from_numpy(w5.doc_chunk_off).to(dev),
@@ -469,6 +493,9 @@ def main():
                              "gemm_bf16_8192_TFLOPs": gemm_tflops,
                              "frac_of_gemm": scan3_tflops / gemm_tflops},
         "pool_GBps": pool_bytes / (sum(pool_us) * 1e-6) / 1e9,
+        "encode_router_keys_10M": {"ms": float(sum(enc_ms)), "GBps": enc_bytes / (sum(enc_ms) * 1e-3) / 1e9,
+                                   "frac_of_8TBps": enc_bytes / (sum(enc_ms) * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                   "d_model": 2560, "projection_TFLOPs_equiv": enc_flops / (sum(enc_ms) * 1e-3) / 1e12},
         "interleave_10M_b4_3rounds_ms": interleave_ms,
         "interleave_round_ms": round_ms,
         "interleave_chains_recovered": f"{chains_ok}/{w5.B}",

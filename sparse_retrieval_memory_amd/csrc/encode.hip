@@ -138,35 +138,35 @@ proj_gemm_kernel(const uint16_t* __restrict__ W, const uint16_t* __restrict__ Ph
   const int col = lane & 31, hf = lane >> 5;
   const int wn = (wave & 1) * 64, wm = (wave >> 1) * 64;   // this wave's sub-tile
 
-  // global -> register staging: thread t copies rows t/4 and t/4 + 64, 16-byte piece t%4
+  // global -> register staging: thread t copies rows t/4 and t/4 + 64, 16-byte piece t%4,
+  // two stages ahead of the MFMAs (register sets A and B alternate)
   const int srow = tid >> 2, spc = tid & 3;
-  const uint16_t* wsrc[2];
-  const uint16_t* hsrc[2];
-  const uint16_t* lsrc[2];
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int rr = srow + 64 * r;
-    int64_t m = m0 + rr;
-    if (m >= M) m = M - 1;                                 // clamp: those chunks are never stored
-    wsrc[r] = W + (int64_t)(n0 + rr) * K + 8 * spc;
-    hsrc[r] = Phi + m * K + 8 * spc;
-    lsrc[r] = Plo + m * K + 8 * spc;
-  }
-  uint4 stg[6];
-  auto fetch = [&](int k0) {
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      stg[3 * r + 0] = *reinterpret_cast<const uint4*>(wsrc[r] + k0);
-      stg[3 * r + 1] = *reinterpret_cast<const uint4*>(hsrc[r] + k0);
-      stg[3 * r + 2] = *reinterpret_cast<const uint4*>(lsrc[r] + k0);
-    }
+  int64_t mA = m0 + srow, mB = m0 + srow + 64;
+  if (mA >= M) mA = M - 1;                                 // clamp: those chunks are never stored
+  if (mB >= M) mB = M - 1;
+  const int64_t w0off = (int64_t)(n0 + srow) * K + 8 * spc, w1off = w0off + (int64_t)64 * K;
+  const int64_t p0off = mA * K + 8 * spc, p1off = mB * K + 8 * spc;
+  struct Stage { uint4 w0, h0, l0, w1, h1, l1; };
+  auto fetch = [&](int stage) {
+    const int k0 = stage * KS;
+    Stage r;
+    r.w0 = *reinterpret_cast<const uint4*>(W + w0off + k0);
+    r.h0 = *reinterpret_cast<const uint4*>(Phi + p0off + k0);
+    r.l0 = *reinterpret_cast<const uint4*>(Plo + p0off + k0);
+    r.w1 = *reinterpret_cast<const uint4*>(W + w1off + k0);
+    r.h1 = *reinterpret_cast<const uint4*>(Phi + p1off + k0);
+    r.l1 = *reinterpret_cast<const uint4*>(Plo + p1off + k0);
+    return r;
   };
-  auto stash = [&](int buf) {
-#pragma unroll
-    for (int r = 0; r < 2; ++r)
-#pragma unroll
-      for (int q = 0; q < 3; ++q)
-        *reinterpret_cast<uint4*>(&lds[buf][q][(srow + 64 * r) * ROWB + 16 * spc]) = stg[3 * r + q];
+  auto stash = [&](const Stage& r, int buf) {
+    uint8_t* t0 = &lds[buf][0][srow * ROWB + 16 * spc];
+    uint8_t* t1 = &lds[buf][0][(srow + 64) * ROWB + 16 * spc];
+    *reinterpret_cast<uint4*>(t0) = r.w0;
+    *reinterpret_cast<uint4*>(t0 + TILEB) = r.h0;
+    *reinterpret_cast<uint4*>(t0 + 2 * TILEB) = r.l0;
+    *reinterpret_cast<uint4*>(t1) = r.w1;
+    *reinterpret_cast<uint4*>(t1 + TILEB) = r.h1;
+    *reinterpret_cast<uint4*>(t1 + 2 * TILEB) = r.l1;
   };
 
   f32x16_t acc[2][2];
@@ -177,13 +177,7 @@ proj_gemm_kernel(const uint16_t* __restrict__ W, const uint16_t* __restrict__ Ph
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][c][i] = 0.f;
 
-  const int nk = K / KS;
-  fetch(0);
-  stash(0);
-  __syncthreads();
-  for (int ks = 0; ks < nk; ++ks) {
-    const int buf = ks & 1;
-    if (ks + 1 < nk) fetch((ks + 1) * KS);                 // next stage in flight during this one's MFMAs
+  auto compute = [&](int buf) {
 #pragma unroll
     for (int k16 = 0; k16 < 2; ++k16) {
       const int kb = 32 * k16 + 16 * hf;                   // byte offset of this lane's 8 k values
@@ -202,10 +196,29 @@ proj_gemm_kernel(const uint16_t* __restrict__ W, const uint16_t* __restrict__ Ph
           acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[a], pl[c], acc[a][c], 0, 0, 0);
         }
     }
-    if (ks + 1 < nk) {
-      stash(buf ^ 1);                                      // the other buffer was last read one stage ago
-      __syncthreads();
-    }
+  };
+
+  const int nk = K / KS;                                   // >= 1
+  // stage s is fetched at most two stages ahead (clamped to the last stage past the end,
+  // so every fetch is unconditional and in bounds; the extra copies are never used)
+  const int last = nk - 1;
+  Stage sa = fetch(0);
+  stash(sa, 0);
+  sa = fetch(1 < last ? 1 : last);
+  Stage sb = fetch(2 < last ? 2 : last);
+  __syncthreads();
+  for (int ks = 0; ks < nk; ks += 2) {
+    // stage ks from buffer 0; stage ks + 1 (set A) goes into buffer 1, read one stage ago
+    compute(0);
+    if (ks + 1 < nk) stash(sa, 1);
+    sa = fetch(ks + 3 < last ? ks + 3 : last);
+    __syncthreads();
+    if (ks + 1 >= nk) break;
+    // stage ks + 1 from buffer 1; stage ks + 2 (set B) into buffer 0
+    compute(1);
+    if (ks + 2 < nk) stash(sb, 0);
+    sb = fetch(ks + 4 < last ? ks + 4 : last);
+    __syncthreads();
   }
 
   // accumulator i of tile (a, c): feature n0 + wn + 32a + 8(i/4) + 4hf + i%4, chunk m0 + wm + 32c + col

@@ -16,7 +16,7 @@ from synth import configs as C
 from synth import native
 from synth import splitmix as sm
 
-from tests.parity import ATT_TOL, GAP, SCORE_TOL, check_topk, dev_bits, rel_rows
+from tests.parity import ATT_TOL, GAP, SCORE_TOL, check_topk, dev_bits, encoded_keys_ok, host_bits, rel_rows
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -322,3 +322,43 @@ def test_cfg5_full_pool_and_interleave():
                     assert g[d] == -np.inf
                 else:
                     assert abs(g[d] - dd[0, 0]) <= 1e-4, (r, b, d)
+
+
+# ------------------------------------------------------- router-key encoding
+D_MODEL = 2560      # hidden size of the pages' backbone family (Qwen3-4B)
+
+
+def test_encode_router_keys_10M_slab_sampled_chunks():
+    """Router-key encoding of the first ~1M-token slab of the 10M-token corpus (document-aligned,
+    hidden states and projection drawn by the generator on the device), checked on sampled chunks
+    against the oracle run on the same rows regenerated on the host."""
+    w = C.config(5)
+    H, D = w.H, w.D
+    d1 = int(np.searchsorted(w.doc_tok_off, 1_000_000, side="right")) - 1
+    t1, c1 = int(w.doc_tok_off[d1]), int(w.doc_chunk_off[d1])
+    announce("encode-10M-slab", d1, t1, c1)
+    hid = torch.empty((t1, D_MODEL), dtype=torch.int16, device=DEV)
+    native.fill_normal_bf16_device(hid, w.seed, sm.TID_HIDDEN, 0, 0)
+    Wd = torch.empty((H * D, D_MODEL), dtype=torch.int16, device=DEV)
+    native.fill_normal_bf16_device(Wd, w.seed, sm.TID_WKR, 0, 0)
+    out = ops.encode_router_keys(hid, Wd, torch.from_numpy(w.doc_tok_off[:d1 + 1].copy()).to(DEV),
+                                 torch.from_numpy(w.doc_chunk_off[:d1 + 1].copy()).to(DEV), c1, H, w.chunk)
+    torch.cuda.synchronize()
+    del hid
+    W = O.bf16_to_f64(C.normal_bf16(w.seed, sm.TID_WKR, 0, 0, H * D * D_MODEL).reshape(H * D, D_MODEL))
+    r = np.random.default_rng(3)
+    chunks = set(r.choice(c1, 60, replace=False).tolist()) | {0, c1 - 1}
+    # plus the partial trailing chunks of a few documents
+    for d in r.choice(d1, 8, replace=False):
+        chunks.add(int(w.doc_chunk_off[d + 1]) - 1)
+    gpu = host_bits(out)
+    for g in sorted(chunks):
+        d = int(np.searchsorted(w.doc_chunk_off, g, side="right")) - 1
+        j = g - int(w.doc_chunk_off[d])
+        a = int(w.doc_tok_off[d]) + j * w.chunk
+        b = min(a + w.chunk, int(w.doc_tok_off[d + 1]))
+        rows = O.bf16_to_f64(C.normal_bf16(w.seed, sm.TID_HIDDEN, 0, a * D_MODEL, (b - a) * D_MODEL)
+                             .reshape(b - a, D_MODEL))
+        ref, _ = O.encode_router_keys(rows, W, [b - a], w.chunk, H, D)
+        mag = (np.abs(rows.mean(axis=0)) @ np.abs(W).T).reshape(ref.shape)
+        assert encoded_keys_ok(gpu[g:g + 1], ref, mag), f"chunk {g}"
