@@ -239,6 +239,36 @@ def assemble(top_idx_row: Sequence[int], doc_chunk_off) -> np.ndarray:
     return np.concatenate(parts) if parts else np.zeros(0, dtype=np.int64)
 
 
+# ------------------------------------------------------------ store updates
+def store_delete(rows, doc_chunk_off, keep):
+    """Delete documents from a pooled store without rebuilding it.
+
+    [abstract]: among the alternatives' weaknesses it lists an inability to
+    modify memory content dynamically.  Reading: the surviving documents keep
+    their order and are renumbered 0, 1, ...; each moves with all its chunk
+    rows (rows: any per-chunk array, e.g. K_r-bar [n_chunks, H, D] or its norms
+    [n_chunks, H]); the chunk offsets are rebuilt.  Returns (rows_out, off_out,
+    new_id) with new_id[d] = the document's new index, or -1 if deleted.
+    """
+    rows = np.asarray(rows)
+    off = np.asarray(doc_chunk_off, dtype=np.int64)
+    keep = np.asarray(keep, dtype=bool)
+    parts = [rows[off[d]:off[d + 1]] for d in range(len(keep)) if keep[d]]
+    out = np.concatenate(parts) if parts else rows[:0].copy()
+    off_out = np.zeros(int(keep.sum()) + 1, dtype=np.int64)
+    np.cumsum(np.diff(off)[keep], out=off_out[1:])
+    new_id = np.where(keep, np.cumsum(keep) - 1, -1).astype(np.int32)
+    return out, off_out, new_id
+
+
+def store_append(rows, doc_chunk_off, new_rows, new_doc_chunk_off):
+    """Append documents (their pooled rows and chunk offsets, starting at 0) after the last one."""
+    off = np.asarray(doc_chunk_off, dtype=np.int64)
+    noff = np.asarray(new_doc_chunk_off, dtype=np.int64)
+    return (np.concatenate([np.asarray(rows), np.asarray(new_rows)]),
+            np.concatenate([off, off[-1] + noff[1:]]))
+
+
 # ---------------------------------------------------------------- attention
 def attend(Q, Kloc, Vloc, Kmem, Vmem, rope_offset: int, base: float, scale: float,
            return_probs: bool = False):

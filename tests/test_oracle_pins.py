@@ -188,6 +188,45 @@ def test_encode_torch_linear_avgpool_and_pool_first():
         t += Ld
 
 
+# ------------------------------------------------------------ store updates
+def _store_of(docs):
+    """An independent construction: a store built from scratch from a list of per-document row blocks."""
+    rows = np.concatenate(docs) if docs else np.zeros((0, 2, 3))
+    return rows, O.chunk_offsets([len(d) for d in docs], 1)
+
+
+def test_store_delete_equals_rebuild_and_ids():
+    r = rng(50)
+    docs = [r.standard_normal((n, 2, 3)) for n in (3, 1, 4, 2, 5)]
+    rows, off = _store_of(docs)
+    keep = np.array([1, 0, 1, 1, 0], bool)
+    out, off_out, new_id = O.store_delete(rows, off, keep)
+    ref_rows, ref_off = _store_of([docs[0], docs[2], docs[3]])
+    assert np.array_equal(out, ref_rows) and np.array_equal(off_out, ref_off)
+    assert new_id.tolist() == [0, -1, 1, 2, -1]
+    # keep everything: identity; keep nothing: empty store
+    out, off_out, new_id = O.store_delete(rows, off, np.ones(5, bool))
+    assert np.array_equal(out, rows) and np.array_equal(off_out, off) and new_id.tolist() == [0, 1, 2, 3, 4]
+    out, off_out, new_id = O.store_delete(rows, off, np.zeros(5, bool))
+    assert out.shape == (0, 2, 3) and off_out.tolist() == [0] and (new_id == -1).all()
+
+
+def test_store_append_then_delete_round_trip():
+    r = rng(51)
+    docs = [r.standard_normal((n, 2, 3)) for n in (2, 6, 1)]
+    more = [r.standard_normal((n, 2, 3)) for n in (4, 3)]
+    rows, off = _store_of(docs)
+    mrows, moff = _store_of(more)
+    a_rows, a_off = O.store_append(rows, off, mrows, moff)
+    ref_rows, ref_off = _store_of(docs + more)
+    assert np.array_equal(a_rows, ref_rows) and np.array_equal(a_off, ref_off)
+    back, back_off, _ = O.store_delete(a_rows, a_off, np.array([1, 1, 1, 0, 0], bool))
+    assert np.array_equal(back, rows) and np.array_equal(back_off, off)
+    # deleting from the middle and appending again keeps routing positions consistent
+    mid, mid_off, ids = O.store_delete(a_rows, a_off, np.array([1, 0, 1, 1, 1], bool))
+    assert np.array_equal(mid[mid_off[ids[3]]:mid_off[ids[3] + 1]], more[0])
+
+
 # -------------------------------------------------------------------- routing
 def test_route_golden():
     g = GOLD["route_two_docs"]
