@@ -8,6 +8,8 @@
  *
  *   msa_pool_chunks         offline: chunk-mean pooled (Kbar, Vbar, Krbar) cache
  *   msa_encode_router_keys  offline: router keys projected from hidden states, chunk-mean pooled
+ *   msa_store_delete        update: delete documents from the routing store (compacted copy)
+ *   msa_store_append        update: append documents to the routing store in place
  *   msa_krbar_inv_norms     offline: 1/|Krbar| per chunk and head, stored beside the store
  *   msa_route_scores        online: cosine routing scan over every Krbar chunk
  *   msa_topk_docs           online: the k most relevant documents
@@ -117,6 +119,46 @@ int msa_encode_router_keys(const uint16_t* hidden, int64_t n_tok, int d_model, c
                            int D, const int64_t* doc_tok_off, const int64_t* doc_chunk_off, int64_t n_docs,
                            int64_t n_chunks, int chunk_len, uint16_t* Krbar, void* workspace,
                            size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * msa_store_delete / msa_store_append -- incremental updates of the routing store.
+ *
+ * Defined by: chatpaper.ai page, Abstract (an inability to modify memory content
+ * dynamically is listed among the alternatives' weaknesses).  Reading: deleted
+ * documents disappear; survivors keep their order, are renumbered 0, 1, ... and
+ * move with all their chunk rows; appended documents follow the last one.  Rows
+ * are moved, not recomputed: an updated store is bit-identical to one built from
+ * the same documents from scratch.  (The pinned host content tier is the
+ * caller's to compact with the same new_id map.)
+ *
+ * msa_store_delete (out of place):
+ *   Krbar          bf16 [n_chunks, H, D]   store; n_chunks == doc_chunk_off[n_docs]
+ *   inv_norm       fp32 [n_chunks, H] or NULL (then inv_norm_out must be NULL too)
+ *   doc_chunk_off  int64 [n_docs+1] (device), doc_chunk_off[0] == 0
+ *   keep           uint8 [n_docs] (device): nonzero = keep
+ *   Krbar_out      bf16 [<= n_chunks, H, D], inv_norm_out fp32 [<= n_chunks, H]:
+ *                  the survivors' rows; must not overlap Krbar / inv_norm
+ *   doc_chunk_off_out int64 [n_docs+1] capacity: the survivors' offsets
+ *   new_id         int32 [n_docs]: new index of each document, -1 if deleted
+ *   counts         int64 [2] (device): surviving documents, surviving chunks
+ *   1 <= n_docs < 2^31; H in {1,2,4,8,16}; D == 128
+ *
+ * msa_store_append (in place, within capacity):
+ *   Krbar [chunk_capacity, H, D], inv_norm [chunk_capacity, H] or NULL (then the
+ *   appended chunks' inverse norms are not computed), doc_chunk_off
+ *   [doc_capacity+1]: the store with n_docs documents and n_chunks ==
+ *   doc_chunk_off[n_docs] chunks; new_Krbar bf16 [n_new_chunks, H, D] and
+ *   new_doc_chunk_off int64 [n_new_docs+1] (device, new_doc_chunk_off[0] == 0,
+ *   new_doc_chunk_off[n_new_docs] == n_new_chunks) are the documents to add.
+ *   On return the store holds n_docs + n_new_docs documents.
+ *   n_chunks + n_new_chunks <= chunk_capacity, n_docs + n_new_docs <= doc_capacity.
+ */
+int msa_store_delete(const uint16_t* Krbar, const float* inv_norm, const int64_t* doc_chunk_off, int64_t n_docs,
+                     int64_t n_chunks, int H, int D, const uint8_t* keep, uint16_t* Krbar_out, float* inv_norm_out,
+                     int64_t* doc_chunk_off_out, int32_t* new_id, int64_t* counts, hipStream_t stream);
+int msa_store_append(uint16_t* Krbar, float* inv_norm, int64_t* doc_chunk_off, int64_t n_docs, int64_t n_chunks,
+                     int H, int D, const uint16_t* new_Krbar, const int64_t* new_doc_chunk_off, int64_t n_new_docs,
+                     int64_t n_new_chunks, int64_t chunk_capacity, int64_t doc_capacity, hipStream_t stream);
 
 /*
  * msa_route_scores -- routing scan: chunk and document relevance.

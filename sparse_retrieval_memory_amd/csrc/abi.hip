@@ -88,6 +88,53 @@ int msa_encode_router_keys(const uint16_t* hidden, int64_t n_tok, int d_model, c
                             chunk_len, Krbar, workspace, stream);
 }
 
+namespace {
+// [a, a + na) and [b, b + nb) (bytes) share no byte
+bool disjoint(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x + na <= y || y + nb <= x;
+}
+}  // namespace
+
+int msa_store_delete(const uint16_t* Krbar, const float* inv_norm, const int64_t* doc_chunk_off, int64_t n_docs,
+                     int64_t n_chunks, int H, int D, const uint8_t* keep, uint16_t* Krbar_out, float* inv_norm_out,
+                     int64_t* doc_chunk_off_out, int32_t* new_id, int64_t* counts, hipStream_t stream) {
+  msa::clear_error();
+  MSA_CHECK_ARG(n_docs >= 1 && n_docs < ((int64_t)1 << 31) && n_chunks >= 0, "1 <= n_docs < 2^31, n_chunks >= 0");
+  MSA_CHECK_ARG(doc_chunk_off && keep && doc_chunk_off_out && new_id && counts, "null pointer");
+  MSA_CHECK_ARG(n_chunks == 0 || (Krbar && Krbar_out), "null store pointer");
+  MSA_CHECK_ARG((inv_norm == nullptr) == (inv_norm_out == nullptr), "inv_norm and inv_norm_out: both or neither");
+  MSA_CHECK_SUPPORTED(D == 128, "D=%d unsupported (D must be 128)", D);
+  MSA_CHECK_SUPPORTED(H == 1 || H == 2 || H == 4 || H == 8 || H == 16, "H=%d unsupported", H);
+  const size_t rb = (size_t)n_chunks * H * D * 2, nbytes = (size_t)n_chunks * H * 4;
+  MSA_CHECK_ARG(n_chunks == 0 || disjoint(Krbar, rb, Krbar_out, rb), "Krbar_out must not overlap Krbar");
+  MSA_CHECK_ARG(!inv_norm || n_chunks == 0 || disjoint(inv_norm, nbytes, inv_norm_out, nbytes),
+                "inv_norm_out must not overlap inv_norm");
+  MSA_CHECK_ARG(n_chunks == 0 || (aligned16(Krbar) && aligned16(Krbar_out)), "store pointers must be 16-byte aligned");
+  return msa::launch_store_delete(Krbar, inv_norm, doc_chunk_off, n_docs, H, keep, Krbar_out, inv_norm_out,
+                                  doc_chunk_off_out, new_id, counts, stream);
+}
+
+int msa_store_append(uint16_t* Krbar, float* inv_norm, int64_t* doc_chunk_off, int64_t n_docs, int64_t n_chunks,
+                     int H, int D, const uint16_t* new_Krbar, const int64_t* new_doc_chunk_off, int64_t n_new_docs,
+                     int64_t n_new_chunks, int64_t chunk_capacity, int64_t doc_capacity, hipStream_t stream) {
+  msa::clear_error();
+  MSA_CHECK_ARG(n_docs >= 0 && n_chunks >= 0 && n_new_docs >= 0 && n_new_chunks >= 0, "negative size");
+  MSA_CHECK_ARG(doc_chunk_off && (n_new_docs == 0 || new_doc_chunk_off), "null offset array");
+  MSA_CHECK_ARG(n_new_chunks == 0 || (Krbar && new_Krbar), "null store pointer");
+  MSA_CHECK_SUPPORTED(D == 128, "D=%d unsupported (D must be 128)", D);
+  MSA_CHECK_SUPPORTED(H == 1 || H == 2 || H == 4 || H == 8 || H == 16, "H=%d unsupported", H);
+  MSA_CHECK_ARG(n_chunks + n_new_chunks <= chunk_capacity && n_docs + n_new_docs <= doc_capacity,
+                "the appended store exceeds its capacity (%lld chunks, %lld documents)", (long long)chunk_capacity,
+                (long long)doc_capacity);
+  MSA_CHECK_ARG(n_new_chunks == 0 || (aligned16(Krbar) && aligned16(new_Krbar)), "store pointers must be 16-byte aligned");
+  MSA_CHECK_ARG(n_new_chunks == 0 || disjoint(Krbar + n_chunks * (int64_t)H * D, (size_t)n_new_chunks * H * D * 2,
+                                              new_Krbar, (size_t)n_new_chunks * H * D * 2),
+                "new_Krbar must not overlap the store's free rows");
+  return msa::launch_store_append(Krbar, inv_norm, doc_chunk_off, n_docs, n_chunks, H, new_Krbar, new_doc_chunk_off,
+                                  n_new_docs, n_new_chunks, stream);
+}
+
 size_t msa_route_workspace_bytes(int B, int T, int H, int D, int64_t n_chunks, int64_t n_docs) {
   (void)D;
   if (B < 1 || T < 1 || n_chunks < 0 || n_docs < 1) return 0;

@@ -133,6 +133,12 @@ int launch_encode(const uint16_t* hidden, int64_t n_tok, int dm, const uint16_t*
                   const int64_t* doc_tok_off, const int64_t* doc_chunk_off, int64_t n_docs, int64_t n_chunks,
                   int chunk_len, uint16_t* Krbar, void* workspace, hipStream_t stream);
 size_t encode_workspace(int64_t n_chunks, int dm);
+int launch_store_delete(const uint16_t* rows, const float* norms, const int64_t* off, int64_t n_docs, int H,
+                        const uint8_t* keep, uint16_t* rows_out, float* norms_out, int64_t* off_out,
+                        int32_t* new_id, int64_t* counts, hipStream_t stream);
+int launch_store_append(uint16_t* rows, float* norms, int64_t* off, int64_t n_docs, int64_t n_chunks, int H,
+                        const uint16_t* new_rows, const int64_t* new_off, int64_t n_new_docs, int64_t n_new_chunks,
+                        hipStream_t stream);
 int launch_gather(const int32_t* top_idx, int B, int k, const uint16_t* host_store,
                   const int64_t* doc_chunk_off, int64_t n_docs, int H, uint16_t* staging, int Mmax,
                   int32_t* mem_len, hipStream_t stream);

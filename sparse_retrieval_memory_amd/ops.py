@@ -91,6 +91,39 @@ def encode_router_keys(hidden, W, doc_tok_off, doc_chunk_off, n_chunks: int, H: 
     return out
 
 
+def store_delete(Krbar, doc_chunk_off, keep, inv_norm=None, out=None, stream=None):
+    """msa_store_delete: (Krbar_out, inv_norm_out or None, doc_chunk_off_out, new_id, counts) with the deleted
+    documents removed; the outputs are sized like the inputs, the first counts[1] rows / counts[0] + 1 offsets
+    are the updated store (counts is a device int64 [2])."""
+    _bf16(Krbar, "Krbar"); _dev(Krbar, "Krbar")
+    n_chunks, H, D = Krbar.shape
+    n_docs = doc_chunk_off.numel() - 1
+    if keep.dtype != torch.uint8 or keep.numel() != n_docs:
+        raise ValueError("keep must be uint8 [n_docs]")
+    dev = Krbar.device
+    if out is None:
+        out = (torch.empty_like(Krbar), None if inv_norm is None else torch.empty_like(inv_norm),
+               torch.empty_like(doc_chunk_off), torch.empty(n_docs, dtype=torch.int32, device=dev),
+               torch.empty(2, dtype=torch.int64, device=dev))
+    kr_o, nrm_o, off_o, ids, counts = out
+    _lib.call("msa_store_delete", _p(Krbar), _p(inv_norm), _p(doc_chunk_off), n_docs, n_chunks, H, D, _p(keep),
+              _p(kr_o), _p(nrm_o), _p(off_o), _p(ids), _p(counts), _stream(stream))
+    return kr_o, nrm_o, off_o, ids, counts
+
+
+def store_append(Krbar, doc_chunk_off, n_docs: int, n_chunks: int, new_Krbar, new_doc_chunk_off, inv_norm=None,
+                 stream=None):
+    """msa_store_append: append documents in place.  Krbar [capacity, H, D] and doc_chunk_off [doc_capacity + 1]
+    hold n_docs documents / n_chunks chunks; returns the new (n_docs, n_chunks)."""
+    _bf16(Krbar, "Krbar"); _bf16(new_Krbar, "new_Krbar"); _dev(Krbar, "Krbar")
+    cap, H, D = Krbar.shape
+    n_new_docs = new_doc_chunk_off.numel() - 1
+    n_new_chunks = new_Krbar.shape[0]
+    _lib.call("msa_store_append", _p(Krbar), _p(inv_norm), _p(doc_chunk_off), n_docs, n_chunks, H, D, _p(new_Krbar),
+              _p(new_doc_chunk_off), n_new_docs, n_new_chunks, cap, doc_chunk_off.numel() - 1, _stream(stream))
+    return n_docs + n_new_docs, n_chunks + n_new_chunks
+
+
 def route_workspace_bytes(B, T, H, D, n_chunks, n_docs) -> int:
     return int(_lib.load().msa_route_workspace_bytes(B, T, H, D, n_chunks, n_docs))
 

@@ -255,6 +255,69 @@ def test_encode_slab_with_offset_bases():
     assert encoded_keys_ok(gpu, ref, mag)
 
 
+# ------------------------------------------------------------ store updates
+def _random_store(n_docs, H, seed, max_chunks=9):
+    r = np.random.default_rng(seed)
+    counts = r.integers(1, max_chunks + 1, n_docs)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    rows = O.f64_to_bf16_bits(r.standard_normal((int(off[-1]), H, 128)))
+    return rows, off, r
+
+
+@pytest.mark.parametrize("n_docs,H,pattern", [(50, 8, "random"), (1, 8, "all"), (1, 8, "none"), (300, 4, "none"),
+                                              (300, 4, "all"), (2000, 8, "random"), (7, 16, "ends")])
+def test_store_delete_bit_exact(n_docs, H, pattern):
+    announce("store-delete", n_docs, H, pattern)
+    rows, off, r = _random_store(n_docs, H, seed=n_docs + H)
+    keep = {"random": r.random(n_docs) < 0.6, "all": np.ones(n_docs, bool), "none": np.zeros(n_docs, bool),
+            "ends": np.array([0, 1, 1, 0, 1, 1, 0], bool)}[pattern]
+    kr = dev_bits(rows)
+    nrm = ops.krbar_inv_norms(kr)
+    kr_o, nrm_o, off_o, ids, counts = ops.store_delete(kr, torch.from_numpy(off).to(DEV),
+                                                       torch.from_numpy(keep.astype(np.uint8)).to(DEV), inv_norm=nrm)
+    torch.cuda.synchronize()
+    ref_rows, ref_off, ref_ids = O.store_delete(rows, off, keep)
+    ref_nrm, _, _ = O.store_delete(nrm.cpu().numpy(), off, keep)
+    nd, nc = (int(x) for x in counts.cpu())
+    assert (nd, nc) == (len(ref_off) - 1, len(ref_rows))
+    assert np.array_equal(host_bits(kr_o)[:nc], ref_rows)
+    assert np.array_equal(nrm_o.cpu().numpy()[:nc], ref_nrm)
+    assert np.array_equal(off_o.cpu().numpy()[:nd + 1], ref_off)
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+
+
+def test_store_append_then_delete_round_trip():
+    announce("store-append")
+    rows, off, r = _random_store(40, 8, seed=11)
+    new_rows, new_off, _ = _random_store(9, 8, seed=12)
+    cap_c, cap_d = len(rows) + len(new_rows) + 5, 40 + 9 + 3
+    kr = torch.zeros((cap_c, 8, 128), dtype=torch.int16, device=DEV)
+    kr[:len(rows)] = dev_bits(rows)
+    nrm = torch.zeros((cap_c, 8), dtype=torch.float32, device=DEV)
+    nrm[:len(rows)] = ops.krbar_inv_norms(kr[:len(rows)])
+    offd = torch.zeros(cap_d + 1, dtype=torch.int64, device=DEV)
+    offd[:41] = torch.from_numpy(off)
+    nd, nc = ops.store_append(kr, offd, 40, len(rows), dev_bits(new_rows), torch.from_numpy(new_off).to(DEV),
+                              inv_norm=nrm)
+    torch.cuda.synchronize()
+    ref_rows, ref_off = O.store_append(rows, off, new_rows, new_off)
+    assert (nd, nc) == (49, len(ref_rows))
+    assert np.array_equal(host_bits(kr)[:nc], ref_rows)
+    assert np.array_equal(offd.cpu().numpy()[:nd + 1], ref_off)
+    # the appended chunks' norms are the ones a scratch build computes
+    scratch = ops.krbar_inv_norms(kr[:nc].contiguous())
+    assert torch.equal(nrm[:nc], scratch)
+    # deleting the appended documents gives the original store back
+    keep = np.r_[np.ones(40, bool), np.zeros(9, bool)]
+    kr_o, nrm_o, off_o, ids, counts = ops.store_delete(kr[:nc].contiguous(), offd[:nd + 1].contiguous(),
+                                                       torch.from_numpy(keep.astype(np.uint8)).to(DEV),
+                                                       inv_norm=nrm[:nc].contiguous())
+    torch.cuda.synchronize()
+    assert [int(x) for x in counts.cpu()] == [40, len(rows)]
+    assert np.array_equal(host_bits(kr_o)[:len(rows)], rows)
+    assert np.array_equal(off_o.cpu().numpy()[:41], off)
+
+
 # ------------------------------------------------------------------ attention
 @pytest.mark.parametrize("B,Tq,Tl,M,offset", [(1, 32, 32, 32, 4), (1, 1, 128, 262, 16), (1, 128, 128, 262, 16),
                                               (2, 64, 64, 133, 16), (1, 5, 9, 0, 0), (1, 17, 40, 1, 3),
