@@ -339,6 +339,14 @@ def main():
     topk_us = 1e3 * time_ms(lambda: ops.topk_docs(doc, k, top_idx=idx_d, top_scores=sc_d, ws=ws_k), 50)
     gather_us = 1e3 * time_ms(lambda: ops.gather_docs(idx_d, store, off_dev, staging, Mmax, mem_len=ml_dev), 50)
     route_nonorm_ms = time_ms(lambda: ops.route_scores(qr[0], krbar[0], off_dev, doc_scores=doc, ws=ws_r), 10)
+    # routing-store update: delete 10% of one layer's documents (store + norms compacted into new buffers)
+    keep_d = torch.from_numpy((np.random.default_rng(9).random(w.n_docs) >= 0.1).astype(np.uint8)).to(dev)
+    del_out = (torch.empty_like(krbar[0]), torch.empty_like(knorm[0]), torch.empty_like(off_dev),
+               torch.empty(w.n_docs, dtype=torch.int32, device=dev), torch.empty(2, dtype=torch.int64, device=dev))
+    delete_ms = time_ms(lambda: ops.store_delete(krbar[0], off_dev, keep_d, inv_norm=knorm[0], out=del_out), 5)
+    kept_chunks = int(del_out[4][1].item())
+    delete_bytes = 2 * kept_chunks * H * (D * 2 + 4) + w.n_docs * (1 + 8 + 4 + 8)
+    del del_out
 
     log("side measurements: host-fetch step, attention, top-k, gather done")
     # the 10M-token batch-16 scan: 16 queries x 64 tokens over 165K chunks (matrix-core bound)
@@ -493,6 +501,8 @@ def main():
                              "gemm_bf16_8192_TFLOPs": gemm_tflops,
                              "frac_of_gemm": scan3_tflops / gemm_tflops},
         "pool_GBps": pool_bytes / (sum(pool_us) * 1e-6) / 1e9,
+        "store_delete_10pct_100M_layer": {"ms": delete_ms, "GBps": delete_bytes / (delete_ms * 1e-3) / 1e9,
+                                          "frac_of_8TBps": delete_bytes / (delete_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "encode_router_keys_10M": {"ms": float(sum(enc_ms)), "GBps": enc_bytes / (sum(enc_ms) * 1e-3) / 1e9,
                                    "frac_of_8TBps": enc_bytes / (sum(enc_ms) * 1e-3) / 1e9 / HBM_PEAK_GBS,
                                    "d_model": 2560, "projection_TFLOPs_equiv": enc_flops / (sum(enc_ms) * 1e-3) / 1e12},

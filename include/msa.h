@@ -141,6 +141,7 @@ int msa_encode_router_keys(const uint16_t* hidden, int64_t n_tok, int d_model, c
  *   doc_chunk_off_out int64 [n_docs+1] capacity: the survivors' offsets
  *   new_id         int32 [n_docs]: new index of each document, -1 if deleted
  *   counts         int64 [2] (device): surviving documents, surviving chunks
+ *   workspace      >= msa_store_delete_workspace_bytes(n_docs) bytes
  *   1 <= n_docs < 2^31; H in {1,2,4,8,16}; D == 128
  *
  * msa_store_append (in place, within capacity):
@@ -153,9 +154,11 @@ int msa_encode_router_keys(const uint16_t* hidden, int64_t n_tok, int d_model, c
  *   On return the store holds n_docs + n_new_docs documents.
  *   n_chunks + n_new_chunks <= chunk_capacity, n_docs + n_new_docs <= doc_capacity.
  */
+size_t msa_store_delete_workspace_bytes(int64_t n_docs);
 int msa_store_delete(const uint16_t* Krbar, const float* inv_norm, const int64_t* doc_chunk_off, int64_t n_docs,
                      int64_t n_chunks, int H, int D, const uint8_t* keep, uint16_t* Krbar_out, float* inv_norm_out,
-                     int64_t* doc_chunk_off_out, int32_t* new_id, int64_t* counts, hipStream_t stream);
+                     int64_t* doc_chunk_off_out, int32_t* new_id, int64_t* counts, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream);
 int msa_store_append(uint16_t* Krbar, float* inv_norm, int64_t* doc_chunk_off, int64_t n_docs, int64_t n_chunks,
                      int H, int D, const uint16_t* new_Krbar, const int64_t* new_doc_chunk_off, int64_t n_new_docs,
                      int64_t n_new_chunks, int64_t chunk_capacity, int64_t doc_capacity, hipStream_t stream);

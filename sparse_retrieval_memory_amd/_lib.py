@@ -36,7 +36,9 @@ SIGNATURES = {
     "msa_encode_workspace_bytes": (c_sz, [c_i64, c_i]),
     "msa_encode_router_keys": (c_i, [c_p, c_i64, c_i, c_p, c_i, c_i, c_p, c_p, c_i64, c_i64, c_i, c_p, c_p,
                                      c_sz, c_p]),
-    "msa_store_delete": (c_i, [c_p, c_p, c_p, c_i64, c_i64, c_i, c_i, c_p, c_p, c_p, c_p, c_p, c_p, c_p]),
+    "msa_store_delete_workspace_bytes": (c_sz, [c_i64]),
+    "msa_store_delete": (c_i, [c_p, c_p, c_p, c_i64, c_i64, c_i, c_i, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_sz,
+                               c_p]),
     "msa_store_append": (c_i, [c_p, c_p, c_p, c_i64, c_i64, c_i, c_i, c_p, c_p, c_i64, c_i64, c_i64, c_i64, c_p]),
     "msa_route_workspace_bytes": (c_sz, [c_i, c_i, c_i, c_i, c_i64, c_i64]),
     "msa_route_scores": (c_i, [c_p, c_i, c_i, c_i, c_i, c_p, c_p, c_i64, c_p, c_i64, c_p, c_p, c_p,

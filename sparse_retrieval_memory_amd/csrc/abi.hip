@@ -96,9 +96,15 @@ bool disjoint(const void* a, size_t na, const void* b, size_t nb) {
 }
 }  // namespace
 
+size_t msa_store_delete_workspace_bytes(int64_t n_docs) {
+  if (n_docs < 1) return 0;
+  return msa::store_delete_workspace(n_docs);
+}
+
 int msa_store_delete(const uint16_t* Krbar, const float* inv_norm, const int64_t* doc_chunk_off, int64_t n_docs,
                      int64_t n_chunks, int H, int D, const uint8_t* keep, uint16_t* Krbar_out, float* inv_norm_out,
-                     int64_t* doc_chunk_off_out, int32_t* new_id, int64_t* counts, hipStream_t stream) {
+                     int64_t* doc_chunk_off_out, int32_t* new_id, int64_t* counts, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
   msa::clear_error();
   MSA_CHECK_ARG(n_docs >= 1 && n_docs < ((int64_t)1 << 31) && n_chunks >= 0, "1 <= n_docs < 2^31, n_chunks >= 0");
   MSA_CHECK_ARG(doc_chunk_off && keep && doc_chunk_off_out && new_id && counts, "null pointer");
@@ -111,8 +117,14 @@ int msa_store_delete(const uint16_t* Krbar, const float* inv_norm, const int64_t
   MSA_CHECK_ARG(!inv_norm || n_chunks == 0 || disjoint(inv_norm, nbytes, inv_norm_out, nbytes),
                 "inv_norm_out must not overlap inv_norm");
   MSA_CHECK_ARG(n_chunks == 0 || (aligned16(Krbar) && aligned16(Krbar_out)), "store pointers must be 16-byte aligned");
+  const size_t need = msa::store_delete_workspace(n_docs);
+  if (workspace == nullptr || workspace_bytes < need) {
+    msa::set_error("workspace %zu bytes < required %zu", workspace_bytes, need);
+    return MSA_ERR_WORKSPACE;
+  }
+  MSA_CHECK_ARG(aligned16(workspace), "workspace must be 16-byte aligned");
   return msa::launch_store_delete(Krbar, inv_norm, doc_chunk_off, n_docs, H, keep, Krbar_out, inv_norm_out,
-                                  doc_chunk_off_out, new_id, counts, stream);
+                                  doc_chunk_off_out, new_id, counts, workspace, stream);
 }
 
 int msa_store_append(uint16_t* Krbar, float* inv_norm, int64_t* doc_chunk_off, int64_t n_docs, int64_t n_chunks,

@@ -135,7 +135,8 @@ int launch_encode(const uint16_t* hidden, int64_t n_tok, int dm, const uint16_t*
 size_t encode_workspace(int64_t n_chunks, int dm);
 int launch_store_delete(const uint16_t* rows, const float* norms, const int64_t* off, int64_t n_docs, int H,
                         const uint8_t* keep, uint16_t* rows_out, float* norms_out, int64_t* off_out,
-                        int32_t* new_id, int64_t* counts, hipStream_t stream);
+                        int32_t* new_id, int64_t* counts, void* workspace, hipStream_t stream);
+size_t store_delete_workspace(int64_t n_docs);
 int launch_store_append(uint16_t* rows, float* norms, int64_t* off, int64_t n_docs, int64_t n_chunks, int H,
                         const uint16_t* new_rows, const int64_t* new_off, int64_t n_new_docs, int64_t n_new_chunks,
                         hipStream_t stream);

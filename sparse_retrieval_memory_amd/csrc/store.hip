@@ -9,9 +9,9 @@
 // the last one.  The rows are moved, never recomputed, so an updated store is
 // bit-identical to one built from scratch from the same documents.
 //
-//   store_scan_kernel   one workgroup: per-thread runs of documents, a workgroup
-//                       scan of (kept documents, kept chunks), then each
-//                       survivor's new index and new first chunk
+//   store_tile_sums / store_tile_bases / store_ids   a three-pass scan of
+//                       (kept documents, kept chunks) over tiles of 1,024
+//                       documents: each survivor's new index and new first chunk
 //   store_move_kernel   one workgroup per old document: its rows, 16 bytes a lane
 //   append_off_kernel   offsets of appended documents, from the device's current end
 #include "msa_internal.h"
@@ -19,46 +19,80 @@
 namespace msa {
 namespace {
 
-constexpr int SCAN_THREADS = 1024;
+constexpr int TILE = 1024;          // documents per scan workgroup (one per thread)
 constexpr int MOVE_THREADS = 256;
+constexpr int MOVE_UNROLL = 4;      // 16-byte vectors in flight per lane
 
-__global__ void __launch_bounds__(SCAN_THREADS)
-store_scan_kernel(const int64_t* __restrict__ off, int64_t n_docs, const uint8_t* __restrict__ keep,
-                  int64_t* __restrict__ off_out, int32_t* __restrict__ new_id, int64_t* __restrict__ counts) {
-  __shared__ int64_t sk[SCAN_THREADS], sc[SCAN_THREADS];
-  const int t = threadIdx.x;
-  const int64_t per = (n_docs + SCAN_THREADS - 1) / SCAN_THREADS;
-  const int64_t d0 = t * per < n_docs ? t * per : n_docs;
-  const int64_t d1 = d0 + per < n_docs ? d0 + per : n_docs;
-  int64_t nk = 0, nc = 0;
-  for (int64_t d = d0; d < d1; ++d)
-    if (keep[d]) { ++nk; nc += off[d + 1] - off[d]; }
-  sk[t] = nk;
-  sc[t] = nc;
+// Inclusive scan of (a, b) over the 1024 threads of a workgroup: per-wave DPP-free
+// shuffles, then the 16 wave totals.  s_a/s_b: 16-entry LDS scratch.
+__device__ __forceinline__ void block_scan2(int64_t& a, int64_t& b, int64_t* s_a, int64_t* s_b) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int s = 1; s < 64; s <<= 1) {
+    const int64_t ua = __shfl_up(a, s), ub = __shfl_up(b, s);
+    if (lane >= s) { a += ua; b += ub; }
+  }
+  if (lane == 63) { s_a[wave] = a; s_b[wave] = b; }
   __syncthreads();
-  // inclusive scan over the threads (Hillis-Steele, log2(1024) steps)
-  for (int s = 1; s < SCAN_THREADS; s <<= 1) {
-    const int64_t ak = t >= s ? sk[t - s] : 0, ac = t >= s ? sc[t - s] : 0;
-    __syncthreads();
-    sk[t] += ak;
-    sc[t] += ac;
+  int64_t ba = 0, bb = 0;
+  for (int w = 0; w < wave; ++w) { ba += s_a[w]; bb += s_b[w]; }
+  a += ba;
+  b += bb;
+}
+
+// Pass 1: per tile of TILE documents, the kept documents and their chunks.
+__global__ void __launch_bounds__(TILE)
+store_tile_sums_kernel(const int64_t* __restrict__ off, int64_t n_docs, const uint8_t* __restrict__ keep,
+                       int64_t* __restrict__ tile_k, int64_t* __restrict__ tile_c) {
+  __shared__ int64_t s_a[TILE / 64], s_b[TILE / 64];
+  const int64_t d = (int64_t)blockIdx.x * TILE + threadIdx.x;
+  int64_t k = 0, c = 0;
+  if (d < n_docs && keep[d]) { k = 1; c = off[d + 1] - off[d]; }
+  block_scan2(k, c, s_a, s_b);
+  if (threadIdx.x == TILE - 1) { tile_k[blockIdx.x] = k; tile_c[blockIdx.x] = c; }
+}
+
+// Pass 2 (one workgroup): exclusive bases of the tiles, in place; totals into counts.
+__global__ void __launch_bounds__(TILE)
+store_tile_bases_kernel(int64_t* __restrict__ tile_k, int64_t* __restrict__ tile_c, int64_t n_tiles,
+                        int64_t* __restrict__ off_out, int64_t* __restrict__ counts) {
+  __shared__ int64_t s_a[TILE / 64], s_b[TILE / 64];
+  __shared__ int64_t carry_k, carry_c;
+  if (threadIdx.x == 0) { carry_k = 0; carry_c = 0; }
+  __syncthreads();
+  for (int64_t t0 = 0; t0 < n_tiles; t0 += TILE) {
+    const int64_t t = t0 + threadIdx.x;
+    const int64_t k0 = t < n_tiles ? tile_k[t] : 0, c0 = t < n_tiles ? tile_c[t] : 0;
+    int64_t k = k0, c = c0;
+    block_scan2(k, c, s_a, s_b);
+    const int64_t bk = carry_k, bc = carry_c;
+    if (t < n_tiles) { tile_k[t] = bk + k - k0; tile_c[t] = bc + c - c0; }
+    __syncthreads();                                   // every thread has read the carry
+    if (threadIdx.x == TILE - 1) { carry_k = bk + k; carry_c = bc + c; }
     __syncthreads();
   }
-  int64_t bk = sk[t] - nk, bc = sc[t] - nc;              // exclusive bases of this thread's run
-  for (int64_t d = d0; d < d1; ++d) {
-    if (keep[d]) {
-      new_id[d] = (int32_t)bk;
-      off_out[bk] = bc;
-      ++bk;
-      bc += off[d + 1] - off[d];
-    } else {
-      new_id[d] = -1;
-    }
+  if (threadIdx.x == 0) {
+    off_out[carry_k] = carry_c;
+    counts[0] = carry_k;
+    counts[1] = carry_c;
   }
-  if (t == SCAN_THREADS - 1) {
-    off_out[sk[t]] = sc[t];
-    counts[0] = sk[t];
-    counts[1] = sc[t];
+}
+
+// Pass 3: each survivor's new index and first chunk.
+__global__ void __launch_bounds__(TILE)
+store_ids_kernel(const int64_t* __restrict__ off, int64_t n_docs, const uint8_t* __restrict__ keep,
+                 const int64_t* __restrict__ tile_k, const int64_t* __restrict__ tile_c,
+                 int64_t* __restrict__ off_out, int32_t* __restrict__ new_id) {
+  __shared__ int64_t s_a[TILE / 64], s_b[TILE / 64];
+  const int64_t d = (int64_t)blockIdx.x * TILE + threadIdx.x;
+  const bool kept = d < n_docs && keep[d];
+  const int64_t k0 = kept ? 1 : 0, c0 = kept ? off[d + 1] - off[d] : 0;
+  int64_t k = k0, c = c0;
+  block_scan2(k, c, s_a, s_b);
+  if (d < n_docs) {
+    const int64_t nk = tile_k[blockIdx.x] + k - k0;   // exclusive
+    new_id[d] = kept ? (int32_t)nk : -1;
+    if (kept) off_out[nk] = tile_c[blockIdx.x] + c - c0;
   }
 }
 
@@ -75,7 +109,19 @@ store_move_kernel(const uint16_t* __restrict__ rows, const float* __restrict__ n
   const uint4* s = reinterpret_cast<const uint4*>(rows + src * row_elems);
   uint4* o = reinterpret_cast<uint4*>(rows_out + dst * row_elems);
   const int64_t nv = n * row_elems / 8;
-  for (int64_t i = threadIdx.x; i < nv; i += MOVE_THREADS) o[i] = s[i];
+  for (int64_t i0 = threadIdx.x; i0 < nv; i0 += MOVE_THREADS * MOVE_UNROLL) {
+    uint4 v[MOVE_UNROLL];
+#pragma unroll
+    for (int u = 0; u < MOVE_UNROLL; ++u) {
+      const int64_t i = i0 + (int64_t)u * MOVE_THREADS;
+      if (i < nv) v[u] = s[i];
+    }
+#pragma unroll
+    for (int u = 0; u < MOVE_UNROLL; ++u) {
+      const int64_t i = i0 + (int64_t)u * MOVE_THREADS;
+      if (i < nv) o[i] = v[u];
+    }
+  }
   if (norms) {
     const float* sn = norms + src * norm_elems;
     float* on = norms_out + dst * norm_elems;
@@ -98,11 +144,25 @@ append_off_kernel(int64_t* __restrict__ off, int64_t n_docs, const int64_t* __re
 
 }  // namespace
 
+size_t store_delete_workspace(int64_t n_docs) {
+  const int64_t n_tiles = (n_docs + TILE - 1) / TILE;
+  return ((size_t)2 * (size_t)n_tiles * sizeof(int64_t) + 255) & ~(size_t)255;
+}
+
 int launch_store_delete(const uint16_t* rows, const float* norms, const int64_t* off, int64_t n_docs, int H,
                         const uint8_t* keep, uint16_t* rows_out, float* norms_out, int64_t* off_out,
-                        int32_t* new_id, int64_t* counts, hipStream_t stream) {
-  hipLaunchKernelGGL(store_scan_kernel, dim3(1), dim3(SCAN_THREADS), 0, stream, off, n_docs, keep, off_out, new_id,
+                        int32_t* new_id, int64_t* counts, void* workspace, hipStream_t stream) {
+  const int64_t n_tiles = (n_docs + TILE - 1) / TILE;
+  int64_t* tile_k = reinterpret_cast<int64_t*>(workspace);
+  int64_t* tile_c = tile_k + n_tiles;
+  hipLaunchKernelGGL(store_tile_sums_kernel, dim3((unsigned)n_tiles), dim3(TILE), 0, stream, off, n_docs, keep,
+                     tile_k, tile_c);
+  MSA_CHECK_LAUNCH();
+  hipLaunchKernelGGL(store_tile_bases_kernel, dim3(1), dim3(TILE), 0, stream, tile_k, tile_c, n_tiles, off_out,
                      counts);
+  MSA_CHECK_LAUNCH();
+  hipLaunchKernelGGL(store_ids_kernel, dim3((unsigned)n_tiles), dim3(TILE), 0, stream, off, n_docs, keep, tile_k,
+                     tile_c, off_out, new_id);
   MSA_CHECK_LAUNCH();
   hipLaunchKernelGGL(store_move_kernel, dim3((unsigned)n_docs), dim3(MOVE_THREADS), 0, stream, rows, norms, off, keep,
                      new_id, off_out, H * 128, H, rows_out, norms_out);

@@ -106,8 +106,9 @@ def store_delete(Krbar, doc_chunk_off, keep, inv_norm=None, out=None, stream=Non
                torch.empty_like(doc_chunk_off), torch.empty(n_docs, dtype=torch.int32, device=dev),
                torch.empty(2, dtype=torch.int64, device=dev))
     kr_o, nrm_o, off_o, ids, counts = out
+    ws = workspace(int(_lib.load().msa_store_delete_workspace_bytes(n_docs)), dev, "store")
     _lib.call("msa_store_delete", _p(Krbar), _p(inv_norm), _p(doc_chunk_off), n_docs, n_chunks, H, D, _p(keep),
-              _p(kr_o), _p(nrm_o), _p(off_o), _p(ids), _p(counts), _stream(stream))
+              _p(kr_o), _p(nrm_o), _p(off_o), _p(ids), _p(counts), _p(ws), ws.numel(), _stream(stream))
     return kr_o, nrm_o, off_o, ids, counts
 
 

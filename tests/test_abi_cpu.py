@@ -17,7 +17,8 @@ def test_exports_every_declared_symbol():
     names = _lib.declared_symbols()
     assert {"msa_pool_chunks", "msa_route_scores", "msa_topk_docs", "msa_sparse_attn_decode",
             "msa_fetch_docs", "msa_gather_docs", "msa_append_router_rows", "msa_encode_router_keys",
-            "msa_encode_workspace_bytes", "msa_store_delete", "msa_store_append"} <= set(names)
+            "msa_encode_workspace_bytes", "msa_store_delete", "msa_store_append",
+            "msa_store_delete_workspace_bytes"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     assert set(_lib.SIGNATURES) == set(names)
@@ -97,14 +98,18 @@ def test_store_update_validation():
     p = ctypes.c_void_p(1 << 20)
     q = ctypes.c_void_p(1 << 30)                      # far from p: no overlap for these sizes
     near = ctypes.c_void_p((1 << 20) + 2048)          # inside p's first rows
-    dl = lambda n_docs=10, n_chunks=100, H=8, D=128, kr=p, kro=q, nrm=N, nrmo=N, keep=p: (
-        kr, nrm, p, n_docs, n_chunks, H, D, keep, kro, nrmo, p, p, p, N)
+    need = _lib.load().msa_store_delete_workspace_bytes(10)
+    assert need >= 16
+    dl = lambda n_docs=10, n_chunks=100, H=8, D=128, kr=p, kro=q, nrm=N, nrmo=N, keep=p, ws=p, wsb=need: (
+        kr, nrm, p, n_docs, n_chunks, H, D, keep, kro, nrmo, p, p, p, ws, wsb, N)
     assert _code("msa_store_delete", *dl(n_docs=0)) == E.MSA_ERR_INVALID_ARG
     assert _code("msa_store_delete", *dl(keep=N)) == E.MSA_ERR_INVALID_ARG
     assert _code("msa_store_delete", *dl(D=64)) == E.MSA_ERR_UNSUPPORTED
     assert _code("msa_store_delete", *dl(H=5)) == E.MSA_ERR_UNSUPPORTED
     assert _code("msa_store_delete", *dl(kro=near)) == E.MSA_ERR_INVALID_ARG          # output overlaps the store
     assert _code("msa_store_delete", *dl(nrm=p)) == E.MSA_ERR_INVALID_ARG             # norms without an output
+    assert _code("msa_store_delete", *dl(wsb=need - 1)) == E.MSA_ERR_WORKSPACE
+    assert _code("msa_store_delete", *dl(ws=N)) == E.MSA_ERR_WORKSPACE
     ap = lambda n_docs=10, n_chunks=100, nnd=2, nnc=5, cap=105, dcap=12, new=q: (
         p, N, p, n_docs, n_chunks, 8, 128, new, p, nnd, nnc, cap, dcap, N)
     assert _code("msa_store_append", *ap(cap=104)) == E.MSA_ERR_INVALID_ARG           # chunk capacity

@@ -362,3 +362,31 @@ def test_encode_router_keys_10M_slab_sampled_chunks():
         ref, _ = O.encode_router_keys(rows, W, [b - a], w.chunk, H, D)
         mag = (np.abs(rows.mean(axis=0)) @ np.abs(W).T).reshape(ref.shape)
         assert encoded_keys_ok(gpu[g:g + 1], ref, mag), f"chunk {g}"
+
+
+# ------------------------------------------------------------ store updates
+def test_store_delete_100M_layer_sampled():
+    """Delete 10% of the documents of one 100M-token routing layer (1.66M chunks, with stored norms): offsets
+    and new ids exact against the oracle, moved rows equal to their source rows on sampled documents."""
+    w = C.config(4)
+    announce("store-delete-100M", w.n_docs, w.n_chunks)
+    kr = device_krbar(w, 0)
+    nrm = ops.krbar_inv_norms(kr)
+    r = np.random.default_rng(9)
+    keep = r.random(w.n_docs) >= 0.1
+    keep[0] = False
+    keep[-1] = True
+    off = torch.from_numpy(w.doc_chunk_off).to(DEV)
+    kr_o, nrm_o, off_o, ids, counts = ops.store_delete(kr, off, torch.from_numpy(keep.astype(np.uint8)).to(DEV),
+                                                       inv_norm=nrm)
+    torch.cuda.synchronize()
+    _, ref_off, ref_ids = O.store_delete(np.zeros(w.n_chunks, np.int8), w.doc_chunk_off, keep)
+    nd, nc = (int(x) for x in counts.cpu())
+    assert nd == int(keep.sum()) and nc == int(ref_off[-1])
+    assert np.array_equal(off_o.cpu().numpy()[:nd + 1], ref_off)
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    for d in list(r.choice(np.flatnonzero(keep), 300, replace=False)) + [w.n_docs - 1]:
+        a, b = int(w.doc_chunk_off[d]), int(w.doc_chunk_off[d + 1])
+        na = int(ref_off[ref_ids[d]])
+        assert torch.equal(kr_o[na:na + b - a], kr[a:b]), f"doc {d}"
+        assert torch.equal(nrm_o[na:na + b - a], nrm[a:b]), f"doc {d}"
