@@ -212,6 +212,53 @@ def route(Qr, Krbar, doc_chunk_off, exclude=None, block: int = 65536):
     return chunk, doc
 
 
+def route_backward(Qr, Krbar, doc_chunk_off, dDoc, exclude=None):
+    """Gradient of the document scores w.r.t. the router queries and the selected chunks' keys.
+
+    [blab] sec. 2 (training): an auxiliary routing loss supervises the sparse
+    attention to attend to the right evidence; [abstract]: MSA is trained end to
+    end.  The loss itself is not given, so the step takes dL/d doc_scores (dDoc,
+    [B, n_docs]) and returns dL/dQr and, per (query, document), dL/dKrbar of the
+    document's selected chunk.  The forward is `route`: a max over a document's
+    chunks, a max over query tokens, a mean over heads of cosines.  Readings:
+    each max passes its gradient to its first (lowest-index) maximiser; an
+    excluded document, an empty document or a zero vector passes nothing.
+    With q^ = q/|q| and k^ = k/|k|:  d cos / dq = (k^ - cos q^) / |q|,
+    d cos / dk = (q^ - cos k^) / |k|.
+    Returns (dQr [B, T, H, D], dK [B, n_docs, H, D], sel int64 [B, n_docs, 2] =
+    (chunk, token) or (-1, -1)).
+    """
+    Qr = np.asarray(Qr, dtype=np.float64)
+    Kb = np.asarray(Krbar, dtype=np.float64)
+    dDoc = np.asarray(dDoc, dtype=np.float64)
+    B, T, H, D = Qr.shape
+    off = np.asarray(doc_chunk_off, dtype=np.int64)
+    n_docs = len(off) - 1
+    dQ = np.zeros_like(Qr)
+    dK = np.zeros((B, n_docs, H, D))
+    sel = np.full((B, n_docs, 2), -1, dtype=np.int64)
+    for b in range(B):
+        for d in range(n_docs):
+            if off[d + 1] == off[d] or (exclude is not None and exclude[b][d]) or dDoc[b, d] == 0.0:
+                continue
+            S = head_mean_cosine(Qr[b], Kb[off[d]:off[d + 1]])           # [T, n_chunks of d]
+            g_rel = int(np.argmax(S.max(axis=0)))                        # first maximising chunk
+            t = int(np.argmax(S[:, g_rel]))                              # first maximising token
+            g = int(off[d]) + g_rel
+            sel[b, d] = (g, t)
+            w = dDoc[b, d] / H
+            for h in range(H):
+                q, k = Qr[b, t, h], Kb[g, h]
+                nq, nk = np.sqrt(q @ q), np.sqrt(k @ k)
+                if nq == 0.0 or nk == 0.0:
+                    continue
+                qh, kh = q / nq, k / nk
+                c = qh @ kh
+                dQ[b, t, h] += w * (kh - c * qh) / nq
+                dK[b, d, h] = w * (qh - c * kh) / nk
+    return dQ, dK, sel
+
+
 def topk(doc_scores, k: int) -> Tuple[np.ndarray, np.ndarray]:
     """The k best documents per query: score descending, ties to the lower id.
 

@@ -188,6 +188,68 @@ def test_encode_torch_linear_avgpool_and_pool_first():
         t += Ld
 
 
+# ------------------------------------------------------- routing backward
+def _route_loss(Qr, Kb, off, G):
+    return float((O.route(Qr, Kb, off)[1] * G).sum())
+
+
+def test_route_backward_finite_differences():
+    # L = sum_d G_d * doc_score_d; central differences in fp64 on well-separated maxima
+    r = rng(60)
+    Qr = r.standard_normal((2, 5, 2, 6)); Kb = r.standard_normal((9, 2, 6))
+    off = np.array([0, 3, 4, 9]); G = r.standard_normal((2, 3))
+    dQ, dK, sel = O.route_backward(Qr, Kb, off, G)
+    eps = 1e-6
+    num = np.zeros_like(Qr)
+    for idx in np.ndindex(Qr.shape):
+        a = Qr.copy(); a[idx] += eps
+        c = Qr.copy(); c[idx] -= eps
+        num[idx] = (_route_loss(a, Kb, off, G) - _route_loss(c, Kb, off, G)) / (2 * eps)
+    np.testing.assert_allclose(dQ, num, atol=1e-7)
+    numK = np.zeros_like(Kb)
+    for idx in np.ndindex(Kb.shape):
+        a = Kb.copy(); a[idx] += eps
+        c = Kb.copy(); c[idx] -= eps
+        numK[idx] = (_route_loss(Qr, a, off, G) - _route_loss(Qr, c, off, G)) / (2 * eps)
+    # dK holds one row per (query, document): scatter it onto the selected chunks
+    dense = np.zeros_like(Kb)
+    for b in range(2):
+        for d in range(3):
+            dense[sel[b, d, 0]] += dK[b, d]
+    np.testing.assert_allclose(dense, numK, atol=1e-7)
+
+
+def test_route_backward_torch_autograd():
+    r = rng(61)
+    Qr = r.standard_normal((1, 7, 3, 8)); Kb = r.standard_normal((12, 3, 8))
+    off = np.array([0, 5, 6, 12]); G = r.standard_normal((1, 3))
+    q = torch.tensor(Qr, requires_grad=True); k = torch.tensor(Kb, requires_grad=True)
+    cos = torch.nn.functional.cosine_similarity(q[0][:, None], k[None], dim=-1).mean(-1)   # [T, n_chunks]
+    chunk = cos.max(dim=0).values
+    doc = torch.stack([chunk[off[d]:off[d + 1]].max() for d in range(3)])
+    (doc * torch.tensor(G[0])).sum().backward()
+    dQ, dK, sel = O.route_backward(Qr, Kb, off, G)
+    np.testing.assert_allclose(dQ, q.grad.numpy(), atol=1e-12)
+    dense = np.zeros_like(Kb)
+    for d in range(3):
+        dense[sel[0, d, 0]] += dK[0, d]
+    np.testing.assert_allclose(dense, k.grad.numpy(), atol=1e-12)
+
+
+def test_route_backward_ties_exclusion_zero_vectors():
+    H, D = 1, 2
+    Kb = np.array([[[1.0, 0.0]], [[1.0, 0.0]], [[0.0, 0.0]]])          # chunks 0 and 1 tie, chunk 2 is zero
+    Qr = np.array([[[[1.0, 0.0]], [[2.0, 0.0]]]])                       # tokens 0 and 1 tie (same direction)
+    off = np.array([0, 2, 3])
+    dQ, dK, sel = O.route_backward(Qr, Kb, off, np.array([[1.0, 5.0]]))
+    assert sel[0, 0].tolist() == [0, 0]                                 # first chunk, first token
+    assert np.all(dK[0, 1] == 0) and sel[0, 1].tolist() == [2, 0]       # zero key: no gradient
+    # q^ = k^: the cosine is at its maximum, so the gradient vanishes
+    assert np.allclose(dQ, 0.0) and np.allclose(dK, 0.0)
+    _, _, sel = O.route_backward(Qr, Kb, off, np.array([[1.0, 5.0]]), exclude=np.array([[True, False]]))
+    assert sel[0, 0].tolist() == [-1, -1]
+
+
 # ------------------------------------------------------------ store updates
 def _store_of(docs):
     """An independent construction: a store built from scratch from a list of per-document row blocks."""
