@@ -347,6 +347,21 @@ def main():
     kept_chunks = int(del_out[4][1].item())
     delete_bytes = 2 * kept_chunks * H * (D * 2 + 4) + w.n_docs * (1 + 8 + 4 + 8)
     del del_out
+    # routing-score backward over one 100M-token layer: every document gets an upstream gradient
+    _, ch0 = ops.route_scores(qr[0], krbar[0], off_dev, want_chunk_scores=True, ws=ws_r, krbar_inv_norm=knorm[0])
+    d_doc = torch.from_numpy(np.random.default_rng(10).standard_normal((1, w.n_docs)).astype(np.float32)).to(dev)
+    bwd_out = (torch.empty((1, w.T, H, D), dtype=torch.float32, device=dev),
+               torch.empty((1, w.n_docs, H, D), dtype=torch.float32, device=dev),
+               torch.empty((1, w.n_docs, 2), dtype=torch.int32, device=dev))
+    ws_b = ops.workspace(ops.route_backward_workspace_bytes(1, w.T, H, D, w.n_docs), dev, "bench-route-bwd")
+    bwd_ms = time_ms(lambda: ops.route_scores_backward(qr[0], krbar[0], off_dev, ch0, d_doc, krbar_inv_norm=knorm[0],
+                                                       dQr=bwd_out[0], dKsel=bwd_out[1], sel=bwd_out[2], ws=ws_b), 5)
+    # algorithmic bytes: chunk scores, offsets and upstream gradients read; each document's selected
+    # Krbar row read once; its fp32 key gradient and (chunk, token) written; Qr read, dQr written
+    bwd_bytes = (G * 4 + (w.n_docs + 1) * 8 + w.n_docs * 4 + w.n_docs * H * D * (2 + 4) + w.n_docs * 8
+                 + w.T * H * D * (2 + 4))
+    bwd_flops = 2.0 * w.n_docs * w.T * H * D          # the recomputed token scores of the selected chunks
+    del bwd_out, ch0
 
     log("side measurements: host-fetch step, attention, top-k, gather done")
     # the 10M-token batch-16 scan: 16 queries x 64 tokens over 165K chunks (matrix-core bound)
@@ -503,6 +518,10 @@ def main():
         "pool_GBps": pool_bytes / (sum(pool_us) * 1e-6) / 1e9,
         "store_delete_10pct_100M_layer": {"ms": delete_ms, "GBps": delete_bytes / (delete_ms * 1e-3) / 1e9,
                                           "frac_of_8TBps": delete_bytes / (delete_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "route_backward_100M_layer": {"ms": bwd_ms, "GBps": bwd_bytes / (bwd_ms * 1e-3) / 1e9,
+                                      "frac_of_8TBps": bwd_bytes / (bwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                      "recompute_TFLOPs": bwd_flops / (bwd_ms * 1e-3) / 1e12,
+                                      "docs_with_gradient": w.n_docs},
         "encode_router_keys_10M": {"ms": float(sum(enc_ms)), "GBps": enc_bytes / (sum(enc_ms) * 1e-3) / 1e9,
                                    "frac_of_8TBps": enc_bytes / (sum(enc_ms) * 1e-3) / 1e9 / HBM_PEAK_GBS,
                                    "d_model": 2560, "projection_TFLOPs_equiv": enc_flops / (sum(enc_ms) * 1e-3) / 1e12},

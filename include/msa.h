@@ -12,6 +12,7 @@
  *   msa_store_append        update: append documents to the routing store in place
  *   msa_krbar_inv_norms     offline: 1/|Krbar| per chunk and head, stored beside the store
  *   msa_route_scores        online: cosine routing scan over every Krbar chunk
+ *   msa_route_scores_backward  training: gradient of the routing scores (Qr, selected Krbar)
  *   msa_topk_docs           online: the k most relevant documents
  *   msa_fetch_docs          online: copy the selected content KV from pinned host
  *   msa_gather_docs         online: same, as one device kernel reading mapped host memory
@@ -194,6 +195,43 @@ int msa_route_scores(const uint16_t* Qr, int B, int T, int H, int D,
                      const int64_t* doc_chunk_off, int64_t n_docs,
                      const uint8_t* doc_exclude, float* doc_scores, float* chunk_scores,
                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * msa_route_scores_backward -- gradient of the routing scores.
+ *
+ * Defined by: b-lab.team summary sec. 2 (an auxiliary routing loss supervises
+ * the sparse attention during training) and chatpaper.ai Abstract (MSA is
+ * trained end to end), applied to the forward of msa_route_scores.  Given
+ * d_doc_scores = dL/d doc_scores it returns dL/dQr and, per (query, document),
+ * dL/dKrbar of the document's selected chunk.  Each max passes its gradient to
+ * its first maximiser: the selected chunk g is the lowest-index maximum of
+ * chunk_scores over the document's chunks, and the selected token t the
+ * lowest-index maximum of S[b, :, g] (recomputed in fp32).  Per head, with
+ * q^ = q/|q|, k^ = k/|k|, c = q^.k^ and w = d_doc_scores[b,d] / H:
+ *   dQr[b,t,h,:]   += w (k^ - c q^) / |q|      (k = Krbar[g,h,:], q = Qr[b,t,h,:])
+ *   dKsel[b,d,h,:]  = w (q^ - c k^) / |k|
+ * A document that is empty, excluded, or has d_doc_scores == 0 passes nothing
+ * (sel = (-1, -1), dKsel row 0); a zero q or k passes nothing for its head.
+ *
+ *   Qr, Krbar, krbar_inv_norm, doc_chunk_off, doc_exclude: as given to
+ *                   msa_route_scores (krbar_inv_norm may be NULL)
+ *   chunk_scores    fp32 [B, n_chunks]: that call's chunk_scores output
+ *   d_doc_scores    fp32 [B, n_docs]
+ *   dQr             fp32 [B, T, H, D] out (every element written)
+ *   dKsel           fp32 [B, n_docs, H, D] out: the gradient w.r.t. Krbar[sel[b,d,0]]
+ *                   (sum over b to accumulate into a store-shaped gradient)
+ *   sel             int32 [B, n_docs, 2] out: (chunk, token) or (-1, -1)
+ *   workspace       >= msa_route_backward_workspace_bytes(B, T, H, D, n_docs) bytes
+ *   H in {1,2,4,8}, D == 128, 1 <= T <= 8192, 1 <= B <= 65535, 1 <= n_docs < 2^30.
+ * Deterministic: the query gradient is summed in document order, without atomics.
+ */
+size_t msa_route_backward_workspace_bytes(int B, int T, int H, int D, int64_t n_docs);
+int msa_route_scores_backward(const uint16_t* Qr, int B, int T, int H, int D,
+                              const uint16_t* Krbar, const float* krbar_inv_norm, int64_t n_chunks,
+                              const int64_t* doc_chunk_off, int64_t n_docs, const uint8_t* doc_exclude,
+                              const float* chunk_scores, const float* d_doc_scores,
+                              float* dQr, float* dKsel, int32_t* sel,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * msa_krbar_inv_norms -- 1/|Krbar[g, h, :]| for every pooled chunk and head.

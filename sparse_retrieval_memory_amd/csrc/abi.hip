@@ -188,6 +188,40 @@ int msa_route_scores(const uint16_t* Qr, int B, int T, int H, int D, const uint1
                            doc_scores, chunk_scores, workspace, stream);
 }
 
+size_t msa_route_backward_workspace_bytes(int B, int T, int H, int D, int64_t n_docs) {
+  (void)D;
+  if (B < 1 || T < 1 || H < 1 || n_docs < 1) return 0;
+  return msa::route_bwd_workspace(B, T, H, n_docs);
+}
+
+int msa_route_scores_backward(const uint16_t* Qr, int B, int T, int H, int D, const uint16_t* Krbar,
+                              const float* krbar_inv_norm, int64_t n_chunks, const int64_t* doc_chunk_off,
+                              int64_t n_docs, const uint8_t* doc_exclude, const float* chunk_scores,
+                              const float* d_doc_scores, float* dQr, float* dKsel, int32_t* sel, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  msa::clear_error();
+  MSA_CHECK_ARG(B >= 1 && T >= 1, "B >= 1 and T >= 1 required (B=%d, T=%d)", B, T);
+  MSA_CHECK_ARG(n_docs >= 1 && n_chunks >= 0, "n_docs >= 1 and n_chunks >= 0 required");
+  MSA_CHECK_ARG(Qr && doc_chunk_off && chunk_scores && d_doc_scores && dQr && dKsel && sel &&
+                    (Krbar || n_chunks == 0),
+                "null pointer");
+  MSA_CHECK_SUPPORTED(D == 128, "D=%d unsupported (D must be 128)", D);
+  MSA_CHECK_SUPPORTED(H == 1 || H == 2 || H == 4 || H == 8, "H=%d unsupported (1, 2, 4 or 8)", H);
+  MSA_CHECK_SUPPORTED(T <= msa::ROUTE_BWD_MAX_T, "T=%d unsupported (T <= %d)", T, msa::ROUTE_BWD_MAX_T);
+  MSA_CHECK_ARG(B <= 65535, "B must be <= 65535");
+  MSA_CHECK_ARG(n_docs < ((int64_t)1 << 30) && n_chunks < ((int64_t)1 << 40), "size out of range");
+  MSA_CHECK_ARG(aligned16(Qr) && (n_chunks == 0 || aligned16(Krbar)) && aligned16(dQr) && aligned16(dKsel),
+                "Qr, Krbar, dQr and dKsel must be 16-byte aligned");
+  const size_t need = msa::route_bwd_workspace(B, T, H, n_docs);
+  if (workspace_bytes < need || workspace == nullptr) {
+    msa::set_error("workspace %zu bytes < required %zu", workspace_bytes, need);
+    return MSA_ERR_WORKSPACE;
+  }
+  MSA_CHECK_ARG(aligned16(workspace), "workspace must be 16-byte aligned");
+  return msa::launch_route_bwd(Qr, B, T, H, Krbar, krbar_inv_norm, n_chunks, doc_chunk_off, n_docs, doc_exclude,
+                               chunk_scores, d_doc_scores, dQr, dKsel, sel, workspace, stream);
+}
+
 size_t msa_topk_workspace_bytes(int B, int64_t n_docs, int k) {
   if (B < 1 || n_docs < 1 || k < 1) return 0;
   return msa::topk_workspace(B, n_docs, k);

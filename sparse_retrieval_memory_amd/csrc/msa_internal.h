@@ -98,6 +98,24 @@ __device__ __forceinline__ void wait_vmem_all() {
   asm volatile("" ::: "memory");
 }
 
+// Inclusive scan of (a, b) over a workgroup of up to 1024 threads (a multiple
+// of 64): shuffles within each wave, then the wave totals.  s_a / s_b: LDS
+// scratch of blockDim.x / 64 entries; callers barrier before reusing them.
+__device__ __forceinline__ void block_scan2(int64_t& a, int64_t& b, int64_t* s_a, int64_t* s_b) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int s = 1; s < 64; s <<= 1) {
+    const int64_t ua = __shfl_up(a, s), ub = __shfl_up(b, s);
+    if (lane >= s) { a += ua; b += ub; }
+  }
+  if (lane == 63) { s_a[wave] = a; s_b[wave] = b; }
+  __syncthreads();
+  int64_t ba = 0, bb = 0;
+  for (int w = 0; w < wave; ++w) { ba += s_a[w]; bb += s_b[w]; }
+  a += ba;
+  b += bb;
+}
+
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 // Asynchronous 16-byte-per-lane global -> LDS copy.  The LDS destination of
@@ -137,6 +155,12 @@ int launch_store_delete(const uint16_t* rows, const float* norms, const int64_t*
                         const uint8_t* keep, uint16_t* rows_out, float* norms_out, int64_t* off_out,
                         int32_t* new_id, int64_t* counts, void* workspace, hipStream_t stream);
 size_t store_delete_workspace(int64_t n_docs);
+int launch_route_bwd(const uint16_t* Qr, int B, int T, int H, const uint16_t* Krbar, const float* inv_norm,
+                     int64_t n_chunks, const int64_t* doc_chunk_off, int64_t n_docs, const uint8_t* doc_exclude,
+                     const float* chunk_scores, const float* d_doc_scores, float* dQr, float* dKsel, int32_t* sel,
+                     void* workspace, hipStream_t stream);
+size_t route_bwd_workspace(int B, int T, int H, int64_t n_docs);
+constexpr int ROUTE_BWD_MAX_T = 8192;
 int launch_store_append(uint16_t* rows, float* norms, int64_t* off, int64_t n_docs, int64_t n_chunks, int H,
                         const uint16_t* new_rows, const int64_t* new_off, int64_t n_new_docs, int64_t n_new_chunks,
                         hipStream_t stream);

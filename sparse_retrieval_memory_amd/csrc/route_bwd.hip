@@ -1,0 +1,609 @@
+// Backward of the routing scores: gradients w.r.t. the router queries and the
+// selected chunks' pooled router keys, given the gradient of the document scores.
+//
+// b-lab.team summary sec. 2 (training): an auxiliary routing loss supervises the
+// sparse attention towards the right evidence; chatpaper.ai Abstract: MSA is
+// trained end to end.  The forward (route.hip) is a head mean of cosines, a max
+// over query tokens, then a max over a document's chunks.  Readings: each max
+// passes its gradient to its first (lowest-index) maximiser; an excluded or empty
+// document, a zero upstream gradient or a zero vector passes nothing.  With
+// q^ = q/|q|, k^ = k/|k| and c = q^.k^ per head:
+//   dc/dq = (k^ - c q^) / |q|,     dc/dk = (q^ - c k^) / |k|.
+//
+// Kernels, in launch order:
+//   route_bwd_select_kernel<H>  32 documents of one query per workgroup (8
+//       lanes each).  The selected chunk is the first maximum of the forward's
+//       chunk scores; the 32 chunk rows are staged in LDS (64 KB at H = 8, so two
+//       workgroups share a CU) and the token scores S[t] = mean_h cos are
+//       recomputed on v_mfma_f32_32x32x16_bf16 (router rows as A, the chunk rows
+//       as the 32 B columns) to find the first maximising token.  Then per
+//       document and head: the cosine, the key-gradient row, and two weights of
+//       the query gradient (w/|k| and w c, w = dL/d doc / H).
+//   hist / scan / scatter  a stable counting sort of the documents by selected
+//       token (tiles of 1,024 documents), so each token's documents sit
+//       contiguously and in document order.
+//   piece<H>  each token's list is cut into pieces of 64 documents; one
+//       workgroup sums w/|k| * k and w c over a piece (16-byte row loads, rows
+//       split over lane groups and added in a fixed order).
+//   final   one workgroup per token adds its pieces in order:
+//       dq = (sum w k/|k| - q^ sum w c) / |q|.  No atomics: the result does not
+//       depend on scheduling.
+#include "msa_internal.h"
+
+#include <math.h>
+
+namespace msa {
+namespace {
+
+constexpr int D = 128;
+constexpr int SEL_DOCS = 32;        // documents per select workgroup (the 32 MFMA B columns)
+constexpr int SEL_THREADS = 256;    // 4 waves; wave w takes token tiles w, w + 4, ...
+constexpr int LPD = SEL_THREADS / SEL_DOCS;   // lanes per document
+constexpr int SORT_TILE = 1024;     // documents per histogram / scatter workgroup
+constexpr int PIECE = 64;           // documents per partial sum of the query gradient
+constexpr int PIECE_UNROLL = 8;
+constexpr int MAX_T = ROUTE_BWD_MAX_T;
+
+template <int H>
+struct SelCfg {
+  static constexpr int HD = H * D;
+  static constexpr int KROW = HD + 8;     // staged row stride (bf16): +16 B staggers the banks by 4
+  static constexpr int VPR = HD / 8;      // 16-byte vectors per chunk row
+};
+
+__device__ __forceinline__ float sq_norm_piece(uint4 v, float acc) {
+  acc = dot2_bf16(v.x, v.x, acc);
+  acc = dot2_bf16(v.y, v.y, acc);
+  acc = dot2_bf16(v.z, v.z, acc);
+  acc = dot2_bf16(v.w, v.w, acc);
+  return acc;
+}
+__device__ __forceinline__ float inv_norm(float ss) { return ss > 0.f ? 1.0f / sqrtf(ss) : 0.f; }
+
+// (score, token) -> key whose maximum is the largest score, then the lowest token.
+__device__ __forceinline__ uint64_t argmax_key(float s, int t) {
+  return ((uint64_t)enc_f32(s) << 32) | (uint32_t)(0x7FFFFFFF - t);
+}
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const uint32_t lo = __shfl_xor((uint32_t)v, m), hi = __shfl_xor((uint32_t)(v >> 32), m);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+template <int H>
+__global__ void __launch_bounds__(SEL_THREADS, 2)
+route_bwd_select_kernel(const uint16_t* __restrict__ Qr, int T, const uint16_t* __restrict__ Krbar,
+                        const float* __restrict__ knorm, const int64_t* __restrict__ off, int64_t n_docs,
+                        int64_t n_chunks, const uint8_t* __restrict__ exclude, const float* __restrict__ chunk_scores,
+                        const float* __restrict__ dDoc, float* __restrict__ dK, int32_t* __restrict__ sel,
+                        float* __restrict__ ikw, float* __restrict__ wcos) {
+  using CF = SelCfg<H>;
+  __shared__ __attribute__((aligned(16))) uint16_t k_s[SEL_DOCS * CF::KROW];
+  __shared__ float ik_s[SEL_DOCS][H];
+  __shared__ __attribute__((aligned(16))) float iq_s[SEL_THREADS / 64][32];
+  __shared__ uint64_t best_s[SEL_THREADS / 64][SEL_DOCS];
+  __shared__ int64_t g_s[SEL_DOCS];
+  __shared__ int t_s[SEL_DOCS];
+  __shared__ int any_s;
+
+  const int b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, m = lane & 31;
+  const int idoc = tid / LPD, sub = tid % LPD;
+  const int64_t d = (int64_t)blockIdx.x * SEL_DOCS + idoc;
+  const int64_t bd = (int64_t)b * n_docs + d;
+  const bool in = d < n_docs;
+
+  // ---- selected chunk: first maximum of the document's chunk scores, LPD lanes per document
+  if (tid == 0) any_s = 0;
+  float dd = 0.f;
+  int64_t c0 = 0;
+  uint64_t key = 0;                   // (score, -chunk within the document); 0 = none
+  if (in) {
+    dd = dDoc[bd];
+    if (!(exclude && exclude[bd]) && dd != 0.f) {
+      c0 = off[d];
+      const int64_t c1 = off[d + 1];
+      for (int64_t c = c0 + sub; c < c1; c += LPD)
+        key = max_u64(key, ((uint64_t)enc_f32(chunk_scores[(int64_t)b * n_chunks + c]) << 32) |
+                               (uint32_t)(0xFFFFFFFFu - (uint32_t)(c - c0)));
+    }
+  }
+#pragma unroll
+  for (int s = 1; s < LPD; s <<= 1) key = max_u64(key, shfl_xor_u64(key, s));
+  __syncthreads();
+  if (sub == 0) {
+    const int64_t g = key ? c0 + (int64_t)(0xFFFFFFFFu - (uint32_t)key) : -1;
+    g_s[idoc] = g;
+    if (g >= 0) any_s = 1;
+  }
+  __syncthreads();
+
+  uint64_t bk = 0;                    // best token key of column m
+  if (any_s) {
+    // ---- stage the selected rows (zeros for documents without one), all loads in flight
+    constexpr int NV = SEL_DOCS * CF::VPR / SEL_THREADS;
+    uint4 v[NV];
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int x = tid + u * SEL_THREADS;
+      const int64_t g = g_s[x / CF::VPR];
+      v[u] = make_uint4(0, 0, 0, 0);
+      if (g >= 0) v[u] = *reinterpret_cast<const uint4*>(Krbar + g * CF::HD + 8 * (x % CF::VPR));
+    }
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int x = tid + u * SEL_THREADS;
+      *reinterpret_cast<uint4*>(&k_s[(x / CF::VPR) * CF::KROW + 8 * (x % CF::VPR)]) = v[u];
+    }
+    __syncthreads();
+    if (tid < SEL_DOCS * H) {
+      const int i = tid / H, h = tid % H;
+      const int64_t g = g_s[i];
+      float ik = 0.f;
+      if (g >= 0) {
+        if (knorm) {
+          ik = knorm[g * H + h];
+        } else {
+          float ss = 0.f;
+          for (int x = 0; x < D / 8; ++x)
+            ss = sq_norm_piece(*reinterpret_cast<const uint4*>(&k_s[i * CF::KROW + h * D + 8 * x]), ss);
+          ik = inv_norm(ss);
+        }
+      }
+      ik_s[i][h] = ik;
+    }
+    __syncthreads();
+
+    // ---- token scores of the selected chunks: 32 tokens x 32 chunks per wave step
+    const int n_tt = (T + 31) / 32;
+    const float inv_h = 1.0f / (float)H;
+    for (int tt = wave; tt < n_tt; tt += SEL_THREADS / 64) {
+      const int t = tt * 32 + m;
+      const bool tv = t < T;
+      const uint16_t* qrow = Qr + ((int64_t)b * T + (tv ? t : 0)) * CF::HD + 8 * half;
+      bf16x8_t a[8];
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        uint4 x = make_uint4(0, 0, 0, 0);
+        if (tv) x = *reinterpret_cast<const uint4*>(qrow + 16 * ks);
+        a[ks] = __builtin_bit_cast(bf16x8_t, x);
+      }
+      f32x16_t s0 = {};
+#pragma unroll 2
+      for (int h = 0; h < H; ++h) {
+        bf16x8_t an[8];
+        if (h + 1 < H) {
+#pragma unroll
+          for (int ks = 0; ks < 8; ++ks) {
+            uint4 x = make_uint4(0, 0, 0, 0);
+            if (tv) x = *reinterpret_cast<const uint4*>(qrow + (h + 1) * D + 16 * ks);
+            an[ks] = __builtin_bit_cast(bf16x8_t, x);
+          }
+        }
+        float ss = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) ss = sq_norm_piece(__builtin_bit_cast(uint4, a[ks]), ss);
+        ss += __shfl_xor(ss, 32);
+        f32x16_t c = {};
+        const uint16_t* bp = &k_s[m * CF::KROW + h * D + 8 * half];
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], *reinterpret_cast<const bf16x8_t*>(bp + 16 * ks), c,
+                                                      0, 0, 0);
+        // the row (token) inverse norms of this head, through a wave-private LDS slot
+        if (half == 0) iq_s[wave][m] = inv_norm(ss);
+        __builtin_amdgcn_wave_barrier();
+        const float ik = ik_s[m][h];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4_t r = *reinterpret_cast<const f32x4_t*>(&iq_s[wave][8 * q + 4 * half]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s0[4 * q + e] += c[4 * q + e] * r[e] * ik;
+        }
+        __builtin_amdgcn_wave_barrier();
+        if (h + 1 < H) {
+#pragma unroll
+          for (int ks = 0; ks < 8; ++ks) a[ks] = an[ks];
+        }
+      }
+      // C register i holds row 8 (i / 4) + 4 half + i % 4 of column m
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int tok = tt * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+        if (tok < T) bk = max_u64(bk, argmax_key(s0[i] * inv_h, tok));
+      }
+    }
+    bk = max_u64(bk, shfl_xor_u64(bk, 32));
+  }
+  if (half == 0) best_s[wave][m] = bk;
+  __syncthreads();
+  if (tid < SEL_DOCS) {
+    uint64_t bb = 0;
+#pragma unroll
+    for (int w = 0; w < SEL_THREADS / 64; ++w) bb = max_u64(bb, best_s[w][tid]);
+    const bool ok = g_s[tid] >= 0 && bb != 0;      // every valid token has a nonzero key
+    t_s[tid] = ok ? 0x7FFFFFFF - (int)(uint32_t)bb : -1;
+    if (!ok) g_s[tid] = -1;
+  }
+  __syncthreads();
+
+  // ---- per document (LPD lanes) and head: cosine, key gradient, query-gradient weights
+  if (!in) return;
+  const int64_t g = g_s[idoc];
+  const int tsel = t_s[idoc];
+  if (sub == 0) {
+    sel[2 * bd] = (int32_t)g;
+    sel[2 * bd + 1] = tsel;
+  }
+  float4* o = reinterpret_cast<float4*>(dK + bd * CF::HD);
+  if (g < 0) {
+#pragma unroll
+    for (int x = sub; x < CF::HD / 4; x += LPD) o[x] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (sub < H) { ikw[bd * H + sub] = 0.f; wcos[bd * H + sub] = 0.f; }
+    return;
+  }
+  const float w = dd * (1.0f / (float)H);
+  const uint16_t* qrow = Qr + ((int64_t)b * T + tsel) * CF::HD;
+  const uint16_t* krow = &k_s[idoc * CF::KROW];
+  uint2 qv[H][4];
+#pragma unroll
+  for (int h = 0; h < H; ++h)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) qv[h][j] = *reinterpret_cast<const uint2*>(qrow + h * D + 4 * (sub + LPD * j));
+  float my_ikw = 0.f, my_wc = 0.f;
+#pragma unroll
+  for (int h = 0; h < H; ++h) {
+    uint2 kv[4];
+    float qq = 0.f, kk = 0.f, qk = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      kv[j] = *reinterpret_cast<const uint2*>(krow + h * D + 4 * (sub + LPD * j));
+      qq = dot2_bf16(qv[h][j].x, qv[h][j].x, qq); qq = dot2_bf16(qv[h][j].y, qv[h][j].y, qq);
+      kk = dot2_bf16(kv[j].x, kv[j].x, kk); kk = dot2_bf16(kv[j].y, kv[j].y, kk);
+      qk = dot2_bf16(qv[h][j].x, kv[j].x, qk); qk = dot2_bf16(qv[h][j].y, kv[j].y, qk);
+    }
+#pragma unroll
+    for (int s = 1; s < LPD; s <<= 1) {
+      qq += __shfl_xor(qq, s);
+      kk += __shfl_xor(kk, s);
+      qk += __shfl_xor(qk, s);
+    }
+    float ca = 0.f, cb = 0.f, ik = 0.f, cs = 0.f;
+    if (qq > 0.f && kk > 0.f) {
+      const float iq = 1.0f / sqrtf(qq);
+      ik = 1.0f / sqrtf(kk);
+      cs = qk * iq * ik;
+      ca = w * ik * iq;        // dK = w (q^ - c k^) / |k| = ca q - cb k
+      cb = w * ik * ik * cs;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      o[h * (D / 4) + sub + LPD * j] =
+          make_float4(ca * bf16_lo(qv[h][j].x) - cb * bf16_lo(kv[j].x), ca * bf16_hi(qv[h][j].x) - cb * bf16_hi(kv[j].x),
+                      ca * bf16_lo(qv[h][j].y) - cb * bf16_lo(kv[j].y), ca * bf16_hi(qv[h][j].y) - cb * bf16_hi(kv[j].y));
+    if (h == sub) { my_ikw = w * ik; my_wc = w * cs; }
+  }
+  if (sub < H) { ikw[bd * H + sub] = my_ikw; wcos[bd * H + sub] = my_wc; }
+}
+
+// Per tile of SORT_TILE documents: how many select each token.
+__global__ void __launch_bounds__(256)
+route_bwd_hist_kernel(const int32_t* __restrict__ sel, int64_t n_docs, int T, int64_t n_tiles,
+                      int32_t* __restrict__ tile_cnt) {
+  __shared__ int cnt[MAX_T];
+  const int b = blockIdx.y, tid = threadIdx.x;
+  const int64_t tile = blockIdx.x;
+  for (int t = tid; t < T; t += 256) cnt[t] = 0;
+  __syncthreads();
+  for (int i = tid; i < SORT_TILE; i += 256) {
+    const int64_t d = tile * SORT_TILE + i;
+    if (d < n_docs) {
+      const int t = sel[((int64_t)b * n_docs + d) * 2 + 1];
+      if (t >= 0) atomicAdd(&cnt[t], 1);
+    }
+  }
+  __syncthreads();
+  int32_t* out = tile_cnt + ((int64_t)b * n_tiles + tile) * T;
+  for (int t = tid; t < T; t += 256) out[t] = cnt[t];
+}
+
+// One workgroup per query: each token's segment in the sorted order (seg), its
+// pieces (pstart), the piece -> token table, and, in place of the tile counts,
+// each tile's offset inside the token's segment.
+__global__ void __launch_bounds__(1024)
+route_bwd_scan_kernel(int32_t* __restrict__ tile_cnt, int64_t n_tiles, int T, int64_t max_pieces,
+                      int32_t* __restrict__ seg, int32_t* __restrict__ pstart, int32_t* __restrict__ piece_t) {
+  constexpr int U = 16;
+  __shared__ int64_t s_a[16], s_b[16];
+  __shared__ int64_t carry_a, carry_b;
+  const int b = blockIdx.x, tid = threadIdx.x;
+  int32_t* tc = tile_cnt + (int64_t)b * n_tiles * T;
+  int32_t* sg = seg + (int64_t)b * (T + 1);
+  int32_t* ps = pstart + (int64_t)b * (T + 1);
+  int32_t* pt = piece_t + (int64_t)b * max_pieces;
+  if (tid == 0) { carry_a = 0; carry_b = 0; }
+  __syncthreads();
+  for (int t0 = 0; t0 < T; t0 += 1024) {
+    const int t = t0 + tid;
+    int64_t tot = 0;
+    if (t < T) {
+      int64_t k0 = 0;
+      for (; k0 + U <= n_tiles; k0 += U) {
+        int32_t c[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) c[u] = tc[(k0 + u) * T + t];
+#pragma unroll
+        for (int u = 0; u < U; ++u) { tc[(k0 + u) * T + t] = (int32_t)tot; tot += c[u]; }
+      }
+      for (; k0 < n_tiles; ++k0) {
+        const int32_t c = tc[k0 * T + t];
+        tc[k0 * T + t] = (int32_t)tot;
+        tot += c;
+      }
+    }
+    const int64_t np = (tot + PIECE - 1) / PIECE;
+    int64_t a = tot, p = np;
+    block_scan2(a, p, s_a, s_b);
+    const int64_t ca = carry_a, cb = carry_b;
+    if (t < T) {
+      const int64_t p0 = cb + p - np;
+      sg[t] = (int32_t)(ca + a - tot);
+      ps[t] = (int32_t)p0;
+      for (int64_t j = 0; j < np; ++j) pt[p0 + j] = t;
+    }
+    __syncthreads();
+    if (tid == 1023) { carry_a = ca + a; carry_b = cb + p; }
+    __syncthreads();
+  }
+  if (tid == 0) { sg[T] = (int32_t)carry_a; ps[T] = (int32_t)carry_b; }
+}
+
+// Stable scatter: document d goes to its token's segment after every earlier
+// document with the same token.
+__global__ void __launch_bounds__(256)
+route_bwd_scatter_kernel(const int32_t* __restrict__ sel, int64_t n_docs, int T, int64_t n_tiles,
+                         const int32_t* __restrict__ tile_cnt, const int32_t* __restrict__ seg,
+                         int32_t* __restrict__ order) {
+  __shared__ int base[MAX_T];
+  __shared__ __attribute__((aligned(16))) int t_s[256];
+  const int b = blockIdx.y, tid = threadIdx.x, wave = tid >> 6;
+  const int64_t tile = blockIdx.x;
+  const int32_t* tc = tile_cnt + ((int64_t)b * n_tiles + tile) * T;
+  const int32_t* sg = seg + (int64_t)b * (T + 1);
+  for (int t = tid; t < T; t += 256) base[t] = sg[t] + tc[t];
+  __syncthreads();
+  for (int sb = 0; sb < SORT_TILE; sb += 256) {
+    if (tile * SORT_TILE + sb >= n_docs) break;
+    const int64_t d = tile * SORT_TILE + sb + tid;
+    const int t = d < n_docs ? sel[((int64_t)b * n_docs + d) * 2 + 1] : -1;
+    t_s[tid] = t;
+    __syncthreads();
+    // rank among the earlier documents of this block with the same token
+    int rank = 0;
+    const int n4 = (wave + 1) * 16;
+#pragma unroll 4
+    for (int j4 = 0; j4 < n4; ++j4) {
+      const int4 v = *reinterpret_cast<const int4*>(&t_s[4 * j4]);
+      const int j = 4 * j4;
+      rank += (j < tid && v.x == t) + (j + 1 < tid && v.y == t) + (j + 2 < tid && v.z == t) +
+              (j + 3 < tid && v.w == t);
+    }
+    if (t >= 0) order[(int64_t)b * n_docs + base[t] + rank] = (int32_t)d;
+    __syncthreads();
+    if (t >= 0) atomicAdd(&base[t], 1);
+    __syncthreads();
+  }
+}
+
+// One piece of one token's list: sum over its documents of (w/|k|) k and w c.
+// Thread x owns 8 dims of the H*D row and every RG-th document of the piece; the
+// RG row groups are then added in order.
+template <int H>
+__global__ void __launch_bounds__(256)
+route_bwd_piece_kernel(const uint16_t* __restrict__ Krbar, int64_t n_docs, int T, const int32_t* __restrict__ sel,
+                       const float* __restrict__ ikw, const float* __restrict__ wcos,
+                       const int32_t* __restrict__ order, const int32_t* __restrict__ seg,
+                       const int32_t* __restrict__ pstart, const int32_t* __restrict__ piece_t, int64_t max_pieces,
+                       float* __restrict__ partial, float* __restrict__ partial_c) {
+  constexpr int HD = H * D, TPR = HD / 8, RG = 256 / TPR;
+  __shared__ int64_t g_s[PIECE], bd_s[PIECE];
+  __shared__ __attribute__((aligned(16))) float red[RG][HD];
+  __shared__ float red_c[RG][H];
+  const int b = blockIdx.y, tid = threadIdx.x;
+  const int64_t p = blockIdx.x;
+  const int32_t* ps = pstart + (int64_t)b * (T + 1);
+  if (p >= ps[T]) return;
+  const int t = piece_t[(int64_t)b * max_pieces + p];
+  const int32_t* sg = seg + (int64_t)b * (T + 1);
+  const int64_t lo = sg[t] + (p - ps[t]) * (int64_t)PIECE;
+  const int64_t hi = sg[t + 1] < lo + PIECE ? (int64_t)sg[t + 1] : lo + PIECE;
+  const int n = (int)(hi - lo);
+  if (tid < n) {
+    const int64_t bd = (int64_t)b * n_docs + order[(int64_t)b * n_docs + lo + tid];
+    bd_s[tid] = bd;
+    g_s[tid] = sel[2 * bd];
+  }
+  __syncthreads();
+  const int rg = tid / TPR, e0 = 8 * (tid % TPR), h = e0 / D;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float cs = 0.f;
+  for (int j0 = rg; j0 < n; j0 += RG * PIECE_UNROLL) {
+    uint4 kv[PIECE_UNROLL];
+    float iw[PIECE_UNROLL], wc[PIECE_UNROLL];
+#pragma unroll
+    for (int u = 0; u < PIECE_UNROLL; ++u) {
+      const int j = j0 + u * RG;
+      if (j < n) {
+        const int64_t bd = bd_s[j];
+        kv[u] = *reinterpret_cast<const uint4*>(Krbar + g_s[j] * HD + e0);
+        iw[u] = ikw[bd * H + h];
+        wc[u] = wcos[bd * H + h];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < PIECE_UNROLL; ++u) {
+      if (j0 + u * RG < n) {
+        const uint32_t x[4] = {kv[u].x, kv[u].y, kv[u].z, kv[u].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] += iw[u] * bf16_lo(x[e]);
+          acc[2 * e + 1] += iw[u] * bf16_hi(x[e]);
+        }
+        cs += wc[u];
+      }
+    }
+  }
+  *reinterpret_cast<float4*>(&red[rg][e0]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  *reinterpret_cast<float4*>(&red[rg][e0 + 4]) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  if ((e0 & (D - 1)) == 0) red_c[rg][h] = cs;
+  __syncthreads();
+  if (rg != 0) return;
+  for (int r = 1; r < RG; ++r) {
+    const float4 x0 = *reinterpret_cast<const float4*>(&red[r][e0]);
+    const float4 x1 = *reinterpret_cast<const float4*>(&red[r][e0 + 4]);
+    acc[0] += x0.x; acc[1] += x0.y; acc[2] += x0.z; acc[3] += x0.w;
+    acc[4] += x1.x; acc[5] += x1.y; acc[6] += x1.z; acc[7] += x1.w;
+    cs += red_c[r][h];
+  }
+  float* o = partial + ((int64_t)b * max_pieces + p) * HD + e0;
+  *reinterpret_cast<float4*>(o) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  *reinterpret_cast<float4*>(o + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  if ((e0 & (D - 1)) == 0) partial_c[((int64_t)b * max_pieces + p) * H + h] = cs;
+}
+
+// One token: its pieces in order, then dq = (A - q^ C) / |q| per head.
+__global__ void __launch_bounds__(256)
+route_bwd_final_kernel(const uint16_t* __restrict__ Qr, int T, int H, const int32_t* __restrict__ pstart,
+                       int64_t max_pieces, const float* __restrict__ partial, const float* __restrict__ partial_c,
+                       float* __restrict__ dQ) {
+  constexpr int U = 8;
+  const int t = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int HD = H * D, e0 = 4 * tid, h = e0 / D;
+  if (e0 >= HD) return;
+  const int32_t* ps = pstart + (int64_t)b * (T + 1);
+  const int64_t p1 = ps[t + 1];
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  float cs = 0.f;
+  for (int64_t p0 = ps[t]; p0 < p1; p0 += U) {
+    float4 v[U];
+    float c[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (p0 + u < p1) {
+        v[u] = *reinterpret_cast<const float4*>(partial + ((int64_t)b * max_pieces + p0 + u) * HD + e0);
+        c[u] = partial_c[((int64_t)b * max_pieces + p0 + u) * H + h];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (p0 + u < p1) {
+        acc[0] += v[u].x; acc[1] += v[u].y; acc[2] += v[u].z; acc[3] += v[u].w;
+        cs += c[u];
+      }
+    }
+  }
+  const uint2 qv = *reinterpret_cast<const uint2*>(Qr + ((int64_t)b * T + t) * HD + e0);
+  const float q[4] = {bf16_lo(qv.x), bf16_hi(qv.x), bf16_lo(qv.y), bf16_hi(qv.y)};
+  float ss = dot2_bf16(qv.x, qv.x, 0.f);
+  ss = dot2_bf16(qv.y, qv.y, ss);
+#pragma unroll
+  for (int s = 1; s < 32; s <<= 1) ss += __shfl_xor(ss, s);   // the 32 threads of head h
+  const float iq = inv_norm(ss);
+  *reinterpret_cast<float4*>(dQ + ((int64_t)b * T + t) * HD + e0) =
+      make_float4(iq * (acc[0] - iq * q[0] * cs), iq * (acc[1] - iq * q[1] * cs), iq * (acc[2] - iq * q[2] * cs),
+                  iq * (acc[3] - iq * q[3] * cs));
+}
+
+struct BwdLayout {
+  int64_t n_tiles, max_pieces;
+  size_t ikw, wcos, tile_cnt, seg, pstart, piece_t, order, partial, partial_c, total;
+};
+
+BwdLayout bwd_layout(int B, int T, int H, int64_t n_docs) {
+  BwdLayout L;
+  size_t o = 0;
+  auto take = [&o](size_t bytes) {
+    const size_t at = o;
+    o += (bytes + 255) & ~(size_t)255;
+    return at;
+  };
+  const size_t Bz = (size_t)B;
+  L.n_tiles = (n_docs + SORT_TILE - 1) / SORT_TILE;
+  L.max_pieces = (n_docs + PIECE - 1) / PIECE + T;
+  L.ikw = take(Bz * n_docs * H * 4);
+  L.wcos = take(Bz * n_docs * H * 4);
+  L.tile_cnt = take(Bz * L.n_tiles * T * 4);
+  L.seg = take(Bz * (T + 1) * 4);
+  L.pstart = take(Bz * (T + 1) * 4);
+  L.piece_t = take(Bz * L.max_pieces * 4);
+  L.order = take(Bz * n_docs * 4);
+  L.partial = take(Bz * L.max_pieces * H * D * 4);
+  L.partial_c = take(Bz * L.max_pieces * H * 4);
+  L.total = o;
+  return L;
+}
+
+struct BwdArgs {
+  const uint16_t* Qr; int B, T; const uint16_t* Krbar; const float* knorm; int64_t n_chunks;
+  const int64_t* off; int64_t n_docs; const uint8_t* exclude; const float* chunk_scores; const float* dDoc;
+  float* dQ; float* dK; int32_t* sel;
+};
+
+template <int H>
+int launch_bwd_h(const BwdArgs& A, const BwdLayout& L, uint8_t* ws, hipStream_t stream) {
+  float* ikw = reinterpret_cast<float*>(ws + L.ikw);
+  float* wcos = reinterpret_cast<float*>(ws + L.wcos);
+  int32_t* tile_cnt = reinterpret_cast<int32_t*>(ws + L.tile_cnt);
+  int32_t* seg = reinterpret_cast<int32_t*>(ws + L.seg);
+  int32_t* pstart = reinterpret_cast<int32_t*>(ws + L.pstart);
+  int32_t* piece_t = reinterpret_cast<int32_t*>(ws + L.piece_t);
+  int32_t* order = reinterpret_cast<int32_t*>(ws + L.order);
+  float* partial = reinterpret_cast<float*>(ws + L.partial);
+  float* partial_c = reinterpret_cast<float*>(ws + L.partial_c);
+  const int B = A.B, T = A.T;
+  const int64_t n_docs = A.n_docs;
+  hipLaunchKernelGGL(route_bwd_select_kernel<H>, dim3((unsigned)((n_docs + SEL_DOCS - 1) / SEL_DOCS), (unsigned)B),
+                     dim3(SEL_THREADS), 0, stream, A.Qr, T, A.Krbar, A.knorm, A.off, n_docs, A.n_chunks, A.exclude,
+                     A.chunk_scores, A.dDoc, A.dK, A.sel, ikw, wcos);
+  MSA_CHECK_LAUNCH();
+  const dim3 gt((unsigned)L.n_tiles, (unsigned)B);
+  hipLaunchKernelGGL(route_bwd_hist_kernel, gt, dim3(256), 0, stream, A.sel, n_docs, T, L.n_tiles, tile_cnt);
+  MSA_CHECK_LAUNCH();
+  hipLaunchKernelGGL(route_bwd_scan_kernel, dim3((unsigned)B), dim3(1024), 0, stream, tile_cnt, L.n_tiles, T,
+                     L.max_pieces, seg, pstart, piece_t);
+  MSA_CHECK_LAUNCH();
+  hipLaunchKernelGGL(route_bwd_scatter_kernel, gt, dim3(256), 0, stream, A.sel, n_docs, T, L.n_tiles, tile_cnt, seg,
+                     order);
+  MSA_CHECK_LAUNCH();
+  hipLaunchKernelGGL(route_bwd_piece_kernel<H>, dim3((unsigned)L.max_pieces, (unsigned)B), dim3(256), 0, stream,
+                     A.Krbar, n_docs, T, A.sel, ikw, wcos, order, seg, pstart, piece_t, L.max_pieces, partial,
+                     partial_c);
+  MSA_CHECK_LAUNCH();
+  hipLaunchKernelGGL(route_bwd_final_kernel, dim3((unsigned)T, (unsigned)B), dim3(256), 0, stream, A.Qr, T, H,
+                     pstart, L.max_pieces, partial, partial_c, A.dQ);
+  MSA_CHECK_LAUNCH();
+  return MSA_OK;
+}
+
+}  // namespace
+
+size_t route_bwd_workspace(int B, int T, int H, int64_t n_docs) { return bwd_layout(B, T, H, n_docs).total; }
+
+int launch_route_bwd(const uint16_t* Qr, int B, int T, int H, const uint16_t* Krbar, const float* inv_norm_k,
+                     int64_t n_chunks, const int64_t* off, int64_t n_docs, const uint8_t* exclude,
+                     const float* chunk_scores, const float* dDoc, float* dQ, float* dK, int32_t* sel,
+                     void* workspace, hipStream_t stream) {
+  const BwdLayout L = bwd_layout(B, T, H, n_docs);
+  const BwdArgs A{Qr, B, T, Krbar, inv_norm_k, n_chunks, off, n_docs, exclude, chunk_scores, dDoc, dQ, dK, sel};
+  uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
+  switch (H) {
+    case 1: return launch_bwd_h<1>(A, L, ws, stream);
+    case 2: return launch_bwd_h<2>(A, L, ws, stream);
+    case 4: return launch_bwd_h<4>(A, L, ws, stream);
+    case 8: return launch_bwd_h<8>(A, L, ws, stream);
+    default: set_error("route backward: H=%d unsupported", H); return MSA_ERR_UNSUPPORTED;
+  }
+}
+
+}  // namespace msa

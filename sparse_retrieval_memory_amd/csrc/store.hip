@@ -23,23 +23,6 @@ constexpr int TILE = 1024;          // documents per scan workgroup (one per thr
 constexpr int MOVE_THREADS = 256;
 constexpr int MOVE_UNROLL = 4;      // 16-byte vectors in flight per lane
 
-// Inclusive scan of (a, b) over the 1024 threads of a workgroup: per-wave DPP-free
-// shuffles, then the 16 wave totals.  s_a/s_b: 16-entry LDS scratch.
-__device__ __forceinline__ void block_scan2(int64_t& a, int64_t& b, int64_t* s_a, int64_t* s_b) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int s = 1; s < 64; s <<= 1) {
-    const int64_t ua = __shfl_up(a, s), ub = __shfl_up(b, s);
-    if (lane >= s) { a += ua; b += ub; }
-  }
-  if (lane == 63) { s_a[wave] = a; s_b[wave] = b; }
-  __syncthreads();
-  int64_t ba = 0, bb = 0;
-  for (int w = 0; w < wave; ++w) { ba += s_a[w]; bb += s_b[w]; }
-  a += ba;
-  b += bb;
-}
-
 // Pass 1: per tile of TILE documents, the kept documents and their chunks.
 __global__ void __launch_bounds__(TILE)
 store_tile_sums_kernel(const int64_t* __restrict__ off, int64_t n_docs, const uint8_t* __restrict__ keep,

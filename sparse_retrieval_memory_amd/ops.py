@@ -166,6 +166,40 @@ def route_scores(Qr, Krbar, doc_chunk_off, doc_exclude=None, want_chunk_scores: 
     return doc_scores
 
 
+def route_backward_workspace_bytes(B, T, H, D, n_docs) -> int:
+    return int(_lib.load().msa_route_backward_workspace_bytes(B, T, H, D, n_docs))
+
+
+def route_scores_backward(Qr, Krbar, doc_chunk_off, chunk_scores, d_doc_scores, doc_exclude=None,
+                          krbar_inv_norm=None, dQr=None, dKsel=None, sel=None, ws=None, stream=None):
+    """msa_route_scores_backward: (dQr fp32 [B, T, H, D], dKsel fp32 [B, n_docs, H, D], sel int32 [B, n_docs, 2])."""
+    _bf16(Qr, "Qr"); _bf16(Krbar, "Krbar"); _dev(Qr, "Qr")
+    B, T, H, D = Qr.shape
+    n_chunks = Krbar.shape[0]
+    n_docs = doc_chunk_off.numel() - 1
+    dev = Qr.device
+    assert chunk_scores.dtype == torch.float32 and chunk_scores.shape == (B, n_chunks) and chunk_scores.is_contiguous()
+    assert d_doc_scores.dtype == torch.float32 and d_doc_scores.shape == (B, n_docs) and d_doc_scores.is_contiguous()
+    if dQr is None:
+        dQr = torch.empty((B, T, H, D), dtype=torch.float32, device=dev)
+    if dKsel is None:
+        dKsel = torch.empty((B, n_docs, H, D), dtype=torch.float32, device=dev)
+    if sel is None:
+        sel = torch.empty((B, n_docs, 2), dtype=torch.int32, device=dev)
+    if doc_exclude is not None:
+        assert doc_exclude.dtype in (torch.uint8, torch.bool) and doc_exclude.shape == (B, n_docs)
+        doc_exclude = doc_exclude.contiguous()
+    if krbar_inv_norm is not None:
+        assert krbar_inv_norm.dtype == torch.float32 and krbar_inv_norm.shape == (n_chunks, H)
+    need = route_backward_workspace_bytes(B, T, H, D, n_docs)
+    if ws is None:
+        ws = workspace(need, dev, "route_bwd")
+    _lib.call("msa_route_scores_backward", _p(Qr), B, T, H, D, _p(Krbar), _p(krbar_inv_norm), n_chunks,
+              _p(doc_chunk_off), n_docs, _p(doc_exclude), _p(chunk_scores), _p(d_doc_scores), _p(dQr), _p(dKsel),
+              _p(sel), _p(ws), ws.numel(), _stream(stream))
+    return dQr, dKsel, sel
+
+
 def topk_workspace_bytes(B, n_docs, k) -> int:
     return int(_lib.load().msa_topk_workspace_bytes(B, n_docs, k))
 

@@ -10,6 +10,15 @@ P4  attention: per output row ||o - o*|| / ||o*|| <= 2e-2 (bf16 inputs, fp32
     accumulation); the oracle attends over the GPU's selected set.
 P5  encoded router keys: within 1 bf16 ulp, or half an ulp plus 2^-14 sum_k |mean h_k||W_nk|
     (see encoded_keys_ok).
+P6  routing-score gradients: per element |gpu - oracle| <= 2^-15 * s, where s
+    sums over the element's contributions the bound 2|w|/|v| of one term
+    (w = dL/d doc / H, v = the query row for dQr, the key row for dK): each
+    term w (u^ - c v^)/|v| is at most 2|w|/|v| per element, and the fp32 norms,
+    cosine and sums carry relative errors of order 128 * 2^-24 ~ 2^-17 of it.
+    The oracle's decisions (chunk, token) are compared exactly where both the
+    chunk and the token maximum are unique by more than 1e-4 (the scores' fp32
+    error is ~1e-6); documents closer to a tie get a zero upstream gradient in
+    the test input, so both sides skip them.
 P1  pooled V/Kr within 1 bf16 ulp of the oracle's rounded mean, K within 2
     ulps or 2^-20 absolute: K's terms are rotated in fp32 (each rounded), so a
     chunk mean that cancels to a tiny value keeps the accumulation's absolute
@@ -112,3 +121,52 @@ def bf16_ulp_diff(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
         x = x.astype(np.int32)
         return np.where(x & 0x8000, 0x8000 - (x & 0x7FFF), 0x8000 + (x & 0x7FFF))
     return np.abs(ordered(a_bits) - ordered(b_bits))
+
+
+GRAD_REL = 2.0 ** -15
+TIE_GAP = 1e-4
+
+
+def route_grad_bounds(Qr, Kr, dDoc, sel):
+    """P6 scales: (sQ [B, T, H], sK [B, n_docs, H]) from the oracle's selection."""
+    B, T, H, _ = Qr.shape
+    nq = np.linalg.norm(Qr, axis=-1)
+    nk = np.linalg.norm(Kr, axis=-1)
+    sQ = np.zeros((B, T, H))
+    sK = np.zeros(sel.shape[:2] + (H,))
+    for b, d in zip(*np.nonzero(sel[..., 0] >= 0)):
+        g, t = int(sel[b, d, 0]), int(sel[b, d, 1])
+        w = abs(float(dDoc[b, d])) / H
+        sK[b, d] = np.where(nk[g] > 0, 2 * w / np.where(nk[g] > 0, nk[g], 1), 0.0)
+        sQ[b, t] += np.where(nq[b, t] > 0, 2 * w / np.where(nq[b, t] > 0, nq[b, t], 1), 0.0)
+    return sQ, sK
+
+
+def grads_ok(gpu: np.ndarray, ref: np.ndarray, scale: np.ndarray, what: str) -> None:
+    """P6 per element; ``scale`` has the shape of ``gpu`` without its last axis."""
+    err = np.abs(gpu.astype(np.float64) - ref)
+    bad = err > GRAD_REL * scale[..., None]
+    if bad.any():
+        i = np.argwhere(bad)[:5]
+        raise AssertionError(f"{what} off at {i.tolist()}: err {err[bad][:5].tolist()} "
+                             f"bound {(GRAD_REL * np.broadcast_to(scale[..., None], bad.shape))[bad][:5].tolist()}")
+
+
+def route_near_ties(Qr, Kr, off, gap: float = TIE_GAP) -> np.ndarray:
+    """bool [B, n_docs]: the document's chunk or token maximum is unique by less than ``gap``
+    (exact ties, which both sides break towards the lower index, are not flagged)."""
+    B = Qr.shape[0]
+    n_docs = len(off) - 1
+    near = np.zeros((B, n_docs), bool)
+    for b in range(B):
+        for d in range(n_docs):
+            if off[d + 1] == off[d]:
+                continue
+            S = O.head_mean_cosine(Qr[b], Kr[off[d]:off[d + 1]])
+            cm = S.max(axis=0)
+            g = int(np.argmax(cm))
+            for v in (cm, S[:, g]):
+                if len(v) > 1:
+                    top2 = np.sort(v)[-2:]
+                    near[b, d] |= 0.0 < top2[1] - top2[0] < gap
+    return near

@@ -18,7 +18,8 @@ def test_exports_every_declared_symbol():
     assert {"msa_pool_chunks", "msa_route_scores", "msa_topk_docs", "msa_sparse_attn_decode",
             "msa_fetch_docs", "msa_gather_docs", "msa_append_router_rows", "msa_encode_router_keys",
             "msa_encode_workspace_bytes", "msa_store_delete", "msa_store_append",
-            "msa_store_delete_workspace_bytes"} <= set(names)
+            "msa_store_delete_workspace_bytes", "msa_route_scores_backward",
+            "msa_route_backward_workspace_bytes"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     assert set(_lib.SIGNATURES) == set(names)
@@ -116,6 +117,29 @@ def test_store_update_validation():
     assert _code("msa_store_append", *ap(dcap=11)) == E.MSA_ERR_INVALID_ARG           # document capacity
     assert _code("msa_store_append", *ap(nnd=-1)) == E.MSA_ERR_INVALID_ARG
     assert _code("msa_store_append", *ap(new=ctypes.c_void_p((1 << 20) + 100 * 2048))) == E.MSA_ERR_INVALID_ARG
+
+
+def test_route_backward_validation():
+    E = _lib
+    p = ctypes.c_void_p(1 << 20)
+    need = _lib.load().msa_route_backward_workspace_bytes(2, 16, 8, 128, 40)
+    assert need > 2 * 40 * 8 * 4 * 2                  # at least the two per-(query, document, head) weight arrays
+    assert _lib.load().msa_route_backward_workspace_bytes(0, 16, 8, 128, 40) == 0
+    bw = lambda B=2, T=16, H=8, D=128, n_chunks=300, n_docs=40, q=p, cs=p, dd=p, dq=p, dk=p, sel=p, ws=p, wsb=need: (
+        q, B, T, H, D, p, N, n_chunks, p, n_docs, N, cs, dd, dq, dk, sel, ws, wsb, N)
+    assert _code("msa_route_scores_backward", *bw(B=0)) == E.MSA_ERR_INVALID_ARG
+    assert _code("msa_route_scores_backward", *bw(T=0)) == E.MSA_ERR_INVALID_ARG
+    assert _code("msa_route_scores_backward", *bw(n_docs=0)) == E.MSA_ERR_INVALID_ARG
+    assert _code("msa_route_scores_backward", *bw(cs=N)) == E.MSA_ERR_INVALID_ARG         # chunk scores required
+    assert _code("msa_route_scores_backward", *bw(dd=N)) == E.MSA_ERR_INVALID_ARG
+    assert _code("msa_route_scores_backward", *bw(sel=N)) == E.MSA_ERR_INVALID_ARG
+    assert _code("msa_route_scores_backward", *bw(D=64)) == E.MSA_ERR_UNSUPPORTED
+    assert _code("msa_route_scores_backward", *bw(H=3)) == E.MSA_ERR_UNSUPPORTED
+    assert _code("msa_route_scores_backward", *bw(T=8193)) == E.MSA_ERR_UNSUPPORTED
+    assert _code("msa_route_scores_backward", *bw(B=70000)) == E.MSA_ERR_INVALID_ARG
+    assert _code("msa_route_scores_backward", *bw(dq=ctypes.c_void_p((1 << 20) + 4))) == E.MSA_ERR_INVALID_ARG
+    assert _code("msa_route_scores_backward", *bw(wsb=need - 1)) == E.MSA_ERR_WORKSPACE
+    assert _code("msa_route_scores_backward", *bw(ws=N)) == E.MSA_ERR_WORKSPACE
 
 
 def test_append_router_rows_validation():

@@ -15,8 +15,8 @@ from synth import configs as C
 from synth import native
 from synth import splitmix as sm
 
-from tests.parity import (ATT_TOL, SCORE_TOL, bf16_ulp_diff, check_topk, dev_bits, encoded_keys_ok, host_bits,
-                          rel_rows)
+from tests.parity import (ATT_TOL, SCORE_TOL, bf16_ulp_diff, check_topk, dev_bits, encoded_keys_ok, grads_ok,
+                          host_bits, rel_rows, route_grad_bounds, route_near_ties)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -134,6 +134,96 @@ def test_route_deterministic():
 
 
 # ---------------------------------------------------------------------- top-k
+# ---------------------------------------------------------- routing backward
+def _run_route_backward(Qr, Kr, off, dDoc, exclude=None, stored_norms=False, score_off=None):
+    """Forward on the GPU for the chunk scores, then the backward.  score_off: offsets for the
+    forward call when ``off`` has empty documents (chunk scores do not depend on the offsets)."""
+    kr = dev_bits(Kr)
+    nrm = ops.krbar_inv_norms(kr) if stored_norms else None
+    q = dev_bits(Qr)
+    fo = off if score_off is None else score_off
+    _, ch = ops.route_scores(q, kr, torch.from_numpy(fo).to(DEV), want_chunk_scores=True, krbar_inv_norm=nrm)
+    ex = None if exclude is None else torch.from_numpy(exclude.astype(np.uint8)).to(DEV)
+    dQ, dK, sel = ops.route_scores_backward(q, kr, torch.from_numpy(off).to(DEV), ch,
+                                            torch.from_numpy(dDoc.astype(np.float32)).to(DEV), doc_exclude=ex,
+                                            krbar_inv_norm=nrm)
+    torch.cuda.synchronize()
+    return dQ.cpu().numpy(), dK.cpu().numpy(), sel.cpu().numpy()
+
+
+def _check_route_backward(Qr, Kr, off, dDoc, exclude=None, stored_norms=False, score_off=None):
+    q64, k64 = f64(Qr), f64(Kr)
+    dDoc = dDoc.astype(np.float32).copy()
+    dDoc[route_near_ties(q64, k64, off)] = 0.0          # P6: near ties get no gradient on either side
+    dQ, dK, sel = _run_route_backward(Qr, Kr, off, dDoc, exclude, stored_norms, score_off)
+    rQ, rK, rsel = O.route_backward(q64, k64, off, dDoc.astype(np.float64), exclude)
+    assert np.array_equal(sel, rsel), f"selection differs at {np.argwhere(sel != rsel)[:5].tolist()}"
+    sQ, sK = route_grad_bounds(q64, k64, dDoc, rsel)
+    grads_ok(dK, rK, sK, "dK")
+    grads_ok(dQ, rQ, sQ, "dQr")
+    return sel
+
+
+@pytest.mark.parametrize("B,T,H,n_docs", [(1, 1, 8, 50), (1, 7, 8, 337), (2, 40, 4, 1500), (1, 130, 8, 3000),
+                                          (3, 5, 2, 700), (1, 33, 1, 2100), (16, 64, 8, 300), (1, 300, 8, 200),
+                                          (2, 128, 8, 1100)])
+def test_route_backward_matches_oracle(B, T, H, n_docs):
+    announce("route-backward", B, T, H, n_docs)
+    Qr, Kr, off = _route_case(B, T, H, n_docs, seed=300 + B * 1000 + T * 10 + H)
+    dDoc = np.random.default_rng(n_docs).standard_normal((B, n_docs))
+    sel = _check_route_backward(Qr, Kr, off, dDoc, stored_norms=(T > 20))
+    assert (sel[..., 0] >= 0).mean() > 0.9
+
+
+def test_route_backward_special_cases():
+    """Exclusion, zero upstream gradients, zero query / key heads, empty documents, exact
+    duplicate chunks and tokens (first maximiser), and a sparse upstream gradient."""
+    B, T, H = 2, 45, 8
+    r = np.random.default_rng(11)
+    lens = r.integers(1, 7, 260)
+    lens[[3, 100, 259]] = 0                               # empty documents
+    off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    G = int(off[-1])
+    Qr = sm.normal_bf16(11, sm.TID_QR, 0, 0, B * T * H * 128).reshape(B, T, H, 128).copy()
+    Kr = sm.normal_bf16(11, sm.TID_KRBAR, 0, 0, G * H * 128).reshape(G, H, 128).copy()
+    Qr[0, 9, 2] = 0                                       # zero query head
+    Qr[1, :, 6] = 0                                       # a head that is zero for every token of query 1
+    Kr[off[10], 4] = 0                                    # zero key head
+    d = next(i for i in range(260) if lens[i] >= 3)
+    Kr[off[d] + 2] = Kr[off[d]]                           # duplicate chunk inside a document
+    Qr[0, 30] = Qr[0, 12]                                 # duplicate token rows
+    excl = np.zeros((B, 260), bool)
+    excl[0, [1, 7, 50]] = True
+    excl[1, 200:210] = True
+    dDoc = r.standard_normal((B, 260))
+    dDoc[0, 20:40] = 0.0
+    # the forward needs no empty documents: chunk scores depend only on the chunks
+    score_off = np.concatenate([[0], np.cumsum(lens[lens > 0])]).astype(np.int64)
+    announce("route-backward-special")
+    for stored in (False, True):
+        sel = _check_route_backward(Qr, Kr, off, dDoc, excl, stored, score_off)
+        assert np.all(sel[excl] == -1) and np.all(sel[:, [3, 100, 259]] == -1) and np.all(sel[0, 20:40] == -1)
+    # sparse upstream gradient: only each query's 16 best documents (a top-k loss)
+    sparse = np.zeros_like(dDoc)
+    top = np.argsort(-O.route(f64(Qr), f64(Kr), score_off)[1], axis=1)[:, :16]
+    ids = np.flatnonzero(lens > 0)                        # score_off's documents -> off's documents
+    for b in range(B):
+        sparse[b, ids[top[b]]] = r.standard_normal(16)
+    announce("route-backward-sparse")
+    sel = _check_route_backward(Qr, Kr, off, sparse, None, True, score_off)
+    assert (sel[..., 0] >= 0).sum() <= 2 * 16
+
+
+def test_route_backward_deterministic():
+    Qr, Kr, off = _route_case(1, 16, 8, n_docs=5000, seed=21)   # ~300 documents per token: several pieces
+    dDoc = np.random.default_rng(2).standard_normal((1, 5000))
+    announce("route-backward-determinism")
+    a = _run_route_backward(Qr, Kr, off, dDoc, stored_norms=True)
+    b = _run_route_backward(Qr, Kr, off, dDoc, stored_norms=True)
+    for x, y in zip(a, b):
+        assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+
+
 @pytest.mark.parametrize("B,n,k", [(1, 64, 4), (1, 1000, 16), (16, 20000, 16), (1, 200000, 16), (4, 20000, 8),
                                    (1, 7, 7), (3, 5, 1), (2, 4097, 1024), (1, 2049, 2), (2, 100, 100),
                                    (1, 70000, 32), (2, 40000, 17), (3, 33000, 5), (1, 32768, 16), (1, 32769, 3),

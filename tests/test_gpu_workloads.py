@@ -16,7 +16,8 @@ from synth import configs as C
 from synth import native
 from synth import splitmix as sm
 
-from tests.parity import ATT_TOL, GAP, SCORE_TOL, check_topk, dev_bits, encoded_keys_ok, host_bits, rel_rows
+from tests.parity import (ATT_TOL, GAP, GRAD_REL, SCORE_TOL, check_topk, dev_bits, encoded_keys_ok, host_bits,
+                          rel_rows)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -390,3 +391,74 @@ def test_store_delete_100M_layer_sampled():
         na = int(ref_off[ref_ids[d]])
         assert torch.equal(kr_o[na:na + b - a], kr[a:b]), f"doc {d}"
         assert torch.equal(nrm_o[na:na + b - a], nrm[a:b]), f"doc {d}"
+
+
+# ------------------------------------------------ routing backward (100M tokens)
+def _doc_decisions(Qr, Krows):
+    """The oracle's token scores of one document: (S [T, n], chunk gap, token gap) for P6's tie rule."""
+    S = O.head_mean_cosine(Qr, Krows)
+    cm = S.max(axis=0)
+    g = int(np.argmax(cm))
+    gap = lambda v: np.inf if len(v) < 2 else float(np.diff(np.sort(v)[-2:])[0])
+    return S, gap(cm), gap(S[:, g])
+
+
+def test_route_backward_100M_layer_sampled():
+    """The routing-score backward over one 100M-token layer (200,000 documents, every one with an
+    upstream gradient), in the launch configuration the benchmark times.  On sampled documents:
+    the (chunk, token) decision is the oracle's where it is clear by 1e-4 and within 1e-4 of the
+    maximum otherwise, and the key gradient is the oracle's for that decision (P6).  On sampled
+    tokens: every document that selected the token is checked the same way, and dQr is the
+    oracle's sum over exactly those documents."""
+    w = C.config(4)
+    layer = 3
+    announce("route-backward-100M", w.n_docs, w.n_chunks)
+    kr = device_krbar(w, layer)
+    nrm = ops.krbar_inv_norms(kr)
+    q = C.queries(w, layer)
+    off = torch.from_numpy(w.doc_chunk_off).to(DEV)
+    qr = dev_bits(q["Qr"])
+    _, ch = ops.route_scores(qr, kr, off, want_chunk_scores=True, krbar_inv_norm=nrm)
+    dDoc = np.random.default_rng(10).standard_normal((1, w.n_docs)).astype(np.float32)
+    dQ, dK, sel = ops.route_scores_backward(qr, kr, off, ch, torch.from_numpy(dDoc).to(DEV), krbar_inv_norm=nrm)
+    torch.cuda.synchronize()
+    dQ, sel = dQ.cpu().numpy()[0], sel.cpu().numpy()[0]
+    assert np.all(sel[:, 0] >= 0)                            # every document has a gradient and chunks
+    Qr = f32(q["Qr"])[0].astype(np.float64)
+
+    def check_doc(d):
+        g0, g1 = int(w.doc_chunk_off[d]), int(w.doc_chunk_off[d + 1])
+        K = f32(C.krbar_block(w, layer, g0, g1)).astype(np.float64)
+        S, cgap, tgap = _doc_decisions(Qr, K)
+        g, t = int(sel[d, 0]) - g0, int(sel[d, 1])
+        assert 0 <= g < g1 - g0 and 0 <= t < w.T, f"doc {d}: selection {sel[d]} outside the document"
+        if cgap >= 1e-4 and tgap >= 1e-4:
+            gr = int(np.argmax(S.max(axis=0)))
+            assert (g, t) == (gr, int(np.argmax(S[:, gr]))), f"doc {d}"
+        else:
+            assert S.max() - S[t, g] <= 1e-4 and S[:, g].max() - S[t, g] <= 1e-4, f"doc {d}"
+        return K[g]
+
+    def pair_grads(docs, t):
+        """The oracle's gradients of the pairs (token t, each document's selected chunk)."""
+        K = np.stack([check_doc(int(d)) for d in docs])
+        one = np.arange(len(docs) + 1, dtype=np.int64)
+        return O.route_backward(Qr[None, t:t + 1], K, one, dDoc[:, docs].astype(np.float64))
+
+    r = np.random.default_rng(4)
+    docs = sample_docs(w, [d for _, d in C.planted_docs(w, layer)], n=300, seed=4)
+    for d in docs:
+        t = int(sel[d, 1])
+        _, rK, _ = pair_grads(np.array([d]), t)
+        gpu = dK[0, d].cpu().numpy()
+        k64 = np.linalg.norm(f32(C.krbar_block(w, layer, int(sel[d, 0]), int(sel[d, 0]) + 1))[0], axis=-1)
+        bound = np.where(k64 > 0, 2 * abs(float(dDoc[0, d])) / w.H / np.where(k64 > 0, k64, 1), 0.0)
+        assert np.all(np.abs(gpu - rK[0, 0]) <= GRAD_REL * bound[:, None]), f"dK of doc {d}"
+    counts = np.bincount(sel[:, 1], minlength=w.T)
+    for t in [int(np.argmax(counts)), int(r.integers(w.T))]:
+        Dt = np.flatnonzero(sel[:, 1] == t)
+        announce("route-backward-100M token", t, len(Dt))
+        rQ, _, _ = pair_grads(Dt, t)
+        nq = np.linalg.norm(Qr[t], axis=-1)
+        bound = 2 * np.abs(dDoc[0, Dt]).astype(np.float64).sum() / w.H / nq
+        assert np.all(np.abs(dQ[t] - rQ[0, 0]) <= GRAD_REL * bound[:, None]), f"dQr of token {t}"
