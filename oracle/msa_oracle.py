@@ -360,6 +360,57 @@ def attend(Q, Kloc, Vloc, Kmem, Vmem, rope_offset: int, base: float, scale: floa
     return (O, P_all) if return_probs else O
 
 
+def attend_backward(Q, Kloc, Vloc, Kmem, Vmem, rope_offset: int, base: float, scale: float, dO):
+    """Gradients of ``attend`` with respect to all five of its tensor inputs, given dL/dO.
+
+    [abstract]: MSA is trained end to end, so the loss reaches the query, the
+    local keys and values and the selected documents' pooled keys and values
+    through this attention.  Per q-head, with S = scale * Qrot Krot^T (masked),
+    P = softmax_rows(S) and O = P V:
+        dV = P^T dO,   dP = dO V^T,   dS = P * (dP - rowsum(P * dP)),
+        dQrot = scale * dS K,   dK = scale * dS^T Qrot.
+    The rotation at position p is orthogonal, so the gradient of an unrotated
+    input is its gradient rotated by -p.  Memory keys are used as given
+    (already rotated), so their gradient is taken as is.  A kv-head collects
+    the gradients of every q-head that reads it.
+    Returns (dQ [Tq, Hq, D], dKloc, dVloc [Tl, Hkv, D], dKmem, dVmem [M, Hkv, D]).
+    """
+    Q = np.asarray(Q, dtype=np.float64)
+    Kloc = np.asarray(Kloc, dtype=np.float64)
+    Vloc = np.asarray(Vloc, dtype=np.float64)
+    Kmem = np.asarray(Kmem, dtype=np.float64).reshape(-1, Kloc.shape[1], Kloc.shape[2])
+    Vmem = np.asarray(Vmem, dtype=np.float64).reshape(-1, Kloc.shape[1], Kloc.shape[2])
+    dO = np.asarray(dO, dtype=np.float64)
+    Tq, Hq, D = Q.shape
+    Tl, Hkv, _ = Kloc.shape
+    M = Kmem.shape[0]
+    group = Hq // Hkv
+    qpos = rope_offset + (Tl - Tq) + np.arange(Tq)
+    kpos = rope_offset + np.arange(Tl)
+    Qrot = rope(Q, qpos[:, None], base)
+    Krot = rope(Kloc, kpos[:, None], base)
+    visible = np.ones((Tq, M + Tl), dtype=bool)
+    visible[:, M:] = np.arange(Tl)[None, :] <= ((Tl - Tq) + np.arange(Tq))[:, None]
+    dQrot = np.zeros_like(Qrot)
+    dK = np.zeros((M + Tl, Hkv, D))           # gradient of the keys as used (memory ++ rotated local)
+    dV = np.zeros((M + Tl, Hkv, D))
+    for h in range(Hq):
+        g = h // group
+        keys = np.concatenate([Kmem[:, g], Krot[:, g]], axis=0)
+        vals = np.concatenate([Vmem[:, g], Vloc[:, g]], axis=0)
+        logits = np.where(visible, (Qrot[:, h] @ keys.T) * scale, -np.inf)
+        e = np.exp(logits - logits.max(axis=1, keepdims=True))
+        P = e / e.sum(axis=1, keepdims=True)
+        dP = dO[:, h] @ vals.T
+        dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+        dV[:, g] += P.T @ dO[:, h]
+        dK[:, g] += scale * (dS.T @ Qrot[:, h])
+        dQrot[:, h] = scale * (dS @ keys)
+    dQ = rope(dQrot, -qpos[:, None], base)
+    dKloc = rope(dK[M:], -kpos[:, None], base)
+    return dQ, dKloc, dV[M:], dK[:M], dV[:M]
+
+
 # --------------------------------------------------------------- interleave
 def interleave(Qr, Krbar, Kbar, Vbar, doc_chunk_off, k: int, rounds: int,
                Q, Kloc, Vloc, base: float, scale: float, exclude0=None) -> List[Dict]:

@@ -474,3 +474,101 @@ def test_attend_gqa_mapping():
     Vl2[:, 1] = 0; Vm2[:, 1] = 0
     o = O.attend(Q, Kl, Vl2, Km, Vm2, 2, BASE, 0.25)
     assert np.all(o[:, 4:] == 0) and np.all(np.abs(o[:, :4]).max(axis=-1) > 0)
+
+
+# ------------------------------------------------------ attention backward
+def _attend_loss(G, *args):
+    Q, Kl, Vl, Km, Vm, off, base, scale = args
+    return float((O.attend(Q, Kl, Vl, Km, Vm, off, base, scale) * G).sum())
+
+
+def test_attend_backward_finite_differences():
+    # L = sum(G * O); central differences of the oracle's own forward, every element of every input
+    Q, Kl, Vl, Km, Vm = _att_case(70, Tq=3, Tl=5, M=4, Hq=4, Hkv=2, D=8)
+    G = rng(71).standard_normal(Q.shape)
+    args = [Q, Kl, Vl, Km, Vm]
+    grads = O.attend_backward(Q, Kl, Vl, Km, Vm, 3, 50.0, 0.4, G)
+    order = [0, 1, 2, 3, 4]                       # attend_backward returns dQ, dKloc, dVloc, dKmem, dVmem
+    eps = 1e-6
+    for which, gidx in zip(range(5), order):
+        x = args[which]
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            a = [y.copy() for y in args]; a[which][idx] += eps
+            c = [y.copy() for y in args]; c[which][idx] -= eps
+            num[idx] = (_attend_loss(G, *a, 3, 50.0, 0.4) - _attend_loss(G, *c, 3, 50.0, 0.4)) / (2 * eps)
+        np.testing.assert_allclose(grads[gidx], num, atol=2e-8, err_msg=f"input {which}")
+
+
+def test_attend_backward_torch_autograd():
+    # an independent forward in torch (textbook masked softmax attention with explicit rotation
+    # matrices and repeated kv heads), differentiated by autograd
+    Tq, Tl, M, Hq, Hkv, D, off, base, scale = 4, 6, 5, 8, 2, 16, 9, 1e4, 0.3
+    Q, Kl, Vl, Km, Vm = _att_case(72, Tq=Tq, Tl=Tl, M=M, Hq=Hq, Hkv=Hkv, D=D)
+    G = rng(73).standard_normal(Q.shape)
+    t = [torch.tensor(a, requires_grad=True) for a in (Q, Kl, Vl, Km, Vm)]
+
+    def rot_matrix(p):
+        R = torch.zeros(D, D, dtype=torch.float64)
+        for i in range(D // 2):
+            a = p * base ** (-2.0 * i / D)
+            R[i, i], R[i, i + D // 2] = np.cos(a), -np.sin(a)
+            R[i + D // 2, i], R[i + D // 2, i + D // 2] = np.sin(a), np.cos(a)
+        return R
+
+    qr = torch.stack([t[0][i] @ rot_matrix(off + Tl - Tq + i).T for i in range(Tq)])
+    kr = torch.stack([t[1][j] @ rot_matrix(off + j).T for j in range(Tl)])
+    keys = torch.cat([t[3], kr]).repeat_interleave(Hq // Hkv, dim=1)            # [M+Tl, Hq, D]
+    vals = torch.cat([t[4], t[2]]).repeat_interleave(Hq // Hkv, dim=1)
+    logits = torch.einsum("ihd,jhd->hij", qr, keys) * scale
+    mask = torch.ones(Tq, M + Tl, dtype=torch.bool)
+    mask[:, M:] = torch.arange(Tl)[None, :] <= (Tl - Tq + torch.arange(Tq))[:, None]
+    P = torch.softmax(logits.masked_fill(~mask, float("-inf")), dim=-1)
+    out = torch.einsum("hij,jhd->ihd", P, vals)
+    (out * torch.tensor(G)).sum().backward()
+    grads = O.attend_backward(Q, Kl, Vl, Km, Vm, off, base, scale, G)
+    for g, ref in zip(grads, (t[0], t[1], t[2], t[3], t[4])):
+        np.testing.assert_allclose(g, ref.grad.numpy(), atol=1e-11)
+
+
+def test_attend_backward_closed_forms():
+    # one visible key: P = 1, so dV = dO, and dS = P (dP - dP) = 0 gives zero dQ and dK
+    Q, Kl, Vl, Km, Vm = _att_case(74, Tq=1, Tl=1, M=0, Hq=2, Hkv=1, D=8)
+    G = rng(75).standard_normal(Q.shape)
+    dQ, dKl, dVl, dKm, dVm = O.attend_backward(Q, Kl, Vl, Km, Vm, 2, BASE, 0.5, G)
+    np.testing.assert_allclose(dVl[0, 0], G[0].sum(axis=0), atol=1e-14)
+    assert np.abs(dQ).max() < 1e-14 and np.abs(dKl).max() < 1e-14 and dKm.shape == (0, 1, 8)
+    # Q = 0: uniform weights over the n visible keys, so dV_j = sum of dO over the rows that see j, / n;
+    # dK = scale dS^T Q = 0; dQrot_i = scale * sum_j (1/n)(dP_ij - mean_j dP_ij) k_j
+    Q, Kl, Vl, Km, Vm = _att_case(76, Tq=2, Tl=3, M=2, Hq=1, Hkv=1, D=8)
+    Q = np.zeros_like(Q)
+    G = rng(77).standard_normal(Q.shape)
+    dQ, dKl, dVl, dKm, dVm = O.attend_backward(Q, Kl, Vl, Km, Vm, 0, BASE, 0.5, G)
+    assert np.abs(dKl).max() < 1e-14 and np.abs(dKm).max() < 1e-14
+    # row 0 sees memory 0, 1 and local 0, 1 (n = 4); row 1 sees all five (n = 5)
+    np.testing.assert_allclose(dVm[0, 0], G[0, 0] / 4 + G[1, 0] / 5, atol=1e-14)
+    np.testing.assert_allclose(dVl[2, 0], G[1, 0] / 5, atol=1e-14)
+    # with Q = 0 the rotation of Q is irrelevant; the gradient of row 1 before un-rotation:
+    keys = np.concatenate([Km[:, 0], O.rope(Kl[:, 0], np.arange(3), BASE)])
+    vals = np.concatenate([Vm[:, 0], Vl[:, 0]])
+    dP = vals @ G[1, 0]
+    want = 0.5 * ((dP - dP.mean()) / 5) @ keys
+    np.testing.assert_allclose(O.rope(dQ[1:2, 0], np.array([2]), BASE)[0], want, atol=1e-13)
+
+
+def test_attend_backward_gqa_and_memory_permutation():
+    Q, Kl, Vl, Km, Vm = _att_case(78, Tq=3, Tl=4, M=6, Hq=8, Hkv=2, D=16)
+    G = rng(79).standard_normal(Q.shape)
+    # a kv head collects only its own q-heads: zero the gradient of q-heads 4..7 -> kv head 1 gets nothing
+    G2 = G.copy(); G2[:, 4:] = 0
+    _, dKl, dVl, dKm, dVm = O.attend_backward(Q, Kl, Vl, Km, Vm, 1, BASE, 0.25, G2)
+    for x in (dKl, dVl, dKm, dVm):
+        assert np.all(x[:, 1] == 0) and np.abs(x[:, 0]).max() > 0
+    # permuting the memory entries permutes their gradients and changes nothing else
+    p = rng(80).permutation(6)
+    a = O.attend_backward(Q, Kl, Vl, Km, Vm, 1, BASE, 0.25, G)
+    b = O.attend_backward(Q, Kl, Vl, Km[p], Vm[p], 1, BASE, 0.25, G)
+    for x, y in zip(a[:3], b[:3]):
+        np.testing.assert_allclose(x, y, atol=1e-12)
+    np.testing.assert_allclose(a[3][p], b[3], atol=1e-12)
+    np.testing.assert_allclose(a[4][p], b[4], atol=1e-12)
