@@ -336,6 +336,21 @@ def main():
                                                                   Mmax, ml_dev, k, w.rope_base), 50)
     attn_us = 1e3 * time_ms(lambda: ops.sparse_attn_decode(Q[0], Kl[0], Vl[0], staging, staging[:, :, 1], 2 * H * D,
                                                            Mmax, ml_dev, k, w.rope_base, out=O_out), 50)
+    # attention backward at the step's shape (Tq = Tl = 128, 32 q-heads over 8 kv-heads, the assembled memory)
+    d_out = torch.from_numpy(np.random.default_rng(11).standard_normal((1, w.Tq, w.Hq, D)).astype(np.float32)).to(dev)
+    ab_out = (torch.empty((1, w.Tq, w.Hq, D), dtype=torch.float32, device=dev),
+              torch.empty((1, w.Tl, H, D), dtype=torch.float32, device=dev),
+              torch.empty((1, w.Tl, H, D), dtype=torch.float32, device=dev),
+              torch.empty((1, Mmax, H, D), dtype=torch.float32, device=dev),
+              torch.empty((1, Mmax, H, D), dtype=torch.float32, device=dev))
+    ws_ab = ops.workspace(ops.attn_backward_workspace_bytes(1, w.Tq, w.Hq, D, w.Tl, H, Mmax), dev, "bench-attn-bwd")
+    attn_bwd_us = 1e3 * time_ms(lambda: ops.sparse_attn_backward(Q[0], Kl[0], Vl[0], staging, staging[:, :, 1],
+                                                                 2 * H * D, Mmax, ml_dev, k, d_out, w.rope_base,
+                                                                 out=ab_out, ws=ws_ab), 50)
+    n_mem = int(ml_dev.item())
+    n_vis = w.Tq * n_mem + sum(w.Tl - w.Tq + i + 1 for i in range(w.Tq))      # visible (row, key) pairs per head
+    attn_bwd_flops = 5 * 2.0 * n_vis * D * w.Hq                                  # S, dP, dV, dK, dQ
+    del ab_out
     topk_us = 1e3 * time_ms(lambda: ops.topk_docs(doc, k, top_idx=idx_d, top_scores=sc_d, ws=ws_k), 50)
     gather_us = 1e3 * time_ms(lambda: ops.gather_docs(idx_d, store, off_dev, staging, Mmax, mem_len=ml_dev), 50)
     route_nonorm_ms = time_ms(lambda: ops.route_scores(qr[0], krbar[0], off_dev, doc_scores=doc, ws=ws_r), 10)
@@ -511,6 +526,8 @@ def main():
         "topk_us": topk_us,
         "gather_us": gather_us,
         "attn_us": {"tq128": attn_us, "tq1_decode": decode_attn_us},
+        "attn_backward_tq128": {"us": attn_bwd_us, "memory_entries": n_mem,
+                                "TFLOPs": attn_bwd_flops / (attn_bwd_us * 1e-6) / 1e12},
         "scan_10M_batch16": {"ms": scan3_ms, "TFLOPs": scan3_tflops,
                              "mfma_frac": scan3_tflops / MFMA_BF16_PEAK_TFLOPS,
                              "gemm_bf16_8192_TFLOPs": gemm_tflops,

@@ -18,6 +18,7 @@
  *   msa_gather_docs         online: same, as one device kernel reading mapped host memory
  *   msa_append_router_rows  interleave: the next round's router rows and exclusions
  *   msa_sparse_attn_decode  generation: GQA attention over [memory ++ local KV]
+ *   msa_sparse_attn_backward   training: gradient of that attention (Q, local K/V, memory K/V)
  *
  * Conventions (every call):
  *   - Tensors are row-major with the last dimension contiguous.  bf16 tensors
@@ -370,6 +371,43 @@ int msa_sparse_attn_decode(const uint16_t* Q, int B, int Tq, int Hq, int D,
                            int64_t mem_entry_stride, int Mmax, const int32_t* mem_len,
                            int rope_offset, double rope_base, float scale,
                            float* O, hipStream_t stream);
+
+/*
+ * msa_sparse_attn_backward -- gradient of msa_sparse_attn_decode.
+ *
+ * Defined by: chatpaper.ai Abstract (MSA is trained end to end, so the loss
+ * reaches the query, the local context and the retrieved memory through this
+ * attention), applied to the forward of msa_sparse_attn_decode (medium
+ * write-up sec. 2, b-lab.team sec. 1 and its Global RoPE bullet).  Per q-head,
+ * with S = scale * Qrot Krot^T over the visible keys, P = softmax_rows(S):
+ *   dV = P^T dO,  dS = P * (dO V^T - rowsum(P * dO V^T)),
+ *   dQrot = scale * dS K,  dK = scale * dS^T Qrot;
+ * a kv-head collects the gradients of the q-heads that read it, and the
+ * gradients of Q and Kloc (rotated inside the forward) are rotated back.
+ * Memory keys are used as given (already rotated by msa_pool_chunks), so dKmem
+ * is the gradient of the given entries.
+ *
+ *   Q, Kloc, Vloc, Kmem, Vmem, mem_entry_stride, Mmax, mem_len, rope_offset,
+ *   rope_base, scale: as given to msa_sparse_attn_decode
+ *   dO          fp32 [B, Tq, Hq, D]
+ *   dQ          fp32 [B, Tq, Hq, D] out
+ *   dKloc, dVloc fp32 [B, Tl, Hkv, D] out
+ *   dKmem, dVmem fp32 [B, Mmax, Hkv, D] out (dense; entries >= mem_len[b] are set to 0);
+ *               may be NULL when Mmax == 0
+ *   workspace   >= msa_sparse_attn_backward_workspace_bytes(B, Tq, Hq, D, Tl, Hkv, Mmax) bytes
+ *   D == 128, 1 <= Tq <= Tl, Hq % Hkv == 0, Hkv <= 16, rope_offset >= 0.
+ * Products use bf16 hi + lo splits of every fp32 operand with fp32 accumulation;
+ * results are deterministic (no atomics).
+ */
+size_t msa_sparse_attn_backward_workspace_bytes(int B, int Tq, int Hq, int D, int Tl, int Hkv, int Mmax);
+int msa_sparse_attn_backward(const uint16_t* Q, int B, int Tq, int Hq, int D,
+                             const uint16_t* Kloc, const uint16_t* Vloc, int Tl, int Hkv,
+                             const uint16_t* Kmem, const uint16_t* Vmem,
+                             int64_t mem_entry_stride, int Mmax, const int32_t* mem_len,
+                             int rope_offset, double rope_base, float scale,
+                             const float* dO, float* dQ, float* dKloc, float* dVloc,
+                             float* dKmem, float* dVmem,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -45,6 +45,9 @@ SIGNATURES = {
                                c_p, c_sz, c_p]),
     "msa_krbar_inv_norms": (c_i, [c_p, c_i64, c_i, c_i, c_p, c_p]),
     "msa_route_backward_workspace_bytes": (c_sz, [c_i, c_i, c_i, c_i, c_i64]),
+    "msa_sparse_attn_backward_workspace_bytes": (c_sz, [c_i, c_i, c_i, c_i, c_i, c_i, c_i]),
+    "msa_sparse_attn_backward": (c_i, [c_p, c_i, c_i, c_i, c_i, c_p, c_p, c_i, c_i, c_p, c_p, c_i64, c_i, c_p,
+                                       c_i, c_d, c_f, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_sz, c_p]),
     "msa_route_scores_backward": (c_i, [c_p, c_i, c_i, c_i, c_i, c_p, c_p, c_i64, c_p, c_i64, c_p, c_p, c_p,
                                         c_p, c_p, c_p, c_p, c_sz, c_p]),
     "msa_topk_workspace_bytes": (c_sz, [c_i, c_i64, c_i]),

@@ -334,4 +334,39 @@ int msa_sparse_attn_decode(const uint16_t* Q, int B, int Tq, int Hq, int D, cons
                           rope_offset, rope_base, scale, O, stream);
 }
 
+size_t msa_sparse_attn_backward_workspace_bytes(int B, int Tq, int Hq, int D, int Tl, int Hkv, int Mmax) {
+  (void)D;
+  if (B < 1 || Tq < 1 || Tl < Tq || Hq < 1 || Hkv < 1 || Mmax < 0) return 0;
+  return msa::attn_bwd_workspace(B, Tq, Hq, Tl, Hkv, Mmax);
+}
+
+int msa_sparse_attn_backward(const uint16_t* Q, int B, int Tq, int Hq, int D, const uint16_t* Kloc,
+                             const uint16_t* Vloc, int Tl, int Hkv, const uint16_t* Kmem, const uint16_t* Vmem,
+                             int64_t mem_entry_stride, int Mmax, const int32_t* mem_len, int rope_offset,
+                             double rope_base, float scale, const float* dO, float* dQ, float* dKloc, float* dVloc,
+                             float* dKmem, float* dVmem, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  msa::clear_error();
+  MSA_CHECK_ARG(B >= 1 && B <= 65535 && Tq >= 1 && Tl >= Tq, "need B >= 1, 1 <= Tq <= Tl");
+  MSA_CHECK_ARG(Hkv >= 1 && Hq >= Hkv && Hq % Hkv == 0 && Hq <= 65535, "need Hq %% Hkv == 0");
+  MSA_CHECK_SUPPORTED(D == 128, "D=%d unsupported (D must be 128)", D);
+  MSA_CHECK_SUPPORTED(Hkv <= 16, "Hkv=%d unsupported (<= 16)", Hkv);
+  MSA_CHECK_ARG(Mmax >= 0 && rope_offset >= 0 && rope_base > 1.0, "need Mmax >= 0, rope_offset >= 0, base > 1");
+  MSA_CHECK_ARG((int64_t)Mmax + Tl < (1 << 24) && Tq < (1 << 24), "sizes out of range");
+  MSA_CHECK_ARG(Q && Kloc && Vloc && mem_len && dO && dQ && dKloc && dVloc, "null pointer");
+  MSA_CHECK_ARG(Mmax == 0 || (Kmem && Vmem && dKmem && dVmem && mem_entry_stride >= (int64_t)Hkv * D),
+                "memory pointers/stride invalid");
+  MSA_CHECK_ARG(aligned16(Q) && aligned16(Kloc) && aligned16(Vloc) && aligned16(dO) && aligned16(dQ) &&
+                    aligned16(dKloc) && aligned16(dVloc),
+                "pointers must be 16-byte aligned");
+  const size_t need = msa::attn_bwd_workspace(B, Tq, Hq, Tl, Hkv, Mmax);
+  if (workspace_bytes < need || workspace == nullptr) {
+    msa::set_error("workspace %zu bytes < required %zu", workspace_bytes, need);
+    return MSA_ERR_WORKSPACE;
+  }
+  MSA_CHECK_ARG(aligned16(workspace), "workspace must be 16-byte aligned");
+  return msa::launch_attn_bwd(Q, B, Tq, Hq, Kloc, Vloc, Tl, Hkv, Kmem, Vmem, mem_entry_stride, Mmax, mem_len,
+                              rope_offset, rope_base, scale, dO, dQ, dKloc, dVloc, dKmem, dVmem, workspace, stream);
+}
+
 }  // extern "C"

@@ -43,12 +43,7 @@ struct bf16pair {
 
 __device__ __forceinline__ uint32_t pack2(uint32_t a, uint32_t b) { return a | (b << 16); }
 
-// x -> (bf16 hi, bf16 lo) with hi = RNE(x), lo = RNE(x - hi); 8 values.  The
-// conversions are gfx950's packed fp32 -> bf16 instruction (round to nearest even).
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t cvt2_bf16(float a, float b) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
-}
+// x -> (bf16 hi, bf16 lo) with hi = RNE(x), lo = RNE(x - hi); 8 values.
 __device__ __forceinline__ bf16pair split8(const float (&x)[8]) {
   uint32_t h[4], l[4];
 #pragma unroll
@@ -65,14 +60,6 @@ __device__ __forceinline__ bf16pair split8(const float (&x)[8]) {
 __device__ __forceinline__ void unpack8(uint4 v, float (&x)[8]) {
   x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x); x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
   x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z); x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
-}
-
-// cos/sin of pos * theta_i, theta_i = base^(-2i/D); rev_i = theta_i / (2 pi) in fp64.
-// The angle in revolutions is reduced to [-1/2, 1/2] in fp64, then evaluated in fp32.
-__device__ __forceinline__ void rope_cs(int pos, double rev_i, float* c, float* s) {
-  double r = (double)pos * rev_i;
-  r -= rint(r);
-  sincospif(2.0f * (float)r, s, c);
 }
 
 // Rotate the pairs (i, i + 64) held by one lane: lo[j] = dims 16 ks + 8 hf + j

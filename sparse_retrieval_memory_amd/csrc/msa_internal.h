@@ -66,6 +66,22 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return u >> 16;
 }
 
+// two fp32 -> packed bf16 pair (a in the low half), gfx950's packed conversion
+// instruction (round to nearest even)
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt2_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+}
+
+// RoPE: cos/sin of pos * theta_i, theta_i = base^(-2i/D), given rev_i = theta_i / (2 pi)
+// in fp64.  The angle in revolutions is reduced to [-1/2, 1/2] in fp64, then
+// evaluated in fp32.
+__device__ __forceinline__ void rope_cs(int pos, double rev_i, float* c, float* s) {
+  double r = (double)pos * rev_i;
+  r -= rint(r);
+  sincospif(2.0f * (float)r, s, c);
+}
+
 // Order-preserving map float -> uint32 (a < b  <=>  enc(a) < enc(b) for non-NaN).
 __device__ __forceinline__ uint32_t enc_f32(float f) {
   uint32_t u = __float_as_uint(f);
@@ -144,6 +160,12 @@ int launch_attn(const uint16_t* Q, int B, int Tq, int Hq, const uint16_t* Kloc, 
                 int Tl, int Hkv, const uint16_t* Kmem, const uint16_t* Vmem, int64_t mem_entry_stride,
                 int Mmax, const int32_t* mem_len, int rope_offset, double rope_base, float scale,
                 float* O, hipStream_t stream);
+int launch_attn_bwd(const uint16_t* Q, int B, int Tq, int Hq, const uint16_t* Kloc, const uint16_t* Vloc, int Tl,
+                    int Hkv, const uint16_t* Kmem, const uint16_t* Vmem, int64_t mem_entry_stride, int Mmax,
+                    const int32_t* mem_len, int rope_offset, double rope_base, float scale, const float* dO,
+                    float* dQ, float* dKloc, float* dVloc, float* dKmem, float* dVmem, void* workspace,
+                    hipStream_t stream);
+size_t attn_bwd_workspace(int B, int Tq, int Hq, int Tl, int Hkv, int Mmax);
 int launch_append_rows(const uint16_t* Qr, int B, int T0, int H, const uint16_t* Krbar,
                        const int64_t* doc_chunk_off, int64_t n_docs, const int32_t* ids, int n_ids, int T_out,
                        uint16_t* rows, int32_t* n_rows, uint8_t* doc_exclude, hipStream_t stream);

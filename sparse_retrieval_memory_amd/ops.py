@@ -293,3 +293,35 @@ def sparse_attn_decode(Q, Kloc, Vloc, Kmem, Vmem, mem_entry_stride: int, Mmax: i
               ctypes.c_void_p(vp), mem_entry_stride, Mmax, _p(mem_len), rope_offset, float(rope_base),
               float(scale), _p(out), _stream(stream))
     return out
+
+
+def attn_backward_workspace_bytes(B, Tq, Hq, D, Tl, Hkv, Mmax) -> int:
+    return int(_lib.load().msa_sparse_attn_backward_workspace_bytes(B, Tq, Hq, D, Tl, Hkv, Mmax))
+
+
+def sparse_attn_backward(Q, Kloc, Vloc, Kmem, Vmem, mem_entry_stride: int, Mmax: int, mem_len, rope_offset: int,
+                         dO, rope_base: float = 1.0e6, scale: Optional[float] = None, out=None, ws=None,
+                         stream=None):
+    """msa_sparse_attn_backward: (dQ [B, Tq, Hq, D], dKloc, dVloc [B, Tl, Hkv, D], dKmem, dVmem [B, Mmax, Hkv, D]),
+    all fp32."""
+    _bf16(Q, "Q"); _bf16(Kloc, "Kloc"); _bf16(Vloc, "Vloc")
+    B, Tq, Hq, D = Q.shape
+    _, Tl, Hkv, _ = Kloc.shape
+    assert dO.dtype == torch.float32 and dO.shape == (B, Tq, Hq, D) and dO.is_contiguous()
+    if scale is None:
+        scale = D ** -0.5
+    dev = Q.device
+    if out is None:
+        f = lambda *s: torch.empty(s, dtype=torch.float32, device=dev)
+        out = (f(B, Tq, Hq, D), f(B, Tl, Hkv, D), f(B, Tl, Hkv, D), f(B, max(Mmax, 1), Hkv, D),
+               f(B, max(Mmax, 1), Hkv, D))
+    need = attn_backward_workspace_bytes(B, Tq, Hq, D, Tl, Hkv, Mmax)
+    if ws is None:
+        ws = workspace(need, dev, "attn_bwd")
+    kp = Kmem.data_ptr() if Kmem is not None else 0
+    vp = Vmem.data_ptr() if Vmem is not None else 0
+    _lib.call("msa_sparse_attn_backward", _p(Q), B, Tq, Hq, D, _p(Kloc), _p(Vloc), Tl, Hkv, ctypes.c_void_p(kp),
+              ctypes.c_void_p(vp), mem_entry_stride, Mmax, _p(mem_len), rope_offset, float(rope_base), float(scale),
+              _p(dO), _p(out[0]), _p(out[1]), _p(out[2]), _p(out[3]), _p(out[4]), _p(ws), ws.numel(),
+              _stream(stream))
+    return out

@@ -19,6 +19,10 @@ P6  routing-score gradients: per element |gpu - oracle| <= 2^-15 * s, where s
     chunk and the token maximum are unique by more than 1e-4 (the scores' fp32
     error is ~1e-6); documents closer to a tie get a zero upstream gradient in
     the test input, so both sides skip them.
+P7  attention gradients (dQ, dK/dV of the local and the memory entries): per row
+    ||g - g*|| / ||g*|| <= 2e-2, the attention budget of P4; the split-bf16
+    operands keep the observed error near 1e-5, and the tests also hold it
+    under 1e-3.
 P1  pooled V/Kr within 1 bf16 ulp of the oracle's rounded mean, K within 2
     ulps or 2^-20 absolute: K's terms are rotated in fp32 (each rounded), so a
     chunk mean that cancels to a tiny value keeps the accumulation's absolute
@@ -37,6 +41,9 @@ from oracle import msa_oracle as O
 SCORE_TOL = 1e-5
 GAP = 1e-3
 ATT_TOL = 2e-2
+# attention gradients: the budget is ATT_TOL per row (P7); the split-bf16 products keep the
+# observed error far inside it, and this second bound holds the kernels to that
+ATT_GRAD_OBS = 1e-3
 
 
 def dev_bits(a, device="cuda:0") -> torch.Tensor:

@@ -19,7 +19,8 @@ def test_exports_every_declared_symbol():
             "msa_fetch_docs", "msa_gather_docs", "msa_append_router_rows", "msa_encode_router_keys",
             "msa_encode_workspace_bytes", "msa_store_delete", "msa_store_append",
             "msa_store_delete_workspace_bytes", "msa_route_scores_backward",
-            "msa_route_backward_workspace_bytes"} <= set(names)
+            "msa_route_backward_workspace_bytes", "msa_sparse_attn_backward",
+            "msa_sparse_attn_backward_workspace_bytes"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     assert set(_lib.SIGNATURES) == set(names)
@@ -140,6 +141,26 @@ def test_route_backward_validation():
     assert _code("msa_route_scores_backward", *bw(dq=ctypes.c_void_p((1 << 20) + 4))) == E.MSA_ERR_INVALID_ARG
     assert _code("msa_route_scores_backward", *bw(wsb=need - 1)) == E.MSA_ERR_WORKSPACE
     assert _code("msa_route_scores_backward", *bw(ws=N)) == E.MSA_ERR_WORKSPACE
+
+
+def test_attention_backward_validation():
+    E = _lib
+    p = ctypes.c_void_p(1 << 20)
+    need = _lib.load().msa_sparse_attn_backward_workspace_bytes(1, 100, 32, 128, 130, 8, 45)
+    # split Q and dO, row-major and transposed (8 arrays of [Hq, 128 padded rows, D] bf16)
+    assert need >= 8 * 32 * 128 * 128 * 2
+    assert _lib.load().msa_sparse_attn_backward_workspace_bytes(1, 100, 32, 128, 99, 8, 45) == 0   # Tl < Tq
+    bw = lambda B=1, Tq=100, Hq=32, D=128, Tl=130, Hkv=8, Mmax=45, km=p, dO=p, dq=p, dkm=p, ws=p, wsb=need: (
+        p, B, Tq, Hq, D, p, p, Tl, Hkv, km, p, 2 * Hkv * 128, Mmax, p, 7, 1e6, 0.088, dO, dq, p, p, dkm, p, ws, wsb, N)
+    assert _code("msa_sparse_attn_backward", *bw(Tl=99)) == E.MSA_ERR_INVALID_ARG          # Tl < Tq
+    assert _code("msa_sparse_attn_backward", *bw(Hq=30)) == E.MSA_ERR_INVALID_ARG          # Hq % Hkv
+    assert _code("msa_sparse_attn_backward", *bw(D=64)) == E.MSA_ERR_UNSUPPORTED
+    assert _code("msa_sparse_attn_backward", *bw(Hkv=32, Hq=32)) == E.MSA_ERR_UNSUPPORTED
+    assert _code("msa_sparse_attn_backward", *bw(dO=N)) == E.MSA_ERR_INVALID_ARG
+    assert _code("msa_sparse_attn_backward", *bw(dkm=N)) == E.MSA_ERR_INVALID_ARG          # memory gradient missing
+    assert _code("msa_sparse_attn_backward", *bw(dq=ctypes.c_void_p((1 << 20) + 8))) == E.MSA_ERR_INVALID_ARG
+    assert _code("msa_sparse_attn_backward", *bw(wsb=need - 1)) == E.MSA_ERR_WORKSPACE
+    assert _code("msa_sparse_attn_backward", *bw(ws=N)) == E.MSA_ERR_WORKSPACE
 
 
 def test_append_router_rows_validation():

@@ -15,7 +15,7 @@ from synth import configs as C
 from synth import native
 from synth import splitmix as sm
 
-from tests.parity import (ATT_TOL, SCORE_TOL, bf16_ulp_diff, check_topk, dev_bits, encoded_keys_ok, grads_ok,
+from tests.parity import (ATT_GRAD_OBS, ATT_TOL, SCORE_TOL, bf16_ulp_diff, check_topk, dev_bits, encoded_keys_ok, grads_ok,
                           host_bits, rel_rows, route_grad_bounds, route_near_ties)
 
 pytestmark = pytest.mark.gpu
@@ -434,6 +434,63 @@ def test_attention_matches_oracle(B, Tq, Tl, M, offset):
                        D ** -0.5)
         assert rel_rows(o[b], ref) <= ATT_TOL
         assert rel_rows(o[b], ref) <= 1e-4          # fp32 path: far inside the bf16 budget
+
+
+# ------------------------------------------------------ attention backward
+def _attn_bwd_case(B, Tq, Tl, M, offset, Hq=32, Hkv=8, seed=0):
+    D = 128
+    Q = sm.normal_bf16(seed, sm.TID_Q, 1, 0, B * Tq * Hq * D).reshape(B, Tq, Hq, D)
+    Kl = sm.normal_bf16(seed, sm.TID_KLOC, 1, 0, B * Tl * Hkv * D).reshape(B, Tl, Hkv, D)
+    Vl = sm.normal_bf16(seed, sm.TID_VLOC, 1, 0, B * Tl * Hkv * D).reshape(B, Tl, Hkv, D)
+    Mmax = max(M, 1)
+    st = sm.normal_bf16(seed, sm.TID_KBAR, 1, 0, B * Mmax * 2 * Hkv * D).reshape(B, Mmax, 2, Hkv, D)
+    mem_len = np.array([max(M - 3 * b, 0) for b in range(B)], dtype=np.int32)
+    dO = np.random.default_rng(seed).standard_normal((B, Tq, Hq, D)).astype(np.float32)
+    return Q, Kl, Vl, st, mem_len, dO, Mmax
+
+
+def _run_attn_bwd(Q, Kl, Vl, st, mem_len, dO, Mmax, offset):
+    stg = dev_bits(st)
+    out = ops.sparse_attn_backward(dev_bits(Q), dev_bits(Kl), dev_bits(Vl), stg, stg[:, :, 1], 2 * st.shape[-2] * 128,
+                                   Mmax, torch.from_numpy(mem_len).to(DEV), offset, torch.from_numpy(dO).to(DEV),
+                                   rope_base=1e6)
+    torch.cuda.synchronize()
+    return [t.cpu().numpy() for t in out]
+
+
+@pytest.mark.parametrize("B,Tq,Tl,M,offset,Hq,Hkv", [(1, 32, 32, 32, 4, 32, 8), (1, 1, 128, 262, 16, 32, 8),
+                                                     (1, 128, 128, 262, 16, 32, 8), (2, 64, 64, 133, 16, 32, 8),
+                                                     (1, 5, 9, 0, 0, 32, 8), (1, 17, 40, 1, 3, 32, 8),
+                                                     (3, 16, 16, 70, 8, 32, 8), (2, 1, 300, 5, 2, 32, 8),
+                                                     (1, 100, 130, 45, 7, 32, 8), (1, 40, 50, 20, 5, 16, 2),
+                                                     (1, 33, 33, 10, 0, 8, 8)])
+def test_attention_backward_matches_oracle(B, Tq, Tl, M, offset, Hq, Hkv):
+    announce("attn-backward", B, Tq, Tl, M, offset, Hq, Hkv)
+    Q, Kl, Vl, st, mem_len, dO, Mmax = _attn_bwd_case(B, Tq, Tl, M, offset, Hq, Hkv, seed=B * 1000 + Tq + M)
+    dQ, dKl, dVl, dKm, dVm = _run_attn_bwd(Q, Kl, Vl, st, mem_len, dO, Mmax, offset)
+    worst = 0.0
+    for b in range(B):
+        m = int(mem_len[b])
+        ref = O.attend_backward(f64(Q[b]), f64(Kl[b]), f64(Vl[b]), f64(st[b, :m, 0]), f64(st[b, :m, 1]), offset,
+                                1e6, 128 ** -0.5, dO[b].astype(np.float64))
+        got = (dQ[b], dKl[b], dVl[b], dKm[b, :m], dVm[b, :m])
+        for name, x, y in zip(("dQ", "dKloc", "dVloc", "dKmem", "dVmem"), got, ref):
+            if y.size:
+                e = rel_rows(x, y)
+                worst = max(worst, e)
+                assert e <= ATT_TOL, f"{name} b={b}: {e}"
+        assert np.all(dKm[b, m:] == 0) and np.all(dVm[b, m:] == 0)
+    print("worst per-row relative error", worst, flush=True)
+    assert worst <= ATT_GRAD_OBS
+
+
+def test_attention_backward_deterministic():
+    Q, Kl, Vl, st, mem_len, dO, Mmax = _attn_bwd_case(2, 128, 128, 262, 16, seed=5)
+    announce("attn-backward-determinism")
+    a = _run_attn_bwd(Q, Kl, Vl, st, mem_len, dO, Mmax, 16)
+    b = _run_attn_bwd(Q, Kl, Vl, st, mem_len, dO, Mmax, 16)
+    for x, y in zip(a, b):
+        assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
 
 
 # ---------------------------------------------------------------- assembly
