@@ -210,8 +210,9 @@ int msa_route_scores_backward(const uint16_t* Qr, int B, int T, int H, int D, co
   MSA_CHECK_SUPPORTED(T <= msa::ROUTE_BWD_MAX_T, "T=%d unsupported (T <= %d)", T, msa::ROUTE_BWD_MAX_T);
   MSA_CHECK_ARG(B <= 65535, "B must be <= 65535");
   MSA_CHECK_ARG(n_docs < ((int64_t)1 << 30) && n_chunks < ((int64_t)1 << 40), "size out of range");
-  MSA_CHECK_ARG(aligned16(Qr) && (n_chunks == 0 || aligned16(Krbar)) && aligned16(dQr) && aligned16(dKsel),
-                "Qr, Krbar, dQr and dKsel must be 16-byte aligned");
+  MSA_CHECK_ARG(aligned16(Qr) && (n_chunks == 0 || aligned16(Krbar)) && aligned16(dQr) && aligned16(dKsel) &&
+                    aligned16(sel),
+                "Qr, Krbar, dQr, dKsel and sel must be 16-byte aligned");
   const size_t need = msa::route_bwd_workspace(B, T, H, n_docs);
   if (workspace_bytes < need || workspace == nullptr) {
     msa::set_error("workspace %zu bytes < required %zu", workspace_bytes, need);

@@ -22,9 +22,12 @@
 //   hist / scan / scatter  a stable counting sort of the documents by selected
 //       token (tiles of 1,024 documents), so each token's documents sit
 //       contiguously and in document order.
-//   piece<H>  each token's list is cut into pieces of 64 documents; one
-//       workgroup sums w/|k| * k and w c over a piece (16-byte row loads, rows
-//       split over lane groups and added in a fixed order).
+//   piece<H>  each token's list is cut into pieces of 64 documents (the scan
+//       writes each piece's first position and count; the scatter writes the
+//       sorted documents' chunk ids next to them, so a piece's row loads wait on
+//       two lookups only); one workgroup sums w/|k| * k and w c over a piece
+//       (16-byte row loads, 16 in flight per lane, rows split over lane groups
+//       and added in a fixed order).
 //   final   one workgroup per token adds its pieces in order:
 //       dq = (sum w k/|k| - q^ sum w c) / |q|.  No atomics: the result does not
 //       depend on scheduling.
@@ -41,7 +44,7 @@ constexpr int SEL_THREADS = 256;    // 4 waves; wave w takes token tiles w, w + 
 constexpr int LPD = SEL_THREADS / SEL_DOCS;   // lanes per document
 constexpr int SORT_TILE = 1024;     // documents per histogram / scatter workgroup
 constexpr int PIECE = 64;           // documents per partial sum of the query gradient
-constexpr int PIECE_UNROLL = 8;
+constexpr int PIECE_UNROLL = 16;
 constexpr int MAX_T = ROUTE_BWD_MAX_T;
 
 template <int H>
@@ -69,6 +72,21 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
   return ((uint64_t)hi << 32) | lo;
 }
 __device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// Sum over each row of 16 lanes, every lane receiving the total: lane swaps within
+// quads (quad_perm [1,0,3,2], [2,3,0,1]), then across the quads of a half-row
+// (row_half_mirror) and across the halves (row_mirror), all DPP moves.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float sum16(float v) {
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  v += dpp_f<0x140>(v);
+  return v;
+}
 
 template <int H>
 __global__ void __launch_bounds__(SEL_THREADS, 2)
@@ -287,6 +305,321 @@ route_bwd_select_kernel(const uint16_t* __restrict__ Qr, int T, const uint16_t* 
   if (sub < H) { ikw[bd * H + sub] = my_ikw; wcos[bd * H + sub] = my_wc; }
 }
 
+// ---------------------------------------------------------------- H = 8 path
+// The selected chunk of every document (first maximum of its chunk scores),
+// LPD lanes per document; -1 for a document that passes no gradient.
+__global__ void __launch_bounds__(256)
+route_bwd_pick_kernel(const int64_t* __restrict__ off, int64_t n_docs, int64_t n_chunks,
+                      const uint8_t* __restrict__ exclude, const float* __restrict__ chunk_scores,
+                      const float* __restrict__ dDoc, int64_t* __restrict__ gsel) {
+  const int b = blockIdx.y;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t d = gid / LPD;
+  const int sub = (int)(gid % LPD);
+  uint64_t key = 0;
+  int64_t c0 = 0;
+  if (d < n_docs) {
+    const int64_t bd = (int64_t)b * n_docs + d;
+    if (!(exclude && exclude[bd]) && dDoc[bd] != 0.f) {
+      c0 = off[d];
+      const int64_t c1 = off[d + 1];
+      for (int64_t c = c0 + sub; c < c1; c += LPD)
+        key = max_u64(key, ((uint64_t)enc_f32(chunk_scores[(int64_t)b * n_chunks + c]) << 32) |
+                               (uint32_t)(0xFFFFFFFFu - (uint32_t)(c - c0)));
+    }
+  }
+#pragma unroll
+  for (int s = 1; s < LPD; s <<= 1) key = max_u64(key, shfl_xor_u64(key, s));
+  if (sub == 0 && d < n_docs)
+    gsel[(int64_t)b * n_docs + d] = key ? c0 + (int64_t)(0xFFFFFFFFu - (uint32_t)key) : -1;
+}
+
+constexpr int PG = 32;                       // documents per group of the persistent kernel
+constexpr int SELECT8_WORKGROUPS = 256;      // one per CU
+constexpr int P_HD = 8 * D;
+constexpr int P_KROW = P_HD + 8;             // staged row stride (bf16): banks staggered by 4
+
+__device__ __forceinline__ int64_t shfl_i64(int64_t v, int src) {
+  const int lo = __shfl((int)(uint32_t)v, src), hi = __shfl((int)(uint32_t)((uint64_t)v >> 32), src);
+  return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+constexpr int S8_WAVES = 8;                  // 4 token tiles x 2 head groups
+constexpr int S8_THREADS = 64 * S8_WAVES;
+
+// This wave copies the selected rows of documents 4w .. 4w+3 of a group into `buf`,
+// one 1 KB half-row per wave instruction (global_load_lds: 16 bytes a lane).  gv:
+// lanes 0..31 hold the group's chunk ids (-1: nothing to copy).
+__device__ __forceinline__ void issue_group(const uint16_t* __restrict__ Krbar, int64_t gv, uint16_t* buf, int wave,
+                                            int lane) {
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int doc = wave * 4 + (q >> 1), hh = q & 1;
+    const int64_t g = shfl_i64(gv, doc);
+    if (g >= 0) dma16(Krbar + g * P_HD + hh * 512 + lane * 8, buf + doc * P_KROW + hh * 512);
+  }
+}
+
+// Router rows of token tile tt as A operands for heads 4 hg .. 4 hg + 3, and their
+// inverse norms per head.
+__device__ __forceinline__ void load_rows4(const uint16_t* __restrict__ Qr, int b, int T, int tt, int hg, int m,
+                                           int half, bf16x8_t (&a)[4][8], float (*iq)[32]) {
+  const int t = tt * 32 + m;
+  const bool tv = t < T;
+  const uint16_t* qrow = Qr + ((int64_t)b * T + (tv ? t : 0)) * P_HD + hg * 4 * D + 8 * half;
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    float ss = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if (tv) x = *reinterpret_cast<const uint4*>(qrow + h * D + 16 * ks);
+      a[h][ks] = __builtin_bit_cast(bf16x8_t, x);
+      ss = sq_norm_piece(x, ss);
+    }
+    ss += __shfl_xor(ss, 32);
+    if (half == 0) iq[h][m] = inv_norm(ss);
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
+struct S8Lds {
+  float ik[PG][8];
+  float iq[S8_WAVES][4][32];
+  f32x4_t xchg[4][64 * 4];             // head group 1's partial scores, per token tile
+  uint64_t best[4][PG];
+  int tsel[PG];
+};
+
+// One group of 32 documents whose rows sit in `cur` (landed); the next group's
+// rows are copied into `nxt` meanwhile.
+__device__ __forceinline__ void select8_group(const uint16_t* __restrict__ Qr, int b, int T,
+                                              const float* __restrict__ knorm, float& ik_pre, int64_t n_docs, const float* __restrict__ dDoc, int64_t grp,
+                                              int64_t g_cur, int64_t g_nxt, bool has_next,
+                                              const uint16_t* __restrict__ Krbar, const uint16_t* cur, uint16_t* nxt,
+                                              bf16x8_t (&a)[4][8], bool resident, S8Lds& sm,
+                                              float* __restrict__ dK, int32_t* __restrict__ sel,
+                                              float* __restrict__ ikw, float* __restrict__ wcos, int tid, int wave,
+                                              int lane) {
+  constexpr int H = 8;
+  const int half = lane >> 5, m = lane & 31;
+  const int rt = wave & 3, hg = wave >> 2;         // token tile slot, head group
+  wait_vmem_all();
+  lds_barrier();                                   // `cur` landed; the previous group is done with `nxt`
+  if (has_next) issue_group(Krbar, g_nxt, nxt, wave, lane);
+  if (tid < PG * H) {
+    // 1/|k| of (document tid % 32, head tid / 32): the stored norm fetched one group
+    // ahead, or from the staged rows (consecutive lanes on consecutive rows: no bank
+    // conflicts)
+    const int doc = tid & 31, h = tid >> 5;
+    float ik = ik_pre;
+    if (!knorm) {
+      float ss = 0.f;
+#pragma unroll
+      for (int x = 0; x < D / 8; ++x)
+        ss = sq_norm_piece(*reinterpret_cast<const uint4*>(cur + doc * P_KROW + h * D + 8 * x), ss);
+      ik = inv_norm(ss);
+    }
+    sm.ik[doc][h] = shfl_i64(g_cur, doc) >= 0 ? ik : 0.f;
+    // the next group's stored norm, in flight while this group is scored
+    if (knorm) {
+      const int64_t gn = shfl_i64(g_nxt, doc);
+      ik_pre = gn >= 0 ? knorm[gn * H + h] : 0.f;
+    }
+  }
+  lds_barrier();
+  // token scores of the 32 rows: wave (rt, hg) takes token tiles rt, rt + 4, ... over heads 4 hg ..
+  uint64_t bk = 0;
+  const int n_tt = (T + 31) / 32;
+  const float inv_h = 1.0f / (float)H;
+  const int n_rounds = (n_tt + 3) / 4;
+  for (int rd = 0; rd < n_rounds; ++rd) {
+    const int tt = rd * 4 + rt;
+    const bool act = tt < n_tt;
+    f32x16_t s0 = {};
+    if (act) {
+      if (!resident) load_rows4(Qr, b, T, tt, hg, m, half, a, sm.iq[wave]);
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        f32x16_t c = {};
+        const uint16_t* bp = cur + m * P_KROW + (hg * 4 + h) * D + 8 * half;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[h][ks], *reinterpret_cast<const bf16x8_t*>(bp + 16 * ks),
+                                                      c, 0, 0, 0);
+        const float ik = sm.ik[m][hg * 4 + h];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4_t r = *reinterpret_cast<const f32x4_t*>(&sm.iq[wave][h][8 * q + 4 * half]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s0[4 * q + e] += c[4 * q + e] * r[e] * ik;
+        }
+      }
+    }
+    // head group 1 hands its partial sums to head group 0 (same token tile)
+    if (hg == 1 && act) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        sm.xchg[rt][lane * 4 + q] = (f32x4_t){s0[4 * q], s0[4 * q + 1], s0[4 * q + 2], s0[4 * q + 3]};
+    }
+    lds_barrier();
+    if (hg == 0 && act) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4_t x = sm.xchg[rt][lane * 4 + q];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s0[4 * q + e] += x[e];
+      }
+      // C register i holds row 8 (i / 4) + 4 half + i % 4 of column m
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int tok = tt * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+        if (tok < T) bk = max_u64(bk, argmax_key(s0[i] * inv_h, tok));
+      }
+    }
+    lds_barrier();                                  // exchange slots free for the next round
+  }
+  if (hg == 0) {
+    bk = max_u64(bk, shfl_xor_u64(bk, 32));
+    if (half == 0) sm.best[rt][m] = bk;
+  }
+  lds_barrier();
+  if (tid < PG) {
+    uint64_t bb = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) bb = max_u64(bb, sm.best[w][tid]);
+    sm.tsel[tid] = (g_cur >= 0 && bb != 0) ? 0x7FFFFFFF - (int)(uint32_t)bb : -1;
+  }
+  lds_barrier();
+
+  // per document (16 lanes) and head: cosine, key gradient, query-gradient weights
+  const int idoc = tid >> 4, sub = tid & 15;
+  const int64_t d = grp * PG + idoc;
+  const int64_t g = shfl_i64(g_cur, idoc);
+  if (d >= n_docs) return;
+  const int tsel = sm.tsel[idoc];
+  const int64_t bd = (int64_t)b * n_docs + d;
+  if (sub == 0) {
+    sel[2 * bd] = tsel < 0 ? -1 : (int32_t)g;
+    sel[2 * bd + 1] = tsel;
+  }
+  float4* o = reinterpret_cast<float4*>(dK + bd * P_HD);
+  if (tsel < 0) {
+#pragma unroll
+    for (int x = 0; x < P_HD / 4 / 16; ++x) o[sub + 16 * x] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (sub < H) { ikw[bd * H + sub] = 0.f; wcos[bd * H + sub] = 0.f; }
+    return;
+  }
+  const float w = dDoc[bd] * (1.0f / (float)H);
+  const uint16_t* qrow = Qr + ((int64_t)b * T + tsel) * P_HD;
+  const uint16_t* krow = cur + idoc * P_KROW;
+  float my_ikw = 0.f, my_wc = 0.f;
+#pragma unroll
+  for (int h0 = 0; h0 < H; h0 += 4) {
+    uint2 qv[4][2], kv[4][2];
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        qv[h][j] = *reinterpret_cast<const uint2*>(qrow + (h0 + h) * D + 4 * (sub + 16 * j));
+        kv[h][j] = *reinterpret_cast<const uint2*>(krow + (h0 + h) * D + 4 * (sub + 16 * j));
+      }
+    float qq[4], kk[4], qk[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      float a2 = 0.f, b2 = 0.f, c2 = 0.f;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        a2 = dot2_bf16(qv[h][j].x, qv[h][j].x, a2); a2 = dot2_bf16(qv[h][j].y, qv[h][j].y, a2);
+        b2 = dot2_bf16(kv[h][j].x, kv[h][j].x, b2); b2 = dot2_bf16(kv[h][j].y, kv[h][j].y, b2);
+        c2 = dot2_bf16(qv[h][j].x, kv[h][j].x, c2); c2 = dot2_bf16(qv[h][j].y, kv[h][j].y, c2);
+      }
+      qq[h] = sum16(a2);
+      kk[h] = sum16(b2);
+      qk[h] = sum16(c2);
+    }
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      float ca = 0.f, cb = 0.f, ik = 0.f, cs = 0.f;
+      if (qq[h] > 0.f && kk[h] > 0.f) {
+        const float iq = 1.0f / sqrtf(qq[h]);
+        ik = 1.0f / sqrtf(kk[h]);
+        cs = qk[h] * iq * ik;
+        ca = w * ik * iq;        // dK = w (q^ - c k^) / |k| = ca q - cb k
+        cb = w * ik * ik * cs;
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        o[(h0 + h) * (D / 4) + sub + 16 * j] =
+            make_float4(ca * bf16_lo(qv[h][j].x) - cb * bf16_lo(kv[h][j].x),
+                        ca * bf16_hi(qv[h][j].x) - cb * bf16_hi(kv[h][j].x),
+                        ca * bf16_lo(qv[h][j].y) - cb * bf16_lo(kv[h][j].y),
+                        ca * bf16_hi(qv[h][j].y) - cb * bf16_hi(kv[h][j].y));
+      if (h0 + h == sub) { my_ikw = w * ik; my_wc = w * cs; }
+    }
+  }
+  if (sub < H) { ikw[bd * H + sub] = my_ikw; wcos[bd * H + sub] = my_wc; }
+}
+
+// Persistent select kernel for H = 8: each workgroup walks groups blockIdx.x,
+// blockIdx.x + gridDim.x, ... of one query.  Eight waves: wave (rt, hg) scores
+// token tile rt (+4, ...) over heads 4 hg .. 4 hg + 3, and with T <= 128 keeps
+// those 32 router rows resident as A operands (128 registers); the two head
+// groups add their partial sums through LDS.  The next group's rows are copied
+// into the other LDS buffer while this one is scored; the buffers are separate
+// LDS objects and the loop is unrolled by two, so the compiler never orders a
+// read of one behind a copy into the other.
+__global__ void __launch_bounds__(S8_THREADS)
+route_bwd_select8_kernel(const uint16_t* __restrict__ Qr, int T, const uint16_t* __restrict__ Krbar,
+                         const float* __restrict__ knorm, int64_t n_docs, const float* __restrict__ dDoc,
+                         const int64_t* __restrict__ gsel, float* __restrict__ dK, int32_t* __restrict__ sel,
+                         float* __restrict__ ikw, float* __restrict__ wcos) {
+  __shared__ __attribute__((aligned(16))) uint16_t kbuf0[PG * P_KROW];
+  __shared__ __attribute__((aligned(16))) uint16_t kbuf1[PG * P_KROW];
+  __shared__ S8Lds sm;
+  const int b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t n_groups = (n_docs + PG - 1) / PG;
+  int64_t grp = blockIdx.x;
+  if (grp >= n_groups) return;
+  const int n_tt = (T + 31) / 32;
+  const bool resident = n_tt <= 4;
+  bf16x8_t a[4][8];
+  if (resident) load_rows4(Qr, b, T, (wave & 3) < n_tt ? (wave & 3) : 0, wave >> 2, lane & 31, lane >> 5, a,
+                           sm.iq[wave]);
+  const int64_t* gs = gsel + (int64_t)b * n_docs;
+  // a group's chunk ids (lanes 0..31 of every wave) and, with stored norms, the
+  // inverse norm of (document tid / 8, head tid % 8), both fetched one group ahead
+  auto chunk_ids = [&](int64_t gr) -> int64_t {
+    const int64_t d = gr * PG + (lane & 31);
+    return (gr < n_groups && lane < 32 && d < n_docs) ? gs[d] : -1;
+  };
+  int64_t g_cur = chunk_ids(grp), g_nxt;
+  float ik_pre = 0.f;
+  if (knorm && tid < PG * 8) {
+    const int64_t g = shfl_i64(g_cur, tid & 31);
+    ik_pre = g >= 0 ? knorm[g * 8 + (tid >> 5)] : 0.f;
+  }
+  issue_group(Krbar, g_cur, kbuf0, wave, lane);
+  while (true) {
+    int64_t nx = grp + gridDim.x;
+    g_nxt = chunk_ids(nx);
+    select8_group(Qr, b, T, knorm, ik_pre, n_docs, dDoc, grp, g_cur, g_nxt, nx < n_groups, Krbar, kbuf0, kbuf1, a,
+                  resident, sm, dK, sel, ikw, wcos, tid, wave, lane);
+    if (nx >= n_groups) break;
+    grp = nx;
+    g_cur = g_nxt;
+    nx = grp + gridDim.x;
+    g_nxt = chunk_ids(nx);
+    select8_group(Qr, b, T, knorm, ik_pre, n_docs, dDoc, grp, g_cur, g_nxt, nx < n_groups, Krbar, kbuf1, kbuf0, a,
+                  resident, sm, dK, sel, ikw, wcos, tid, wave, lane);
+    if (nx >= n_groups) break;
+    grp = nx;
+    g_cur = g_nxt;
+  }
+  wait_vmem_all();                                 // no copy into LDS outlives the workgroup
+}
+
 // Per tile of SORT_TILE documents: how many select each token.
 __global__ void __launch_bounds__(256)
 route_bwd_hist_kernel(const int32_t* __restrict__ sel, int64_t n_docs, int T, int64_t n_tiles,
@@ -313,7 +646,7 @@ route_bwd_hist_kernel(const int32_t* __restrict__ sel, int64_t n_docs, int T, in
 // each tile's offset inside the token's segment.
 __global__ void __launch_bounds__(1024)
 route_bwd_scan_kernel(int32_t* __restrict__ tile_cnt, int64_t n_tiles, int T, int64_t max_pieces,
-                      int32_t* __restrict__ seg, int32_t* __restrict__ pstart, int32_t* __restrict__ piece_t) {
+                      int32_t* __restrict__ seg, int32_t* __restrict__ pstart, int4* __restrict__ pdesc) {
   constexpr int U = 16;
   __shared__ int64_t s_a[16], s_b[16];
   __shared__ int64_t carry_a, carry_b;
@@ -321,7 +654,7 @@ route_bwd_scan_kernel(int32_t* __restrict__ tile_cnt, int64_t n_tiles, int T, in
   int32_t* tc = tile_cnt + (int64_t)b * n_tiles * T;
   int32_t* sg = seg + (int64_t)b * (T + 1);
   int32_t* ps = pstart + (int64_t)b * (T + 1);
-  int32_t* pt = piece_t + (int64_t)b * max_pieces;
+  int4* pd = pdesc + (int64_t)b * max_pieces;
   if (tid == 0) { carry_a = 0; carry_b = 0; }
   __syncthreads();
   for (int t0 = 0; t0 < T; t0 += 1024) {
@@ -350,13 +683,18 @@ route_bwd_scan_kernel(int32_t* __restrict__ tile_cnt, int64_t n_tiles, int T, in
       const int64_t p0 = cb + p - np;
       sg[t] = (int32_t)(ca + a - tot);
       ps[t] = (int32_t)p0;
-      for (int64_t j = 0; j < np; ++j) pt[p0 + j] = t;
+      const int64_t s0 = ca + a - tot;
+      for (int64_t j = 0; j < np; ++j) {
+        const int64_t left = tot - j * PIECE;
+        pd[p0 + j] = make_int4(t, (int)(s0 + j * PIECE), (int)(left < PIECE ? left : PIECE), 0);
+      }
     }
     __syncthreads();
     if (tid == 1023) { carry_a = ca + a; carry_b = cb + p; }
     __syncthreads();
   }
   if (tid == 0) { sg[T] = (int32_t)carry_a; ps[T] = (int32_t)carry_b; }
+  for (int64_t j = carry_b + tid; j < max_pieces; j += 1024) pd[j] = make_int4(0, 0, 0, 0);   // unused: empty
 }
 
 // Stable scatter: document d goes to its token's segment after every earlier
@@ -364,7 +702,7 @@ route_bwd_scan_kernel(int32_t* __restrict__ tile_cnt, int64_t n_tiles, int T, in
 __global__ void __launch_bounds__(256)
 route_bwd_scatter_kernel(const int32_t* __restrict__ sel, int64_t n_docs, int T, int64_t n_tiles,
                          const int32_t* __restrict__ tile_cnt, const int32_t* __restrict__ seg,
-                         int32_t* __restrict__ order) {
+                         int32_t* __restrict__ order, int64_t* __restrict__ ordg) {
   __shared__ int base[MAX_T];
   __shared__ __attribute__((aligned(16))) int t_s[256];
   const int b = blockIdx.y, tid = threadIdx.x, wave = tid >> 6;
@@ -376,7 +714,9 @@ route_bwd_scatter_kernel(const int32_t* __restrict__ sel, int64_t n_docs, int T,
   for (int sb = 0; sb < SORT_TILE; sb += 256) {
     if (tile * SORT_TILE + sb >= n_docs) break;
     const int64_t d = tile * SORT_TILE + sb + tid;
-    const int t = d < n_docs ? sel[((int64_t)b * n_docs + d) * 2 + 1] : -1;
+    int2 gt = make_int2(-1, -1);
+    if (d < n_docs) gt = *reinterpret_cast<const int2*>(sel + ((int64_t)b * n_docs + d) * 2);
+    const int t = gt.y;
     t_s[tid] = t;
     __syncthreads();
     // rank among the earlier documents of this block with the same token
@@ -389,7 +729,11 @@ route_bwd_scatter_kernel(const int32_t* __restrict__ sel, int64_t n_docs, int T,
       rank += (j < tid && v.x == t) + (j + 1 < tid && v.y == t) + (j + 2 < tid && v.z == t) +
               (j + 3 < tid && v.w == t);
     }
-    if (t >= 0) order[(int64_t)b * n_docs + base[t] + rank] = (int32_t)d;
+    if (t >= 0) {
+      const int64_t pos = (int64_t)b * n_docs + base[t] + rank;
+      order[pos] = (int32_t)d;
+      ordg[pos] = gt.x;
+    }
     __syncthreads();
     if (t >= 0) atomicAdd(&base[t], 1);
     __syncthreads();
@@ -401,10 +745,9 @@ route_bwd_scatter_kernel(const int32_t* __restrict__ sel, int64_t n_docs, int T,
 // RG row groups are then added in order.
 template <int H>
 __global__ void __launch_bounds__(256)
-route_bwd_piece_kernel(const uint16_t* __restrict__ Krbar, int64_t n_docs, int T, const int32_t* __restrict__ sel,
-                       const float* __restrict__ ikw, const float* __restrict__ wcos,
-                       const int32_t* __restrict__ order, const int32_t* __restrict__ seg,
-                       const int32_t* __restrict__ pstart, const int32_t* __restrict__ piece_t, int64_t max_pieces,
+route_bwd_piece_kernel(const uint16_t* __restrict__ Krbar, int64_t n_docs, const float* __restrict__ ikw,
+                       const float* __restrict__ wcos, const int32_t* __restrict__ order,
+                       const int64_t* __restrict__ ordg, const int4* __restrict__ pdesc, int64_t max_pieces,
                        float* __restrict__ partial, float* __restrict__ partial_c) {
   constexpr int HD = H * D, TPR = HD / 8, RG = 256 / TPR;
   __shared__ int64_t g_s[PIECE], bd_s[PIECE];
@@ -412,17 +755,13 @@ route_bwd_piece_kernel(const uint16_t* __restrict__ Krbar, int64_t n_docs, int T
   __shared__ float red_c[RG][H];
   const int b = blockIdx.y, tid = threadIdx.x;
   const int64_t p = blockIdx.x;
-  const int32_t* ps = pstart + (int64_t)b * (T + 1);
-  if (p >= ps[T]) return;
-  const int t = piece_t[(int64_t)b * max_pieces + p];
-  const int32_t* sg = seg + (int64_t)b * (T + 1);
-  const int64_t lo = sg[t] + (p - ps[t]) * (int64_t)PIECE;
-  const int64_t hi = sg[t + 1] < lo + PIECE ? (int64_t)sg[t + 1] : lo + PIECE;
-  const int n = (int)(hi - lo);
+  const int4 pd = pdesc[(int64_t)b * max_pieces + p];       // (token, first position, count)
+  const int n = pd.z;
+  if (n == 0) return;
   if (tid < n) {
-    const int64_t bd = (int64_t)b * n_docs + order[(int64_t)b * n_docs + lo + tid];
-    bd_s[tid] = bd;
-    g_s[tid] = sel[2 * bd];
+    const int64_t pos = (int64_t)b * n_docs + pd.y + tid;
+    bd_s[tid] = (int64_t)b * n_docs + order[pos];
+    g_s[tid] = ordg[pos];
   }
   __syncthreads();
   const int rg = tid / TPR, e0 = 8 * (tid % TPR), h = e0 / D;
@@ -517,7 +856,7 @@ route_bwd_final_kernel(const uint16_t* __restrict__ Qr, int T, int H, const int3
 
 struct BwdLayout {
   int64_t n_tiles, max_pieces;
-  size_t ikw, wcos, tile_cnt, seg, pstart, piece_t, order, partial, partial_c, total;
+  size_t ikw, wcos, tile_cnt, seg, pstart, pdesc, order, ordg, partial, partial_c, gsel, total;
 };
 
 BwdLayout bwd_layout(int B, int T, int H, int64_t n_docs) {
@@ -536,10 +875,12 @@ BwdLayout bwd_layout(int B, int T, int H, int64_t n_docs) {
   L.tile_cnt = take(Bz * L.n_tiles * T * 4);
   L.seg = take(Bz * (T + 1) * 4);
   L.pstart = take(Bz * (T + 1) * 4);
-  L.piece_t = take(Bz * L.max_pieces * 4);
+  L.pdesc = take(Bz * L.max_pieces * 16);
   L.order = take(Bz * n_docs * 4);
+  L.ordg = take(Bz * n_docs * 8);
   L.partial = take(Bz * L.max_pieces * H * D * 4);
   L.partial_c = take(Bz * L.max_pieces * H * 4);
+  L.gsel = take(H == 8 ? Bz * n_docs * 8 : 0);
   L.total = o;
   return L;
 }
@@ -557,28 +898,42 @@ int launch_bwd_h(const BwdArgs& A, const BwdLayout& L, uint8_t* ws, hipStream_t 
   int32_t* tile_cnt = reinterpret_cast<int32_t*>(ws + L.tile_cnt);
   int32_t* seg = reinterpret_cast<int32_t*>(ws + L.seg);
   int32_t* pstart = reinterpret_cast<int32_t*>(ws + L.pstart);
-  int32_t* piece_t = reinterpret_cast<int32_t*>(ws + L.piece_t);
+  int4* pdesc = reinterpret_cast<int4*>(ws + L.pdesc);
   int32_t* order = reinterpret_cast<int32_t*>(ws + L.order);
+  int64_t* ordg = reinterpret_cast<int64_t*>(ws + L.ordg);
   float* partial = reinterpret_cast<float*>(ws + L.partial);
   float* partial_c = reinterpret_cast<float*>(ws + L.partial_c);
   const int B = A.B, T = A.T;
   const int64_t n_docs = A.n_docs;
-  hipLaunchKernelGGL(route_bwd_select_kernel<H>, dim3((unsigned)((n_docs + SEL_DOCS - 1) / SEL_DOCS), (unsigned)B),
-                     dim3(SEL_THREADS), 0, stream, A.Qr, T, A.Krbar, A.knorm, A.off, n_docs, A.n_chunks, A.exclude,
-                     A.chunk_scores, A.dDoc, A.dK, A.sel, ikw, wcos);
-  MSA_CHECK_LAUNCH();
+  if constexpr (H == 8) {
+    int64_t* gsel = reinterpret_cast<int64_t*>(ws + L.gsel);
+    hipLaunchKernelGGL(route_bwd_pick_kernel, dim3((unsigned)((n_docs * LPD + 255) / 256), (unsigned)B), dim3(256), 0,
+                       stream, A.off, n_docs, A.n_chunks, A.exclude, A.chunk_scores, A.dDoc, gsel);
+    MSA_CHECK_LAUNCH();
+    // one persistent workgroup per CU (its LDS holds two groups of rows)
+    const int64_t n_groups = (n_docs + PG - 1) / PG;
+    int64_t per_b = (SELECT8_WORKGROUPS + B - 1) / B;
+    per_b = per_b < n_groups ? per_b : n_groups;
+    hipLaunchKernelGGL(route_bwd_select8_kernel, dim3((unsigned)per_b, (unsigned)B), dim3(S8_THREADS), 0, stream,
+                       A.Qr, T, A.Krbar, A.knorm, n_docs, A.dDoc, gsel, A.dK, A.sel, ikw, wcos);
+    MSA_CHECK_LAUNCH();
+  } else {
+    hipLaunchKernelGGL(route_bwd_select_kernel<H>, dim3((unsigned)((n_docs + SEL_DOCS - 1) / SEL_DOCS), (unsigned)B),
+                       dim3(SEL_THREADS), 0, stream, A.Qr, T, A.Krbar, A.knorm, A.off, n_docs, A.n_chunks, A.exclude,
+                       A.chunk_scores, A.dDoc, A.dK, A.sel, ikw, wcos);
+    MSA_CHECK_LAUNCH();
+  }
   const dim3 gt((unsigned)L.n_tiles, (unsigned)B);
   hipLaunchKernelGGL(route_bwd_hist_kernel, gt, dim3(256), 0, stream, A.sel, n_docs, T, L.n_tiles, tile_cnt);
   MSA_CHECK_LAUNCH();
   hipLaunchKernelGGL(route_bwd_scan_kernel, dim3((unsigned)B), dim3(1024), 0, stream, tile_cnt, L.n_tiles, T,
-                     L.max_pieces, seg, pstart, piece_t);
+                     L.max_pieces, seg, pstart, pdesc);
   MSA_CHECK_LAUNCH();
   hipLaunchKernelGGL(route_bwd_scatter_kernel, gt, dim3(256), 0, stream, A.sel, n_docs, T, L.n_tiles, tile_cnt, seg,
-                     order);
+                     order, ordg);
   MSA_CHECK_LAUNCH();
   hipLaunchKernelGGL(route_bwd_piece_kernel<H>, dim3((unsigned)L.max_pieces, (unsigned)B), dim3(256), 0, stream,
-                     A.Krbar, n_docs, T, A.sel, ikw, wcos, order, seg, pstart, piece_t, L.max_pieces, partial,
-                     partial_c);
+                     A.Krbar, n_docs, ikw, wcos, order, ordg, pdesc, L.max_pieces, partial, partial_c);
   MSA_CHECK_LAUNCH();
   hipLaunchKernelGGL(route_bwd_final_kernel, dim3((unsigned)T, (unsigned)B), dim3(256), 0, stream, A.Qr, T, H,
                      pstart, L.max_pieces, partial, partial_c, A.dQ);
