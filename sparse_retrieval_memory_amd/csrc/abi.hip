@@ -355,10 +355,12 @@ int msa_sparse_attn_backward(const uint16_t* Q, int B, int Tq, int Hq, int D, co
   MSA_CHECK_ARG(Mmax >= 0 && rope_offset >= 0 && rope_base > 1.0, "need Mmax >= 0, rope_offset >= 0, base > 1");
   MSA_CHECK_ARG((int64_t)Mmax + Tl < (1 << 24) && Tq < (1 << 24), "sizes out of range");
   MSA_CHECK_ARG(Q && Kloc && Vloc && mem_len && dO && dQ && dKloc && dVloc, "null pointer");
-  MSA_CHECK_ARG(Mmax == 0 || (Kmem && Vmem && dKmem && dVmem && mem_entry_stride >= (int64_t)Hkv * D),
+  MSA_CHECK_ARG(Mmax == 0 || (Kmem && Vmem && dKmem && dVmem && mem_entry_stride >= (int64_t)Hkv * D &&
+                               mem_entry_stride % 8 == 0),
                 "memory pointers/stride invalid");
   MSA_CHECK_ARG(aligned16(Q) && aligned16(Kloc) && aligned16(Vloc) && aligned16(dO) && aligned16(dQ) &&
-                    aligned16(dKloc) && aligned16(dVloc),
+                    aligned16(dKloc) && aligned16(dVloc) &&
+                    (Mmax == 0 || (aligned16(Kmem) && aligned16(Vmem) && aligned16(dKmem) && aligned16(dVmem))),
                 "pointers must be 16-byte aligned");
   const size_t need = msa::attn_bwd_workspace(B, Tq, Hq, Tl, Hkv, Mmax);
   if (workspace_bytes < need || workspace == nullptr) {
