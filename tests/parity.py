@@ -21,8 +21,9 @@ P6  routing-score gradients: per element |gpu - oracle| <= 2^-15 * s, where s
     the test input, so both sides skip them.
 P7  attention gradients (dQ, dK/dV of the local and the memory entries): per row
     ||g - g*|| / ||g*|| <= 2e-2, the attention budget of P4; the split-bf16
-    operands keep the observed error near 1e-5, and the tests also hold it
-    under 1e-3.
+    operands keep the observed error near 1e-5 (up to ~4e-4 for single rows over
+    thousands of keys, where dQ sums terms that cancel), and the tests also hold
+    it under 1e-3.
 P1  pooled V/Kr within 1 bf16 ulp of the oracle's rounded mean, K within 2
     ulps or 2^-20 absolute: K's terms are rotated in fp32 (each rounded), so a
     chunk mean that cancels to a tiny value keeps the accumulation's absolute

@@ -214,6 +214,17 @@ def test_route_backward_special_cases():
     assert (sel[..., 0] >= 0).sum() <= 2 * 16
 
 
+@pytest.mark.parametrize("B,T,H,n_docs", [(1, 8192, 8, 90), (2, 600, 8, 700), (1, 8192, 2, 40)])
+def test_route_backward_long_queries(B, T, H, n_docs):
+    """The longest router queries the call accepts (T = 8192: 256 token tiles, the router rows
+    no longer resident in the H = 8 kernel) and a ragged long case."""
+    announce("route-backward-long", B, T, H, n_docs)
+    Qr, Kr, off = _route_case(B, T, H, n_docs, seed=900 + T + H)
+    dDoc = np.random.default_rng(T).standard_normal((B, n_docs))
+    sel = _check_route_backward(Qr, Kr, off, dDoc, stored_norms=True)
+    assert (sel[..., 0] >= 0).mean() > 0.8
+
+
 def test_route_backward_deterministic():
     Qr, Kr, off = _route_case(1, 16, 8, n_docs=5000, seed=21)   # ~300 documents per token: several pieces
     dDoc = np.random.default_rng(2).standard_normal((1, 5000))
@@ -480,6 +491,24 @@ def test_attention_backward_matches_oracle(B, Tq, Tl, M, offset, Hq, Hkv):
                 worst = max(worst, e)
                 assert e <= ATT_TOL, f"{name} b={b}: {e}"
         assert np.all(dKm[b, m:] == 0) and np.all(dVm[b, m:] == 0)
+    print("worst per-row relative error", worst, flush=True)
+    assert worst <= ATT_GRAD_OBS
+
+
+@pytest.mark.parametrize("B,Tq,Tl,M,offset", [(1, 512, 1024, 700, 16), (2, 300, 300, 0, 0), (1, 1, 2000, 950, 8)])
+def test_attention_backward_long(B, Tq, Tl, M, offset):
+    """Many row and key tiles: long local contexts, large memories, no memory, a single row."""
+    announce("attn-backward-long", B, Tq, Tl, M, offset)
+    Q, Kl, Vl, st, mem_len, dO, Mmax = _attn_bwd_case(B, Tq, Tl, M, offset, seed=7 * Tq + M)
+    dQ, dKl, dVl, dKm, dVm = _run_attn_bwd(Q, Kl, Vl, st, mem_len, dO, Mmax, offset)
+    worst = 0.0
+    for b in range(B):
+        m = int(mem_len[b])
+        ref = O.attend_backward(f64(Q[b]), f64(Kl[b]), f64(Vl[b]), f64(st[b, :m, 0]), f64(st[b, :m, 1]), offset,
+                                1e6, 128 ** -0.5, dO[b].astype(np.float64))
+        for x, y in zip((dQ[b], dKl[b], dVl[b], dKm[b, :m], dVm[b, :m]), ref):
+            if y.size:
+                worst = max(worst, rel_rows(x, y))
     print("worst per-row relative error", worst, flush=True)
     assert worst <= ATT_GRAD_OBS
 
