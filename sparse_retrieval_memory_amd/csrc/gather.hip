@@ -21,26 +21,44 @@ gather_kernel(const int32_t* __restrict__ top_idx, int k, const uint16_t* __rest
               uint16_t* __restrict__ staging, int Mmax, int32_t* __restrict__ mem_len) {
   const int r = blockIdx.x, b = blockIdx.y;
   __shared__ int64_t sh_dst, sh_src, sh_n;
-  if (threadIdx.x == 0) {
+  // where rank r's chunks go: the first wave reads the ranks' chunk counts, one lane
+  // per rank (64 at a time), and prefix-sums them
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
     int64_t before = 0, total = 0, mine_src = 0, mine_n = 0;
-    for (int q = 0; q < k; ++q) {
-      const int32_t d = top_idx[(int64_t)b * k + q];
+    for (int q0 = 0; q0 < k; q0 += 64) {
+      const int q = q0 + lane;
       int64_t n = 0, g0 = 0;
-      if (d >= 0 && d < n_docs) {
-        g0 = doc_chunk_off[d];
-        n = doc_chunk_off[d + 1] - g0;
+      if (q < k) {
+        const int32_t d = top_idx[(int64_t)b * k + q];
+        if (d >= 0 && d < n_docs) {
+          g0 = doc_chunk_off[d];
+          n = doc_chunk_off[d + 1] - g0;
+        }
       }
-      if (q < r) before += n;
-      if (q == r) { mine_src = g0; mine_n = n; }
-      total += n;
+      int64_t incl = n;                                  // inclusive prefix over the 64 lanes
+#pragma unroll
+      for (int s = 1; s < 64; s <<= 1) {
+        const int64_t u = __shfl_up(incl, s);
+        if (lane >= s) incl += u;
+      }
+      if (q == r) { mine_src = g0; mine_n = n; before = total + incl - n; }
+      total += __shfl(incl, 63);
     }
-    int64_t n = mine_n;
-    if (before >= Mmax) n = 0;
-    else if (before + n > Mmax) n = Mmax - before;
-    sh_dst = before;
-    sh_src = mine_src;
-    sh_n = n;
-    if (r == 0 && blockIdx.z == 0) mem_len[b] = (int32_t)(total < Mmax ? total : Mmax);
+    // lane r % 64 holds rank r's values; hand them to lane 0
+    const int owner = r & 63;
+    before = __shfl(before, owner);
+    mine_src = __shfl(mine_src, owner);
+    mine_n = __shfl(mine_n, owner);
+    if (lane == 0) {
+      int64_t n = mine_n;
+      if (before >= Mmax) n = 0;
+      else if (before + n > Mmax) n = Mmax - before;
+      sh_dst = before;
+      sh_src = mine_src;
+      sh_n = n;
+      if (r == 0 && blockIdx.z == 0) mem_len[b] = (int32_t)(total < Mmax ? total : Mmax);
+    }
   }
   __syncthreads();
   // blockIdx.z splits one document's copy over several workgroups: reads over the host
