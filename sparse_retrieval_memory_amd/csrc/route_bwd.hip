@@ -73,6 +73,13 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
 }
 __device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 
+// The fp32 key-gradient rows are written once and not read again here: streaming
+// (non-temporal) stores keep them from sitting dirty in L2 / Infinity Cache, where
+// their write-back would otherwise slow the later kernels' reads.
+__device__ __forceinline__ void nt_store4(float4* p, float a, float b, float c, float d) {
+  __builtin_nontemporal_store((f32x4_t){a, b, c, d}, reinterpret_cast<f32x4_t*>(p));
+}
+
 // Sum over each row of 16 lanes, every lane receiving the total: lane swaps within
 // quads (quad_perm [1,0,3,2], [2,3,0,1]), then across the quads of a half-row
 // (row_half_mirror) and across the halves (row_mirror), all DPP moves.
@@ -257,7 +264,7 @@ route_bwd_select_kernel(const uint16_t* __restrict__ Qr, int T, const uint16_t* 
   float4* o = reinterpret_cast<float4*>(dK + bd * CF::HD);
   if (g < 0) {
 #pragma unroll
-    for (int x = sub; x < CF::HD / 4; x += LPD) o[x] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int x = sub; x < CF::HD / 4; x += LPD) nt_store4(o + x, 0.f, 0.f, 0.f, 0.f);
     if (sub < H) { ikw[bd * H + sub] = 0.f; wcos[bd * H + sub] = 0.f; }
     return;
   }
@@ -297,9 +304,9 @@ route_bwd_select_kernel(const uint16_t* __restrict__ Qr, int T, const uint16_t* 
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      o[h * (D / 4) + sub + LPD * j] =
-          make_float4(ca * bf16_lo(qv[h][j].x) - cb * bf16_lo(kv[j].x), ca * bf16_hi(qv[h][j].x) - cb * bf16_hi(kv[j].x),
-                      ca * bf16_lo(qv[h][j].y) - cb * bf16_lo(kv[j].y), ca * bf16_hi(qv[h][j].y) - cb * bf16_hi(kv[j].y));
+      nt_store4(o + h * (D / 4) + sub + LPD * j, ca * bf16_lo(qv[h][j].x) - cb * bf16_lo(kv[j].x),
+                ca * bf16_hi(qv[h][j].x) - cb * bf16_hi(kv[j].x), ca * bf16_lo(qv[h][j].y) - cb * bf16_lo(kv[j].y),
+                ca * bf16_hi(qv[h][j].y) - cb * bf16_hi(kv[j].y));
     if (h == sub) { my_ikw = w * ik; my_wc = w * cs; }
   }
   if (sub < H) { ikw[bd * H + sub] = my_ikw; wcos[bd * H + sub] = my_wc; }
@@ -506,7 +513,7 @@ __device__ __forceinline__ void select8_group(const uint16_t* __restrict__ Qr, i
   float4* o = reinterpret_cast<float4*>(dK + bd * P_HD);
   if (tsel < 0) {
 #pragma unroll
-    for (int x = 0; x < P_HD / 4 / 16; ++x) o[sub + 16 * x] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int x = 0; x < P_HD / 4 / 16; ++x) nt_store4(o + sub + 16 * x, 0.f, 0.f, 0.f, 0.f);
     if (sub < H) { ikw[bd * H + sub] = 0.f; wcos[bd * H + sub] = 0.f; }
     return;
   }
@@ -550,11 +557,11 @@ __device__ __forceinline__ void select8_group(const uint16_t* __restrict__ Qr, i
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        o[(h0 + h) * (D / 4) + sub + 16 * j] =
-            make_float4(ca * bf16_lo(qv[h][j].x) - cb * bf16_lo(kv[h][j].x),
-                        ca * bf16_hi(qv[h][j].x) - cb * bf16_hi(kv[h][j].x),
-                        ca * bf16_lo(qv[h][j].y) - cb * bf16_lo(kv[h][j].y),
-                        ca * bf16_hi(qv[h][j].y) - cb * bf16_hi(kv[h][j].y));
+        nt_store4(o + (h0 + h) * (D / 4) + sub + 16 * j,
+                  ca * bf16_lo(qv[h][j].x) - cb * bf16_lo(kv[h][j].x),
+                  ca * bf16_hi(qv[h][j].x) - cb * bf16_hi(kv[h][j].x),
+                  ca * bf16_lo(qv[h][j].y) - cb * bf16_lo(kv[h][j].y),
+                  ca * bf16_hi(qv[h][j].y) - cb * bf16_hi(kv[h][j].y));
       if (h0 + h == sub) { my_ikw = w * ik; my_wc = w * cs; }
     }
   }
