@@ -265,18 +265,25 @@ topk_from_groups(const float* __restrict__ scores, const uint64_t* __restrict__ 
 // longer one by all waves and a merge; if phase A's list would overflow LDS
 // (adversarial score layouts), the unfiltered path runs instead.
 constexpr int LIST_CAP = 1024;
-constexpr int ONE_WAVE = 4;                   // keys per lane when one wave reduces the list
+constexpr int GPL = 4;                        // group maxima per lane loaded in one batch
+
+// A list of n <= RANK_MAX keys is reduced by ranking: 4 threads per key count the
+// keys above it (keys are unique, so the ranks are 0..n-1), and the key of rank r < k
+// goes to out[r]; out[n..63] are cleared.  Longer lists: waves + merge.
+constexpr int RANK_MAX = 16 * P2_WAVES;
 
 template <int RM>
 __device__ __forceinline__ void reduce_list(const uint64_t* list, int n, int k, uint64_t (*lists)[64], uint64_t* out,
                                             int wave, int lane) {
-  if (n <= 64 * ONE_WAVE) {                   // uniform branch: n is read from LDS after a barrier
-    if (wave == 0) {
-      uint64_t kv[ONE_WAVE];
-#pragma unroll
-      for (int j = 0; j < ONE_WAVE; ++j) kv[j] = j * 64 + lane < n ? list[j * 64 + lane] : 0ull;
-      out[lane] = wave_extract_topk<ONE_WAVE>(kv, k, lane);
-    }
+  if (n <= RANK_MAX) {                        // uniform branch: n is read from LDS after a barrier
+    const int t = threadIdx.x, i = t >> 2, part = t & 3;
+    const uint64_t key = i < n ? list[i] : 0ull;
+    int above = 0;
+    for (int j = part; j < n; j += 4) above += list[j] > key;
+    above += __shfl_xor(above, 1);
+    above += __shfl_xor(above, 2);
+    if (i < n && part == 0 && above < k) out[above] = key;
+    if (t >= n && t < 64) out[t] = 0ull;
     __syncthreads();
   } else {
     topk_by_waves<RM>(n, k, [&](int64_t x) { return list[x]; }, lists, out, wave, lane);
@@ -312,9 +319,21 @@ topk_from_groups_filtered(const float* __restrict__ scores, const uint64_t* __re
   const int64_t g0 = wave * per;
   const int64_t g1 = (g0 + per < n_groups) ? g0 + per : n_groups;
 
-  // A1: wave maxima, then T0 = the k-th largest of them (0 if fewer than k are non-empty)
+  // A1: wave maxima, then T0 = the k-th largest of them (0 if fewer than k are non-empty).
+  // Up to 64 * GPL group maxima per wave stay in registers for A2; the loads of a batch are
+  // issued together so their latencies overlap.
+  const bool in_regs = per <= 64 * GPL;
+  uint64_t gv[GPL];
   uint64_t lm = 0;
-  for (int64_t x = g0 + lane; x < g1; x += 64) lm = gm[x] > lm ? gm[x] : lm;
+  for (int64_t base = g0; base < g1; base += 64 * GPL) {
+#pragma unroll
+    for (int j = 0; j < GPL; ++j) {
+      const int64_t x = base + j * 64 + lane;
+      gv[j] = x < g1 ? gm[x] : 0ull;
+    }
+#pragma unroll
+    for (int j = 0; j < GPL; ++j) lm = gv[j] > lm ? gv[j] : lm;
+  }
   const uint64_t wm = wave_max_key(lm);
   if (lane == 0) wmax[wave] = wm;
   if (threadIdx.x == 0) { thresh = 0; count = 0; }
@@ -329,9 +348,20 @@ topk_from_groups_filtered(const float* __restrict__ scores, const uint64_t* __re
   __syncthreads();
   // A2: keys >= T0 into the list
   const uint64_t t0 = thresh;
-  for (int64_t base = g0; base < g1; base += 64) {
-    const int64_t x = base + lane;
-    append_ge(x < g1 ? gm[x] : 0ull, t0, list, &count, lane);
+  if (in_regs) {
+#pragma unroll
+    for (int j = 0; j < GPL; ++j)
+      if (g0 + j * 64 < g1) append_ge(gv[j], t0, list, &count, lane);
+  } else {
+    for (int64_t base = g0; base < g1; base += 64 * GPL) {
+#pragma unroll
+      for (int j = 0; j < GPL; ++j) {
+        const int64_t x = base + j * 64 + lane;
+        gv[j] = x < g1 ? gm[x] : 0ull;
+      }
+#pragma unroll
+      for (int j = 0; j < GPL; ++j) append_ge(gv[j], t0, list, &count, lane);
+    }
   }
   __syncthreads();
   const int na = count;
