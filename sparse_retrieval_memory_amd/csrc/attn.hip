@@ -112,8 +112,10 @@ attn_mfma_kernel(const uint16_t* __restrict__ Q, int Tq, int Hq, const uint16_t*
                  int rope_offset, const RopeTables tabs, float scale_log2e, float* __restrict__ O) {
   __shared__ double rev[D / 2];
   // cos/sin of positions rope_offset + p (p < n_local <= TAB_POS), frequency i: every query row
-  // and local key of this workgroup sits at such a position
-  __shared__ __attribute__((aligned(16))) float2 cs_tab[TAB_POS][D / 2];
+  // and local key of this workgroup sits at such a position.  Rows are padded by 16 bytes: the
+  // 32 lanes of a rotation read 32 consecutive positions at one frequency, which with 512-byte
+  // rows would all fall in the same four banks.
+  __shared__ __attribute__((aligned(16))) float2 cs_tab[TAB_POS][D / 2 + 2];
   // per wave: V^T of its current tile [D][VT_STRIDE] bf16; reused at the end for the merge
   __shared__ __attribute__((aligned(16))) float smem[NWAVE * RT * PART_STRIDE];
   static_assert(sizeof(smem) >= sizeof(uint16_t) * NWAVE * D * VT_STRIDE, "V^T area");
