@@ -67,7 +67,7 @@ def route_source_hash() -> str:
 def cpu_baseline(w, seconds: float):
     """Oracle route + top-k on a bounded slice of layer 0 (documents from the start)."""
     from oracle import msa_oracle as O
-    from synth import configs as C
+    from synth import workloads as C
     try:
         from threadpoolctl import threadpool_info
         cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
@@ -98,7 +98,7 @@ def route_only(w, n, dev):
     """One layer of the 100M-token store routed n times, after a 1 GiB device-to-device copy."""
     import torch
     from sparse_retrieval_memory_amd import ops
-    from synth import configs as C
+    from synth import workloads as C
     from synth import native
     from synth import splitmix as sm
     kr = torch.empty((w.n_chunks, w.H, w.D), dtype=torch.int16, device=dev)
@@ -179,8 +179,8 @@ def main():
                          "--route-only runs) to profiles/traffic_route_100M.json and exit; needs no GPU")
     args = ap.parse_args()
     if args.traffic_from:
-        from synth import configs as C
-        tr = traffic_from(args.traffic_from[0], args.traffic_from[1], C.config(4))
+        from synth import workloads as C
+        tr = traffic_from(args.traffic_from[0], args.traffic_from[1], C.workload("100M-18layer"))
         with open(TRAFFIC_FILE, "w") as f:
             json.dump(tr, f, indent=1)
         print(json.dumps({k: tr[k] for k in ("bytes_per_launch", "algorithmic_bytes_per_launch", "source_hash")}))
@@ -192,13 +192,13 @@ def main():
 
     import torch
     from sparse_retrieval_memory_amd import ops
-    from synth import configs as C
+    from synth import workloads as C
     from synth import native
     from synth import splitmix as sm
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = C.config(4)
+    w = C.workload("100M-18layer")
     if args.route_only:
         route_only(w, args.route_only, dev)
         return
@@ -386,7 +386,7 @@ def main():
 
     log("side measurements: host-fetch step, attention, top-k, gather done")
     # the 10M-token batch-16 scan: 16 queries x 64 tokens over 165K chunks (matrix-core bound)
-    w3 = C.config(3)
+    w3 = C.workload("10M-batch16")
     kr3 = torch.empty((w3.n_chunks, H, D), dtype=torch.int16, device=dev)
     native.fill_normal_bf16_device(kr3, w3.seed, sm.TID_KRBAR, 0, 0)
     for g, row in C.pooled_plants(w3, 0).items():
@@ -416,7 +416,7 @@ def main():
     log(f"10M batch-16 scan: {scan3_ms:.3f} ms")
     # pooling throughput, then the interleave workload's rounds (10M tokens, 4 queries, 3 rounds, top-8)
     from sparse_retrieval_memory_amd.interleave import Interleave
-    w5 = C.config(5)
+    w5 = C.workload("10M-interleave")
     E = w5.row_elems
     pooled5 = tuple(torch.empty((w5.n_chunks, H, D), dtype=torch.int16, device=dev) for _ in range(3))
     plants5 = C.raw_plants(w5)

@@ -4,4 +4,4 @@ Holds input generation only (counter-based SplitMix64 + an N(0,1) bf16 table,
 the five workloads and their planted needles/chains); none of the method's
 arithmetic lives here.
 """
-from . import splitmix, configs, native  # noqa: F401
+from . import splitmix, workloads, native  # noqa: F401

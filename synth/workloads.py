@@ -119,26 +119,28 @@ class Workload:
 
 
 # ------------------------------------------------------------------ workloads
-def config(i: int, seed: int | None = None, **over) -> Workload:
-    """Workload ``i`` (1..5) with the stated seed (default: seed = i)."""
-    s = i if seed is None else seed
-    if i == 1:
-        w = Workload("tiny-32K", s, 64, "const512", B=1, T=32, Tq=32, Tl=32, k=4,
-                     pooled="raw", plant="mean_raw", n_needles=1)
-    elif i == 2:
-        w = Workload("1M", s, 1000, "uniform256_1792", B=1, T=128, Tq=128, Tl=128, k=16,
-                     pooled="direct", plant="token", n_needles=10)
-    elif i == 3:
-        w = Workload("10M-batch16", s, 20000, "lognormal400", B=16, T=64, Tq=64, Tl=64, k=16,
-                     pooled="direct", plant="token", n_needles=16)
-    elif i == 4:
-        w = Workload("100M-18layer", s, 200000, "uniform64_936", B=1, T=128, Tq=128, Tl=128,
-                     k=16, n_layers=18, pooled="direct", plant="token", n_needles=10)
-    elif i == 5:
-        w = Workload("10M-interleave", s, 20000, "lognormal400", B=4, T=128, Tq=128, Tl=128,
-                     k=8, pooled="raw", plant="chain", n_needles=0, rounds=3)
-    else:
-        raise ValueError(i)
+# name -> (default seed, fields); the seeds are fixed so stored expected values stay valid
+_WORKLOADS = {
+    "tiny-32K": (1, dict(n_docs=64, length_law="const512", B=1, T=32, Tq=32, Tl=32, k=4,
+                         pooled="raw", plant="mean_raw", n_needles=1)),
+    "1M": (2, dict(n_docs=1000, length_law="uniform256_1792", B=1, T=128, Tq=128, Tl=128, k=16,
+                   pooled="direct", plant="token", n_needles=10)),
+    "10M-batch16": (3, dict(n_docs=20000, length_law="lognormal400", B=16, T=64, Tq=64, Tl=64, k=16,
+                            pooled="direct", plant="token", n_needles=16)),
+    "100M-18layer": (4, dict(n_docs=200000, length_law="uniform64_936", B=1, T=128, Tq=128, Tl=128,
+                             k=16, n_layers=18, pooled="direct", plant="token", n_needles=10)),
+    "10M-interleave": (5, dict(n_docs=20000, length_law="lognormal400", B=4, T=128, Tq=128, Tl=128,
+                               k=8, pooled="raw", plant="chain", n_needles=0, rounds=3)),
+}
+WORKLOAD_NAMES = tuple(_WORKLOADS)
+
+
+def workload(name: str, seed: int | None = None, **over) -> Workload:
+    """The named workload with its default seed (or ``seed``), fields overridden by ``over``."""
+    if name not in _WORKLOADS:
+        raise ValueError(f"unknown workload {name!r}; known: {', '.join(WORKLOAD_NAMES)}")
+    s0, fields = _WORKLOADS[name]
+    w = Workload(name, s0 if seed is None else seed, **fields)
     return dataclasses.replace(w, **over) if over else w
 
 

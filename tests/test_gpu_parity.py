@@ -11,7 +11,7 @@ import torch
 
 from oracle import msa_oracle as O
 from sparse_retrieval_memory_amd import ops
-from synth import configs as C
+from synth import workloads as C
 from synth import native
 from synth import splitmix as sm
 
@@ -287,7 +287,7 @@ def test_topk_score_layouts(pattern, n, k):
                                     (2, [300, 5, 64])])
 def test_pool_matches_oracle(H, lens):
     announce("pool", H, lens)
-    w = C.config(1, n_docs=len(lens), length_law="custom", custom_lengths=tuple(lens), H=H)
+    w = C.workload("tiny-32K", n_docs=len(lens), length_law="custom", custom_lengths=tuple(lens), H=H)
     K = C.raw_block(w, "K", 0, w.n_tok); V = C.raw_block(w, "V", 0, w.n_tok); Kr = C.raw_block(w, "Kr", 0, w.n_tok)
     Kb, Vb, Rb = ops.pool_chunks(dev_bits(K), dev_bits(V), dev_bits(Kr), torch.from_numpy(w.doc_tok_off).to(DEV),
                                  torch.from_numpy(w.doc_chunk_off).to(DEV), w.n_chunks, 64, w.rope_base)
@@ -301,7 +301,7 @@ def test_pool_matches_oracle(H, lens):
 def test_pool_slab_with_offset_bases():
     # a slab of documents 3..5 of a corpus: offsets rebased by the caller's first row
     lens = [100, 64, 1, 300, 65, 2]
-    w = C.config(1, n_docs=6, length_law="custom", custom_lengths=tuple(lens))
+    w = C.workload("tiny-32K", n_docs=6, length_law="custom", custom_lengths=tuple(lens))
     K = C.raw_block(w, "K", 0, w.n_tok); V = C.raw_block(w, "V", 0, w.n_tok); Kr = C.raw_block(w, "Kr", 0, w.n_tok)
     t0, t1 = int(w.doc_tok_off[3]), int(w.doc_tok_off[6])
     c0, c1 = int(w.doc_chunk_off[3]), int(w.doc_chunk_off[6])
@@ -552,10 +552,10 @@ def test_fetch_and_gather_assemble_rank_order():
 
 
 # ------------------------------------------------------------- end to end
-def test_cfg1_end_to_end_step():
+def test_tiny_corpus_end_to_end_step():
     """Pool raw K/V/Kr, route, top-k, fetch from pinned host, attend (Tq = T and Tq = 1)."""
-    w = C.config(1)
-    announce("cfg1 e2e", w.describe())
+    w = C.workload("tiny-32K")
+    announce("tiny-32K e2e", w.describe())
     K = C.raw_block(w, "K", 0, w.n_tok); V = C.raw_block(w, "V", 0, w.n_tok); Kr = C.raw_block(w, "Kr", 0, w.n_tok)
     q = C.queries(w)
     tok_off = torch.from_numpy(w.doc_tok_off).to(DEV); ch_off = torch.from_numpy(w.doc_chunk_off).to(DEV)

@@ -12,7 +12,7 @@ import torch
 
 from oracle import msa_oracle as O
 from sparse_retrieval_memory_amd import ops
-from synth import configs as C
+from synth import workloads as C
 from synth import native
 from synth import splitmix as sm
 
@@ -99,10 +99,10 @@ def check_attention(w, q, outs, gpu_idx, batches):
 
 
 # ------------------------------------------------------------------ 1M tokens
-def test_cfg2_full_step():
+def test_1M_corpus_full_step():
     """1,000 documents, 16.6K chunks, T = 128, k = 16: every score against the oracle."""
-    w = C.config(2)
-    announce("cfg2 full", w.describe())
+    w = C.workload("1M")
+    announce("1M full", w.describe())
     kr = device_krbar(w, 0)
     host_kr = C.krbar_block(w, 0, 0, w.n_chunks)
     q = C.queries(w)
@@ -123,13 +123,13 @@ def test_cfg2_full_step():
 
 
 # ----------------------------------------------------------------- 10M tokens
-def test_cfg3_full_route_sampled_queries():
+def test_10M_batch16_route_sampled_queries():
     """20,000 documents, 165K chunks, 16 queries x 64 tokens (the MFMA-bound shape).
 
     The GPU scores all 16 queries in one launch; the oracle checks every
     document of four of them (P2, P3) and the needles of all sixteen."""
-    w = C.config(3)
-    announce("cfg3 full", w.describe())
+    w = C.workload("10M-batch16")
+    announce("10M-batch16", w.describe())
     kr = device_krbar(w, 0)
     host_kr = f32(C.krbar_block(w, 0, 0, w.n_chunks))
     q = C.queries(w)
@@ -149,16 +149,16 @@ def test_cfg3_full_route_sampled_queries():
 
 
 # ---------------------------------------------------------------- 100M tokens
-def test_cfg4_layer_sampled_documents():
+def test_100M_layer_sampled_documents():
     """200,000 documents, 1.66M chunks (one routed layer of the 100M-token store).
 
     The oracle scores a sample of documents (needles, the GPU's selection,
     extremes, 2,000 random); P2 on all of them, and P3 in the form that holds
     for a sample: the GPU's k-th score is no lower than any sampled document
     outside its set (less the gap), and its selected scores are the oracle's."""
-    w = C.config(4)
+    w = C.workload("100M-18layer")
     layer = 3
-    announce("cfg4 layer", layer, w.describe())
+    announce("100M layer", layer, w.describe())
     kr = device_krbar(w, layer)
     q = C.queries(w, layer)
     off = torch.from_numpy(w.doc_chunk_off).to(DEV)
@@ -244,12 +244,12 @@ def interleave_on_gpu(w, pooled, q, fetch="gather"):
     return res
 
 
-def test_cfg5_interleave_reduced_against_oracle():
+def test_interleave_reduced_against_oracle():
     """300 documents of the interleave corpus: pooled on the GPU from raw tokens, then 3 rounds per query,
     every round against the oracle's own pooling and interleave loop."""
     from tests.parity import bf16_ulp_diff, host_bits, pooled_k_ok
-    w = C.config(5, n_docs=300)
-    announce("cfg5 reduced", w.describe())
+    w = C.workload("10M-interleave", n_docs=300)
+    announce("interleave reduced", w.describe())
     pooled = gpu_pool_corpus(w)
     K = O.bf16_to_f64(C.raw_block(w, "K", 0, w.n_tok)); V = O.bf16_to_f64(C.raw_block(w, "V", 0, w.n_tok))
     Kr = O.bf16_to_f64(C.raw_block(w, "Kr", 0, w.n_tok))
@@ -280,15 +280,15 @@ def test_cfg5_interleave_reduced_against_oracle():
         assert ch["A"] in res[0].top_idx[b] and ch["B"] in res[1].top_idx[b] and ch["C"] in res[2].top_idx[b]
 
 
-def test_cfg5_full_pool_and_interleave():
+def test_10M_interleave_full_pool_and_rounds():
     """The whole 10M-token interleave workload: pooled on the GPU in 1M-token slabs, 4 queries x 3 rounds.
 
     Pooled rows against the oracle's pooling on sampled documents (P1); round-1 and round-2 document
     scores against the oracle on sampled documents; every planted 3-hop chain recovered hop by hop;
     no document retrieved twice."""
     from tests.parity import bf16_ulp_diff, host_bits, pooled_k_ok
-    w = C.config(5)
-    announce("cfg5 full", w.describe())
+    w = C.workload("10M-interleave")
+    announce("10M interleave", w.describe())
     pooled = gpu_pool_corpus(w)
     q = C.queries(w)
     res = interleave_on_gpu(w, pooled, q)
@@ -333,7 +333,7 @@ def test_encode_router_keys_10M_slab_sampled_chunks():
     """Router-key encoding of the first ~1M-token slab of the 10M-token corpus (document-aligned,
     hidden states and projection drawn by the generator on the device), checked on sampled chunks
     against the oracle run on the same rows regenerated on the host."""
-    w = C.config(5)
+    w = C.workload("10M-interleave")
     H, D = w.H, w.D
     d1 = int(np.searchsorted(w.doc_tok_off, 1_000_000, side="right")) - 1
     t1, c1 = int(w.doc_tok_off[d1]), int(w.doc_chunk_off[d1])
@@ -369,7 +369,7 @@ def test_encode_router_keys_10M_slab_sampled_chunks():
 def test_store_delete_100M_layer_sampled():
     """Delete 10% of the documents of one 100M-token routing layer (1.66M chunks, with stored norms): offsets
     and new ids exact against the oracle, moved rows equal to their source rows on sampled documents."""
-    w = C.config(4)
+    w = C.workload("100M-18layer")
     announce("store-delete-100M", w.n_docs, w.n_chunks)
     kr = device_krbar(w, 0)
     nrm = ops.krbar_inv_norms(kr)
@@ -410,7 +410,7 @@ def test_route_backward_100M_layer_sampled():
     maximum otherwise, and the key gradient is the oracle's for that decision (P6).  On sampled
     tokens: every document that selected the token is checked the same way, and dQr is the
     oracle's sum over exactly those documents."""
-    w = C.config(4)
+    w = C.workload("100M-18layer")
     layer = 3
     announce("route-backward-100M", w.n_docs, w.n_chunks)
     kr = device_krbar(w, layer)

@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 
 from oracle import msa_oracle as O
-from synth import configs as C
+from synth import workloads as C
 
 
 def _bf(x):
@@ -23,8 +23,8 @@ def pooled_from_raw(w):
     return O.round_bf16(Kb), O.round_bf16(Vb), O.round_bf16(Rb)
 
 
-def test_cfg1_needle_retrieved():
-    w = C.config(1)
+def test_tiny_corpus_needle_retrieved():
+    w = C.workload("tiny-32K")
     Kb, Vb, Rb = pooled_from_raw(w)
     q = C.queries(w)
     ch, doc = O.route(_bf(q["Qr"]), Rb, w.doc_chunk_off)
@@ -34,8 +34,8 @@ def test_cfg1_needle_retrieved():
     assert doc[0, d] > 0.2 and np.sort(doc[0])[-2] < doc[0, d] - 0.05
 
 
-def test_cfg2_needles_retrieved():
-    w = C.config(2)
+def test_1M_corpus_needles_retrieved():
+    w = C.workload("1M")
     Rb = _bf(C.krbar_block(w, 0, 0, w.n_chunks))
     q = C.queries(w)
     ch, doc = O.route(_bf(q["Qr"]), Rb, w.doc_chunk_off)
@@ -45,8 +45,8 @@ def test_cfg2_needles_retrieved():
         assert doc[b, d] > 0.9
 
 
-def test_cfg3_shape_needles_retrieved_reduced():
-    w = C.config(3, n_docs=2000)
+def test_10M_batch16_shape_needles_retrieved_reduced():
+    w = C.workload("10M-batch16", n_docs=2000)
     Rb = _bf(C.krbar_block(w, 0, 0, w.n_chunks))
     q = C.queries(w)
     ch, doc = O.route(_bf(q["Qr"]), Rb, w.doc_chunk_off)
@@ -55,8 +55,8 @@ def test_cfg3_shape_needles_retrieved_reduced():
         assert idx[b, 0] == d
 
 
-def test_cfg5_chain_recovered_by_interleave_reduced():
-    w = C.config(5, n_docs=300)
+def test_interleave_chain_recovered_reduced():
+    w = C.workload("10M-interleave", n_docs=300)
     Kb, Vb, Rb = pooled_from_raw(w)
     q = C.queries(w)
     Qr, Q, Kl, Vl = (_bf(q[x]) for x in ("Qr", "Q", "Kloc", "Vloc"))

@@ -5,7 +5,7 @@ the workloads' stated shapes."""
 import numpy as np
 import pytest
 
-from synth import configs as C
+from synth import workloads as C
 from synth import native
 from synth import splitmix as sm
 
@@ -48,14 +48,14 @@ def test_uniform_int_range():
 
 
 def test_workload_shapes():
-    w1 = C.config(1)
+    w1 = C.workload("tiny-32K")
     assert (w1.n_docs, w1.n_tok, w1.n_chunks) == (64, 32768, 512)
-    w2 = C.config(2)
+    w2 = C.workload("1M")
     assert w2.doc_len.min() >= 256 and w2.doc_len.max() <= 1792 and abs(w2.n_tok - 1.0e6) < 0.1e6
-    w3 = C.config(3)
+    w3 = C.workload("10M-batch16")
     assert w3.doc_len.min() >= 64 and w3.doc_len.max() <= 8192
     assert abs(np.median(w3.doc_len) - 400) < 15 and abs(w3.n_tok - 1.0e7) < 0.5e6
-    w4 = C.config(4)
+    w4 = C.workload("100M-18layer")
     assert w4.doc_len.min() == 64 and w4.doc_len.max() == 936
     assert abs(w4.n_tok - 1.0e8) < 1e6 and w4.n_layers == 18
     # every document owns ceil(L/64) >= 1 chunks
@@ -64,7 +64,7 @@ def test_workload_shapes():
 
 
 def test_plants():
-    w2 = C.config(2)
+    w2 = C.workload("1M")
     nd = C.needles(w2)
     assert len(nd) == 10 and len({d for _, d, _, _ in nd}) == 10 and len({t for *_, t in nd}) == 10
     rows = C.pooled_plants(w2)
@@ -72,9 +72,9 @@ def test_plants():
     g = next(iter(rows))
     blk = C.krbar_block(w2, 0, g, g + 1)
     assert np.array_equal(blk[0], rows[g])
-    w3 = C.config(3)
+    w3 = C.workload("10M-batch16")
     assert sorted(b for b, *_ in C.needles(w3)) == list(range(16))
-    w5 = C.config(5, n_docs=400)
+    w5 = C.workload("10M-interleave", n_docs=400)
     ch = C.chains(w5)
     docs = [c[x] for c in ch for x in "ABC"]
     assert len(ch) == 4 and len(set(docs)) == 12
