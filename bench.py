@@ -134,7 +134,7 @@ def traffic_from(fetch_csv: str, write_csv: str, w) -> dict:
         for r in csv.DictReader(open(path)):
             if r["Counter_Name"] != counter:
                 continue
-            if "route_mfma_kernel<8, true>" in r["Kernel_Name"]:
+            if "route_mfma_kernel<8, true, " in r["Kernel_Name"]:
                 kern.append(float(r["Counter_Value"]))
             elif "copyBuffer" in r["Kernel_Name"]:
                 copy.append(float(r["Counter_Value"]))
@@ -146,7 +146,7 @@ def traffic_from(fetch_csv: str, write_csv: str, w) -> dict:
     fk, fc = read(fetch_csv, "FETCH_SIZE")
     wk, wc = read(write_csv, "WRITE_SIZE")
     fs, ws = copy_bytes / (fc * 1024), copy_bytes / (wc * 1024)
-    return {"kernel": "route_mfma_kernel<8, true> (stored norms)",
+    return {"kernel": "route_mfma_kernel<8, true, POL_NT> (stored norms, non-temporal copies)",
             "workload": f"100M-token memory, one routed layer ({w.n_chunks:,} chunks), batch 1, "
                         f"{w.B * w.T} router rows, stored norms",
             "source_hash": route_source_hash(),

@@ -136,8 +136,13 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 
 // Asynchronous 16-byte-per-lane global -> LDS copy.  The LDS destination of
 // lane i is lds_base + 16 * i (lds_base must be wave-uniform).
+// POL is the copy's cache policy: 0 = default, POL_NT = non-temporal (streamed data
+// that no other workgroup re-reads; on MI355X a stream of such copies reaches ~7.1 TB/s
+// against ~6.3 TB/s with the default policy).
+constexpr int POL_NT = 2;
+template <int POL = 0>
 __device__ __forceinline__ void dma16(const void* gptr, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(gptr, (lds_void_t*)lds_base, 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(gptr, (lds_void_t*)lds_base, 16, 0, POL);
 }
 
 }  // namespace msa

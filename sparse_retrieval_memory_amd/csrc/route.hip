@@ -112,7 +112,7 @@ __device__ __forceinline__ TileSrc tile_src(const uint8_t* __restrict__ kr, int6
 // each wave instruction moves 1 KB of contiguous global memory (half a chunk
 // row for H = 8) into the row's skewed LDS slot; for H <= 2 LDS slot j instead
 // holds piece (j % PIECES) ^ (n & 15) of chunk n = j / PIECES.
-template <int H>
+template <int H, int POL>
 __device__ __forceinline__ void issue_piece(const TileSrc& src, uint8_t* lds, int wave, int lane, int i) {
   using CF = Cfg<H>;
   const int slot0 = (i * CF::NWAVES + wave) * 64;     // wave-uniform
@@ -120,20 +120,20 @@ __device__ __forceinline__ void issue_piece(const TileSrc& src, uint8_t* lds, in
     const int n = slot0 / CF::PIECES;                 // one chunk per wave instruction: uniform
     const int ne = n < src.nmax ? n : src.nmax;
     const uint8_t* sb = src.base + ne * CF::ROW_BYTES + (slot0 % CF::PIECES) * 16;
-    dma16(sb + (uint32_t)lane * 16u, lds + n * CF::ROW_STRIDE + (slot0 % CF::PIECES) * 16);
+    dma16<POL>(sb + (uint32_t)lane * 16u, lds + n * CF::ROW_STRIDE + (slot0 % CF::PIECES) * 16);
   } else {
     const int n = (slot0 + lane) / CF::PIECES;
     const int pp = (slot0 + lane) % CF::PIECES;
     const int ne = n < src.nmax ? n : src.nmax;
     const uint32_t off = (uint32_t)((pp ^ (n & 15)) * 16);
-    dma16(src.base + ne * CF::ROW_BYTES + off, lds + slot0 * 16);
+    dma16<POL>(src.base + ne * CF::ROW_BYTES + off, lds + slot0 * 16);
   }
 }
 
 // With stored norms (H >= 4) the tile's fp32 [TC][H] block of 1/|k| goes into
 // `lds_rk` (one instruction of the last wave; 16-byte granules never straddle a
 // chunk boundary for H >= 4, so clamping is per chunk).
-template <int H>
+template <int H, int POL>
 __device__ __forceinline__ void issue_norms(const float* __restrict__ knorm, int64_t n_chunks, int64_t tile,
                                             float* lds_rk, int wave, int lane) {
   using CF = Cfg<H>;
@@ -145,24 +145,24 @@ __device__ __forceinline__ void issue_norms(const float* __restrict__ knorm, int
       const uint64_t base = (uint64_t)(knorm + tile * TC * H);
       const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
       const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
-      dma16((const uint8_t*)(((uint64_t)hi << 32) | lo) + (uint32_t)lane * 16u, lds_rk);
+      dma16<POL>((const uint8_t*)(((uint64_t)hi << 32) | lo) + (uint32_t)lane * 16u, lds_rk);
     } else {
       const int n = lane * 4 / H;
       const int64_t g = (tile * TC + n < n_chunks) ? tile * TC + n : n_chunks - 1;
-      dma16(knorm + g * H + (lane * 4) % H, lds_rk);
+      dma16<POL>(knorm + g * H + (lane * 4) % H, lds_rk);
     }
   }
 }
 
 // The whole tile (and its norms block) at once.
-template <int H, bool NORMS>
+template <int H, bool NORMS, int POL>
 __device__ __forceinline__ void issue_tile(const uint8_t* __restrict__ kr, const float* __restrict__ knorm,
                                            int64_t n_chunks, int64_t tile, uint8_t* lds, float* lds_rk,
                                            int wave, int lane) {
   const TileSrc src = tile_src<H>(kr, n_chunks, tile);
 #pragma unroll
-  for (int i = 0; i < Cfg<H>::DMA_ITERS; ++i) issue_piece<H>(src, lds, wave, lane, i);
-  if constexpr (NORMS) issue_norms<H>(knorm, n_chunks, tile, lds_rk, wave, lane);
+  for (int i = 0; i < Cfg<H>::DMA_ITERS; ++i) issue_piece<H, POL>(src, lds, wave, lane, i);
+  if constexpr (NORMS) issue_norms<H, POL>(knorm, n_chunks, tile, lds_rk, wave, lane);
 }
 
 // Token max of a finished 32-row x 32-chunk head sum, then the chunk's atomic max.
@@ -192,7 +192,7 @@ __device__ __forceinline__ void finish_tile(const f32x16_t& sacc, int half, int 
 // depend on the DMA into the other.  PAR is the tile's parity within the
 // workgroup's range: on even tiles head group 1 sends and group 0 finishes,
 // on odd tiles the other way round.
-template <int H, bool NORMS, int PAR>
+template <int H, bool NORMS, int PAR, int POL>
 __device__ __forceinline__ void mfma_tile_step(const uint8_t* __restrict__ kr, const float* __restrict__ knorm,
                                                int64_t n_chunks, int64_t tile, bool has_prev, bool has_next,
                                                const uint8_t* cur, const float* cur_rk, uint8_t* nxt, float* nxt_rk,
@@ -211,11 +211,11 @@ __device__ __forceinline__ void mfma_tile_step(const uint8_t* __restrict__ kr, c
   // instead of branching around every instruction.
   const TileSrc src = tile_src<H>(kr, n_chunks, has_next ? tile + 1 : tile);
   if constexpr (NORMS) {
-    if (has_next) issue_norms<H>(knorm, n_chunks, tile + 1, nxt_rk, wave, lane);
+    if (has_next) issue_norms<H, POL>(knorm, n_chunks, tile + 1, nxt_rk, wave, lane);
   }
   if (!wave_active) {
 #pragma unroll
-    for (int i = 0; i < CF::DMA_ITERS; ++i) issue_piece<H>(src, nxt, wave, lane, i);
+    for (int i = 0; i < CF::DMA_ITERS; ++i) issue_piece<H, POL>(src, nxt, wave, lane, i);
   }
 
   f32x4_t* x = xchg + lane;                   // layout [q4][lane]: 16-byte lane stride, conflict-free
@@ -255,7 +255,7 @@ __device__ __forceinline__ void mfma_tile_step(const uint8_t* __restrict__ kr, c
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[hh][k4 + ks], bv[ks], acc, 0, 0, 0);
         if constexpr (!NORMS) ss = sq_norm_piece(__builtin_bit_cast(uint4, bv[ks]), ss);
         const int mf = hh * 8 + k4 + ks;      // MFMA number within the step (compile time)
-        if (mf < CF::DMA_ITERS) issue_piece<H>(src, nxt, wave, lane, mf);
+        if (mf < CF::DMA_ITERS) issue_piece<H, POL>(src, nxt, wave, lane, mf);
       }
     }
   };
@@ -316,7 +316,7 @@ __device__ __forceinline__ void mfma_tile_step(const uint8_t* __restrict__ kr, c
   }
 }
 
-template <int H, bool NORMS>
+template <int H, bool NORMS, int POL>
 __global__ void __launch_bounds__(Cfg<H>::THREADS, 1)
 route_mfma_kernel(const uint16_t* __restrict__ Qr, int B, int T, int RTq, int P, int S,
                   const uint16_t* __restrict__ Krbar, const float* __restrict__ knorm, int64_t n_chunks,
@@ -385,14 +385,14 @@ route_mfma_kernel(const uint16_t* __restrict__ Qr, int B, int T, int RTq, int P,
   f32x16_t sprev;
 #pragma unroll
   for (int i = 0; i < 16; ++i) sprev[i] = 0.f;
-  issue_tile<H, NORMS>(kr, knorm, n_chunks, tile_begin, lds_a, rk_a, wave, lane);
+  issue_tile<H, NORMS, POL>(kr, knorm, n_chunks, tile_begin, lds_a, rk_a, wave, lane);
   int64_t tile = tile_begin;
   for (; tile < tile_end; tile += 2) {
-    mfma_tile_step<H, NORMS, 0>(kr, knorm, n_chunks, tile, tile > tile_begin, tile + 1 < tile_end, lds_a, rk_a,
+    mfma_tile_step<H, NORMS, 0, POL>(kr, knorm, n_chunks, tile, tile > tile_begin, tile + 1 < tile_end, lds_a, rk_a,
                                 lds_b, rk_b, lds_rq[rtl], lds_x[rtl], qf, sprev, wave_active, hs, b, t0, T,
                                 chunk_enc, wave, lane);
     if (tile + 1 < tile_end)
-      mfma_tile_step<H, NORMS, 1>(kr, knorm, n_chunks, tile + 1, true, tile + 2 < tile_end, lds_b, rk_b, lds_a,
+      mfma_tile_step<H, NORMS, 1, POL>(kr, knorm, n_chunks, tile + 1, true, tile + 2 < tile_end, lds_b, rk_b, lds_a,
                                   rk_a, lds_rq[rtl], lds_x[rtl], qf, sprev, wave_active, hs, b, t0, T,
                                   chunk_enc, wave, lane);
   }
@@ -631,16 +631,25 @@ int launch_route_h(const uint16_t* Qr, int B, int T, const uint16_t* Krbar, cons
     hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, chunk_enc, n, 0u);
   }
   MSA_CHECK_LAUNCH();
+  // A slice read by one row block is streamed once: its copies take the non-temporal
+  // policy.  Several row blocks of a slice share its lines in L2, so those keep the default.
+#define MSA_ROUTE_MFMA(NORMS_, POL_, KN_)                                                                    \
+  hipLaunchKernelGGL((route_mfma_kernel<H, NORMS_, POL_>), dim3((unsigned)grid), dim3(Cfg<H>::THREADS), 0, stream, \
+                     Qr, B, T, RTq, P, (int)S, Krbar, KN_, n_chunks, per, chunk_enc)
+  const bool stream_once = P == 1;
+  bool launched = false;
   if constexpr (H >= 4) {
     if (inv_norm) {
-      hipLaunchKernelGGL((route_mfma_kernel<H, true>), dim3((unsigned)grid), dim3(Cfg<H>::THREADS), 0, stream, Qr,
-                         B, T, RTq, P, (int)S, Krbar, inv_norm, n_chunks, per, chunk_enc);
-      MSA_CHECK_LAUNCH();
-      return MSA_OK;
+      if (stream_once) MSA_ROUTE_MFMA(true, POL_NT, inv_norm);
+      else MSA_ROUTE_MFMA(true, 0, inv_norm);
+      launched = true;
     }
   }
-  hipLaunchKernelGGL((route_mfma_kernel<H, false>), dim3((unsigned)grid), dim3(Cfg<H>::THREADS), 0, stream, Qr, B,
-                     T, RTq, P, (int)S, Krbar, (const float*)nullptr, n_chunks, per, chunk_enc);
+  if (!launched) {
+    if (stream_once) MSA_ROUTE_MFMA(false, POL_NT, (const float*)nullptr);
+    else MSA_ROUTE_MFMA(false, 0, (const float*)nullptr);
+  }
+#undef MSA_ROUTE_MFMA
   MSA_CHECK_LAUNCH();
   return MSA_OK;
 }

@@ -282,6 +282,38 @@ def test_topk_score_layouts(pattern, n, k):
     assert np.array_equal(sc.cpu().numpy().astype(np.float64), ref_sc)
 
 
+@pytest.mark.parametrize("n_s", [255, 256, 1023, 1024])
+@pytest.mark.parametrize("within", ["constant", "one_doc"])
+def test_topk_short_list_boundaries(n_s, within):
+    """The filtered path's short lists at their size limits (200,000 documents, k = 16).
+
+    Documents score -1 except: document 0 scores 0.5 (the smallest of the 16 waves'
+    maxima, so the first threshold is its key), and n_s groups spread over the other
+    waves' shares score 1.0 — every document of the group ("constant": the second list
+    then holds the 15 best groups' 64 documents + 1 = 961 keys) or its first document
+    only ("one_doc": 16 keys).  The first list holds n_s + 1 keys: 256 (ranked), 257
+    and 1,024 (reduced by waves), 1,025 (overflow: selection over every group maximum)."""
+    announce("topk list", n_s, within)
+    n, k = 200000, 16
+    n_groups = (n + 63) // 64
+    per = (n_groups + 15) // 16
+    s = np.full(n, -1.0, dtype=np.float32)
+    s[0] = 0.5
+    groups = np.unique(np.linspace(per, n_groups - 1, n_s).astype(np.int64))
+    assert len(groups) == n_s
+    for g in groups:
+        if within == "constant":
+            s[g * 64: min(n, g * 64 + 64)] = 1.0
+        else:
+            s[g * 64] = 1.0
+    s = s[None]
+    idx, sc = ops.topk_docs(torch.from_numpy(s).to(DEV), k)
+    torch.cuda.synchronize()
+    ref_idx, ref_sc = O.topk(s.astype(np.float64), k)
+    assert np.array_equal(idx.cpu().numpy(), ref_idx)
+    assert np.array_equal(sc.cpu().numpy().astype(np.float64), ref_sc)
+
+
 # ---------------------------------------------------------------------- pool
 @pytest.mark.parametrize("H,lens", [(8, [1, 63, 64, 65, 130, 512, 7, 200]), (4, [64, 3, 129]), (16, [70, 1]),
                                     (2, [300, 5, 64])])
