@@ -77,7 +77,7 @@ hidden_pool_kernel(const uint16_t* __restrict__ hidden, int64_t n_tok, int dm,
   for (; t + POOL_UNROLL <= cnt; t += POOL_UNROLL) {
     uint4 v[POOL_UNROLL];
 #pragma unroll
-    for (int u = 0; u < POOL_UNROLL; ++u) v[u] = *reinterpret_cast<const uint4*>(src + (int64_t)(t + u) * dm);
+    for (int u = 0; u < POOL_UNROLL; ++u) v[u] = load_nt16(src + (int64_t)(t + u) * dm);
 #pragma unroll
     for (int u = 0; u < POOL_UNROLL; ++u) {
       acc[0] += bf16_lo(v[u].x); acc[1] += bf16_hi(v[u].x);
@@ -87,7 +87,7 @@ hidden_pool_kernel(const uint16_t* __restrict__ hidden, int64_t n_tok, int dm,
     }
   }
   for (; t < cnt; ++t) {
-    const uint4 v = *reinterpret_cast<const uint4*>(src + (int64_t)t * dm);
+    const uint4 v = load_nt16(src + (int64_t)t * dm);
     acc[0] += bf16_lo(v.x); acc[1] += bf16_hi(v.x);
     acc[2] += bf16_lo(v.y); acc[3] += bf16_hi(v.y);
     acc[4] += bf16_lo(v.z); acc[5] += bf16_hi(v.z);

@@ -55,6 +55,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -143,6 +144,12 @@ constexpr int POL_NT = 2;
 template <int POL = 0>
 __device__ __forceinline__ void dma16(const void* gptr, void* lds_base) {
   __builtin_amdgcn_global_load_lds(gptr, (lds_void_t*)lds_base, 16, 0, POL);
+}
+
+// 16-byte vector load with the non-temporal policy, for data a kernel reads once.
+__device__ __forceinline__ uint4 load_nt16(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
 }  // namespace msa

@@ -93,12 +93,12 @@ pool_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, cons
     for (int tt = tq; tt < tn; tt += TOKPAR) {
       const int64_t r = row0 + t0 + tt;
       const int64_t base = (r * H + h) * D;
-      const uint4 k1 = *reinterpret_cast<const uint4*>(K + base + i0);
-      const uint4 k2 = *reinterpret_cast<const uint4*>(K + base + 64 + i0);
-      const uint4 v1 = *reinterpret_cast<const uint4*>(V + base + i0);
-      const uint4 v2 = *reinterpret_cast<const uint4*>(V + base + 64 + i0);
-      const uint4 r1 = *reinterpret_cast<const uint4*>(Kr + base + i0);
-      const uint4 r2 = *reinterpret_cast<const uint4*>(Kr + base + 64 + i0);
+      const uint4 k1 = load_nt16(K + base + i0);          // raw tokens are read once
+      const uint4 k2 = load_nt16(K + base + 64 + i0);
+      const uint4 v1 = load_nt16(V + base + i0);
+      const uint4 v2 = load_nt16(V + base + 64 + i0);
+      const uint4 r1 = load_nt16(Kr + base + i0);
+      const uint4 r2 = load_nt16(Kr + base + 64 + i0);
       const uint32_t kw1[4] = {k1.x, k1.y, k1.z, k1.w}, kw2[4] = {k2.x, k2.y, k2.z, k2.w};
       const uint32_t vw1[4] = {v1.x, v1.y, v1.z, v1.w}, vw2[4] = {v2.x, v2.y, v2.z, v2.w};
       const uint32_t rw1[4] = {r1.x, r1.y, r1.z, r1.w}, rw2[4] = {r2.x, r2.y, r2.z, r2.w};

@@ -7,7 +7,7 @@
 // HBM-resident Krbar store once per call (the only O(L) online step), so the
 // kernels are built around streaming it at HBM rate:
 //
-//  * MFMA path (rows = B*T > 15): each workgroup keeps 128 router rows
+//  * Every row count takes the matrix cores: each workgroup keeps 128 router rows
 //    resident in registers (8 waves: 4 row tiles of 32 x 2 head groups, bf16
 //    MFMA A operands) and streams tiles of 32 chunks (64 KB for 8 heads)
 //    through LDS with asynchronous global->LDS DMA, double buffered; chunk
@@ -19,9 +19,9 @@
 //    token max is a register max plus one cross-lane step, combined across
 //    waves/workgroups with an integer atomicMax on an order-preserving
 //    encoding (deterministic).
-//  * VALU path (rows <= 15): one thread per (chunk, head) holds that 256-byte
-//    slice in registers, dots it with every router row (LDS broadcast reads,
-//    v_dot2_f32_bf16), and a DPP butterfly sums the heads.
+//    With few rows the idle row tiles only issue copies, and the scan streams at
+//    the memory's rate (a VALU kernel with one thread per (chunk, head) was 1.1x
+//    to 3.4x slower for 1 to 15 rows and has been removed).
 //
 // Normalisation is applied in fp32 after the exact bf16 dot products instead
 // of rounding normalised vectors to bf16, which would move scores by ~1e-3.
@@ -37,7 +37,6 @@ constexpr int D = 128;
 constexpr int TC = 32;   // chunks per MFMA tile (MFMA N)
 constexpr int NW = 4;    // waves per MFMA workgroup
 constexpr int RW = 32;   // router rows per wave (MFMA M)
-constexpr int VALU_MAX_ROWS = 15;
 
 // p[0, n) = v; p is 16-byte aligned (the route workspace), so whole 16-byte stores
 // cover all but the last n % 4 words.
@@ -414,133 +413,6 @@ route_mfma_kernel(const uint16_t* __restrict__ Qr, int B, int T, int RTq, int P,
   wait_vmem_all();                            // the last step's copy lands before the LDS is released
 }
 
-// ------------------------------------------------------------------ VALU path
-template <int H>
-__device__ __forceinline__ float head_sum(float x) {
-  if (H >= 2) x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
-  if (H >= 4) x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
-  if (H >= 8) x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false));
-  return x;
-}
-
-// one 64 KB tile = (256 / H) chunks; thread tid owns (chunk tid / H, head tid % H)
-template <int H>
-__device__ __forceinline__ void issue_tile_valu(const uint8_t* __restrict__ kr, int64_t n_chunks,
-                                                int64_t tile, uint8_t* lds, int wave, int lane) {
-  constexpr int CPT = 256 / H;
-  constexpr int ROW = H * D * 2;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int slot0 = (i * NW + wave) * 64;
-    const int slot = slot0 + lane;
-    const int owner = slot >> 4;             // (chunk, head) pair = the thread that reads it
-    const int lp = (slot & 15) ^ (owner & 15);
-    const int n = owner / H, h = owner % H;
-    int64_t g = tile * CPT + n;
-    if (g >= n_chunks) g = n_chunks - 1;
-    dma16(kr + g * ROW + h * (D * 2) + lp * 16, lds + slot0 * 16);
-  }
-}
-
-template <int H>
-__device__ __forceinline__ void valu_tile_step(const uint8_t* __restrict__ kr, int64_t n_chunks, int64_t tile,
-                                               bool has_next, const uint8_t* cur, uint8_t* nxt,
-                                               const uint8_t* lds_q, const float (&rq)[VALU_MAX_ROWS], int B, int T,
-                                               uint32_t* chunk_enc, int tid, int wave, int lane) {
-  constexpr int CPT = 256 / H;
-  const int h = tid % H;
-  const int sw = tid & 15;
-  wait_vmem_all();
-  lds_barrier();
-  if (has_next) issue_tile_valu<H>(kr, n_chunks, tile + 1, nxt, wave, lane);
-
-  // this thread's (chunk, head) slice
-  uint4 kv[16];
-  const uint8_t* mine = cur + tid * 256;
-  float ss = 0.f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    kv[i] = *reinterpret_cast<const uint4*>(mine + ((i ^ sw) * 16));
-    ss = sq_norm_piece(kv[i], ss);
-  }
-  const float rk = inv_norm(ss);
-  const int64_t g = tile * CPT + tid / H;
-
-  const uint8_t* qh = lds_q + h * 256;
-  int r = 0;
-  for (int bq = 0; bq < B; ++bq) {
-    float best = -INFINITY;
-    for (int t = 0; t < T; ++t, ++r) {
-      const uint8_t* qrow = qh + r * H * 256;
-      float dot = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const uint4 qv = *reinterpret_cast<const uint4*>(qrow + ((i ^ h) & 15) * 16);
-        dot = dot2_bf16(qv.x, kv[i].x, dot);
-        dot = dot2_bf16(qv.y, kv[i].y, dot);
-        dot = dot2_bf16(qv.z, kv[i].z, dot);
-        dot = dot2_bf16(qv.w, kv[i].w, dot);
-      }
-      float rqr = rq[0];
-#pragma unroll
-      for (int rr = 1; rr < VALU_MAX_ROWS; ++rr) rqr = (r == rr) ? rq[rr] : rqr;
-      const float sc = head_sum<H>(dot * rk * rqr);
-      best = fmaxf(best, sc);
-    }
-    if (h == 0 && g < n_chunks) chunk_enc[(int64_t)bq * n_chunks + g] = enc_f32(best * (1.0f / H));
-  }
-}
-
-template <int H>
-__global__ void __launch_bounds__(256, 1)
-route_valu_kernel(const uint16_t* __restrict__ Qr, int B, int T,
-                  const uint16_t* __restrict__ Krbar, int64_t n_chunks, int64_t tiles_per_block,
-                  uint32_t* __restrict__ chunk_enc) {
-  constexpr int CPT = 256 / H;
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a[65536];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_b[65536];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_q[VALU_MAX_ROWS * H * D * 2];
-
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int h = tid % H;
-  const int R = B * T;
-
-  // stage the router rows: row r, head hh, piece i stored at piece i ^ hh
-  for (int x = tid; x < R * H * 16; x += 256) {
-    const int i = x & 15, hh = (x >> 4) % H, r = (x >> 4) / H;
-    const uint4 v = *reinterpret_cast<const uint4*>(Qr + ((int64_t)r * H + hh) * D + 8 * i);
-    *reinterpret_cast<uint4*>(lds_q + (((r * H + hh) * 16) + (i ^ (hh & 15))) * 16) = v;
-  }
-  // 1/|q| of every row for this thread's head
-  float rq[VALU_MAX_ROWS];
-#pragma unroll
-  for (int r = 0; r < VALU_MAX_ROWS; ++r) {
-    float ss = 0.f;
-    if (r < R) {
-      const uint16_t* q = Qr + ((int64_t)r * H + h) * D;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) ss = sq_norm_piece(*reinterpret_cast<const uint4*>(q + 8 * i), ss);
-    }
-    rq[r] = inv_norm(ss);
-  }
-
-  const int64_t n_tiles = (n_chunks + CPT - 1) / CPT;
-  const int64_t tile_begin = (int64_t)blockIdx.x * tiles_per_block;
-  int64_t tile_end = tile_begin + tiles_per_block;
-  if (tile_end > n_tiles) tile_end = n_tiles;
-  if (tile_begin >= tile_end) return;
-
-  const uint8_t* kr = reinterpret_cast<const uint8_t*>(Krbar);
-  issue_tile_valu<H>(kr, n_chunks, tile_begin, lds_a, wave, lane);
-  for (int64_t tile = tile_begin; tile < tile_end; tile += 2) {
-    valu_tile_step<H>(kr, n_chunks, tile, tile + 1 < tile_end, lds_a, lds_b, lds_q, rq, B, T, chunk_enc, tid,
-                      wave, lane);
-    if (tile + 1 < tile_end)
-      valu_tile_step<H>(kr, n_chunks, tile + 1, tile + 2 < tile_end, lds_b, lds_a, lds_q, rq, B, T, chunk_enc,
-                        tid, wave, lane);
-  }
-}
-
 // ------------------------------------------------------ stored key norms
 // 1/|Krbar[g, h]| for every chunk and head, fp32 [n_chunks, H].  Built once per
 // routing-key store (offline, beside the store) so the online scan needs no
@@ -599,20 +471,7 @@ int num_cus() {
 template <int H>
 int launch_route_h(const uint16_t* Qr, int B, int T, const uint16_t* Krbar, const float* inv_norm,
                    int64_t n_chunks, uint32_t* chunk_enc, hipStream_t stream) {
-  const int R = B * T;
   const int cus = num_cus();
-  if (R <= VALU_MAX_ROWS) {
-    constexpr int CPT = 256 / H;
-    const int64_t n_tiles = (n_chunks + CPT - 1) / CPT;
-    int64_t blocks = n_tiles < cus ? n_tiles : cus;
-    if (blocks < 1) blocks = 1;
-    const int64_t per = (n_tiles + blocks - 1) / blocks;
-    blocks = (n_tiles + per - 1) / per;
-    hipLaunchKernelGGL(route_valu_kernel<H>, dim3((unsigned)blocks), dim3(256), 0, stream, Qr, B, T,
-                       Krbar, n_chunks, per, chunk_enc);
-    MSA_CHECK_LAUNCH();
-    return MSA_OK;
-  }
   const int RTq = (T + RW - 1) / RW;
   const int P = (B * RTq + NW - 1) / NW;
   const int64_t n_tiles = (n_chunks + TC - 1) / TC;

@@ -114,10 +114,10 @@ def test_route_exclusion_and_zero_vectors():
         assert np.abs(ch - ref_ch).max() <= SCORE_TOL
 
 
-def test_route_valu_exclusion():
+def test_route_few_rows_exclusion():
     Qr, Kr, off = _route_case(1, 3, 8, n_docs=50, seed=6)
     excl = np.zeros((1, 50), bool); excl[0, ::7] = True
-    announce("route-valu-exclude")
+    announce("route-few-rows-exclude")
     doc, _ = _run_route(Qr, Kr, off, excl)
     _, ref_doc = O.route(f64(Qr), f64(Kr), off, excl)
     assert np.all(doc[excl] == -np.inf)
