@@ -353,6 +353,17 @@ def main():
     attn_bwd_us = 1e3 * time_ms(lambda: ops.sparse_attn_backward(Q[0], Kl[0], Vl[0], staging, staging[:, :, 1],
                                                                  2 * H * D, Mmax, ml_dev, k, d_out, w.rope_base,
                                                                  out=ab_out, ws=ws_ab), 50)
+    # the same backward given the forward's output and log-sum-exp (no statistics pass)
+    o_fw, lse_fw = ops.sparse_attn_forward(Q[0], Kl[0], Vl[0], staging, staging[:, :, 1], 2 * H * D, Mmax, ml_dev, k,
+                                           w.rope_base)
+    attn_bwd_saved_us = 1e3 * time_ms(lambda: ops.sparse_attn_backward(Q[0], Kl[0], Vl[0], staging,
+                                                                       staging[:, :, 1], 2 * H * D, Mmax, ml_dev, k,
+                                                                       d_out, w.rope_base, out=ab_out, ws=ws_ab,
+                                                                       O=o_fw, lse=lse_fw), 50)
+    attn_fwd_lse_us = 1e3 * time_ms(lambda: ops.sparse_attn_forward(Q[0], Kl[0], Vl[0], staging, staging[:, :, 1],
+                                                                    2 * H * D, Mmax, ml_dev, k, w.rope_base,
+                                                                    out=o_fw, lse=lse_fw), 50)
+    del o_fw, lse_fw
     n_mem = int(ml_dev.item())
     n_vis = w.Tq * n_mem + sum(w.Tl - w.Tq + i + 1 for i in range(w.Tq))      # visible (row, key) pairs per head
     attn_bwd_flops = 5 * 2.0 * n_vis * D * w.Hq                                  # S, dP, dV, dK, dQ
@@ -533,7 +544,8 @@ def main():
         "gather_us": gather_us,
         "attn_us": {"tq128": attn_us, "tq1_decode": decode_attn_us},
         "attn_backward_tq128": {"us": attn_bwd_us, "memory_entries": n_mem,
-                                "TFLOPs": attn_bwd_flops / (attn_bwd_us * 1e-6) / 1e12},
+                                "TFLOPs": attn_bwd_flops / (attn_bwd_us * 1e-6) / 1e12,
+                                "us_with_saved_stats": attn_bwd_saved_us, "forward_with_lse_us": attn_fwd_lse_us},
         "scan_10M_batch16": {"ms": scan3_ms, "TFLOPs": scan3_tflops,
                              "mfma_frac": scan3_tflops / MFMA_BF16_PEAK_TFLOPS,
                              "gemm_bf16_8192_TFLOPs": gemm_tflops,

@@ -18,7 +18,9 @@
  *   msa_gather_docs         online: same, as one device kernel reading mapped host memory
  *   msa_append_router_rows  interleave: the next round's router rows and exclusions
  *   msa_sparse_attn_decode  generation: GQA attention over [memory ++ local KV]
+ *   msa_sparse_attn_forward    training: the same attention, also returning each row's log-sum-exp
  *   msa_sparse_attn_backward   training: gradient of that attention (Q, local K/V, memory K/V)
+ *   msa_sparse_attn_backward_saved  the same gradient from the forward's saved output and log-sum-exp
  *
  * Conventions (every call):
  *   - Tensors are row-major with the last dimension contiguous.  bf16 tensors
@@ -373,6 +375,25 @@ int msa_sparse_attn_decode(const uint16_t* Q, int B, int Tq, int Hq, int D,
                            float* O, hipStream_t stream);
 
 /*
+ * msa_sparse_attn_forward -- msa_sparse_attn_decode that also returns each
+ * row's log-sum-exp, for training (msa_sparse_attn_backward_saved reuses it).
+ *
+ * Defined by: as msa_sparse_attn_decode; the log-sum-exp is the normaliser of
+ * the softmax there:
+ *   lse[b,i,h] = ln sum_{visible j} exp(scale * <q_i, k_j>)   (natural log)
+ *
+ *   arguments as msa_sparse_attn_decode, plus
+ *   lse         fp32 [B, Tq, Hq] out, 4-byte aligned; NULL skips it (then this
+ *               is msa_sparse_attn_decode)
+ */
+int msa_sparse_attn_forward(const uint16_t* Q, int B, int Tq, int Hq, int D,
+                            const uint16_t* Kloc, const uint16_t* Vloc, int Tl, int Hkv,
+                            const uint16_t* Kmem, const uint16_t* Vmem,
+                            int64_t mem_entry_stride, int Mmax, const int32_t* mem_len,
+                            int rope_offset, double rope_base, float scale,
+                            float* O, float* lse, hipStream_t stream);
+
+/*
  * msa_sparse_attn_backward -- gradient of msa_sparse_attn_decode.
  *
  * Defined by: chatpaper.ai Abstract (MSA is trained end to end, so the loss
@@ -408,6 +429,27 @@ int msa_sparse_attn_backward(const uint16_t* Q, int B, int Tq, int Hq, int D,
                              const float* dO, float* dQ, float* dKloc, float* dVloc,
                              float* dKmem, float* dVmem,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * msa_sparse_attn_backward_saved -- msa_sparse_attn_backward given the
+ * forward's output O and log-sum-exp (msa_sparse_attn_forward), which replace
+ * the pass that recomputes every row's softmax statistics:
+ *   rowsum(P * dO V^T) = rowsum(dO * O),  P = exp(S - lse).
+ * Same definition, arguments and outputs as msa_sparse_attn_backward, plus
+ *   O           fp32 [B, Tq, Hq, D], 16-byte aligned (the forward's output)
+ *   lse         fp32 [B, Tq, Hq], 4-byte aligned (its log-sum-exp)
+ * Both NULL: identical to msa_sparse_attn_backward; one of them NULL: error.
+ * The same workspace size applies.
+ */
+int msa_sparse_attn_backward_saved(const uint16_t* Q, int B, int Tq, int Hq, int D,
+                                   const uint16_t* Kloc, const uint16_t* Vloc, int Tl, int Hkv,
+                                   const uint16_t* Kmem, const uint16_t* Vmem,
+                                   int64_t mem_entry_stride, int Mmax, const int32_t* mem_len,
+                                   int rope_offset, double rope_base, float scale,
+                                   const float* dO, const float* O, const float* lse,
+                                   float* dQ, float* dKloc, float* dVloc,
+                                   float* dKmem, float* dVmem,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

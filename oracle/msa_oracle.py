@@ -360,6 +360,30 @@ def attend(Q, Kloc, Vloc, Kmem, Vmem, rope_offset: int, base: float, scale: floa
     return (O, P_all) if return_probs else O
 
 
+def attend_lse(Q, Kloc, Kmem, rope_offset: int, base: float, scale: float):
+    """Natural log-sum-exp of each row's visible scaled scores: the normaliser of
+    ``attend``'s softmax ([medium] sec. 2, [blab] sec. 1 and its Global RoPE bullet,
+    the same scores and visibility as ``attend``).  Returns [Tq, Hq] float64."""
+    Q = np.asarray(Q, dtype=np.float64)
+    Kloc = np.asarray(Kloc, dtype=np.float64)
+    Kmem = np.asarray(Kmem, dtype=np.float64).reshape(-1, Kloc.shape[1], Kloc.shape[2])
+    Tq, Hq, D = Q.shape
+    Tl, Hkv, _ = Kloc.shape
+    M = Kmem.shape[0]
+    group = Hq // Hkv
+    Qrot = rope(Q, (rope_offset + (Tl - Tq) + np.arange(Tq))[:, None], base)
+    Krot = rope(Kloc, (rope_offset + np.arange(Tl))[:, None], base)
+    visible = np.ones((Tq, M + Tl), dtype=bool)
+    visible[:, M:] = np.arange(Tl)[None, :] <= ((Tl - Tq) + np.arange(Tq))[:, None]
+    lse = np.empty((Tq, Hq))
+    for h in range(Hq):
+        keys = np.concatenate([Kmem[:, h // group], Krot[:, h // group]], axis=0)
+        logits = np.where(visible, (Qrot[:, h] @ keys.T) * scale, -np.inf)
+        mx = logits.max(axis=1)
+        lse[:, h] = mx + np.log(np.exp(logits - mx[:, None]).sum(axis=1))
+    return lse
+
+
 def attend_backward(Q, Kloc, Vloc, Kmem, Vmem, rope_offset: int, base: float, scale: float, dO):
     """Gradients of ``attend`` with respect to all five of its tensor inputs, given dL/dO.
 

@@ -319,6 +319,14 @@ int msa_sparse_attn_decode(const uint16_t* Q, int B, int Tq, int Hq, int D, cons
                            const uint16_t* Vloc, int Tl, int Hkv, const uint16_t* Kmem, const uint16_t* Vmem,
                            int64_t mem_entry_stride, int Mmax, const int32_t* mem_len, int rope_offset,
                            double rope_base, float scale, float* O, hipStream_t stream) {
+  return msa_sparse_attn_forward(Q, B, Tq, Hq, D, Kloc, Vloc, Tl, Hkv, Kmem, Vmem, mem_entry_stride, Mmax, mem_len,
+                                 rope_offset, rope_base, scale, O, nullptr, stream);
+}
+
+int msa_sparse_attn_forward(const uint16_t* Q, int B, int Tq, int Hq, int D, const uint16_t* Kloc,
+                            const uint16_t* Vloc, int Tl, int Hkv, const uint16_t* Kmem, const uint16_t* Vmem,
+                            int64_t mem_entry_stride, int Mmax, const int32_t* mem_len, int rope_offset,
+                            double rope_base, float scale, float* O, float* lse, hipStream_t stream) {
   msa::clear_error();
   MSA_CHECK_ARG(B >= 1 && B <= 65535 && Tq >= 1 && Tl >= Tq, "need B >= 1, 1 <= Tq <= Tl");
   MSA_CHECK_ARG(Hkv >= 1 && Hq >= Hkv && Hq % Hkv == 0 && Hq <= 65535, "need Hq %% Hkv == 0");
@@ -326,13 +334,14 @@ int msa_sparse_attn_decode(const uint16_t* Q, int B, int Tq, int Hq, int D, cons
   MSA_CHECK_SUPPORTED(Hkv <= 16, "Hkv=%d unsupported (<= 16)", Hkv);
   MSA_CHECK_ARG(Mmax >= 0 && rope_offset >= 0 && rope_base > 1.0, "need Mmax >= 0, rope_offset >= 0, base > 1");
   MSA_CHECK_ARG(Q && Kloc && Vloc && O && mem_len, "null pointer");
+  MSA_CHECK_ARG(((uintptr_t)lse & 3) == 0, "lse must be 4-byte aligned");
   MSA_CHECK_ARG(Mmax == 0 || (Kmem && Vmem && mem_entry_stride >= (int64_t)Hkv * D && mem_entry_stride % 8 == 0),
                 "memory pointers/stride invalid");
   MSA_CHECK_ARG(aligned16(Q) && aligned16(Kloc) && aligned16(Vloc) && aligned16(O) &&
                     (Mmax == 0 || (aligned16(Kmem) && aligned16(Vmem))),
                 "pointers must be 16-byte aligned");
   return msa::launch_attn(Q, B, Tq, Hq, Kloc, Vloc, Tl, Hkv, Kmem, Vmem, mem_entry_stride, Mmax, mem_len,
-                          rope_offset, rope_base, scale, O, stream);
+                          rope_offset, rope_base, scale, O, lse, stream);
 }
 
 size_t msa_sparse_attn_backward_workspace_bytes(int B, int Tq, int Hq, int D, int Tl, int Hkv, int Mmax) {
@@ -347,6 +356,17 @@ int msa_sparse_attn_backward(const uint16_t* Q, int B, int Tq, int Hq, int D, co
                              double rope_base, float scale, const float* dO, float* dQ, float* dKloc, float* dVloc,
                              float* dKmem, float* dVmem, void* workspace, size_t workspace_bytes,
                              hipStream_t stream) {
+  return msa_sparse_attn_backward_saved(Q, B, Tq, Hq, D, Kloc, Vloc, Tl, Hkv, Kmem, Vmem, mem_entry_stride, Mmax,
+                                        mem_len, rope_offset, rope_base, scale, dO, nullptr, nullptr, dQ, dKloc, dVloc,
+                                        dKmem, dVmem, workspace, workspace_bytes, stream);
+}
+
+int msa_sparse_attn_backward_saved(const uint16_t* Q, int B, int Tq, int Hq, int D, const uint16_t* Kloc,
+                                   const uint16_t* Vloc, int Tl, int Hkv, const uint16_t* Kmem, const uint16_t* Vmem,
+                                   int64_t mem_entry_stride, int Mmax, const int32_t* mem_len, int rope_offset,
+                                   double rope_base, float scale, const float* dO, const float* O, const float* lse,
+                                   float* dQ, float* dKloc, float* dVloc, float* dKmem, float* dVmem, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
   msa::clear_error();
   MSA_CHECK_ARG(B >= 1 && B <= 65535 && Tq >= 1 && Tl >= Tq, "need B >= 1, 1 <= Tq <= Tl");
   MSA_CHECK_ARG(Hkv >= 1 && Hq >= Hkv && Hq % Hkv == 0 && Hq <= 65535, "need Hq %% Hkv == 0");
@@ -362,6 +382,8 @@ int msa_sparse_attn_backward(const uint16_t* Q, int B, int Tq, int Hq, int D, co
                     aligned16(dKloc) && aligned16(dVloc) &&
                     (Mmax == 0 || (aligned16(Kmem) && aligned16(Vmem) && aligned16(dKmem) && aligned16(dVmem))),
                 "pointers must be 16-byte aligned");
+  MSA_CHECK_ARG((O == nullptr) == (lse == nullptr), "O and lse are given together or not at all");
+  MSA_CHECK_ARG(O == nullptr || (aligned16(O) && ((uintptr_t)lse & 3) == 0), "O must be 16-byte aligned, lse 4-byte");
   const size_t need = msa::attn_bwd_workspace(B, Tq, Hq, Tl, Hkv, Mmax);
   if (workspace_bytes < need || workspace == nullptr) {
     msa::set_error("workspace %zu bytes < required %zu", workspace_bytes, need);
@@ -369,7 +391,8 @@ int msa_sparse_attn_backward(const uint16_t* Q, int B, int Tq, int Hq, int D, co
   }
   MSA_CHECK_ARG(aligned16(workspace), "workspace must be 16-byte aligned");
   return msa::launch_attn_bwd(Q, B, Tq, Hq, Kloc, Vloc, Tl, Hkv, Kmem, Vmem, mem_entry_stride, Mmax, mem_len,
-                              rope_offset, rope_base, scale, dO, dQ, dKloc, dVloc, dKmem, dVmem, workspace, stream);
+                              rope_offset, rope_base, scale, dO, O, lse, dQ, dKloc, dVloc, dKmem, dVmem, workspace,
+                              stream);
 }
 
 }  // extern "C"

@@ -109,7 +109,8 @@ __global__ void __launch_bounds__(THREADS, 1)
 attn_mfma_kernel(const uint16_t* __restrict__ Q, int Tq, int Hq, const uint16_t* __restrict__ Kloc,
                  const uint16_t* __restrict__ Vloc, int Tl, int Hkv, const uint16_t* __restrict__ Kmem,
                  const uint16_t* __restrict__ Vmem, int64_t mstride, int Mmax, const int32_t* __restrict__ mem_len,
-                 int rope_offset, const RopeTables tabs, float scale_log2e, float* __restrict__ O) {
+                 int rope_offset, const RopeTables tabs, float scale_log2e, float* __restrict__ O,
+                 float* __restrict__ LSE) {
   __shared__ double rev[D / 2];
   // cos/sin of positions rope_offset + p (p < n_local <= TAB_POS), frequency i: every query row
   // and local key of this workgroup sits at such a position.  Rows are padded by 16 bytes: the
@@ -378,6 +379,9 @@ attn_mfma_kernel(const uint16_t* __restrict__ Q, int Tq, int Hq, const uint16_t*
 #pragma unroll
   for (int w = 0; w < NWAVE; ++w) lt += (m_sh[w][col] == -INFINITY) ? 0.f : l_sh[w][col] * exp2f(m_sh[w][col] - mx);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  // log-sum-exp of the row's scaled scores in natural units, for a backward that reuses it
+  if (LSE && wave == 0 && hf == 0 && r0 + col < Tq)
+    LSE[((int64_t)b * Tq + r0 + col) * Hq + h] = (mx + log2f(lt)) * 0.6931471805599453f;
   // scaled partial outputs through LDS (fp32 [wave][row][dims], rows skewed; in the V^T area):
   // accumulators i..i+3 of a dim tile are 4 consecutive dims, written as one 16-byte store
   float* part = smem;                                         // NWAVE x RT x PART_STRIDE floats
@@ -416,7 +420,7 @@ attn_mfma_kernel(const uint16_t* __restrict__ Q, int Tq, int Hq, const uint16_t*
 int launch_attn(const uint16_t* Q, int B, int Tq, int Hq, const uint16_t* Kloc, const uint16_t* Vloc,
                 int Tl, int Hkv, const uint16_t* Kmem, const uint16_t* Vmem, int64_t mem_entry_stride,
                 int Mmax, const int32_t* mem_len, int rope_offset, double rope_base, float scale,
-                float* O, hipStream_t stream) {
+                float* O, float* lse, hipStream_t stream) {
   dim3 grid((unsigned)((Tq + RT - 1) / RT), (unsigned)Hq, (unsigned)B);
   const float scale_log2e = scale * 1.4426950408889634f;
   // RoPE constants in fp64: angle of position p at frequency i in revolutions, reduced to
@@ -434,7 +438,7 @@ int launch_attn(const uint16_t* Q, int B, int Tq, int Hq, const uint16_t* Kloc, 
     tabs.step[i] = cs(1.0);
   }
   hipLaunchKernelGGL(attn_mfma_kernel, grid, dim3(THREADS), 0, stream, Q, Tq, Hq, Kloc, Vloc, Tl, Hkv, Kmem,
-                     Vmem, mem_entry_stride, Mmax, mem_len, rope_offset, tabs, scale_log2e, O);
+                     Vmem, mem_entry_stride, Mmax, mem_len, rope_offset, tabs, scale_log2e, O, lse);
   MSA_CHECK_LAUNCH();
   return MSA_OK;
 }

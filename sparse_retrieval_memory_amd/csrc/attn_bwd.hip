@@ -126,6 +126,8 @@ __device__ __forceinline__ uint4 tile_blk8(const uint16_t (*t)[TS], int r0, int 
 struct PrepArgs {
   const uint16_t *Q, *Kloc, *Vloc, *Kmem, *Vmem;
   const float* dO;
+  const float *O, *lse;   // the forward's output and natural log-sum-exp [B, Tq, Hq], or null
+  float *LSE2, *DLT;      // per-row statistics the gradient pass reads (written here when O is given)
   const int32_t* mem_len;
   int B, Tq, Tq32, Hq, Tl, Hkv, Mmax, NK, rope_offset;
   int64_t mstride;
@@ -139,7 +141,9 @@ __device__ __forceinline__ void prep_q_tile(const uint16_t* __restrict__ Q, cons
                                             uint16_t* __restrict__ QTh, uint16_t* __restrict__ QTl,
                                             uint16_t* __restrict__ Oh, uint16_t* __restrict__ Ol,
                                             uint16_t* __restrict__ OTh, uint16_t* __restrict__ OTl, int rt, int h,
-                                            int b, uint16_t (*tile)[32][TS]) {
+                                            int b, uint16_t (*tile)[32][TS], const float* __restrict__ Ofw,
+                                            const float* __restrict__ lse, float* __restrict__ LSE2,
+                                            float* __restrict__ DLT) {
   const int tid = threadIdx.x;
   const int r = tid >> 3, p0 = (tid & 7) * 8;                           // tile row, first pair
   const int i = rt * 32 + r;
@@ -157,6 +161,30 @@ __device__ __forceinline__ void prep_q_tile(const uint16_t* __restrict__ Q, cons
     o1[0] = a0.x; o1[1] = a0.y; o1[2] = a0.z; o1[3] = a0.w; o1[4] = a1.x; o1[5] = a1.y; o1[6] = a1.z; o1[7] = a1.w;
     o2[0] = b0.x; o2[1] = b0.y; o2[2] = b0.z; o2[3] = b0.w; o2[4] = b1.x; o2[5] = b1.y; o2[6] = b1.z; o2[7] = b1.w;
     rotate8(q1, q2, rope_offset + (Tl - Tq) + i, rr, p0);
+  }
+  // With the forward's output and log-sum-exp: Delta_i = sum_d dO_id O_id (= sum_j P_ij dP_ij)
+  // and the log2-sum-exp of the pre-scaled scores, so the statistics pass is not needed.
+  // The 8 threads of a row are consecutive lanes of one wave.
+  if (Ofw) {
+    float dl = 0.f;
+    if (i < Tq) {
+      const int64_t src = (((int64_t)b * Tq + i) * Hq + h) * D;
+      const float4 c0 = *reinterpret_cast<const float4*>(Ofw + src + p0);
+      const float4 c1 = *reinterpret_cast<const float4*>(Ofw + src + p0 + 4);
+      const float4 d0 = *reinterpret_cast<const float4*>(Ofw + src + 64 + p0);
+      const float4 d1 = *reinterpret_cast<const float4*>(Ofw + src + 64 + p0 + 4);
+      dl = o1[0] * c0.x + o1[1] * c0.y + o1[2] * c0.z + o1[3] * c0.w + o1[4] * c1.x + o1[5] * c1.y + o1[6] * c1.z +
+           o1[7] * c1.w + o2[0] * d0.x + o2[1] * d0.y + o2[2] * d0.z + o2[3] * d0.w + o2[4] * d1.x + o2[5] * d1.y +
+           o2[6] * d1.z + o2[7] * d1.w;
+    }
+    dl += __shfl_xor(dl, 1);
+    dl += __shfl_xor(dl, 2);
+    dl += __shfl_xor(dl, 4);
+    if ((tid & 7) == 0) {
+      const int64_t st = ((int64_t)b * Hq + h) * Tq32 + i;
+      DLT[st] = i < Tq ? dl : 0.f;
+      LSE2[st] = i < Tq ? lse[((int64_t)b * Tq + i) * Hq + h] * 1.4426950408889634f : INFINITY;   // padded rows: P = 0
+    }
   }
   bf16x8_t qh1, ql1, qh2, ql2, oh1, ol1, oh2, ol2;
   split8(q1, qh1, ql1);
@@ -261,7 +289,7 @@ bwd_prep_kernel(const PrepArgs A, const RopeRev rr) {
   if (id < n_q) {
     const int rt = (int)(id % n_rt), h = (int)(id / n_rt % A.Hq), b = (int)(id / ((int64_t)n_rt * A.Hq));
     prep_q_tile(A.Q, A.dO, A.Tq, A.Tq32, A.Hq, A.Tl, A.rope_offset, rr, A.Qh, A.Ql, A.QTh, A.QTl, A.Oh, A.Ol, A.OTh,
-                A.OTl, rt, h, b, tile);
+                A.OTl, rt, h, b, tile, A.O, A.lse, A.LSE2, A.DLT);
   } else {
     id -= n_q;
     const int kt = (int)(id % n_kt), g = (int)(id / n_kt % A.Hkv), b = (int)(id / ((int64_t)n_kt * A.Hkv));
@@ -739,8 +767,8 @@ size_t attn_bwd_workspace(int B, int Tq, int Hq, int Tl, int Hkv, int Mmax) {
 int launch_attn_bwd(const uint16_t* Q, int B, int Tq, int Hq, const uint16_t* Kloc, const uint16_t* Vloc, int Tl,
                     int Hkv, const uint16_t* Kmem, const uint16_t* Vmem, int64_t mem_entry_stride, int Mmax,
                     const int32_t* mem_len, int rope_offset, double rope_base, float scale, const float* dO,
-                    float* dQ, float* dKloc, float* dVloc, float* dKmem, float* dVmem, void* workspace,
-                    hipStream_t stream) {
+                    const float* O, const float* lse_saved, float* dQ, float* dKloc, float* dVloc, float* dKmem,
+                    float* dVmem, void* workspace, hipStream_t stream) {
   const BwdLayout L = layout(B, Tq, Hq, Tl, Hkv, Mmax);
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
   uint16_t* qa[8];
@@ -756,16 +784,20 @@ int launch_attn_bwd(const uint16_t* Q, int B, int Tq, int Hq, const uint16_t* Kl
   for (int i = 0; i < D / 2; ++i) rr.rev[i] = pow(rope_base, -2.0 * i / D) / two_pi;
   const float scale_log2e = scale * 1.4426950408889634f;
 
-  const PrepArgs pa{Q, Kloc, Vloc, Kmem, Vmem, dO, mem_len, B, Tq, L.Tq32, Hq, Tl, Hkv, Mmax, L.NK, rope_offset,
+  const bool saved = O && lse_saved;
+  const PrepArgs pa{Q, Kloc, Vloc, Kmem, Vmem, dO, saved ? O : nullptr, lse_saved, lse, dlt, mem_len, B, Tq, L.Tq32,
+                    Hq, Tl, Hkv, Mmax, L.NK, rope_offset,
                     mem_entry_stride, qa[0], qa[1], qa[2], qa[3], qa[4], qa[5], qa[6], qa[7], ka[0], ka[1], ka[2],
                     ka[3], ka[4], dKmem, dVmem};
   const int64_t n_prep = (int64_t)(L.Tq32 / 32) * Hq * B + (int64_t)(L.NK / 32) * Hkv * B;
   hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)n_prep), dim3(256), 0, stream, pa, rr);
   MSA_CHECK_LAUNCH();
   const Ops op{qa[0], qa[1], qa[2], qa[3], qa[4], qa[5], qa[6], qa[7], ka[0], ka[1], ka[2], ka[3], ka[4]};
-  hipLaunchKernelGGL(bwd_stats_kernel, dim3((unsigned)(L.Tq32 / 32), (unsigned)Hq, (unsigned)B), dim3(THREADS), 0,
-                     stream, op, mem_len, Tq, L.Tq32, Hq, Tl, Hkv, Mmax, L.NK, rope_offset, rr, scale_log2e, lse, dlt);
-  MSA_CHECK_LAUNCH();
+  if (!saved) {
+    hipLaunchKernelGGL(bwd_stats_kernel, dim3((unsigned)(L.Tq32 / 32), (unsigned)Hq, (unsigned)B), dim3(THREADS), 0,
+                       stream, op, mem_len, Tq, L.Tq32, Hq, Tl, Hkv, Mmax, L.NK, rope_offset, rr, scale_log2e, lse, dlt);
+    MSA_CHECK_LAUNCH();
+  }
   const int hpw = KV_HPW;
   const int64_t n_wg = (int64_t)(L.Tq32 / 32) * Hq * B + (int64_t)(L.NK / 32) * (Hq / hpw) * B;
   hipLaunchKernelGGL(bwd_grad_kernel, dim3((unsigned)n_wg), dim3(THREADS), 0, stream, op, mem_len, B, Tq, L.Tq32, Hq,

@@ -171,12 +171,12 @@ size_t topk_workspace(int B, int64_t n_docs, int k);
 int launch_attn(const uint16_t* Q, int B, int Tq, int Hq, const uint16_t* Kloc, const uint16_t* Vloc,
                 int Tl, int Hkv, const uint16_t* Kmem, const uint16_t* Vmem, int64_t mem_entry_stride,
                 int Mmax, const int32_t* mem_len, int rope_offset, double rope_base, float scale,
-                float* O, hipStream_t stream);
+                float* O, float* lse, hipStream_t stream);
 int launch_attn_bwd(const uint16_t* Q, int B, int Tq, int Hq, const uint16_t* Kloc, const uint16_t* Vloc, int Tl,
                     int Hkv, const uint16_t* Kmem, const uint16_t* Vmem, int64_t mem_entry_stride, int Mmax,
                     const int32_t* mem_len, int rope_offset, double rope_base, float scale, const float* dO,
-                    float* dQ, float* dKloc, float* dVloc, float* dKmem, float* dVmem, void* workspace,
-                    hipStream_t stream);
+                    const float* O, const float* lse, float* dQ, float* dKloc, float* dVloc, float* dKmem,
+                    float* dVmem, void* workspace, hipStream_t stream);
 size_t attn_bwd_workspace(int B, int Tq, int Hq, int Tl, int Hkv, int Mmax);
 int launch_append_rows(const uint16_t* Qr, int B, int T0, int H, const uint16_t* Krbar,
                        const int64_t* doc_chunk_off, int64_t n_docs, const int32_t* ids, int n_ids, int T_out,

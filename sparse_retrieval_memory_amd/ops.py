@@ -295,15 +295,38 @@ def sparse_attn_decode(Q, Kloc, Vloc, Kmem, Vmem, mem_entry_stride: int, Mmax: i
     return out
 
 
+def sparse_attn_forward(Q, Kloc, Vloc, Kmem, Vmem, mem_entry_stride: int, Mmax: int, mem_len,
+                        rope_offset: int, rope_base: float = 1.0e6, scale: Optional[float] = None,
+                        out=None, lse=None, stream=None):
+    """msa_sparse_attn_forward: (O fp32 [B, Tq, Hq, D], lse fp32 [B, Tq, Hq], natural log)."""
+    _bf16(Q, "Q"); _bf16(Kloc, "Kloc"); _bf16(Vloc, "Vloc")
+    B, Tq, Hq, D = Q.shape
+    _, Tl, Hkv, _ = Kloc.shape
+    if scale is None:
+        scale = D ** -0.5
+    if out is None:
+        out = torch.empty((B, Tq, Hq, D), dtype=torch.float32, device=Q.device)
+    if lse is None:
+        lse = torch.empty((B, Tq, Hq), dtype=torch.float32, device=Q.device)
+    assert lse.dtype == torch.float32 and lse.shape == (B, Tq, Hq) and lse.is_contiguous()
+    kp = Kmem.data_ptr() if Kmem is not None else 0
+    vp = Vmem.data_ptr() if Vmem is not None else 0
+    _lib.call("msa_sparse_attn_forward", _p(Q), B, Tq, Hq, D, _p(Kloc), _p(Vloc), Tl, Hkv, ctypes.c_void_p(kp),
+              ctypes.c_void_p(vp), mem_entry_stride, Mmax, _p(mem_len), rope_offset, float(rope_base),
+              float(scale), _p(out), _p(lse), _stream(stream))
+    return out, lse
+
+
 def attn_backward_workspace_bytes(B, Tq, Hq, D, Tl, Hkv, Mmax) -> int:
     return int(_lib.load().msa_sparse_attn_backward_workspace_bytes(B, Tq, Hq, D, Tl, Hkv, Mmax))
 
 
 def sparse_attn_backward(Q, Kloc, Vloc, Kmem, Vmem, mem_entry_stride: int, Mmax: int, mem_len, rope_offset: int,
                          dO, rope_base: float = 1.0e6, scale: Optional[float] = None, out=None, ws=None,
-                         stream=None):
+                         stream=None, O=None, lse=None):
     """msa_sparse_attn_backward: (dQ [B, Tq, Hq, D], dKloc, dVloc [B, Tl, Hkv, D], dKmem, dVmem [B, Mmax, Hkv, D]),
-    all fp32."""
+    all fp32.  With the forward's output O and log-sum-exp lse (sparse_attn_forward), calls
+    msa_sparse_attn_backward_saved, which reuses them instead of recomputing the softmax statistics."""
     _bf16(Q, "Q"); _bf16(Kloc, "Kloc"); _bf16(Vloc, "Vloc")
     B, Tq, Hq, D = Q.shape
     _, Tl, Hkv, _ = Kloc.shape
@@ -320,8 +343,17 @@ def sparse_attn_backward(Q, Kloc, Vloc, Kmem, Vmem, mem_entry_stride: int, Mmax:
         ws = workspace(need, dev, "attn_bwd")
     kp = Kmem.data_ptr() if Kmem is not None else 0
     vp = Vmem.data_ptr() if Vmem is not None else 0
-    _lib.call("msa_sparse_attn_backward", _p(Q), B, Tq, Hq, D, _p(Kloc), _p(Vloc), Tl, Hkv, ctypes.c_void_p(kp),
-              ctypes.c_void_p(vp), mem_entry_stride, Mmax, _p(mem_len), rope_offset, float(rope_base), float(scale),
-              _p(dO), _p(out[0]), _p(out[1]), _p(out[2]), _p(out[3]), _p(out[4]), _p(ws), ws.numel(),
-              _stream(stream))
+    if O is None and lse is None:
+        _lib.call("msa_sparse_attn_backward", _p(Q), B, Tq, Hq, D, _p(Kloc), _p(Vloc), Tl, Hkv,
+                  ctypes.c_void_p(kp), ctypes.c_void_p(vp), mem_entry_stride, Mmax, _p(mem_len), rope_offset,
+                  float(rope_base), float(scale), _p(dO), _p(out[0]), _p(out[1]), _p(out[2]), _p(out[3]),
+                  _p(out[4]), _p(ws), ws.numel(), _stream(stream))
+        return out
+    assert O is not None and lse is not None, "O and lse are given together"
+    assert O.dtype == torch.float32 and O.shape == (B, Tq, Hq, D) and O.is_contiguous()
+    assert lse.dtype == torch.float32 and lse.shape == (B, Tq, Hq) and lse.is_contiguous()
+    _lib.call("msa_sparse_attn_backward_saved", _p(Q), B, Tq, Hq, D, _p(Kloc), _p(Vloc), Tl, Hkv,
+              ctypes.c_void_p(kp), ctypes.c_void_p(vp), mem_entry_stride, Mmax, _p(mem_len), rope_offset,
+              float(rope_base), float(scale), _p(dO), _p(O), _p(lse), _p(out[0]), _p(out[1]), _p(out[2]),
+              _p(out[3]), _p(out[4]), _p(ws), ws.numel(), _stream(stream))
     return out

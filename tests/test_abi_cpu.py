@@ -20,7 +20,8 @@ def test_exports_every_declared_symbol():
             "msa_encode_workspace_bytes", "msa_store_delete", "msa_store_append",
             "msa_store_delete_workspace_bytes", "msa_route_scores_backward",
             "msa_route_backward_workspace_bytes", "msa_sparse_attn_backward",
-            "msa_sparse_attn_backward_workspace_bytes"} <= set(names)
+            "msa_sparse_attn_backward_workspace_bytes", "msa_sparse_attn_forward",
+            "msa_sparse_attn_backward_saved"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     assert set(_lib.SIGNATURES) == set(names)
@@ -75,6 +76,9 @@ def test_pool_and_attention_validation():
     assert _code("msa_sparse_attn_decode", *args(Tq=5)) == E.MSA_ERR_INVALID_ARG
     assert _code("msa_sparse_attn_decode", *args(Hq=30)) == E.MSA_ERR_INVALID_ARG
     assert _code("msa_sparse_attn_decode", *args(D=64)) == E.MSA_ERR_UNSUPPORTED
+    fw = lambda lse=p, **kw: (lambda a: a[:18] + (lse,) + a[18:])(args(**kw))      # + lse before the stream
+    assert _code("msa_sparse_attn_forward", *fw(Tq=5)) == E.MSA_ERR_INVALID_ARG
+    assert _code("msa_sparse_attn_forward", *fw(lse=ctypes.c_void_p((1 << 20) + 2))) == E.MSA_ERR_INVALID_ARG
 
 
 def test_encode_validation():
@@ -161,6 +165,14 @@ def test_attention_backward_validation():
     assert _code("msa_sparse_attn_backward", *bw(dq=ctypes.c_void_p((1 << 20) + 8))) == E.MSA_ERR_INVALID_ARG
     assert _code("msa_sparse_attn_backward", *bw(wsb=need - 1)) == E.MSA_ERR_WORKSPACE
     assert _code("msa_sparse_attn_backward", *bw(ws=N)) == E.MSA_ERR_WORKSPACE
+    # the saved-statistics variant: O and lse together or not at all, O 16-byte aligned, lse 4-byte
+    sv = lambda O=p, lse=p, **kw: (lambda a: a[:18] + (O, lse) + a[18:])(bw(**kw))
+    assert _code("msa_sparse_attn_backward_saved", *sv(O=N)) == E.MSA_ERR_INVALID_ARG
+    assert _code("msa_sparse_attn_backward_saved", *sv(lse=N)) == E.MSA_ERR_INVALID_ARG
+    assert _code("msa_sparse_attn_backward_saved", *sv(O=ctypes.c_void_p((1 << 20) + 4))) == E.MSA_ERR_INVALID_ARG
+    assert _code("msa_sparse_attn_backward_saved", *sv(lse=ctypes.c_void_p((1 << 20) + 2))) == E.MSA_ERR_INVALID_ARG
+    assert _code("msa_sparse_attn_backward_saved", *sv(Tl=99)) == E.MSA_ERR_INVALID_ARG
+    assert _code("msa_sparse_attn_backward_saved", *sv(wsb=need - 1)) == E.MSA_ERR_WORKSPACE
 
 
 def test_append_router_rows_validation():

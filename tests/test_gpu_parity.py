@@ -492,11 +492,17 @@ def _attn_bwd_case(B, Tq, Tl, M, offset, Hq=32, Hkv=8, seed=0):
     return Q, Kl, Vl, st, mem_len, dO, Mmax
 
 
-def _run_attn_bwd(Q, Kl, Vl, st, mem_len, dO, Mmax, offset):
+def _run_attn_bwd(Q, Kl, Vl, st, mem_len, dO, Mmax, offset, saved=False):
+    """The backward on the GPU; saved=True first runs the forward with its log-sum-exp and
+    hands (O, lse) to msa_sparse_attn_backward_saved."""
     stg = dev_bits(st)
-    out = ops.sparse_attn_backward(dev_bits(Q), dev_bits(Kl), dev_bits(Vl), stg, stg[:, :, 1], 2 * st.shape[-2] * 128,
-                                   Mmax, torch.from_numpy(mem_len).to(DEV), offset, torch.from_numpy(dO).to(DEV),
-                                   rope_base=1e6)
+    args = (dev_bits(Q), dev_bits(Kl), dev_bits(Vl), stg, stg[:, :, 1], 2 * st.shape[-2] * 128, Mmax,
+            torch.from_numpy(mem_len).to(DEV), offset)
+    kw = {}
+    if saved:
+        o, lse = ops.sparse_attn_forward(*args, rope_base=1e6)
+        kw = dict(O=o, lse=lse)
+    out = ops.sparse_attn_backward(*args, torch.from_numpy(dO).to(DEV), rope_base=1e6, **kw)
     torch.cuda.synchronize()
     return [t.cpu().numpy() for t in out]
 
@@ -507,10 +513,12 @@ def _run_attn_bwd(Q, Kl, Vl, st, mem_len, dO, Mmax, offset):
                                                      (3, 16, 16, 70, 8, 32, 8), (2, 1, 300, 5, 2, 32, 8),
                                                      (1, 100, 130, 45, 7, 32, 8), (1, 40, 50, 20, 5, 16, 2),
                                                      (1, 33, 33, 10, 0, 8, 8)])
-def test_attention_backward_matches_oracle(B, Tq, Tl, M, offset, Hq, Hkv):
-    announce("attn-backward", B, Tq, Tl, M, offset, Hq, Hkv)
+@pytest.mark.parametrize("saved", [False, True])
+def test_attention_backward_matches_oracle(B, Tq, Tl, M, offset, Hq, Hkv, saved):
+    """saved=True: msa_sparse_attn_backward_saved with the GPU forward's O and log-sum-exp."""
+    announce("attn-backward", B, Tq, Tl, M, offset, Hq, Hkv, "saved" if saved else "recomputed")
     Q, Kl, Vl, st, mem_len, dO, Mmax = _attn_bwd_case(B, Tq, Tl, M, offset, Hq, Hkv, seed=B * 1000 + Tq + M)
-    dQ, dKl, dVl, dKm, dVm = _run_attn_bwd(Q, Kl, Vl, st, mem_len, dO, Mmax, offset)
+    dQ, dKl, dVl, dKm, dVm = _run_attn_bwd(Q, Kl, Vl, st, mem_len, dO, Mmax, offset, saved=saved)
     worst = 0.0
     for b in range(B):
         m = int(mem_len[b])
@@ -525,6 +533,38 @@ def test_attention_backward_matches_oracle(B, Tq, Tl, M, offset, Hq, Hkv):
         assert np.all(dKm[b, m:] == 0) and np.all(dVm[b, m:] == 0)
     print("worst per-row relative error", worst, flush=True)
     assert worst <= ATT_GRAD_OBS
+
+
+# lse of the GPU forward against the oracle: scores carry ~2^-16 of sum_d |q_d k_d| * scale
+# (about 1e-4 for N(0,1) rows at D = 128), so the log-sum-exp is within 1e-3 absolute
+LSE_TOL = 1e-3
+
+
+@pytest.mark.parametrize("B,Tq,Tl,M,offset,Hq,Hkv", [(1, 128, 128, 262, 16, 32, 8), (2, 64, 64, 133, 16, 32, 8),
+                                                     (1, 1, 128, 262, 16, 32, 8), (1, 5, 9, 0, 0, 32, 8),
+                                                     (1, 100, 130, 45, 7, 32, 8), (1, 40, 50, 20, 5, 16, 2)])
+def test_attention_forward_lse_matches_oracle(B, Tq, Tl, M, offset, Hq, Hkv):
+    """msa_sparse_attn_forward: O as msa_sparse_attn_decode, and each row's natural log-sum-exp."""
+    announce("attn-forward-lse", B, Tq, Tl, M, offset, Hq, Hkv)
+    Q, Kl, Vl, st, mem_len, _, Mmax = _attn_bwd_case(B, Tq, Tl, M, offset, Hq, Hkv, seed=B * 500 + Tq + M)
+    stg = dev_bits(st)
+    args = (dev_bits(Q), dev_bits(Kl), dev_bits(Vl), stg, stg[:, :, 1], 2 * Hkv * 128, Mmax,
+            torch.from_numpy(mem_len).to(DEV), offset)
+    o, lse = ops.sparse_attn_forward(*args, rope_base=1e6)
+    o_dec = ops.sparse_attn_decode(*args, rope_base=1e6)
+    torch.cuda.synchronize()
+    o, lse, o_dec = o.cpu().numpy(), lse.cpu().numpy(), o_dec.cpu().numpy()
+    assert np.array_equal(o.view(np.uint32), o_dec.view(np.uint32))       # same kernel, same output
+    worst = 0.0
+    for b in range(B):
+        m = int(mem_len[b])
+        ref = O.attend_lse(f64(Q[b]), f64(Kl[b]), f64(st[b, :m, 0]), offset, 1e6, 128 ** -0.5)
+        worst = max(worst, float(np.abs(lse[b] - ref).max()))
+        ref_o = O.attend(f64(Q[b]), f64(Kl[b]), f64(Vl[b]), f64(st[b, :m, 0]), f64(st[b, :m, 1]), offset, 1e6,
+                         128 ** -0.5)
+        assert rel_rows(o[b], ref_o) <= ATT_TOL
+    print("worst lse error", worst, flush=True)
+    assert worst <= LSE_TOL
 
 
 @pytest.mark.parametrize("B,Tq,Tl,M,offset", [(1, 512, 1024, 700, 16), (2, 300, 300, 0, 0), (1, 1, 2000, 950, 8)])

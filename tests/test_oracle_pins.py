@@ -572,3 +572,37 @@ def test_attend_backward_gqa_and_memory_permutation():
         np.testing.assert_allclose(x, y, atol=1e-12)
     np.testing.assert_allclose(a[3][p], b[3], atol=1e-12)
     np.testing.assert_allclose(a[4][p], b[4], atol=1e-12)
+
+
+# ------------------------------------------------------------- attention log-sum-exp
+def test_attend_lse_single_key_is_the_scaled_score():
+    """One query row, one local key at the same position, no memory: the rotation
+    preserves the dot product, so lse = scale * <q, k> exactly (closed form)."""
+    r = np.random.default_rng(3)
+    q = r.standard_normal((1, 4, 128)); k = r.standard_normal((1, 2, 128))
+    lse = O.attend_lse(q, k, np.zeros((0, 2, 128)), 5, 1e6, 0.25)
+    for h in range(4):
+        assert abs(lse[0, h] - 0.25 * float(q[0, h] @ k[0, h // 2])) < 1e-12
+
+
+def test_attend_lse_equal_scores_is_log_count():
+    """Zero keys give equal scores, so lse of row i is ln(number of visible keys):
+    M memory entries + (Tl - Tq) + i + 1 local keys."""
+    Tq, Tl, M = 5, 9, 7
+    q = np.random.default_rng(4).standard_normal((Tq, 8, 128))
+    lse = O.attend_lse(q, np.zeros((Tl, 2, 128)), np.zeros((M, 2, 128)), 3, 1e6, 0.1)
+    for i in range(Tq):
+        assert np.allclose(lse[i], np.log(M + (Tl - Tq) + i + 1), rtol=0, atol=1e-13)
+
+
+def test_attend_lse_memory_and_causal_mask_closed_form():
+    """rope_offset 0, so row 0 and local key 0 sit at position 0 (no rotation):
+    with one memory entry m, row 0's lse = ln(exp(s*<q0,m>) + exp(s*<q0,k0>)) -- the
+    memory entry is visible and local key 1 is not (causal)."""
+    r = np.random.default_rng(6)
+    q = r.standard_normal((2, 2, 128)); kl = r.standard_normal((2, 1, 128)); km = r.standard_normal((1, 1, 128))
+    s_ = 0.05
+    lse = O.attend_lse(q, kl, km, 0, 1e6, s_)
+    for h in range(2):
+        a, b = s_ * float(q[0, h] @ km[0, 0]), s_ * float(q[0, h] @ kl[0, 0])
+        assert abs(lse[0, h] - np.logaddexp(a, b)) < 1e-12
