@@ -261,8 +261,8 @@ topk_from_groups(const float* __restrict__ scores, const uint64_t* __restrict__ 
 //   B: the k winning groups' best documents are k distinct documents with keys
 //      >= T1 = the k-th winning group's key, so the k best documents all have
 //      keys >= T1; those are appended to the list.
-// A list of at most 256 keys is reduced by one wave (k extraction rounds); a
-// longer one by all waves and a merge; if phase A's list would overflow LDS
+// A list of at most 256 keys is ranked in one step (reduce_list); a longer one
+// is reduced by all waves and a merge; if phase A's list would overflow LDS
 // (adversarial score layouts), the unfiltered path runs instead.
 constexpr int LIST_CAP = 1024;
 constexpr int GPL = 4;                        // group maxima per lane loaded in one batch
