@@ -18,6 +18,8 @@
  *   msa_gather_docs         online: same, as one device kernel reading mapped host memory
  *   msa_append_router_rows  interleave: the next round's router rows and exclusions
  *   msa_sparse_attn_decode  generation: GQA attention over [memory ++ local KV]
+ *   msa_sparse_attn_local_partial, msa_sparse_attn_memory_merge  the same attention in two launches
+ *                              (the local-key half needs nothing retrieved)
  *   msa_sparse_attn_forward    training: the same attention, also returning each row's log-sum-exp
  *   msa_sparse_attn_backward   training: gradient of that attention (Q, local K/V, memory K/V)
  *   msa_sparse_attn_backward_saved  the same gradient from the forward's saved output and log-sum-exp
@@ -392,6 +394,43 @@ int msa_sparse_attn_forward(const uint16_t* Q, int B, int Tq, int Hq, int D,
                             int64_t mem_entry_stride, int Mmax, const int32_t* mem_len,
                             int rope_offset, double rope_base, float scale,
                             float* O, float* lse, hipStream_t stream);
+
+/*
+ * msa_sparse_attn_local_partial / msa_sparse_attn_memory_merge -- the same
+ * attention as msa_sparse_attn_decode in two launches, so that the local-key
+ * half can run while the memory is still being selected and assembled.
+ *
+ * Defined by: as msa_sparse_attn_decode.  The softmax over [memory ++ local]
+ * splits exactly into two partial sums over the two key sets, each with its
+ * own running maximum, combined at the end:
+ *   local_partial:  m_L = max_j s_j,  l_L = sum_j 2^(s_j - m_L),
+ *                   part_O = sum_j 2^(s_j - m_L) v_j      (local keys j, visible)
+ *   memory_merge:   the same over the memory entries, then
+ *                   O = (2^(m_M - m) sum_M + 2^(m_L - m) part_O) / (2^(m_M - m) l_M + 2^(m_L - m) l_L),
+ *                   m = max(m_M, m_L)
+ * with s_j = scale * log2(e) * <q_i, k_j> (log2 units).  Query positions do not
+ * depend on the memory (rope_offset is the number of selected documents, known
+ * before selection), so the local partial needs only Q and the local K/V.
+ *
+ *   Q, Kloc, Vloc, Tl, Hkv, rope_offset, rope_base, scale: as msa_sparse_attn_decode
+ *   part_O      fp32 [B, Tq, Hq, D] (written by local_partial, read by memory_merge),
+ *               16-byte aligned
+ *   part_ml     fp32 [B, Tq, Hq, 2] = (m_L, l_L), 8-byte aligned
+ *   Kmem, Vmem, mem_entry_stride, Mmax, mem_len: as msa_sparse_attn_decode
+ *   O           fp32 [B, Tq, Hq, D] out; lse fp32 [B, Tq, Hq] out or NULL
+ *               (natural log, as msa_sparse_attn_forward)
+ * memory_merge must be ordered after local_partial on the caller's streams.
+ */
+int msa_sparse_attn_local_partial(const uint16_t* Q, int B, int Tq, int Hq, int D,
+                                  const uint16_t* Kloc, const uint16_t* Vloc, int Tl, int Hkv,
+                                  int rope_offset, double rope_base, float scale,
+                                  float* part_O, float* part_ml, hipStream_t stream);
+int msa_sparse_attn_memory_merge(const uint16_t* Q, int B, int Tq, int Hq, int D, int Tl, int Hkv,
+                                 const uint16_t* Kmem, const uint16_t* Vmem,
+                                 int64_t mem_entry_stride, int Mmax, const int32_t* mem_len,
+                                 int rope_offset, double rope_base, float scale,
+                                 const float* part_O, const float* part_ml,
+                                 float* O, float* lse, hipStream_t stream);
 
 /*
  * msa_sparse_attn_backward -- gradient of msa_sparse_attn_decode.

@@ -57,6 +57,10 @@ SIGNATURES = {
     "msa_append_router_rows": (c_i, [c_p, c_i, c_i, c_i, c_i, c_p, c_p, c_i64, c_p, c_i, c_i, c_p, c_p, c_p, c_p]),
     "msa_sparse_attn_decode": (c_i, [c_p, c_i, c_i, c_i, c_i, c_p, c_p, c_i, c_i, c_p, c_p, c_i64,
                                      c_i, c_p, c_i, c_d, c_f, c_p, c_p]),
+    "msa_sparse_attn_local_partial": (c_i, [c_p, c_i, c_i, c_i, c_i, c_p, c_p, c_i, c_i, c_i, c_d, c_f, c_p, c_p,
+                                            c_p]),
+    "msa_sparse_attn_memory_merge": (c_i, [c_p, c_i, c_i, c_i, c_i, c_i, c_i, c_p, c_p, c_i64, c_i, c_p, c_i, c_d,
+                                           c_f, c_p, c_p, c_p, c_p, c_p]),
     "msa_sparse_attn_forward": (c_i, [c_p, c_i, c_i, c_i, c_i, c_p, c_p, c_i, c_i, c_p, c_p, c_i64,
                                       c_i, c_p, c_i, c_d, c_f, c_p, c_p, c_p]),
     "msa_sparse_attn_backward_saved": (c_i, [c_p, c_i, c_i, c_i, c_i, c_p, c_p, c_i, c_i, c_p, c_p, c_i64, c_i,

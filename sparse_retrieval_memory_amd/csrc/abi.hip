@@ -1,6 +1,7 @@
 // C ABI entry points of libmsa: host-side argument validation, then the
 // launchers in the kernel sources.  Nothing is launched when validation fails.
 #include "msa_internal.h"
+#include "attn_split.h"
 
 #include <string.h>
 
@@ -342,6 +343,44 @@ int msa_sparse_attn_forward(const uint16_t* Q, int B, int Tq, int Hq, int D, con
                 "pointers must be 16-byte aligned");
   return msa::launch_attn(Q, B, Tq, Hq, Kloc, Vloc, Tl, Hkv, Kmem, Vmem, mem_entry_stride, Mmax, mem_len,
                           rope_offset, rope_base, scale, O, lse, stream);
+}
+
+int msa_sparse_attn_local_partial(const uint16_t* Q, int B, int Tq, int Hq, int D, const uint16_t* Kloc,
+                                  const uint16_t* Vloc, int Tl, int Hkv, int rope_offset, double rope_base,
+                                  float scale, float* part_O, float* part_ml, hipStream_t stream) {
+  msa::clear_error();
+  MSA_CHECK_ARG(B >= 1 && B <= 65535 && Tq >= 1 && Tl >= Tq, "need B >= 1, 1 <= Tq <= Tl");
+  MSA_CHECK_ARG(Hkv >= 1 && Hq >= Hkv && Hq % Hkv == 0 && Hq <= 65535, "need Hq %% Hkv == 0");
+  MSA_CHECK_SUPPORTED(D == 128, "D=%d unsupported (D must be 128)", D);
+  MSA_CHECK_SUPPORTED(Hkv <= 16, "Hkv=%d unsupported (<= 16)", Hkv);
+  MSA_CHECK_ARG(rope_offset >= 0 && rope_base > 1.0, "need rope_offset >= 0, base > 1");
+  MSA_CHECK_ARG(Q && Kloc && Vloc && part_O && part_ml, "null pointer");
+  MSA_CHECK_ARG(aligned16(Q) && aligned16(Kloc) && aligned16(Vloc) && aligned16(part_O) &&
+                    ((uintptr_t)part_ml & 7) == 0,
+                "Q, Kloc, Vloc, part_O must be 16-byte aligned, part_ml 8-byte");
+  return msa::launch_attn_local(Q, B, Tq, Hq, Kloc, Vloc, Tl, Hkv, rope_offset, rope_base, scale, part_O, part_ml,
+                                stream);
+}
+
+int msa_sparse_attn_memory_merge(const uint16_t* Q, int B, int Tq, int Hq, int D, int Tl, int Hkv,
+                                 const uint16_t* Kmem, const uint16_t* Vmem, int64_t mem_entry_stride, int Mmax,
+                                 const int32_t* mem_len, int rope_offset, double rope_base, float scale,
+                                 const float* part_O, const float* part_ml, float* O, float* lse,
+                                 hipStream_t stream) {
+  msa::clear_error();
+  MSA_CHECK_ARG(B >= 1 && B <= 65535 && Tq >= 1 && Tl >= Tq, "need B >= 1, 1 <= Tq <= Tl");
+  MSA_CHECK_ARG(Hkv >= 1 && Hq >= Hkv && Hq % Hkv == 0 && Hq <= 65535, "need Hq %% Hkv == 0");
+  MSA_CHECK_SUPPORTED(D == 128, "D=%d unsupported (D must be 128)", D);
+  MSA_CHECK_SUPPORTED(Hkv <= 16, "Hkv=%d unsupported (<= 16)", Hkv);
+  MSA_CHECK_ARG(Mmax >= 0 && rope_offset >= 0 && rope_base > 1.0, "need Mmax >= 0, rope_offset >= 0, base > 1");
+  MSA_CHECK_ARG(Q && O && mem_len && part_O && part_ml, "null pointer");
+  MSA_CHECK_ARG(Mmax == 0 || (Kmem && Vmem && mem_entry_stride >= (int64_t)Hkv * D && mem_entry_stride % 8 == 0),
+                "memory pointers/stride invalid");
+  MSA_CHECK_ARG(aligned16(Q) && aligned16(O) && aligned16(part_O) && ((uintptr_t)part_ml & 7) == 0 &&
+                    ((uintptr_t)lse & 3) == 0 && (Mmax == 0 || (aligned16(Kmem) && aligned16(Vmem))),
+                "pointers misaligned (16 bytes; part_ml 8, lse 4)");
+  return msa::launch_attn_memory(Q, B, Tq, Hq, Tl, Hkv, Kmem, Vmem, mem_entry_stride, Mmax, mem_len, rope_offset,
+                                 rope_base, scale, part_O, part_ml, O, lse, stream);
 }
 
 size_t msa_sparse_attn_backward_workspace_bytes(int B, int Tq, int Hq, int D, int Tl, int Hkv, int Mmax) {

@@ -24,6 +24,7 @@
 // and local keys read.  Scores are pre-scaled by scale * log2(e) so the
 // exponentials are exp2.
 #include "msa_internal.h"
+#include "attn_split.h"
 
 #include <math.h>
 
@@ -93,6 +94,13 @@ __device__ __forceinline__ void rotate_pairs_tab(float (&lo)[8], float (&hi)[8],
 }
 
 constexpr int TAB_POS = 128;    // positions the LDS cos/sin table covers (local keys and queries)
+// Which keys a launch covers and what it writes:
+//   FULL   memory entries ++ local keys; O (and optionally the log-sum-exp)
+//   LOCAL  local keys only; the unnormalised partial sum, its row max and sum (PO, PML)
+//   MEMORY memory entries only, merged with a LOCAL partial; O (and optionally the log-sum-exp)
+// LOCAL needs nothing retrieved, so it can run while the memory is still being selected and
+// assembled; LOCAL + MEMORY give the same O as FULL up to the order of the sums.
+constexpr int MODE_FULL = 0, MODE_LOCAL = 1, MODE_MEMORY = 2;
 constexpr int TAB_SEG = 32;     // positions one thread steps through from an exact start
 constexpr int PART_STRIDE = D + 4;   // floats per (wave, row) in the merge area: 16-byte rows skewed by 4 banks
 
@@ -110,7 +118,7 @@ attn_mfma_kernel(const uint16_t* __restrict__ Q, int Tq, int Hq, const uint16_t*
                  const uint16_t* __restrict__ Vloc, int Tl, int Hkv, const uint16_t* __restrict__ Kmem,
                  const uint16_t* __restrict__ Vmem, int64_t mstride, int Mmax, const int32_t* __restrict__ mem_len,
                  int rope_offset, const RopeTables tabs, float scale_log2e, float* __restrict__ O,
-                 float* __restrict__ LSE) {
+                 float* __restrict__ LSE, int mode, float* __restrict__ PO, float* __restrict__ PML) {
   __shared__ double rev[D / 2];
   // cos/sin of positions rope_offset + p (p < n_local <= TAB_POS), frequency i: every query row
   // and local key of this workgroup sits at such a position.  Rows are padded by 16 bytes: the
@@ -129,12 +137,13 @@ attn_mfma_kernel(const uint16_t* __restrict__ Q, int Tq, int Hq, const uint16_t*
   const int h = blockIdx.y;
   const int b = blockIdx.z;
   const int g = h / (Hq / Hkv);
-  int M = mem_len[b];
+  int M = mode == MODE_LOCAL ? 0 : mem_len[b];
   if (M < 0) M = 0;
   if (M > Mmax) M = Mmax;
   int last = r0 + RT - 1;
   if (last > Tq - 1) last = Tq - 1;
-  const int n_local = (Tl - Tq) + last + 1;
+  const int n_pos = (Tl - Tq) + last + 1;          // positions of this tile's rows and their local keys
+  const int n_local = mode == MODE_MEMORY ? 0 : n_pos;
   const int n_keys = M + n_local;
   const int n_tiles = (n_keys + KT - 1) / KT;
 
@@ -177,7 +186,7 @@ attn_mfma_kernel(const uint16_t* __restrict__ Q, int Tq, int Hq, const uint16_t*
   bool lc = false;
   if (wave < n_tiles) load_tile(wave, kc, vc, lc);
 
-  const bool use_tab = n_local <= TAB_POS;
+  const bool use_tab = n_pos <= TAB_POS;
   if (!use_tab && tid < D / 2) rev[tid] = tabs.rev[tid];
   // Table for n_local <= TAB_POS: thread (frequency i, segment sg) starts from the exact angle at the
   // segment's first position and steps by the exact one-position rotation (error ~1e-6 after 32 steps).
@@ -185,11 +194,11 @@ attn_mfma_kernel(const uint16_t* __restrict__ Q, int Tq, int Hq, const uint16_t*
     const int i = tid & (D / 2 - 1), sg = tid / (D / 2);
     static_assert(THREADS / (D / 2) * TAB_SEG == TAB_POS, "one segment per thread covers the table");
     const int p0 = sg * TAB_SEG;
-    if (p0 < n_local) {
+    if (p0 < n_pos) {
       const float2 st = tabs.start[sg][i], d1 = tabs.step[i];
       float c = st.x, s_ = st.y;
       const float cd = d1.x, sd = d1.y;
-      const int p1 = p0 + TAB_SEG < n_local ? p0 + TAB_SEG : n_local;
+      const int p1 = p0 + TAB_SEG < n_pos ? p0 + TAB_SEG : n_pos;
       for (int p = p0; p < p1; ++p) {
         cs_tab[p][i] = make_float2(c, s_);
         const float cn = c * cd - s_ * sd;
@@ -380,12 +389,12 @@ attn_mfma_kernel(const uint16_t* __restrict__ Q, int Tq, int Hq, const uint16_t*
   for (int w = 0; w < NWAVE; ++w) lt += (m_sh[w][col] == -INFINITY) ? 0.f : l_sh[w][col] * exp2f(m_sh[w][col] - mx);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   // log-sum-exp of the row's scaled scores in natural units, for a backward that reuses it
-  if (LSE && wave == 0 && hf == 0 && r0 + col < Tq)
+  if (LSE && mode == MODE_FULL && wave == 0 && hf == 0 && r0 + col < Tq)
     LSE[((int64_t)b * Tq + r0 + col) * Hq + h] = (mx + log2f(lt)) * 0.6931471805599453f;
   // scaled partial outputs through LDS (fp32 [wave][row][dims], rows skewed; in the V^T area):
   // accumulators i..i+3 of a dim tile are 4 consecutive dims, written as one 16-byte store
   float* part = smem;                                         // NWAVE x RT x PART_STRIDE floats
-  const float sc = wscale * inv;
+  const float sc = mode == MODE_FULL ? wscale * inv : wscale;   // partial modes stay unnormalised
   __syncthreads();
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
@@ -401,7 +410,29 @@ attn_mfma_kernel(const uint16_t* __restrict__ Q, int Tq, int Hq, const uint16_t*
   for (int x = tid; x < RT * (D / 16); x += THREADS) {
     const int row_ = x / (D / 16), d0 = (x % (D / 16)) * 16;
     if (r0 + row_ >= Tq) continue;
-    float* out = O + (((int64_t)b * Tq + r0 + row_) * Hq + h) * D + d0;
+    const int64_t ri = ((int64_t)b * Tq + r0 + row_) * Hq + h;     // (query, row, q-head)
+    float* out = O + ri * D + d0;
+    // partial modes: the row's merged max (log2 units of the pre-scaled scores) and sum
+    float mxr = -INFINITY, ltr = 0.f;
+    if (mode != MODE_FULL) {
+#pragma unroll
+      for (int w = 0; w < NWAVE; ++w) mxr = fmaxf(mxr, m_sh[w][row_]);
+#pragma unroll
+      for (int w = 0; w < NWAVE; ++w) ltr += (m_sh[w][row_] == -INFINITY) ? 0.f : l_sh[w][row_] * exp2f(m_sh[w][row_] - mxr);
+    }
+    // MEMORY: weights of this launch's sum and of the LOCAL partial (whose max is finite: every
+    // row sees at least one local key)
+    float a = 1.f, c = 0.f, rden = 1.f;
+    if (mode == MODE_MEMORY) {
+      const float ml = PML[2 * ri], ll = PML[2 * ri + 1];
+      const float mt = fmaxf(mxr, ml);
+      a = mxr == -INFINITY ? 0.f : exp2f(mxr - mt);
+      c = exp2f(ml - mt);
+      const float den = a * ltr + c * ll;
+      rden = 1.f / den;
+      if (LSE && d0 == 0) LSE[ri] = (mt + log2f(den)) * 0.6931471805599453f;
+    }
+    if (mode == MODE_LOCAL && d0 == 0) { PML[2 * ri] = mxr; PML[2 * ri + 1] = ltr; }
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -410,17 +441,27 @@ attn_mfma_kernel(const uint16_t* __restrict__ Q, int Tq, int Hq, const uint16_t*
         const float4 v = *reinterpret_cast<const float4*>(&part[(w * RT + row_) * PART_STRIDE + d0 + 4 * q4]);
         acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
       }
-      *reinterpret_cast<float4*>(out + 4 * q4) = acc;
+      if (mode == MODE_LOCAL) {
+        *reinterpret_cast<float4*>(PO + ri * D + d0 + 4 * q4) = acc;
+      } else {
+        if (mode == MODE_MEMORY) {
+          const float4 pl = *reinterpret_cast<const float4*>(PO + ri * D + d0 + 4 * q4);
+          acc.x = (a * acc.x + c * pl.x) * rden; acc.y = (a * acc.y + c * pl.y) * rden;
+          acc.z = (a * acc.z + c * pl.z) * rden; acc.w = (a * acc.w + c * pl.w) * rden;
+        }
+        *reinterpret_cast<float4*>(out + 4 * q4) = acc;
+      }
     }
   }
 }
 
 }  // namespace
 
-int launch_attn(const uint16_t* Q, int B, int Tq, int Hq, const uint16_t* Kloc, const uint16_t* Vloc,
-                int Tl, int Hkv, const uint16_t* Kmem, const uint16_t* Vmem, int64_t mem_entry_stride,
-                int Mmax, const int32_t* mem_len, int rope_offset, double rope_base, float scale,
-                float* O, float* lse, hipStream_t stream) {
+namespace {
+int launch_attn_mode(const uint16_t* Q, int B, int Tq, int Hq, const uint16_t* Kloc, const uint16_t* Vloc,
+                     int Tl, int Hkv, const uint16_t* Kmem, const uint16_t* Vmem, int64_t mem_entry_stride,
+                     int Mmax, const int32_t* mem_len, int rope_offset, double rope_base, float scale,
+                     float* O, float* lse, int mode, float* PO, float* PML, hipStream_t stream) {
   dim3 grid((unsigned)((Tq + RT - 1) / RT), (unsigned)Hq, (unsigned)B);
   const float scale_log2e = scale * 1.4426950408889634f;
   // RoPE constants in fp64: angle of position p at frequency i in revolutions, reduced to
@@ -438,9 +479,34 @@ int launch_attn(const uint16_t* Q, int B, int Tq, int Hq, const uint16_t* Kloc, 
     tabs.step[i] = cs(1.0);
   }
   hipLaunchKernelGGL(attn_mfma_kernel, grid, dim3(THREADS), 0, stream, Q, Tq, Hq, Kloc, Vloc, Tl, Hkv, Kmem,
-                     Vmem, mem_entry_stride, Mmax, mem_len, rope_offset, tabs, scale_log2e, O, lse);
+                     Vmem, mem_entry_stride, Mmax, mem_len, rope_offset, tabs, scale_log2e, O, lse, mode, PO, PML);
   MSA_CHECK_LAUNCH();
   return MSA_OK;
+}
+}  // namespace
+
+int launch_attn(const uint16_t* Q, int B, int Tq, int Hq, const uint16_t* Kloc, const uint16_t* Vloc,
+                int Tl, int Hkv, const uint16_t* Kmem, const uint16_t* Vmem, int64_t mem_entry_stride,
+                int Mmax, const int32_t* mem_len, int rope_offset, double rope_base, float scale,
+                float* O, float* lse, hipStream_t stream) {
+  return launch_attn_mode(Q, B, Tq, Hq, Kloc, Vloc, Tl, Hkv, Kmem, Vmem, mem_entry_stride, Mmax, mem_len, rope_offset,
+                          rope_base, scale, O, lse, MODE_FULL, nullptr, nullptr, stream);
+}
+
+int launch_attn_local(const uint16_t* Q, int B, int Tq, int Hq, const uint16_t* Kloc, const uint16_t* Vloc, int Tl,
+                      int Hkv, int rope_offset, double rope_base, float scale, float* part_O, float* part_ml,
+                      hipStream_t stream) {
+  return launch_attn_mode(Q, B, Tq, Hq, Kloc, Vloc, Tl, Hkv, nullptr, nullptr, 0, 0, nullptr, rope_offset,
+                          rope_base, scale, nullptr, nullptr, MODE_LOCAL, part_O, part_ml, stream);
+}
+
+int launch_attn_memory(const uint16_t* Q, int B, int Tq, int Hq, int Tl, int Hkv, const uint16_t* Kmem,
+                       const uint16_t* Vmem, int64_t mem_entry_stride, int Mmax, const int32_t* mem_len,
+                       int rope_offset, double rope_base, float scale, const float* part_O, const float* part_ml,
+                       float* O, float* lse, hipStream_t stream) {
+  return launch_attn_mode(Q, B, Tq, Hq, nullptr, nullptr, Tl, Hkv, Kmem, Vmem, mem_entry_stride, Mmax, mem_len,
+                          rope_offset, rope_base, scale, O, lse, MODE_MEMORY, const_cast<float*>(part_O),
+                          const_cast<float*>(part_ml), stream);
 }
 
 }  // namespace msa

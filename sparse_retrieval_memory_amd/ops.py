@@ -317,6 +317,42 @@ def sparse_attn_forward(Q, Kloc, Vloc, Kmem, Vmem, mem_entry_stride: int, Mmax: 
     return out, lse
 
 
+def sparse_attn_local_partial(Q, Kloc, Vloc, rope_offset: int, rope_base: float = 1.0e6,
+                              scale: Optional[float] = None, part=None, stream=None):
+    """msa_sparse_attn_local_partial: the local-key half of the attention; returns
+    part = (part_O fp32 [B, Tq, Hq, D], part_ml fp32 [B, Tq, Hq, 2])."""
+    _bf16(Q, "Q"); _bf16(Kloc, "Kloc"); _bf16(Vloc, "Vloc")
+    B, Tq, Hq, D = Q.shape
+    _, Tl, Hkv, _ = Kloc.shape
+    if scale is None:
+        scale = D ** -0.5
+    if part is None:
+        part = (torch.empty((B, Tq, Hq, D), dtype=torch.float32, device=Q.device),
+                torch.empty((B, Tq, Hq, 2), dtype=torch.float32, device=Q.device))
+    _lib.call("msa_sparse_attn_local_partial", _p(Q), B, Tq, Hq, D, _p(Kloc), _p(Vloc), Tl, Hkv, rope_offset,
+              float(rope_base), float(scale), _p(part[0]), _p(part[1]), _stream(stream))
+    return part
+
+
+def sparse_attn_memory_merge(Q, Tl: int, Hkv: int, Kmem, Vmem, mem_entry_stride: int, Mmax: int, mem_len,
+                             rope_offset: int, part, rope_base: float = 1.0e6, scale: Optional[float] = None,
+                             out=None, lse=None, stream=None):
+    """msa_sparse_attn_memory_merge: the memory half merged with ``part``; O fp32 [B, Tq, Hq, D]
+    (and the log-sum-exp into ``lse`` when given)."""
+    _bf16(Q, "Q")
+    B, Tq, Hq, D = Q.shape
+    if scale is None:
+        scale = D ** -0.5
+    if out is None:
+        out = torch.empty((B, Tq, Hq, D), dtype=torch.float32, device=Q.device)
+    kp = Kmem.data_ptr() if Kmem is not None else 0
+    vp = Vmem.data_ptr() if Vmem is not None else 0
+    _lib.call("msa_sparse_attn_memory_merge", _p(Q), B, Tq, Hq, D, Tl, Hkv, ctypes.c_void_p(kp), ctypes.c_void_p(vp),
+              mem_entry_stride, Mmax, _p(mem_len), rope_offset, float(rope_base), float(scale), _p(part[0]),
+              _p(part[1]), _p(out), ctypes.c_void_p(lse.data_ptr() if lse is not None else 0), _stream(stream))
+    return out
+
+
 def attn_backward_workspace_bytes(B, Tq, Hq, D, Tl, Hkv, Mmax) -> int:
     return int(_lib.load().msa_sparse_attn_backward_workspace_bytes(B, Tq, Hq, D, Tl, Hkv, Mmax))
 

@@ -21,7 +21,8 @@ def test_exports_every_declared_symbol():
             "msa_store_delete_workspace_bytes", "msa_route_scores_backward",
             "msa_route_backward_workspace_bytes", "msa_sparse_attn_backward",
             "msa_sparse_attn_backward_workspace_bytes", "msa_sparse_attn_forward",
-            "msa_sparse_attn_backward_saved"} <= set(names)
+            "msa_sparse_attn_backward_saved", "msa_sparse_attn_local_partial",
+            "msa_sparse_attn_memory_merge"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     assert set(_lib.SIGNATURES) == set(names)
@@ -79,6 +80,17 @@ def test_pool_and_attention_validation():
     fw = lambda lse=p, **kw: (lambda a: a[:18] + (lse,) + a[18:])(args(**kw))      # + lse before the stream
     assert _code("msa_sparse_attn_forward", *fw(Tq=5)) == E.MSA_ERR_INVALID_ARG
     assert _code("msa_sparse_attn_forward", *fw(lse=ctypes.c_void_p((1 << 20) + 2))) == E.MSA_ERR_INVALID_ARG
+    # split attention: the local partial and the memory pass validate like the one-launch call
+    assert _code("msa_sparse_attn_local_partial", p, 1, 5, 32, 128, p, p, 4, 8, 0, 1e6, 0.1, p, p, N) == \
+        E.MSA_ERR_INVALID_ARG                                                        # Tq > Tl
+    assert _code("msa_sparse_attn_local_partial", p, 1, 4, 32, 64, p, p, 4, 8, 0, 1e6, 0.1, p, p, N) == \
+        E.MSA_ERR_UNSUPPORTED                                                        # D
+    assert _code("msa_sparse_attn_local_partial", p, 1, 4, 32, 128, p, p, 4, 8, 0, 1e6, 0.1, p,
+                 ctypes.c_void_p((1 << 20) + 4), N) == E.MSA_ERR_INVALID_ARG          # part_ml alignment
+    mm = lambda Tq=4, part_ml=p, O=p: (p, 1, Tq, 32, 128, 4, 8, p, p, 2048, 8, p, 0, 1e6, 0.1, p, part_ml, O, N, N)
+    assert _code("msa_sparse_attn_memory_merge", *mm(Tq=5)) == E.MSA_ERR_INVALID_ARG
+    assert _code("msa_sparse_attn_memory_merge", *mm(O=N)) == E.MSA_ERR_INVALID_ARG
+    assert _code("msa_sparse_attn_memory_merge", *mm(part_ml=ctypes.c_void_p((1 << 20) + 4))) == E.MSA_ERR_INVALID_ARG
 
 
 def test_encode_validation():

@@ -18,6 +18,10 @@ from synth import splitmix as sm
 from tests.parity import (ATT_GRAD_OBS, ATT_TOL, SCORE_TOL, bf16_ulp_diff, check_topk, dev_bits, encoded_keys_ok, grads_ok,
                           host_bits, rel_rows, route_grad_bounds, route_near_ties)
 
+# lse of the GPU forward against the oracle: scores carry ~2^-16 of sum_d |q_d k_d| * scale
+# (about 1e-4 for N(0,1) rows at D = 128), so the log-sum-exp is within 1e-3 absolute
+LSE_TOL = 1e-3
+
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
@@ -479,6 +483,43 @@ def test_attention_matches_oracle(B, Tq, Tl, M, offset):
         assert rel_rows(o[b], ref) <= 1e-4          # fp32 path: far inside the bf16 budget
 
 
+@pytest.mark.parametrize("B,Tq,Tl,M,offset,Hq,Hkv", [(1, 32, 32, 32, 4, 32, 8), (1, 1, 128, 262, 16, 32, 8),
+                                                     (1, 128, 128, 262, 16, 32, 8), (2, 64, 64, 133, 16, 32, 8),
+                                                     (1, 5, 9, 0, 0, 32, 8), (2, 1, 300, 5, 2, 32, 8),
+                                                     (1, 100, 130, 45, 7, 32, 8), (1, 40, 50, 20, 5, 16, 2),
+                                                     (1, 300, 1000, 700, 16, 32, 8)])
+def test_attention_split_matches_fused_and_oracle(B, Tq, Tl, M, offset, Hq, Hkv):
+    """msa_sparse_attn_local_partial on a side stream, then msa_sparse_attn_memory_merge after an
+    event: O against the oracle and against the one-launch kernel, lse against the oracle."""
+    announce("attn-split", B, Tq, Tl, M, offset, Hq, Hkv)
+    Q, Kl, Vl, st, mem_len, _, Mmax = _attn_bwd_case(B, Tq, Tl, M, offset, Hq, Hkv, seed=B * 700 + Tq + M)
+    stg = dev_bits(st)
+    q, kl, vl = dev_bits(Q), dev_bits(Kl), dev_bits(Vl)
+    ml = torch.from_numpy(mem_len).to(DEV)
+    side = torch.cuda.Stream()
+    ev = torch.cuda.Event()
+    side.wait_stream(torch.cuda.current_stream())               # inputs are ready
+    with torch.cuda.stream(side):
+        part = ops.sparse_attn_local_partial(q, kl, vl, offset, 1e6, stream=side)
+        ev.record(side)
+    torch.cuda.current_stream().wait_event(ev)
+    lse = torch.empty((B, Tq, Hq), dtype=torch.float32, device=DEV)
+    o = ops.sparse_attn_memory_merge(q, Tl, Hkv, stg, stg[:, :, 1], 2 * Hkv * 128, Mmax, ml, offset, part, 1e6, lse=lse)
+    fused = ops.sparse_attn_decode(q, kl, vl, stg, stg[:, :, 1], 2 * Hkv * 128, Mmax, ml, offset, 1e6)
+    torch.cuda.synchronize()
+    o, lse, fused = o.cpu().numpy(), lse.cpu().numpy(), fused.cpu().numpy()
+    assert rel_rows(o, fused) <= 1e-5                            # same sums in another order
+    worst = 0.0
+    for b in range(B):
+        m = int(mem_len[b])
+        ref = O.attend(f64(Q[b]), f64(Kl[b]), f64(Vl[b]), f64(st[b, :m, 0]), f64(st[b, :m, 1]), offset, 1e6,
+                       128 ** -0.5)
+        assert rel_rows(o[b], ref) <= 1e-4
+        ref_lse = O.attend_lse(f64(Q[b]), f64(Kl[b]), f64(st[b, :m, 0]), offset, 1e6, 128 ** -0.5)
+        worst = max(worst, float(np.abs(lse[b] - ref_lse).max()))
+    assert worst <= LSE_TOL
+
+
 # ------------------------------------------------------ attention backward
 def _attn_bwd_case(B, Tq, Tl, M, offset, Hq=32, Hkv=8, seed=0):
     D = 128
@@ -533,11 +574,6 @@ def test_attention_backward_matches_oracle(B, Tq, Tl, M, offset, Hq, Hkv, saved)
         assert np.all(dKm[b, m:] == 0) and np.all(dVm[b, m:] == 0)
     print("worst per-row relative error", worst, flush=True)
     assert worst <= ATT_GRAD_OBS
-
-
-# lse of the GPU forward against the oracle: scores carry ~2^-16 of sum_d |q_d k_d| * scale
-# (about 1e-4 for N(0,1) rows at D = 128), so the log-sum-exp is within 1e-3 absolute
-LSE_TOL = 1e-3
 
 
 @pytest.mark.parametrize("B,Tq,Tl,M,offset,Hq,Hkv", [(1, 128, 128, 262, 16, 32, 8), (2, 64, 64, 133, 16, 32, 8),
