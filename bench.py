@@ -243,6 +243,7 @@ def main():
     sc_d = torch.empty((1, k), dtype=torch.float32, device=dev)
     ws_r = ops.workspace(ops.route_workspace_bytes(1, w.T, H, D, G, w.n_docs), dev, "bench-route")
     ws_k = ops.workspace(ops.topk_workspace_bytes(1, w.n_docs, k), dev, "bench-topk")
+    ws_rt = ops.workspace(ops.route_topk_workspace_bytes(1, w.T, H, D, G, w.n_docs, k), dev, "bench-route-topk")
     comp = torch.cuda.current_stream()
     side = torch.cuda.Stream()
     side_attn = torch.cuda.Stream()          # local-key attention partial, overlapping top-k + gather
@@ -257,22 +258,30 @@ def main():
     ev_a1 = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
 
     def layer_step(layer, rec=None, split=False):
-        """route -> top-k -> device-side assembly from the pinned host tier -> attend, one stream, no host sync.
+        """route + top-k (one call) -> device-side assembly from the pinned host tier -> attend, one stream, no
+        host sync (the instrumented pass times msa_route_scores and msa_topk_docs as separate calls).
         split (a side measurement): the local-key half of the attention runs on a second stream once the scan
         is done (it needs nothing retrieved), overlapping top-k and the gather; the memory half then merges
         with it."""
-        if rec is not None:
-            ev_r0[rec].record(comp)
-        ops.route_scores(qr[layer], krbar[layer], off_dev, doc_scores=doc, ws=ws_r, krbar_inv_norm=knorm[layer])
-        if rec is not None:
-            ev_r1[rec].record(comp)
+        fused = rec is None and not split
+        if fused:
+            # scan, document max with the top-k's group maxima, top-k: one call
+            ops.route_topk(qr[layer], krbar[layer], off_dev, k, krbar_inv_norm=knorm[layer], doc_scores=doc,
+                           top_idx=idx_d, top_scores=sc_d, ws=ws_rt)
+        else:
+            if rec is not None:
+                ev_r0[rec].record(comp)
+            ops.route_scores(qr[layer], krbar[layer], off_dev, doc_scores=doc, ws=ws_r, krbar_inv_norm=knorm[layer])
+            if rec is not None:
+                ev_r1[rec].record(comp)
         if split:
             ev_scan.record(comp)
             side_attn.wait_event(ev_scan)
             ops.sparse_attn_local_partial(Q[layer], Kl[layer], Vl[layer], k, w.rope_base, part=part,
                                           stream=side_attn)
             ev_local.record(side_attn)
-        ops.topk_docs(doc, k, top_idx=idx_d, top_scores=sc_d, ws=ws_k)
+        if not fused:
+            ops.topk_docs(doc, k, top_idx=idx_d, top_scores=sc_d, ws=ws_k)
         ops.gather_docs(idx_d, store, off_dev, staging, Mmax, mem_len=ml_dev)
         if split:
             comp.wait_event(ev_local)
@@ -554,8 +563,8 @@ def main():
         "config": {"workload": "100M-token memory, 18 routed layers, batch 1, 128-token query, top-16",
                    "n_docs": w.n_docs, "memory_tokens": w.n_tok, "n_chunks": G, "layers": L,
                    "router_heads": H, "head_dim": D, "q_heads": w.Hq, "chunk": w.chunk, "top_k": k,
-                   "step": "18 x (route -> top-k -> assemble selected K/V from the pinned host tier by a device "
-                           "kernel -> attend), one stream, no host round trip"},
+                   "step": "18 x (route + top-k (msa_route_topk) -> assemble selected K/V from the pinned host "
+                           "tier by a device kernel -> attend), one stream, no host round trip"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "msa_route_scores (scan + document max), bytes = Krbar + its stored norms + "

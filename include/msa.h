@@ -18,6 +18,7 @@
  *   msa_gather_docs         online: same, as one device kernel reading mapped host memory
  *   msa_append_router_rows  interleave: the next round's router rows and exclusions
  *   msa_sparse_attn_decode  generation: GQA attention over [memory ++ local KV]
+ *   msa_route_topk             msa_route_scores + msa_topk_docs in one call (k <= 32)
  *   msa_sparse_attn_local_partial, msa_sparse_attn_memory_merge  the same attention in two launches
  *                              (the local-key half needs nothing retrieved)
  *   msa_sparse_attn_forward    training: the same attention, also returning each row's log-sum-exp
@@ -271,6 +272,25 @@ size_t msa_topk_workspace_bytes(int B, int64_t n_docs, int k);
 int msa_topk_docs(const float* doc_scores, int B, int64_t n_docs, int k,
                   int32_t* top_idx, float* top_scores,
                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * msa_route_topk -- msa_route_scores followed by msa_topk_docs in one call, for
+ * 1 <= k <= 32: the document max and the top-k's per-64-document group maxima
+ * are formed in one pass over the chunk maxima (one launch fewer).
+ *
+ * Defined by: as msa_route_scores and msa_topk_docs (same outputs, bit for bit).
+ *   arguments as msa_route_scores, plus k and
+ *   top_idx     int32 [B, k] out; top_scores fp32 [B, k] out
+ *   workspace   >= msa_route_topk_workspace_bytes(B, T, H, D, n_chunks, n_docs, k)
+ *               bytes, 16-byte aligned (0 returned for k outside 1..32)
+ *   doc_scores  fp32 [B, n_docs] out (as msa_route_scores); chunk_scores optional
+ */
+size_t msa_route_topk_workspace_bytes(int B, int T, int H, int D, int64_t n_chunks, int64_t n_docs, int k);
+int msa_route_topk(const uint16_t* Qr, int B, int T, int H, int D, const uint16_t* Krbar,
+                   const float* krbar_inv_norm, int64_t n_chunks, const int64_t* doc_chunk_off, int64_t n_docs,
+                   const uint8_t* doc_exclude, int k, float* doc_scores, float* chunk_scores,
+                   int32_t* top_idx, float* top_scores, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream);
 
 /*
  * msa_fetch_docs -- context assembly from the host tier (host-driven copies).

@@ -52,6 +52,9 @@ SIGNATURES = {
                                         c_p, c_p, c_p, c_p, c_sz, c_p]),
     "msa_topk_workspace_bytes": (c_sz, [c_i, c_i64, c_i]),
     "msa_topk_docs": (c_i, [c_p, c_i, c_i64, c_i, c_p, c_p, c_p, c_sz, c_p]),
+    "msa_route_topk_workspace_bytes": (c_sz, [c_i, c_i, c_i, c_i, c_i64, c_i64, c_i]),
+    "msa_route_topk": (c_i, [c_p, c_i, c_i, c_i, c_i, c_p, c_p, c_i64, c_p, c_i64, c_p, c_i, c_p, c_p, c_p, c_p, c_p,
+                             c_sz, c_p]),
     "msa_fetch_docs": (c_i, [c_p, c_i, c_i, c_p, c_p, c_i64, c_i, c_i, c_p, c_i, c_p, c_p, c_p]),
     "msa_gather_docs": (c_i, [c_p, c_i, c_i, c_p, c_p, c_i64, c_i, c_i, c_p, c_i, c_p, c_p]),
     "msa_append_router_rows": (c_i, [c_p, c_i, c_i, c_i, c_i, c_p, c_p, c_i64, c_p, c_i, c_i, c_p, c_p, c_p, c_p]),

@@ -189,6 +189,47 @@ int msa_route_scores(const uint16_t* Qr, int B, int T, int H, int D, const uint1
                            doc_scores, chunk_scores, workspace, stream);
 }
 
+size_t msa_route_topk_workspace_bytes(int B, int T, int H, int D, int64_t n_chunks, int64_t n_docs, int k) {
+  (void)D;
+  if (B < 1 || T < 1 || n_docs < 1 || n_chunks < 0 || k < 1 || k > 32) return 0;
+  const size_t r = (msa::route_workspace(B, T, H, n_chunks, n_docs) + 255) & ~(size_t)255;
+  return r + msa::topk_workspace(B, n_docs, k);
+}
+
+int msa_route_topk(const uint16_t* Qr, int B, int T, int H, int D, const uint16_t* Krbar,
+                   const float* krbar_inv_norm, int64_t n_chunks, const int64_t* doc_chunk_off, int64_t n_docs,
+                   const uint8_t* doc_exclude, int k, float* doc_scores, float* chunk_scores, int32_t* top_idx,
+                   float* top_scores, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  msa::clear_error();
+  MSA_CHECK_ARG(B >= 1 && T >= 1, "B >= 1 and T >= 1 required (B=%d, T=%d)", B, T);
+  MSA_CHECK_ARG(n_docs >= 1 && n_chunks >= 0, "n_docs >= 1 and n_chunks >= 0 required");
+  MSA_CHECK_ARG(Qr && doc_chunk_off && doc_scores && top_idx && top_scores && (Krbar || n_chunks == 0),
+                "null pointer");
+  MSA_CHECK_SUPPORTED(D == 128, "D=%d unsupported (D must be 128)", D);
+  MSA_CHECK_SUPPORTED(H == 1 || H == 2 || H == 4 || H == 8, "H=%d unsupported (1, 2, 4 or 8)", H);
+  MSA_CHECK_SUPPORTED(k >= 1 && k <= 32, "k=%d unsupported here (1..32; larger k: msa_route_scores + msa_topk_docs)",
+                      k);
+  MSA_CHECK_ARG(k <= n_docs, "k=%d > n_docs", k);
+  MSA_CHECK_ARG(B <= 65535 && (int64_t)B * T <= (1 << 24), "B*T too large");
+  MSA_CHECK_ARG(n_docs < 0x7FFFFFFF / 256 * 256 && n_chunks < ((int64_t)1 << 40), "size out of range");
+  MSA_CHECK_ARG(aligned16(Qr) && (n_chunks == 0 || aligned16(Krbar)), "Qr and Krbar must be 16-byte aligned");
+  MSA_CHECK_ARG(krbar_inv_norm == nullptr || aligned16(krbar_inv_norm), "krbar_inv_norm must be 16-byte aligned");
+  const size_t need = msa_route_topk_workspace_bytes(B, T, H, D, n_chunks, n_docs, k);
+  if (workspace_bytes < need || workspace == nullptr) {
+    msa::set_error("workspace %zu bytes < required %zu", workspace_bytes, need);
+    return MSA_ERR_WORKSPACE;
+  }
+  MSA_CHECK_ARG(aligned16(workspace), "workspace must be 16-byte aligned");
+  uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
+  const size_t r = (msa::route_workspace(B, T, H, n_chunks, n_docs) + 255) & ~(size_t)255;
+  int rc = msa::launch_route(Qr, B, T, H, Krbar, krbar_inv_norm, n_chunks, doc_chunk_off, n_docs, doc_exclude,
+                             doc_scores, chunk_scores, ws, stream, /*reduce_docs=*/false);
+  if (rc != MSA_OK) return rc;
+  return msa::launch_docs_topk(reinterpret_cast<const uint32_t*>(ws), n_chunks, doc_chunk_off, n_docs, doc_exclude,
+                               B, k, doc_scores, chunk_scores, top_idx, top_scores,
+                               reinterpret_cast<uint64_t*>(ws + r), stream);
+}
+
 size_t msa_route_backward_workspace_bytes(int B, int T, int H, int D, int64_t n_docs) {
   (void)D;
   if (B < 1 || T < 1 || H < 1 || n_docs < 1) return 0;

@@ -162,12 +162,18 @@ int launch_pool(const uint16_t* K, const uint16_t* V, const uint16_t* Kr, const 
                 hipStream_t stream);
 int launch_route(const uint16_t* Qr, int B, int T, int H, const uint16_t* Krbar, const float* inv_norm,
                  int64_t n_chunks, const int64_t* doc_chunk_off, int64_t n_docs, const uint8_t* doc_exclude,
-                 float* doc_scores, float* chunk_scores, void* workspace, hipStream_t stream);
+                 float* doc_scores, float* chunk_scores, void* workspace, hipStream_t stream,
+                 bool reduce_docs = true);
 int launch_krbar_norms(const uint16_t* Krbar, int64_t n_chunks, int H, float* inv_norm, hipStream_t stream);
 size_t route_workspace(int B, int T, int H, int64_t n_chunks, int64_t n_docs);
 int launch_topk(const float* doc_scores, int B, int64_t n_docs, int k, int32_t* top_idx,
                 float* top_scores, void* workspace, hipStream_t stream);
 size_t topk_workspace(int B, int64_t n_docs, int k);
+// Document max from the scan's chunk maxima fused with top-k's group maxima, then the
+// group-based top-k (1 <= k <= 32); gmax holds B * ceil(n_docs / 64) keys.
+int launch_docs_topk(const uint32_t* chunk_enc, int64_t n_chunks, const int64_t* doc_chunk_off, int64_t n_docs,
+                     const uint8_t* doc_exclude, int B, int k, float* doc_scores, float* chunk_scores,
+                     int32_t* top_idx, float* top_scores, uint64_t* gmax, hipStream_t stream);
 int launch_attn(const uint16_t* Q, int B, int Tq, int Hq, const uint16_t* Kloc, const uint16_t* Vloc,
                 int Tl, int Hkv, const uint16_t* Kmem, const uint16_t* Vmem, int64_t mem_entry_stride,
                 int Mmax, const int32_t* mem_len, int rope_offset, double rope_base, float scale,

@@ -531,7 +531,8 @@ int launch_krbar_norms(const uint16_t* Krbar, int64_t n_chunks, int H, float* in
 
 int launch_route(const uint16_t* Qr, int B, int T, int H, const uint16_t* Krbar, const float* inv_norm,
                  int64_t n_chunks, const int64_t* doc_chunk_off, int64_t n_docs, const uint8_t* doc_exclude,
-                 float* doc_scores, float* chunk_scores, void* workspace, hipStream_t stream) {
+                 float* doc_scores, float* chunk_scores, void* workspace, hipStream_t stream,
+                 bool reduce_docs) {
   uint32_t* chunk_enc = reinterpret_cast<uint32_t*>(workspace);
   int rc = MSA_OK;
   if (n_chunks > 0) {
@@ -544,6 +545,7 @@ int launch_route(const uint16_t* Qr, int B, int T, int H, const uint16_t* Krbar,
     }
     if (rc != MSA_OK) return rc;
   }
+  if (!reduce_docs) return MSA_OK;           // the caller reduces the chunk maxima itself
   dim3 grid((unsigned)((n_docs + 255) / 256), (unsigned)B);
   hipLaunchKernelGGL(doc_reduce_kernel, grid, dim3(256), 0, stream, chunk_enc, n_chunks, doc_chunk_off,
                      n_docs, doc_exclude, doc_scores, chunk_scores);

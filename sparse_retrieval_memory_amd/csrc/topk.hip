@@ -392,12 +392,46 @@ topk_from_groups_filtered(const float* __restrict__ scores, const uint64_t* __re
   }
 }
 
-int launch_topk_small(const float* doc_scores, int B, int64_t n_docs, int k, int32_t* top_idx, float* top_scores,
-                      uint64_t* gmax, hipStream_t stream) {
+// The document max (the last step of the routing scores: a document's score is the max of its
+// chunks', -inf when excluded or empty) with the group maxima of the top-k folded in: a wave
+// holds 64 consecutive documents, i.e. one group, so it also writes the group's largest key.
+__global__ void __launch_bounds__(256)
+doc_reduce_groups_kernel(const uint32_t* __restrict__ chunk_enc, int64_t n_chunks,
+                         const int64_t* __restrict__ doc_chunk_off, int64_t n_docs,
+                         const uint8_t* __restrict__ doc_exclude, float* __restrict__ doc_scores,
+                         float* __restrict__ chunk_scores, int64_t n_groups, uint64_t* __restrict__ gmax) {
+  const int b = blockIdx.y;
+  const int64_t d = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  uint64_t key = 0ull;
+  if (d < n_docs) {
+    int64_t g0 = doc_chunk_off[d], g1 = doc_chunk_off[d + 1];
+    if (g0 < 0) g0 = 0;
+    if (g1 > n_chunks) g1 = n_chunks;
+    const uint32_t* ce = chunk_enc + (int64_t)b * n_chunks;
+    uint32_t best = 0;
+    for (int64_t g = g0; g < g1; ++g) {
+      const uint32_t e = ce[g];
+      best = e > best ? e : best;
+      if (chunk_scores) chunk_scores[(int64_t)b * n_chunks + g] = dec_f32(e);
+    }
+    float s = (g1 > g0) ? dec_f32(best) : -INFINITY;
+    if (doc_exclude && doc_exclude[(int64_t)b * n_docs + d]) s = -INFINITY;
+    doc_scores[(int64_t)b * n_docs + d] = s;
+    key = make_key(s, (uint32_t)d);
+  }
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) {
+    const uint64_t o = shfl_xor_u64(key, m);
+    key = o > key ? o : key;
+  }
+  const int64_t grp = d / GROUP;
+  if ((threadIdx.x & 63) == 0 && grp < n_groups) gmax[(int64_t)b * n_groups + grp] = key;
+}
+
+// The group-based selection from group maxima already in gmax (1 <= k <= 32).
+int launch_topk_from_groups(const float* doc_scores, int B, int64_t n_docs, int k, int32_t* top_idx,
+                            float* top_scores, const uint64_t* gmax, hipStream_t stream) {
   const int64_t n_groups = (n_docs + GROUP - 1) / GROUP;
-  hipLaunchKernelGGL(topk_group_max, dim3((unsigned)((n_docs + 255) / 256), (unsigned)B), dim3(256), 0, stream,
-                     doc_scores, n_docs, n_groups, gmax);
-  MSA_CHECK_LAUNCH();
 #define MSA_TOPK_GROUPS(RMV, RBV)                                                                        \
   hipLaunchKernelGGL((topk_from_groups<RMV, RBV>), dim3((unsigned)B), dim3(64 * P2_WAVES), 0, stream, doc_scores, \
                      gmax, n_docs, n_groups, k, top_idx, top_scores)
@@ -414,12 +448,32 @@ int launch_topk_small(const float* doc_scores, int B, int64_t n_docs, int k, int
   return MSA_OK;
 }
 
+int launch_topk_small(const float* doc_scores, int B, int64_t n_docs, int k, int32_t* top_idx, float* top_scores,
+                      uint64_t* gmax, hipStream_t stream) {
+  const int64_t n_groups = (n_docs + GROUP - 1) / GROUP;
+  hipLaunchKernelGGL(topk_group_max, dim3((unsigned)((n_docs + 255) / 256), (unsigned)B), dim3(256), 0, stream,
+                     doc_scores, n_docs, n_groups, gmax);
+  MSA_CHECK_LAUNCH();
+  return launch_topk_from_groups(doc_scores, B, n_docs, k, top_idx, top_scores, gmax, stream);
+}
+
 int64_t pass1_blocks(int64_t n_docs, int k) {
   const int64_t piece = SORT_N - k;
   return (n_docs + piece - 1) / piece;
 }
 
 }  // namespace
+
+int launch_docs_topk(const uint32_t* chunk_enc, int64_t n_chunks, const int64_t* doc_chunk_off, int64_t n_docs,
+                     const uint8_t* doc_exclude, int B, int k, float* doc_scores, float* chunk_scores,
+                     int32_t* top_idx, float* top_scores, uint64_t* gmax, hipStream_t stream) {
+  const int64_t n_groups = (n_docs + GROUP - 1) / GROUP;
+  hipLaunchKernelGGL(doc_reduce_groups_kernel, dim3((unsigned)((n_docs + 255) / 256), (unsigned)B), dim3(256), 0,
+                     stream, chunk_enc, n_chunks, doc_chunk_off, n_docs, doc_exclude, doc_scores, chunk_scores,
+                     n_groups, gmax);
+  MSA_CHECK_LAUNCH();
+  return launch_topk_from_groups(doc_scores, B, n_docs, k, top_idx, top_scores, gmax, stream);
+}
 
 size_t topk_workspace(int B, int64_t n_docs, int k) {
   if (k < 1 || k > KMAX) return 0;

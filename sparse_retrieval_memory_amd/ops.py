@@ -166,6 +166,37 @@ def route_scores(Qr, Krbar, doc_chunk_off, doc_exclude=None, want_chunk_scores: 
     return doc_scores
 
 
+def route_topk_workspace_bytes(B, T, H, D, n_chunks, n_docs, k) -> int:
+    return int(_lib.load().msa_route_topk_workspace_bytes(B, T, H, D, n_chunks, n_docs, k))
+
+
+def route_topk(Qr, Krbar, doc_chunk_off, k: int, doc_exclude=None, krbar_inv_norm=None, doc_scores=None,
+               top_idx=None, top_scores=None, ws=None, stream=None):
+    """msa_route_topk: (doc_scores fp32 [B, n_docs], top_idx int32 [B, k], top_scores fp32 [B, k])."""
+    _bf16(Qr, "Qr"); _bf16(Krbar, "Krbar"); _dev(Qr, "Qr")
+    B, T, H, D = Qr.shape
+    n_chunks = Krbar.shape[0]
+    n_docs = doc_chunk_off.numel() - 1
+    dev = Qr.device
+    if doc_scores is None:
+        doc_scores = torch.empty((B, n_docs), dtype=torch.float32, device=dev)
+    if top_idx is None:
+        top_idx = torch.empty((B, k), dtype=torch.int32, device=dev)
+    if top_scores is None:
+        top_scores = torch.empty((B, k), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = workspace(route_topk_workspace_bytes(B, T, H, D, n_chunks, n_docs, k), dev, "route-topk")
+    if doc_exclude is not None:
+        assert doc_exclude.dtype in (torch.uint8, torch.bool) and doc_exclude.shape == (B, n_docs)
+        doc_exclude = doc_exclude.contiguous()
+    if krbar_inv_norm is not None:
+        assert krbar_inv_norm.dtype == torch.float32 and krbar_inv_norm.shape == (n_chunks, H)
+    _lib.call("msa_route_topk", _p(Qr), B, T, H, D, _p(Krbar), _p(krbar_inv_norm), n_chunks, _p(doc_chunk_off), n_docs,
+              _p(doc_exclude), k, _p(doc_scores), None, _p(top_idx), _p(top_scores), _p(ws), ws.numel(),
+              _stream(stream))
+    return doc_scores, top_idx, top_scores
+
+
 def route_backward_workspace_bytes(B, T, H, D, n_docs) -> int:
     return int(_lib.load().msa_route_backward_workspace_bytes(B, T, H, D, n_docs))
 

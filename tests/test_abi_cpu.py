@@ -22,7 +22,7 @@ def test_exports_every_declared_symbol():
             "msa_route_backward_workspace_bytes", "msa_sparse_attn_backward",
             "msa_sparse_attn_backward_workspace_bytes", "msa_sparse_attn_forward",
             "msa_sparse_attn_backward_saved", "msa_sparse_attn_local_partial",
-            "msa_sparse_attn_memory_merge"} <= set(names)
+            "msa_sparse_attn_memory_merge", "msa_route_topk", "msa_route_topk_workspace_bytes"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     assert set(_lib.SIGNATURES) == set(names)
@@ -217,3 +217,21 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         _lib.load()
+
+
+def test_route_topk_validation():
+    E = _lib
+    p = ctypes.c_void_p(1 << 20)
+    lib = _lib.load()
+    need = lib.msa_route_topk_workspace_bytes(1, 128, 8, 128, 1000, 100, 16)
+    assert need >= lib.msa_topk_workspace_bytes(1, 100, 16) + 4 * 1000        # chunk maxima + group maxima
+    assert lib.msa_route_topk_workspace_bytes(1, 128, 8, 128, 1000, 100, 33) == 0
+    rt = lambda k=16, H=8, D=128, n_docs=100, ws=p, wsb=need, ti=p: (
+        p, 1, 128, H, D, p, N, 1000, p, n_docs, N, k, p, N, ti, p, ws, wsb, N)
+    assert _code("msa_route_topk", *rt(k=33)) == E.MSA_ERR_UNSUPPORTED
+    assert _code("msa_route_topk", *rt(k=0)) == E.MSA_ERR_UNSUPPORTED
+    assert _code("msa_route_topk", *rt(k=16, n_docs=10)) == E.MSA_ERR_INVALID_ARG        # k > n_docs
+    assert _code("msa_route_topk", *rt(H=3)) == E.MSA_ERR_UNSUPPORTED
+    assert _code("msa_route_topk", *rt(ti=N)) == E.MSA_ERR_INVALID_ARG
+    assert _code("msa_route_topk", *rt(wsb=need - 1)) == E.MSA_ERR_WORKSPACE
+    assert _code("msa_route_topk", *rt(ws=N)) == E.MSA_ERR_WORKSPACE

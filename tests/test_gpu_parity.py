@@ -239,6 +239,29 @@ def test_route_backward_deterministic():
         assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
 
 
+@pytest.mark.parametrize("B,T,n_docs,k,norms", [(1, 128, 3000, 16, True), (1, 128, 3000, 16, False), (2, 40, 1500, 5, True),
+                                                (3, 7, 700, 1, True), (1, 33, 130, 32, False), (16, 64, 300, 16, True),
+                                                (1, 128, 64, 32, True)])
+def test_route_topk_matches_separate_calls(B, T, n_docs, k, norms):
+    """msa_route_topk (document max and group maxima in one pass) gives exactly what
+    msa_route_scores followed by msa_topk_docs gives, with excluded documents."""
+    announce("route-topk", B, T, n_docs, k, norms)
+    Qr, Kr, off = _route_case(B, T, 8, n_docs=n_docs, seed=B * 31 + T + k)
+    q, kr, offd = dev_bits(Qr), dev_bits(Kr), torch.from_numpy(off).to(DEV)
+    excl = np.zeros((B, n_docs), np.uint8); excl[:, 3::11] = 1
+    ex = torch.from_numpy(excl).to(DEV)
+    nrm = ops.krbar_inv_norms(kr) if norms else None
+    d1, i1, s1 = ops.route_topk(q, kr, offd, k, doc_exclude=ex, krbar_inv_norm=nrm)
+    d2 = ops.route_scores(q, kr, offd, doc_exclude=ex, krbar_inv_norm=nrm)
+    i2, s2 = ops.topk_docs(d2, k)
+    torch.cuda.synchronize()
+    assert np.array_equal(d1.cpu().numpy().view(np.uint32), d2.cpu().numpy().view(np.uint32))
+    assert np.array_equal(i1.cpu().numpy(), i2.cpu().numpy())
+    assert np.array_equal(s1.cpu().numpy().view(np.uint32), s2.cpu().numpy().view(np.uint32))
+    ref_idx, ref_sc = O.topk(d1.cpu().numpy().astype(np.float64), k)
+    assert np.array_equal(i1.cpu().numpy(), ref_idx)
+
+
 @pytest.mark.parametrize("B,n,k", [(1, 64, 4), (1, 1000, 16), (16, 20000, 16), (1, 200000, 16), (4, 20000, 8),
                                    (1, 7, 7), (3, 5, 1), (2, 4097, 1024), (1, 2049, 2), (2, 100, 100),
                                    (1, 70000, 32), (2, 40000, 17), (3, 33000, 5), (1, 32768, 16), (1, 32769, 3),
