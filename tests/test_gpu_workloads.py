@@ -149,6 +149,35 @@ def test_10M_batch16_route_sampled_queries():
 
 
 # ---------------------------------------------------------------- 100M tokens
+def test_100M_layer_route_topk_equals_separate_calls():
+    """msa_route_topk, the call the 18-layer step times, on a full 100M-token layer (200,000
+    documents, 1.66M chunks, 128 router rows, stored norms, a tenth of the documents excluded):
+    document scores, selection and selected scores bit-identical to msa_route_scores followed by
+    msa_topk_docs; every planted needle of the layer that is not excluded is selected."""
+    w = C.workload("100M-18layer")
+    layer = 5
+    announce("100M route_topk", layer, w.describe())
+    kr = device_krbar(w, layer)
+    q = C.queries(w, layer)
+    off = torch.from_numpy(w.doc_chunk_off).to(DEV)
+    nrm = ops.krbar_inv_norms(kr)
+    qr = dev_bits(q["Qr"])
+    needles = set(d for _, d in C.planted_docs(w, layer))
+    excl = (np.arange(w.n_docs) % 10 == 7).astype(np.uint8)
+    excl[list(needles)] = 0
+    ex = torch.from_numpy(excl[None]).to(DEV)
+    d1, i1, s1 = ops.route_topk(qr, kr, off, w.k, doc_exclude=ex, krbar_inv_norm=nrm)
+    d2 = ops.route_scores(qr, kr, off, doc_exclude=ex, krbar_inv_norm=nrm)
+    i2, s2 = ops.topk_docs(d2, w.k)
+    torch.cuda.synchronize()
+    assert np.array_equal(d1.cpu().numpy().view(np.uint32), d2.cpu().numpy().view(np.uint32))
+    assert np.array_equal(i1.cpu().numpy(), i2.cpu().numpy())
+    assert np.array_equal(s1.cpu().numpy().view(np.uint32), s2.cpu().numpy().view(np.uint32))
+    sel = set(int(x) for x in i1.cpu().numpy()[0])
+    assert needles <= sel, f"needles {sorted(needles - sel)} not selected"
+    assert not any(excl[d] for d in sel)
+
+
 def test_100M_layer_sampled_documents():
     """200,000 documents, 1.66M chunks (one routed layer of the 100M-token store).
 
