@@ -458,6 +458,189 @@ attn_mfma_kernel(const uint16_t* __restrict__ Q, int Tq, int Hq, const uint16_t*
 }  // namespace
 
 namespace {
+// ---------------------------------------------------------------- few query rows
+// For decoding (Tq <= DEC_MAX_ROWS) one matrix-core tile would use 1 of its 32 rows.  Here a
+// workgroup owns one (query row, q-head) and one lane owns one key: lanes form the key's
+// score in fp32 (memory keys as given, local keys rotated from the LDS cos/sin table), the
+// workgroup takes the softmax, and the output is summed over V rows staged in LDS (the table's
+// space, free once the scores are formed).  Used when every key fits: Mmax + Tl <= DEC_MAX_KEYS
+// and Tl <= TAB_POS.
+constexpr int DEC_THREADS = 512;             // two waves per SIMD
+constexpr int DEC_LPK = 8;                    // lanes per key in the score pass (16 dims each)
+constexpr int DEC_KPP = DEC_THREADS / DEC_LPK;   // keys per pass
+constexpr int DEC_MAX_KEYS = DEC_THREADS;     // one key per lane in the softmax
+constexpr int DEC_PASSES = DEC_MAX_KEYS / DEC_KPP;
+constexpr int DEC_VPT = DEC_MAX_KEYS * 16 / DEC_THREADS;   // 16-byte V pieces per thread
+constexpr int DEC_MAX_ROWS = 4;
+constexpr int DEC_WAVES = DEC_THREADS / 64;
+
+__global__ void __launch_bounds__(DEC_THREADS, 1)
+attn_decode_kernel(const uint16_t* __restrict__ Q, int Tq, int Hq, const uint16_t* __restrict__ Kloc,
+                   const uint16_t* __restrict__ Vloc, int Tl, int Hkv, const uint16_t* __restrict__ Kmem,
+                   const uint16_t* __restrict__ Vmem, int64_t mstride, int Mmax, const int32_t* __restrict__ mem_len,
+                   int rope_offset, const RopeTables tabs, float scale_log2e, float* __restrict__ O,
+                   float* __restrict__ LSE) {
+  // one area: the cos/sin table (positions rope_offset + p, p < TAB_POS) while the scores are
+  // formed, then the V rows [key][dim]
+  __shared__ __attribute__((aligned(16))) uint8_t area[DEC_MAX_KEYS * D * 2];
+  static_assert(sizeof(float2) * TAB_POS * (D / 2 + 2) <= sizeof(area), "table fits the V area");
+  float2 (*cs_tab)[D / 2 + 2] = reinterpret_cast<float2 (*)[D / 2 + 2]>(area);
+  uint16_t (*vs)[D] = reinterpret_cast<uint16_t (*)[D]>(area);
+  __shared__ float qs[D];
+  __shared__ float ps[DEC_MAX_KEYS];
+  __shared__ float red[2][DEC_WAVES];
+  __shared__ float2 pv[DEC_WAVES][D / 2];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int g = h / (Hq / Hkv);
+  int M = mem_len[b];
+  if (M < 0) M = 0;
+  if (M > Mmax) M = Mmax;
+  const int n_loc = (Tl - Tq) + i + 1;            // local keys this row sees
+  const int n = M + n_loc;                        // <= Mmax + Tl <= DEC_MAX_KEYS (checked at launch)
+
+  auto key_row = [&](int key, const uint16_t* mem, const uint16_t* loc) {
+    return key < M ? mem + ((int64_t)b * Mmax + key) * mstride + (int64_t)g * D
+                   : loc + (((int64_t)b * Tl + (key - M)) * Hkv + g) * D;
+  };
+  // key rows, loaded up front and coalesced: 8 lanes per key, lane `sub` holds dims [8 sub, 8 sub + 8)
+  // and their rotation partners [64 + 8 sub, 64 + 8 sub + 8); pass r covers keys DEC_KPP r + tid / 8
+  const int sub = tid & (DEC_LPK - 1), kslot = tid / DEC_LPK;
+  uint4 kr[DEC_PASSES][2];
+#pragma unroll
+  for (int r = 0; r < DEC_PASSES; ++r) {
+    const int key = kslot + DEC_KPP * r;
+    if (key < n) {
+      const uint16_t* kp = key_row(key, Kmem, Kloc);
+      kr[r][0] = *reinterpret_cast<const uint4*>(kp + 8 * sub);
+      kr[r][1] = *reinterpret_cast<const uint4*>(kp + D / 2 + 8 * sub);
+    }
+  }
+  // the query row, rotated at its position and pre-scaled by scale * log2(e)
+  if (tid < D / 2) {
+    const uint16_t* q = Q + (((int64_t)b * Tq + i) * Hq + h) * D;
+    const float x1 = __uint_as_float((uint32_t)q[tid] << 16), x2 = __uint_as_float((uint32_t)q[tid + D / 2] << 16);
+    float c, sn;
+    rope_cs(rope_offset + (Tl - Tq) + i, tabs.rev[tid], &c, &sn);
+    qs[tid] = (x1 * c - x2 * sn) * scale_log2e;
+    qs[tid + D / 2] = (x2 * c + x1 * sn) * scale_log2e;
+  }
+  // cos/sin table of the local keys' positions (as the matrix-core kernel builds it)
+  {
+    const int fi = tid & (D / 2 - 1), sg = tid / (D / 2);
+    static_assert(DEC_THREADS / (D / 2) * TAB_SEG >= TAB_POS, "the segments cover the table");
+    const int p0 = sg * TAB_SEG;
+    if (sg < TAB_POS / TAB_SEG && p0 < n_loc) {
+      const float2 st = tabs.start[sg][fi], d1 = tabs.step[fi];
+      float c = st.x, s_ = st.y;
+      const int p1 = p0 + TAB_SEG < n_loc ? p0 + TAB_SEG : n_loc;
+      for (int p = p0; p < p1; ++p) {
+        cs_tab[p][fi] = make_float2(c, s_);
+        const float cn = c * d1.x - s_ * d1.y;
+        s_ = s_ * d1.x + c * d1.y;
+        c = cn;
+      }
+    }
+  }
+  __syncthreads();
+
+  // scores: each key's 8 lanes rotate their pairs (local keys, from the table), take their share of
+  // the dot product and sum it over the 8 lanes; the first lane stores the score
+#pragma unroll
+  for (int r = 0; r < DEC_PASSES; ++r) {
+    const int key = kslot + DEC_KPP * r;
+    if (DEC_KPP * r < n) {                        // uniform: some key of this pass exists
+      float part = 0.f;
+      if (key < n) {
+        const uint4 a4 = kr[r][0], c4 = kr[r][1];
+        float lo[8] = {bf16_lo(a4.x), bf16_hi(a4.x), bf16_lo(a4.y), bf16_hi(a4.y),
+                       bf16_lo(a4.z), bf16_hi(a4.z), bf16_lo(a4.w), bf16_hi(a4.w)};
+        float hi[8] = {bf16_lo(c4.x), bf16_hi(c4.x), bf16_lo(c4.y), bf16_hi(c4.y),
+                       bf16_lo(c4.z), bf16_hi(c4.z), bf16_lo(c4.w), bf16_hi(c4.w)};
+        if (key >= M) {
+          const float4* t = reinterpret_cast<const float4*>(&cs_tab[key - M][8 * sub]);
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const float4 v = t[q4];
+            float x1 = lo[2 * q4], x2 = hi[2 * q4];
+            lo[2 * q4] = x1 * v.x - x2 * v.y; hi[2 * q4] = x2 * v.x + x1 * v.y;
+            x1 = lo[2 * q4 + 1]; x2 = hi[2 * q4 + 1];
+            lo[2 * q4 + 1] = x1 * v.z - x2 * v.w; hi[2 * q4 + 1] = x2 * v.z + x1 * v.w;
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part += lo[e] * qs[8 * sub + e] + hi[e] * qs[D / 2 + 8 * sub + e];
+      }
+      part += __shfl_xor(part, 1);
+      part += __shfl_xor(part, 2);
+      part += __shfl_xor(part, 4);
+      if (sub == 0 && key < n) ps[key] = part;
+    }
+  }
+  __syncthreads();
+  float sc[1] = {tid < n ? ps[tid] : -INFINITY};
+  // softmax over the row's keys: block max, then the block sum of exp2(score - max)
+  float m = sc[0];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if (lane == 0) red[0][wave] = m;
+  __syncthreads();                                // also: every table read is done
+  // V rows into the table's space by LDS DMA: piece e = tid + DEC_THREADS * u (key e / 16, dims
+  // 8 (e % 16) ..); a wave's 64 pieces are 1 KB of consecutive LDS, its base wave-uniform
+#pragma unroll 4
+  for (int u = 0; u < DEC_VPT; ++u) {
+    const int e = tid + DEC_THREADS * u, key = e >> 4;
+    if (key < n) dma16(key_row(key, Vmem, Vloc) + 8 * (e & 15), area + (size_t)(e - lane) * 16);
+  }
+  float mx = red[0][0];
+#pragma unroll
+  for (int w = 1; w < DEC_WAVES; ++w) mx = fmaxf(mx, red[0][w]);
+  const float p = tid < n ? exp2f(sc[0] - mx) : 0.f;
+  ps[tid] = p;                                    // each lane rewrites only its own score
+  float l = p;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o);
+  if (lane == 0) red[1][wave] = l;
+  wait_vmem_all();                                // this wave's V copies have landed
+  __syncthreads();
+  float lt = 0.f;
+#pragma unroll
+  for (int w = 0; w < DEC_WAVES; ++w) lt += red[1][w];
+  // O = sum_j p_j v_j / l: lane -> dims (2 lane, 2 lane + 1), wave -> keys wave, wave + DEC_WAVES, ...
+  // four independent accumulator pairs, so the LDS reads of consecutive keys overlap
+  float oa[4] = {0.f, 0.f, 0.f, 0.f}, ob[4] = {0.f, 0.f, 0.f, 0.f};
+  int k = wave;
+  for (; k + 3 * DEC_WAVES < n; k += 4 * DEC_WAVES) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float w = ps[k + c * DEC_WAVES];
+      const uint32_t v2 = *reinterpret_cast<const uint32_t*>(&vs[k + c * DEC_WAVES][2 * lane]);
+      oa[c] += w * bf16_lo(v2);
+      ob[c] += w * bf16_hi(v2);
+    }
+  }
+  for (; k < n; k += DEC_WAVES) {
+    const float w = ps[k];
+    const uint32_t v2 = *reinterpret_cast<const uint32_t*>(&vs[k][2 * lane]);
+    oa[0] += w * bf16_lo(v2);
+    ob[0] += w * bf16_hi(v2);
+  }
+  pv[wave][lane] = make_float2((oa[0] + oa[1]) + (oa[2] + oa[3]), (ob[0] + ob[1]) + (ob[2] + ob[3]));
+  __syncthreads();
+  if (tid < D / 2) {
+    float2 acc = make_float2(0.f, 0.f);
+#pragma unroll
+    for (int w = 0; w < DEC_WAVES; ++w) { acc.x += pv[w][tid].x; acc.y += pv[w][tid].y; }
+    const float inv = 1.f / lt;
+    const int64_t ri = ((int64_t)b * Tq + i) * Hq + h;
+    *reinterpret_cast<float2*>(O + ri * D + 2 * tid) = make_float2(acc.x * inv, acc.y * inv);
+    if (LSE && tid == 0) LSE[ri] = (mx + log2f(lt)) * 0.6931471805599453f;
+  }
+}
+}  // namespace
+
+namespace {
 int launch_attn_mode(const uint16_t* Q, int B, int Tq, int Hq, const uint16_t* Kloc, const uint16_t* Vloc,
                      int Tl, int Hkv, const uint16_t* Kmem, const uint16_t* Vmem, int64_t mem_entry_stride,
                      int Mmax, const int32_t* mem_len, int rope_offset, double rope_base, float scale,
@@ -465,18 +648,35 @@ int launch_attn_mode(const uint16_t* Q, int B, int Tq, int Hq, const uint16_t* K
   dim3 grid((unsigned)((Tq + RT - 1) / RT), (unsigned)Hq, (unsigned)B);
   const float scale_log2e = scale * 1.4426950408889634f;
   // RoPE constants in fp64: angle of position p at frequency i in revolutions, reduced to
-  // [-1/2, 1/2] before cos/sin (the same reduction the device fallback uses)
-  RopeTables tabs;
-  const double two_pi = 6.283185307179586;
-  for (int i = 0; i < D / 2; ++i) {
-    tabs.rev[i] = pow(rope_base, -2.0 * i / D) / two_pi;
-    auto cs = [&](double pos) {
-      double r = pos * tabs.rev[i];
-      r -= rint(r);
-      return make_float2((float)cos(two_pi * r), (float)sin(two_pi * r));
-    };
-    for (int sg = 0; sg < TAB_POS / TAB_SEG; ++sg) tabs.start[sg][i] = cs((double)rope_offset + TAB_SEG * sg);
-    tabs.step[i] = cs(1.0);
+  // [-1/2, 1/2] before cos/sin (the same reduction the device fallback uses).  They depend on
+  // (rope_offset, rope_base) only; the last set is kept per host thread, since recomputing them
+  // (~700 fp64 transcendentals) costs about as much host time as a decode call's GPU time.
+  struct CachedTables { bool valid; int offset; double base; RopeTables t; };
+  static thread_local CachedTables cache{false, 0, 0.0, {}};
+  if (!cache.valid || cache.offset != rope_offset || cache.base != rope_base) {
+    RopeTables& tb = cache.t;
+    const double two_pi = 6.283185307179586;
+    for (int i = 0; i < D / 2; ++i) {
+      tb.rev[i] = pow(rope_base, -2.0 * i / D) / two_pi;
+      auto cs = [&](double pos) {
+        double r = pos * tb.rev[i];
+        r -= rint(r);
+        return make_float2((float)cos(two_pi * r), (float)sin(two_pi * r));
+      };
+      for (int sg = 0; sg < TAB_POS / TAB_SEG; ++sg) tb.start[sg][i] = cs((double)rope_offset + TAB_SEG * sg);
+      tb.step[i] = cs(1.0);
+    }
+    cache.valid = true;
+    cache.offset = rope_offset;
+    cache.base = rope_base;
+  }
+  const RopeTables& tabs = cache.t;
+  if (mode == MODE_FULL && Tq <= DEC_MAX_ROWS && Tl <= TAB_POS && (int64_t)Mmax + Tl <= DEC_MAX_KEYS) {
+    hipLaunchKernelGGL(attn_decode_kernel, dim3((unsigned)Tq, (unsigned)Hq, (unsigned)B), dim3(DEC_THREADS), 0,
+                       stream, Q, Tq, Hq, Kloc, Vloc, Tl, Hkv, Kmem, Vmem, mem_entry_stride, Mmax, mem_len,
+                       rope_offset, tabs, scale_log2e, O, lse);
+    MSA_CHECK_LAUNCH();
+    return MSA_OK;
   }
   hipLaunchKernelGGL(attn_mfma_kernel, grid, dim3(THREADS), 0, stream, Q, Tq, Hq, Kloc, Vloc, Tl, Hkv, Kmem,
                      Vmem, mem_entry_stride, Mmax, mem_len, rope_offset, tabs, scale_log2e, O, lse, mode, PO, PML);

@@ -482,7 +482,10 @@ def test_store_append_then_delete_round_trip():
 @pytest.mark.parametrize("B,Tq,Tl,M,offset", [(1, 32, 32, 32, 4), (1, 1, 128, 262, 16), (1, 128, 128, 262, 16),
                                               (2, 64, 64, 133, 16), (1, 5, 9, 0, 0), (1, 17, 40, 1, 3),
                                               (3, 16, 16, 70, 8), (1, 128, 128, 448, 16),
-                                              (1, 64, 200, 40, 7), (2, 1, 300, 5, 2)])
+                                              (1, 64, 200, 40, 7), (2, 1, 300, 5, 2),
+                                              # <= 4 rows, Mmax + Tl <= 512, Tl <= 128: the few-row kernel
+                                              (1, 1, 128, 133, 16), (1, 3, 100, 50, 7), (2, 4, 4, 0, 0),
+                                              (1, 1, 1, 1, 0), (1, 2, 128, 384, 16), (3, 1, 64, 77, 5)])
 def test_attention_matches_oracle(B, Tq, Tl, M, offset):
     announce("attn", B, Tq, Tl, M, offset)
     seed = B * 1000 + Tq + M
@@ -601,7 +604,8 @@ def test_attention_backward_matches_oracle(B, Tq, Tl, M, offset, Hq, Hkv, saved)
 
 @pytest.mark.parametrize("B,Tq,Tl,M,offset,Hq,Hkv", [(1, 128, 128, 262, 16, 32, 8), (2, 64, 64, 133, 16, 32, 8),
                                                      (1, 1, 128, 262, 16, 32, 8), (1, 5, 9, 0, 0, 32, 8),
-                                                     (1, 100, 130, 45, 7, 32, 8), (1, 40, 50, 20, 5, 16, 2)])
+                                                     (1, 100, 130, 45, 7, 32, 8), (1, 40, 50, 20, 5, 16, 2),
+                                                     (1, 2, 64, 30, 3, 16, 2), (2, 4, 100, 300, 9, 8, 8)])
 def test_attention_forward_lse_matches_oracle(B, Tq, Tl, M, offset, Hq, Hkv):
     """msa_sparse_attn_forward: O as msa_sparse_attn_decode, and each row's natural log-sum-exp."""
     announce("attn-forward-lse", B, Tq, Tl, M, offset, Hq, Hkv)
