@@ -68,7 +68,7 @@ def test_interleave_chain_recovered_reduced():
         assert ch["C"] in res[2]["top_idx"]
         allr = res[-1]["retrieved"]
         assert len(allr) == len(set(allr)) == w.k * w.rounds
-        # round 1 is the single-step route + top-k
+        # the first interleave round is the single-step route + top-k
         _, doc1 = O.route(Qr[b][None], Rb, w.doc_chunk_off)
         i1, _ = O.topk(doc1, w.k)
         assert list(i1[0]) == list(res[0]["top_idx"])
