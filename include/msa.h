@@ -12,6 +12,7 @@
  *   msa_store_append        update: append documents to the routing store in place
  *   msa_krbar_inv_norms     offline: 1/|Krbar| per chunk and head, stored beside the store
  *   msa_route_scores        online: cosine routing scan over every Krbar chunk
+ *   msa_route_scan, msa_route_select  the same as two calls: the scan, then document max + top-k
  *   msa_route_scores_backward  training: gradient of the routing scores (Qr, selected Krbar)
  *   msa_topk_docs           online: the k most relevant documents
  *   msa_fetch_docs          online: copy the selected content KV from pinned host
@@ -30,8 +31,11 @@
  *     are passed as uint16_t bit patterns.  Pointers are device pointers
  *     unless the parameter name ends in _host.
  *   - The caller allocates and frees every buffer (including workspaces and the
- *     pinned host store).  The library allocates nothing and keeps no state
- *     besides a thread-local error message.
+ *     pinned host store).  The library allocates nothing.  Its only state: a
+ *     thread-local error message; per host thread, the RoPE constants of the
+ *     last attention launch (a pure function of its rope_offset and rope_base,
+ *     kept to skip recomputing them); per device, the compute-unit count (read
+ *     once, used to size the routing scan's grid).
  *   - Calls are asynchronous on `stream`; results are valid once the stream has
  *     reached the call.  Arguments are validated on the host before anything
  *     is launched: an invalid call returns a negative status and launches
@@ -180,17 +184,22 @@ int msa_store_append(uint16_t* Krbar, float* inv_norm, int64_t* doc_chunk_off, i
  *
  *   S[b,t,g]           = (1/H) sum_h cos(Qr[b,t,h,:], Krbar[g,h,:])   (cos := 0 on a zero vector)
  *   chunk_scores[b,g]  = max_{t<T} S[b,t,g]
- *   doc_scores[b,d]    = max over d's chunks, or -inf where doc_exclude[b,d] != 0
+ *   doc_scores[b,d]    = max over d's chunks, or -inf where doc_exclude[b,d] != 0 or
+ *                        where d has no chunks (doc_chunk_off[d] == doc_chunk_off[d+1])
  *
  *   Qr            bf16 [B, T, H, D]
  *   Krbar         bf16 [n_chunks, H, D]        (HBM-resident routing-key store)
  *   krbar_inv_norm fp32 [n_chunks, H] from msa_krbar_inv_norms for this Krbar, or
  *                 NULL (the scan then derives the norms from the tiles it streams)
- *   doc_chunk_off int64 [n_docs+1] (device), doc_chunk_off[0] == 0, doc_chunk_off[n_docs] == n_chunks
+ *   doc_chunk_off int64 [n_docs+1] (device), non-decreasing, doc_chunk_off[0] == 0,
+ *                 doc_chunk_off[n_docs] == n_chunks (empty documents allowed)
  *   doc_exclude   uint8 [B, n_docs] or NULL
  *   doc_scores    fp32 [B, n_docs] out
  *   chunk_scores  fp32 [B, n_chunks] out, or NULL
- *   workspace     >= msa_route_workspace_bytes(B, T, H, D, n_chunks, n_docs) bytes
+ *   workspace     >= msa_route_workspace_bytes(B, T, H, D, n_chunks, n_docs) bytes, all
+ *                 zero before its first use (hipMemset, a zero-filled allocation or
+ *                 msa_route_workspace_clear); every successful call returns it to zero,
+ *                 so it can be reused without clearing.  After MSA_ERR_HIP clear it again.
  *   H in {1,2,4,8}, D == 128, B >= 1, T >= 1, n_docs >= 1.
  * Products use the raw bf16 operands (exact) with fp32 accumulation; norms are
  * applied in fp32.  Results are deterministic (max reductions only).
@@ -250,8 +259,9 @@ int msa_route_scores_backward(const uint16_t* Qr, int B, int T, int H, int D,
  *
  *   Krbar      bf16 [n_chunks, H, D], D == 128
  *   inv_norm   fp32 [n_chunks, H] out (hardware reciprocal square root, ~1 ulp)
- * Pass the result as krbar_inv_norm to msa_route_scores (used when H >= 4 and
- * B*T > 15; otherwise the scan computes the norms itself).
+ * Pass the result as krbar_inv_norm to msa_route_scores / msa_route_topk /
+ * msa_route_scan (used when H >= 4; with H < 4 the scan derives the norms from
+ * the tiles it streams).
  */
 int msa_krbar_inv_norms(const uint16_t* Krbar, int64_t n_chunks, int H, int D, float* inv_norm,
                         hipStream_t stream);
@@ -282,7 +292,9 @@ int msa_topk_docs(const float* doc_scores, int B, int64_t n_docs, int k,
  *   arguments as msa_route_scores, plus k and
  *   top_idx     int32 [B, k] out; top_scores fp32 [B, k] out
  *   workspace   >= msa_route_topk_workspace_bytes(B, T, H, D, n_chunks, n_docs, k)
- *               bytes, 16-byte aligned (0 returned for k outside 1..32)
+ *               bytes, 16-byte aligned (0 returned for k outside 1..32); zero before
+ *               its first use and returned to zero by every successful call, as for
+ *               msa_route_scores
  *   doc_scores  fp32 [B, n_docs] out (as msa_route_scores); chunk_scores optional
  */
 size_t msa_route_topk_workspace_bytes(int B, int T, int H, int D, int64_t n_chunks, int64_t n_docs, int k);
@@ -291,6 +303,45 @@ int msa_route_topk(const uint16_t* Qr, int B, int T, int H, int D, const uint16_
                    const uint8_t* doc_exclude, int k, float* doc_scores, float* chunk_scores,
                    int32_t* top_idx, float* top_scores, void* workspace, size_t workspace_bytes,
                    hipStream_t stream);
+
+/*
+ * msa_route_scan / msa_route_select -- msa_route_topk (or msa_route_scores) as two
+ * calls: the scan over the store (the only step whose cost grows with the memory),
+ * then the document max and the top-k.  Between them the chunk maxima live in the
+ * workspace (an opaque encoding), so the two calls must get the same workspace, in
+ * order, on one stream (or ordered by events).  The scan alone can then be timed
+ * or overlapped with other work.
+ *
+ * Defined by: as msa_route_scores (b-lab.team summary sec. 1, the cosine scan and
+ * the token maximum) and msa_topk_docs (document selection).
+ *
+ * msa_route_scan:   Qr, B, T, H, D, Krbar, krbar_inv_norm, n_chunks as msa_route_scores;
+ *                   workspace >= msa_route_workspace_bytes(B, T, H, D, n_chunks, 1) bytes,
+ *                   zero on entry (see msa_route_scores).
+ * msa_route_select: B, n_chunks, doc_chunk_off, n_docs, doc_exclude, doc_scores,
+ *                   chunk_scores as msa_route_scores; 0 <= k <= 32.  k == 0: document
+ *                   scores only (top_idx, top_scores may be NULL; workspace >=
+ *                   msa_route_workspace_bytes); k >= 1: also top_idx int32 [B, k] and
+ *                   top_scores fp32 [B, k] as msa_topk_docs, workspace >=
+ *                   msa_route_topk_workspace_bytes(B, 1, 1, 128, n_chunks, n_docs, k).
+ *                   Returns the workspace to zero.
+ * scan + select(k) gives msa_route_topk's outputs bit for bit; scan + select(0) gives
+ * msa_route_scores'.
+ */
+int msa_route_scan(const uint16_t* Qr, int B, int T, int H, int D, const uint16_t* Krbar,
+                   const float* krbar_inv_norm, int64_t n_chunks, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream);
+int msa_route_select(int B, int64_t n_chunks, const int64_t* doc_chunk_off, int64_t n_docs,
+                     const uint8_t* doc_exclude, int k, float* doc_scores, float* chunk_scores, int32_t* top_idx,
+                     float* top_scores, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * msa_route_workspace_clear -- set a routing workspace to zero with a kernel on
+ * `stream` (no memset node, so it can be recorded into a graph); needed once per
+ * new workspace and after a call that returned MSA_ERR_HIP.
+ *   workspace_bytes a multiple of 4; workspace 16-byte aligned.
+ */
+int msa_route_workspace_clear(void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * msa_fetch_docs -- context assembly from the host tier (host-driven copies).

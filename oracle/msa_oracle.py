@@ -2,6 +2,8 @@
 
 TEST INFRASTRUCTURE ONLY.  Plain, slow, float64 numpy code that states what the
 path computes, step by step, so that the HIP kernels can be checked against it.
+(``pool_means`` is also restated in plain C, oracle/csrc/pool_means.c through
+oracle/native.py, so that whole corpora can be pooled; the two are pinned equal.)
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import it; the product library never does, and it shares no
 code, constants or helpers with ``sparse_retrieval_memory_amd/``.
@@ -134,6 +136,28 @@ def pool(K, V, Kr, doc_len: Sequence[int], chunk: int, base: float):
     return Kb, Vb, Rb, off_c
 
 
+def pool_means(X, doc_len: Sequence[int], chunk: int) -> np.ndarray:
+    """Chunk means of X without rotation: the V and K_r part of ``pool``.
+
+    Same chunking as ``pool`` ([medium] sec. 2: fixed-length chunks that never
+    cross a document, a trailing partial chunk averaged over its actual length),
+    written as one segmented sum over the tokens so that whole corpora can be
+    pooled.  X: [n_tok, ...] in document order; returns float64 [n_chunks, ...].
+    """
+    X = np.asarray(X, dtype=np.float64)
+    L = np.asarray(doc_len, dtype=np.int64)
+    n_ch = (L + chunk - 1) // chunk
+    tok_off = np.concatenate([[0], np.cumsum(L)])
+    doc = np.repeat(np.arange(len(L)), n_ch)                  # document of every chunk
+    j = np.arange(int(n_ch.sum())) - np.repeat(np.cumsum(n_ch) - n_ch, n_ch)   # chunk index within it
+    start = tok_off[doc] + j * chunk
+    count = np.minimum(chunk, L[doc] - j * chunk)
+    if len(start) == 0:
+        return np.zeros((0,) + X.shape[1:])
+    sums = np.add.reduceat(X[:int(tok_off[-1])], start, axis=0)
+    return sums / count.reshape((-1,) + (1,) * (X.ndim - 1))
+
+
 def encode_router_keys(hidden, W, doc_len: Sequence[int], chunk: int, H: int, D: int):
     """Global memory encoding of the router keys: project, then chunk-mean pool.
 
@@ -190,7 +214,7 @@ def route(Qr, Krbar, doc_chunk_off, exclude=None, block: int = 65536):
     pooled K_r by cosine similarity, averaged over heads, then the token-wise
     maximum is taken; [medium] sec. 2 / [blab] pipeline stage 2: the result
     ranks documents.  Document score = max over its chunks.  Excluded
-    documents score -inf.
+    documents, and documents with no chunks, score -inf.
 
     Qr: [B, T, H, D]; Krbar: [G, H, D]; doc_chunk_off: [n_docs + 1];
     exclude: bool [B, n_docs] or None.  Returns (chunk_scores [B, G],
@@ -206,7 +230,13 @@ def route(Qr, Krbar, doc_chunk_off, exclude=None, block: int = 65536):
         g1 = min(G, g0 + block)
         S = head_mean_cosine(rows, np.asarray(Krbar[g0:g1], dtype=np.float64))
         chunk[:, g0:g1] = S.reshape(B, T, g1 - g0).max(axis=1)
-    doc = np.maximum.reduceat(chunk, off[:-1], axis=1) if G else np.empty((B, 0))
+    # a document's score is the max over its own chunks; a document without
+    # chunks has nothing to score and gets -inf, like an excluded one
+    n_docs = len(off) - 1
+    doc = np.full((B, n_docs), -np.inf)
+    has = np.flatnonzero(off[1:] > off[:-1])
+    if len(has):
+        doc[:, has] = np.maximum.reduceat(chunk[:, :off[-1]], off[has], axis=1)
     if exclude is not None:
         doc = np.where(np.asarray(exclude, dtype=bool), -np.inf, doc)
     return chunk, doc

@@ -222,12 +222,70 @@ int msa_route_topk(const uint16_t* Qr, int B, int T, int H, int D, const uint16_
   MSA_CHECK_ARG(aligned16(workspace), "workspace must be 16-byte aligned");
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
   const size_t r = (msa::route_workspace(B, T, H, n_chunks, n_docs) + 255) & ~(size_t)255;
-  int rc = msa::launch_route(Qr, B, T, H, Krbar, krbar_inv_norm, n_chunks, doc_chunk_off, n_docs, doc_exclude,
-                             doc_scores, chunk_scores, ws, stream, /*reduce_docs=*/false);
+  int rc = msa::launch_route_scan(Qr, B, T, H, Krbar, krbar_inv_norm, n_chunks, reinterpret_cast<uint32_t*>(ws),
+                                  stream);
   if (rc != MSA_OK) return rc;
-  return msa::launch_docs_topk(reinterpret_cast<const uint32_t*>(ws), n_chunks, doc_chunk_off, n_docs, doc_exclude,
+  return msa::launch_docs_topk(reinterpret_cast<uint32_t*>(ws), n_chunks, doc_chunk_off, n_docs, doc_exclude,
                                B, k, doc_scores, chunk_scores, top_idx, top_scores,
                                reinterpret_cast<uint64_t*>(ws + r), stream);
+}
+
+int msa_route_scan(const uint16_t* Qr, int B, int T, int H, int D, const uint16_t* Krbar,
+                   const float* krbar_inv_norm, int64_t n_chunks, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream) {
+  msa::clear_error();
+  MSA_CHECK_ARG(B >= 1 && T >= 1, "B >= 1 and T >= 1 required (B=%d, T=%d)", B, T);
+  MSA_CHECK_ARG(n_chunks >= 0, "n_chunks >= 0 required");
+  MSA_CHECK_ARG(Qr && (Krbar || n_chunks == 0), "null pointer");
+  MSA_CHECK_SUPPORTED(D == 128, "D=%d unsupported (D must be 128)", D);
+  MSA_CHECK_SUPPORTED(H == 1 || H == 2 || H == 4 || H == 8, "H=%d unsupported (1, 2, 4 or 8)", H);
+  MSA_CHECK_ARG(B <= 65535 && (int64_t)B * T <= (1 << 24), "B*T too large");
+  MSA_CHECK_ARG(n_chunks < ((int64_t)1 << 40), "size out of range");
+  MSA_CHECK_ARG(aligned16(Qr) && (n_chunks == 0 || aligned16(Krbar)), "Qr and Krbar must be 16-byte aligned");
+  MSA_CHECK_ARG(krbar_inv_norm == nullptr || aligned16(krbar_inv_norm), "krbar_inv_norm must be 16-byte aligned");
+  const size_t need = msa::route_workspace(B, T, H, n_chunks, 1);
+  if (workspace_bytes < need || (need > 0 && workspace == nullptr)) {
+    msa::set_error("workspace %zu bytes < required %zu", workspace_bytes, need);
+    return MSA_ERR_WORKSPACE;
+  }
+  MSA_CHECK_ARG(workspace == nullptr || aligned16(workspace), "workspace must be 16-byte aligned");
+  return msa::launch_route_scan(Qr, B, T, H, Krbar, krbar_inv_norm, n_chunks, reinterpret_cast<uint32_t*>(workspace),
+                                stream);
+}
+
+int msa_route_select(int B, int64_t n_chunks, const int64_t* doc_chunk_off, int64_t n_docs,
+                     const uint8_t* doc_exclude, int k, float* doc_scores, float* chunk_scores, int32_t* top_idx,
+                     float* top_scores, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  msa::clear_error();
+  MSA_CHECK_ARG(B >= 1 && B <= 65535, "1 <= B <= 65535 required (B=%d)", B);
+  MSA_CHECK_ARG(n_docs >= 1 && n_chunks >= 0, "n_docs >= 1 and n_chunks >= 0 required");
+  MSA_CHECK_ARG(doc_chunk_off && doc_scores, "null pointer");
+  MSA_CHECK_SUPPORTED(k >= 0 && k <= 32, "k=%d unsupported here (0..32; larger k: msa_topk_docs)", k);
+  MSA_CHECK_ARG(k <= n_docs, "k=%d > n_docs", k);
+  MSA_CHECK_ARG(k == 0 || (top_idx && top_scores), "null top-k output");
+  MSA_CHECK_ARG(n_docs < 0x7FFFFFFF / 256 * 256 && n_chunks < ((int64_t)1 << 40), "size out of range");
+  const size_t r = (msa::route_workspace(B, 1, 1, n_chunks, n_docs) + 255) & ~(size_t)255;
+  const size_t need = k == 0 ? msa::route_workspace(B, 1, 1, n_chunks, n_docs) : r + msa::topk_workspace(B, n_docs, k);
+  if (workspace_bytes < need || (need > 0 && workspace == nullptr)) {
+    msa::set_error("workspace %zu bytes < required %zu", workspace_bytes, need);
+    return MSA_ERR_WORKSPACE;
+  }
+  MSA_CHECK_ARG(workspace == nullptr || aligned16(workspace), "workspace must be 16-byte aligned");
+  uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
+  if (k == 0)
+    return msa::launch_doc_reduce(reinterpret_cast<uint32_t*>(ws), n_chunks, doc_chunk_off, n_docs, doc_exclude, B,
+                                  doc_scores, chunk_scores, stream);
+  return msa::launch_docs_topk(reinterpret_cast<uint32_t*>(ws), n_chunks, doc_chunk_off, n_docs, doc_exclude, B, k,
+                               doc_scores, chunk_scores, top_idx, top_scores, reinterpret_cast<uint64_t*>(ws + r),
+                               stream);
+}
+
+int msa_route_workspace_clear(void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  msa::clear_error();
+  MSA_CHECK_ARG(workspace != nullptr || workspace_bytes == 0, "null workspace");
+  MSA_CHECK_ARG(workspace_bytes % 4 == 0, "workspace_bytes must be a multiple of 4");
+  MSA_CHECK_ARG(workspace == nullptr || aligned16(workspace), "workspace must be 16-byte aligned");
+  return msa::launch_clear_u32(workspace, (int64_t)(workspace_bytes / 4), stream);
 }
 
 size_t msa_route_backward_workspace_bytes(int B, int T, int H, int D, int64_t n_docs) {

@@ -160,10 +160,17 @@ int launch_pool(const uint16_t* K, const uint16_t* V, const uint16_t* Kr, const 
                 const int64_t* doc_chunk_off, int64_t n_docs, int64_t n_tok, int64_t n_chunks, int H,
                 int chunk_len, double rope_base, uint16_t* Kbar, uint16_t* Vbar, uint16_t* Krbar,
                 hipStream_t stream);
+// Routing workspace contract: the chunk maxima (B * n_chunks uint32, the order-preserving
+// encoding) start at 0 and are set back to 0 by the document max that reads them; the
+// top-k's group maxima are cleared by the selection that reads them.
 int launch_route(const uint16_t* Qr, int B, int T, int H, const uint16_t* Krbar, const float* inv_norm,
                  int64_t n_chunks, const int64_t* doc_chunk_off, int64_t n_docs, const uint8_t* doc_exclude,
-                 float* doc_scores, float* chunk_scores, void* workspace, hipStream_t stream,
-                 bool reduce_docs = true);
+                 float* doc_scores, float* chunk_scores, void* workspace, hipStream_t stream);
+int launch_route_scan(const uint16_t* Qr, int B, int T, int H, const uint16_t* Krbar, const float* inv_norm,
+                      int64_t n_chunks, uint32_t* chunk_enc, hipStream_t stream);
+int launch_doc_reduce(uint32_t* chunk_enc, int64_t n_chunks, const int64_t* doc_chunk_off, int64_t n_docs,
+                      const uint8_t* doc_exclude, int B, float* doc_scores, float* chunk_scores, hipStream_t stream);
+int launch_clear_u32(void* p, int64_t words, hipStream_t stream);
 int launch_krbar_norms(const uint16_t* Krbar, int64_t n_chunks, int H, float* inv_norm, hipStream_t stream);
 size_t route_workspace(int B, int T, int H, int64_t n_chunks, int64_t n_docs);
 int launch_topk(const float* doc_scores, int B, int64_t n_docs, int k, int32_t* top_idx,
@@ -171,7 +178,7 @@ int launch_topk(const float* doc_scores, int B, int64_t n_docs, int k, int32_t* 
 size_t topk_workspace(int B, int64_t n_docs, int k);
 // Document max from the scan's chunk maxima fused with top-k's group maxima, then the
 // group-based top-k (1 <= k <= 32); gmax holds B * ceil(n_docs / 64) keys.
-int launch_docs_topk(const uint32_t* chunk_enc, int64_t n_chunks, const int64_t* doc_chunk_off, int64_t n_docs,
+int launch_docs_topk(uint32_t* chunk_enc, int64_t n_chunks, const int64_t* doc_chunk_off, int64_t n_docs,
                      const uint8_t* doc_exclude, int B, int k, float* doc_scores, float* chunk_scores,
                      int32_t* top_idx, float* top_scores, uint64_t* gmax, hipStream_t stream);
 int launch_attn(const uint16_t* Q, int B, int Tq, int Hq, const uint16_t* Kloc, const uint16_t* Vloc,

@@ -432,8 +432,11 @@ krbar_norms_kernel(const uint16_t* __restrict__ Krbar, int64_t n_rows, float* __
 }
 
 // ------------------------------------------------------------ document max
+// Each document's thread reads its chunks' maxima and sets them back to 0 (re-arming
+// the workspace for the next scan: documents own disjoint chunk ranges, so no other
+// thread touches those words).
 __global__ void __launch_bounds__(256)
-doc_reduce_kernel(const uint32_t* __restrict__ chunk_enc, int64_t n_chunks,
+doc_reduce_kernel(uint32_t* __restrict__ chunk_enc, int64_t n_chunks,
                   const int64_t* __restrict__ doc_chunk_off, int64_t n_docs,
                   const uint8_t* __restrict__ doc_exclude, float* __restrict__ doc_scores,
                   float* __restrict__ chunk_scores) {
@@ -443,10 +446,11 @@ doc_reduce_kernel(const uint32_t* __restrict__ chunk_enc, int64_t n_chunks,
   int64_t g0 = doc_chunk_off[d], g1 = doc_chunk_off[d + 1];
   if (g0 < 0) g0 = 0;
   if (g1 > n_chunks) g1 = n_chunks;
-  const uint32_t* ce = chunk_enc + (int64_t)b * n_chunks;
+  uint32_t* ce = chunk_enc + (int64_t)b * n_chunks;
   uint32_t best = 0;
   for (int64_t g = g0; g < g1; ++g) {
     const uint32_t e = ce[g];
+    ce[g] = 0u;
     best = e > best ? e : best;
     if (chunk_scores) chunk_scores[(int64_t)b * n_chunks + g] = dec_f32(e);
   }
@@ -455,17 +459,24 @@ doc_reduce_kernel(const uint32_t* __restrict__ chunk_enc, int64_t n_chunks,
   doc_scores[(int64_t)b * n_docs + d] = s;
 }
 
+// Compute units of the calling thread's current device, looked up once per device.
+// Every thread that fills a slot stores the same value, so relaxed atomics suffice.
 int num_cus() {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-      cus = v;
-    else
-      cus = 256;
+  constexpr int MAXDEV = 64;
+  static int cus[MAXDEV] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  if (dev >= MAXDEV) {
+    int v = 0;
+    return hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0 ? v : 256;
   }
-  return cus;
+  int c = __atomic_load_n(&cus[dev], __ATOMIC_RELAXED);
+  if (c == 0) {
+    int v = 0;
+    c = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0 ? v : 256;
+    __atomic_store_n(&cus[dev], c, __ATOMIC_RELAXED);
+  }
+  return c;
 }
 
 template <int H>
@@ -482,14 +493,8 @@ int launch_route_h(const uint16_t* Qr, int B, int T, const uint16_t* Krbar, cons
   const int64_t per = (n_tiles + S - 1) / S;
   S = (n_tiles + per - 1) / per;
   const int64_t grid = ((S + 7) / 8) * 8 * (int64_t)P;
-  // fill with the encoding's minimum: below every float, so atomicMax takes the first value
-  {
-    const int64_t n = (int64_t)B * n_chunks;
-    int64_t blocks = ((n >> 2) + 255) / 256;
-    blocks = blocks < 1 ? 1 : (blocks > 2048 ? 2048 : blocks);
-    hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, chunk_enc, n, 0u);
-  }
-  MSA_CHECK_LAUNCH();
+  // The chunk maxima arrive armed: every word holds 0, the encoding's minimum (below
+  // every float), so atomicMax takes the first value; the document max re-arms them.
   // A slice read by one row block is streamed once: its copies take the non-temporal
   // policy.  Several row blocks of a slice share its lines in L2, so those keep the default.
 #define MSA_ROUTE_MFMA(NORMS_, POL_, KN_)                                                                    \
@@ -529,26 +534,43 @@ int launch_krbar_norms(const uint16_t* Krbar, int64_t n_chunks, int H, float* in
   return MSA_OK;
 }
 
-int launch_route(const uint16_t* Qr, int B, int T, int H, const uint16_t* Krbar, const float* inv_norm,
-                 int64_t n_chunks, const int64_t* doc_chunk_off, int64_t n_docs, const uint8_t* doc_exclude,
-                 float* doc_scores, float* chunk_scores, void* workspace, hipStream_t stream,
-                 bool reduce_docs) {
-  uint32_t* chunk_enc = reinterpret_cast<uint32_t*>(workspace);
-  int rc = MSA_OK;
-  if (n_chunks > 0) {
-    switch (H) {
-      case 1: rc = launch_route_h<1>(Qr, B, T, Krbar, inv_norm, n_chunks, chunk_enc, stream); break;
-      case 2: rc = launch_route_h<2>(Qr, B, T, Krbar, inv_norm, n_chunks, chunk_enc, stream); break;
-      case 4: rc = launch_route_h<4>(Qr, B, T, Krbar, inv_norm, n_chunks, chunk_enc, stream); break;
-      case 8: rc = launch_route_h<8>(Qr, B, T, Krbar, inv_norm, n_chunks, chunk_enc, stream); break;
-      default: set_error("H=%d unsupported", H); return MSA_ERR_UNSUPPORTED;
-    }
-    if (rc != MSA_OK) return rc;
+int launch_route_scan(const uint16_t* Qr, int B, int T, int H, const uint16_t* Krbar, const float* inv_norm,
+                      int64_t n_chunks, uint32_t* chunk_enc, hipStream_t stream) {
+  if (n_chunks == 0) return MSA_OK;
+  switch (H) {
+    case 1: return launch_route_h<1>(Qr, B, T, Krbar, inv_norm, n_chunks, chunk_enc, stream);
+    case 2: return launch_route_h<2>(Qr, B, T, Krbar, inv_norm, n_chunks, chunk_enc, stream);
+    case 4: return launch_route_h<4>(Qr, B, T, Krbar, inv_norm, n_chunks, chunk_enc, stream);
+    case 8: return launch_route_h<8>(Qr, B, T, Krbar, inv_norm, n_chunks, chunk_enc, stream);
+    default: set_error("H=%d unsupported", H); return MSA_ERR_UNSUPPORTED;
   }
-  if (!reduce_docs) return MSA_OK;           // the caller reduces the chunk maxima itself
+}
+
+int launch_doc_reduce(uint32_t* chunk_enc, int64_t n_chunks, const int64_t* doc_chunk_off, int64_t n_docs,
+                      const uint8_t* doc_exclude, int B, float* doc_scores, float* chunk_scores, hipStream_t stream) {
   dim3 grid((unsigned)((n_docs + 255) / 256), (unsigned)B);
   hipLaunchKernelGGL(doc_reduce_kernel, grid, dim3(256), 0, stream, chunk_enc, n_chunks, doc_chunk_off,
                      n_docs, doc_exclude, doc_scores, chunk_scores);
+  MSA_CHECK_LAUNCH();
+  return MSA_OK;
+}
+
+int launch_route(const uint16_t* Qr, int B, int T, int H, const uint16_t* Krbar, const float* inv_norm,
+                 int64_t n_chunks, const int64_t* doc_chunk_off, int64_t n_docs, const uint8_t* doc_exclude,
+                 float* doc_scores, float* chunk_scores, void* workspace, hipStream_t stream) {
+  uint32_t* chunk_enc = reinterpret_cast<uint32_t*>(workspace);
+  const int rc = launch_route_scan(Qr, B, T, H, Krbar, inv_norm, n_chunks, chunk_enc, stream);
+  if (rc != MSA_OK) return rc;
+  return launch_doc_reduce(chunk_enc, n_chunks, doc_chunk_off, n_docs, doc_exclude, B, doc_scores, chunk_scores,
+                           stream);
+}
+
+int launch_clear_u32(void* p, int64_t words, hipStream_t stream) {
+  if (words <= 0) return MSA_OK;
+  int64_t blocks = ((words >> 2) + 255) / 256;
+  blocks = blocks < 1 ? 1 : (blocks > 2048 ? 2048 : blocks);
+  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, reinterpret_cast<uint32_t*>(p),
+                     words, 0u);
   MSA_CHECK_LAUNCH();
   return MSA_OK;
 }

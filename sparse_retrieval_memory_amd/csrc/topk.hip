@@ -212,15 +212,23 @@ __device__ __forceinline__ void topk_by_waves(int64_t n, int k, Get key, uint64_
   __syncthreads();
 }
 
+// Set a query's group maxima back to 0 once every wave is past its last read of them
+// (the routing workspace is handed back cleared; see launch_docs_topk).
+__device__ __forceinline__ void clear_groups(uint64_t* gm, int64_t n_groups) {
+  __syncthreads();
+  for (int64_t x = threadIdx.x; x < n_groups; x += blockDim.x) gm[x] = 0ull;
+}
+
 template <int RM, int RB>   // RM: merge keys per lane; RB = ceil(k / P2_WAVES) winning groups per wave
 __global__ void __launch_bounds__(64 * P2_WAVES)
-topk_from_groups(const float* __restrict__ scores, const uint64_t* __restrict__ gmax, int64_t n_docs,
-                 int64_t n_groups, int k, int32_t* __restrict__ top_idx, float* __restrict__ top_scores) {
+topk_from_groups(const float* __restrict__ scores, uint64_t* __restrict__ gmax, int64_t n_docs,
+                 int64_t n_groups, int k, int32_t* __restrict__ top_idx, float* __restrict__ top_scores,
+                 int clear) {
   __shared__ uint64_t lists[P2_WAVES][64];
   __shared__ uint64_t groups[64];
   const int b = blockIdx.x;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const uint64_t* gm = gmax + (int64_t)b * n_groups;
+  uint64_t* gm = gmax + (int64_t)b * n_groups;
 
   // A: the k best group maxima
   topk_by_waves<RM>(n_groups, k, [&](int64_t x) { return gm[x]; }, lists, groups, wave, lane);
@@ -250,6 +258,7 @@ topk_from_groups(const float* __restrict__ scores, const uint64_t* __restrict__ 
       top_scores[(int64_t)b * k + lane] = dec_f32((uint32_t)(key >> 32));
     }
   }
+  if (clear) clear_groups(gmax + (int64_t)b * n_groups, n_groups);
 }
 
 // k <= P2_WAVES: the same two selections, each preceded by a threshold that
@@ -304,8 +313,9 @@ __device__ __forceinline__ void append_ge(uint64_t key, uint64_t t, uint64_t* li
 
 template <int RM>
 __global__ void __launch_bounds__(64 * P2_WAVES)
-topk_from_groups_filtered(const float* __restrict__ scores, const uint64_t* __restrict__ gmax, int64_t n_docs,
-                          int64_t n_groups, int k, int32_t* __restrict__ top_idx, float* __restrict__ top_scores) {
+topk_from_groups_filtered(const float* __restrict__ scores, uint64_t* __restrict__ gmax, int64_t n_docs,
+                          int64_t n_groups, int k, int32_t* __restrict__ top_idx, float* __restrict__ top_scores,
+                          int clear) {
   __shared__ uint64_t lists[P2_WAVES][64];
   __shared__ uint64_t groups[64];
   __shared__ uint64_t list[LIST_CAP];
@@ -314,7 +324,7 @@ topk_from_groups_filtered(const float* __restrict__ scores, const uint64_t* __re
   __shared__ int count;
   const int b = blockIdx.x;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const uint64_t* gm = gmax + (int64_t)b * n_groups;
+  uint64_t* gm = gmax + (int64_t)b * n_groups;
   const int64_t per = (n_groups + P2_WAVES - 1) / P2_WAVES;
   const int64_t g0 = wave * per;
   const int64_t g1 = (g0 + per < n_groups) ? g0 + per : n_groups;
@@ -390,13 +400,15 @@ topk_from_groups_filtered(const float* __restrict__ scores, const uint64_t* __re
     top_idx[(int64_t)b * k + lane] = (int32_t)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFull));
     top_scores[(int64_t)b * k + lane] = dec_f32((uint32_t)(key >> 32));
   }
+  if (clear) clear_groups(gm, n_groups);
 }
 
 // The document max (the last step of the routing scores: a document's score is the max of its
 // chunks', -inf when excluded or empty) with the group maxima of the top-k folded in: a wave
 // holds 64 consecutive documents, i.e. one group, so it also writes the group's largest key.
+// Each document's thread sets its chunks' maxima back to 0 after reading them.
 __global__ void __launch_bounds__(256)
-doc_reduce_groups_kernel(const uint32_t* __restrict__ chunk_enc, int64_t n_chunks,
+doc_reduce_groups_kernel(uint32_t* __restrict__ chunk_enc, int64_t n_chunks,
                          const int64_t* __restrict__ doc_chunk_off, int64_t n_docs,
                          const uint8_t* __restrict__ doc_exclude, float* __restrict__ doc_scores,
                          float* __restrict__ chunk_scores, int64_t n_groups, uint64_t* __restrict__ gmax) {
@@ -407,10 +419,11 @@ doc_reduce_groups_kernel(const uint32_t* __restrict__ chunk_enc, int64_t n_chunk
     int64_t g0 = doc_chunk_off[d], g1 = doc_chunk_off[d + 1];
     if (g0 < 0) g0 = 0;
     if (g1 > n_chunks) g1 = n_chunks;
-    const uint32_t* ce = chunk_enc + (int64_t)b * n_chunks;
+    uint32_t* ce = chunk_enc + (int64_t)b * n_chunks;
     uint32_t best = 0;
     for (int64_t g = g0; g < g1; ++g) {
       const uint32_t e = ce[g];
+      ce[g] = 0u;                             // re-arm the chunk maximum for the next scan
       best = e > best ? e : best;
       if (chunk_scores) chunk_scores[(int64_t)b * n_chunks + g] = dec_f32(e);
     }
@@ -430,14 +443,14 @@ doc_reduce_groups_kernel(const uint32_t* __restrict__ chunk_enc, int64_t n_chunk
 
 // The group-based selection from group maxima already in gmax (1 <= k <= 32).
 int launch_topk_from_groups(const float* doc_scores, int B, int64_t n_docs, int k, int32_t* top_idx,
-                            float* top_scores, const uint64_t* gmax, hipStream_t stream) {
+                            float* top_scores, uint64_t* gmax, int clear, hipStream_t stream) {
   const int64_t n_groups = (n_docs + GROUP - 1) / GROUP;
 #define MSA_TOPK_GROUPS(RMV, RBV)                                                                        \
   hipLaunchKernelGGL((topk_from_groups<RMV, RBV>), dim3((unsigned)B), dim3(64 * P2_WAVES), 0, stream, doc_scores, \
-                     gmax, n_docs, n_groups, k, top_idx, top_scores)
+                     gmax, n_docs, n_groups, k, top_idx, top_scores, clear)
 #define MSA_TOPK_FILTERED(RMV)                                                                          \
   hipLaunchKernelGGL((topk_from_groups_filtered<RMV>), dim3((unsigned)B), dim3(64 * P2_WAVES), 0, stream,     \
-                     doc_scores, gmax, n_docs, n_groups, k, top_idx, top_scores)
+                     doc_scores, gmax, n_docs, n_groups, k, top_idx, top_scores, clear)
   if (k <= 4) MSA_TOPK_FILTERED(1);
   else if (k <= 8) MSA_TOPK_FILTERED(2);
   else if (k <= 16) MSA_TOPK_FILTERED(4);
@@ -454,7 +467,7 @@ int launch_topk_small(const float* doc_scores, int B, int64_t n_docs, int k, int
   hipLaunchKernelGGL(topk_group_max, dim3((unsigned)((n_docs + 255) / 256), (unsigned)B), dim3(256), 0, stream,
                      doc_scores, n_docs, n_groups, gmax);
   MSA_CHECK_LAUNCH();
-  return launch_topk_from_groups(doc_scores, B, n_docs, k, top_idx, top_scores, gmax, stream);
+  return launch_topk_from_groups(doc_scores, B, n_docs, k, top_idx, top_scores, gmax, 0, stream);
 }
 
 int64_t pass1_blocks(int64_t n_docs, int k) {
@@ -464,7 +477,7 @@ int64_t pass1_blocks(int64_t n_docs, int k) {
 
 }  // namespace
 
-int launch_docs_topk(const uint32_t* chunk_enc, int64_t n_chunks, const int64_t* doc_chunk_off, int64_t n_docs,
+int launch_docs_topk(uint32_t* chunk_enc, int64_t n_chunks, const int64_t* doc_chunk_off, int64_t n_docs,
                      const uint8_t* doc_exclude, int B, int k, float* doc_scores, float* chunk_scores,
                      int32_t* top_idx, float* top_scores, uint64_t* gmax, hipStream_t stream) {
   const int64_t n_groups = (n_docs + GROUP - 1) / GROUP;
@@ -472,7 +485,7 @@ int launch_docs_topk(const uint32_t* chunk_enc, int64_t n_chunks, const int64_t*
                      stream, chunk_enc, n_chunks, doc_chunk_off, n_docs, doc_exclude, doc_scores, chunk_scores,
                      n_groups, gmax);
   MSA_CHECK_LAUNCH();
-  return launch_topk_from_groups(doc_scores, B, n_docs, k, top_idx, top_scores, gmax, stream);
+  return launch_topk_from_groups(doc_scores, B, n_docs, k, top_idx, top_scores, gmax, 1, stream);
 }
 
 size_t topk_workspace(int B, int64_t n_docs, int k) {

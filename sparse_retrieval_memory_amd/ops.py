@@ -40,16 +40,23 @@ def _dev(t: torch.Tensor, name: str):
 
 
 def workspace(nbytes: int, device, tag: str = "route") -> torch.Tensor:
-    """A cached device scratch buffer of at least nbytes (one per device and tag).
+    """A cached device scratch buffer of at least nbytes (one per device and tag),
+    zero-filled when allocated (the routing calls need a zero workspace on their
+    first use and hand it back zeroed).
 
     Calls on one stream reuse it in order; callers that run on several streams
     at once pass their own buffers instead."""
     key = (torch.device(device), tag)
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:
-        buf = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=key[0])
+        buf = torch.zeros(max((int(nbytes) + 255) // 256 * 256, 256), dtype=torch.uint8, device=key[0])
         _ws_cache[key] = buf
     return buf
+
+
+def route_workspace_clear(ws, stream=None):
+    """msa_route_workspace_clear: zero a routing workspace with a kernel."""
+    _lib.call("msa_route_workspace_clear", _p(ws), ws.numel() * ws.element_size() // 4 * 4, _stream(stream))
 
 
 def pool_chunks(K, V, Kr, doc_tok_off, doc_chunk_off, n_chunks: int, chunk_len: int = 64,
@@ -195,6 +202,38 @@ def route_topk(Qr, Krbar, doc_chunk_off, k: int, doc_exclude=None, krbar_inv_nor
               _p(doc_exclude), k, _p(doc_scores), None, _p(top_idx), _p(top_scores), _p(ws), ws.numel(),
               _stream(stream))
     return doc_scores, top_idx, top_scores
+
+
+def route_scan(Qr, Krbar, ws, krbar_inv_norm=None, stream=None):
+    """msa_route_scan: the scan only; the chunk maxima stay in ``ws`` for route_select."""
+    _bf16(Qr, "Qr"); _bf16(Krbar, "Krbar"); _dev(Qr, "Qr")
+    B, T, H, D = Qr.shape
+    n_chunks = Krbar.shape[0]
+    if krbar_inv_norm is not None:
+        assert krbar_inv_norm.dtype == torch.float32 and krbar_inv_norm.shape == (n_chunks, H)
+    _lib.call("msa_route_scan", _p(Qr), B, T, H, D, _p(Krbar), _p(krbar_inv_norm), n_chunks, _p(ws), ws.numel(),
+              _stream(stream))
+
+
+def route_select(B, n_chunks, doc_chunk_off, k: int, ws, doc_exclude=None, doc_scores=None, chunk_scores=None,
+                 top_idx=None, top_scores=None, stream=None):
+    """msa_route_select: document max (+ top-k for k >= 1) from the chunk maxima route_scan left in ``ws``.
+    Returns doc_scores, or (doc_scores, top_idx, top_scores) for k >= 1."""
+    n_docs = doc_chunk_off.numel() - 1
+    dev = doc_chunk_off.device
+    if doc_scores is None:
+        doc_scores = torch.empty((B, n_docs), dtype=torch.float32, device=dev)
+    if k > 0:
+        if top_idx is None:
+            top_idx = torch.empty((B, k), dtype=torch.int32, device=dev)
+        if top_scores is None:
+            top_scores = torch.empty((B, k), dtype=torch.float32, device=dev)
+    if doc_exclude is not None:
+        assert doc_exclude.dtype in (torch.uint8, torch.bool) and doc_exclude.shape == (B, n_docs)
+        doc_exclude = doc_exclude.contiguous()
+    _lib.call("msa_route_select", B, n_chunks, _p(doc_chunk_off), n_docs, _p(doc_exclude), k, _p(doc_scores),
+              _p(chunk_scores), _p(top_idx), _p(top_scores), _p(ws), ws.numel(), _stream(stream))
+    return (doc_scores, top_idx, top_scores) if k > 0 else doc_scores
 
 
 def route_backward_workspace_bytes(B, T, H, D, n_docs) -> int:

@@ -235,3 +235,32 @@ def test_route_topk_validation():
     assert _code("msa_route_topk", *rt(ti=N)) == E.MSA_ERR_INVALID_ARG
     assert _code("msa_route_topk", *rt(wsb=need - 1)) == E.MSA_ERR_WORKSPACE
     assert _code("msa_route_topk", *rt(ws=N)) == E.MSA_ERR_WORKSPACE
+
+
+def test_route_scan_select_clear_validation():
+    E = _lib
+    p = ctypes.c_void_p(1 << 20)
+    lib = _lib.load()
+    need_scan = lib.msa_route_workspace_bytes(2, 64, 8, 128, 1000, 1)
+    sc = lambda B=2, T=64, H=8, D=128, q=p, ws=p, wsb=need_scan, nrm=N: (q, B, T, H, D, p, nrm, 1000, ws, wsb, N)
+    assert _code("msa_route_scan", *sc(B=0)) == E.MSA_ERR_INVALID_ARG
+    assert _code("msa_route_scan", *sc(q=N)) == E.MSA_ERR_INVALID_ARG
+    assert _code("msa_route_scan", *sc(D=64)) == E.MSA_ERR_UNSUPPORTED
+    assert _code("msa_route_scan", *sc(H=16)) == E.MSA_ERR_UNSUPPORTED
+    assert _code("msa_route_scan", *sc(wsb=need_scan - 1)) == E.MSA_ERR_WORKSPACE
+    assert _code("msa_route_scan", *sc(nrm=ctypes.c_void_p(20))) == E.MSA_ERR_INVALID_ARG
+    need_sel = lib.msa_route_topk_workspace_bytes(2, 1, 1, 128, 1000, 100, 16)
+    sl = lambda B=2, k=16, n_docs=100, off=p, ti=p, ws=p, wsb=need_sel: (
+        B, 1000, off, n_docs, N, k, p, N, ti, p, ws, wsb, N)
+    assert _code("msa_route_select", *sl(k=33)) == E.MSA_ERR_UNSUPPORTED
+    assert _code("msa_route_select", *sl(k=-1)) == E.MSA_ERR_UNSUPPORTED
+    assert _code("msa_route_select", *sl(k=16, n_docs=10)) == E.MSA_ERR_INVALID_ARG
+    assert _code("msa_route_select", *sl(ti=N)) == E.MSA_ERR_INVALID_ARG
+    assert _code("msa_route_select", *sl(off=N)) == E.MSA_ERR_INVALID_ARG
+    assert _code("msa_route_select", *sl(B=0)) == E.MSA_ERR_INVALID_ARG
+    assert _code("msa_route_select", *sl(wsb=need_sel - 1)) == E.MSA_ERR_WORKSPACE
+    # k = 0 needs only the chunk maxima and no top-k outputs: a short workspace is enough
+    assert _code("msa_route_select", *sl(k=0, ti=N, wsb=need_scan - 1)) == E.MSA_ERR_WORKSPACE
+    assert _code("msa_route_workspace_clear", N, 256, N) == E.MSA_ERR_INVALID_ARG
+    assert _code("msa_route_workspace_clear", p, 255, N) == E.MSA_ERR_INVALID_ARG
+    assert _code("msa_route_workspace_clear", ctypes.c_void_p(20), 256, N) == E.MSA_ERR_INVALID_ARG

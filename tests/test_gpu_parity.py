@@ -137,6 +137,104 @@ def test_route_deterministic():
         assert np.array_equal(a.view(np.uint64), b.view(np.uint64))
 
 
+def test_route_empty_documents_match_oracle():
+    """Documents without chunks (leading, several in a row, in the middle, trailing) score -inf and
+    the others keep their own chunks' maximum: msa_route_scores (with and without stored norms),
+    msa_route_topk and msa_route_scan + msa_route_select against the oracle, with exclusions."""
+    r = np.random.default_rng(41)
+    lens = r.integers(1, 5, 300)
+    lens[[0, 7, 8, 9, 150, 297, 298, 299]] = 0
+    B = 2
+    Qr, Kr, off = _route_case(B, 40, 8, 300, seed=41, lens=lens)
+    excl = np.zeros((B, 300), bool); excl[0, [3, 8, 200]] = True
+    empty = lens == 0
+    announce("route-empty-docs")
+    ref_ch, ref_doc = O.route(f64(Qr), f64(Kr), off, excl)
+    assert np.all(ref_doc[:, empty] == -np.inf)
+    fin = np.isfinite(ref_doc)
+    for stored in (False, True):
+        doc, ch = _run_route(Qr, Kr, off, excl, stored_norms=stored)
+        assert np.array_equal(np.isfinite(doc), fin)
+        assert np.abs(doc[fin] - ref_doc[fin]).max() <= SCORE_TOL
+        assert np.abs(ch - ref_ch).max() <= SCORE_TOL
+    q, kr, offd = dev_bits(Qr), dev_bits(Kr), torch.from_numpy(off).to(DEV)
+    ex = torch.from_numpy(excl.astype(np.uint8)).to(DEV)
+    k = 16
+    d1, i1, s1 = ops.route_topk(q, kr, offd, k, doc_exclude=ex)
+    ws = ops.workspace(ops.route_topk_workspace_bytes(B, 40, 8, 128, len(Kr), 300, k), DEV, "test-empty")
+    ops.route_scan(q, kr, ws)
+    d2, i2, s2 = ops.route_select(B, len(Kr), offd, k, ws, doc_exclude=ex)
+    torch.cuda.synchronize()
+    assert np.array_equal(d1.cpu().numpy().view(np.uint32), d2.cpu().numpy().view(np.uint32))
+    assert np.array_equal(i1.cpu().numpy(), i2.cpu().numpy())
+    gi = i1.cpu().numpy()
+    for b in range(B):
+        check_topk(gi[b], ref_doc[b], k)
+        assert not np.any(empty[gi[b]]) and not np.any(excl[b, gi[b]])
+    # more documents requested than have chunks: the rest are -inf documents, lowest ids first
+    lens2 = np.array([0, 2, 0, 1, 0, 0, 3, 0])
+    Qr2, Kr2, off2 = _route_case(1, 5, 8, 8, seed=42, lens=lens2)
+    _, ref2 = O.route(f64(Qr2), f64(Kr2), off2)
+    _, i3, s3 = ops.route_topk(dev_bits(Qr2), dev_bits(Kr2), torch.from_numpy(off2).to(DEV), 6)
+    ridx, rsc = O.topk(ref2, 6)
+    assert list(i3.cpu().numpy()[0]) == list(ridx[0])
+    assert np.all(s3.cpu().numpy()[0][3:] == -np.inf)
+
+
+def test_route_workspace_reuse_across_sizes():
+    """One routing workspace reused by calls of different sizes (batch, chunks, documents, k) in a
+    row, without clearing: every call's outputs are bit-identical to the same call on a fresh
+    zero workspace (each call hands the workspace back zeroed)."""
+    cases = [(2, 40, 3000, 16), (1, 128, 400, 4), (3, 20, 1200, 8), (1, 7, 5000, 32), (2, 64, 50, 1)]
+    max_bytes = max(ops.route_topk_workspace_bytes(B, T, 8, 128, 4 * n, n, k) for B, T, n, k in cases)
+    shared = torch.zeros(max_bytes, dtype=torch.uint8, device=DEV)
+    for i, (B, T, n_docs, k) in enumerate(cases):
+        announce("route-workspace-reuse", B, T, n_docs, k)
+        Qr, Kr, off = _route_case(B, T, 8, n_docs, seed=500 + i)
+        q, kr, offd = dev_bits(Qr), dev_bits(Kr), torch.from_numpy(off).to(DEV)
+        nrm = ops.krbar_inv_norms(kr)
+        fresh = torch.zeros_like(shared)
+        a = ops.route_topk(q, kr, offd, k, krbar_inv_norm=nrm, ws=shared)
+        b = ops.route_topk(q, kr, offd, k, krbar_inv_norm=nrm, ws=fresh)
+        c = ops.route_scores(q, kr, offd, krbar_inv_norm=nrm, ws=shared)
+        torch.cuda.synchronize()
+        for x, y in zip(a, b):
+            assert torch.equal(x, y)
+        assert torch.equal(a[0], c)
+        assert int(shared.count_nonzero().item()) == 0 and int(fresh.count_nonzero().item()) == 0
+        _, ref_doc = O.route(f64(Qr), f64(Kr), off)
+        assert np.abs(c.cpu().numpy() - ref_doc).max() <= SCORE_TOL
+        for bb in range(B):
+            check_topk(a[1].cpu().numpy()[bb], ref_doc[bb], k)
+
+
+def test_route_scan_select_equal_one_call():
+    """msa_route_scan + msa_route_select(k) == msa_route_topk and scan + select(0) == msa_route_scores,
+    bit for bit (scores, chunk scores, ids), over a multi-row-block batch with exclusions."""
+    B, T, n_docs, k = 4, 96, 2500, 16
+    Qr, Kr, off = _route_case(B, T, 8, n_docs, seed=77)
+    q, kr, offd = dev_bits(Qr), dev_bits(Kr), torch.from_numpy(off).to(DEV)
+    nrm = ops.krbar_inv_norms(kr)
+    excl = (np.random.default_rng(77).random((B, n_docs)) < 0.05).astype(np.uint8)
+    ex = torch.from_numpy(excl).to(DEV)
+    announce("route-scan-select")
+    G = len(Kr)
+    d1, i1, s1 = ops.route_topk(q, kr, offd, k, doc_exclude=ex, krbar_inv_norm=nrm)
+    d0, c0 = ops.route_scores(q, kr, offd, doc_exclude=ex, krbar_inv_norm=nrm, want_chunk_scores=True)
+    ws = ops.workspace(ops.route_topk_workspace_bytes(B, T, 8, 128, G, n_docs, k), DEV, "test-scan-select")
+    ops.route_scan(q, kr, ws, krbar_inv_norm=nrm)
+    d2, i2, s2 = ops.route_select(B, G, offd, k, ws, doc_exclude=ex)
+    ops.route_scan(q, kr, ws, krbar_inv_norm=nrm)
+    c3 = torch.empty((B, G), dtype=torch.float32, device=DEV)
+    d3 = ops.route_select(B, G, offd, 0, ws, doc_exclude=ex, chunk_scores=c3)
+    torch.cuda.synchronize()
+    bits = lambda t: t.cpu().numpy().view(np.uint32)
+    assert np.array_equal(bits(d1), bits(d2)) and np.array_equal(bits(d0), bits(d3))
+    assert np.array_equal(bits(d0), bits(d1))
+    assert np.array_equal(bits(c0), bits(c3))
+    assert torch.equal(i1, i2) and np.array_equal(bits(s1), bits(s2))
+
+
 # ---------------------------------------------------------------------- top-k
 # ---------------------------------------------------------- routing backward
 def _run_route_backward(Qr, Kr, off, dDoc, exclude=None, stored_norms=False, score_off=None):

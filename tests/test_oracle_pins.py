@@ -139,6 +139,27 @@ def test_pool_bruteforce():
 
 
 # ----------------------------------------------------- router-key encoding
+def test_pool_means_equals_pool_and_native():
+    """The whole-corpus chunk means (numpy and C) against the pinned pooling: the V and K_r outputs
+    of O.pool on random bf16 rows with partial chunks and one-token documents, bit for bit."""
+    from oracle import native as ON
+    r = rng(31)
+    lens = [1, 64, 65, 130, 7, 200, 63, 128]
+    n = int(sum(lens))
+    bits = sm.normal_bf16(31, 5, 0, 0, n * 2 * 16).reshape(n, 2, 16)
+    X = O.bf16_to_f64(bits)
+    _, Vb, Rb, off = O.pool(r.standard_normal((n, 2, 16)), X, X, lens, 64, 1e6)
+    M = O.pool_means(X, lens, 64)
+    np.testing.assert_array_equal(M, Vb)
+    np.testing.assert_array_equal(M, Rb)
+    np.testing.assert_array_equal(ON.pool_means_bf16(bits, lens, 64), M)
+    assert M.shape[0] == off[-1] == 1 + 1 + 2 + 3 + 1 + 4 + 1 + 2
+    # constant rows pool to that constant; a one-token document is its token
+    c = np.full((n, 2, 16), 0.375)
+    np.testing.assert_array_equal(O.pool_means(c, lens, 64), np.full((int(off[-1]), 2, 16), 0.375))
+    np.testing.assert_array_equal(M[0], X[0])
+
+
 def test_encode_one_hot_closed_form():
     # one-hot hidden states select columns of W: K_r,t = W[:, i_t]; chunk means by hand
     W = np.array([[1.0, 2.0, 3.0], [4.0, 5.0, 6.0]])            # [H*D = 2, d_model = 3]
@@ -315,6 +336,31 @@ def test_route_bruteforce_and_exclusion():
     np.testing.assert_allclose(ch, bch, atol=1e-13)
     np.testing.assert_allclose(doc, bdoc, atol=1e-13)
     assert doc[1, 3] == -np.inf and np.isfinite(doc[0, 3])
+
+
+def test_route_empty_documents_score_minus_inf():
+    """Documents without chunks (equal consecutive offsets): leading, in the middle, several in a
+    row and trailing.  Each scores -inf and the others keep their own chunks' maximum, as the
+    brute-force scan gives; removing the empty documents leaves the others' scores unchanged."""
+    r = rng(21)
+    n_ch = np.array([0, 2, 0, 0, 3, 1, 0, 2, 0, 0])
+    off = np.concatenate([[0], np.cumsum(n_ch)])
+    Qr = r.standard_normal((2, 4, 3, 8))
+    Kb = r.standard_normal((int(off[-1]), 3, 8))
+    excl = np.zeros((2, len(n_ch)), bool); excl[0, 4] = True; excl[1, 2] = True
+    ch, doc = O.route(Qr, Kb, off, excl)
+    bch, bdoc = bf.route(Qr.tolist(), Kb.tolist(), list(n_ch), excl.tolist())
+    np.testing.assert_allclose(ch, bch, atol=1e-13)
+    np.testing.assert_array_equal(np.isfinite(doc), np.isfinite(bdoc))
+    np.testing.assert_allclose(doc[np.isfinite(doc)], np.asarray(bdoc)[np.isfinite(doc)], atol=1e-13)
+    assert np.all(doc[:, n_ch == 0] == -np.inf)
+    ne = np.flatnonzero(n_ch > 0)
+    _, doc_ne = O.route(Qr, Kb, np.concatenate([[0], np.cumsum(n_ch[ne])]), excl[:, ne])
+    np.testing.assert_array_equal(doc[:, ne], doc_ne)
+    # each non-empty document's score is the max of its own chunk scores, by explicit slicing
+    for d in ne:
+        if not excl[1, d]:
+            assert doc[1, d] == ch[1, off[d]:off[d + 1]].max()
 
 
 def test_route_invariants():
