@@ -20,6 +20,7 @@
  *   msa_append_router_rows  interleave: the next round's router rows and exclusions
  *   msa_sparse_attn_decode  generation: GQA attention over [memory ++ local KV]
  *   msa_route_topk             msa_route_scores + msa_topk_docs in one call (k <= 32)
+ *   msa_route_topk_noalloc     the same with a fixed scratch array in the library (no workspace)
  *   msa_sparse_attn_local_partial, msa_sparse_attn_memory_merge  the same attention in two launches
  *                              (the local-key half needs nothing retrieved)
  *   msa_sparse_attn_forward    training: the same attention, also returning each row's log-sum-exp
@@ -342,6 +343,29 @@ int msa_route_select(int B, int64_t n_chunks, const int64_t* doc_chunk_off, int6
  *   workspace_bytes a multiple of 4; workspace 16-byte aligned.
  */
 int msa_route_workspace_clear(void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * msa_route_topk_noalloc -- msa_route_topk without a caller workspace, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).
+ *
+ * Same arguments, outputs and errors as msa_route_topk, minus the workspace: the
+ * call uses a fixed array of MSA_NOALLOC_SCRATCH_BYTES (16 MiB) inside the library,
+ * one per device, held until the process ends.  The call fails with
+ * MSA_ERR_WORKSPACE (nothing launched) when
+ *   msa_route_topk_workspace_bytes(B, T, H, D, n_chunks, n_docs, k) > MSA_NOALLOC_SCRATCH_BYTES,
+ * i.e. roughly when B * n_chunks * 4 + B * ceil(n_docs / 64) * 8 exceeds 16 MiB
+ * (a 100M-token store at batch 1 needs 6.7 MB).  It allocates nothing itself.  All
+ * calls on one device share that device's array: calls that overlap on one device
+ * (several streams or threads at once) race and must be serialised by the caller.
+ * The first call on a device looks up the array's device address and clears it
+ * with a kernel on `stream`; later calls find it zeroed.
+ */
+#define MSA_NOALLOC_SCRATCH_BYTES (16u << 20)
+int msa_route_topk_noalloc(const uint16_t* Qr, int B, int T, int H, int D, const uint16_t* Krbar,
+                           const float* krbar_inv_norm, int64_t n_chunks, const int64_t* doc_chunk_off,
+                           int64_t n_docs, const uint8_t* doc_exclude, int k, float* doc_scores, float* chunk_scores,
+                           int32_t* top_idx, float* top_scores, hipStream_t stream);
 
 /*
  * msa_fetch_docs -- context assembly from the host tier (host-driven copies).

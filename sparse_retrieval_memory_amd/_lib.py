@@ -55,6 +55,8 @@ SIGNATURES = {
     "msa_route_topk_workspace_bytes": (c_sz, [c_i, c_i, c_i, c_i, c_i64, c_i64, c_i]),
     "msa_route_topk": (c_i, [c_p, c_i, c_i, c_i, c_i, c_p, c_p, c_i64, c_p, c_i64, c_p, c_i, c_p, c_p, c_p, c_p, c_p,
                              c_sz, c_p]),
+    "msa_route_topk_noalloc": (c_i, [c_p, c_i, c_i, c_i, c_i, c_p, c_p, c_i64, c_p, c_i64, c_p, c_i, c_p, c_p, c_p,
+                                     c_p, c_p]),
     "msa_route_scan": (c_i, [c_p, c_i, c_i, c_i, c_i, c_p, c_p, c_i64, c_p, c_sz, c_p]),
     "msa_route_select": (c_i, [c_i, c_i64, c_p, c_i64, c_p, c_i, c_p, c_p, c_p, c_p, c_p, c_sz, c_p]),
     "msa_route_workspace_clear": (c_i, [c_p, c_sz, c_p]),

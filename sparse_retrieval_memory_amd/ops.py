@@ -204,6 +204,29 @@ def route_topk(Qr, Krbar, doc_chunk_off, k: int, doc_exclude=None, krbar_inv_nor
     return doc_scores, top_idx, top_scores
 
 
+def route_topk_noalloc(Qr, Krbar, doc_chunk_off, k: int, doc_exclude=None, krbar_inv_norm=None, doc_scores=None,
+                       top_idx=None, top_scores=None, stream=None):
+    """msa_route_topk_noalloc: msa_route_topk with the library's fixed scratch array as workspace."""
+    _bf16(Qr, "Qr"); _bf16(Krbar, "Krbar"); _dev(Qr, "Qr")
+    B, T, H, D = Qr.shape
+    n_chunks = Krbar.shape[0]
+    n_docs = doc_chunk_off.numel() - 1
+    dev = Qr.device
+    if doc_scores is None:
+        doc_scores = torch.empty((B, n_docs), dtype=torch.float32, device=dev)
+    if top_idx is None:
+        top_idx = torch.empty((B, k), dtype=torch.int32, device=dev)
+    if top_scores is None:
+        top_scores = torch.empty((B, k), dtype=torch.float32, device=dev)
+    if doc_exclude is not None:
+        assert doc_exclude.dtype in (torch.uint8, torch.bool) and doc_exclude.shape == (B, n_docs)
+        doc_exclude = doc_exclude.contiguous()
+    _lib.call("msa_route_topk_noalloc", _p(Qr), B, T, H, D, _p(Krbar), _p(krbar_inv_norm), n_chunks,
+              _p(doc_chunk_off), n_docs, _p(doc_exclude), k, _p(doc_scores), None, _p(top_idx), _p(top_scores),
+              _stream(stream))
+    return doc_scores, top_idx, top_scores
+
+
 def route_scan(Qr, Krbar, ws, krbar_inv_norm=None, stream=None):
     """msa_route_scan: the scan only; the chunk maxima stay in ``ws`` for route_select."""
     _bf16(Qr, "Qr"); _bf16(Krbar, "Krbar"); _dev(Qr, "Qr")

@@ -264,3 +264,28 @@ def test_route_scan_select_clear_validation():
     assert _code("msa_route_workspace_clear", N, 256, N) == E.MSA_ERR_INVALID_ARG
     assert _code("msa_route_workspace_clear", p, 255, N) == E.MSA_ERR_INVALID_ARG
     assert _code("msa_route_workspace_clear", ctypes.c_void_p(20), 256, N) == E.MSA_ERR_INVALID_ARG
+
+
+def test_route_topk_noalloc_validation():
+    """Invalid arguments and sizes beyond the fixed scratch are rejected on the host, before any
+    device call (so these run without a GPU)."""
+    E = _lib
+    p = ctypes.c_void_p(1 << 20)
+    lib = _lib.load()
+    cap = 16 << 20
+    rt = lambda B=1, T=128, k=16, H=8, n_chunks=1000, n_docs=100, ti=p: (
+        p, B, T, H, 128, p, N, n_chunks, p, n_docs, N, k, p, N, ti, p, N)
+    assert _code("msa_route_topk_noalloc", *rt(k=33)) == E.MSA_ERR_UNSUPPORTED
+    assert _code("msa_route_topk_noalloc", *rt(H=3)) == E.MSA_ERR_UNSUPPORTED
+    assert _code("msa_route_topk_noalloc", *rt(ti=N)) == E.MSA_ERR_INVALID_ARG
+    assert _code("msa_route_topk_noalloc", *rt(k=16, n_docs=10)) == E.MSA_ERR_INVALID_ARG
+    # the largest store that fits at batch 1, and one chunk more
+    n_docs = 200_000
+    gm = (n_docs + 63) // 64 * 8
+    fit = (cap - gm) // 4 // 64 * 64
+    assert lib.msa_route_topk_workspace_bytes(1, 128, 8, 128, fit, n_docs, 16) <= cap
+    over = fit + 64 * 4
+    assert lib.msa_route_topk_workspace_bytes(1, 128, 8, 128, over, n_docs, 16) > cap
+    assert _code("msa_route_topk_noalloc", *rt(n_chunks=over, n_docs=n_docs)) == E.MSA_ERR_WORKSPACE
+    assert b"scratch" in lib.msa_last_error()
+    assert _code("msa_route_topk_noalloc", *rt(B=4, n_chunks=fit, n_docs=n_docs)) == E.MSA_ERR_WORKSPACE
