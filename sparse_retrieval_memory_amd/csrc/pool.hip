@@ -6,14 +6,25 @@
 // every document, so K is rotated at its document-local position before
 // pooling.  b-lab.team pipeline stage 1 caches the pooled (Kbar, Vbar, Krbar).
 //
-// One workgroup per chunk.  The chunk's document comes from a 64-way search of
-// the chunk offsets by one wave (3 steps for 200K documents).  The rotation
-// table for the chunk's positions is built once per workgroup in LDS with
-// fp64 angles.  Each wave accumulates every 4th token in fp32 registers (a lane
-// owns 8 dims and their 8 RoPE partners of one head, loaded as 16-byte
-// vectors); the four partial sums meet in LDS, and the mean is rounded to bf16
-// (nearest even) and stored as 16-byte vectors.  The kernel is HBM-bound:
-// 3 * chunk_len * H * D * 2 bytes in, 3 * H * D * 2 bytes out per chunk.
+// The step is a streaming reduction bound by HBM (3 * chunk_len * H * D * 2
+// bytes in, 3 * H * D * 2 bytes out per chunk), so the kernel is laid out to
+// keep many independent loads in flight and to touch LDS as little as possible:
+//
+//  * A workgroup is three waves, one per tensor (K, V, K_r); each wave walks
+//    the workgroup's contiguous range of chunks on its own, keeping its chunk
+//    sums in registers (a lane owns 8 dims of a head and their 8 RoPE partners,
+//    read as 16-byte non-temporal loads, 8 tokens per step), so no partial sums
+//    meet in LDS and the waves never wait for one another.
+//  * Rotation is linear, so a chunk's rotated sum is
+//      sum_t R((p0 + t) theta) K_t = R(p0 theta) sum_t R(t theta) K_t :
+//    the K wave rotates every token by its offset t inside the chunk, from a
+//    table of cos/sin(t theta_i), t < 64, built once per workgroup in LDS
+//    (angles reduced in fp64), and rotates the finished sum once by the chunk's
+//    start angle (longer chunks do this per block of 64 tokens).
+//  * The chunk's document is found once per workgroup by a 64-way search of
+//    the chunk offsets and then advanced chunk by chunk.
+// The three sums are divided by the token count, rounded to bf16 (nearest
+// even) and stored as 16-byte vectors.
 #include "msa_internal.h"
 
 #include <math.h>
@@ -22,138 +33,224 @@ namespace msa {
 namespace {
 
 constexpr int D = 128;
-constexpr int THREADS = 256;
-constexpr int MAXC = 64;      // rotation-table rows kept in LDS (longer chunks loop over it)
+constexpr int TABT = 64;           // token offsets in the rotation table (one block)
+constexpr int WG_PER_CU = 4;       // LDS: a 32 KB table per workgroup
+constexpr int STEP = 8;            // tokens per load batch
 
+// Lane layout for H heads: a token row of one tensor is H * D bf16; a lane takes 8 dims
+// [i0, i0 + 8) of a head and their partners [64 + i0, 72 + i0).  With H < 8 a wave covers
+// TPW = 8 / H tokens at once; with H = 16 a lane takes two heads.
 template <int H>
-__global__ void __launch_bounds__(THREADS)
-pool_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, const uint16_t* __restrict__ Kr,
-            const int64_t* __restrict__ doc_tok_off, const int64_t* __restrict__ doc_chunk_off,
-            int64_t n_docs, int64_t n_tok, int64_t n_chunks, int chunk_len, double log2_base,
-            uint16_t* __restrict__ Kbar, uint16_t* __restrict__ Vbar, uint16_t* __restrict__ Krbar) {
-  constexpr int LANES_PER_TOK = H * 8;                 // lane -> (head, 8-dim group)
-  constexpr int TOKPAR = THREADS / LANES_PER_TOK;      // tokens in flight per step
-  __shared__ float cs_tab[MAXC][D / 2];
-  __shared__ float sn_tab[MAXC][D / 2];
-  __shared__ float part[TOKPAR][3][H * D];
-  __shared__ int64_t sh_doc;
+struct PoolCfg {
+  static constexpr int TPW = H >= 8 ? 1 : 8 / H;   // tokens per wave step
+  static constexpr int HPL = H >= 8 ? H / 8 : 1;   // heads per lane
+};
 
-  const int tid = threadIdx.x;
-  const int64_t gl = blockIdx.x;                       // local chunk row
-  const int64_t cbase = doc_chunk_off[0];
-  const int64_t g = cbase + gl;                        // global chunk index
-
-  // --- find the document: doc_chunk_off[d] <= g < doc_chunk_off[d+1]
-  if (tid < 64) {
-    int64_t lo = 0, hi = n_docs;
-    while (hi - lo > 1) {
-      const int64_t span = hi - lo;
-      const int64_t piv = lo + (span * tid) / 64;
-      const bool le = doc_chunk_off[piv] <= g;
-      const uint64_t mask = __ballot(le);
-      const int c = __popcll(mask);                    // pivots at or below g form a prefix
-      const int64_t nlo = lo + (span * (c - 1)) / 64;
-      const int64_t nhi = (c < 64) ? lo + (span * c) / 64 : hi;
-      lo = nlo;
-      hi = nhi > nlo ? nhi : nlo + 1;
-    }
-    if (tid == 0) sh_doc = lo;
+// First chunk of document d and the document of chunk g (doc_chunk_off[d] <= g < doc_chunk_off[d+1]),
+// by one wave: 64 pivots per step narrow [lo, hi) by 64x.
+__device__ int64_t find_doc(const int64_t* __restrict__ doc_chunk_off, int64_t n_docs, int64_t g, int lane) {
+  int64_t lo = 0, hi = n_docs;
+  while (hi - lo > 1) {
+    const int64_t span = hi - lo;
+    const int64_t piv = lo + (span * lane) / 64;
+    const bool le = doc_chunk_off[piv] <= g;
+    const uint64_t mask = __ballot(le);
+    const int c = __popcll(mask);                        // pivots at or below g form a prefix
+    const int64_t nlo = lo + (span * (c - 1)) / 64;
+    const int64_t nhi = (c < 64) ? lo + (span * c) / 64 : hi;
+    lo = nlo;
+    hi = nhi > nlo ? nhi : nlo + 1;
   }
-  __syncthreads();
-  const int64_t d = sh_doc;
-  const int64_t j = g - doc_chunk_off[d];
-  const int64_t tbase = doc_tok_off[0];
-  const int64_t doc_t0 = doc_tok_off[d];
-  const int64_t L = doc_tok_off[d + 1] - doc_t0;
-  const int64_t p0 = j * chunk_len;                    // first document-local position
-  int cnt = (int)((L - p0) < chunk_len ? (L - p0) : chunk_len);
-  const int64_t row0 = doc_t0 - tbase + p0;            // first input row
-  if (cnt < 0 || row0 < 0 || row0 + cnt > n_tok) cnt = 0;   // inconsistent offsets: write zeros
+  return lo;
+}
 
-  const int tq = tid / LANES_PER_TOK;                  // token phase of this lane
-  const int ln = tid % LANES_PER_TOK;
-  const int h = ln / 8, grp = ln % 8;
-  const int i0 = grp * 8;                              // pair indices i0..i0+7 (dims i and i+64)
-  float ak[16], av[16], ar[16];
-#pragma unroll
-  for (int e = 0; e < 16; ++e) { ak[e] = 0.f; av[e] = 0.f; ar[e] = 0.f; }
+// 8 bf16 (one 16-byte load) -> fp32, added to acc[0..8)
+__device__ __forceinline__ void add8(const uint4 v, float* acc) {
+  acc[0] += bf16_lo(v.x); acc[1] += bf16_hi(v.x);
+  acc[2] += bf16_lo(v.y); acc[3] += bf16_hi(v.y);
+  acc[4] += bf16_lo(v.z); acc[5] += bf16_hi(v.z);
+  acc[6] += bf16_lo(v.w); acc[7] += bf16_hi(v.w);
+}
 
-  for (int t0 = 0; t0 < cnt; t0 += MAXC) {
-    const int tn = (cnt - t0) < MAXC ? (cnt - t0) : MAXC;
-    __syncthreads();
-    for (int x = tid; x < tn * (D / 2); x += THREADS) {
-      const int tt = x / (D / 2), i = x % (D / 2);
-      const double theta = exp2(-(2.0 * i / D) * log2_base);
-      double sn, cs;
-      sincos((double)(p0 + t0 + tt) * theta, &sn, &cs);
-      cs_tab[tt][i] = (float)cs;
-      sn_tab[tt][i] = (float)sn;
-    }
-    __syncthreads();
-    for (int tt = tq; tt < tn; tt += TOKPAR) {
-      const int64_t r = row0 + t0 + tt;
-      const int64_t base = (r * H + h) * D;
-      const uint4 k1 = load_nt16(K + base + i0);          // raw tokens are read once
-      const uint4 k2 = load_nt16(K + base + 64 + i0);
-      const uint4 v1 = load_nt16(V + base + i0);
-      const uint4 v2 = load_nt16(V + base + 64 + i0);
-      const uint4 r1 = load_nt16(Kr + base + i0);
-      const uint4 r2 = load_nt16(Kr + base + 64 + i0);
-      const uint32_t kw1[4] = {k1.x, k1.y, k1.z, k1.w}, kw2[4] = {k2.x, k2.y, k2.z, k2.w};
-      const uint32_t vw1[4] = {v1.x, v1.y, v1.z, v1.w}, vw2[4] = {v2.x, v2.y, v2.z, v2.w};
-      const uint32_t rw1[4] = {r1.x, r1.y, r1.z, r1.w}, rw2[4] = {r2.x, r2.y, r2.z, r2.w};
-      const float4 c0 = *reinterpret_cast<const float4*>(&cs_tab[tt][i0]);
-      const float4 c1 = *reinterpret_cast<const float4*>(&cs_tab[tt][i0 + 4]);
-      const float4 s0 = *reinterpret_cast<const float4*>(&sn_tab[tt][i0]);
-      const float4 s1 = *reinterpret_cast<const float4*>(&sn_tab[tt][i0 + 4]);
-      const float cc[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-      const float ss[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t w1 = kw1[e >> 1], w2 = kw2[e >> 1];
-        const float x1 = (e & 1) ? bf16_hi(w1) : bf16_lo(w1);
-        const float x2 = (e & 1) ? bf16_hi(w2) : bf16_lo(w2);
-        ak[e] += x1 * cc[e] - x2 * ss[e];
-        ak[8 + e] += x2 * cc[e] + x1 * ss[e];
-        av[e] += (e & 1) ? bf16_hi(vw1[e >> 1]) : bf16_lo(vw1[e >> 1]);
-        av[8 + e] += (e & 1) ? bf16_hi(vw2[e >> 1]) : bf16_lo(vw2[e >> 1]);
-        ar[e] += (e & 1) ? bf16_hi(rw1[e >> 1]) : bf16_lo(rw1[e >> 1]);
-        ar[8 + e] += (e & 1) ? bf16_hi(rw2[e >> 1]) : bf16_lo(rw2[e >> 1]);
-      }
-    }
-  }
-
-  // --- combine the TOKPAR token phases, divide, round, store
+// The rotated pair sum: a1 += x1 c - x2 s, a2 += x2 c + x1 s for 8 frequencies.
+__device__ __forceinline__ void rot_add8(const uint4 u1, const uint4 u2, const float2* __restrict__ cs, float* a1,
+                                         float* a2) {
+  const uint32_t w1[4] = {u1.x, u1.y, u1.z, u1.w}, w2[4] = {u2.x, u2.y, u2.z, u2.w};
+  const float4 t0 = *reinterpret_cast<const float4*>(cs);
+  const float4 t1 = *reinterpret_cast<const float4*>(cs + 2);
+  const float4 t2 = *reinterpret_cast<const float4*>(cs + 4);
+  const float4 t3 = *reinterpret_cast<const float4*>(cs + 6);
+  const float c[8] = {t0.x, t0.z, t1.x, t1.z, t2.x, t2.z, t3.x, t3.z};
+  const float s[8] = {t0.y, t0.w, t1.y, t1.w, t2.y, t2.w, t3.y, t3.w};
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    part[tq][0][h * D + i0 + e] = ak[e];
-    part[tq][0][h * D + 64 + i0 + e] = ak[8 + e];
-    part[tq][1][h * D + i0 + e] = av[e];
-    part[tq][1][h * D + 64 + i0 + e] = av[8 + e];
-    part[tq][2][h * D + i0 + e] = ar[e];
-    part[tq][2][h * D + 64 + i0 + e] = ar[8 + e];
+    const float x1 = (e & 1) ? bf16_hi(w1[e >> 1]) : bf16_lo(w1[e >> 1]);
+    const float x2 = (e & 1) ? bf16_hi(w2[e >> 1]) : bf16_lo(w2[e >> 1]);
+    a1[e] = fmaf(x1, c[e], a1[e]);
+    a1[e] = fmaf(-x2, s[e], a1[e]);
+    a2[e] = fmaf(x2, c[e], a2[e]);
+    a2[e] = fmaf(x1, s[e], a2[e]);
+  }
+}
+
+struct ChunkInfo {
+  int64_t row0;    // first input row
+  int64_t p0;      // document-local position of the first token
+  int cnt;         // tokens (0 when the offsets are inconsistent: the chunk is written as zeros)
+};
+
+template <int H>
+__global__ void __launch_bounds__(192)
+pool_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, const uint16_t* __restrict__ Kr,
+            const int64_t* __restrict__ doc_tok_off, const int64_t* __restrict__ doc_chunk_off,
+            int64_t n_docs, int64_t n_tok, int64_t n_chunks, int64_t per_wg, int chunk_len, double log2_base,
+            uint16_t* __restrict__ Kbar, uint16_t* __restrict__ Vbar, uint16_t* __restrict__ Krbar) {
+  using CF = PoolCfg<H>;
+  // cos/sin(t theta_i), t < 64, i < 64, as (cos, sin) pairs; rows padded by 16 bytes so that
+  // lanes reading different t rows at the same i fall in different banks
+  __shared__ __attribute__((aligned(16))) float2 tab[TABT][D / 2 + 2];
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;   // wave 0: K, 1: V, 2: K_r
+  const int64_t c_begin = (int64_t)blockIdx.x * per_wg;
+  int64_t c_end = c_begin + per_wg;
+  if (c_end > n_chunks) c_end = n_chunks;
+
+  // rotation table (angles reduced in fp64, evaluated in fp32)
+  for (int x = threadIdx.x; x < TABT * (D / 2); x += 192) {
+    const int t = x / (D / 2), i = x % (D / 2);
+    const double rev = exp2(-(2.0 * i / D) * log2_base) * 0.15915494309189535;   // theta_i / (2 pi)
+    float c, s;
+    rope_cs(t, rev, &c, &s);
+    tab[t][i] = make_float2(c, s);
   }
   __syncthreads();
-  if (gl >= n_chunks) return;
-  const float inv = cnt > 0 ? 1.0f / (float)cnt : 0.f;
-  constexpr int VEC = 3 * H * D / 8;                   // 16-byte output vectors
-  for (int x = tid; x < VEC; x += THREADS) {
-    const int which = x / (H * D / 8);
-    const int col = (x % (H * D / 8)) * 8;
-    uint32_t w[4];
+  if (c_begin >= c_end) return;
+
+  const int ln = lane % (8 * H < 64 ? 8 * H : 64);
+  const int tsub = lane / (8 * H < 64 ? 8 * H : 64);         // token sub-index (H < 8)
+  const int grp = ln % 8;                                     // 8-dim group: pair dims i0..i0+7
+  const int h0 = ln / 8;                                      // first head of the lane
+  const int i0 = grp * 8;
+  const uint16_t* src = wave == 0 ? K : (wave == 1 ? V : Kr);
+  uint16_t* dst = wave == 0 ? Kbar : (wave == 1 ? Vbar : Krbar);
+  double rev[8];                                              // this lane's frequencies, for the start angles
+  if (wave == 0) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-      for (int p = 0; p < TOKPAR; ++p) {
-        a0 += part[p][which][col + 2 * e];
-        a1 += part[p][which][col + 2 * e + 1];
-      }
-      w[e] = f32_to_bf16_rne(a0 * inv) | (f32_to_bf16_rne(a1 * inv) << 16);
-    }
-    uint16_t* dst = (which == 0 ? Kbar : which == 1 ? Vbar : Krbar) + gl * (int64_t)(H * D) + col;
-    *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+    for (int e = 0; e < 8; ++e) rev[e] = exp2(-(2.0 * (i0 + e) / D) * log2_base) * 0.15915494309189535;
   }
+
+  const int64_t cbase = doc_chunk_off[0];
+  const int64_t tbase = doc_tok_off[0];
+  int64_t d = find_doc(doc_chunk_off, n_docs, cbase + c_begin, lane);
+  for (int64_t gl = c_begin; gl < c_end; ++gl) {
+    const int64_t g = cbase + gl;
+    while (d + 1 < n_docs && doc_chunk_off[d + 1] <= g) ++d;
+    ChunkInfo ci;
+    {
+      const int64_t doc_t0 = doc_tok_off[d];
+      const int64_t L = doc_tok_off[d + 1] - doc_t0;
+      ci.p0 = (g - doc_chunk_off[d]) * chunk_len;
+      int64_t cnt = L - ci.p0 < chunk_len ? L - ci.p0 : chunk_len;
+      ci.row0 = doc_t0 - tbase + ci.p0;
+      if (cnt < 0 || ci.row0 < 0 || ci.row0 + cnt > n_tok || g < doc_chunk_off[d]) cnt = 0;
+      ci.cnt = (int)cnt;
+    }
+    float out1[CF::HPL][8], out2[CF::HPL][8];                // the chunk's sums (dims i0.., 64 + i0..)
+#pragma unroll
+    for (int hp = 0; hp < CF::HPL; ++hp)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { out1[hp][e] = 0.f; out2[hp][e] = 0.f; }
+
+    for (int b0 = 0; b0 < ci.cnt; b0 += TABT) {              // blocks of 64 tokens
+      const int bn = ci.cnt - b0 < TABT ? ci.cnt - b0 : TABT;
+      float a1[CF::HPL][8], a2[CF::HPL][8];
+#pragma unroll
+      for (int hp = 0; hp < CF::HPL; ++hp)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { a1[hp][e] = 0.f; a2[hp][e] = 0.f; }
+      for (int t0 = 0; t0 < bn; t0 += STEP * CF::TPW) {
+        uint4 u1[STEP][CF::HPL], u2[STEP][CF::HPL];
+#pragma unroll
+        for (int k = 0; k < STEP; ++k) {
+          const int t = t0 + k * CF::TPW + tsub;
+#pragma unroll
+          for (int hp = 0; hp < CF::HPL; ++hp) {
+            u1[k][hp] = make_uint4(0, 0, 0, 0);
+            u2[k][hp] = make_uint4(0, 0, 0, 0);
+            if (t < bn) {
+              const uint16_t* p = src + ((ci.row0 + b0 + t) * H + h0 + 8 * hp) * D + i0;
+              u1[k][hp] = load_nt16(p);                         // raw tokens are read once
+              u2[k][hp] = load_nt16(p + 64);
+            }
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < STEP; ++k) {
+          const int t = t0 + k * CF::TPW + tsub;
+          if (wave == 0) {
+            const float2* cs = &tab[t < TABT ? t : 0][i0];      // zero rows past bn add nothing
+#pragma unroll
+            for (int hp = 0; hp < CF::HPL; ++hp) rot_add8(u1[k][hp], u2[k][hp], cs, a1[hp], a2[hp]);
+          } else {
+#pragma unroll
+            for (int hp = 0; hp < CF::HPL; ++hp) { add8(u1[k][hp], a1[hp]); add8(u2[k][hp], a2[hp]); }
+          }
+        }
+      }
+      if (wave == 0) {
+        // rotate the block's sum by its first token's angle, R((p0 + b0) theta)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float c, s;
+          rope_cs((int)(ci.p0 + b0), rev[e], &c, &s);
+#pragma unroll
+          for (int hp = 0; hp < CF::HPL; ++hp) {
+            out1[hp][e] += a1[hp][e] * c - a2[hp][e] * s;
+            out2[hp][e] += a2[hp][e] * c + a1[hp][e] * s;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int hp = 0; hp < CF::HPL; ++hp)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) { out1[hp][e] += a1[hp][e]; out2[hp][e] += a2[hp][e]; }
+      }
+    }
+    // H < 8: add the token sub-lanes' sums (lanes 8H, 16H, ... apart), in a fixed order
+#pragma unroll
+    for (int m = 8 * H; m < 64; m <<= 1) {
+#pragma unroll
+      for (int hp = 0; hp < CF::HPL; ++hp)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          out1[hp][e] += __shfl_xor(out1[hp][e], m);
+          out2[hp][e] += __shfl_xor(out2[hp][e], m);
+        }
+    }
+    if (tsub == 0) {
+      const float inv = ci.cnt > 0 ? 1.0f / (float)ci.cnt : 0.f;
+#pragma unroll
+      for (int hp = 0; hp < CF::HPL; ++hp) {
+        uint16_t* o = dst + (gl * H + h0 + 8 * hp) * D + i0;
+        uint32_t w1[4], w2[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          w1[e] = f32_to_bf16_rne(out1[hp][2 * e] * inv) | (f32_to_bf16_rne(out1[hp][2 * e + 1] * inv) << 16);
+          w2[e] = f32_to_bf16_rne(out2[hp][2 * e] * inv) | (f32_to_bf16_rne(out2[hp][2 * e + 1] * inv) << 16);
+        }
+        *reinterpret_cast<uint4*>(o) = make_uint4(w1[0], w1[1], w1[2], w1[3]);
+        *reinterpret_cast<uint4*>(o + 64) = make_uint4(w2[0], w2[1], w2[2], w2[3]);
+      }
+    }
+  }
+}
+
+int pool_cus() {
+  int dev = 0, v = 0;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+    return v;
+  return 256;
 }
 
 }  // namespace
@@ -164,11 +261,15 @@ int launch_pool(const uint16_t* K, const uint16_t* V, const uint16_t* Kr, const 
                 hipStream_t stream) {
   if (n_chunks == 0) return MSA_OK;
   const double lb = log2(rope_base);
-  dim3 grid((unsigned)n_chunks);
+  int64_t wgs = (int64_t)pool_cus() * WG_PER_CU;
+  if (wgs > n_chunks) wgs = n_chunks;
+  const int64_t per = (n_chunks + wgs - 1) / wgs;
+  wgs = (n_chunks + per - 1) / per;
+  dim3 grid((unsigned)wgs);
 #define MSA_POOL_CASE(HH)                                                                        \
   case HH:                                                                                       \
-    hipLaunchKernelGGL(pool_kernel<HH>, grid, dim3(THREADS), 0, stream, K, V, Kr, doc_tok_off,  \
-                       doc_chunk_off, n_docs, n_tok, n_chunks, chunk_len, lb, Kbar, Vbar, Krbar); \
+    hipLaunchKernelGGL(pool_kernel<HH>, grid, dim3(192), 0, stream, K, V, Kr, doc_tok_off,       \
+                       doc_chunk_off, n_docs, n_tok, n_chunks, per, chunk_len, lb, Kbar, Vbar, Krbar); \
     break;
   switch (H) {
     MSA_POOL_CASE(1)

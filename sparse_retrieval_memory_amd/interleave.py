@@ -9,7 +9,8 @@ attends over all retrieved documents (retrieval order) with the global RoPE
 offset equal to their count.
 
 This module only sequences the library's calls; every step runs in libmsa's
-kernels (``msa_append_router_rows``, ``msa_route_scores``, ``msa_topk_docs``,
+kernels (``msa_append_router_rows``, ``msa_route_topk`` (``msa_route_scores`` +
+``msa_topk_docs`` for k > 32),
 ``msa_gather_docs`` or ``msa_fetch_docs``, ``msa_sparse_attn_decode``).  The
 one host round trip per round is the selected ids: the host sizes the next
 round's router rows and the staging buffer from them.  The content is
@@ -78,9 +79,13 @@ class Interleave:
                 ids = torch.from_numpy(retrieved).to(dev, non_blocking=True)
                 rows, _ = ops.append_router_rows(Qr, self.krbar, self.doc_chunk_off, ids, n_rows,
                                                  doc_exclude=exclude)
-            doc = ops.route_scores(rows, self.krbar, self.doc_chunk_off, doc_exclude=exclude if r else None,
-                                   krbar_inv_norm=self.krbar_inv_norm)
-            idx, sc = ops.topk_docs(doc, k)
+            if k <= 32:          # scan, document max and top-k in one call
+                doc, idx, sc = ops.route_topk(rows, self.krbar, self.doc_chunk_off, k,
+                                              doc_exclude=exclude if r else None, krbar_inv_norm=self.krbar_inv_norm)
+            else:
+                doc = ops.route_scores(rows, self.krbar, self.doc_chunk_off, doc_exclude=exclude if r else None,
+                                       krbar_inv_norm=self.krbar_inv_norm)
+                idx, sc = ops.topk_docs(doc, k)
             new = idx.cpu().numpy()
             retrieved = np.concatenate([retrieved, new], axis=1).astype(np.int32)
             Mmax = int(n_chunks_of[retrieved].sum(axis=1).max())

@@ -16,7 +16,7 @@ from synth import native
 from synth import splitmix as sm
 
 from tests.parity import (ATT_GRAD_OBS, ATT_TOL, SCORE_TOL, bf16_ulp_diff, check_topk, dev_bits, encoded_keys_ok, grads_ok,
-                          host_bits, rel_rows, route_grad_bounds, route_near_ties)
+                          host_bits, pooled_k_ok, pooled_k_scales, rel_rows, route_grad_bounds, route_near_ties)
 
 # lse of the GPU forward against the oracle: scores carry ~2^-16 of sum_d |q_d k_d| * scale
 # (about 1e-4 for N(0,1) rows at D = 128), so the log-sum-exp is within 1e-3 absolute
@@ -452,7 +452,25 @@ def test_pool_matches_oracle(H, lens):
     rK, rV, rR, off = O.pool(f64(K), f64(V), f64(Kr), w.doc_len, 64, w.rope_base)
     assert bf16_ulp_diff(host_bits(Vb), O.f64_to_bf16_bits(rV)).max() <= 1
     assert bf16_ulp_diff(host_bits(Rb), O.f64_to_bf16_bits(rR)).max() <= 1
-    assert bf16_ulp_diff(host_bits(Kb), O.f64_to_bf16_bits(rK)).max() <= 2
+    assert pooled_k_ok(host_bits(Kb), rK, *pooled_k_scales(f64(K), w.doc_len, 64))
+
+
+@pytest.mark.parametrize("chunk,lens", [(1, [5, 1, 3]), (100, [100, 101, 250, 37, 1]), (256, [600, 256, 1, 70]),
+                                        (1024, [1500, 1024, 3]), (33, [99, 34, 2])])
+def test_pool_chunk_lengths_match_oracle(chunk, lens):
+    """Chunk lengths other than 64: one token per chunk, chunks of several 64-token rotation blocks
+    with a ragged last block, the 1024 maximum, and lengths that do not divide 64."""
+    announce("pool-chunk", chunk, lens)
+    w = C.workload("tiny-32K", n_docs=len(lens), length_law="custom", custom_lengths=tuple(lens), chunk=chunk)
+    K = C.raw_block(w, "K", 0, w.n_tok); V = C.raw_block(w, "V", 0, w.n_tok); Kr = C.raw_block(w, "Kr", 0, w.n_tok)
+    Kb, Vb, Rb = ops.pool_chunks(dev_bits(K), dev_bits(V), dev_bits(Kr), torch.from_numpy(w.doc_tok_off).to(DEV),
+                                 torch.from_numpy(w.doc_chunk_off).to(DEV), w.n_chunks, chunk, w.rope_base)
+    torch.cuda.synchronize()
+    rK, rV, rR, off = O.pool(f64(K), f64(V), f64(Kr), w.doc_len, chunk, w.rope_base)
+    assert Kb.shape[0] == off[-1]
+    assert bf16_ulp_diff(host_bits(Vb), O.f64_to_bf16_bits(rV)).max() <= 1
+    assert bf16_ulp_diff(host_bits(Rb), O.f64_to_bf16_bits(rR)).max() <= 1
+    assert pooled_k_ok(host_bits(Kb), rK, *pooled_k_scales(f64(K), w.doc_len, chunk))
 
 
 def test_pool_slab_with_offset_bases():
@@ -469,7 +487,9 @@ def test_pool_slab_with_offset_bases():
     torch.cuda.synchronize()
     rK, rV, rR, off = O.pool(f64(K), f64(V), f64(Kr), w.doc_len, 64, w.rope_base)
     assert bf16_ulp_diff(host_bits(Vb), O.f64_to_bf16_bits(rV[c0:c1])).max() <= 1
-    assert bf16_ulp_diff(host_bits(Kb), O.f64_to_bf16_bits(rK[c0:c1])).max() <= 2
+    assert bf16_ulp_diff(host_bits(Rb), O.f64_to_bf16_bits(rR[c0:c1])).max() <= 1
+    m, n = pooled_k_scales(f64(K), w.doc_len, 64)
+    assert pooled_k_ok(host_bits(Kb), rK[c0:c1], m[c0:c1], n[c0:c1])
 
 
 # ------------------------------------------------------- router-key encoding

@@ -1,8 +1,10 @@
 """The path at the workloads' full sizes on the GPU, in the launch
-configurations the benchmark uses, against the oracle: in full where the oracle
-finishes in seconds, otherwise on sampled documents and queries (every planted
-needle, the GPU's own selection, the shortest and longest documents and a
-seeded random sample).  Rules P2-P4 are in tests/parity.py."""
+configurations the benchmark uses, against the oracle: every document score,
+every query's top-k and every query's attention output (Tq = T and Tq = 1) of
+the 1M, 10M batch-16 and 100M-token workloads, and all three interleave rounds
+of the 10M-token interleave workload (pooled on the GPU from raw tokens; the
+oracle pools every document's router keys itself).  Rules P1-P4 are in
+tests/parity.py."""
 
 import sys
 
@@ -16,8 +18,8 @@ from synth import workloads as C
 from synth import native
 from synth import splitmix as sm
 
-from tests.parity import (ATT_TOL, GAP, GRAD_REL, SCORE_TOL, check_topk, dev_bits, encoded_keys_ok, host_bits,
-                          rel_rows)
+from tests.parity import (ATT_TOL, GRAD_REL, SCORE_TOL, check_topk, dev_bits, encoded_keys_ok, host_bits,
+                          pooled_k_ok, pooled_k_scales, rel_rows)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -31,6 +33,20 @@ def announce(*a):
 def f32(bits):
     """bf16 bits -> float32 (exact); the oracle widens to float64 block by block."""
     return (np.asarray(bits).astype(np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+class LazyKrbar:
+    """The oracle's view of a drawn pooled router-key store: chunk blocks regenerated on the host
+    generator when the oracle slices them (float32, exact bf16 values), so a 3.4 GB layer is never
+    held whole."""
+
+    def __init__(self, w, layer):
+        self.w, self.layer = w, layer
+        self.shape = (w.n_chunks, w.H, w.D)
+
+    def __getitem__(self, sl):
+        assert isinstance(sl, slice) and sl.step is None
+        return f32(C.krbar_block(self.w, self.layer, sl.start, min(sl.stop, self.w.n_chunks)))
 
 
 def device_krbar(w, layer):
@@ -123,29 +139,31 @@ def test_1M_corpus_full_step():
 
 
 # ----------------------------------------------------------------- 10M tokens
-def test_10M_batch16_route_sampled_queries():
-    """20,000 documents, 165K chunks, 16 queries x 64 tokens (the MFMA-bound shape).
-
-    The GPU scores all 16 queries in one launch; the oracle checks every
-    document of four of them (P2, P3) and the needles of all sixteen."""
+@pytest.mark.timeout(900)
+def test_10M_batch16_full_against_oracle():
+    """20,000 documents, 165K chunks, 16 queries x 64 tokens (the MFMA-bound shape), in the benchmark's
+    launch: msa_route_topk with stored norms over all 16 queries.  Every document score of every query
+    (P2), every query's top-16 (P3), every planted needle, and every query's attention output over its
+    selected documents (Tq = 64 and Tq = 1, P4)."""
     w = C.workload("10M-batch16")
-    announce("10M-batch16", w.describe())
+    announce("10M-batch16 full", w.describe())
     kr = device_krbar(w, 0)
-    host_kr = f32(C.krbar_block(w, 0, 0, w.n_chunks))
     q = C.queries(w)
     off = torch.from_numpy(w.doc_chunk_off).to(DEV)
-    doc = ops.route_scores(dev_bits(q["Qr"]), kr, off, krbar_inv_norm=ops.krbar_inv_norms(kr))
-    idx, sc = ops.topk_docs(doc, w.k)
-    gd, gi = doc.cpu().numpy(), idx.cpu().numpy()
-    checked = [0, 5, 10, 15]
-    _, ref_doc = O.route(f32(q["Qr"])[checked], host_kr, w.doc_chunk_off)
-    for j, b in enumerate(checked):
-        assert np.abs(gd[b] - ref_doc[j]).max() <= SCORE_TOL
-        check_topk(gi[b], ref_doc[j], w.k)
+    doc, idx, sc = ops.route_topk(dev_bits(q["Qr"]), kr, off, w.k, krbar_inv_norm=ops.krbar_inv_norms(kr))
+    gd, gi, gs = doc.cpu().numpy(), idx.cpu().numpy(), sc.cpu().numpy()
+    del kr
+    _, ref_doc = O.route(f32(q["Qr"]), LazyKrbar(w, 0), w.doc_chunk_off)
+    assert np.abs(gd - ref_doc).max() <= SCORE_TOL
+    for b in range(w.B):
+        check_topk(gi[b], ref_doc[b], w.k)
+        assert np.abs(gs[b] - ref_doc[b, gi[b]]).max() <= SCORE_TOL
     for b, d in C.planted_docs(w):
         assert gi[b, 0] == d
-    outs, _ = fetch_and_attend(w, idx, content_store(w), q)
-    check_attention(w, q, outs, gi, [0, 15])
+    outs, ml = fetch_and_attend(w, idx, content_store(w), q)
+    for b in range(w.B):
+        assert ml[b] == len(O.assemble(gi[b], w.doc_chunk_off))
+    check_attention(w, q, outs, gi, range(w.B))
 
 
 # ---------------------------------------------------------------- 100M tokens
@@ -178,43 +196,31 @@ def test_100M_layer_route_topk_equals_separate_calls():
     assert not any(excl[d] for d in sel)
 
 
-def test_100M_layer_sampled_documents():
-    """200,000 documents, 1.66M chunks (one routed layer of the 100M-token store).
-
-    The oracle scores a sample of documents (needles, the GPU's selection,
-    extremes, 2,000 random); P2 on all of them, and P3 in the form that holds
-    for a sample: the GPU's k-th score is no lower than any sampled document
-    outside its set (less the gap), and its selected scores are the oracle's."""
+@pytest.mark.timeout(900)
+def test_100M_layer_full_against_oracle():
+    """One routed layer of the 100M-token store (200,000 documents, 1.66M chunks, 128 router rows,
+    stored norms) in the benchmark's launch (msa_route_topk): all 200,000 document scores against the
+    oracle's scan of the whole layer (P2), the top-16 (P3: exact ids where the oracle's rank-16 gap
+    is >= 1e-3), every planted needle, and the attention over the GPU's selection at Tq = 128 and
+    Tq = 1 (P4)."""
     w = C.workload("100M-18layer")
     layer = 3
-    announce("100M layer", layer, w.describe())
+    announce("100M layer full", layer, w.describe())
     kr = device_krbar(w, layer)
     q = C.queries(w, layer)
     off = torch.from_numpy(w.doc_chunk_off).to(DEV)
-    doc = ops.route_scores(dev_bits(q["Qr"]), kr, off, krbar_inv_norm=ops.krbar_inv_norms(kr))
-    idx, sc = ops.topk_docs(doc, w.k)
+    doc, idx, sc = ops.route_topk(dev_bits(q["Qr"]), kr, off, w.k, krbar_inv_norm=ops.krbar_inv_norms(kr))
     gd, gi, gs = doc.cpu().numpy()[0], idx.cpu().numpy()[0], sc.cpu().numpy()[0]
-    needles = [d for _, d in C.planted_docs(w, layer)]
-    docs = sample_docs(w, list(gi) + needles)
-    # oracle on the sampled documents' chunks only (the generator regenerates any chunk range)
-    ref = np.empty(len(docs))
-    Qr = f32(q["Qr"])
-    for i, d in enumerate(docs):
-        g0, g1 = int(w.doc_chunk_off[d]), int(w.doc_chunk_off[d + 1])
-        _, dd = O.route(Qr, f32(C.krbar_block(w, layer, g0, g1)), np.array([0, g1 - g0]))
-        ref[i] = dd[0, 0]
-    assert np.abs(gd[docs] - ref).max() <= SCORE_TOL
-    pos = {int(d): i for i, d in enumerate(docs)}
-    sel = np.array([ref[pos[int(d)]] for d in gi])
-    assert np.abs(gs - sel).max() <= SCORE_TOL
-    assert np.all(np.diff(sel) <= 2 * SCORE_TOL)       # descending, up to the score tolerance
-    outside = np.array([ref[i] for i, d in enumerate(docs) if int(d) not in set(int(x) for x in gi)])
-    assert outside.max() <= sel.min() + GAP
-    for d in needles:
+    del kr
+    _, ref_doc = O.route(f32(q["Qr"]), LazyKrbar(w, layer), w.doc_chunk_off)
+    ref = ref_doc[0]
+    err = np.abs(gd - ref)
+    announce("100M layer full: max |score error|", float(err.max()))
+    assert err.max() <= SCORE_TOL
+    check_topk(gi, ref, w.k)
+    assert np.abs(gs - ref[gi]).max() <= SCORE_TOL
+    for _, d in C.planted_docs(w, layer):
         assert d in gi
-    # the GPU's scores over all documents: its selection is the exact top-k of what it computed
-    order = np.lexsort((np.arange(w.n_docs), -gd.astype(np.float64)))[: w.k]
-    assert list(order) == list(gi)
     outs, _ = fetch_and_attend(w, idx, content_store(w), q)
     check_attention(w, q, outs, gi[None], [0])
 
@@ -249,17 +255,6 @@ def gpu_pool_corpus(w, slab_tokens=1_000_000):
     return out
 
 
-def oracle_pool_docs(w, docs):
-    """The oracle's pooled (rounded) rows of the given documents: {doc: (K, V, Kr) float64 [n_d, H, D]}."""
-    res = {}
-    for d in docs:
-        t0, t1 = int(w.doc_tok_off[d]), int(w.doc_tok_off[d + 1])
-        K, V, Kr = (O.bf16_to_f64(C.raw_block(w, x, t0, t1)) for x in ("K", "V", "Kr"))
-        pk, pv, pr, _ = O.pool(K, V, Kr, [t1 - t0], w.chunk, w.rope_base)
-        res[int(d)] = (O.round_bf16(pk), O.round_bf16(pv), O.round_bf16(pr))
-    return res
-
-
 def interleave_on_gpu(w, pooled, q, fetch="gather"):
     from sparse_retrieval_memory_amd.interleave import Interleave
     Kb, Vb, Rb = pooled
@@ -276,17 +271,17 @@ def interleave_on_gpu(w, pooled, q, fetch="gather"):
 def test_interleave_reduced_against_oracle():
     """300 documents of the interleave corpus: pooled on the GPU from raw tokens, then 3 rounds per query,
     every round against the oracle's own pooling and interleave loop."""
-    from tests.parity import bf16_ulp_diff, host_bits, pooled_k_ok
+    from tests.parity import bf16_ulp_diff, host_bits, pooled_k_ok, pooled_k_scales
     w = C.workload("10M-interleave", n_docs=300)
     announce("interleave reduced", w.describe())
     pooled = gpu_pool_corpus(w)
     K = O.bf16_to_f64(C.raw_block(w, "K", 0, w.n_tok)); V = O.bf16_to_f64(C.raw_block(w, "V", 0, w.n_tok))
     Kr = O.bf16_to_f64(C.raw_block(w, "Kr", 0, w.n_tok))
     rK, rV, rR, off = O.pool(K, V, Kr, w.doc_len, w.chunk, w.rope_base)
+    assert pooled_k_ok(host_bits(pooled[0]), rK, *pooled_k_scales(K, w.doc_len, w.chunk))
     rK, rV, rR = O.round_bf16(rK), O.round_bf16(rV), O.round_bf16(rR)
     assert bf16_ulp_diff(host_bits(pooled[1]), O.f64_to_bf16_bits(rV)).max() <= 1
     assert bf16_ulp_diff(host_bits(pooled[2]), O.f64_to_bf16_bits(rR)).max() <= 1
-    assert pooled_k_ok(host_bits(pooled[0]), rK)
     q = C.queries(w)
     res = interleave_on_gpu(w, pooled, q)
     # the host-copy assembly gives bit-identical rounds
@@ -309,15 +304,69 @@ def test_interleave_reduced_against_oracle():
         assert ch["A"] in res[0].top_idx[b] and ch["B"] in res[1].top_idx[b] and ch["C"] in res[2].top_idx[b]
 
 
-def test_10M_interleave_full_pool_and_rounds():
-    """The whole 10M-token interleave workload: pooled on the GPU in 1M-token slabs, 4 queries x 3 rounds.
+def oracle_krbar_corpus(w, slab_tokens=1_000_000):
+    """The oracle's pooled router keys of every document: chunk means of the raw K_r (regenerated on the
+    host in document-aligned slabs, chain plants applied) in float64, rounded to bf16; float64 [G, H, D]."""
+    from oracle import native as ON
+    out = np.empty((w.n_chunks, w.H, w.D))
+    d0 = 0
+    while d0 < w.n_docs:
+        d1 = int(np.searchsorted(w.doc_tok_off, w.doc_tok_off[d0] + slab_tokens, side="right")) - 1
+        d1 = min(max(d1, d0 + 1), w.n_docs)
+        t0, t1 = int(w.doc_tok_off[d0]), int(w.doc_tok_off[d1])
+        c0, c1 = int(w.doc_chunk_off[d0]), int(w.doc_chunk_off[d1])
+        out[c0:c1] = O.round_bf16(ON.pool_means_bf16(C.raw_block(w, "Kr", t0, t1), w.doc_len[d0:d1], w.chunk))
+        d0 = d1
+    return out
 
-    Pooled rows against the oracle's pooling on sampled documents (P1); round-1 and round-2 document
-    scores against the oracle on sampled documents; every planted 3-hop chain recovered hop by hop;
-    no document retrieved twice."""
-    from tests.parity import bf16_ulp_diff, host_bits, pooled_k_ok
+
+class OracleContent:
+    """The oracle's pooled content rows (rotated K, V; rounded to bf16), pooled per document from the raw
+    tokens when first asked for.  ``K[idx]`` / ``V[idx]`` take arrays of global chunk ids."""
+
+    class _View:
+        def __init__(self, owner, j):
+            self.owner, self.j = owner, j
+
+        def __getitem__(self, idx):
+            return self.owner.rows(np.asarray(idx, dtype=np.int64), self.j)
+
+    def __init__(self, w):
+        self.w, self.cache = w, {}
+        self.K, self.V = OracleContent._View(self, 0), OracleContent._View(self, 1)
+
+    def doc(self, d):
+        if d not in self.cache:
+            w = self.w
+            t0, t1 = int(w.doc_tok_off[d]), int(w.doc_tok_off[d + 1])
+            K, V, Kr = (O.bf16_to_f64(C.raw_block(w, x, t0, t1)) for x in ("K", "V", "Kr"))
+            pk, pv, _, _ = O.pool(K, V, Kr, [t1 - t0], w.chunk, w.rope_base)
+            m, n = pooled_k_scales(K, [t1 - t0], w.chunk)
+            self.cache[d] = (O.round_bf16(pk), O.round_bf16(pv), pk, m, n)
+        return self.cache[d]
+
+    def rows(self, idx, j):
+        w = self.w
+        if len(idx) == 0:
+            return np.zeros((0, w.H, w.D))
+        docs = w.doc_of_chunk(idx)
+        return np.stack([self.doc(int(d))[j][int(g - w.doc_chunk_off[d])] for g, d in zip(idx, docs)])
+
+
+@pytest.mark.timeout(1200)
+def test_10M_interleave_full_against_oracle():
+    """The whole 10M-token interleave workload (20,000 documents, 165K chunks): pooled on the GPU in
+    1M-token slabs, then 4 queries x 3 rounds of route -> top-8 -> assemble -> attend.
+
+    P1 on every pooled router key of the corpus (the oracle pools all 10M tokens' K_r itself) and on
+    the pooled K and V of the retrieved and sampled documents; then each query's three rounds against
+    the oracle's interleave loop over its own pooled store: all 20,000 document scores per round
+    (excluded documents -inf on both sides), the top-8 (P3), and the attention output over the
+    retrieved documents (P4, rounds until the first admissible different selection); every planted
+    3-hop chain recovered hop by hop; no document retrieved twice."""
+    from tests.parity import bf16_ulp_diff, host_bits
     w = C.workload("10M-interleave")
-    announce("10M interleave", w.describe())
+    announce("10M interleave full", w.describe())
     pooled = gpu_pool_corpus(w)
     q = C.queries(w)
     res = interleave_on_gpu(w, pooled, q)
@@ -328,30 +377,32 @@ def test_10M_interleave_full_pool_and_rounds():
         assert ch["C"] in res[2].top_idx[b], (b, "hop 3")
         allr = res[-1].retrieved[b]
         assert len(set(int(x) for x in allr)) == len(allr) == w.k * w.rounds
-    # pooled rows and scores on a document sample (chains, the GPU's picks, extremes, random)
-    extra = [ch[x] for ch in chains for x in ("A", "B", "C")] + list(res[0].top_idx.ravel()) + \
-        list(res[1].top_idx.ravel())
-    docs = sample_docs(w, extra, n=100)
-    ref = oracle_pool_docs(w, docs)
     Kb, Vb, Rb = (host_bits(t) for t in pooled)
-    for d, (pk, pv, pr) in ref.items():
+    del pooled
+    announce("10M interleave full: oracle pools the router keys of all documents")
+    rR = oracle_krbar_corpus(w)
+    assert bf16_ulp_diff(Rb, O.f64_to_bf16_bits(rR)).max() <= 1
+    content = OracleContent(w)
+    extra = [ch[x] for ch in chains for x in ("A", "B", "C")] + [int(d) for d in np.ravel(res[-1].retrieved)]
+    for d in sample_docs(w, extra, n=60):
+        pk, pv, pk_exact, m, n = content.doc(int(d))
         g0, g1 = int(w.doc_chunk_off[d]), int(w.doc_chunk_off[d + 1])
         assert bf16_ulp_diff(Vb[g0:g1], O.f64_to_bf16_bits(pv)).max() <= 1
-        assert bf16_ulp_diff(Rb[g0:g1], O.f64_to_bf16_bits(pr)).max() <= 1
-        assert pooled_k_ok(Kb[g0:g1], pk)
-    Qr = f32(q["Qr"])
-    for r in (0, 1):
-        for b in range(w.B):
-            rows = Qr[b]
-            if r == 1:
-                rows = np.concatenate([rows] + [ref[int(d)][2] for d in res[0].top_idx[b]])
+        assert pooled_k_ok(Kb[g0:g1], pk_exact, m, n)
+    for b in range(w.B):
+        announce("10M interleave full: oracle rounds of query", b)
+        ref = O.interleave(f32(q["Qr"][b]), rR, content.K, content.V, w.doc_chunk_off, w.k, w.rounds,
+                           f32(q["Q"][b]), f32(q["Kloc"][b]), f32(q["Vloc"][b]), w.rope_base, w.D ** -0.5)
+        for r in range(w.rounds):
             g = res[r].doc_scores.cpu().numpy()[b]
-            for d in docs:
-                _, dd = O.route(rows[None], ref[int(d)][2], np.array([0, len(ref[int(d)][2])]))
-                if r == 1 and d in set(int(x) for x in res[0].top_idx[b]):
-                    assert g[d] == -np.inf
-                else:
-                    assert abs(g[d] - dd[0, 0]) <= 1e-4, (r, b, d)
+            s = ref[r]["doc_scores"]
+            fin = np.isfinite(s)
+            assert np.array_equal(fin, np.isfinite(g)), (b, r)           # the same documents are excluded
+            assert np.abs(g[fin] - s[fin]).max() <= 1e-4, (b, r)         # pooled stores may differ by an ulp
+            if check_topk(res[r].top_idx[b], s, w.k):
+                announce("10M interleave full: admissible different selection", b, r)
+                break      # an admissible different set (gap < 1e-3): later rounds no longer share inputs
+            assert rel_rows(res[r].O.cpu().numpy()[b], ref[r]["O"]) <= ATT_TOL, (b, r)
 
 
 # ------------------------------------------------------- router-key encoding
