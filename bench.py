@@ -314,7 +314,7 @@ def traffic_from(fetch_csv: str, write_csv: str, w) -> dict:
         for r in csv.DictReader(open(path)):
             if r["Counter_Name"] != counter:
                 continue
-            if "route_mfma_kernel<8, true, " in r["Kernel_Name"]:
+            if "route_ring8_kernel<true, " in r["Kernel_Name"]:
                 kern.append(float(r["Counter_Value"]))
             elif "copyBuffer" in r["Kernel_Name"]:
                 copy.append(float(r["Counter_Value"]))
@@ -326,7 +326,7 @@ def traffic_from(fetch_csv: str, write_csv: str, w) -> dict:
     fk, fc = read(fetch_csv, "FETCH_SIZE")
     wk, wc = read(write_csv, "WRITE_SIZE")
     fs, ws = copy_bytes / (fc * 1024), copy_bytes / (wc * 1024)
-    return {"kernel": "route_mfma_kernel<8, true, POL_NT> (stored norms, non-temporal copies)",
+    return {"kernel": "route_ring8_kernel<true, POL_NT> (8 heads, stored norms, non-temporal copies)",
             "workload": f"100M-token memory, one routed layer ({w.n_chunks:,} chunks), batch 1, "
                         f"{w.B * w.T} router rows, stored norms",
             "source_hash": route_source_hash(),
@@ -916,7 +916,7 @@ def main():
                            "trip"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "route_mfma_kernel (msa_route_scan), mean of HIP-event durations around the scan of "
+                     "kernel": "route_ring8_kernel (msa_route_scan), mean of HIP-event durations around the scan of "
                                f"layers {list(SCAN_EVENT_LAYERS)} in every timed step ({len(scan_ms)} launches); bytes = "
                                "Krbar + doc offsets + Qr + doc scores (32 B per memory token)",
                      "bytes_per_launch": bytes_algo,
