@@ -11,7 +11,8 @@ import os
 import re
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmsa.so")
+# MSA_LIBRARY names another build of the same library (e.g. the host-sanitizer build)
+LIB_PATH = os.environ.get("MSA_LIBRARY") or os.path.join(_HERE, "libmsa.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "msa.h")
 
 MSA_OK = 0

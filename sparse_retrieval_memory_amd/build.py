@@ -24,5 +24,22 @@ def build(verbose: bool = True, extra=()) -> str:
     return LIB
 
 
+def build_sanitized(out: str, verbose: bool = False) -> str:
+    """The same library with its host code built under AddressSanitizer and
+    UndefinedBehaviorSanitizer (device code unchanged), for checking the C ABI's
+    host-side validation; load it with the ASan runtime preloaded."""
+    flags = [f for f in FLAGS if f != "-O3"]
+    cmd = ["/opt/rocm/bin/hipcc", *flags, "-O1", "-g", "-fno-omit-frame-pointer",
+           "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           *SOURCES, "-o", out]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True, capture_output=not verbose)
+    return out
+
+
 if __name__ == "__main__":
-    build(extra=sys.argv[1:])
+    if sys.argv[1:2] == ["--sanitized"]:
+        build_sanitized(sys.argv[2], verbose=True)
+    else:
+        build(extra=sys.argv[1:])

@@ -748,34 +748,6 @@ krbar_norms_kernel(const uint16_t* __restrict__ Krbar, int64_t n_rows, float* __
   if (r < n_rows && piece == 0) out[r] = inv_norm_fast(ss);
 }
 
-// ------------------------------------------------------------ document max
-// Each document's thread reads its chunks' maxima and sets them back to 0 (re-arming
-// the workspace for the next scan: documents own disjoint chunk ranges, so no other
-// thread touches those words).
-__global__ void __launch_bounds__(256)
-doc_reduce_kernel(uint32_t* __restrict__ chunk_enc, int64_t n_chunks,
-                  const int64_t* __restrict__ doc_chunk_off, int64_t n_docs,
-                  const uint8_t* __restrict__ doc_exclude, float* __restrict__ doc_scores,
-                  float* __restrict__ chunk_scores) {
-  const int b = blockIdx.y;
-  const int64_t d = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (d >= n_docs) return;
-  int64_t g0 = doc_chunk_off[d], g1 = doc_chunk_off[d + 1];
-  if (g0 < 0) g0 = 0;
-  if (g1 > n_chunks) g1 = n_chunks;
-  uint32_t* ce = chunk_enc + (int64_t)b * n_chunks;
-  uint32_t best = 0;
-  for (int64_t g = g0; g < g1; ++g) {
-    const uint32_t e = ce[g];
-    ce[g] = 0u;
-    best = e > best ? e : best;
-    if (chunk_scores) chunk_scores[(int64_t)b * n_chunks + g] = dec_f32(e);
-  }
-  float s = (g1 > g0) ? dec_f32(best) : -INFINITY;
-  if (doc_exclude && doc_exclude[(int64_t)b * n_docs + d]) s = -INFINITY;
-  doc_scores[(int64_t)b * n_docs + d] = s;
-}
-
 // Compute units of the calling thread's current device, looked up once per device.
 // Every thread that fills a slot stores the same value, so relaxed atomics suffice.
 int num_cus() {
@@ -867,15 +839,6 @@ int launch_route_scan(const uint16_t* Qr, int B, int T, int H, const uint16_t* K
     case 8: return launch_route_h<8>(Qr, B, T, Krbar, inv_norm, n_chunks, chunk_enc, stream);
     default: set_error("H=%d unsupported", H); return MSA_ERR_UNSUPPORTED;
   }
-}
-
-int launch_doc_reduce(uint32_t* chunk_enc, int64_t n_chunks, const int64_t* doc_chunk_off, int64_t n_docs,
-                      const uint8_t* doc_exclude, int B, float* doc_scores, float* chunk_scores, hipStream_t stream) {
-  dim3 grid((unsigned)((n_docs + 255) / 256), (unsigned)B);
-  hipLaunchKernelGGL(doc_reduce_kernel, grid, dim3(256), 0, stream, chunk_enc, n_chunks, doc_chunk_off,
-                     n_docs, doc_exclude, doc_scores, chunk_scores);
-  MSA_CHECK_LAUNCH();
-  return MSA_OK;
 }
 
 int launch_route(const uint16_t* Qr, int B, int T, int H, const uint16_t* Krbar, const float* inv_norm,

@@ -404,41 +404,81 @@ topk_from_groups_filtered(const float* __restrict__ scores, uint64_t* __restrict
 }
 
 // The document max (the last step of the routing scores: a document's score is the max of its
-// chunks', -inf when excluded or empty) with the group maxima of the top-k folded in: a wave
-// holds 64 consecutive documents, i.e. one group, so it also writes the group's largest key.
-// Each document's thread sets its chunks' maxima back to 0 after reading them.
+// chunks', -inf when excluded or empty), with the group maxima of the top-k folded in (GROUPS).
+// One workgroup per (group of 64 documents, query).  Offsets are non-decreasing, so the group's
+// documents own the contiguous chunk range [off[d0], off[d0 + nd]): the 256 threads read it and
+// set it back to 0 (re-arming the workspace for the next scan) with coalesced accesses, two
+// chunks in flight per thread, and each chunk finds its document by a binary search over the
+// group's offsets in LDS and adds its maximum to the document's LDS slot with an LDS atomic max;
+// then the first wave forms the 64 scores and the group's largest key.  Offsets are clamped to
+// [0, n_chunks] and the search stays inside the group, so offsets that break the contract give
+// wrong scores but no access outside the buffers.
+template <bool GROUPS>
 __global__ void __launch_bounds__(256)
-doc_reduce_groups_kernel(uint32_t* __restrict__ chunk_enc, int64_t n_chunks,
-                         const int64_t* __restrict__ doc_chunk_off, int64_t n_docs,
-                         const uint8_t* __restrict__ doc_exclude, float* __restrict__ doc_scores,
-                         float* __restrict__ chunk_scores, int64_t n_groups, uint64_t* __restrict__ gmax) {
+doc_reduce_kernel(uint32_t* __restrict__ chunk_enc, int64_t n_chunks,
+                  const int64_t* __restrict__ doc_chunk_off, int64_t n_docs,
+                  const uint8_t* __restrict__ doc_exclude, float* __restrict__ doc_scores,
+                  float* __restrict__ chunk_scores, int64_t n_groups, uint64_t* __restrict__ gmax) {
+  __shared__ int64_t s_off[GROUP + 1];
+  __shared__ uint32_t s_best[GROUP];
   const int b = blockIdx.y;
-  const int64_t d = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  uint64_t key = 0ull;
-  if (d < n_docs) {
-    int64_t g0 = doc_chunk_off[d], g1 = doc_chunk_off[d + 1];
-    if (g0 < 0) g0 = 0;
-    if (g1 > n_chunks) g1 = n_chunks;
-    uint32_t* ce = chunk_enc + (int64_t)b * n_chunks;
-    uint32_t best = 0;
-    for (int64_t g = g0; g < g1; ++g) {
-      const uint32_t e = ce[g];
-      ce[g] = 0u;                             // re-arm the chunk maximum for the next scan
-      best = e > best ? e : best;
-      if (chunk_scores) chunk_scores[(int64_t)b * n_chunks + g] = dec_f32(e);
+  const int64_t grp = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int64_t d0 = grp * GROUP;
+  const int nd = (int)(n_docs - d0 < GROUP ? n_docs - d0 : GROUP);   // >= 1
+  if (tid <= nd) {
+    int64_t o = doc_chunk_off[d0 + tid];
+    o = o < 0 ? 0 : (o > n_chunks ? n_chunks : o);
+    s_off[tid] = o;
+  }
+  if (tid < GROUP) s_best[tid] = 0u;
+  __syncthreads();
+  const int64_t c0 = s_off[0], c1 = s_off[nd];
+  uint32_t* ce = chunk_enc + (int64_t)b * n_chunks;
+  float* cs = chunk_scores ? chunk_scores + (int64_t)b * n_chunks : nullptr;
+  // the largest j < nd with s_off[j] <= c (for c0 <= c < c1: the non-empty document holding c)
+  auto doc_of = [&](int64_t c) {
+    int lo = 0, hi = nd;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_off[mid] <= c) lo = mid;
+      else hi = mid;
     }
-    float s = (g1 > g0) ? dec_f32(best) : -INFINITY;
-    if (doc_exclude && doc_exclude[(int64_t)b * n_docs + d]) s = -INFINITY;
-    doc_scores[(int64_t)b * n_docs + d] = s;
-    key = make_key(s, (uint32_t)d);
+    return lo;
+  };
+  for (int64_t c = c0 + tid; c < c1; c += 512) {
+    const int64_t c2 = c + 256;
+    const bool two = c2 < c1;
+    const uint32_t e = ce[c];
+    const uint32_t e2 = two ? ce[c2] : 0u;
+    ce[c] = 0u;
+    if (two) ce[c2] = 0u;
+    if (cs) {
+      cs[c] = dec_f32(e);
+      if (two) cs[c2] = dec_f32(e2);
+    }
+    atomicMax(&s_best[doc_of(c)], e);
+    if (two) atomicMax(&s_best[doc_of(c2)], e2);
   }
+  __syncthreads();
+  if (tid < GROUP) {
+    uint64_t key = 0ull;
+    if (tid < nd) {
+      const int64_t d = d0 + tid;
+      float s = s_off[tid + 1] > s_off[tid] ? dec_f32(s_best[tid]) : -INFINITY;
+      if (doc_exclude && doc_exclude[(int64_t)b * n_docs + d]) s = -INFINITY;
+      doc_scores[(int64_t)b * n_docs + d] = s;
+      key = make_key(s, (uint32_t)d);
+    }
+    if constexpr (GROUPS) {
 #pragma unroll
-  for (int m = 32; m > 0; m >>= 1) {
-    const uint64_t o = shfl_xor_u64(key, m);
-    key = o > key ? o : key;
+      for (int m = 32; m > 0; m >>= 1) {
+        const uint64_t o = shfl_xor_u64(key, m);
+        key = o > key ? o : key;
+      }
+      if (tid == 0) gmax[(int64_t)b * n_groups + grp] = key;
+    }
   }
-  const int64_t grp = d / GROUP;
-  if ((threadIdx.x & 63) == 0 && grp < n_groups) gmax[(int64_t)b * n_groups + grp] = key;
 }
 
 // The group-based selection from group maxima already in gmax (1 <= k <= 32).
@@ -481,11 +521,21 @@ int launch_docs_topk(uint32_t* chunk_enc, int64_t n_chunks, const int64_t* doc_c
                      const uint8_t* doc_exclude, int B, int k, float* doc_scores, float* chunk_scores,
                      int32_t* top_idx, float* top_scores, uint64_t* gmax, hipStream_t stream) {
   const int64_t n_groups = (n_docs + GROUP - 1) / GROUP;
-  hipLaunchKernelGGL(doc_reduce_groups_kernel, dim3((unsigned)((n_docs + 255) / 256), (unsigned)B), dim3(256), 0,
-                     stream, chunk_enc, n_chunks, doc_chunk_off, n_docs, doc_exclude, doc_scores, chunk_scores,
-                     n_groups, gmax);
+  hipLaunchKernelGGL(doc_reduce_kernel<true>, dim3((unsigned)n_groups, (unsigned)B), dim3(256), 0, stream,
+                     chunk_enc, n_chunks, doc_chunk_off, n_docs, doc_exclude, doc_scores, chunk_scores, n_groups,
+                     gmax);
   MSA_CHECK_LAUNCH();
   return launch_topk_from_groups(doc_scores, B, n_docs, k, top_idx, top_scores, gmax, 1, stream);
+}
+
+int launch_doc_reduce(uint32_t* chunk_enc, int64_t n_chunks, const int64_t* doc_chunk_off, int64_t n_docs,
+                      const uint8_t* doc_exclude, int B, float* doc_scores, float* chunk_scores, hipStream_t stream) {
+  const int64_t n_groups = (n_docs + GROUP - 1) / GROUP;
+  hipLaunchKernelGGL(doc_reduce_kernel<false>, dim3((unsigned)n_groups, (unsigned)B), dim3(256), 0, stream,
+                     chunk_enc, n_chunks, doc_chunk_off, n_docs, doc_exclude, doc_scores, chunk_scores, n_groups,
+                     nullptr);
+  MSA_CHECK_LAUNCH();
+  return MSA_OK;
 }
 
 size_t topk_workspace(int B, int64_t n_docs, int k) {
