@@ -36,7 +36,9 @@
  *     thread-local error message; per host thread, the RoPE constants of the
  *     last attention launch (a pure function of its rope_offset and rope_base,
  *     kept to skip recomputing them); per device, the compute-unit count (read
- *     once, used to size the routing scan's grid).
+ *     once, used to size the routing scan's grid) and the address of the
+ *     fixed-size scratch array that msa_route_topk_noalloc uses in place of a
+ *     workspace (a static device array of the library, present from load).
  *   - Calls are asynchronous on `stream`; results are valid once the stream has
  *     reached the call.  Arguments are validated on the host before anything
  *     is launched: an invalid call returns a negative status and launches

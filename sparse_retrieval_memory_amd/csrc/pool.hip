@@ -10,14 +10,17 @@
 // bytes in, 3 * H * D * 2 bytes out per chunk), so the kernel is laid out to
 // keep many independent loads in flight and to touch LDS as little as possible:
 //
-//  * A workgroup is three waves, one per tensor (K, V, K_r); each wave walks
-//    the workgroup's contiguous range of chunks on its own, keeping its chunk
-//    sums in registers (a lane owns 8 dims of a head and their 8 RoPE partners,
-//    read as 16-byte non-temporal loads, 8 tokens per step), so no partial sums
-//    meet in LDS and the waves never wait for one another.
+//  * A workgroup is three waves walking the workgroup's contiguous range of
+//    chunks, each chunk's three tensors (K, V, K_r) split over the three waves;
+//    which wave takes which tensor rotates from chunk to chunk, so the rotation
+//    work of K is shared evenly (a wave that always took K lagged the two that
+//    only add).  A wave keeps its chunk sums in registers (a lane owns 8 dims
+//    of a head and their 8 RoPE partners, read as 16-byte non-temporal loads,
+//    16 tokens per step), so no partial sums meet in LDS and the waves never
+//    wait for one another.
 //  * Rotation is linear, so a chunk's rotated sum is
 //      sum_t R((p0 + t) theta) K_t = R(p0 theta) sum_t R(t theta) K_t :
-//    the K wave rotates every token by its offset t inside the chunk, from a
+//    the wave holding K rotates every token by its offset t inside the chunk, from a
 //    table of cos/sin(t theta_i), t < 64, built once per workgroup in LDS
 //    (angles reduced in fp64), and rotates the finished sum once by the chunk's
 //    start angle (longer chunks do this per block of 64 tokens).
@@ -34,8 +37,8 @@ namespace {
 
 constexpr int D = 128;
 constexpr int TABT = 64;           // token offsets in the rotation table (one block)
-constexpr int WG_PER_CU = 4;       // LDS: a 32 KB table per workgroup
-constexpr int STEP = 8;            // tokens per load batch
+constexpr int WG_PER_CU = 2;       // three waves of ~220 registers each: two workgroups per CU
+constexpr int STEP = 16;           // tokens per load batch
 
 // Lane layout for H heads: a token row of one tensor is H * D bf16; a lane takes 8 dims
 // [i0, i0 + 8) of a head and their partners [64 + i0, 72 + i0).  With H < 8 a wave covers
@@ -131,19 +134,18 @@ pool_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, cons
   const int grp = ln % 8;                                     // 8-dim group: pair dims i0..i0+7
   const int h0 = ln / 8;                                      // first head of the lane
   const int i0 = grp * 8;
-  const uint16_t* src = wave == 0 ? K : (wave == 1 ? V : Kr);
-  uint16_t* dst = wave == 0 ? Kbar : (wave == 1 ? Vbar : Krbar);
   double rev[8];                                              // this lane's frequencies, for the start angles
-  if (wave == 0) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) rev[e] = exp2(-(2.0 * (i0 + e) / D) * log2_base) * 0.15915494309189535;
-  }
+  for (int e = 0; e < 8; ++e) rev[e] = exp2(-(2.0 * (i0 + e) / D) * log2_base) * 0.15915494309189535;
 
   const int64_t cbase = doc_chunk_off[0];
   const int64_t tbase = doc_tok_off[0];
   int64_t d = find_doc(doc_chunk_off, n_docs, cbase + c_begin, lane);
   for (int64_t gl = c_begin; gl < c_end; ++gl) {
     const int64_t g = cbase + gl;
+    const int role = (int)((wave + (gl - c_begin)) % 3);        // 0: K, 1: V, 2: K_r, rotating over the waves
+    const uint16_t* src = role == 0 ? K : (role == 1 ? V : Kr);
+    uint16_t* dst = role == 0 ? Kbar : (role == 1 ? Vbar : Krbar);
     while (d + 1 < n_docs && doc_chunk_off[d + 1] <= g) ++d;
     ChunkInfo ci;
     {
@@ -187,7 +189,7 @@ pool_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, cons
 #pragma unroll
         for (int k = 0; k < STEP; ++k) {
           const int t = t0 + k * CF::TPW + tsub;
-          if (wave == 0) {
+          if (role == 0) {
             const float2* cs = &tab[t < TABT ? t : 0][i0];      // zero rows past bn add nothing
 #pragma unroll
             for (int hp = 0; hp < CF::HPL; ++hp) rot_add8(u1[k][hp], u2[k][hp], cs, a1[hp], a2[hp]);
@@ -197,7 +199,7 @@ pool_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, cons
           }
         }
       }
-      if (wave == 0) {
+      if (role == 0) {
         // rotate the block's sum by its first token's angle, R((p0 + b0) theta)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
