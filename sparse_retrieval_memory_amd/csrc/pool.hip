@@ -10,14 +10,13 @@
 // bytes in, 3 * H * D * 2 bytes out per chunk), so the kernel is laid out to
 // keep many independent loads in flight and to touch LDS as little as possible:
 //
-//  * A workgroup is three waves walking the workgroup's contiguous range of
-//    chunks, each chunk's three tensors (K, V, K_r) split over the three waves;
-//    which wave takes which tensor rotates from chunk to chunk, so the rotation
-//    work of K is shared evenly (a wave that always took K lagged the two that
-//    only add).  A wave keeps its chunk sums in registers (a lane owns 8 dims
-//    of a head and their 8 RoPE partners, read as 16-byte non-temporal loads,
-//    16 tokens per step), so no partial sums meet in LDS and the waves never
-//    wait for one another.
+//  * A workgroup is four waves walking the workgroup's contiguous range of
+//    chunks as a list of (chunk, tensor) items, tensor = K, V, K_r in turn;
+//    wave w takes items w, w + 4, ..., so the rotation work of K is shared
+//    evenly (a wave that always took K lagged those that only add).  A wave
+//    keeps an item's sums in registers (a lane owns 8 dims of a head and their
+//    8 RoPE partners, read as 16-byte non-temporal loads, 16 tokens per step),
+//    so no partial sums meet in LDS and the waves never wait for one another.
 //  * Rotation is linear, so a chunk's rotated sum is
 //      sum_t R((p0 + t) theta) K_t = R(p0 theta) sum_t R(t theta) K_t :
 //    the wave holding K rotates every token by its offset t inside the chunk, from a
@@ -37,8 +36,9 @@ namespace {
 
 constexpr int D = 128;
 constexpr int TABT = 64;           // token offsets in the rotation table (one block)
-constexpr int WG_PER_CU = 2;       // three waves of ~220 registers each: two workgroups per CU
+constexpr int WG_PER_CU = 2;       // four waves of ~230 registers each: two workgroups per CU
 constexpr int STEP = 16;           // tokens per load batch
+constexpr int POOL_WAVES = 4;      // waves per workgroup
 
 // Lane layout for H heads: a token row of one tensor is H * D bf16; a lane takes 8 dims
 // [i0, i0 + 8) of a head and their partners [64 + i0, 72 + i0).  With H < 8 a wave covers
@@ -103,7 +103,7 @@ struct ChunkInfo {
 };
 
 template <int H>
-__global__ void __launch_bounds__(192)
+__global__ void __launch_bounds__(64 * POOL_WAVES)
 pool_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, const uint16_t* __restrict__ Kr,
             const int64_t* __restrict__ doc_tok_off, const int64_t* __restrict__ doc_chunk_off,
             int64_t n_docs, int64_t n_tok, int64_t n_chunks, int64_t per_wg, int chunk_len, double log2_base,
@@ -113,13 +113,13 @@ pool_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, cons
   // lanes reading different t rows at the same i fall in different banks
   __shared__ __attribute__((aligned(16))) float2 tab[TABT][D / 2 + 2];
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;   // wave 0: K, 1: V, 2: K_r
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t c_begin = (int64_t)blockIdx.x * per_wg;
   int64_t c_end = c_begin + per_wg;
   if (c_end > n_chunks) c_end = n_chunks;
 
   // rotation table (angles reduced in fp64, evaluated in fp32)
-  for (int x = threadIdx.x; x < TABT * (D / 2); x += 192) {
+  for (int x = threadIdx.x; x < TABT * (D / 2); x += 64 * POOL_WAVES) {
     const int t = x / (D / 2), i = x % (D / 2);
     const double rev = exp2(-(2.0 * i / D) * log2_base) * 0.15915494309189535;   // theta_i / (2 pi)
     float c, s;
@@ -141,9 +141,11 @@ pool_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, cons
   const int64_t cbase = doc_chunk_off[0];
   const int64_t tbase = doc_tok_off[0];
   int64_t d = find_doc(doc_chunk_off, n_docs, cbase + c_begin, lane);
-  for (int64_t gl = c_begin; gl < c_end; ++gl) {
+  const int64_t n_items = 3 * (c_end - c_begin);
+  for (int64_t j = wave; j < n_items; j += POOL_WAVES) {
+    const int64_t gl = c_begin + j / 3;
     const int64_t g = cbase + gl;
-    const int role = (int)((wave + (gl - c_begin)) % 3);        // 0: K, 1: V, 2: K_r, rotating over the waves
+    const int role = (int)(j % 3);                              // 0: K, 1: V, 2: K_r
     const uint16_t* src = role == 0 ? K : (role == 1 ? V : Kr);
     uint16_t* dst = role == 0 ? Kbar : (role == 1 ? Vbar : Krbar);
     while (d + 1 < n_docs && doc_chunk_off[d + 1] <= g) ++d;
@@ -270,7 +272,7 @@ int launch_pool(const uint16_t* K, const uint16_t* V, const uint16_t* Kr, const 
   dim3 grid((unsigned)wgs);
 #define MSA_POOL_CASE(HH)                                                                        \
   case HH:                                                                                       \
-    hipLaunchKernelGGL(pool_kernel<HH>, grid, dim3(192), 0, stream, K, V, Kr, doc_tok_off,       \
+    hipLaunchKernelGGL(pool_kernel<HH>, grid, dim3(64 * POOL_WAVES), 0, stream, K, V, Kr, doc_tok_off,       \
                        doc_chunk_off, n_docs, n_tok, n_chunks, per, chunk_len, lb, Kbar, Vbar, Krbar); \
     break;
   switch (H) {
