@@ -475,18 +475,19 @@ __device__ __forceinline__ void ring_dma(const i32x4_t& rs, uint32_t soff, uint3
 }
 
 // Copies of half-tile (tile, hf) into `lds`: wave w moves the hf half-rows of chunks w, w + 8, ...
-// through a buffer resource on the tile's first row (tiles past the slice's last one re-read the
-// store's last tile; rows past the store's end re-read its last row).
+// through a buffer resource on the tile's first row (rows past the store's end re-read its last
+// row).  Tiles past the slice's end (te) get an empty resource: their copies, issued ahead so the
+// waits keep their fixed count, touch no memory (the range check turns them into zeros).
 struct RingSrc {
   i32x4_t rs;
   int last;                                    // last valid row of the tile
 };
-__device__ __forceinline__ RingSrc ring_src(const uint8_t* kr, int64_t n_chunks, int64_t tile) {
+__device__ __forceinline__ RingSrc ring_src(const uint8_t* kr, int64_t n_chunks, int64_t tile, int64_t te) {
   const int64_t n_tiles = (n_chunks + TC - 1) / TC;
   const int64_t t = tile < n_tiles ? tile : n_tiles - 1;
   const int64_t left = n_chunks - 1 - t * TC;
   RingSrc r;
-  r.rs = ring_rsrc(kr + t * TC * (2 * RING_ROW), TC * 2 * RING_ROW);
+  r.rs = ring_rsrc(kr + t * TC * (2 * RING_ROW), tile < te ? TC * 2 * RING_ROW : 0u);
   r.last = __builtin_amdgcn_readfirstlane((int)(left < TC - 1 ? left : TC - 1));
   return r;
 }
@@ -499,13 +500,14 @@ __device__ __forceinline__ void ring_copy(const RingSrc& src, int hf, uint8_t* l
 
 // The tile's 1/|k| block, fp32 [32][8] = 1 KB: wave w copies quarter w % 4 (chunks 8q .. 8q + 7, 256 B)
 // with a 4-byte-per-lane copy (waves 4-7 repeat waves 0-3, writing the same values).  voff4 =
-// 4 lane + 256 q; lanes past the store's end read 0 (the buffer's range check).
+// 4 lane + 256 q; lanes past the store's end read 0 (the buffer's range check), as does the whole
+// block of a tile past the slice's end.
 template <int POL>
-__device__ __forceinline__ void ring_norms(const float* knorm, int64_t n_chunks, int64_t tile,
+__device__ __forceinline__ void ring_norms(const float* knorm, int64_t n_chunks, int64_t tile, int64_t te,
                                            float* lds_rk, int wave, uint32_t voff4) {
   const int64_t n_tiles = (n_chunks + TC - 1) / TC;
   const int64_t t = tile < n_tiles ? tile : n_tiles - 1;
-  const i32x4_t rs = ring_rsrc(knorm + t * TC * 8, (uint32_t)((n_chunks - t * TC) * 8 * 4));
+  const i32x4_t rs = ring_rsrc(knorm + t * TC * 8, tile < te ? (uint32_t)((n_chunks - t * TC) * 8 * 4) : 0u);
   ring_dma<POL, 4>(rs, 0u, voff4, lds_rk + 64 * (wave & 3));
 }
 
@@ -514,7 +516,7 @@ __device__ __forceinline__ void ring_norms(const float* knorm, int64_t n_chunks,
 // into `nxt`, and (HF == 0) finish the previous tile if this wave is its receiver.
 template <bool NORMS, int POL, int J4>
 __device__ __forceinline__ void ring_sub_step(const uint8_t* __restrict__ kr, const float* __restrict__ knorm,
-                                              int64_t n_chunks, int64_t tile, bool has_prev,
+                                              int64_t n_chunks, int64_t tile, int64_t te, bool has_prev,
                                               const uint8_t* cur, uint8_t* nxt, const float* rk_cur,
                                               float* rk_next, float (*lds_rq)[RW], f32x4_t* xchg,
                                               const bf16x8_t (&qf)[4][8], f32x16_t& sacc, f32x16_t& sprev,
@@ -529,14 +531,14 @@ __device__ __forceinline__ void ring_sub_step(const uint8_t* __restrict__ kr, co
   asm volatile("" ::: "memory");
   lds_barrier();                              // everyone's copies visible; slot j - 1 fully consumed
   // half-tile j + 3: (tile + 1, 1 - HF) when HF == 0 ... (tile + 2, 0) when HF == 1
-  const RingSrc csrc = ring_src(kr, n_chunks, HF == 0 ? tile + 1 : tile + 2);
+  const RingSrc csrc = ring_src(kr, n_chunks, HF == 0 ? tile + 1 : tile + 2, te);
   constexpr int CHF = 1 - HF;
   if constexpr (NORMS && HF == 0) {
     // this tile's 1/|k| for the wave's four heads, read before the next tile's block is requested
     const float2 lo = *reinterpret_cast<const float2*>(rk_cur + nb * 8 + 2 * hs);
     const float2 hi = *reinterpret_cast<const float2*>(rk_cur + nb * 8 + 4 + 2 * hs);
     rk4 = make_float4(lo.x, lo.y, hi.x, hi.y);
-    ring_norms<POL>(knorm, n_chunks, tile + 1, rk_next, wave, voff4);
+    ring_norms<POL>(knorm, n_chunks, tile + 1, te, rk_next, wave, voff4);
   }
   f32x4_t* x = xchg + lane;
   if constexpr (HF == 0) {
@@ -691,9 +693,9 @@ route_ring8_kernel(const uint16_t* __restrict__ Qr, int B, int T, int RTq, int P
   // prologue: the tile's norms, then half-tiles 0, 1, 2 (the order the sub-steps' waits assume)
   const uint32_t voff = (uint32_t)lane * 16u;       // the lane's byte in a copied half-row
   const uint32_t voff4 = (uint32_t)lane * 4u + (uint32_t)(wave & 3) * 256u;   // ... in a norms block
-  if constexpr (NORMS) ring_norms<POL>(knorm, n_chunks, tb, rk0, wave, voff4);
+  if constexpr (NORMS) ring_norms<POL>(knorm, n_chunks, tb, te, rk0, wave, voff4);
   {
-    const RingSrc s0 = ring_src(kr, n_chunks, tb), s1 = ring_src(kr, n_chunks, tb + 1);
+    const RingSrc s0 = ring_src(kr, n_chunks, tb, te), s1 = ring_src(kr, n_chunks, tb + 1, te);
 #pragma unroll
     for (int i = 0; i < RING_COPIES; ++i) ring_copy<POL>(s0, 0, ring0, wave, voff, i);
 #pragma unroll
@@ -703,7 +705,7 @@ route_ring8_kernel(const uint16_t* __restrict__ Qr, int B, int T, int RTq, int P
   }
 
 #define MSA_RING_SUB(J4, TILE, CUR, NXT, RKC, RKN)                                                              \
-  ring_sub_step<NORMS, POL, J4>(kr, knorm, n_chunks, TILE, (TILE) > tb, CUR, NXT, RKC, RKN, lds_rq[rtl],         \
+  ring_sub_step<NORMS, POL, J4>(kr, knorm, n_chunks, TILE, te, (TILE) > tb, CUR, NXT, RKC, RKN, lds_rq[rtl],     \
                                 lds_x[rtl], qf, sacc, sprev, hs, b, t0, T, chunk_enc, wave, lane, rk4, voff, voff4)
   for (int64_t tile = tb; tile < te; tile += 2) {
     MSA_RING_SUB(0, tile, ring0, ring3, rk0, rk1);

@@ -181,6 +181,35 @@ def test_route_empty_documents_match_oracle():
     assert np.all(s3.cpu().numpy()[0][3:] == -np.inf)
 
 
+def test_route_long_documents_match_oracle():
+    """Groups of 64 documents whose chunk ranges span more than one pass of the document-max
+    workgroup (a 1,500-chunk document, several of 300-700 chunks, single-chunk and empty ones):
+    document scores, chunk scores and top-k against the oracle, and the workspace handed back zeroed."""
+    r = np.random.default_rng(43)
+    n_docs = 200
+    lens = r.integers(0, 3, n_docs)
+    lens[[5, 70, 71, 140]] = [1500, 700, 333, 513]
+    lens[[64, 65, 127, 199]] = 0
+    B, T, k = 2, 48, 8
+    Qr, Kr, off = _route_case(B, T, 8, n_docs, seed=43, lens=lens)
+    announce("route-long-docs", int(lens.sum()))
+    ref_ch, ref_doc = O.route(f64(Qr), f64(Kr), off)
+    fin = np.isfinite(ref_doc)
+    q, kr, offd = dev_bits(Qr), dev_bits(Kr), torch.from_numpy(off).to(DEV)
+    ws = torch.zeros(ops.route_topk_workspace_bytes(B, T, 8, 128, len(Kr), n_docs, k), dtype=torch.uint8, device=DEV)
+    ops.route_scan(q, kr, ws)
+    ch = torch.empty((B, len(Kr)), dtype=torch.float32, device=DEV)
+    doc, idx, _ = ops.route_select(B, len(Kr), offd, k, ws, chunk_scores=ch)
+    torch.cuda.synchronize()
+    doc = doc.cpu().numpy()
+    assert np.array_equal(np.isfinite(doc), fin)
+    assert np.abs(doc[fin] - ref_doc[fin]).max() <= SCORE_TOL
+    assert np.abs(ch.cpu().numpy() - ref_ch).max() <= SCORE_TOL
+    for bb in range(B):
+        check_topk(idx.cpu().numpy()[bb], ref_doc[bb], k)
+    assert int(ws.count_nonzero().item()) == 0
+
+
 def test_route_workspace_reuse_across_sizes():
     """One routing workspace reused by calls of different sizes (batch, chunks, documents, k) in a
     row, without clearing: every call's outputs are bit-identical to the same call on a fresh
