@@ -168,6 +168,8 @@ int launch_route(const uint16_t* Qr, int B, int T, int H, const uint16_t* Krbar,
                  float* doc_scores, float* chunk_scores, void* workspace, hipStream_t stream);
 int launch_route_scan(const uint16_t* Qr, int B, int T, int H, const uint16_t* Krbar, const float* inv_norm,
                       int64_t n_chunks, uint32_t* chunk_enc, hipStream_t stream);
+// Compute units of the calling thread's current device (looked up once per device).
+int num_cus();
 int launch_doc_reduce(uint32_t* chunk_enc, int64_t n_chunks, const int64_t* doc_chunk_off, int64_t n_docs,
                       const uint8_t* doc_exclude, int B, float* doc_scores, float* chunk_scores, hipStream_t stream);
 int launch_clear_u32(void* p, int64_t words, hipStream_t stream);

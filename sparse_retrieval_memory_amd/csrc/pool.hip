@@ -249,14 +249,6 @@ pool_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, cons
   }
 }
 
-int pool_cus() {
-  int dev = 0, v = 0;
-  if (hipGetDevice(&dev) == hipSuccess &&
-      hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-    return v;
-  return 256;
-}
-
 }  // namespace
 
 int launch_pool(const uint16_t* K, const uint16_t* V, const uint16_t* Kr, const int64_t* doc_tok_off,
@@ -265,7 +257,7 @@ int launch_pool(const uint16_t* K, const uint16_t* V, const uint16_t* Kr, const 
                 hipStream_t stream) {
   if (n_chunks == 0) return MSA_OK;
   const double lb = log2(rope_base);
-  int64_t wgs = (int64_t)pool_cus() * WG_PER_CU;
+  int64_t wgs = (int64_t)num_cus() * WG_PER_CU;
   if (wgs > n_chunks) wgs = n_chunks;
   const int64_t per = (n_chunks + wgs - 1) / wgs;
   wgs = (n_chunks + per - 1) / per;

@@ -750,6 +750,8 @@ krbar_norms_kernel(const uint16_t* __restrict__ Krbar, int64_t n_rows, float* __
   if (r < n_rows && piece == 0) out[r] = inv_norm_fast(ss);
 }
 
+}  // namespace
+
 // Compute units of the calling thread's current device, looked up once per device.
 // Every thread that fills a slot stores the same value, so relaxed atomics suffice.
 int num_cus() {
@@ -769,6 +771,8 @@ int num_cus() {
   }
   return c;
 }
+
+namespace {
 
 template <int H>
 int launch_route_h(const uint16_t* Qr, int B, int T, const uint16_t* Krbar, const float* inv_norm,
