@@ -507,7 +507,8 @@ __device__ __forceinline__ void ring_norms(const float* knorm, int64_t n_chunks,
                                            float* lds_rk, int wave, uint32_t voff4) {
   const int64_t n_tiles = (n_chunks + TC - 1) / TC;
   const int64_t t = tile < n_tiles ? tile : n_tiles - 1;
-  const i32x4_t rs = ring_rsrc(knorm + t * TC * 8, tile < te ? (uint32_t)((n_chunks - t * TC) * 8 * 4) : 0u);
+  const int64_t rows = n_chunks - t * TC < TC ? n_chunks - t * TC : TC;   // the tile's rows in the store
+  const i32x4_t rs = ring_rsrc(knorm + t * TC * 8, tile < te ? (uint32_t)(rows * 8 * 4) : 0u);
   ring_dma<POL, 4>(rs, 0u, voff4, lds_rk + 64 * (wave & 3));
 }
 
