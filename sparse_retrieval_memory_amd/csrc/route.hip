@@ -512,9 +512,12 @@ __device__ __forceinline__ void ring_norms(const float* knorm, int64_t n_chunks,
   ring_dma<POL, 4>(rs, 0u, voff4, lds_rk + 64 * (wave & 3));
 }
 
-// One sub-step: score half HF of tile `tile` from `cur` (ring slot J4 = j % 4, so HF = J4 & 1
-// and PAR = J4 >> 1 is the tile's parity in the slice), start the copies of half-tile j + 3
-// into `nxt`, and (HF == 0) finish the previous tile if this wave is its receiver.
+// One sub-step: score half HF of tile `tile` from `cur` (ring slot J4 = j % 4, so HF = J4 & 1),
+// start the copies of half-tile j + 3 into `nxt`, and (HF == 0) finish the previous tile if this
+// wave is its receiver.  The wave of the first head group (hs = 0) receives and finishes every
+// tile: the second group's waves, issued after it on the same SIMDs, reach the end of a
+// sub-step ~10% later, so giving the finish to the first group balances the pair (1-2.5% faster
+// than alternating the roles by tile parity, A/B on one box).
 template <bool NORMS, int POL, int J4>
 __device__ __forceinline__ void ring_sub_step(const uint8_t* __restrict__ kr, const float* __restrict__ knorm,
                                               int64_t n_chunks, int64_t tile, int64_t te, bool has_prev,
@@ -525,7 +528,6 @@ __device__ __forceinline__ void ring_sub_step(const uint8_t* __restrict__ kr, co
                                               uint32_t* chunk_enc, int wave, int lane,
                                               float4& rk4, uint32_t voff, uint32_t voff4) {
   constexpr int HF = J4 & 1;
-  constexpr int PAR = J4 >> 1;
   const int half = lane >> 5;
   const int nb = lane & 31;
   __builtin_amdgcn_s_waitcnt(0x0F78);         // vmcnt(8): this wave's copies of half-tile j are done
@@ -543,8 +545,8 @@ __device__ __forceinline__ void ring_sub_step(const uint8_t* __restrict__ kr, co
   }
   f32x4_t* x = xchg + lane;
   if constexpr (HF == 0) {
-    if (has_prev && hs == (PAR == 0 ? 1 : 0)) {
-      // receiver of the previous tile (parity 1 - PAR): add the sender's half and finish it
+    if (has_prev && hs == 0) {
+      // receiver of the previous tile: add the sender's half and finish it
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const f32x4_t o = x[q4 * 64];
@@ -617,7 +619,7 @@ __device__ __forceinline__ void ring_sub_step(const uint8_t* __restrict__ kr, co
     head_epilogue(1, acc_b, ss_b, rqv);
   }
   if constexpr (HF == 1) {
-    if (hs == (PAR == 0 ? 1 : 0)) {           // sender of this tile
+    if (hs == 1) {                            // sender of this tile
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4)
         x[q4 * 64] = f32x4_t{sacc[4 * q4], sacc[4 * q4 + 1], sacc[4 * q4 + 2], sacc[4 * q4 + 3]};
@@ -717,11 +719,10 @@ route_ring8_kernel(const uint16_t* __restrict__ Qr, int B, int T, int RTq, int P
     }
   }
 #undef MSA_RING_SUB
-  // finish the last tile: its parity decides which head group receives
+  // finish the last tile (the first head group receives)
   const int64_t last = te - 1;
-  const int par = (int)((last - tb) & 1);
   lds_barrier();
-  if (hs == (par == 0 ? 0 : 1)) {
+  if (hs == 0) {
     f32x4_t* x = lds_x[rtl] + lane;
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
