@@ -575,10 +575,17 @@ def main():
     side_out["topk_us"] = 1e3 * time_ms(lambda: ops.topk_docs(doc, k, top_idx=idx_d, top_scores=sc_d, ws=ws_k), 50)
     side_out["gather_us"] = 1e3 * time_ms(lambda: ops.gather_docs(idx_d, store, off_dev, staging, Mmax, mem_len=ml_dev),
                                           50)
-    side_out["select_us"] = 1e3 * time_ms(lambda: (ops.route_scan(qr[0], krbar[0], ws, krbar_inv_norm=knorm[0]),
-                                                   ops.route_select(1, G, off_dev, k, ws, doc_scores=doc,
-                                                                    top_idx=idx_d, top_scores=sc_d)), 10) \
-        - 1e3 * float(np.median(scan_ms))
+    # document max + top-k alone: each call's events bracket only msa_route_select, after a scan
+    sel_ev = []
+    for _ in range(10):
+        ops.route_scan(qr[0], krbar[0], ws, krbar_inv_norm=knorm[0])
+        a_, b2 = Ev(), Ev()
+        a_.record()
+        ops.route_select(1, G, off_dev, k, ws, doc_scores=doc, top_idx=idx_d, top_scores=sc_d)
+        b2.record()
+        sel_ev.append((a_, b2))
+    torch.cuda.synchronize()
+    side_out["select_us"] = 1e3 * float(np.median([a_.elapsed_time(b2) for a_, b2 in sel_ev[1:]]))
     ws_nn = ops.workspace(ops.route_workspace_bytes(1, w.T, H, D, G, w.n_docs), dev, "bench-nonorm")
     side_out["scan_ms_norms_in_kernel"] = time_ms(lambda: (ops.route_scan(qr[0], krbar[0], ws_nn),
                                                            ops.route_workspace_clear(ws_nn)), 10)

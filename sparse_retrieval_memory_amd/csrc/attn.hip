@@ -5,13 +5,14 @@
 // by k, the number of retrieved blocks).
 //
 // Flash-style on the matrix cores.  One workgroup owns 32 query rows of one
-// q-head; its 4 waves take every 4th tile of 32 keys (memory entries first,
-// then local keys up to the causal limit of the last row) and keep a running
-// max, sum and output per row; the waves' partial results are merged at the
-// end.  Per key tile, a wave computes S^T = K Q^T (keys x rows) with
-// v_mfma_f32_32x32x16_bf16, so every lane holds one query row's scores, and
-// the softmax statistics of a row live in one lane pair.  O^T += V^T P^T
-// then uses the same layout (V is transposed through LDS).
+// q-head; its 8 waves (two per SIMD) take runs of consecutive tiles of 32 keys
+// (memory entries first, then local keys up to the causal limit of the last
+// row) and keep a running max, sum and output per row; the waves' partial
+// results are merged at the end.  Per key tile, a wave computes S^T = K Q^T
+// (keys x rows) with v_mfma_f32_32x32x16_bf16, so every lane holds one query
+// row's scores, and the softmax statistics of a row live in one lane pair.
+// O^T += V^T P^T then uses the same layout: V is copied to LDS by LDS DMA and
+// read back transposed by ds_read_b64_tr_b16.
 //
 // Precision: the operands of both products are split into bf16 hi + lo parts
 // (q = qh + ql with |ql| <= 2^-9 |q|), so with fp32 accumulation the scores
@@ -34,9 +35,11 @@ namespace {
 constexpr int D = 128;
 constexpr int RT = 32;          // query rows per workgroup (MFMA N)
 constexpr int KT = 32;          // keys per tile (MFMA M)
-constexpr int NWAVE = 4;
+constexpr int NWAVE = 8;        // two waves per SIMD
 constexpr int THREADS = 64 * NWAVE;
-constexpr int VT_STRIDE = KT + 8;   // bf16 per transposed V row (dims x keys), padded
+constexpr int V_ROW = D * 2;        // bytes of one key's V row in a wave's LDS buffer
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 struct bf16pair {
   bf16x8_t hi, lo;
@@ -106,11 +109,12 @@ constexpr int PART_STRIDE = D + 4;   // floats per (wave, row) in the merge area
 
 // RoPE constants computed on the host in fp64 and passed with the launch:
 // rev[i] = theta_i / (2 pi); start[sg][i] = (cos, sin) at position rope_offset +
-// TAB_SEG * sg; step[i] = (cos, sin) of one position.
+// TAB_SEG * sg; step[i], step8[i] = (cos, sin) of one and of eight positions.
 struct RopeTables {
   double rev[D / 2];
   float2 start[TAB_POS / TAB_SEG][D / 2];
   float2 step[D / 2];
+  float2 step8[D / 2];
 };
 
 __global__ void __launch_bounds__(THREADS, 1)
@@ -120,14 +124,17 @@ attn_mfma_kernel(const uint16_t* __restrict__ Q, int Tq, int Hq, const uint16_t*
                  int rope_offset, const RopeTables tabs, float scale_log2e, float* __restrict__ O,
                  float* __restrict__ LSE, int mode, float* __restrict__ PO, float* __restrict__ PML) {
   __shared__ double rev[D / 2];
-  // cos/sin of positions rope_offset + p (p < n_local <= TAB_POS), frequency i: every query row
-  // and local key of this workgroup sits at such a position.  Rows are padded by 16 bytes: the
-  // 32 lanes of a rotation read 32 consecutive positions at one frequency, which with 512-byte
-  // rows would all fall in the same four banks.
-  __shared__ __attribute__((aligned(16))) float2 cs_tab[TAB_POS][D / 2 + 2];
-  // per wave: V^T of its current tile [D][VT_STRIDE] bf16; reused at the end for the merge
-  __shared__ __attribute__((aligned(16))) float smem[NWAVE * RT * PART_STRIDE];
-  static_assert(sizeof(smem) >= sizeof(uint16_t) * NWAVE * D * VT_STRIDE, "V^T area");
+  // LDS: first cos/sin of positions rope_offset + p (p < n_local <= TAB_POS), frequency i: every
+  // query row and local key of this workgroup sits at such a position.  Rows are padded by 16
+  // bytes: the 32 lanes of a rotation read 32 consecutive positions at one frequency, which with
+  // 512-byte rows would all fall in the same four banks.  Then, per wave, V of its current tile
+  // (KT rows of V_ROW bytes).  The merge's partial outputs overwrite both once every tile is done.
+  constexpr int TAB_FLOATS = TAB_POS * (D / 2 + 2) * 2;
+  constexpr int V_FLOATS = NWAVE * KT * V_ROW / 4;
+  constexpr int PART_FLOATS = NWAVE * RT * PART_STRIDE;
+  __shared__ __attribute__((aligned(16))) float lds[TAB_FLOATS + V_FLOATS > PART_FLOATS ? TAB_FLOATS + V_FLOATS
+                                                                                       : PART_FLOATS];
+  float2 (*cs_tab)[D / 2 + 2] = reinterpret_cast<float2 (*)[D / 2 + 2]>(lds);
   __shared__ float m_sh[NWAVE][RT], l_sh[NWAVE][RT];
 
   const int tid = threadIdx.x;
@@ -137,77 +144,110 @@ attn_mfma_kernel(const uint16_t* __restrict__ Q, int Tq, int Hq, const uint16_t*
   const int h = blockIdx.y;
   const int b = blockIdx.z;
   const int g = h / (Hq / Hkv);
-  int M = mode == MODE_LOCAL ? 0 : mem_len[b];
-  if (M < 0) M = 0;
-  if (M > Mmax) M = Mmax;
   int last = r0 + RT - 1;
   if (last > Tq - 1) last = Tq - 1;
   const int n_pos = (Tl - Tq) + last + 1;          // positions of this tile's rows and their local keys
   const int n_local = mode == MODE_MEMORY ? 0 : n_pos;
-  const int n_keys = M + n_local;
-  const int n_tiles = (n_keys + KT - 1) / KT;
 
-  // Raw K and V of key tile t for this lane (key k0 + col): K dims 16 (ks % 4) + 64 (ks / 4) + 8 hf + e
-  // (the A-operand order), V dims 64 hf + 8 i + e.  Keys past the end read as zeros.
-  auto load_tile = [&](int t, uint4 (&kr)[8], uint4 (&vr)[8], bool& local) {
-    const int j = t * KT + col;
-    local = false;
-    const uint16_t *kp = nullptr, *vp = nullptr;
-    if (j < M) {
-      kp = Kmem + ((int64_t)b * Mmax + j) * mstride + (int64_t)g * D;
-      vp = Vmem + ((int64_t)b * Mmax + j) * mstride + (int64_t)g * D;
-    } else if (j < n_keys) {
-      local = true;
-      kp = Kloc + (((int64_t)b * Tl + (j - M)) * Hkv + g) * D;
-      vp = Vloc + (((int64_t)b * Tl + (j - M)) * Hkv + g) * D;
-    }
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-      kr[ks] = kp ? *reinterpret_cast<const uint4*>(kp + 16 * (ks & 3) + 64 * (ks >> 2) + 8 * hf)
-                  : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      vr[i] = vp ? *reinterpret_cast<const uint4*>(vp + 64 * hf + 8 * i) : make_uint4(0, 0, 0, 0);
-  };
-
-  // The query rows and this wave's first key tile are loaded before the tables are
-  // built, so their memory latency overlaps the table set-up.
+  // Loads in the order their data is needed (vector loads complete in order): the table's
+  // constants, then the query rows and the memory length, whose latency overlaps the table set-up.
+  const bool use_tab = n_pos <= TAB_POS;
+  const int ti = tid & (D / 2 - 1), tsg = tid / (D / 2);
+  static_assert(THREADS >= TAB_POS / TAB_SEG * (D / 2), "one segment per thread covers the table");
+  const bool tab_thread = use_tab && tid < TAB_POS / TAB_SEG * (D / 2) && tsg * TAB_SEG < n_pos;
+  float2 t_st = make_float2(0.f, 0.f), t_d1 = t_st, t_d8 = t_st;
+  if (tab_thread) {
+    t_st = tabs.start[tsg][ti];
+    t_d1 = tabs.step[ti];
+    t_d8 = tabs.step8[ti];
+  }
   const int row = r0 + col;
   uint4 qraw[8];
-  if (row < Tq) {
-    const uint16_t* q = Q + (((int64_t)b * Tq + row) * Hq + h) * D;
+  {
+    // rows past the end read the last row (unconditional loads keep the waits' counts exact);
+    // their values are replaced by zeros below
+    const uint16_t* q = Q + (((int64_t)b * Tq + (row < Tq ? row : Tq - 1)) * Hq + h) * D;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       qraw[ks] = *reinterpret_cast<const uint4*>(q + 16 * ks + 8 * hf);
       qraw[ks + 4] = *reinterpret_cast<const uint4*>(q + 64 + 16 * ks + 8 * hf);
     }
   }
-  uint4 kc[8], vc[8];
-  bool lc = false;
-  if (wave < n_tiles) load_tile(wave, kc, vc, lc);
+  const int m_in = mode == MODE_LOCAL ? 0 : mem_len[b];
 
-  const bool use_tab = n_pos <= TAB_POS;
   if (!use_tab && tid < D / 2) rev[tid] = tabs.rev[tid];
-  // Table for n_local <= TAB_POS: thread (frequency i, segment sg) starts from the exact angle at the
-  // segment's first position and steps by the exact one-position rotation (error ~1e-6 after 32 steps).
-  if (use_tab) {
-    const int i = tid & (D / 2 - 1), sg = tid / (D / 2);
-    static_assert(THREADS / (D / 2) * TAB_SEG == TAB_POS, "one segment per thread covers the table");
-    const int p0 = sg * TAB_SEG;
-    if (p0 < n_pos) {
-      const float2 st = tabs.start[sg][i], d1 = tabs.step[i];
-      float c = st.x, s_ = st.y;
-      const float cd = d1.x, sd = d1.y;
-      const int p1 = p0 + TAB_SEG < n_pos ? p0 + TAB_SEG : n_pos;
-      for (int p = p0; p < p1; ++p) {
-        cs_tab[p][i] = make_float2(c, s_);
-        const float cn = c * cd - s_ * sd;
-        s_ = s_ * cd + c * sd;
-        c = cn;
+  // Table for n_local <= TAB_POS: thread (frequency i, segment sg) covers the segment's 32 positions
+  // as 4 interleaved runs of 8.  From the exact angle at the segment's first position, the runs' starts
+  // follow by exact 8-position rotations and each run by exact one-position rotations, so every
+  // entry is at most 10 rotations from an exact value (error ~1e-6).
+  if (tab_thread) {
+    static_assert(TAB_SEG == 4 * 8, "four runs of eight positions per segment");
+    const int p0 = tsg * TAB_SEG;
+    float c[4], s_[4];
+    c[0] = t_st.x;
+    s_[0] = t_st.y;
+#pragma unroll
+    for (int m = 1; m < 4; ++m) {
+      c[m] = c[m - 1] * t_d8.x - s_[m - 1] * t_d8.y;
+      s_[m] = s_[m - 1] * t_d8.x + c[m - 1] * t_d8.y;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int p = p0 + 8 * m + u;
+        if (p < n_pos) cs_tab[p][ti] = make_float2(c[m], s_[m]);
+        const float cn = c[m] * t_d1.x - s_[m] * t_d1.y;
+        s_[m] = s_[m] * t_d1.x + c[m] * t_d1.y;
+        c[m] = cn;
       }
     }
   }
   __syncthreads();
+
+  const int M = m_in < 0 ? 0 : (m_in > Mmax ? Mmax : m_in);
+  const int n_keys = M + n_local;
+  const int n_tiles = (n_keys + KT - 1) / KT;
+
+  // Raw K of key tile t for this lane (key k0 + col) in registers: dims 16 (ks % 4) + 64 (ks / 4) +
+  // 8 hf + e (the A-operand order).  Keys past the end read the tile's first key (unconditional
+  // loads keep the waits' counts exact); their scores are masked.
+  auto load_k = [&](int t, uint4 (&kr)[8], bool& local) {
+    const int j0 = t * KT + col;
+    const int j = j0 < n_keys ? j0 : t * KT;
+    local = j0 < n_keys && j0 >= M;
+    const uint16_t* kp = j < M ? Kmem + ((int64_t)b * Mmax + j) * mstride + (int64_t)g * D
+                               : Kloc + (((int64_t)b * Tl + (j - M)) * Hkv + g) * D;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      kr[ks] = *reinterpret_cast<const uint4*>(kp + 16 * (ks & 3) + 64 * (ks >> 2) + 8 * hf);
+  };
+  // V of key tile t into this wave's LDS buffer by 8 LDS-DMA copies of 1 KB: copy n fills rows
+  // 4n .. 4n + 3; lane l fills row 4n + l / 16, 16-byte slot l % 16, which holds dims 8 p .. 8 p + 7
+  // of the row's key with p = slot ^ 4 (row % 4) (the swizzle makes the transposing reads below
+  // conflict-free).  Keys past the end copy the tile's first key: their probabilities are zero.
+  uint8_t* const vbuf = reinterpret_cast<uint8_t*>(lds + TAB_FLOATS) + wave * KT * V_ROW;
+  auto load_v = [&](int t) {
+    const int slot = lane & 15, r4 = lane >> 4;
+#pragma unroll
+    for (int n = 0; n < KT / 4; ++n) {
+      int j = t * KT + 4 * n + r4;
+      if (j >= n_keys) j = t * KT;
+      const uint16_t* vp = j < M ? Vmem + ((int64_t)b * Mmax + j) * mstride + (int64_t)g * D
+                                 : Vloc + (((int64_t)b * Tl + (j - M)) * Hkv + g) * D;
+      dma16(vp + 8 * (slot ^ (r4 << 2)), vbuf + 4 * V_ROW * n);
+    }
+  };
+
+  // wave w takes a run of consecutive tiles; the first n_tiles % NWAVE waves take one more, so the
+  // longer runs start with memory tiles, which cost less than local ones (no rotation or split)
+  const int per = n_tiles / NWAVE, extra = n_tiles % NWAVE;
+  const int t_begin = wave * per + (wave < extra ? wave : extra);
+  const int t_end = t_begin + per + (wave < extra ? 1 : 0);
+  // The first tile's V copies overlap the query set-up.  The query rows have arrived long since;
+  // waiting for them here keeps the wait before their use from also covering these copies.
+  __builtin_amdgcn_s_waitcnt(0x0F70);     // vmcnt(0)
+  if (t_begin < t_end) load_v(t_begin);
 
   // ---- Q^T as the B operand: lane (col, hf) holds query row r0 + col, dims 16 ks + 8 hf + j
   bf16x8_t qh[8], ql[8];
@@ -253,60 +293,50 @@ attn_mfma_kernel(const uint16_t* __restrict__ Q, int Tq, int Hq, const uint16_t*
 
   const int qrow = r0 + col;
   const int lim = (Tl - Tq) + qrow;      // last visible local key of this row
-  uint16_t (*myvt)[VT_STRIDE] = reinterpret_cast<uint16_t (*)[VT_STRIDE]>(smem) + wave * D;
 
-  for (int t = wave; t < n_tiles; t += NWAVE) {
+  for (int t = t_begin; t < t_end; ++t) {
     const int k0 = t * KT;
     const int j = k0 + col;
-    // prefetch this wave's next tile while the current one is scored
-    uint4 kn[8], vn[8];
-    bool ln = false;
-    if (t + NWAVE < n_tiles) load_tile(t + NWAVE, kn, vn, ln);
-    const bool local = lc;
-    // V tile -> LDS, transposed: myvt[dim][key]; lane (col, hf) copies dims [64 hf, 64 hf + 64) of key col
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t w4[4] = {vc[i].x, vc[i].y, vc[i].z, vc[i].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        myvt[64 * hf + 8 * i + 2 * e][col] = (uint16_t)(w4[e] & 0xFFFFu);
-        myvt[64 * hf + 8 * i + 2 * e + 1][col] = (uint16_t)(w4[e] >> 16);
-      }
-    }
+    uint4 kc[8];
+    bool local;
+    load_k(t, kc, local);
+    if (t != t_begin) load_v(t);
     f32x16_t s;
 #pragma unroll
     for (int i = 0; i < 16; ++i) s[i] = 0.f;
     const bool tile_local = __builtin_amdgcn_readfirstlane((int)(k0 + KT > M && M < n_keys)) != 0;
     if (!tile_local) {
-      // memory keys only: exact bf16 operands, Q split in two
+      // memory keys only: exact bf16 operands, Q split in two (two accumulation chains)
+      f32x16_t s2;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s2[i] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
         const bf16x8_t kb = __builtin_bit_cast(bf16x8_t, kc[ks]);
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, qh[ks], s, 0, 0, 0);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, ql[ks], s, 0, 0, 0);
+        s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, ql[ks], s2, 0, 0, 0);
       }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[i] += s2[i];
     } else {
-      float lo[4][8], hi[4][8];
+      // local keys (or a tile holding both kinds): rotate in fp32, split in two; a dim block
+      // ks < 4 and its RoPE partners ks + 4 at a time, so few unpacked values are live
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        unpack8(kc[ks], lo[ks]);
-        unpack8(kc[ks + 4], hi[ks]);
-      }
-      if (local) {
-        if (use_tab) {
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) rotate_pairs_tab(lo[ks], hi[ks], cs_tab[j - M], 16 * ks + 8 * hf);
-        } else {
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) rotate_pairs(lo[ks], hi[ks], rope_offset + (j - M), rev, 16 * ks + 8 * hf);
+        float lo[8], hi[8];
+        unpack8(kc[ks], lo);
+        unpack8(kc[ks + 4], hi);
+        if (local) {
+          if (use_tab) rotate_pairs_tab(lo, hi, cs_tab[j - M], 16 * ks + 8 * hf);
+          else rotate_pairs(lo, hi, rope_offset + (j - M), rev, 16 * ks + 8 * hf);
         }
-      }
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const bf16pair kb = split8(ks < 4 ? lo[ks] : hi[ks - 4]);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb.hi, qh[ks], s, 0, 0, 0);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb.hi, ql[ks], s, 0, 0, 0);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb.lo, qh[ks], s, 0, 0, 0);
+        const bf16pair ka = split8(lo), kb = split8(hi);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka.hi, qh[ks], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka.hi, ql[ks], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka.lo, qh[ks], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb.hi, qh[ks + 4], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb.hi, ql[ks + 4], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb.lo, qh[ks + 4], s, 0, 0, 0);
       }
     }
 
@@ -356,22 +386,31 @@ attn_mfma_kernel(const uint16_t* __restrict__ Q, int Tq, int Hq, const uint16_t*
     }
     const bf16pair p0 = split8(pb[0]), p1 = split8(pb[1]);
 
-    // ---- O^T += V^T P^T: A = V^T (32 dims x 16 keys) from LDS
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // this wave's LDS writes of V^T have completed
-    __builtin_amdgcn_wave_barrier();
+    // ---- O^T += V^T P^T: A = V^T (32 dims x 16 keys) by transposing LDS reads.  In each 16-lane
+    // group a read hands lane i element i % 4 of the 8-byte piece that lane 4 r + i / 4 addresses,
+    // as its element r; so lane (col, hf) receives dim 32 dt + col of keys 16 st + 8 hf + 4 h + r when
+    // lane 4 r + c of its group addresses dims 32 dt + 16 (col / 16) + 4 c .. + 3 of that key's row.
+    const int gi = lane & 15;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        const bf16x8_t va = *reinterpret_cast<const bf16x8_t*>(&myvt[32 * dt + col][16 * st + 8 * hf]);
+        i16x4_t part[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int row = 16 * st + 8 * hf + 4 * h + (gi >> 2);
+          const int p = 4 * dt + 2 * ((lane >> 4) & 1) + ((gi & 3) >> 1);    // logical 16-byte slot
+          const int off = row * V_ROW + ((p ^ ((row & 3) << 2)) << 4) + ((gi & 1) << 3);
+          part[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vbuf + off));
+        }
+        const bf16x8_t va = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
         oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, st == 0 ? p0.hi : p1.hi, oacc[dt], 0, 0, 0);
         oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, st == 0 ? p0.lo : p1.lo, oacc[dt], 0, 0, 0);
       }
     }
-    __builtin_amdgcn_wave_barrier();      // V^T reads done before the next tile overwrites it
-#pragma unroll
-    for (int i = 0; i < 8; ++i) { kc[i] = kn[i]; vc[i] = vn[i]; }
-    lc = ln;
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // the reads of V are done before the next copies overwrite it
+    asm volatile("" ::: "memory");
   }
 
   // ---- merge the waves: O = sum_w 2^(m_w - m) O_w / sum_w 2^(m_w - m) l_w
@@ -393,7 +432,7 @@ attn_mfma_kernel(const uint16_t* __restrict__ Q, int Tq, int Hq, const uint16_t*
     LSE[((int64_t)b * Tq + r0 + col) * Hq + h] = (mx + log2f(lt)) * 0.6931471805599453f;
   // scaled partial outputs through LDS (fp32 [wave][row][dims], rows skewed; in the V^T area):
   // accumulators i..i+3 of a dim tile are 4 consecutive dims, written as one 16-byte store
-  float* part = smem;                                         // NWAVE x RT x PART_STRIDE floats
+  float* part = lds;                                          // NWAVE x RT x PART_STRIDE floats
   const float sc = mode == MODE_FULL ? wscale * inv : wscale;   // partial modes stay unnormalised
   __syncthreads();
 #pragma unroll
@@ -406,9 +445,9 @@ attn_mfma_kernel(const uint16_t* __restrict__ Q, int Tq, int Hq, const uint16_t*
                       oacc[dt][4 * i4 + 3] * sc);
     }
   __syncthreads();
-  // thread -> (row, 16 dims): sum the waves' parts and write 16 contiguous floats
-  for (int x = tid; x < RT * (D / 16); x += THREADS) {
-    const int row_ = x / (D / 16), d0 = (x % (D / 16)) * 16;
+  // thread -> (row, 8 dims): sum the waves' parts and write 8 contiguous floats
+  for (int x = tid; x < RT * (D / 8); x += THREADS) {
+    const int row_ = x / (D / 8), d0 = (x % (D / 8)) * 8;
     if (r0 + row_ >= Tq) continue;
     const int64_t ri = ((int64_t)b * Tq + r0 + row_) * Hq + h;     // (query, row, q-head)
     float* out = O + ri * D + d0;
@@ -434,7 +473,7 @@ attn_mfma_kernel(const uint16_t* __restrict__ Q, int Tq, int Hq, const uint16_t*
     }
     if (mode == MODE_LOCAL && d0 == 0) { PML[2 * ri] = mxr; PML[2 * ri + 1] = ltr; }
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
+    for (int q4 = 0; q4 < 2; ++q4) {
       float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
       for (int w = 0; w < NWAVE; ++w) {
@@ -665,6 +704,7 @@ int launch_attn_mode(const uint16_t* Q, int B, int Tq, int Hq, const uint16_t* K
       };
       for (int sg = 0; sg < TAB_POS / TAB_SEG; ++sg) tb.start[sg][i] = cs((double)rope_offset + TAB_SEG * sg);
       tb.step[i] = cs(1.0);
+      tb.step8[i] = cs(8.0);
     }
     cache.valid = true;
     cache.offset = rope_offset;
