@@ -117,6 +117,34 @@ struct RopeTables {
   float2 step8[D / 2];
 };
 
+// One table thread's share: positions p0 .. p0 + TAB_SEG - 1 (below n_pos) at frequency i, as 4
+// interleaved runs of 8.  From the exact (cos, sin) at p0 the runs' starts follow by exact 8-position
+// rotations and each run by exact one-position rotations, so every entry is at most 10 rotations
+// from an exact value (error ~1e-6).
+__device__ __forceinline__ void fill_cs_segment(float2 (*cs_tab)[D / 2 + 2], int i, int p0, int n_pos, float2 st,
+                                                float2 d1, float2 d8) {
+  static_assert(TAB_SEG == 4 * 8, "four runs of eight positions per segment");
+  float c[4], s_[4];
+  c[0] = st.x;
+  s_[0] = st.y;
+#pragma unroll
+  for (int m = 1; m < 4; ++m) {
+    c[m] = c[m - 1] * d8.x - s_[m - 1] * d8.y;
+    s_[m] = s_[m - 1] * d8.x + c[m - 1] * d8.y;
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int p = p0 + 8 * m + u;
+      if (p < n_pos) cs_tab[p][i] = make_float2(c[m], s_[m]);
+      const float cn = c[m] * d1.x - s_[m] * d1.y;
+      s_[m] = s_[m] * d1.x + c[m] * d1.y;
+      c[m] = cn;
+    }
+  }
+}
+
 __global__ void __launch_bounds__(THREADS, 1)
 attn_mfma_kernel(const uint16_t* __restrict__ Q, int Tq, int Hq, const uint16_t* __restrict__ Kloc,
                  const uint16_t* __restrict__ Vloc, int Tl, int Hkv, const uint16_t* __restrict__ Kmem,
@@ -176,39 +204,24 @@ attn_mfma_kernel(const uint16_t* __restrict__ Q, int Tq, int Hq, const uint16_t*
   const int m_in = mode == MODE_LOCAL ? 0 : mem_len[b];
 
   if (!use_tab && tid < D / 2) rev[tid] = tabs.rev[tid];
-  // Table for n_local <= TAB_POS: thread (frequency i, segment sg) covers the segment's 32 positions
-  // as 4 interleaved runs of 8.  From the exact angle at the segment's first position, the runs' starts
-  // follow by exact 8-position rotations and each run by exact one-position rotations, so every
-  // entry is at most 10 rotations from an exact value (error ~1e-6).
-  if (tab_thread) {
-    static_assert(TAB_SEG == 4 * 8, "four runs of eight positions per segment");
-    const int p0 = tsg * TAB_SEG;
-    float c[4], s_[4];
-    c[0] = t_st.x;
-    s_[0] = t_st.y;
-#pragma unroll
-    for (int m = 1; m < 4; ++m) {
-      c[m] = c[m - 1] * t_d8.x - s_[m - 1] * t_d8.y;
-      s_[m] = s_[m - 1] * t_d8.x + c[m - 1] * t_d8.y;
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int p = p0 + 8 * m + u;
-        if (p < n_pos) cs_tab[p][ti] = make_float2(c[m], s_[m]);
-        const float cn = c[m] * t_d1.x - s_[m] * t_d1.y;
-        s_[m] = s_[m] * t_d1.x + c[m] * t_d1.y;
-        c[m] = cn;
-      }
-    }
-  }
+  // Table for n_local <= TAB_POS: thread (frequency ti, segment tsg) fills the segment's positions.
+  if (tab_thread) fill_cs_segment(cs_tab, ti, tsg * TAB_SEG, n_pos, t_st, t_d1, t_d8);
   __syncthreads();
 
   const int M = m_in < 0 ? 0 : (m_in > Mmax ? Mmax : m_in);
   const int n_keys = M + n_local;
   const int n_tiles = (n_keys + KT - 1) / KT;
 
+  // Row of key j (memory entry j < M, else local key j - M) of this workgroup's kv head, with the
+  // choice made on offsets (one select instead of two address paths)
+  const int64_t mem_base = (int64_t)b * Mmax * mstride + (int64_t)g * D;
+  const int64_t loc_base = ((int64_t)b * Tl - M) * Hkv * D + (int64_t)g * D;
+  const int64_t loc_stride = (int64_t)Hkv * D;
+  auto key_row = [&](const uint16_t* mem, const uint16_t* loc, int j) -> const uint16_t* {
+    const bool in_mem = j < M;
+    const int64_t off = in_mem ? mem_base + (int64_t)j * mstride : loc_base + (int64_t)j * loc_stride;
+    return (in_mem ? mem : loc) + off;
+  };
   // Raw K of key tile t for this lane (key k0 + col) in registers: dims 16 (ks % 4) + 64 (ks / 4) +
   // 8 hf + e (the A-operand order).  Keys past the end read the tile's first key (unconditional
   // loads keep the waits' counts exact); their scores are masked.
@@ -216,8 +229,7 @@ attn_mfma_kernel(const uint16_t* __restrict__ Q, int Tq, int Hq, const uint16_t*
     const int j0 = t * KT + col;
     const int j = j0 < n_keys ? j0 : t * KT;
     local = j0 < n_keys && j0 >= M;
-    const uint16_t* kp = j < M ? Kmem + ((int64_t)b * Mmax + j) * mstride + (int64_t)g * D
-                               : Kloc + (((int64_t)b * Tl + (j - M)) * Hkv + g) * D;
+    const uint16_t* kp = key_row(Kmem, Kloc, j);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
       kr[ks] = *reinterpret_cast<const uint4*>(kp + 16 * (ks & 3) + 64 * (ks >> 2) + 8 * hf);
@@ -233,8 +245,7 @@ attn_mfma_kernel(const uint16_t* __restrict__ Q, int Tq, int Hq, const uint16_t*
     for (int n = 0; n < KT / 4; ++n) {
       int j = t * KT + 4 * n + r4;
       if (j >= n_keys) j = t * KT;
-      const uint16_t* vp = j < M ? Vmem + ((int64_t)b * Mmax + j) * mstride + (int64_t)g * D
-                                 : Vloc + (((int64_t)b * Tl + (j - M)) * Hkv + g) * D;
+      const uint16_t* vp = key_row(Vmem, Vloc, j);
       dma16(vp + 8 * (slot ^ (r4 << 2)), vbuf + 4 * V_ROW * n);
     }
   };
@@ -432,9 +443,9 @@ attn_mfma_kernel(const uint16_t* __restrict__ Q, int Tq, int Hq, const uint16_t*
     LSE[((int64_t)b * Tq + r0 + col) * Hq + h] = (mx + log2f(lt)) * 0.6931471805599453f;
   // scaled partial outputs through LDS (fp32 [wave][row][dims], rows skewed; in the V^T area):
   // accumulators i..i+3 of a dim tile are 4 consecutive dims, written as one 16-byte store
+  // (every wave has left its tile loop at the barrier above, so the table and V areas are free)
   float* part = lds;                                          // NWAVE x RT x PART_STRIDE floats
   const float sc = mode == MODE_FULL ? wscale * inv : wscale;   // partial modes stay unnormalised
-  __syncthreads();
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -570,17 +581,8 @@ attn_decode_kernel(const uint16_t* __restrict__ Q, int Tq, int Hq, const uint16_
     const int fi = tid & (D / 2 - 1), sg = tid / (D / 2);
     static_assert(DEC_THREADS / (D / 2) * TAB_SEG >= TAB_POS, "the segments cover the table");
     const int p0 = sg * TAB_SEG;
-    if (sg < TAB_POS / TAB_SEG && p0 < n_loc) {
-      const float2 st = tabs.start[sg][fi], d1 = tabs.step[fi];
-      float c = st.x, s_ = st.y;
-      const int p1 = p0 + TAB_SEG < n_loc ? p0 + TAB_SEG : n_loc;
-      for (int p = p0; p < p1; ++p) {
-        cs_tab[p][fi] = make_float2(c, s_);
-        const float cn = c * d1.x - s_ * d1.y;
-        s_ = s_ * d1.x + c * d1.y;
-        c = cn;
-      }
-    }
+    if (sg < TAB_POS / TAB_SEG && p0 < n_loc)
+      fill_cs_segment(cs_tab, fi, p0, n_loc, tabs.start[sg][fi], tabs.step[fi], tabs.step8[fi]);
   }
   __syncthreads();
 
