@@ -239,14 +239,24 @@ attn_mfma_kernel(const uint16_t* __restrict__ Q, int Tq, int Hq, const uint16_t*
   // of the row's key with p = slot ^ 4 (row % 4) (the swizzle makes the transposing reads below
   // conflict-free).  Keys past the end copy the tile's first key: their probabilities are zero.
   uint8_t* const vbuf = reinterpret_cast<uint8_t*>(lds + TAB_FLOATS) + wave * KT * V_ROW;
+  const int64_t v_piece = 8 * ((lane & 15) ^ ((lane >> 4) << 2));   // this lane's 16-byte slot's dims
   auto load_v = [&](int t) {
-    const int slot = lane & 15, r4 = lane >> 4;
+    // row 4n + r4 of the tile: offsets advance by 4 rows per copy in both address ranges
+    const int j0 = t * KT + (lane >> 4);
+    int64_t om = mem_base + (int64_t)j0 * mstride + v_piece;
+    int64_t ol = loc_base + (int64_t)j0 * loc_stride + v_piece;
+    const int64_t of = (t * KT < M ? mem_base + (int64_t)(t * KT) * mstride : loc_base + (int64_t)(t * KT) * loc_stride)
+                       + v_piece;                              // the tile's first key, for keys past the end
+    const bool first_mem = t * KT < M;
 #pragma unroll
     for (int n = 0; n < KT / 4; ++n) {
-      int j = t * KT + 4 * n + r4;
-      if (j >= n_keys) j = t * KT;
-      const uint16_t* vp = key_row(Vmem, Vloc, j);
-      dma16(vp + 8 * (slot ^ (r4 << 2)), vbuf + 4 * V_ROW * n);
+      const int j = j0 + 4 * n;
+      const bool in_mem = j < M, valid = j < n_keys;
+      const bool use_mem = valid ? in_mem : first_mem;
+      const int64_t off = valid ? (in_mem ? om : ol) : of;
+      dma16((use_mem ? Vmem : Vloc) + off, vbuf + 4 * V_ROW * n);
+      om += 4 * mstride;
+      ol += 4 * loc_stride;
     }
   };
 
@@ -353,13 +363,21 @@ attn_mfma_kernel(const uint16_t* __restrict__ Q, int Tq, int Hq, const uint16_t*
 
     // ---- mask and online softmax for this lane's row (keys 8 (i/4) + 4 hf + i % 4 of the tile)
     float tmax = -INFINITY;
+    // every (row, key) of the tile visible: all rows exist and the last key is within the
+    // first row's causal limit (memory keys always are)
+    const bool all_vis = r0 + RT <= Tq && k0 + KT <= n_keys && k0 + KT - 1 - M <= (Tl - Tq) + r0;
+    if (all_vis) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = k0 + 8 * (i >> 2) + 4 * hf + (i & 3);
-      bool vis = key < n_keys && qrow < Tq;
-      if (key >= M) vis = vis && (key - M) <= lim;
-      s[i] = vis ? s[i] : -INFINITY;
-      tmax = fmaxf(tmax, s[i]);
+      for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = k0 + 8 * (i >> 2) + 4 * hf + (i & 3);
+        bool vis = key < n_keys && qrow < Tq;
+        if (key >= M) vis = vis && (key - M) <= lim;
+        s[i] = vis ? s[i] : -INFINITY;
+        tmax = fmaxf(tmax, s[i]);
+      }
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
     const float m_new = fmaxf(m_run, tmax);

@@ -630,6 +630,8 @@ def test_store_append_then_delete_round_trip():
                                               (2, 64, 64, 133, 16), (1, 5, 9, 0, 0), (1, 17, 40, 1, 3),
                                               (3, 16, 16, 70, 8), (1, 128, 128, 448, 16),
                                               (1, 64, 200, 40, 7), (2, 1, 300, 5, 2),
+                                              # 32-row tiles with 5-8, 14-16 and 17 key tiles over 8 waves
+                                              (1, 128, 128, 128, 16), (1, 96, 96, 416, 16), (1, 32, 128, 400, 9),
                                               # <= 4 rows, Mmax + Tl <= 512, Tl <= 128: the few-row kernel
                                               (1, 1, 128, 133, 16), (1, 3, 100, 50, 7), (2, 4, 4, 0, 0),
                                               (1, 1, 1, 1, 0), (1, 2, 128, 384, 16), (3, 1, 64, 77, 5)])
