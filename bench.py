@@ -371,8 +371,8 @@ def main():
         print(json.dumps({k: tr[k] for k in ("bytes_per_launch", "algorithmic_bytes_per_launch", "source_hash")}))
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): this build runs the path on a "
-              "single MI355X and is not sharded across GPUs.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): the library runs the path on a "
+              "single MI355X and does not shard it across GPUs.", file=sys.stderr)
         sys.exit(2)
 
     import torch

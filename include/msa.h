@@ -59,7 +59,7 @@ extern "C" {
 
 #define MSA_OK 0
 #define MSA_ERR_INVALID_ARG (-1)   /* null pointer, bad size, bad alignment, ... */
-#define MSA_ERR_UNSUPPORTED (-2)   /* a shape this build does not implement (e.g. D != 128) */
+#define MSA_ERR_UNSUPPORTED (-2)   /* a shape the library does not implement (e.g. D != 128) */
 #define MSA_ERR_WORKSPACE (-3)     /* workspace smaller than the *_workspace_bytes() value */
 #define MSA_ERR_HIP (-4)           /* a HIP runtime call failed */
 

@@ -23,7 +23,7 @@ Sources (web pages on MSA; cited by page and section):
 * [blog]      jkf87.github.io post on MSA, "core technique 1: Top-k Sparse
   Attention", "core technique 2: Document-wise RoPE".
 
-Readings where the pages leave a step open (each listed in the design doc):
+Readings where the pages leave a step open:
 
 * pooled chunks never cross documents; a trailing partial chunk is averaged
   over its actual length;
