@@ -695,6 +695,44 @@ def test_attention_split_matches_fused_and_oracle(B, Tq, Tl, M, offset, Hq, Hkv)
     assert worst <= LSE_TOL
 
 
+def _random_attn_shapes(n=24, seed=20261204):
+    """Seeded shapes across both attention kernels: 1-4 query rows (the few-row kernel when the
+    keys fit) and up to 200 (the matrix-core kernel), local lengths past the 128-position table,
+    memory lengths from none to several hundred entries, and four GQA ratios."""
+    rng = np.random.default_rng(seed)
+    heads = [(32, 8), (16, 2), (8, 8), (32, 4)]
+    out = []
+    for i in range(n):
+        Tq = int(rng.choice([1, 2, 4])) if i % 3 == 0 else int(rng.integers(1, 201))
+        Tl = Tq + int(rng.integers(0, 301))
+        M = int(rng.choice([0, int(rng.integers(1, 33)), int(rng.integers(33, 401))]))
+        Hq, Hkv = heads[i % len(heads)]
+        out.append((int(rng.integers(1, 3)), Tq, Tl, M, int(rng.integers(0, 33)), Hq, Hkv))
+    return out
+
+
+@pytest.mark.parametrize("B,Tq,Tl,M,offset,Hq,Hkv", _random_attn_shapes())
+def test_attention_random_shapes_match_oracle(B, Tq, Tl, M, offset, Hq, Hkv):
+    """msa_sparse_attn_decode and msa_sparse_attn_forward (O and log-sum-exp) against the oracle."""
+    announce("attn-random", B, Tq, Tl, M, offset, Hq, Hkv)
+    Q, Kl, Vl, st, mem_len, _, Mmax = _attn_bwd_case(B, Tq, Tl, M, offset, Hq, Hkv, seed=B * 911 + Tq * 7 + M)
+    stg = dev_bits(st)
+    args = (dev_bits(Q), dev_bits(Kl), dev_bits(Vl), stg, stg[:, :, 1], 2 * Hkv * 128, Mmax,
+            torch.from_numpy(mem_len).to(DEV), offset)
+    o_dec = ops.sparse_attn_decode(*args, 1e6)
+    o_fwd, lse = ops.sparse_attn_forward(*args, rope_base=1e6)
+    torch.cuda.synchronize()
+    o_dec, o_fwd, lse = o_dec.cpu().numpy(), o_fwd.cpu().numpy(), lse.cpu().numpy()
+    for b in range(B):
+        m = int(mem_len[b])
+        ref = O.attend(f64(Q[b]), f64(Kl[b]), f64(Vl[b]), f64(st[b, :m, 0]), f64(st[b, :m, 1]), offset, 1e6,
+                       128 ** -0.5)
+        assert rel_rows(o_dec[b], ref) <= 1e-4
+        assert rel_rows(o_fwd[b], ref) <= 1e-4
+        ref_lse = O.attend_lse(f64(Q[b]), f64(Kl[b]), f64(st[b, :m, 0]), offset, 1e6, 128 ** -0.5)
+        assert float(np.abs(lse[b] - ref_lse).max()) <= LSE_TOL
+
+
 # ------------------------------------------------------ attention backward
 def _attn_bwd_case(B, Tq, Tl, M, offset, Hq=32, Hkv=8, seed=0):
     D = 128
