@@ -21,9 +21,9 @@
 // queries, and the probabilities, are split.  RoPE angles are reduced in fp64
 // (position x frequency in revolutions) and evaluated in fp32; up to 128 local
 // positions the workgroup first builds a cos/sin table in LDS (an exact value
-// every 32 positions, one-position rotations in between) that the query rows
-// and local keys read.  Scores are pre-scaled by scale * log2(e) so the
-// exponentials are exp2.
+// every 32 positions, then 8-position and one-position rotations, at most 10
+// from an exact value) that the query rows and local keys read.  Scores are
+// pre-scaled by scale * log2(e) so the exponentials are exp2.
 #include "msa_internal.h"
 #include "attn_split.h"
 
