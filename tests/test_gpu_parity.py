@@ -713,7 +713,8 @@ def _random_attn_shapes(n=24, seed=20261204):
 
 @pytest.mark.parametrize("B,Tq,Tl,M,offset,Hq,Hkv", _random_attn_shapes())
 def test_attention_random_shapes_match_oracle(B, Tq, Tl, M, offset, Hq, Hkv):
-    """msa_sparse_attn_decode and msa_sparse_attn_forward (O and log-sum-exp) against the oracle."""
+    """msa_sparse_attn_decode and msa_sparse_attn_forward (O and log-sum-exp) against the oracle; the
+    two-launch split (local partial + memory merge) against the one-launch forward."""
     announce("attn-random", B, Tq, Tl, M, offset, Hq, Hkv)
     Q, Kl, Vl, st, mem_len, _, Mmax = _attn_bwd_case(B, Tq, Tl, M, offset, Hq, Hkv, seed=B * 911 + Tq * 7 + M)
     stg = dev_bits(st)
@@ -721,8 +722,13 @@ def test_attention_random_shapes_match_oracle(B, Tq, Tl, M, offset, Hq, Hkv):
             torch.from_numpy(mem_len).to(DEV), offset)
     o_dec = ops.sparse_attn_decode(*args, 1e6)
     o_fwd, lse = ops.sparse_attn_forward(*args, rope_base=1e6)
+    # the same attention in two launches: local-key partial, then the memory pass merging with it
+    part = ops.sparse_attn_local_partial(args[0], args[1], args[2], offset, 1e6)
+    o_split = ops.sparse_attn_memory_merge(args[0], Tl, Hkv, stg, stg[:, :, 1], 2 * Hkv * 128, Mmax, args[7], offset,
+                                           part, 1e6)
     torch.cuda.synchronize()
     o_dec, o_fwd, lse = o_dec.cpu().numpy(), o_fwd.cpu().numpy(), lse.cpu().numpy()
+    assert rel_rows(o_split.cpu().numpy(), o_fwd) <= 1e-5      # same sums in another order
     for b in range(B):
         m = int(mem_len[b])
         ref = O.attend(f64(Q[b]), f64(Kl[b]), f64(Vl[b]), f64(st[b, :m, 0]), f64(st[b, :m, 1]), offset, 1e6,
