@@ -245,9 +245,10 @@ attn_mfma_kernel(const uint16_t* __restrict__ Q, int Tq, int Hq, const uint16_t*
     const int j0 = t * KT + (lane >> 4);
     int64_t om = mem_base + (int64_t)j0 * mstride + v_piece;
     int64_t ol = loc_base + (int64_t)j0 * loc_stride + v_piece;
-    const int64_t of = (t * KT < M ? mem_base + (int64_t)(t * KT) * mstride : loc_base + (int64_t)(t * KT) * loc_stride)
-                       + v_piece;                              // the tile's first key, for keys past the end
+    // the tile's first key, read in place of keys past the end
     const bool first_mem = t * KT < M;
+    const int64_t of = (first_mem ? mem_base + (int64_t)(t * KT) * mstride
+                                  : loc_base + (int64_t)(t * KT) * loc_stride) + v_piece;
 #pragma unroll
     for (int n = 0; n < KT / 4; ++n) {
       const int j = j0 + 4 * n;
