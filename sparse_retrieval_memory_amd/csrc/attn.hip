@@ -531,15 +531,16 @@ namespace {
 // For decoding (Tq <= DEC_MAX_ROWS) one matrix-core tile would use 1 of its 32 rows.  Here a
 // workgroup owns one (query row, q-head) and one lane owns one key: lanes form the key's
 // score in fp32 (memory keys as given, local keys rotated from the LDS cos/sin table), the
-// workgroup takes the softmax, and the output is summed over V rows staged in LDS (the table's
-// space, free once the scores are formed).  Used when every key fits: Mmax + Tl <= DEC_MAX_KEYS
-// and Tl <= TAB_POS.
+// workgroup takes the softmax, and the output is summed over V rows that every thread loads into
+// registers at the start (16 bytes of each of its keys), so their latency hides behind the scores.
+// Used when every key fits: Mmax + Tl <= DEC_MAX_KEYS and Tl <= TAB_POS.
 constexpr int DEC_THREADS = 512;             // two waves per SIMD
 constexpr int DEC_LPK = 8;                    // lanes per key in the score pass (16 dims each)
 constexpr int DEC_KPP = DEC_THREADS / DEC_LPK;   // keys per pass
 constexpr int DEC_MAX_KEYS = DEC_THREADS;     // one key per lane in the softmax
 constexpr int DEC_PASSES = DEC_MAX_KEYS / DEC_KPP;
-constexpr int DEC_VPT = DEC_MAX_KEYS * 16 / DEC_THREADS;   // 16-byte V pieces per thread
+constexpr int DEC_VSLOTS = DEC_THREADS / 16;  // V: 16 lanes per key row (16 bytes each), key slots
+constexpr int DEC_VPT = DEC_MAX_KEYS / DEC_VSLOTS;   // keys per thread in the weighted sum
 constexpr int DEC_MAX_ROWS = 4;
 constexpr int DEC_WAVES = DEC_THREADS / 64;
 
@@ -550,23 +551,35 @@ attn_decode_kernel(const uint16_t* __restrict__ Q, int Tq, int Hq, const uint16_
                    int rope_offset, const RopeTables tabs, float scale_log2e, float* __restrict__ O,
                    float* __restrict__ LSE) {
   // one area: the cos/sin table (positions rope_offset + p, p < TAB_POS) while the scores are
-  // formed, then the V rows [key][dim]
-  __shared__ __attribute__((aligned(16))) uint8_t area[DEC_MAX_KEYS * D * 2];
-  static_assert(sizeof(float2) * TAB_POS * (D / 2 + 2) <= sizeof(area), "table fits the V area");
+  // formed, then the key slots' partial weighted sums [slot][dim]
+  constexpr int TAB_BYTES = (int)sizeof(float2) * TAB_POS * (D / 2 + 2);
+  constexpr int PV_BYTES = (int)sizeof(float) * DEC_VSLOTS * D;
+  __shared__ __attribute__((aligned(16))) uint8_t area[TAB_BYTES > PV_BYTES ? TAB_BYTES : PV_BYTES];
   float2 (*cs_tab)[D / 2 + 2] = reinterpret_cast<float2 (*)[D / 2 + 2]>(area);
-  uint16_t (*vs)[D] = reinterpret_cast<uint16_t (*)[D]>(area);
+  float (*pv)[D] = reinterpret_cast<float (*)[D]>(area);
   __shared__ float qs[D];
   __shared__ float ps[DEC_MAX_KEYS];
   __shared__ float red[2][DEC_WAVES];
-  __shared__ float2 pv[DEC_WAVES][D / 2];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int g = h / (Hq / Hkv);
+  const int n_loc = (Tl - Tq) + i + 1;            // local keys this row sees
+  // Loads in the order their data is needed (vector loads complete in order): the memory length,
+  // the query pair and the table's constants before the key and value rows, so that the set-up
+  // below waits for those alone.
   int M = mem_len[b];
+  const int qt = tid & (D / 2 - 1);
+  const uint16_t* qrow = Q + (((int64_t)b * Tq + i) * Hq + h) * D;
+  const uint16_t q_x1 = qrow[qt], q_x2 = qrow[qt + D / 2];
+  const double q_rev = tabs.rev[qt];
+  const int fi = tid & (D / 2 - 1), sg = tid / (D / 2);
+  static_assert(DEC_THREADS / (D / 2) * TAB_SEG >= TAB_POS, "the segments cover the table");
+  const bool tab_thread = sg < TAB_POS / TAB_SEG && sg * TAB_SEG < n_loc;
+  // every thread loads (segment index wrapped), so no load sits behind a branch
+  const float2 t_st = tabs.start[sg & (TAB_POS / TAB_SEG - 1)][fi], t_d1 = tabs.step[fi], t_d8 = tabs.step8[fi];
   if (M < 0) M = 0;
   if (M > Mmax) M = Mmax;
-  const int n_loc = (Tl - Tq) + i + 1;            // local keys this row sees
   const int n = M + n_loc;                        // <= Mmax + Tl <= DEC_MAX_KEYS (checked at launch)
 
   auto key_row = [&](int key, const uint16_t* mem, const uint16_t* loc) {
@@ -579,30 +592,31 @@ attn_decode_kernel(const uint16_t* __restrict__ Q, int Tq, int Hq, const uint16_
   uint4 kr[DEC_PASSES][2];
 #pragma unroll
   for (int r = 0; r < DEC_PASSES; ++r) {
+    // keys past n read key n - 1 (unconditional loads keep the waits' counts exact); unused
     const int key = kslot + DEC_KPP * r;
-    if (key < n) {
-      const uint16_t* kp = key_row(key, Kmem, Kloc);
-      kr[r][0] = *reinterpret_cast<const uint4*>(kp + 8 * sub);
-      kr[r][1] = *reinterpret_cast<const uint4*>(kp + D / 2 + 8 * sub);
-    }
+    const uint16_t* kp = key_row(key < n ? key : n - 1, Kmem, Kloc);
+    kr[r][0] = *reinterpret_cast<const uint4*>(kp + 8 * sub);
+    kr[r][1] = *reinterpret_cast<const uint4*>(kp + D / 2 + 8 * sub);
+  }
+  // V rows for the weighted sum, also up front: key slot vs = tid / 16 holds keys vs, vs + 32, ...,
+  // lane vd = tid % 16 dims [8 vd, 8 vd + 8) of each (a wave reads four 256-byte rows at a time)
+  const int vslot = tid >> 4, vd = tid & 15;
+  uint4 vr[DEC_VPT];
+#pragma unroll
+  for (int u = 0; u < DEC_VPT; ++u) {
+    const int key = vslot + DEC_VSLOTS * u;       // past n: key n - 1 again, with weight zero
+    vr[u] = *reinterpret_cast<const uint4*>(key_row(key < n ? key : n - 1, Vmem, Vloc) + 8 * vd);
   }
   // the query row, rotated at its position and pre-scaled by scale * log2(e)
   if (tid < D / 2) {
-    const uint16_t* q = Q + (((int64_t)b * Tq + i) * Hq + h) * D;
-    const float x1 = __uint_as_float((uint32_t)q[tid] << 16), x2 = __uint_as_float((uint32_t)q[tid + D / 2] << 16);
+    const float x1 = __uint_as_float((uint32_t)q_x1 << 16), x2 = __uint_as_float((uint32_t)q_x2 << 16);
     float c, sn;
-    rope_cs(rope_offset + (Tl - Tq) + i, tabs.rev[tid], &c, &sn);
+    rope_cs(rope_offset + (Tl - Tq) + i, q_rev, &c, &sn);
     qs[tid] = (x1 * c - x2 * sn) * scale_log2e;
     qs[tid + D / 2] = (x2 * c + x1 * sn) * scale_log2e;
   }
   // cos/sin table of the local keys' positions (as the matrix-core kernel builds it)
-  {
-    const int fi = tid & (D / 2 - 1), sg = tid / (D / 2);
-    static_assert(DEC_THREADS / (D / 2) * TAB_SEG >= TAB_POS, "the segments cover the table");
-    const int p0 = sg * TAB_SEG;
-    if (sg < TAB_POS / TAB_SEG && p0 < n_loc)
-      fill_cs_segment(cs_tab, fi, p0, n_loc, tabs.start[sg][fi], tabs.step[fi], tabs.step8[fi]);
-  }
+  if (tab_thread) fill_cs_segment(cs_tab, fi, sg * TAB_SEG, n_loc, t_st, t_d1, t_d8);
   __syncthreads();
 
   // scores: each key's 8 lanes rotate their pairs (local keys, from the table), take their share of
@@ -646,13 +660,6 @@ attn_decode_kernel(const uint16_t* __restrict__ Q, int Tq, int Hq, const uint16_
   for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
   if (lane == 0) red[0][wave] = m;
   __syncthreads();                                // also: every table read is done
-  // V rows into the table's space by LDS DMA: piece e = tid + DEC_THREADS * u (key e / 16, dims
-  // 8 (e % 16) ..); a wave's 64 pieces are 1 KB of consecutive LDS, its base wave-uniform
-#pragma unroll 4
-  for (int u = 0; u < DEC_VPT; ++u) {
-    const int e = tid + DEC_THREADS * u, key = e >> 4;
-    if (key < n) dma16(key_row(key, Vmem, Vloc) + 8 * (e & 15), area + (size_t)(e - lane) * 16);
-  }
   float mx = red[0][0];
 #pragma unroll
   for (int w = 1; w < DEC_WAVES; ++w) mx = fmaxf(mx, red[0][w]);
@@ -662,39 +669,35 @@ attn_decode_kernel(const uint16_t* __restrict__ Q, int Tq, int Hq, const uint16_
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o);
   if (lane == 0) red[1][wave] = l;
-  wait_vmem_all();                                // this wave's V copies have landed
   __syncthreads();
   float lt = 0.f;
 #pragma unroll
   for (int w = 0; w < DEC_WAVES; ++w) lt += red[1][w];
-  // O = sum_j p_j v_j / l: lane -> dims (2 lane, 2 lane + 1), wave -> keys wave, wave + DEC_WAVES, ...
-  // four independent accumulator pairs, so the LDS reads of consecutive keys overlap
-  float oa[4] = {0.f, 0.f, 0.f, 0.f}, ob[4] = {0.f, 0.f, 0.f, 0.f};
-  int k = wave;
-  for (; k + 3 * DEC_WAVES < n; k += 4 * DEC_WAVES) {
+  // O = sum_j p_j v_j / l: each thread sums its key slot's keys over its 8 dims (keys past n hold
+  // zero rows and zero weights), then the slots' sums are added in order through LDS
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const float w = ps[k + c * DEC_WAVES];
-      const uint32_t v2 = *reinterpret_cast<const uint32_t*>(&vs[k + c * DEC_WAVES][2 * lane]);
-      oa[c] += w * bf16_lo(v2);
-      ob[c] += w * bf16_hi(v2);
+  for (int u = 0; u < DEC_VPT; ++u) {
+    const int key = vslot + DEC_VSLOTS * u;
+    if (DEC_VSLOTS * u < n) {                     // uniform: some key of this round exists
+      const float w = key < n ? ps[key] : 0.f;
+      const uint4 v = vr[u];
+      acc[0] += w * bf16_lo(v.x); acc[1] += w * bf16_hi(v.x);
+      acc[2] += w * bf16_lo(v.y); acc[3] += w * bf16_hi(v.y);
+      acc[4] += w * bf16_lo(v.z); acc[5] += w * bf16_hi(v.z);
+      acc[6] += w * bf16_lo(v.w); acc[7] += w * bf16_hi(v.w);
     }
   }
-  for (; k < n; k += DEC_WAVES) {
-    const float w = ps[k];
-    const uint32_t v2 = *reinterpret_cast<const uint32_t*>(&vs[k][2 * lane]);
-    oa[0] += w * bf16_lo(v2);
-    ob[0] += w * bf16_hi(v2);
-  }
-  pv[wave][lane] = make_float2((oa[0] + oa[1]) + (oa[2] + oa[3]), (ob[0] + ob[1]) + (ob[2] + ob[3]));
+  *reinterpret_cast<float4*>(&pv[vslot][8 * vd]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  *reinterpret_cast<float4*>(&pv[vslot][8 * vd + 4]) = make_float4(acc[4], acc[5], acc[6], acc[7]);
   __syncthreads();
-  if (tid < D / 2) {
-    float2 acc = make_float2(0.f, 0.f);
-#pragma unroll
-    for (int w = 0; w < DEC_WAVES; ++w) { acc.x += pv[w][tid].x; acc.y += pv[w][tid].y; }
+  if (tid < D) {
+    float sum = 0.f;
+#pragma unroll 8
+    for (int sl = 0; sl < DEC_VSLOTS; ++sl) sum += pv[sl][tid];
     const float inv = 1.f / lt;
     const int64_t ri = ((int64_t)b * Tq + i) * Hq + h;
-    *reinterpret_cast<float2*>(O + ri * D + 2 * tid) = make_float2(acc.x * inv, acc.y * inv);
+    O[ri * D + tid] = sum * inv;
     if (LSE && tid == 0) LSE[ri] = (mx + log2f(lt)) * 0.6931471805599453f;
   }
 }
