@@ -354,17 +354,77 @@ __device__ __forceinline__ int64_t shfl_i64(int64_t v, int src) {
 constexpr int S8_WAVES = 8;                  // 4 token tiles x 2 head groups
 constexpr int S8_THREADS = 64 * S8_WAVES;
 
-// This wave copies the selected rows of documents 4w .. 4w+3 of a group into `buf`,
-// one 1 KB half-row per wave instruction (global_load_lds: 16 bytes a lane).  gv:
-// lanes 0..31 hold the group's chunk ids (-1: nothing to copy).
-__device__ __forceinline__ void issue_group(const uint16_t* __restrict__ Krbar, int64_t gv, uint16_t* buf, int wave,
-                                            int lane) {
+// Copies into LDS for the persistent select kernel, written as inline assembly: the compiler does
+// not track them, so it neither orders later LDS reads behind them nor counts them in the waits of
+// the group's own loads; the group loop waits for them with an explicit count instead.  Each copy
+// only reads its operands (no register is written), and M0 is set right before it.
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+// raw buffer resource on `base` covering `bytes` (reads past them return 0); wave-uniform values
+__device__ __forceinline__ i32x4_t copy_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  i32x4_t r;
+  r[0] = (int32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+  r[1] = (int32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xFFFFu);   // stride 0
+  r[2] = (int32_t)__builtin_amdgcn_readfirstlane(bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* lds) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void_t*)lds);
+}
+// 16 bytes a lane: lane i reads the resource at voff and writes lds + 16 i
+__device__ __forceinline__ void copy16_buf(const i32x4_t& rs, uint32_t voff, const void* lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds_addr(lds)), "v"(voff), "s"(rs) : "memory", "m0");
+}
+// 4 bytes a lane: lane i reads the resource at voff and writes lds + 4 i
+__device__ __forceinline__ void copy4_buf(const i32x4_t& rs, uint32_t voff, const void* lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :: "s"(lds_addr(lds)), "v"(voff), "s"(rs) : "memory", "m0");
+}
+// 4 bytes a lane from its own address: lane i reads *gptr and writes lds + 4 i
+__device__ __forceinline__ void copy4_addr(const void* gptr, const void* lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+               :: "s"(lds_addr(lds)), "v"(gptr) : "memory", "m0");
+}
+
+// Copies for one group: its selected rows into `rows` (wave w: documents 4w .. 4w+3, one 1 KB
+// half-row per copy) and, with stored norms, their 1/|k| into `ik` (waves 0-3: lane l of wave w
+// takes entry 64 w + l, i.e. document (64 w + l) / 8, head l % 8).  gv: lanes 0..31 hold the
+// group's chunk ids.  A document with id -1 gets zero rows and chunk 0's norms (none at all when the
+// store is empty); its scores are discarded.
+__device__ __forceinline__ void copy_group(const uint16_t* __restrict__ Krbar, const float* __restrict__ knorm,
+                                           int64_t n_chunks, int64_t gv, uint16_t* rows, float* ik, int wave,
+                                           int lane, uint32_t voff16) {
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
     const int doc = wave * 4 + (q >> 1), hh = q & 1;
     const int64_t g = shfl_i64(gv, doc);
-    if (g >= 0) dma16(Krbar + g * P_HD + hh * 512 + lane * 8, buf + doc * P_KROW + hh * 512);
+    copy16_buf(copy_rsrc(Krbar + (g >= 0 ? g : 0) * P_HD + hh * 512, g >= 0 ? 1024u : 0u), voff16,
+               rows + doc * P_KROW + hh * 512);
   }
+  if (knorm && n_chunks > 0 && wave < 4) {
+    const int e = wave * 64 + lane;
+    const int64_t g = shfl_i64(gv, e >> 3);
+    copy4_addr(knorm + (g >= 0 ? g : 0) * 8 + (e & 7), ik + wave * 64);
+  }
+}
+
+// Chunk ids of group `gr` (32 int64, 256 B) into `ids`: one 4-byte copy by the last wave.  Entries
+// past the last document read 0 (the resource's range); group_ids masks them.
+__device__ __forceinline__ void copy_ids(const int64_t* __restrict__ gs, int64_t n_docs, int64_t gr, int64_t* ids,
+                                         int wave, uint32_t voff4) {
+  if (wave == S8_WAVES - 1) {
+    const int64_t first = gr * PG;
+    const int64_t left = first < n_docs ? n_docs - first : 0;
+    copy4_buf(copy_rsrc(gs + (left > 0 ? first : 0), (uint32_t)((left < PG ? left : PG) * 8)), voff4, ids);
+  }
+}
+// lanes 0..31: the chunk id of document gr * 32 + lane from the copied ids (-1 past the end)
+__device__ __forceinline__ int64_t group_ids(const int64_t* ids, int64_t gr, int64_t n_docs, int lane) {
+  const int64_t d = gr * PG + (lane & 31);
+  const int64_t v = ids[lane & 31];
+  return (lane < 32 && d < n_docs) ? v : -1;
 }
 
 // Router rows of token tile tt as A operands for heads 4 hg .. 4 hg + 3, and their
@@ -391,48 +451,56 @@ __device__ __forceinline__ void load_rows4(const uint16_t* __restrict__ Qr, int 
 }
 
 struct S8Lds {
-  float ik[PG][8];
+  float ik[2][PG][8];                  // 1/|k| of (document, head), one per row buffer
+  int64_t ids[2][PG];                  // chunk ids, copied two groups ahead
   float iq[S8_WAVES][4][32];
   f32x4_t xchg[4][64 * 4];             // head group 1's partial scores, per token tile
   uint64_t best[4][PG];
   int tsel[PG];
 };
 
-// One group of 32 documents whose rows sit in `cur` (landed); the next group's
-// rows are copied into `nxt` meanwhile.
+// One group of 32 documents whose rows sit in `cur` and norms in `ik_cur`; the next group's
+// copies go into `nxt` / `ik_nxt` meanwhile, and the chunk ids of the group after it into
+// `ids_wr`.  g_cur (lanes 0..31): this group's chunk ids on entry, the next group's on exit.
+// RESIDENT (T <= 128): the router rows stay in `a` for the whole kernel; else each token tile's
+// rows are loaded per round.
+template <bool RESIDENT>
 __device__ __forceinline__ void select8_group(const uint16_t* __restrict__ Qr, int b, int T,
-                                              const float* __restrict__ knorm, float& ik_pre, int64_t n_docs, const float* __restrict__ dDoc, int64_t grp,
-                                              int64_t g_cur, int64_t g_nxt, bool has_next,
-                                              const uint16_t* __restrict__ Krbar, const uint16_t* cur, uint16_t* nxt,
-                                              bf16x8_t (&a)[4][8], bool resident, S8Lds& sm,
+                                              const uint16_t* __restrict__ Krbar, const float* __restrict__ knorm,
+                                              int64_t n_chunks, int64_t n_docs, const float* __restrict__ dDoc,
+                                              const int64_t* __restrict__ gs, int64_t grp, int64_t stride,
+                                              int64_t& g_cur, bool first, const uint16_t* cur, uint16_t* nxt,
+                                              float* ik_cur, float* ik_nxt, const int64_t* ids_rd, int64_t* ids_wr,
+                                              bf16x8_t (&a)[4][8], S8Lds& sm,
                                               float* __restrict__ dK, int32_t* __restrict__ sel,
                                               float* __restrict__ ikw, float* __restrict__ wcos, int tid, int wave,
-                                              int lane) {
+                                              int lane, uint32_t voff16, uint32_t voff4) {
   constexpr int H = 8;
   const int half = lane >> 5, m = lane & 31;
   const int rt = wave & 3, hg = wave >> 2;         // token tile slot, head group
-  wait_vmem_all();
-  lds_barrier();                                   // `cur` landed; the previous group is done with `nxt`
-  if (has_next) issue_group(Krbar, g_nxt, nxt, wave, lane);
-  if (tid < PG * H) {
-    // 1/|k| of (document tid % 32, head tid / 32): the stored norm fetched one group
-    // ahead, or from the staged rows (consecutive lanes on consecutive rows: no bank
-    // conflicts)
+  // This wave's copies for this group: the prologue's (first group: wait for everything), else
+  // those issued at the previous group's start.  The previous group was not the last one, so all
+  // its documents exist and this wave issued its 16 key-gradient stores after those copies: they
+  // may stay in flight (vector memory completes in order).
+  if (first)
+    __builtin_amdgcn_s_waitcnt(0x0F70);            // vmcnt(0)
+  else
+    __builtin_amdgcn_s_waitcnt(0x4F70);            // vmcnt(16)
+  asm volatile("" ::: "memory");
+  lds_barrier();                                   // everyone's copies landed; the previous group is done with `nxt`
+  const int64_t nx = grp + stride;
+  const int64_t g_nxt = group_ids(ids_rd, nx, n_docs, lane);
+  copy_group(Krbar, knorm, n_chunks, g_nxt, nxt, ik_nxt, wave, lane, voff16);
+  copy_ids(gs, n_docs, nx + stride, ids_wr, wave, voff4);
+  if (!knorm && tid < PG * H) {
+    // 1/|k| of (document tid % 32, head tid / 32) from the staged rows (consecutive lanes on
+    // consecutive rows: no bank conflicts)
     const int doc = tid & 31, h = tid >> 5;
-    float ik = ik_pre;
-    if (!knorm) {
-      float ss = 0.f;
+    float ss = 0.f;
 #pragma unroll
-      for (int x = 0; x < D / 8; ++x)
-        ss = sq_norm_piece(*reinterpret_cast<const uint4*>(cur + doc * P_KROW + h * D + 8 * x), ss);
-      ik = inv_norm(ss);
-    }
-    sm.ik[doc][h] = shfl_i64(g_cur, doc) >= 0 ? ik : 0.f;
-    // the next group's stored norm, in flight while this group is scored
-    if (knorm) {
-      const int64_t gn = shfl_i64(g_nxt, doc);
-      ik_pre = gn >= 0 ? knorm[gn * H + h] : 0.f;
-    }
+    for (int x = 0; x < D / 8; ++x)
+      ss = sq_norm_piece(*reinterpret_cast<const uint4*>(cur + doc * P_KROW + h * D + 8 * x), ss);
+    ik_cur[doc * 8 + h] = inv_norm(ss);
   }
   lds_barrier();
   // token scores of the 32 rows: wave (rt, hg) takes token tiles rt, rt + 4, ... over heads 4 hg ..
@@ -445,7 +513,7 @@ __device__ __forceinline__ void select8_group(const uint16_t* __restrict__ Qr, i
     const bool act = tt < n_tt;
     f32x16_t s0 = {};
     if (act) {
-      if (!resident) load_rows4(Qr, b, T, tt, hg, m, half, a, sm.iq[wave]);
+      if constexpr (!RESIDENT) load_rows4(Qr, b, T, tt, hg, m, half, a, sm.iq[wave]);
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
         f32x16_t c = {};
@@ -454,7 +522,7 @@ __device__ __forceinline__ void select8_group(const uint16_t* __restrict__ Qr, i
         for (int ks = 0; ks < 8; ++ks)
           c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[h][ks], *reinterpret_cast<const bf16x8_t*>(bp + 16 * ks),
                                                       c, 0, 0, 0);
-        const float ik = sm.ik[m][hg * 4 + h];
+        const float ik = ik_cur[m * 8 + hg * 4 + h];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const f32x4_t r = *reinterpret_cast<const f32x4_t*>(&sm.iq[wave][h][8 * q + 4 * half]);
@@ -503,67 +571,67 @@ __device__ __forceinline__ void select8_group(const uint16_t* __restrict__ Qr, i
   const int idoc = tid >> 4, sub = tid & 15;
   const int64_t d = grp * PG + idoc;
   const int64_t g = shfl_i64(g_cur, idoc);
-  if (d >= n_docs) return;
+  g_cur = g_nxt;
+  if (d >= n_docs) return;                         // only in the last group
   const int tsel = sm.tsel[idoc];
   const int64_t bd = (int64_t)b * n_docs + d;
-  if (sub == 0) {
-    sel[2 * bd] = tsel < 0 ? -1 : (int32_t)g;
-    sel[2 * bd + 1] = tsel;
-  }
   float4* o = reinterpret_cast<float4*>(dK + bd * P_HD);
   if (tsel < 0) {
+    if (sub == 0) {
+      sel[2 * bd] = -1;
+      sel[2 * bd + 1] = -1;
+    }
 #pragma unroll
     for (int x = 0; x < P_HD / 4 / 16; ++x) nt_store4(o + sub + 16 * x, 0.f, 0.f, 0.f, 0.f);
     if (sub < H) { ikw[bd * H + sub] = 0.f; wcos[bd * H + sub] = 0.f; }
     return;
   }
+  // every load of this phase before its first store (a load issued after a store would wait for it)
   const float w = dDoc[bd] * (1.0f / (float)H);
   const uint16_t* qrow = Qr + ((int64_t)b * T + tsel) * P_HD;
+  uint2 qv[H][2];
+#pragma unroll
+  for (int h = 0; h < H; ++h)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) qv[h][j] = *reinterpret_cast<const uint2*>(qrow + h * D + 4 * (sub + 16 * j));
+  if (sub == 0) {
+    sel[2 * bd] = (int32_t)g;
+    sel[2 * bd + 1] = tsel;
+  }
   const uint16_t* krow = cur + idoc * P_KROW;
   float my_ikw = 0.f, my_wc = 0.f;
 #pragma unroll
-  for (int h0 = 0; h0 < H; h0 += 4) {
-    uint2 qv[4][2], kv[4][2];
+  for (int h = 0; h < H; ++h) {
+    uint2 kv[2];
 #pragma unroll
-    for (int h = 0; h < 4; ++h)
+    for (int j = 0; j < 2; ++j) kv[j] = *reinterpret_cast<const uint2*>(krow + h * D + 4 * (sub + 16 * j));
+    float qq = 0.f, kk = 0.f, qk = 0.f;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        qv[h][j] = *reinterpret_cast<const uint2*>(qrow + (h0 + h) * D + 4 * (sub + 16 * j));
-        kv[h][j] = *reinterpret_cast<const uint2*>(krow + (h0 + h) * D + 4 * (sub + 16 * j));
-      }
-    float qq[4], kk[4], qk[4];
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      float a2 = 0.f, b2 = 0.f, c2 = 0.f;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        a2 = dot2_bf16(qv[h][j].x, qv[h][j].x, a2); a2 = dot2_bf16(qv[h][j].y, qv[h][j].y, a2);
-        b2 = dot2_bf16(kv[h][j].x, kv[h][j].x, b2); b2 = dot2_bf16(kv[h][j].y, kv[h][j].y, b2);
-        c2 = dot2_bf16(qv[h][j].x, kv[h][j].x, c2); c2 = dot2_bf16(qv[h][j].y, kv[h][j].y, c2);
-      }
-      qq[h] = sum16(a2);
-      kk[h] = sum16(b2);
-      qk[h] = sum16(c2);
+    for (int j = 0; j < 2; ++j) {
+      const uint2 x = qv[h][j], y = kv[j];
+      qq = dot2_bf16(x.x, x.x, qq); qq = dot2_bf16(x.y, x.y, qq);
+      kk = dot2_bf16(y.x, y.x, kk); kk = dot2_bf16(y.y, y.y, kk);
+      qk = dot2_bf16(x.x, y.x, qk); qk = dot2_bf16(x.y, y.y, qk);
+    }
+    qq = sum16(qq);
+    kk = sum16(kk);
+    qk = sum16(qk);
+    float ca = 0.f, cb = 0.f, ik = 0.f, cs = 0.f;
+    if (qq > 0.f && kk > 0.f) {
+      const float iq = 1.0f / sqrtf(qq);
+      ik = 1.0f / sqrtf(kk);
+      cs = qk * iq * ik;
+      ca = w * ik * iq;          // dK = w (q^ - c k^) / |k| = ca q - cb k
+      cb = w * ik * ik * cs;
     }
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      float ca = 0.f, cb = 0.f, ik = 0.f, cs = 0.f;
-      if (qq[h] > 0.f && kk[h] > 0.f) {
-        const float iq = 1.0f / sqrtf(qq[h]);
-        ik = 1.0f / sqrtf(kk[h]);
-        cs = qk[h] * iq * ik;
-        ca = w * ik * iq;        // dK = w (q^ - c k^) / |k| = ca q - cb k
-        cb = w * ik * ik * cs;
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        nt_store4(o + (h0 + h) * (D / 4) + sub + 16 * j,
-                  ca * bf16_lo(qv[h][j].x) - cb * bf16_lo(kv[h][j].x),
-                  ca * bf16_hi(qv[h][j].x) - cb * bf16_hi(kv[h][j].x),
-                  ca * bf16_lo(qv[h][j].y) - cb * bf16_lo(kv[h][j].y),
-                  ca * bf16_hi(qv[h][j].y) - cb * bf16_hi(kv[h][j].y));
-      if (h0 + h == sub) { my_ikw = w * ik; my_wc = w * cs; }
+    for (int j = 0; j < 2; ++j) {
+      const uint2 x = qv[h][j], y = kv[j];
+      nt_store4(o + h * (D / 4) + sub + 16 * j,
+                ca * bf16_lo(x.x) - cb * bf16_lo(y.x), ca * bf16_hi(x.x) - cb * bf16_hi(y.x),
+                ca * bf16_lo(x.y) - cb * bf16_lo(y.y), ca * bf16_hi(x.y) - cb * bf16_hi(y.y));
     }
+    if (h == sub) { my_ikw = w * ik; my_wc = w * cs; }
   }
   if (sub < H) { ikw[bd * H + sub] = my_ikw; wcos[bd * H + sub] = my_wc; }
 }
@@ -572,57 +640,53 @@ __device__ __forceinline__ void select8_group(const uint16_t* __restrict__ Qr, i
 // blockIdx.x + gridDim.x, ... of one query.  Eight waves: wave (rt, hg) scores
 // token tile rt (+4, ...) over heads 4 hg .. 4 hg + 3, and with T <= 128 keeps
 // those 32 router rows resident as A operands (128 registers); the two head
-// groups add their partial sums through LDS.  The next group's rows are copied
-// into the other LDS buffer while this one is scored; the buffers are separate
-// LDS objects and the loop is unrolled by two, so the compiler never orders a
-// read of one behind a copy into the other.
+// groups add their partial sums through LDS.  While a group is scored, the next
+// group's rows and norms and the chunk ids of the group after it are copied into
+// LDS; the loop is unrolled by two so every buffer address is static.
+template <bool RESIDENT>
 __global__ void __launch_bounds__(S8_THREADS)
 route_bwd_select8_kernel(const uint16_t* __restrict__ Qr, int T, const uint16_t* __restrict__ Krbar,
-                         const float* __restrict__ knorm, int64_t n_docs, const float* __restrict__ dDoc,
-                         const int64_t* __restrict__ gsel, float* __restrict__ dK, int32_t* __restrict__ sel,
-                         float* __restrict__ ikw, float* __restrict__ wcos) {
+                         const float* __restrict__ knorm, int64_t n_chunks, int64_t n_docs,
+                         const float* __restrict__ dDoc, const int64_t* __restrict__ gsel, float* __restrict__ dK,
+                         int32_t* __restrict__ sel, float* __restrict__ ikw, float* __restrict__ wcos) {
   __shared__ __attribute__((aligned(16))) uint16_t kbuf0[PG * P_KROW];
   __shared__ __attribute__((aligned(16))) uint16_t kbuf1[PG * P_KROW];
-  __shared__ S8Lds sm;
+  __shared__ __attribute__((aligned(16))) S8Lds sm;
   const int b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t n_groups = (n_docs + PG - 1) / PG;
+  const int64_t stride = gridDim.x;
   int64_t grp = blockIdx.x;
   if (grp >= n_groups) return;
   const int n_tt = (T + 31) / 32;
-  const bool resident = n_tt <= 4;
   bf16x8_t a[4][8];
-  if (resident) load_rows4(Qr, b, T, (wave & 3) < n_tt ? (wave & 3) : 0, wave >> 2, lane & 31, lane >> 5, a,
+  if constexpr (RESIDENT) load_rows4(Qr, b, T, (wave & 3) < n_tt ? (wave & 3) : 0, wave >> 2, lane & 31, lane >> 5, a,
                            sm.iq[wave]);
   const int64_t* gs = gsel + (int64_t)b * n_docs;
-  // a group's chunk ids (lanes 0..31 of every wave) and, with stored norms, the
-  // inverse norm of (document tid / 8, head tid % 8), both fetched one group ahead
-  auto chunk_ids = [&](int64_t gr) -> int64_t {
-    const int64_t d = gr * PG + (lane & 31);
-    return (gr < n_groups && lane < 32 && d < n_docs) ? gs[d] : -1;
-  };
-  int64_t g_cur = chunk_ids(grp), g_nxt;
-  float ik_pre = 0.f;
-  if (knorm && tid < PG * 8) {
-    const int64_t g = shfl_i64(g_cur, tid & 31);
-    ik_pre = g >= 0 ? knorm[g * 8 + (tid >> 5)] : 0.f;
+  const uint32_t voff16 = (uint32_t)lane * 16u, voff4 = (uint32_t)lane * 4u;
+  // prologue: this group's chunk ids (lanes 0..31), its copies, and the next group's ids
+  int64_t g_cur = -1;
+  {
+    const int64_t d = grp * PG + (lane & 31);
+    if (lane < 32 && d < n_docs) g_cur = gs[d];
   }
-  issue_group(Krbar, g_cur, kbuf0, wave, lane);
+  copy_group(Krbar, knorm, n_chunks, g_cur, kbuf0, &sm.ik[0][0][0], wave, lane, voff16);
+  copy_ids(gs, n_docs, grp + stride, sm.ids[1], wave, voff4);
+  bool first = true;
   while (true) {
-    int64_t nx = grp + gridDim.x;
-    g_nxt = chunk_ids(nx);
-    select8_group(Qr, b, T, knorm, ik_pre, n_docs, dDoc, grp, g_cur, g_nxt, nx < n_groups, Krbar, kbuf0, kbuf1, a,
-                  resident, sm, dK, sel, ikw, wcos, tid, wave, lane);
-    if (nx >= n_groups) break;
-    grp = nx;
-    g_cur = g_nxt;
-    nx = grp + gridDim.x;
-    g_nxt = chunk_ids(nx);
-    select8_group(Qr, b, T, knorm, ik_pre, n_docs, dDoc, grp, g_cur, g_nxt, nx < n_groups, Krbar, kbuf1, kbuf0, a,
-                  resident, sm, dK, sel, ikw, wcos, tid, wave, lane);
-    if (nx >= n_groups) break;
-    grp = nx;
-    g_cur = g_nxt;
+    select8_group<RESIDENT>(Qr, b, T, Krbar, knorm, n_chunks, n_docs, dDoc, gs, grp, stride, g_cur, first, kbuf0,
+                            kbuf1,
+                  &sm.ik[0][0][0], &sm.ik[1][0][0], sm.ids[1], sm.ids[0], a, sm, dK, sel, ikw, wcos, tid,
+                  wave, lane, voff16, voff4);
+    first = false;
+    grp += stride;
+    if (grp >= n_groups) break;
+    select8_group<RESIDENT>(Qr, b, T, Krbar, knorm, n_chunks, n_docs, dDoc, gs, grp, stride, g_cur, false, kbuf1,
+                            kbuf0,
+                  &sm.ik[1][0][0], &sm.ik[0][0][0], sm.ids[0], sm.ids[1], a, sm, dK, sel, ikw, wcos, tid,
+                  wave, lane, voff16, voff4);
+    grp += stride;
+    if (grp >= n_groups) break;
   }
   wait_vmem_all();                                 // no copy into LDS outlives the workgroup
 }
@@ -921,8 +985,14 @@ int launch_bwd_h(const BwdArgs& A, const BwdLayout& L, uint8_t* ws, hipStream_t 
     const int64_t n_groups = (n_docs + PG - 1) / PG;
     int64_t per_b = (SELECT8_WORKGROUPS + B - 1) / B;
     per_b = per_b < n_groups ? per_b : n_groups;
-    hipLaunchKernelGGL(route_bwd_select8_kernel, dim3((unsigned)per_b, (unsigned)B), dim3(S8_THREADS), 0, stream,
-                       A.Qr, T, A.Krbar, A.knorm, n_docs, A.dDoc, gsel, A.dK, A.sel, ikw, wcos);
+    if (T <= 128)
+      hipLaunchKernelGGL(route_bwd_select8_kernel<true>, dim3((unsigned)per_b, (unsigned)B), dim3(S8_THREADS), 0,
+                         stream, A.Qr, T, A.Krbar, A.knorm, A.n_chunks, n_docs, A.dDoc, gsel, A.dK, A.sel,
+                         ikw, wcos);
+    else
+      hipLaunchKernelGGL(route_bwd_select8_kernel<false>, dim3((unsigned)per_b, (unsigned)B), dim3(S8_THREADS), 0,
+                         stream, A.Qr, T, A.Krbar, A.knorm, A.n_chunks, n_docs, A.dDoc, gsel, A.dK, A.sel,
+                         ikw, wcos);
     MSA_CHECK_LAUNCH();
   } else {
     hipLaunchKernelGGL(route_bwd_select_kernel<H>, dim3((unsigned)((n_docs + SEL_DOCS - 1) / SEL_DOCS), (unsigned)B),

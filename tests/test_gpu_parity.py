@@ -345,6 +345,23 @@ def test_route_backward_special_cases():
     assert (sel[..., 0] >= 0).sum() <= 2 * 16
 
 
+@pytest.mark.parametrize("B,T,stored", [(4, 12, True), (4, 8, False)])
+def test_route_backward_many_groups_per_workgroup(B, T, stored):
+    """H = 8 with several groups of 32 documents per workgroup of the persistent selection kernel
+    (9,001 documents over 4 queries: ~4 groups each, a partial last group), so the copies issued
+    one group ahead and the chunk ids copied two groups ahead are exercised, with and without
+    stored key norms."""
+    n_docs = 9001
+    announce("route-backward-many-groups", B, T, stored, n_docs)
+    lens = np.random.default_rng(T).integers(1, 3, n_docs)
+    Qr, Kr, off = _route_case(B, T, 8, n_docs, seed=1700 + T, lens=lens)
+    dDoc = np.random.default_rng(T + 1).standard_normal((B, n_docs))
+    excl = np.zeros((B, n_docs), bool)
+    excl[1, ::97] = True
+    sel = _check_route_backward(Qr, Kr, off, dDoc, excl, stored_norms=stored)
+    assert (sel[..., 0] >= 0).mean() > 0.9
+
+
 @pytest.mark.parametrize("B,T,H,n_docs", [(1, 8192, 8, 90), (2, 600, 8, 700), (1, 8192, 2, 40)])
 def test_route_backward_long_queries(B, T, H, n_docs):
     """The longest router queries the call accepts (T = 8192: 256 token tiles, the router rows
