@@ -399,7 +399,9 @@ __device__ __forceinline__ void copy_group(const uint16_t* __restrict__ Krbar, c
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
     const int doc = wave * 4 + (q >> 1), hh = q & 1;
-    const int64_t g = shfl_i64(gv, doc);
+    // the document's id straight into scalar registers (the lane is wave-uniform)
+    const int64_t g = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)((uint64_t)gv >> 32), doc) << 32) |
+                                (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)gv, doc));
     copy16_buf(copy_rsrc(Krbar + (g >= 0 ? g : 0) * P_HD + hh * 512, g >= 0 ? 1024u : 0u), voff16,
                rows + doc * P_KROW + hh * 512);
   }
@@ -545,12 +547,19 @@ __device__ __forceinline__ void select8_group(const uint16_t* __restrict__ Qr, i
 #pragma unroll
         for (int e = 0; e < 4; ++e) s0[4 * q + e] += x[e];
       }
-      // C register i holds row 8 (i / 4) + 4 half + i % 4 of column m
+      // C register i holds row 8 (i / 4) + 4 half + i % 4 of column m: rows increase with i, so
+      // the first largest sum is the lowest maximising token.  32-bit compares on the
+      // order-preserving encoding (0 = none), then one 64-bit key per lane; scaling by 1 / H
+      // (a power of two) keeps the order and the ties.
+      uint32_t be = 0u;
+      int btok = 0;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int tok = tt * 32 + 8 * (i / 4) + 4 * half + (i % 4);
-        if (tok < T) bk = max_u64(bk, argmax_key(s0[i] * inv_h, tok));
+        const uint32_t e = tok < T ? enc_f32(s0[i]) : 0u;
+        if (e > be) { be = e; btok = tok; }
       }
+      if (be != 0u) bk = max_u64(bk, argmax_key(dec_f32(be) * inv_h, btok));
     }
     lds_barrier();                                  // exchange slots free for the next round
   }
@@ -618,8 +627,8 @@ __device__ __forceinline__ void select8_group(const uint16_t* __restrict__ Qr, i
     qk = sum16(qk);
     float ca = 0.f, cb = 0.f, ik = 0.f, cs = 0.f;
     if (qq > 0.f && kk > 0.f) {
-      const float iq = 1.0f / sqrtf(qq);
-      ik = 1.0f / sqrtf(kk);
+      const float iq = __builtin_amdgcn_rsqf(qq);   // hardware reciprocal square root (~1 ulp)
+      ik = __builtin_amdgcn_rsqf(kk);
       cs = qk * iq * ik;
       ca = w * ik * iq;          // dK = w (q^ - c k^) / |k| = ca q - cb k
       cb = w * ik * ik * cs;
