@@ -405,16 +405,22 @@ topk_from_groups_filtered(const float* __restrict__ scores, uint64_t* __restrict
 
 // The document max (the last step of the routing scores: a document's score is the max of its
 // chunks', -inf when excluded or empty), with the group maxima of the top-k folded in (GROUPS).
-// One workgroup per (group of 64 documents, query).  Offsets are non-decreasing, so the group's
-// documents own the contiguous chunk range [off[d0], off[d0 + nd]): the 256 threads read it and
-// set it back to 0 (re-arming the workspace for the next scan) with coalesced accesses, two
-// chunks in flight per thread, and each chunk finds its document by a binary search over the
-// group's offsets in LDS and adds its maximum to the document's LDS slot with an LDS atomic max;
-// then the first wave forms the 64 scores and the group's largest key.  Offsets are clamped to
-// [0, n_chunks] and the search stays inside the group, so offsets that break the contract give
-// wrong scores but no access outside the buffers.
+// One workgroup of 128 threads per (group of 64 documents, query), so that every workgroup of a
+// 100M-token layer's 3,125 groups is resident at once and the kernel costs about one workgroup's
+// latency.  Offsets are non-decreasing, so the group's documents own the contiguous chunk range
+// [off[d0], off[d0 + nd]): the threads read it and set it back to 0 (re-arming the workspace for
+// the next scan) with coalesced accesses, DR_BATCH chunks in flight per thread (one pass for up to
+// 1,024 chunks), and each chunk finds its document by a binary search over the group's offsets in
+// LDS and adds its maximum to the document's LDS slot with an LDS atomic max; then the first wave
+// forms the 64 scores and the group's largest key.  The exclusion flags are loaded with the
+// offsets, before the first barrier.  Offsets are clamped to [0, n_chunks] and the search stays
+// inside the group, so offsets that break the contract give wrong scores but no access outside
+// the buffers.
+constexpr int DR_THREADS = 128;
+constexpr int DR_BATCH = 8;
+
 template <bool GROUPS>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(DR_THREADS)
 doc_reduce_kernel(uint32_t* __restrict__ chunk_enc, int64_t n_chunks,
                   const int64_t* __restrict__ doc_chunk_off, int64_t n_docs,
                   const uint8_t* __restrict__ doc_exclude, float* __restrict__ doc_scores,
@@ -426,6 +432,8 @@ doc_reduce_kernel(uint32_t* __restrict__ chunk_enc, int64_t n_chunks,
   const int tid = threadIdx.x;
   const int64_t d0 = grp * GROUP;
   const int nd = (int)(n_docs - d0 < GROUP ? n_docs - d0 : GROUP);   // >= 1
+  bool excluded = false;
+  if (doc_exclude && tid < nd) excluded = doc_exclude[(int64_t)b * n_docs + d0 + tid] != 0;
   if (tid <= nd) {
     int64_t o = doc_chunk_off[d0 + tid];
     o = o < 0 ? 0 : (o > n_chunks ? n_chunks : o);
@@ -446,19 +454,22 @@ doc_reduce_kernel(uint32_t* __restrict__ chunk_enc, int64_t n_chunks,
     }
     return lo;
   };
-  for (int64_t c = c0 + tid; c < c1; c += 512) {
-    const int64_t c2 = c + 256;
-    const bool two = c2 < c1;
-    const uint32_t e = ce[c];
-    const uint32_t e2 = two ? ce[c2] : 0u;
-    ce[c] = 0u;
-    if (two) ce[c2] = 0u;
-    if (cs) {
-      cs[c] = dec_f32(e);
-      if (two) cs[c2] = dec_f32(e2);
+  for (int64_t c = c0 + tid; c < c1; c += DR_THREADS * DR_BATCH) {
+    uint32_t e[DR_BATCH];
+#pragma unroll
+    for (int u = 0; u < DR_BATCH; ++u) {
+      const int64_t cu = c + u * DR_THREADS;
+      e[u] = cu < c1 ? ce[cu] : 0u;
     }
-    atomicMax(&s_best[doc_of(c)], e);
-    if (two) atomicMax(&s_best[doc_of(c2)], e2);
+#pragma unroll
+    for (int u = 0; u < DR_BATCH; ++u) {
+      const int64_t cu = c + u * DR_THREADS;
+      if (cu < c1) {
+        ce[cu] = 0u;
+        if (cs) cs[cu] = dec_f32(e[u]);
+        atomicMax(&s_best[doc_of(cu)], e[u]);
+      }
+    }
   }
   __syncthreads();
   if (tid < GROUP) {
@@ -466,7 +477,7 @@ doc_reduce_kernel(uint32_t* __restrict__ chunk_enc, int64_t n_chunks,
     if (tid < nd) {
       const int64_t d = d0 + tid;
       float s = s_off[tid + 1] > s_off[tid] ? dec_f32(s_best[tid]) : -INFINITY;
-      if (doc_exclude && doc_exclude[(int64_t)b * n_docs + d]) s = -INFINITY;
+      if (excluded) s = -INFINITY;
       doc_scores[(int64_t)b * n_docs + d] = s;
       key = make_key(s, (uint32_t)d);
     }
@@ -521,7 +532,7 @@ int launch_docs_topk(uint32_t* chunk_enc, int64_t n_chunks, const int64_t* doc_c
                      const uint8_t* doc_exclude, int B, int k, float* doc_scores, float* chunk_scores,
                      int32_t* top_idx, float* top_scores, uint64_t* gmax, hipStream_t stream) {
   const int64_t n_groups = (n_docs + GROUP - 1) / GROUP;
-  hipLaunchKernelGGL(doc_reduce_kernel<true>, dim3((unsigned)n_groups, (unsigned)B), dim3(256), 0, stream,
+  hipLaunchKernelGGL(doc_reduce_kernel<true>, dim3((unsigned)n_groups, (unsigned)B), dim3(DR_THREADS), 0, stream,
                      chunk_enc, n_chunks, doc_chunk_off, n_docs, doc_exclude, doc_scores, chunk_scores, n_groups,
                      gmax);
   MSA_CHECK_LAUNCH();
@@ -531,7 +542,7 @@ int launch_docs_topk(uint32_t* chunk_enc, int64_t n_chunks, const int64_t* doc_c
 int launch_doc_reduce(uint32_t* chunk_enc, int64_t n_chunks, const int64_t* doc_chunk_off, int64_t n_docs,
                       const uint8_t* doc_exclude, int B, float* doc_scores, float* chunk_scores, hipStream_t stream) {
   const int64_t n_groups = (n_docs + GROUP - 1) / GROUP;
-  hipLaunchKernelGGL(doc_reduce_kernel<false>, dim3((unsigned)n_groups, (unsigned)B), dim3(256), 0, stream,
+  hipLaunchKernelGGL(doc_reduce_kernel<false>, dim3((unsigned)n_groups, (unsigned)B), dim3(DR_THREADS), 0, stream,
                      chunk_enc, n_chunks, doc_chunk_off, n_docs, doc_exclude, doc_scores, chunk_scores, n_groups,
                      nullptr);
   MSA_CHECK_LAUNCH();

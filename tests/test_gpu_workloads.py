@@ -316,6 +316,7 @@ def oracle_krbar_corpus(w, slab_tokens=1_000_000):
         t0, t1 = int(w.doc_tok_off[d0]), int(w.doc_tok_off[d1])
         c0, c1 = int(w.doc_chunk_off[d0]), int(w.doc_chunk_off[d1])
         out[c0:c1] = O.round_bf16(ON.pool_means_bf16(C.raw_block(w, "Kr", t0, t1), w.doc_len[d0:d1], w.chunk))
+        announce("oracle router-key pooling: documents", d0, "..", d1 - 1, "of", w.n_docs)
         d0 = d1
     return out
 
