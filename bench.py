@@ -353,6 +353,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-baseline-seconds", type=float, default=12.0)
     ap.add_argument("--skip-side", action="store_true", help="headline only (for profiler runs)")
+    ap.add_argument("--jsonl", metavar="PATH", default=None,
+                    help="also append the result line to PATH (one JSON object per run)")
     ap.add_argument("--route-only", type=int, default=0, metavar="N",
                     help="counter-collection mode: one 100M-token layer, a 1 GiB device copy (the reference for "
                          "scaling FETCH_SIZE/WRITE_SIZE), then N routing scans; prints one line and exits")
@@ -934,7 +936,11 @@ def main():
         "needles_retrieved": f"{needles_found}/{L * w.n_needles}",
     }
     out.update(side_out)
-    print(json.dumps(out), flush=True)
+    line = json.dumps(out)
+    print(line, flush=True)
+    if args.jsonl:
+        with open(args.jsonl, "a") as fh:
+            fh.write(line + "\n")
 
 
 if __name__ == "__main__":
